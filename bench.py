@@ -1,0 +1,246 @@
+"""Benchmark of the sketch hot path on one MI355X.
+
+One step = the whole path for one training step of one Qwen3-1.7B-shaped
+block (q 2048->2048, k and v 2048->1024, o 2048->2048, gate and up
+2048->6144, down 6144->2048; W is out x in), rank 64, QR-of-Gaussian
+projections redrawn every step, 32768 tokens in 8 microbatches of 4096:
+
+  7 x rgc_sample_projection (QR)
+  8 x 7 x (rgc_project + rgc_accumulate)
+  7 x rgc_apply (tau = 1e-3)
+
+Inputs are synthetic and resident in HBM before timing: X ~ N(0,1) (shared by
+q/k/v and by gate/up, as in the real block), D ~ N(0, 1e-3^2), W ~ N(0, 0.02^2),
+all bf16. Prints one JSON line (see the fields below).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+BLOCK_1P7B = [  # name, d (out), k (in), input activation
+    ("q", 2048, 2048, "attn_in"), ("k", 1024, 2048, "attn_in"), ("v", 1024, 2048, "attn_in"),
+    ("o", 2048, 2048, "attn_out"), ("gate", 6144, 2048, "mlp_in"), ("up", 6144, 2048, "mlp_in"),
+    ("down", 2048, 6144, "mlp_act"),
+]
+WORKLOAD = {"name": "qwen3-1.7b-block", "matrices": BLOCK_1P7B, "r": 64, "kind": "qr", "tokens": 32768,
+            "microbatch": 4096, "tau": 1e-3}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    return ap.parse_args()
+
+
+def step_seed(step: int, m: int) -> int:
+    return (2 << 32) | (step << 8) | m
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from rank_randomized_gradient_amd import rgc
+
+    rgc.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    wl = WORKLOAD
+    r, T, mb = wl["r"], wl["tokens"], wl["microbatch"]
+    n_mb = T // mb
+    mats = wl["matrices"]
+
+    # ---- synthetic inputs, resident in HBM ------------------------------------
+    g = torch.Generator(device=dev)
+    g.manual_seed(2024)
+
+    def normal(shape, std):
+        return (torch.randn(*shape, generator=g, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
+
+    acts = {"attn_in": 2048, "attn_out": 2048, "mlp_in": 2048, "mlp_act": 6144}
+    X = {name: normal((T, width), 1.0) for name, width in acts.items()}
+    D = [normal((T, d), 1e-3) for _, d, _, _ in mats]
+    W = [normal((d, k), 0.02) for _, d, k, _ in mats]
+    P = [torch.empty((k, r), dtype=torch.bfloat16, device=dev) for _, _, k, _ in mats]
+    C = [torch.zeros((d, r), dtype=torch.float32, device=dev) for _, d, _, _ in mats]
+    XP = [torch.empty((mb, r), dtype=torch.bfloat16, device=dev) for _ in mats]
+    ws = rgc.Workspace(dev)
+    torch.cuda.synchronize()
+
+    timers = None  # when set: {op: [(start, end), ...]}
+
+    def timed(op, fn):
+        if timers is None:
+            fn()
+            return
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        timers.setdefault(op, []).append((s, e))
+
+    def one_step(step):
+        for m, (_, d, k, _) in enumerate(mats):
+            timed("sample_projection", lambda: rgc.rgc_sample_projection(wl["kind"], step_seed(step, m), k, r,
+                                                                          out=P[m], workspace=ws))
+            C[m].zero_()
+        for i in range(n_mb):
+            for m, (_, d, k, src) in enumerate(mats):
+                xs = X[src][i * mb:(i + 1) * mb]
+                ds = D[m][i * mb:(i + 1) * mb]
+                timed("project", lambda: rgc.rgc_project(xs, P[m], out=XP[m], workspace=ws))
+                timed("accumulate", lambda: rgc.rgc_accumulate(ds, XP[m], C[m], workspace=ws))
+        for m in range(len(mats)):
+            timed("apply", lambda: rgc.rgc_apply(W[m], C[m], P[m], wl["tau"], step_seed(step, m), workspace=ws))
+
+    for s in range(args.warmup):
+        one_step(s)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps ------------------------------------------
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        one_step(args.warmup + s)
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    tokens_per_s = T / (ms_per_step / 1e3)
+
+    # ---- per-entry-point timing (HIP events on the launch stream) --------------
+    kern = {}
+    if not args.no_kernel_timing:
+        timers = {}
+        torch.cuda.synchronize()
+        for s in range(args.steps):
+            one_step(args.warmup + args.steps + s)
+        torch.cuda.synchronize()
+        durs = {op: [a.elapsed_time(b) * 1e-3 for a, b in ev] for op, ev in timers.items()}
+        timers = None
+        # algorithmic work per launch (bytes and flops), per op, in launch order
+        acc_bytes = sum(2 * mb * d + 2 * mb * r + 8 * d * r for _, d, _, _ in mats) * n_mb
+        acc_flops = sum(2 * mb * d * r for _, d, _, _ in mats) * n_mb
+        prj_bytes = sum(2 * mb * k + 2 * mb * r + 2 * k * r for _, _, k, _ in mats) * n_mb
+        prj_flops = sum(2 * mb * k * r for _, _, k, _ in mats) * n_mb
+        app_bytes = sum(6 * d * k + 8 * d * r + 4 * k * r for _, d, k, _ in mats)
+        smp_bytes = sum(2 * k * r for _, _, k, _ in mats)
+        per_step = {op: sum(v) / args.steps for op, v in durs.items()}
+        kern = {
+            "accumulate": {"s_per_step": per_step["accumulate"], "launches_per_step": n_mb * len(mats),
+                           "avg_us": 1e6 * per_step["accumulate"] / (n_mb * len(mats)),
+                           "GBs": acc_bytes / per_step["accumulate"] / 1e9,
+                           "TFLOPs": acc_flops / per_step["accumulate"] / 1e12},
+            "project": {"s_per_step": per_step["project"], "launches_per_step": n_mb * len(mats),
+                        "avg_us": 1e6 * per_step["project"] / (n_mb * len(mats)),
+                        "GBs": prj_bytes / per_step["project"] / 1e9,
+                        "TFLOPs": prj_flops / per_step["project"] / 1e12},
+            "apply": {"s_per_step": per_step["apply"], "launches_per_step": len(mats),
+                      "avg_us": 1e6 * per_step["apply"] / len(mats),
+                      "GBs": app_bytes / per_step["apply"] / 1e9},
+            "sample_projection": {"s_per_step": per_step["sample_projection"], "launches_per_step": len(mats),
+                                  "avg_us": 1e6 * per_step["sample_projection"] / len(mats),
+                                  "GBs": smp_bytes / per_step["sample_projection"] / 1e9},
+        }
+        for v in kern.values():
+            v["hbm_frac"] = v["GBs"] / HBM_PEAK_GBS
+        kern["accumulate"]["mfma_frac"] = kern["accumulate"]["TFLOPs"] / BF16_PEAK_TFLOPS
+        kern["project"]["mfma_frac"] = kern["project"]["TFLOPs"] / BF16_PEAK_TFLOPS
+
+    # dominant kernel: the accumulate (the metric's named contraction); HBM-bound at r = 64
+    roofline = None
+    if kern:
+        a = kern["accumulate"]
+        roofline = {"kernel": "accumulate_kernel<64>", "bound": "hbm", "achieved": round(a["GBs"], 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(a["hbm_frac"], 4), "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(X, D, W, mats, wl)
+
+    out = {
+        "metric": "sketch-accumulate TFLOP/s + fused-apply HBM GB/s (% roofline), tokens/s/step",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-1.7b-block 7 projections, r=64 QR, 32768 tokens in 8x4096",
+                   "r": r, "tokens_per_step": T, "microbatch": mb, "projection": "qr-gaussian", "tau": wl["tau"]},
+        "sketch_accumulate_TFLOPs": round(kern["accumulate"]["TFLOPs"], 2) if kern else None,
+        "sketch_accumulate_frac_bf16_peak": round(kern["accumulate"]["mfma_frac"], 4) if kern else None,
+        "fused_apply_GBs": round(kern["apply"]["GBs"], 1) if kern else None,
+        "fused_apply_frac_hbm_peak": round(kern["apply"]["hbm_frac"], 4) if kern else None,
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kern.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(X, D, W, mats, wl):
+    """The CPU oracle, untuned, on a bounded sample of the same workload: all 7
+    QR projections, one 4096-token microbatch of project + accumulate for all 7
+    matrices, and all 7 applies; the step time is extrapolated to 8 microbatches."""
+    import numpy as np
+
+    import oracle as orc
+    from rank_randomized_gradient_amd import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    r, mb = wl["r"], wl["microbatch"]
+    n_mb = wl["tokens"] // mb
+    bits = synth.to_numpy_bits
+    xs = {name: bits(x[:mb]) for name, x in X.items()}
+    ds = [bits(d[:mb]) for d in D]
+    ws = [bits(w) for w in W]
+    t0 = time.perf_counter()
+    ps = [orc.qr_projection(step_seed(0, m), k, r) for m, (_, _, k, _) in enumerate(mats)]
+    t1 = time.perf_counter()
+    cs = []
+    for m, (_, d, k, src) in enumerate(mats):
+        c = np.zeros((d, r), np.float32)
+        cs.append(orc.accumulate(c, ds[m], orc.project(xs[src], ps[m])))
+    t2 = time.perf_counter()
+    for m in range(len(mats)):
+        orc.apply_update(ws[m], cs[m], ps[m], wl["tau"], step_seed(0, m))
+    t3 = time.perf_counter()
+    step_s = (t1 - t0) + n_mb * (t2 - t1) + (t3 - t2)
+    return {"value": round(wl["tokens"] / step_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"7 QR projections + 1 of {n_mb} microbatches (project+accumulate, 7 matrices) + 7 applies, "
+                      f"measured {t3 - t0:.1f}s; step time = projections + {n_mb} x microbatch + applies "
+                      f"= {step_s:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

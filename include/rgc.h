@@ -1,0 +1,170 @@
+/*
+ * rgc.h -- C ABI of the randomized low-rank gradient-sketch library (gfx950).
+ *
+ * One linear layer W (d x k, out x in) is trained from a rank-r sketch of its
+ * gradient instead of the dense gradient:
+ *
+ *   1. P  = rgc_sample_projection(seed)      k x r, fixed for one accumulation
+ *   2. XP = rgc_project(X, P)                the layer keeps XP (T x r), not X
+ *   3. C += rgc_accumulate(D, XP)            C = D^T (X P), d x r, fp32
+ *   4. W  = rgc_apply(W, C, P)               W <- SR_bf16(W - tau*||W||*H/||H||),
+ *                                            H = C P^T rebuilt in tiles, never stored
+ *
+ * Sources, by page title and section:
+ *   [RGC]     "Randomized Gradient Compression": "How it works" (C += D^T (X P),
+ *             the saved X P, H = C P^T rebuilt 128 rows at a time, the normalized
+ *             update, bf16 weights with stochastic rounding), footnote 1 (the
+ *             QR-of-Gaussian frame scaled by sqrt(input width / rank)).
+ *   [LoGRA-S] "LoGRA: Scaling LLM Reinforcement Learning with Low-Rank Gradient
+ *             Sketches": Key Contributions item 1 (fp32 sketch S = G A^T, d x r,
+ *             accumulated per microbatch, never forming G).
+ *   [LoGRA-M] "LoGRA: Low-Rank Gradient Sketches": "Why the Sketch Can Be
+ *             Accumulated Without a Full Gradient" (random signs scaled by
+ *             1/sqrt(r)), "Minimal Causal Code" (caller-zeroed fp32 sketch,
+ *             projection regenerated from a seed).
+ *
+ * Conventions for every call:
+ *   - bf16 tensors travel as uint16_t bit patterns; all matrices are row-major.
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library
+ *     allocates no memory, keeps no pointer after a call returns and has no
+ *     mutable global state. Buffers passed to one call must not alias each
+ *     other (except where noted).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *     call only enqueues kernels on it and never synchronizes; results are
+ *     ready when the stream reaches them.
+ *   - Workspaces: device memory of at least the queried size, 256-byte
+ *     aligned, ZERO-FILLED BEFORE ITS FIRST USE. A call may use the first
+ *     RGC_WS_COUNTER_BYTES bytes as completion counters and returns them to
+ *     zero before its last kernel ends, so one zeroed workspace can be reused
+ *     by any later call that is ordered after it on a stream. Calls that run
+ *     concurrently need separate workspaces.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error nothing is launched and no buffer changes. Conditions that are only
+ *     known on the device (a zero sketch, non-finite values) are reported
+ *     through `stats` (rgc_apply).
+ *   - Shape limits: r is a multiple of 16 in [16, 256] (QR projections:
+ *     r <= 128); d and k are multiples of 8; T >= 0 (T = 0 is a no-op); leading
+ *     dimensions are multiples of 8 elements; tensor base pointers are 16-byte
+ *     aligned.
+ */
+#ifndef RGC_H
+#define RGC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RGC_ABI_VERSION 1
+#define RGC_WS_COUNTER_BYTES 4096
+
+typedef enum {
+  RGC_OK = 0,
+  RGC_ERR_NULL = 1,        /* a required pointer is NULL */
+  RGC_ERR_SHAPE = 2,       /* a dimension is negative, r > k, or ld < width */
+  RGC_ERR_UNSUPPORTED = 3, /* r or d/k outside the supported set (see above) */
+  RGC_ERR_ALIGN = 4,       /* a base pointer or leading dimension is misaligned */
+  RGC_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the query */
+  RGC_ERR_HIP = 6          /* a kernel launch failed */
+} rgc_status_t;
+
+typedef enum {
+  /* Entries +-bf16(1/sqrt(r)) from counter-based sign bits [LoGRA-M]. */
+  RGC_PROJ_RADEMACHER = 0,
+  /* sqrt(k/r) * Q, Q the sign-corrected QR factor of a Gaussian k x r matrix,
+   * computed by CholeskyQR2 in fp64 and rounded fp64 -> fp32 -> bf16 [RGC, fn 1]. */
+  RGC_PROJ_QR_GAUSSIAN = 1
+} rgc_proj_kind_t;
+
+int rgc_abi_version(void);
+const char* rgc_status_string(rgc_status_t status);
+
+/* ---- 1. Projection ------------------------------------------------------ */
+
+/* Workspace bytes rgc_sample_projection needs for (kind, k, r); 0 means none. */
+size_t rgc_sample_projection_workspace_size(rgc_proj_kind_t kind, int64_t k, int64_t r);
+
+/* Fill P (k x r bf16, row-major, leading dimension r) from `seed`.
+ * Rademacher: one Philox4x32-10 call (counter (i, j/128, 1, 0), key = seed)
+ *   per row i and block of 128 columns; bit (j % 32) of word ((j / 32) % 4) set
+ *   gives -a, clear gives +a, a = bf16(1/sqrt(r)).
+ * QR-Gaussian: A[i][j] Box-Muller normals from Philox (counter (i, j/4, 2, 0),
+ *   key = seed; columns 4q,4q+1 use words 0,1 and 4q+2,4q+3 use words 2,3;
+ *   u = (w + 1/2) / 2^32; even column rho*cos, odd column rho*sin); then
+ *   Q = A R^-1 with R upper triangular, diag(R) > 0 (CholeskyQR2, fp64);
+ *   P = bf16(fp32(sqrt(k/r) * Q)). Needs a workspace (see the query).
+ * The same (kind, seed, k, r) always gives the same bits, on any device. */
+rgc_status_t rgc_sample_projection(rgc_proj_kind_t kind, uint64_t seed, int64_t k, int64_t r,
+                                   uint16_t* P, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- 2. Projected activations --------------------------------------------- */
+
+/* Workspace bytes rgc_project needs (split-k partial sums). */
+size_t rgc_project_workspace_size(int64_t T, int64_t k, int64_t r);
+
+/* XP = bf16_rne(X P) [RGC, "How it works": the layer keeps X P, not X].
+ * X: T x k bf16, row stride ldx (>= k). P: k x r bf16 (row stride r).
+ * XP: T x r bf16, row stride r. Products of bf16 in fp32 (MFMA), fp32 sums in a
+ * fixed order (deterministic), one rounding to bf16. */
+rgc_status_t rgc_project(const uint16_t* X, int64_t ldx, const uint16_t* P, uint16_t* XP,
+                         int64_t T, int64_t k, int64_t r, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- 3. Sketch accumulation ----------------------------------------------- */
+
+/* Workspace bytes rgc_accumulate needs (split-token partial sums). */
+size_t rgc_accumulate_workspace_size(int64_t T, int64_t d, int64_t r);
+
+/* C += D^T XP over this microbatch's T tokens [RGC, "How it works"; LoGRA-S,
+ * Key Contributions 1]. D: T x d bf16 (row stride ldd >= d) = dL/dY of the
+ * layer's output. XP: T x r bf16 (row stride r) from rgc_project. C: d x r
+ * fp32 (row stride r), read-modify-written; it only adds, so the caller zeroes
+ * C once per update (as the pages' loop does). Products in fp32 on MFMA, token
+ * partial sums reduced in a fixed order (bit-reproducible). */
+rgc_status_t rgc_accumulate(const uint16_t* D, int64_t ldd, const uint16_t* XP, float* C,
+                            int64_t T, int64_t d, int64_t r, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* ---- 4. Normalized update with stochastic rounding ------------------------ */
+
+/* Workspace bytes rgc_apply needs (norm partials and the step scalar). */
+size_t rgc_apply_workspace_size(int64_t d, int64_t k, int64_t r);
+
+/* W <- SR_bf16(W - s * H), H = C P^T, s = fp32(tau * ||W||_F / ||H||_F)
+ * [RGC, "How it works"]. W: d x k bf16 (row stride ldw >= k), updated in place;
+ * C: d x r fp32; P: k x r bf16. H is rebuilt tile by tile in registers (MFMA,
+ * C split into two bf16 terms) and never written to memory. The pre-rounding
+ * value is v = fp32(w - fp32(s*h)) (no fused multiply-add); stochastic
+ * rounding adds 16 random bits to v's low half and keeps the high half, the
+ * bits coming from Philox4x32-10 (counter (j/8, i, 3, 0), key = seed; column j
+ * uses word (j%8)/2, low half for even j). When ||H|| = 0 or s is not finite
+ * the update is skipped: W is left bit-identical and flag = 1.
+ * stats: NULL or device float[4] receiving {||W||, ||H||, s, flag}. */
+rgc_status_t rgc_apply(uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d,
+                       int64_t k, int64_t r, float tau, uint64_t seed, float* stats, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* ---- Test hooks (same library; used by the parity tests) ----------------- */
+
+/* out[4*i .. 4*i+3] = Philox4x32-10(counter ctr[4*i .. 4*i+3], key = seed) for
+ * i < n. ctr and out: device uint32 arrays of 4*n words. */
+rgc_status_t rgc_test_philox(uint64_t seed, int64_t n, const uint32_t* ctr, uint32_t* out,
+                             void* stream);
+
+/* out[i][j] = SR(v[i][j]) with the rounding bits of weight element
+ * (row0 + i, col0 + j) under `seed`, exactly as rgc_apply draws them.
+ * v: rows x cols fp32 (row stride ld); out: rows x cols bf16 (row stride ld). */
+rgc_status_t rgc_test_stochastic_round(const float* v, uint16_t* out, int64_t rows, int64_t cols,
+                                       int64_t ld, int64_t row0, int64_t col0, uint64_t seed,
+                                       void* stream);
+
+/* H = C P^T in fp32 through the apply kernel's tile code (d x k, row stride k). */
+rgc_status_t rgc_test_reconstruct(const float* C, const uint16_t* P, float* H, int64_t d,
+                                  int64_t k, int64_t r, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RGC_H */

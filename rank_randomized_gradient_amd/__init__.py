@@ -1,0 +1,20 @@
+"""Randomized low-rank gradient sketching on MI355X (gfx950).
+
+The hot path of a linear layer W (d x k) trained from a rank-r sketch of its
+gradient, as hand-written HIP kernels behind the C ABI in include/rgc.h:
+projection sampling, XP = X P, C += D^T (X P), and the normalized update
+with stochastic rounding to bf16. `rgc` is the thin ctypes binding.
+"""
+from .rgc import (  # noqa: F401
+    RgcError,
+    Workspace,
+    abi_version,
+    load_library,
+    rgc_accumulate,
+    rgc_apply,
+    rgc_project,
+    rgc_sample_projection,
+    rgc_test_philox,
+    rgc_test_reconstruct,
+    rgc_test_stochastic_round,
+)

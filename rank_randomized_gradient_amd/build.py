@@ -1,0 +1,64 @@
+"""Builds librgc.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG_DIR, "csrc")
+BUILD_DIR = os.path.join(PKG_DIR, "_build")
+LIB_PATH = os.path.join(PKG_DIR, "librgc.so")
+SOURCES = ["rgc_sketch.hip", "rgc_apply.hip", "rgc_projection.hip", "rgc_abi.cpp"]
+
+# -ffp-contract=off: the update's pre-rounding value w - s*h and the Box-Muller
+# formulas are two separately rounded operations, never fused.
+# -packed-fp32-ops off: no packed fp32 instructions are generated.
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    cand = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(cand) and shutil.which(cand) is None:
+        raise RuntimeError("hipcc not found; the HIP library cannot be built")
+    return cand
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cc = hipcc()
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmd = [cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for src, p in procs:
+        out, _ = p.communicate()
+        lines = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln]
+        if p.returncode != 0:
+            failed.append(src)
+            sys.stderr.write("\n".join(lines) + "\n")
+        elif verbose and lines:
+            print("\n".join(lines))
+    if failed:
+        raise RuntimeError(f"hipcc failed on {failed}")
+    tmp = LIB_PATH + ".tmp"
+    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,139 @@
+// Device helpers shared by the gfx950 kernels of the sketch library:
+// the Philox4x32-10 counter generator, bf16 bit helpers, the bf16 MFMA
+// wrapper and the register transposes that feed token-major operands to it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rgc {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
+
+// Streaming loads for data read exactly once (nontemporal hint).
+__device__ __forceinline__ u32x4v_t load_stream_16b(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4v_t*>(p));
+}
+__device__ __forceinline__ u32x2v_t load_stream_8b(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2v_t*>(p));
+}
+
+struct u32x4 {
+  uint32_t x, y, z, w;
+};
+
+// Stream tags (counter word 2): projection signs, Gaussian draws, rounding bits.
+constexpr uint32_t kTagRademacher = 1;
+constexpr uint32_t kTagGaussian = 2;
+constexpr uint32_t kTagRounding = 3;
+
+// Philox4x32-10 (Salmon et al., SC'11): ten rounds, each multiplying counter
+// words 0 and 2 by the two round constants (full 64-bit products), mixing the
+// halves with words 1 and 3 and the key, and bumping the key by the Weyl
+// increments afterwards. The key is wave-uniform, so its schedule lives in
+// scalar registers.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    u32x4 n;
+    n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+    n.y = (uint32_t)p1;
+    n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+    n.w = (uint32_t)p0;
+    c = n;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN becomes a quiet NaN keeping its sign.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (b >> 16) | 0x40u;
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Stochastic rounding fp32 -> bf16 with 16 random bits: the random integer is
+// added to the dropped low half, so the kept half rounds up with probability
+// (low half) / 2^16. Infinities are kept, NaN becomes a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_sr(float f, uint32_t r16) {
+  const uint32_t b = __float_as_uint(f);
+  if ((b & 0x7F800000u) == 0x7F800000u) return (b & 0x007FFFFFu) ? ((b >> 16) | 0x40u) : (b >> 16);
+  return (b + r16) >> 16;
+}
+
+// Two bf16 packed in a dword, element 0 in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(uint32_t lo, uint32_t hi) { return (lo & 0xFFFFu) | (hi << 16); }
+
+// v_perm_b32 selectors: low halves of (a, b) -> (a.lo, b.lo); high halves likewise.
+constexpr uint32_t kSelLo = 0x05040100u;
+constexpr uint32_t kSelHi = 0x07060302u;
+// Returns a dword whose low half is the selected half of `first` and whose
+// high half is the selected half of `second`.
+__device__ __forceinline__ uint32_t pick_halves(uint32_t first, uint32_t second, uint32_t sel) {
+  return __builtin_amdgcn_perm(second, first, sel);
+}
+
+// D = A B + C for one 16x16 output tile with K = 32 (bf16 in, fp32 out).
+// Lane l supplies A row (l % 16) and B column (l % 16), each with the eight
+// consecutive K values 8*(l/16) .. 8*(l/16)+7 packed as four bf16 pairs;
+// it receives D rows 4*(l/16) .. 4*(l/16)+3 of column (l % 16).
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const uint32_t (&a)[4], const uint32_t (&b)[4], f32x4_t c) {
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  u4v av = {a[0], a[1], a[2], a[3]};
+  u4v bv = {b[0], b[1], b[2], b[3]};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv),
+                                                 c, 0, 0, 0);
+}
+
+// Register transpose for token-major operands. A lane has read, for eight
+// consecutive tokens j = 0..7, CPL consecutive bf16 columns of one row each
+// (rows[j] holds them: one dword per two columns). For column c it returns the
+// eight tokens of that column packed as four bf16 pairs (token 2p in the low
+// half of dword p): the MFMA operand of "column c".
+template <int CPL>
+__device__ __forceinline__ void transpose_8xcpl(const uint32_t (&rows)[8][(CPL + 1) / 2], int c, uint32_t (&out)[4]) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    if constexpr (CPL == 1) {
+      out[p] = pack_bf16x2(rows[2 * p][0], rows[2 * p + 1][0]);
+    } else {
+      const uint32_t sel = (c & 1) ? kSelHi : kSelLo;
+      out[p] = pick_halves(rows[2 * p][c >> 1], rows[2 * p + 1][c >> 1], sel);
+    }
+  }
+}
+
+// Cross-workgroup completion: every wave publishes its earlier global stores
+// at device scope (release: they reach memory visible to all XCDs), one
+// thread takes a ticket, and only the workgroup that draws the last ticket
+// acquires (invalidates its stale cached lines) and goes on to read the
+// others' results. No workgroup ever waits for another.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t last_ticket) {
+  __shared__ uint32_t ticket;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const bool last = ticket == last_ticket;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
+// Wave-wide sum of a double (64 lanes) with cross-lane shuffles.
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace rgc

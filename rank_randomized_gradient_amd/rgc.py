@@ -1,0 +1,252 @@
+"""Thin Python binding of librgc (the gfx950 sketch library), through ctypes.
+
+Argument marshalling only: every step runs in the HIP kernels of librgc.so.
+torch supplies device memory and the current HIP stream. There is no CPU
+fallback: if the library is missing or a GPU is absent, calls raise.
+
+Names mirror the C ABI in include/rgc.h:
+  rgc_sample_projection(kind, seed, k, r)  -> P (k x r bf16)
+  rgc_project(X, P)                         -> XP = bf16(X P)
+  rgc_accumulate(D, XP, C)                  C += D^T XP (in place)
+  rgc_apply(W, C, P, tau, seed)             W <- SR(W - tau ||W|| H / ||H||) (in place)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "librgc.so")
+
+RGC_PROJ_RADEMACHER = 0
+RGC_PROJ_QR_GAUSSIAN = 1
+_KINDS = {"rademacher": RGC_PROJ_RADEMACHER, "qr": RGC_PROJ_QR_GAUSSIAN}
+
+_i64 = ctypes.c_int64
+_u64 = ctypes.c_uint64
+_sz = ctypes.c_size_t
+_vp = ctypes.c_void_p
+_f32 = ctypes.c_float
+
+# (name, restype, argtypes) for every exported function of include/rgc.h
+SIGNATURES = {
+    "rgc_abi_version": (ctypes.c_int, []),
+    "rgc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "rgc_sample_projection_workspace_size": (_sz, [ctypes.c_int, _i64, _i64]),
+    "rgc_sample_projection": (ctypes.c_int, [ctypes.c_int, _u64, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "rgc_project_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "rgc_project": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "rgc_accumulate_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "rgc_accumulate": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "rgc_apply_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "rgc_apply": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _f32, _u64, _vp, _vp, _sz, _vp]),
+    "rgc_test_philox": (ctypes.c_int, [_u64, _i64, _vp, _vp, _vp]),
+    "rgc_test_stochastic_round": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _u64, _vp]),
+    "rgc_test_reconstruct": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+}
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+class RgcError(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads librgc.so and declares its signatures (no GPU needed)."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RgcError(f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def abi_version() -> int:
+    return load_library().rgc_abi_version()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load_library().rgc_status_string(status).decode()
+        raise RgcError(f"librgc status {status}: {msg}")
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need_gpu(*tensors: torch.Tensor) -> torch.device:
+    dev = tensors[0].device
+    if dev.type != "cuda":
+        raise RgcError("librgc runs on the GPU only: tensors must be on a cuda (HIP) device")
+    for t in tensors:
+        if t.device != dev:
+            raise RgcError("all tensors must be on the same device")
+    return dev
+
+
+def _rows(t: torch.Tensor, dtype: torch.dtype, name: str) -> int:
+    """Checks a row-major 2-D tensor (unit column stride) and returns its row stride."""
+    if t.dtype != dtype:
+        raise RgcError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise RgcError(f"{name} must be 2-D with unit column stride")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+def _dense(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if t.dtype != dtype or not t.is_contiguous():
+        raise RgcError(f"{name} must be a contiguous {dtype} tensor")
+
+
+class Workspace:
+    """Zero-initialised device scratch for one stream, grown on demand.
+
+    The library leaves the completion counters at the start of a workspace at
+    zero after each call, so one buffer serves every call ordered on a stream.
+    """
+
+    def __init__(self, device: torch.device):
+        self.device = device
+        self.buf = torch.zeros(0, dtype=torch.uint8, device=device)
+
+    def get(self, nbytes: int) -> tuple[ctypes.c_void_p, int]:
+        if nbytes == 0:
+            return ctypes.c_void_p(self.buf.data_ptr() if self.buf.numel() else 0), self.buf.numel()
+        if self.buf.numel() < nbytes:
+            self.buf = torch.zeros(((nbytes + 4095) // 4096) * 4096, dtype=torch.uint8, device=self.device)
+        return ctypes.c_void_p(self.buf.data_ptr()), self.buf.numel()
+
+
+_workspaces: dict = {}
+
+
+def default_workspace(dev: torch.device) -> Workspace:
+    key = (dev.index if dev.index is not None else torch.cuda.current_device(), torch.cuda.current_stream(dev).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = Workspace(torch.device("cuda", key[0]))
+        _workspaces[key] = ws
+    return ws
+
+
+def rgc_sample_projection(kind: str, seed: int, k: int, r: int, out: torch.Tensor | None = None,
+                          device=None, workspace: Workspace | None = None) -> torch.Tensor:
+    lib = load_library()
+    if out is None:
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        out = torch.empty((k, r), dtype=torch.bfloat16, device=dev)
+    dev = _need_gpu(out)
+    _dense(out, torch.bfloat16, "P")
+    kid = _KINDS[kind]
+    ws = workspace or default_workspace(dev)
+    wp, wn = ws.get(lib.rgc_sample_projection_workspace_size(kid, k, r))
+    _check(lib.rgc_sample_projection(kid, seed & 0xFFFFFFFFFFFFFFFF, k, r, out.data_ptr(), wp, wn, _stream(dev)))
+    return out
+
+
+def rgc_project(X: torch.Tensor, P: torch.Tensor, out: torch.Tensor | None = None,
+                workspace: Workspace | None = None) -> torch.Tensor:
+    lib = load_library()
+    dev = _need_gpu(X, P)
+    ldx = _rows(X, torch.bfloat16, "X")
+    _dense(P, torch.bfloat16, "P")
+    T, k = X.shape
+    r = P.shape[1]
+    if P.shape[0] != k:
+        raise RgcError("P must be k x r with k = X.shape[1]")
+    if out is None:
+        out = torch.empty((T, r), dtype=torch.bfloat16, device=dev)
+    _dense(out, torch.bfloat16, "XP")
+    ws = workspace or default_workspace(dev)
+    wp, wn = ws.get(lib.rgc_project_workspace_size(T, k, r))
+    _check(lib.rgc_project(X.data_ptr(), ldx, P.data_ptr(), out.data_ptr(), T, k, r, wp, wn, _stream(dev)))
+    return out
+
+
+def rgc_accumulate(D: torch.Tensor, XP: torch.Tensor, C: torch.Tensor, workspace: Workspace | None = None) -> torch.Tensor:
+    lib = load_library()
+    dev = _need_gpu(D, XP, C)
+    ldd = _rows(D, torch.bfloat16, "D")
+    _dense(XP, torch.bfloat16, "XP")
+    _dense(C, torch.float32, "C")
+    T, d = D.shape
+    r = XP.shape[1]
+    if XP.shape[0] != T or tuple(C.shape) != (d, r):
+        raise RgcError("shapes must be D: T x d, XP: T x r, C: d x r")
+    ws = workspace or default_workspace(dev)
+    wp, wn = ws.get(lib.rgc_accumulate_workspace_size(T, d, r))
+    _check(lib.rgc_accumulate(D.data_ptr(), ldd, XP.data_ptr(), C.data_ptr(), T, d, r, wp, wn, _stream(dev)))
+    return C
+
+
+def rgc_apply(W: torch.Tensor, C: torch.Tensor, P: torch.Tensor, tau: float, seed: int,
+              stats: torch.Tensor | None = None, workspace: Workspace | None = None) -> torch.Tensor:
+    lib = load_library()
+    dev = _need_gpu(W, C, P)
+    ldw = _rows(W, torch.bfloat16, "W")
+    _dense(C, torch.float32, "C")
+    _dense(P, torch.bfloat16, "P")
+    d, k = W.shape
+    r = C.shape[1]
+    if tuple(C.shape) != (d, r) or tuple(P.shape) != (k, r):
+        raise RgcError("shapes must be W: d x k, C: d x r, P: k x r")
+    sp = None
+    if stats is not None:
+        _need_gpu(stats)
+        _dense(stats, torch.float32, "stats")
+        if stats.numel() < 4:
+            raise RgcError("stats needs 4 floats")
+        sp = stats.data_ptr()
+    ws = workspace or default_workspace(dev)
+    wp, wn = ws.get(lib.rgc_apply_workspace_size(d, k, r))
+    _check(lib.rgc_apply(W.data_ptr(), ldw, C.data_ptr(), P.data_ptr(), d, k, r, float(tau),
+                         seed & 0xFFFFFFFFFFFFFFFF, sp, wp, wn, _stream(dev)))
+    return W
+
+
+# ---- test hooks -------------------------------------------------------------
+
+def rgc_test_philox(seed: int, ctr: torch.Tensor) -> torch.Tensor:
+    """ctr: (n, 4) int32 tensor of counter words (bit patterns); returns (n, 4) int32."""
+    lib = load_library()
+    dev = _need_gpu(ctr)
+    _dense(ctr, torch.int32, "ctr")
+    out = torch.empty_like(ctr)
+    _check(lib.rgc_test_philox(seed & 0xFFFFFFFFFFFFFFFF, ctr.shape[0], ctr.data_ptr(), out.data_ptr(), _stream(dev)))
+    return out
+
+
+def rgc_test_stochastic_round(v: torch.Tensor, seed: int, row0: int = 0, col0: int = 0) -> torch.Tensor:
+    lib = load_library()
+    dev = _need_gpu(v)
+    _dense(v, torch.float32, "v")
+    rows, cols = v.shape
+    out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
+    _check(lib.rgc_test_stochastic_round(v.data_ptr(), out.data_ptr(), rows, cols, cols, row0, col0,
+                                         seed & 0xFFFFFFFFFFFFFFFF, _stream(dev)))
+    return out
+
+
+def rgc_test_reconstruct(C: torch.Tensor, P: torch.Tensor) -> torch.Tensor:
+    lib = load_library()
+    dev = _need_gpu(C, P)
+    _dense(C, torch.float32, "C")
+    _dense(P, torch.bfloat16, "P")
+    d, r = C.shape
+    k = P.shape[0]
+    H = torch.empty((d, k), dtype=torch.float32, device=dev)
+    _check(lib.rgc_test_reconstruct(C.data_ptr(), P.data_ptr(), H.data_ptr(), d, k, r, _stream(dev)))
+    return H

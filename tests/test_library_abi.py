@@ -1,0 +1,134 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before launching anything (CPU only: no call here ever
+reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rank_randomized_gradient_amd as rgc_pkg
+from rank_randomized_gradient_amd import rgc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rgc.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+FAKE = 0x10000  # an aligned address that is never dereferenced: every call below fails validation first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rgc_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rgc.LIB_PATH):
+        pytest.fail("librgc.so is not built (run __graft_entry__.build())")
+    return rgc.load_library()
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(rgc.SIGNATURES), set(names) ^ set(rgc.SIGNATURES)
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define RGC_ABI_VERSION (\d+)", open(HEADER).read())
+    assert rgc_pkg.abi_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.rgc_status_string(s)
+    assert b"unknown" in lib.rgc_status_string(99)
+
+
+def test_workspace_queries(lib):
+    assert lib.rgc_sample_projection_workspace_size(0, 2048, 64) == 0
+    qr = lib.rgc_sample_projection_workspace_size(1, 2048, 64)
+    assert qr >= 2 * 2048 * 64 * 8
+    assert lib.rgc_sample_projection_workspace_size(1, 2048, 256) == 0  # QR limited to r <= 128
+    assert lib.rgc_accumulate_workspace_size(4096, 2048, 64) >= 0
+    assert lib.rgc_apply_workspace_size(2048, 2048, 64) >= 4096
+    assert lib.rgc_apply_workspace_size(2048, 2048, 40) == 0  # unsupported rank
+
+
+def test_project_validation(lib):
+    s = None
+    # shape errors
+    assert lib.rgc_project(FAKE, 63, FAKE, FAKE, 16, 64, 16, None, 0, s) == SHAPE  # ldx < k
+    assert lib.rgc_project(FAKE, 64, FAKE, FAKE, -1, 64, 16, None, 0, s) == SHAPE
+    assert lib.rgc_project(FAKE, 64, FAKE, FAKE, 16, 8, 16, None, 0, s) == SHAPE  # r > k
+    # unsupported
+    assert lib.rgc_project(FAKE, 64, FAKE, FAKE, 16, 64, 24, None, 0, s) == UNSUP
+    assert lib.rgc_project(FAKE, 68, FAKE, FAKE, 16, 68, 16, None, 0, s) == UNSUP  # k % 8
+    # T = 0 is a no-op
+    assert lib.rgc_project(None, 64, None, None, 0, 64, 16, None, 0, s) == OK
+    assert lib.rgc_project(None, 64, FAKE, FAKE, 16, 64, 16, None, 0, s) == NULL
+    assert lib.rgc_project(FAKE + 2, 64, FAKE, FAKE, 16, 64, 16, None, 0, s) == ALIGN
+    assert lib.rgc_project(FAKE, 68, FAKE, FAKE, 16, 64, 16, None, 0, s) == ALIGN  # ldx % 8
+    need = lib.rgc_project_workspace_size(4096, 2048, 64)
+    assert need > 0
+    assert lib.rgc_project(FAKE, 2048, FAKE, FAKE, 4096, 2048, 64, None, 0, s) == WS
+    assert lib.rgc_project(FAKE, 2048, FAKE, FAKE, 4096, 2048, 64, FAKE, need - 1, s) == WS
+    assert lib.rgc_project(FAKE, 2048, FAKE, FAKE, 4096, 2048, 64, FAKE + 16, need, s) == ALIGN
+
+
+def test_accumulate_validation(lib):
+    s = None
+    assert lib.rgc_accumulate(FAKE, 255, FAKE, FAKE, 16, 256, 16, None, 0, s) == SHAPE
+    assert lib.rgc_accumulate(FAKE, 256, FAKE, FAKE, 16, 256, 20, None, 0, s) == UNSUP
+    assert lib.rgc_accumulate(FAKE, 260, FAKE, FAKE, 16, 260, 16, None, 0, s) == UNSUP
+    assert lib.rgc_accumulate(None, 256, None, None, 0, 256, 16, None, 0, s) == OK
+    assert lib.rgc_accumulate(FAKE, 256, None, FAKE, 16, 256, 16, None, 0, s) == NULL
+    assert lib.rgc_accumulate(FAKE, 256, FAKE, FAKE + 4, 16, 256, 16, None, 0, s) == ALIGN
+    need = lib.rgc_accumulate_workspace_size(4096, 2048, 64)
+    assert need > 0
+    assert lib.rgc_accumulate(FAKE, 2048, FAKE, FAKE, 4096, 2048, 64, FAKE, need - 4, s) == WS
+    assert lib.rgc_accumulate(FAKE, 1 << 20, FAKE, FAKE, 4096, 1 << 20, 64, FAKE, need, s) == UNSUP  # d > limit
+
+
+def test_apply_validation(lib):
+    s = None
+    f = ctypes.c_float(1e-3)
+    assert lib.rgc_apply(FAKE, 255, FAKE, FAKE, 64, 256, 16, f, 0, None, FAKE, 1 << 20, s) == SHAPE
+    assert lib.rgc_apply(FAKE, 256, FAKE, FAKE, 64, 256, 272, f, 0, None, FAKE, 1 << 20, s) == SHAPE  # r > k
+    assert lib.rgc_apply(FAKE, 256, FAKE, FAKE, 60, 256, 16, f, 0, None, FAKE, 1 << 20, s) == UNSUP
+    assert lib.rgc_apply(FAKE, 256, None, FAKE, 64, 256, 16, f, 0, None, FAKE, 1 << 20, s) == NULL
+    assert lib.rgc_apply(FAKE, 256, FAKE, FAKE, 64, 256, 16, f, 0, FAKE + 2, FAKE, 1 << 20, s) == ALIGN
+    assert lib.rgc_apply(FAKE, 256, FAKE, FAKE, 64, 256, 16, f, 0, None, None, 0, s) == WS
+    assert lib.rgc_apply(FAKE, 256, FAKE, FAKE, 64, 256, 16, f, 0, None, FAKE + 64, 1 << 20, s) == ALIGN
+
+
+def test_projection_validation(lib):
+    s = None
+    assert lib.rgc_sample_projection(0, 1, 64, 128, FAKE, None, 0, s) == SHAPE  # r > k
+    assert lib.rgc_sample_projection(0, 1, 64, 24, FAKE, None, 0, s) == UNSUP
+    assert lib.rgc_sample_projection(1, 1, 1024, 256, FAKE, None, 0, s) == UNSUP  # QR r > 128
+    assert lib.rgc_sample_projection(7, 1, 1024, 64, FAKE, None, 0, s) == UNSUP
+    assert lib.rgc_sample_projection(0, 1, 1024, 64, None, None, 0, s) == NULL
+    assert lib.rgc_sample_projection(1, 1, 1024, 64, FAKE, None, 0, s) == WS
+    assert lib.rgc_sample_projection(0, 1, 1024, 64, FAKE + 8, None, 0, s) == ALIGN
+
+
+def test_test_hooks_validation(lib):
+    s = None
+    assert lib.rgc_test_philox(0, -1, FAKE, FAKE, s) == SHAPE
+    assert lib.rgc_test_philox(0, 0, None, None, s) == OK
+    assert lib.rgc_test_stochastic_round(FAKE, FAKE, 4, 8, 7, 0, 0, 0, s) == SHAPE
+    assert lib.rgc_test_reconstruct(FAKE, FAKE, FAKE, 64, 256, 24, s) == UNSUP
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    x = torch.zeros(16, 64, dtype=torch.bfloat16)
+    p = torch.zeros(64, 16, dtype=torch.bfloat16)
+    with pytest.raises(rgc.RgcError):
+        rgc.rgc_project(x, p)
