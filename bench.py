@@ -5,8 +5,8 @@ block (q 2048->2048, k and v 2048->1024, o 2048->2048, gate and up
 2048->6144, down 6144->2048; W is out x in), rank 64, QR-of-Gaussian
 projections redrawn every step, 32768 tokens in 8 microbatches of 4096:
 
-  7 x rgc_sample_projection (QR)
-  8 x 7 x (rgc_project + rgc_accumulate)
+  rgc_sample_projections (QR, the 7 matrices in one batched call)
+  8 x (rgc_project_batch + rgc_accumulate_batch), each covering the 7 matrices
   7 x rgc_apply (tau = 1e-3)
 
 Inputs are synthetic and resident in HBM before timing: X ~ N(0,1) (shared by
@@ -85,31 +85,29 @@ def main():
     ws = rgc.Workspace(dev)
     torch.cuda.synchronize()
 
-    timers = None  # when set: {op: [(start, end), ...]}
+    def sample_all(step):
+        # all projections of the block in one batched call (same bits as one call per matrix)
+        rgc.rgc_sample_projections(wl["kind"], [step_seed(step, m) for m in range(len(mats))], P, workspace=ws)
 
-    def timed(op, fn):
-        if timers is None:
-            fn()
-            return
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        fn()
-        e.record()
-        timers.setdefault(op, []).append((s, e))
+    def project_mb(i):
+        # the 7 projections of microbatch i in one launch (q/k/v and gate/up share their X)
+        rgc.rgc_project_batch([X[src][i * mb:(i + 1) * mb] for _, _, _, src in mats], P, outs=XP, workspace=ws)
+
+    def accumulate_mb(i):
+        rgc.rgc_accumulate_batch([D[m][i * mb:(i + 1) * mb] for m in range(len(mats))], XP, C, workspace=ws)
+
+    def apply_one(step, m):
+        rgc.rgc_apply(W[m], C[m], P[m], wl["tau"], step_seed(step, m), workspace=ws)
 
     def one_step(step):
-        for m, (_, d, k, _) in enumerate(mats):
-            timed("sample_projection", lambda: rgc.rgc_sample_projection(wl["kind"], step_seed(step, m), k, r,
-                                                                          out=P[m], workspace=ws))
+        sample_all(step)
+        for m in range(len(mats)):
             C[m].zero_()
         for i in range(n_mb):
-            for m, (_, d, k, src) in enumerate(mats):
-                xs = X[src][i * mb:(i + 1) * mb]
-                ds = D[m][i * mb:(i + 1) * mb]
-                timed("project", lambda: rgc.rgc_project(xs, P[m], out=XP[m], workspace=ws))
-                timed("accumulate", lambda: rgc.rgc_accumulate(ds, XP[m], C[m], workspace=ws))
+            project_mb(i)
+            accumulate_mb(i)
         for m in range(len(mats)):
-            timed("apply", lambda: rgc.rgc_apply(W[m], C[m], P[m], wl["tau"], step_seed(step, m), workspace=ws))
+            apply_one(step, m)
 
     for s in range(args.warmup):
         one_step(s)
@@ -126,38 +124,49 @@ def main():
     ms_per_step = start.elapsed_time(end) / args.steps
     tokens_per_s = T / (ms_per_step / 1e3)
 
-    # ---- per-entry-point timing (HIP events on the launch stream) --------------
+    # ---- per-entry-point timing ---------------------------------------------------
+    # HIP events on the launch stream around K repetitions of one step's calls of
+    # a single entry point, issued back to back (an event pair around every
+    # microsecond-scale launch would time the event packets, not the kernels).
     kern = {}
     if not args.no_kernel_timing:
-        timers = {}
-        torch.cuda.synchronize()
-        for s in range(args.steps):
-            one_step(args.warmup + args.steps + s)
-        torch.cuda.synchronize()
-        durs = {op: [a.elapsed_time(b) * 1e-3 for a, b in ev] for op, ev in timers.items()}
-        timers = None
-        # algorithmic work per launch (bytes and flops), per op, in launch order
+        def time_op(fn):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for s in range(args.steps):
+                fn(s)
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e-3 / args.steps  # seconds per step
+
+        per_step = {
+            "sample_projection": time_op(lambda s: sample_all(s)),
+            "project": time_op(lambda s: [project_mb(i) for i in range(n_mb)]),
+            "accumulate": time_op(lambda s: [accumulate_mb(i) for i in range(n_mb)]),
+            "apply": time_op(lambda s: [apply_one(s, m) for m in range(len(mats))]),
+        }
+        # algorithmic work per step (bytes and flops), per entry point
         acc_bytes = sum(2 * mb * d + 2 * mb * r + 8 * d * r for _, d, _, _ in mats) * n_mb
         acc_flops = sum(2 * mb * d * r for _, d, _, _ in mats) * n_mb
         prj_bytes = sum(2 * mb * k + 2 * mb * r + 2 * k * r for _, _, k, _ in mats) * n_mb
         prj_flops = sum(2 * mb * k * r for _, _, k, _ in mats) * n_mb
         app_bytes = sum(6 * d * k + 8 * d * r + 4 * k * r for _, d, k, _ in mats)
         smp_bytes = sum(2 * k * r for _, _, k, _ in mats)
-        per_step = {op: sum(v) / args.steps for op, v in durs.items()}
         kern = {
-            "accumulate": {"s_per_step": per_step["accumulate"], "launches_per_step": n_mb * len(mats),
-                           "avg_us": 1e6 * per_step["accumulate"] / (n_mb * len(mats)),
+            "accumulate": {"s_per_step": per_step["accumulate"], "launches_per_step": n_mb,
+                           "avg_us": 1e6 * per_step["accumulate"] / n_mb,
                            "GBs": acc_bytes / per_step["accumulate"] / 1e9,
                            "TFLOPs": acc_flops / per_step["accumulate"] / 1e12},
-            "project": {"s_per_step": per_step["project"], "launches_per_step": n_mb * len(mats),
-                        "avg_us": 1e6 * per_step["project"] / (n_mb * len(mats)),
+            "project": {"s_per_step": per_step["project"], "launches_per_step": n_mb,
+                        "avg_us": 1e6 * per_step["project"] / n_mb,
                         "GBs": prj_bytes / per_step["project"] / 1e9,
                         "TFLOPs": prj_flops / per_step["project"] / 1e12},
             "apply": {"s_per_step": per_step["apply"], "launches_per_step": len(mats),
                       "avg_us": 1e6 * per_step["apply"] / len(mats),
                       "GBs": app_bytes / per_step["apply"] / 1e9},
-            "sample_projection": {"s_per_step": per_step["sample_projection"], "launches_per_step": len(mats),
-                                  "avg_us": 1e6 * per_step["sample_projection"] / len(mats),
+            "sample_projection": {"s_per_step": per_step["sample_projection"], "launches_per_step": 1,
+                                  "avg_us": 1e6 * per_step["sample_projection"],
                                   "GBs": smp_bytes / per_step["sample_projection"] / 1e9},
         }
         for v in kern.values():

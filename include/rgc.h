@@ -32,20 +32,19 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
  *     call only enqueues kernels on it and never synchronizes; results are
  *     ready when the stream reaches them.
- *   - Workspaces: device memory of at least the queried size, 256-byte
- *     aligned, ZERO-FILLED BEFORE ITS FIRST USE. A call may use the first
- *     RGC_WS_COUNTER_BYTES bytes as completion counters and returns them to
- *     zero before its last kernel ends, so one zeroed workspace can be reused
- *     by any later call that is ordered after it on a stream. Calls that run
- *     concurrently need separate workspaces.
+ *   - Workspaces: device scratch of at least the queried size (0 means none
+ *     is needed), 256-byte aligned, owned by the caller. Its contents need no
+ *     initialisation and are dead after the call's kernels complete, so one
+ *     workspace can serve any sequence of calls ordered on a stream; calls
+ *     that may run concurrently need separate workspaces.
  *   - Arguments are validated on the host before anything is enqueued; on any
  *     error nothing is launched and no buffer changes. Conditions that are only
  *     known on the device (a zero sketch, non-finite values) are reported
  *     through `stats` (rgc_apply).
- *   - Shape limits: r is a multiple of 16 in [16, 256] (QR projections:
- *     r <= 128); d and k are multiples of 8; T >= 0 (T = 0 is a no-op); leading
- *     dimensions are multiples of 8 elements; tensor base pointers are 16-byte
- *     aligned.
+ *   - Shape limits: r is one of 16, 32, 48, 64, 128, 192, 256 (QR
+ *     projections: r <= 128); d and k are multiples of 8; T >= 0 (T = 0 is a
+ *     no-op); T and d at most 65536 per call; leading dimensions are
+ *     multiples of 8 elements; tensor base pointers are 16-byte aligned.
  */
 #ifndef RGC_H
 #define RGC_H
@@ -58,7 +57,6 @@ extern "C" {
 #endif
 
 #define RGC_ABI_VERSION 1
-#define RGC_WS_COUNTER_BYTES 4096
 
 typedef enum {
   RGC_OK = 0,
@@ -99,6 +97,16 @@ size_t rgc_sample_projection_workspace_size(rgc_proj_kind_t kind, int64_t k, int
 rgc_status_t rgc_sample_projection(rgc_proj_kind_t kind, uint64_t seed, int64_t k, int64_t r,
                                    uint16_t* P, void* ws, size_t ws_bytes, void* stream);
 
+/* Batched form for the projections of several matrices with the same rank
+ * (e.g. all projections of one transformer block): P[m] is filled exactly as
+ * rgc_sample_projection(kind, seeds[m], ks[m], r, P[m], ...) would fill it,
+ * but each step of the QR pipeline is one launch for the whole batch.
+ * seeds, ks and Ps are HOST arrays of n entries (n <= 16); the P[m] are
+ * device pointers. The workspace query takes the same ks. */
+size_t rgc_sample_projections_workspace_size(rgc_proj_kind_t kind, int64_t n, const int64_t* ks, int64_t r);
+rgc_status_t rgc_sample_projections(rgc_proj_kind_t kind, int64_t n, const uint64_t* seeds, const int64_t* ks,
+                                    int64_t r, uint16_t* const* Ps, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- 2. Projected activations --------------------------------------------- */
 
 /* Workspace bytes rgc_project needs (split-k partial sums). */
@@ -110,6 +118,17 @@ size_t rgc_project_workspace_size(int64_t T, int64_t k, int64_t r);
  * fixed order (deterministic), one rounding to bf16. */
 rgc_status_t rgc_project(const uint16_t* X, int64_t ldx, const uint16_t* P, uint16_t* XP,
                          int64_t T, int64_t k, int64_t r, void* ws, size_t ws_bytes, void* stream);
+
+/* Batched form: n independent projections (n <= 16, one rank r, one token
+ * count T) in one launch, e.g. all projections of a transformer block for one
+ * microbatch (items may share an X, which then streams from cache). Item m
+ * computes XPs[m] = bf16(Xs[m] Ps[m]) with X of width ks[m] and row stride
+ * ldxs[m], exactly as rgc_project does (same rounding; the fp32 summation
+ * order may differ). Xs, ldxs, ks, Ps, XPs are HOST arrays of n entries. */
+size_t rgc_project_batch_workspace_size(int64_t n, const int64_t* ks, int64_t T, int64_t r);
+rgc_status_t rgc_project_batch(int64_t n, const uint16_t* const* Xs, const int64_t* ldxs, const int64_t* ks,
+                               const uint16_t* const* Ps, uint16_t* const* XPs, int64_t T, int64_t r, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /* ---- 3. Sketch accumulation ----------------------------------------------- */
 
@@ -125,6 +144,14 @@ size_t rgc_accumulate_workspace_size(int64_t T, int64_t d, int64_t r);
 rgc_status_t rgc_accumulate(const uint16_t* D, int64_t ldd, const uint16_t* XP, float* C,
                             int64_t T, int64_t d, int64_t r, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* Batched form: n independent accumulations (n <= 16, one rank r, one token
+ * count T) in one launch: Cs[m] += Ds[m]^T XPs[m], D of width ds[m] and row
+ * stride ldds[m]. All arrays are HOST arrays of n entries. */
+size_t rgc_accumulate_batch_workspace_size(int64_t n, const int64_t* ds, int64_t T, int64_t r);
+rgc_status_t rgc_accumulate_batch(int64_t n, const uint16_t* const* Ds, const int64_t* ldds, const int64_t* ds,
+                                  const uint16_t* const* XPs, float* const* Cs, int64_t T, int64_t r, void* ws,
+                                  size_t ws_bytes, void* stream);
 
 /* ---- 4. Normalized update with stochastic rounding ------------------------ */
 

@@ -11,9 +11,12 @@ from .rgc import (  # noqa: F401
     abi_version,
     load_library,
     rgc_accumulate,
+    rgc_accumulate_batch,
     rgc_apply,
     rgc_project,
+    rgc_project_batch,
     rgc_sample_projection,
+    rgc_sample_projections,
     rgc_test_philox,
     rgc_test_reconstruct,
     rgc_test_stochastic_round,

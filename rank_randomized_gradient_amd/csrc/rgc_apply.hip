@@ -11,16 +11,19 @@
 //
 // Two sweeps over W:
 //   sweep 1 reads W and rebuilds H to get sum(w^2) and sum(h^2) (fp64 per lane,
-//           fixed-order reductions across lanes, waves and workgroups); the
-//           last workgroup turns them into s and a skip flag in the workspace;
-//   sweep 2 reads W again, rebuilds the same H (same code, same order), forms
-//           v = fp32(w - fp32(s*h)) and rounds stochastically with 16 bits per
-//           element from Philox4x32-10 keyed on (seed, row, column).
+//           fixed-order reductions across lanes and waves), one partial pair
+//           per workgroup (at most a few hundred workgroups);
+//   sweep 2 first sums those partials in a fixed order in every workgroup (all
+//           get the identical s and skip flag, with no signalling between
+//           workgroups), then reads W again, rebuilds the same H (same code,
+//           same order), forms v = fp32(w - fp32(s*h)) and rounds
+//           stochastically with 16 bits per element from Philox4x32-10 keyed
+//           on (seed, row, column).
 //
-// Lane layout of a tile: the M-tile t row (4*(m/4)... ) ordering below gives
-// lane (g = lane/16, n = lane%16) the 16 consecutive columns jb + 16g .. +15 of
-// row ib + n, i.e. two 16-byte loads of W and two Philox calls (8 columns
-// each) per lane per tile.
+// Lane layout of a tile: M-tile t row m stands for column
+// jb + 16*(m/4) + 4*t + (m%4), which gives lane (g = lane/16, n = lane%16) the
+// 16 consecutive columns jb + 16g .. +15 of row ib + n, i.e. two 16-byte loads
+// of W and two Philox calls (8 columns each) per lane per tile.
 #include "rgc_internal.hpp"
 
 namespace rgc {
@@ -29,13 +32,6 @@ enum ApplyMode { kModeNorms = 0, kModeUpdate = 1, kModeReconstruct = 2 };
 
 constexpr int kApplyRowsPerWG = 64;  // 4 waves x 16 rows
 constexpr int kApplyColsPerTile = 64;
-
-struct ApplyScalars {
-  float s;
-  uint32_t flag;
-  double sum_w2;
-  double sum_h2;
-};
 
 // The C side of the tile product for the 16 rows a wave owns: K-step q holds
 // C[i][32q + 8g .. +7] as bf16 high parts and bf16 remainders.
@@ -117,13 +113,48 @@ __device__ __forceinline__ void rounding_words(uint64_t seed, int64_t i, int64_t
   words[0] = o.x; words[1] = o.y; words[2] = o.z; words[3] = o.w;
 }
 
+// Fixed-order sum of sweep 1's partials (thread t holds partials t, t+256, ...
+// in order; then a butterfly within each wave and the waves in order), and the
+// step s = fp32(tau * ||W|| / ||H||); flag = 1 when ||H|| is zero or not finite
+// or s is not finite (then s = 0).
+__device__ __forceinline__ void step_from_partials(const double* __restrict__ partials, int nparts, float tau, int wave,
+                                                   int lane, float& s, uint32_t& flag, double& nw, double& nh) {
+  __shared__ double red[2][4];
+  double aw = 0.0, ah = 0.0;
+  for (int b = threadIdx.x; b < nparts; b += blockDim.x) {
+    aw += partials[2 * b];
+    ah += partials[2 * b + 1];
+  }
+  aw = wave_sum(aw);
+  ah = wave_sum(ah);
+  if (lane == 0) {
+    red[0][wave] = aw;
+    red[1][wave] = ah;
+  }
+  __syncthreads();
+  const double tw = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+  const double th = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
+  nw = sqrt(tw);
+  nh = sqrt(th);
+  s = 0.f;
+  flag = 0u;
+  if (!(nh > 0.0) || !isfinite(nh)) {
+    flag = 1u;
+  } else {
+    s = (float)((double)tau * nw / nh);
+    if (!isfinite(s)) {
+      s = 0.f;
+      flag = 1u;
+    }
+  }
+}
+
 template <int R, int MODE>
 __global__ __launch_bounds__(256) void apply_kernel(uint16_t* __restrict__ W, int64_t ldw, const float* __restrict__ C,
                                                     const uint16_t* __restrict__ P, int64_t d, int64_t k,
                                                     int tiles_per_wg, float tau, uint64_t seed,
-                                                    float* __restrict__ stats, ApplyScalars* __restrict__ scalars,
-                                                    double* __restrict__ partials, uint32_t* __restrict__ counter,
-                                                    float* __restrict__ Hout) {
+                                                    float* __restrict__ stats, double* __restrict__ partials,
+                                                    int nparts, float* __restrict__ Hout) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int64_t i = (int64_t)blockIdx.x * kApplyRowsPerWG + 16 * wave + n;
@@ -132,8 +163,18 @@ __global__ __launch_bounds__(256) void apply_kernel(uint16_t* __restrict__ W, in
 
   float s = 0.f;
   if constexpr (MODE == kModeUpdate) {
-    if (scalars->flag) return;  // zero or non-finite step: leave W untouched
-    s = scalars->s;
+    // Every workgroup sums sweep 1's partials in the same fixed order, so all
+    // compute the identical step s; workgroup 0 reports it.
+    uint32_t flag;
+    double nw, nh;
+    step_from_partials(partials, nparts, tau, wave, lane, s, flag, nw, nh);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && stats) {
+      stats[0] = (float)nw;
+      stats[1] = (float)nh;
+      stats[2] = s;
+      stats[3] = (float)flag;
+    }
+    if (flag) return;  // zero or non-finite step: leave W untouched
   }
 
   RowOperand<R> rop;
@@ -203,53 +244,10 @@ __global__ __launch_bounds__(256) void apply_kernel(uint16_t* __restrict__ W, in
       red[1][wave] = sh;
     }
     __syncthreads();
-    const int64_t nblocks = (int64_t)gridDim.x * gridDim.y;
-    const int64_t bid = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
     if (threadIdx.x == 0) {
+      const int64_t bid = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
       partials[2 * bid] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
       partials[2 * bid + 1] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
-    }
-    if (!arrive_last(counter, (uint32_t)(nblocks - 1))) return;
-    // Last workgroup: fixed-order sum of all partials.
-    double aw = 0.0, ah = 0.0;
-    for (int64_t b = threadIdx.x; b < nblocks; b += blockDim.x) {
-      aw += __builtin_nontemporal_load(partials + 2 * b);
-      ah += __builtin_nontemporal_load(partials + 2 * b + 1);
-    }
-    aw = wave_sum(aw);
-    ah = wave_sum(ah);
-    __syncthreads();
-    if (lane == 0) {
-      red[0][wave] = aw;
-      red[1][wave] = ah;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const double tw = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
-      const double th = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
-      const double nw = sqrt(tw), nh = sqrt(th);
-      float sc = 0.f;
-      uint32_t flag = 0u;
-      if (!(nh > 0.0) || !isfinite(nh)) {
-        flag = 1u;
-      } else {
-        sc = (float)((double)tau * nw / nh);
-        if (!isfinite(sc)) {
-          sc = 0.f;
-          flag = 1u;
-        }
-      }
-      scalars->s = sc;
-      scalars->flag = flag;
-      scalars->sum_w2 = tw;
-      scalars->sum_h2 = th;
-      if (stats) {
-        stats[0] = (float)nw;
-        stats[1] = (float)nh;
-        stats[2] = sc;
-        stats[3] = (float)flag;
-      }
-      *counter = 0u;
     }
   }
 }
@@ -289,11 +287,12 @@ struct ApplyPlan {
   int64_t col_groups;
 };
 
-ApplyPlan apply_plan(int64_t d, int64_t k) {
+// Grid over (64-row blocks) x (groups of 64-column tiles) with at most
+// `target` workgroups.
+ApplyPlan apply_plan(int64_t d, int64_t k, int64_t target) {
   ApplyPlan p;
   p.row_blocks = (d + kApplyRowsPerWG - 1) / kApplyRowsPerWG;
   p.col_tiles = (k + kApplyColsPerTile - 1) / kApplyColsPerTile;
-  const int64_t target = env_int("RGC_APPLY_WGS", 1024);
   int64_t tpw = (p.row_blocks * p.col_tiles + target - 1) / target;
   if (tpw < 1) tpw = 1;
   if (tpw > p.col_tiles) tpw = p.col_tiles;
@@ -301,35 +300,35 @@ ApplyPlan apply_plan(int64_t d, int64_t k) {
   p.col_groups = (p.col_tiles + tpw - 1) / tpw;
   return p;
 }
+// Sweep 1 writes one partial per workgroup and every sweep-2 workgroup reads
+// them all, so sweep 1's grid stays small; sweep 2's is sized for the chip.
+ApplyPlan norms_plan(int64_t d, int64_t k) { return apply_plan(d, k, env_int("RGC_NORM_WGS", 256)); }
+ApplyPlan update_plan(int64_t d, int64_t k) { return apply_plan(d, k, env_int("RGC_APPLY_WGS", 1024)); }
 
 size_t apply_ws(int64_t d, int64_t k) {
-  const ApplyPlan p = apply_plan(d, k);
-  return kCounterBytes + 256 + (size_t)p.row_blocks * p.col_groups * 2 * sizeof(double);
+  const ApplyPlan p = norms_plan(d, k);
+  return (size_t)p.row_blocks * p.col_groups * 2 * sizeof(double);
 }
 
 template <int R>
 rgc_status_t apply_launch(uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d, int64_t k,
                           float tau, uint64_t seed, float* stats, void* ws, hipStream_t s) {
-  const ApplyPlan p = apply_plan(d, k);
-  char* base = static_cast<char*>(ws);
-  uint32_t* counter = reinterpret_cast<uint32_t*>(base);
-  ApplyScalars* scalars = reinterpret_cast<ApplyScalars*>(base + kCounterBytes);
-  double* partials = reinterpret_cast<double*>(base + kCounterBytes + 256);
-  dim3 grid((unsigned)p.row_blocks, (unsigned)p.col_groups);
-  hipLaunchKernelGGL((apply_kernel<R, kModeNorms>), grid, dim3(256), 0, s, W, ldw, C, P, d, k, p.tiles_per_wg, tau,
-                     seed, stats, scalars, partials, counter, nullptr);
-  if (hipGetLastError() != hipSuccess) return RGC_ERR_HIP;
-  hipLaunchKernelGGL((apply_kernel<R, kModeUpdate>), grid, dim3(256), 0, s, W, ldw, C, P, d, k, p.tiles_per_wg, tau,
-                     seed, stats, scalars, partials, counter, nullptr);
+  const ApplyPlan p1 = norms_plan(d, k), p2 = update_plan(d, k);
+  double* partials = static_cast<double*>(ws);
+  const int nparts = (int)(p1.row_blocks * p1.col_groups);
+  hipLaunchKernelGGL((apply_kernel<R, kModeNorms>), dim3((unsigned)p1.row_blocks, (unsigned)p1.col_groups), dim3(256),
+                     0, s, W, ldw, C, P, d, k, p1.tiles_per_wg, tau, seed, nullptr, partials, nparts, nullptr);
+  hipLaunchKernelGGL((apply_kernel<R, kModeUpdate>), dim3((unsigned)p2.row_blocks, (unsigned)p2.col_groups), dim3(256),
+                     0, s, W, ldw, C, P, d, k, p2.tiles_per_wg, tau, seed, stats, partials, nparts, nullptr);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
 template <int R>
 rgc_status_t reconstruct_launch(const float* C, const uint16_t* P, float* H, int64_t d, int64_t k, hipStream_t s) {
-  const ApplyPlan p = apply_plan(d, k);
+  const ApplyPlan p = update_plan(d, k);
   dim3 grid((unsigned)p.row_blocks, (unsigned)p.col_groups);
   hipLaunchKernelGGL((apply_kernel<R, kModeReconstruct>), grid, dim3(256), 0, s, nullptr, k, C, P, d, k,
-                     p.tiles_per_wg, 0.f, 0ull, nullptr, nullptr, nullptr, nullptr, H);
+                     p.tiles_per_wg, 0.f, 0ull, nullptr, nullptr, 0, H);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 

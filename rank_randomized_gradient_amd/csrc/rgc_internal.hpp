@@ -12,10 +12,9 @@
 
 namespace rgc {
 
-constexpr size_t kCounterBytes = RGC_WS_COUNTER_BYTES;
-// Tiled dimensions (tokens for project, d for accumulate) are limited so that
-// one completion counter per 64-wide tile fits in the counter region.
-constexpr int64_t kMaxTiledDim = 64 * (int64_t)(kCounterBytes / sizeof(uint32_t));
+// Per-call limit on the tiled dimension (tokens for project, d for
+// accumulate); keeps every in-kernel offset within 32 bits.
+constexpr int64_t kMaxTiledDim = 65536;
 
 // Tiling of the rank dimension r (a multiple of 16, at most 64, or a multiple
 // of 64 up to 256). A wave covers RPW rank columns in NG groups of GW columns;

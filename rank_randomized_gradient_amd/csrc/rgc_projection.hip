@@ -7,14 +7,20 @@
 //
 // QR of a Gaussian [page "Randomized Gradient Compression", footnote 1]:
 // P = sqrt(k/r) Q with Q the sign-corrected (diag R > 0) thin QR factor of a
-// Gaussian k x r matrix. Q is computed by CholeskyQR2 in fp64:
-//   A  = Box-Muller normals from Philox                  (gram pass 1 writes A)
-//   R1 = chol(A^T A),   Q1 = A R1^-1                      (reduce+factor, trmul)
-//   R2 = chol(Q1^T Q1), Q  = Q1 R2^-1                     (gram, reduce+factor, trmul)
+// Gaussian k x r matrix. Q is computed by CholeskyQR2 in fp64, for a batch of
+// matrices of one rank at once (each launch covers every matrix, so the
+// latency-bound steps are paid once per batch, not once per matrix):
+//   fill     A = Box-Muller normals from Philox
+//   gram     partial Grams of A over 128-row blocks
+//   reduce   G1 = A^T A (partials summed in block order)
+//   factor   U1 = chol(G1)^-1
+//   gram     Q1 = A U1 (stored), partial Grams of Q1
+//   reduce   G2 = Q1^T Q1
+//   factor   U2 = chol(G2)^-1
+//   gram     P = bf16(fp32(sqrt(k/r) * Q1 U2))
 // Cholesky factors have a positive diagonal, so Q is the unique factor with
 // the standard sign correction; the second pass restores orthogonality to
-// fp64 accuracy. The Gram matrices are summed from per-workgroup partials in a
-// fixed order, so P is bit-reproducible.
+// fp64 accuracy. Every reduction has a fixed order, so P is bit-reproducible.
 #include <math.h>
 #include <string.h>
 
@@ -50,10 +56,34 @@ __global__ void rademacher_kernel(uint16_t* __restrict__ P, int64_t k, int r, ui
 }
 
 // ---------------------------------------------------------------------------
-// CholeskyQR2 pieces. R is the rank (<= 128), templated for register tiles.
+// CholeskyQR2, batched over up to kQrMaxBatch matrices of one rank R <= 128.
 // ---------------------------------------------------------------------------
-constexpr int kQrRowsPerChunk = 16;
+constexpr int kQrMaxBatch = 16;
+constexpr int kQrBlockRows = 128;  // rows per Gram / multiply workgroup
+constexpr int kQrSub = 16;         // rows staged in LDS at a time
 constexpr double kTwoPi = 6.283185307179586;  // 2*pi rounded to double
+
+struct QrBatch {
+  int n;
+  int64_t k[kQrMaxBatch];
+  uint64_t seed[kQrMaxBatch];
+  double scale[kQrMaxBatch];
+  uint16_t* P[kQrMaxBatch];
+  double* A[kQrMaxBatch];     // k x R Gaussian
+  double* Q1[kQrMaxBatch];    // k x R after the first pass
+  double* part[kQrMaxBatch];  // one R x R partial Gram per 128-row block
+  double* U1[kQrMaxBatch];
+  double* U2[kQrMaxBatch];
+  uint32_t* status[kQrMaxBatch];
+  int fill_begin[kQrMaxBatch + 1];   // workgroup prefix of the Gaussian fill
+  int block_begin[kQrMaxBatch + 1];  // workgroup prefix of the 128-row blocks
+};
+
+__device__ __forceinline__ int batch_item(const int* begin, int n, int b) {
+  int m = 0;
+  while (m + 1 < n && b >= begin[m + 1]) ++m;
+  return m;
+}
 
 // Normal draws for row i, columns 4q .. 4q+3 (Box-Muller on Philox words).
 __device__ __forceinline__ void gaussian4(uint64_t seed, int64_t i, int q, double (&z)[4]) {
@@ -71,199 +101,279 @@ __device__ __forceinline__ void gaussian4(uint64_t seed, int64_t i, int q, doubl
   }
 }
 
-// Gram partials: block b sums rows [b*rows_per_block, ...) of M^T M into
-// partial[b] (R x R, fp64). GEN: M is drawn here (and stored to M);
-// otherwise M is read.
-template <int R, bool GEN>
-__global__ __launch_bounds__(256) void gram_kernel(double* __restrict__ M, int64_t k, int64_t rows_per_block,
-                                                   uint64_t seed, double* __restrict__ partial) {
-  constexpr int TU = R / 16;  // each thread owns a TU x TU sub-tile
-  __shared__ double rows[kQrRowsPerChunk][R];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  double acc[TU][TU];
+// A = Gaussian, one thread per (row, 4 columns).
+template <int R>
+__global__ __launch_bounds__(256) void gauss_fill_kernel(QrBatch b) {
+  const int m = batch_item(b.fill_begin, b.n, blockIdx.x);
+  const int64_t idx = (int64_t)(blockIdx.x - b.fill_begin[m]) * blockDim.x + threadIdx.x;
+  if (idx >= b.k[m] * (R / 4)) return;
+  const int64_t i = idx / (R / 4);
+  const int q = (int)(idx % (R / 4));
+  double z[4];
+  gaussian4(b.seed[m], i, q, z);
+  double* dst = b.A[m] + i * R + 4 * q;
 #pragma unroll
-  for (int u = 0; u < TU; ++u)
-#pragma unroll
-    for (int v = 0; v < TU; ++v) acc[u][v] = 0.0;
-  const int64_t rbeg = (int64_t)blockIdx.x * rows_per_block;
-  const int64_t rend = rbeg + rows_per_block < k ? rbeg + rows_per_block : k;
-  for (int64_t r0 = rbeg; r0 < rend; r0 += kQrRowsPerChunk) {
-    __syncthreads();
-    if constexpr (GEN) {
-      // kQrRowsPerChunk x R/4 Philox calls for this chunk
-      for (int t = threadIdx.x; t < kQrRowsPerChunk * (R / 4); t += blockDim.x) {
-        const int lr = t / (R / 4), q = t % (R / 4);
-        const int64_t row = r0 + lr;
-        double z[4] = {0.0, 0.0, 0.0, 0.0};
-        if (row < rend) {
-          gaussian4(seed, row, q, z);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) M[row * R + 4 * q + e] = z[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rows[lr][4 * q + e] = z[e];
-      }
-    } else {
-      for (int t = threadIdx.x; t < kQrRowsPerChunk * R; t += blockDim.x) {
-        const int lr = t / R, c = t % R;
-        const int64_t row = r0 + lr;
-        rows[lr][c] = row < rend ? M[row * R + c] : 0.0;
-      }
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int lr = 0; lr < kQrRowsPerChunk; ++lr) {
-      double a[TU], b[TU];
-#pragma unroll
-      for (int u = 0; u < TU; ++u) a[u] = rows[lr][ty + 16 * u];
-#pragma unroll
-      for (int v = 0; v < TU; ++v) b[v] = rows[lr][tx + 16 * v];
-#pragma unroll
-      for (int u = 0; u < TU; ++u)
-#pragma unroll
-        for (int v = 0; v < TU; ++v) acc[u][v] += a[u] * b[v];
-    }
-  }
-  double* out = partial + (int64_t)blockIdx.x * R * R;
-#pragma unroll
-  for (int u = 0; u < TU; ++u)
-#pragma unroll
-    for (int v = 0; v < TU; ++v) out[(ty + 16 * u) * R + tx + 16 * v] = acc[u][v];
+  for (int e = 0; e < 4; ++e) dst[e] = z[e];
 }
 
-// Sums the Gram partials in block order (each block a slice of the R x R
-// entries); the last block to finish writes U = R^-1 for the upper Cholesky
-// factor R of G (G = R^T R, diag R > 0), upper triangular with zeros below.
+// Rows staged in LDS at a time: a whole 128-row block when U (R x R) and the
+// rows fit together, else 16 (R = 128).
+template <int R>
+struct QrTile {
+  static constexpr int SUB = R <= 64 ? kQrBlockRows : 16;
+};
+
+// One 128-row block of one matrix, staged through LDS (all at once when it fits).
+//   MODE 0: partial Gram of A.
+//   MODE 1: Q1 = A U1 (stored), then partial Gram of Q1.
+//   MODE 2: P = bf16(fp32(scale * Q1 U2)).
+// Thread (tx, ty) (16 x 16) owns Gram entries (ty + 16a, tx + 16c) and, in the
+// multiply, rows ty + 16i of the staged rows at columns tx + 16v. U is dense
+// with zeros below the diagonal, so the multiply needs no triangular test.
+template <int R, int MODE>
+__global__ __launch_bounds__(256) void qr_block_kernel(QrBatch b) {
+  constexpr int TU = R / 16;
+  constexpr int SUB = QrTile<R>::SUB;
+  constexpr int RI = SUB / 16;  // staged rows per thread in the multiply
+  __shared__ double rows[SUB][R + 1];  // +1: rows read by different lanes sit on different banks
+  __shared__ double u[MODE == 0 ? 1 : R][MODE == 0 ? 1 : R];
+  const int m = batch_item(b.block_begin, b.n, blockIdx.x);
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int64_t k = b.k[m];
+  const int64_t rbeg = (int64_t)(blockIdx.x - b.block_begin[m]) * kQrBlockRows;
+  const int64_t rend = rbeg + kQrBlockRows < k ? rbeg + kQrBlockRows : k;
+  const double* src = MODE == 2 ? b.Q1[m] : b.A[m];
+  if constexpr (MODE != 0) {
+    // R*R/256 loads per thread, all issued before the first LDS store
+    const double* U = MODE == 1 ? b.U1[m] : b.U2[m];
+    constexpr int NU = R * R / 256;
+    double uv[NU];
+#pragma unroll
+    for (int e = 0; e < NU; ++e) uv[e] = U[threadIdx.x + 256 * e];
+#pragma unroll
+    for (int e = 0; e < NU; ++e) {
+      const int t = threadIdx.x + 256 * e;
+      u[t / R][t % R] = uv[e];
+    }
+  }
+  double acc[TU][TU];
+#pragma unroll
+  for (int a = 0; a < TU; ++a)
+#pragma unroll
+    for (int c = 0; c < TU; ++c) acc[a][c] = 0.0;
+
+  for (int64_t r0 = rbeg; r0 < rend; r0 += SUB) {
+    __syncthreads();
+    {
+      // SUB*R/256 loads per thread (rows clamped to a valid one, then zeroed),
+      // all issued before the first LDS store
+      constexpr int NS = SUB * R / 256;
+      double sv[NS];
+#pragma unroll
+      for (int e = 0; e < NS; ++e) {
+        const int t = threadIdx.x + 256 * e;
+        const int64_t row = r0 + t / R;
+        sv[e] = src[(row < rend ? row : rend - 1) * R + t % R];
+      }
+#pragma unroll
+      for (int e = 0; e < NS; ++e) {
+        const int t = threadIdx.x + 256 * e;
+        rows[t / R][t % R] = r0 + t / R < rend ? sv[e] : 0.0;
+      }
+    }
+    __syncthreads();
+    if constexpr (MODE != 0) {
+      double y[RI][TU];
+#pragma unroll
+      for (int i = 0; i < RI; ++i)
+#pragma unroll
+        for (int v = 0; v < TU; ++v) y[i][v] = 0.0;
+#pragma unroll 2
+      for (int a = 0; a < R; ++a) {
+        double x[RI], w[TU];
+#pragma unroll
+        for (int i = 0; i < RI; ++i) x[i] = rows[ty + 16 * i][a];
+#pragma unroll
+        for (int v = 0; v < TU; ++v) w[v] = u[a][tx + 16 * v];
+#pragma unroll
+        for (int i = 0; i < RI; ++i)
+#pragma unroll
+          for (int v = 0; v < TU; ++v) y[i][v] += x[i] * w[v];
+      }
+      if constexpr (MODE == 2) {
+#pragma unroll
+        for (int i = 0; i < RI; ++i) {
+          const int64_t row = r0 + ty + 16 * i;
+          if (row >= rend) continue;
+#pragma unroll
+          for (int v = 0; v < TU; ++v)
+            b.P[m][row * R + tx + 16 * v] = (uint16_t)f32_to_bf16_rne((float)(b.scale[m] * y[i][v]));
+        }
+        continue;
+      } else {
+#pragma unroll
+        for (int i = 0; i < RI; ++i) {
+          const int64_t row = r0 + ty + 16 * i;
+          if (row >= rend) continue;
+#pragma unroll
+          for (int v = 0; v < TU; ++v) b.Q1[m][row * R + tx + 16 * v] = y[i][v];
+        }
+        __syncthreads();  // everyone is done reading the staged rows
+#pragma unroll
+        for (int i = 0; i < RI; ++i) {
+          const bool in = r0 + ty + 16 * i < rend;
+#pragma unroll
+          for (int v = 0; v < TU; ++v) rows[ty + 16 * i][tx + 16 * v] = in ? y[i][v] : 0.0;
+        }
+        __syncthreads();
+      }
+    }
+    if constexpr (MODE != 2) {
+      const int nr = (int)(rend - r0 < SUB ? rend - r0 : SUB);
+#pragma unroll 4
+      for (int lr = 0; lr < nr; ++lr) {
+        double x[TU], w[TU];
+#pragma unroll
+        for (int a = 0; a < TU; ++a) x[a] = rows[lr][ty + 16 * a];
+#pragma unroll
+        for (int c = 0; c < TU; ++c) w[c] = rows[lr][tx + 16 * c];
+#pragma unroll
+        for (int a = 0; a < TU; ++a)
+#pragma unroll
+          for (int c = 0; c < TU; ++c) acc[a][c] += x[a] * w[c];
+      }
+    }
+  }
+  if constexpr (MODE != 2) {
+    double* out = b.part[m] + (int64_t)(blockIdx.x - b.block_begin[m]) * R * R;
+#pragma unroll
+    for (int a = 0; a < TU; ++a)
+#pragma unroll
+      for (int c = 0; c < TU; ++c) out[(ty + 16 * a) * R + tx + 16 * c] = acc[a][c];
+  }
+}
+
+// G = sum of a matrix's block partials in block order, upper triangle only
+// (one thread per entry, 16 blocks' loads in flight at a time).
+template <int R>
+__global__ __launch_bounds__(256) void qr_gram_reduce_kernel(QrBatch b, double* __restrict__ G_all) {
+  const int m = blockIdx.y;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= b.n || e >= R * R) return;
+  const int row = e / R, col = e % R;
+  if (col < row) return;
+  const int nparts = b.block_begin[m + 1] - b.block_begin[m];
+  const double* part = b.part[m];
+  double sum = 0.0;
+  for (int p0 = 0; p0 < nparts; p0 += 16) {
+    double v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = part[(int64_t)(p0 + i < nparts ? p0 + i : nparts - 1) * R * R + e];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (p0 + i < nparts) sum = (p0 + i == 0) ? v[i] : sum + v[i];
+  }
+  G_all[(int64_t)m * R * R + e] = sum;
+}
+
+// One workgroup (1024 threads) per matrix: U = chol(G)^-1 (upper triangular,
+// zeros below) from the summed Gram G (upper triangle).
 //
 // U comes from one Gaussian elimination of [G | I] without pivoting (stable
 // for symmetric positive definite G): with G = L D L^T (L unit lower), the
 // eliminated left block is D L^T and the right block is L^-1, so
-// R = D^1/2 L^T and R^-1 = L^-T D^-1/2. The symmetric Schur complement is
-// kept in g's upper triangle and L^-1 (unit diagonal implied) in its strictly
-// lower triangle; each column costs one barrier.
+// R = D^1/2 L^T and R^-1 = L^-T D^-1/2. Thread (ty, tx) of a 32 x 32 grid
+// keeps elements (ty + 32a, tx + 32c) in registers: the symmetric Schur
+// complement in the upper triangle and L^-1 (unit diagonal implied) in the
+// strictly lower one. Only the pivot row travels through LDS, double
+// buffered, so each column costs one barrier.
 template <int R>
-__global__ __launch_bounds__(256) void reduce_factor_kernel(const double* __restrict__ partial, int nparts,
-                                                            double* __restrict__ G, double* __restrict__ U,
-                                                            uint32_t* __restrict__ counter,
-                                                            uint32_t* __restrict__ status) {
-  __shared__ double g[R][R + 1];  // +1 pads rows off the same banks
+__global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double* __restrict__ G_all, int second) {
+  constexpr int T32 = (R + 31) / 32;
+  __shared__ double rowbuf[2][R];
+  __shared__ double diag[R];
+  const int m = blockIdx.x;
   const int tid = threadIdx.x;
-  const int ty = tid >> 4, tx = tid & 15;
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + tid;
-  if (e < (int64_t)R * R) {
-    double s = 0.0;
-    for (int p = 0; p < nparts; ++p) s += partial[(int64_t)p * R * R + e];
-    G[e] = s;
-  }
-  if (!arrive_last(counter, gridDim.x - 1)) return;
-  for (int a = ty; a < R; a += 16)
-    for (int c = tx; c < R; c += 16) g[a][c] = (c >= a) ? G[a * R + c] : 0.0;
-  __syncthreads();
+  const int tx = tid & 31, ty = tid >> 5;
+  double* U = second ? b.U2[m] : b.U1[m];
+  const double* G = G_all + (int64_t)m * R * R;
 
+  // 2. elimination with register-resident elements
+  double a[T32][T32];
+#pragma unroll
+  for (int i = 0; i < T32; ++i)
+#pragma unroll
+    for (int j = 0; j < T32; ++j) {
+      const int l = ty + 32 * i, c = tx + 32 * j;
+      a[i][j] = (l < R && c < R && c >= l) ? G[l * R + c] : 0.0;
+      if (l == 0 && c < R) rowbuf[0][c] = a[i][j];
+    }
   for (int j = 0; j < R; ++j) {
-    const double piv = g[j][j];
-    for (int l = j + 1 + ty; l < R; l += 16) {
-      const double f = g[j][l] / piv;  // G(l, j) / G(j, j), using the symmetric upper copy
-      for (int m = l + tx; m < R; m += 16) g[l][m] -= f * g[j][m];
-      for (int c = tx; c < j; c += 16) g[l][c] -= f * g[j][c];
-      if (tx == 0) g[l][j] = -f;  // E(l, j) = 0 - f * E(j, j)
-    }
     __syncthreads();
-  }
-  if (tid == 0) {
-    bool ok = true;
-    for (int j = 0; j < R; ++j) ok = ok && (g[j][j] > 0.0) && isfinite(g[j][j]);
-    *status = ok ? 0u : 1u;
-  }
-  for (int a = ty; a < R; a += 16)
-    for (int c = tx; c < R; c += 16) {
-      const double rs = 1.0 / sqrt(g[c][c]);
-      double v = 0.0;
-      if (c == a) v = rs;
-      else if (c > a) v = g[c][a] * rs;
-      U[a * R + c] = v;
-    }
-  if (tid == 0) *counter = 0u;
-}
-
-// Y = M U for U upper triangular (R x R). FINAL: P = bf16(fp32(scale * Y)),
-// else Y is written in fp64.
-template <int R, bool FINAL>
-__global__ __launch_bounds__(256) void trmul_kernel(const double* __restrict__ M, const double* __restrict__ U,
-                                                    int64_t k, int64_t rows_per_block, double scale,
-                                                    double* __restrict__ Y, uint16_t* __restrict__ P) {
-  constexpr int TU = R / 16;
-  __shared__ double u[R][R];
-  __shared__ double rows[kQrRowsPerChunk][R + 1];  // +1: rows read by different lanes sit on different banks
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  for (int t = threadIdx.x; t < R * R; t += blockDim.x) u[t / R][t % R] = U[t];
-  const int64_t rbeg = (int64_t)blockIdx.x * rows_per_block;
-  const int64_t rend = rbeg + rows_per_block < k ? rbeg + rows_per_block : k;
-  for (int64_t r0 = rbeg; r0 < rend; r0 += kQrRowsPerChunk) {
-    __syncthreads();
-    for (int t = threadIdx.x; t < kQrRowsPerChunk * R; t += blockDim.x) {
-      const int lr = t / R, c = t % R;
-      const int64_t row = r0 + lr;
-      rows[lr][c] = row < rend ? M[row * R + c] : 0.0;
-    }
-    __syncthreads();
-    // thread (tx, ty): row r0 + ty, columns tx + 16 v
-    const int64_t row = r0 + ty;
-    double y[TU];
+    const double* rb = rowbuf[j & 1];
+    const double inv = 1.0 / rb[j];
 #pragma unroll
-    for (int v = 0; v < TU; ++v) y[v] = 0.0;
-    for (int a = 0; a < R; ++a) {
-      const double ma = rows[ty][a];
+    for (int i = 0; i < T32; ++i) {
+      const int l = ty + 32 * i;
+      if (l <= j || l >= R) continue;
+      const double f = rb[l] * inv;  // G(l, j) / G(j, j), from the symmetric upper copy
 #pragma unroll
-      for (int v = 0; v < TU; ++v) {
-        const int c = tx + 16 * v;
-        if (a <= c) y[v] += ma * u[a][c];
+      for (int jj = 0; jj < T32; ++jj) {
+        const int c = tx + 32 * jj;
+        if (c >= R) continue;
+        if (c >= l || c < j) a[i][jj] -= f * rb[c];
+        else if (c == j) a[i][jj] = -f;  // E(l, j) = 0 - f * E(j, j)
       }
-    }
-    if (row < rend) {
+      if (l == j + 1) {
 #pragma unroll
-      for (int v = 0; v < TU; ++v) {
-        const int c = tx + 16 * v;
-        if constexpr (FINAL) {
-          const float f = (float)(scale * y[v]);
-          P[row * R + c] = (uint16_t)f32_to_bf16_rne(f);
-        } else {
-          Y[row * R + c] = y[v];
+        for (int jj = 0; jj < T32; ++jj) {
+          const int c = tx + 32 * jj;
+          if (c < R) rowbuf[(j + 1) & 1][c] = a[i][jj];
         }
       }
     }
   }
+  // 3. U[x][y] = E(y, x) / sqrt(D_y) above the diagonal, 1 / sqrt(D_y) on it
+#pragma unroll
+  for (int i = 0; i < T32; ++i)
+#pragma unroll
+    for (int j = 0; j < T32; ++j) {
+      const int l = ty + 32 * i, c = tx + 32 * j;
+      if (l < R && c == l) diag[l] = a[i][j];
+    }
+  __syncthreads();
+  if (tid == 0) {
+    bool ok = true;
+    for (int c = 0; c < R; ++c) ok = ok && (diag[c] > 0.0) && isfinite(diag[c]);
+    b.status[m][second] = ok ? 0u : 1u;
+  }
+#pragma unroll
+  for (int i = 0; i < T32; ++i)
+#pragma unroll
+    for (int j = 0; j < T32; ++j) {
+      const int l = ty + 32 * i, c = tx + 32 * j;
+      if (l >= R || c >= R || c > l) continue;
+      const double rs = 1.0 / sqrt(diag[l]);
+      if (c == l) {
+        U[l * R + l] = rs;
+      } else {
+        U[c * R + l] = a[i][j] * rs;
+        U[l * R + c] = 0.0;
+      }
+    }
 }
 
 namespace {
 
-struct QrPlan {
-  int64_t rows_per_block;
+struct QrItemLayout {
+  size_t a, q1, part, u1, u2, status, total;
   int blocks;
 };
 
-QrPlan qr_plan(int64_t k, int64_t r) {
-  QrPlan p;
-  // about 2K fp64 multiply-adds per thread in the Gram pass, 8..128 blocks
-  int64_t target = (k * r * r + 256 * 2048 - 1) / (256 * 2048);
-  if (target < 8) target = 8;
-  if (target > 128) target = 128;
-  int64_t rpb = (k + target - 1) / target;
-  rpb = ((rpb + kQrRowsPerChunk - 1) / kQrRowsPerChunk) * kQrRowsPerChunk;
-  if (rpb < kQrRowsPerChunk) rpb = kQrRowsPerChunk;
-  p.rows_per_block = rpb;
-  p.blocks = (int)((k + rpb - 1) / rpb);
-  return p;
-}
-
-struct QrLayout {
-  size_t a, q1, partial, g, u1, u2, status, total;
-};
-
-QrLayout qr_layout(int64_t k, int64_t r) {
-  const QrPlan p = qr_plan(k, r);
-  QrLayout l;
-  size_t off = kCounterBytes;
+QrItemLayout qr_item_layout(int64_t k, int64_t r) {
+  QrItemLayout l;
+  l.blocks = (int)((k + kQrBlockRows - 1) / kQrBlockRows);
+  size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
     off += (bytes + 255) / 256 * 256;
@@ -271,45 +381,83 @@ QrLayout qr_layout(int64_t k, int64_t r) {
   };
   l.a = take((size_t)k * r * sizeof(double));
   l.q1 = take((size_t)k * r * sizeof(double));
-  l.partial = take((size_t)p.blocks * r * r * sizeof(double));
-  l.g = take((size_t)r * r * sizeof(double));
+  l.part = take((size_t)l.blocks * r * r * sizeof(double));
   l.u1 = take((size_t)r * r * sizeof(double));
   l.u2 = take((size_t)r * r * sizeof(double));
-  l.status = take(256);
+  l.status = take(2 * sizeof(uint32_t));
   l.total = off;
   return l;
 }
 
-template <int R>
-rgc_status_t qr_launch(uint64_t seed, int64_t k, uint16_t* P, void* ws, hipStream_t s) {
-  const QrPlan p = qr_plan(k, R);
-  const QrLayout l = qr_layout(k, R);
-  char* base = static_cast<char*>(ws);
-  uint32_t* counter = reinterpret_cast<uint32_t*>(base);
-  double* A = reinterpret_cast<double*>(base + l.a);
-  double* Q1 = reinterpret_cast<double*>(base + l.q1);
-  double* part = reinterpret_cast<double*>(base + l.partial);
-  double* G = reinterpret_cast<double*>(base + l.g);
-  double* U1 = reinterpret_cast<double*>(base + l.u1);
-  double* U2 = reinterpret_cast<double*>(base + l.u2);
-  uint32_t* status = reinterpret_cast<uint32_t*>(base + l.status);
-  const unsigned red_blocks = (unsigned)((R * R + 255) / 256);
-  const double scale = sqrt((double)k / (double)R);
+size_t qr_gram_bytes(int64_t n, int64_t r) { return ((size_t)n * r * r * sizeof(double) + 255) / 256 * 256; }
 
-  hipLaunchKernelGGL((gram_kernel<R, true>), dim3(p.blocks), dim3(256), 0, s, A, k, p.rows_per_block, seed, part);
-  hipLaunchKernelGGL((reduce_factor_kernel<R>), dim3(red_blocks), dim3(256), 0, s, part, p.blocks, G, U1, counter,
-                     status);
-  hipLaunchKernelGGL((trmul_kernel<R, false>), dim3(p.blocks), dim3(256), 0, s, A, U1, k, p.rows_per_block, 1.0, Q1,
-                     nullptr);
-  hipLaunchKernelGGL((gram_kernel<R, false>), dim3(p.blocks), dim3(256), 0, s, Q1, k, p.rows_per_block, seed, part);
-  hipLaunchKernelGGL((reduce_factor_kernel<R>), dim3(red_blocks), dim3(256), 0, s, part, p.blocks, G, U2, counter,
-                     status + 1);
-  hipLaunchKernelGGL((trmul_kernel<R, true>), dim3(p.blocks), dim3(256), 0, s, Q1, U2, k, p.rows_per_block, scale,
-                     nullptr, P);
+template <int R>
+rgc_status_t qr_launch(int n, const uint64_t* seeds, const int64_t* ks, uint16_t* const* Ps, void* ws, hipStream_t s) {
+  QrBatch b = {};
+  b.n = n;
+  char* base = static_cast<char*>(ws);
+  // the n summed Gram matrices first, then each item's buffers
+  double* G_all = reinterpret_cast<double*>(base);
+  size_t off = qr_gram_bytes(n, R);
+  b.fill_begin[0] = 0;
+  b.block_begin[0] = 0;
+  for (int m = 0; m < n; ++m) {
+    const QrItemLayout l = qr_item_layout(ks[m], R);
+    b.k[m] = ks[m];
+    b.seed[m] = seeds[m];
+    b.scale[m] = sqrt((double)ks[m] / (double)R);
+    b.P[m] = Ps[m];
+    b.A[m] = reinterpret_cast<double*>(base + off + l.a);
+    b.Q1[m] = reinterpret_cast<double*>(base + off + l.q1);
+    b.part[m] = reinterpret_cast<double*>(base + off + l.part);
+    b.U1[m] = reinterpret_cast<double*>(base + off + l.u1);
+    b.U2[m] = reinterpret_cast<double*>(base + off + l.u2);
+    b.status[m] = reinterpret_cast<uint32_t*>(base + off + l.status);
+    b.fill_begin[m + 1] = b.fill_begin[m] + (int)((ks[m] * (R / 4) + 255) / 256);
+    b.block_begin[m + 1] = b.block_begin[m] + l.blocks;
+    off += l.total;
+  }
+  hipLaunchKernelGGL((gauss_fill_kernel<R>), dim3(b.fill_begin[n]), dim3(256), 0, s, b);
+  hipLaunchKernelGGL((qr_block_kernel<R, 0>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
+  const dim3 red_grid((unsigned)((R * R + 255) / 256), (unsigned)n);
+  hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
+  hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(1024), 0, s, b, G_all, 0);
+  hipLaunchKernelGGL((qr_block_kernel<R, 1>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
+  hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
+  hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(1024), 0, s, b, G_all, 1);
+  hipLaunchKernelGGL((qr_block_kernel<R, 2>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
 bool qr_rank_supported(int64_t r) { return r == 16 || r == 32 || r == 48 || r == 64 || r == 128; }
+
+uint32_t rademacher_magnitude(int64_t r) {
+  // a = bf16(fp32(1/sqrt(r))), both roundings to nearest even
+  const float af = (float)(1.0 / sqrt((double)r));
+  uint32_t bits;
+  memcpy(&bits, &af, sizeof(bits));
+  return (bits + 0x7FFFu + ((bits >> 16) & 1u)) >> 16;
+}
+
+rgc_status_t check_item(rgc_proj_kind_t kind, int64_t k, int64_t r, const uint16_t* P) {
+  if (k <= 0 || r <= 0 || r > k) return RGC_ERR_SHAPE;
+  if (kind != RGC_PROJ_RADEMACHER && kind != RGC_PROJ_QR_GAUSSIAN) return RGC_ERR_UNSUPPORTED;
+  if (!rank_supported(r) || (k % 8) != 0 || k > (int64_t)0x7FFFFFFF) return RGC_ERR_UNSUPPORTED;
+  if (kind == RGC_PROJ_QR_GAUSSIAN && !qr_rank_supported(r)) return RGC_ERR_UNSUPPORTED;
+  if (!P) return RGC_ERR_NULL;
+  if (!aligned16(P)) return RGC_ERR_ALIGN;
+  return RGC_OK;
+}
+
+size_t batch_ws(rgc_proj_kind_t kind, int64_t n, const int64_t* ks, int64_t r) {
+  if (kind != RGC_PROJ_QR_GAUSSIAN || !qr_rank_supported(r) || n <= 0 || n > kQrMaxBatch || !ks) return 0;
+  size_t total = qr_gram_bytes(n, r);
+  for (int64_t m = 0; m < n; ++m) {
+    if (ks[m] <= 0) return 0;
+    total += qr_item_layout(ks[m], r).total;
+  }
+  return total;
+}
 
 }  // namespace
 }  // namespace rgc
@@ -317,39 +465,48 @@ bool qr_rank_supported(int64_t r) { return r == 16 || r == 32 || r == 48 || r ==
 using namespace rgc;
 
 extern "C" size_t rgc_sample_projection_workspace_size(rgc_proj_kind_t kind, int64_t k, int64_t r) {
-  if (kind == RGC_PROJ_RADEMACHER) return 0;
-  if (kind != RGC_PROJ_QR_GAUSSIAN || k <= 0 || !qr_rank_supported(r)) return 0;
-  return qr_layout(k, r).total;
+  return batch_ws(kind, 1, &k, r);
+}
+
+extern "C" size_t rgc_sample_projections_workspace_size(rgc_proj_kind_t kind, int64_t n, const int64_t* ks,
+                                                        int64_t r) {
+  return batch_ws(kind, n, ks, r);
+}
+
+extern "C" rgc_status_t rgc_sample_projections(rgc_proj_kind_t kind, int64_t n, const uint64_t* seeds,
+                                               const int64_t* ks, int64_t r, uint16_t* const* Ps, void* ws,
+                                               size_t ws_bytes, void* stream) {
+  if (n < 0 || n > kQrMaxBatch) return RGC_ERR_UNSUPPORTED;
+  if (n == 0) return RGC_OK;
+  if (!seeds || !ks || !Ps) return RGC_ERR_NULL;
+  for (int64_t m = 0; m < n; ++m) {
+    const rgc_status_t st = check_item(kind, ks[m], r, Ps[m]);
+    if (st != RGC_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kind == RGC_PROJ_RADEMACHER) {
+    const uint32_t mag = rademacher_magnitude(r);
+    for (int64_t m = 0; m < n; ++m) {
+      const int64_t cnt = ks[m] * (r / 8);
+      hipLaunchKernelGGL(rademacher_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, s, Ps[m], ks[m], (int)r,
+                         seeds[m], mag);
+    }
+    return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+  }
+  const size_t need = batch_ws(kind, n, ks, r);
+  if (!ws || ws_bytes < need) return RGC_ERR_WORKSPACE;
+  if (!aligned_to(ws, 256)) return RGC_ERR_ALIGN;
+  switch (r) {
+    case 16: return qr_launch<16>((int)n, seeds, ks, Ps, ws, s);
+    case 32: return qr_launch<32>((int)n, seeds, ks, Ps, ws, s);
+    case 48: return qr_launch<48>((int)n, seeds, ks, Ps, ws, s);
+    case 64: return qr_launch<64>((int)n, seeds, ks, Ps, ws, s);
+    case 128: return qr_launch<128>((int)n, seeds, ks, Ps, ws, s);
+    default: return RGC_ERR_UNSUPPORTED;
+  }
 }
 
 extern "C" rgc_status_t rgc_sample_projection(rgc_proj_kind_t kind, uint64_t seed, int64_t k, int64_t r, uint16_t* P,
                                               void* ws, size_t ws_bytes, void* stream) {
-  if (k <= 0 || r <= 0 || r > k) return RGC_ERR_SHAPE;
-  if (kind != RGC_PROJ_RADEMACHER && kind != RGC_PROJ_QR_GAUSSIAN) return RGC_ERR_UNSUPPORTED;
-  if (!rank_supported(r) || (k % 8) != 0 || k > (int64_t)0xFFFFFFFF) return RGC_ERR_UNSUPPORTED;
-  if (kind == RGC_PROJ_QR_GAUSSIAN && !qr_rank_supported(r)) return RGC_ERR_UNSUPPORTED;
-  if (!P) return RGC_ERR_NULL;
-  if (!aligned16(P)) return RGC_ERR_ALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (kind == RGC_PROJ_RADEMACHER) {
-    // a = bf16(fp32(1/sqrt(r))), both roundings to nearest even
-    const float af = (float)(1.0 / sqrt((double)r));
-    uint32_t b;
-    memcpy(&b, &af, sizeof(b));
-    const uint32_t mag = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-    const int64_t n = k * (r / 8);
-    hipLaunchKernelGGL(rademacher_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, P, k, (int)r, seed, mag);
-    return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
-  }
-  const size_t need = qr_layout(k, r).total;
-  if (!ws || ws_bytes < need) return RGC_ERR_WORKSPACE;
-  if (!aligned_to(ws, 256)) return RGC_ERR_ALIGN;
-  switch (r) {
-    case 16: return qr_launch<16>(seed, k, P, ws, s);
-    case 32: return qr_launch<32>(seed, k, P, ws, s);
-    case 48: return qr_launch<48>(seed, k, P, ws, s);
-    case 64: return qr_launch<64>(seed, k, P, ws, s);
-    case 128: return qr_launch<128>(seed, k, P, ws, s);
-    default: return RGC_ERR_UNSUPPORTED;
-  }
+  return rgc_sample_projections(kind, 1, &seed, &k, r, &P, ws, ws_bytes, stream);
 }

@@ -37,9 +37,18 @@ SIGNATURES = {
     "rgc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "rgc_sample_projection_workspace_size": (_sz, [ctypes.c_int, _i64, _i64]),
     "rgc_sample_projection": (ctypes.c_int, [ctypes.c_int, _u64, _i64, _i64, _vp, _vp, _sz, _vp]),
+    "rgc_sample_projections_workspace_size": (_sz, [ctypes.c_int, _i64, ctypes.POINTER(_i64), _i64]),
+    "rgc_sample_projections": (ctypes.c_int, [ctypes.c_int, _i64, ctypes.POINTER(_u64), ctypes.POINTER(_i64), _i64,
+                                               ctypes.POINTER(_vp), _vp, _sz, _vp]),
     "rgc_project_workspace_size": (_sz, [_i64, _i64, _i64]),
     "rgc_project": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "rgc_project_batch_workspace_size": (_sz, [_i64, ctypes.POINTER(_i64), _i64, _i64]),
+    "rgc_project_batch": (ctypes.c_int, [_i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64),
+                                         ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64, _i64, _vp, _sz, _vp]),
     "rgc_accumulate_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "rgc_accumulate_batch_workspace_size": (_sz, [_i64, ctypes.POINTER(_i64), _i64, _i64]),
+    "rgc_accumulate_batch": (ctypes.c_int, [_i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64),
+                                            ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64, _i64, _vp, _sz, _vp]),
     "rgc_accumulate": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "rgc_apply_workspace_size": (_sz, [_i64, _i64, _i64]),
     "rgc_apply": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _f32, _u64, _vp, _vp, _sz, _vp]),
@@ -112,10 +121,10 @@ def _dense(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
 
 
 class Workspace:
-    """Zero-initialised device scratch for one stream, grown on demand.
+    """Device scratch for the calls ordered on one stream, grown on demand.
 
-    The library leaves the completion counters at the start of a workspace at
-    zero after each call, so one buffer serves every call ordered on a stream.
+    Workspace contents are dead after each call's kernels complete, so one
+    buffer serves every call ordered on a stream.
     """
 
     def __init__(self, device: torch.device):
@@ -126,7 +135,7 @@ class Workspace:
         if nbytes == 0:
             return ctypes.c_void_p(self.buf.data_ptr() if self.buf.numel() else 0), self.buf.numel()
         if self.buf.numel() < nbytes:
-            self.buf = torch.zeros(((nbytes + 4095) // 4096) * 4096, dtype=torch.uint8, device=self.device)
+            self.buf = torch.empty(((nbytes + 4095) // 4096) * 4096, dtype=torch.uint8, device=self.device)
         return ctypes.c_void_p(self.buf.data_ptr()), self.buf.numel()
 
 
@@ -155,6 +164,28 @@ def rgc_sample_projection(kind: str, seed: int, k: int, r: int, out: torch.Tenso
     wp, wn = ws.get(lib.rgc_sample_projection_workspace_size(kid, k, r))
     _check(lib.rgc_sample_projection(kid, seed & 0xFFFFFFFFFFFFFFFF, k, r, out.data_ptr(), wp, wn, _stream(dev)))
     return out
+
+
+def rgc_sample_projections(kind: str, seeds, Ps, workspace: Workspace | None = None):
+    """Fills each P in Ps (k_m x r bf16) as rgc_sample_projection(kind, seeds[m], ...), in one batch."""
+    lib = load_library()
+    n = len(Ps)
+    if n == 0:
+        return Ps
+    dev = _need_gpu(*Ps)
+    r = Ps[0].shape[1]
+    for p in Ps:
+        _dense(p, torch.bfloat16, "P")
+        if p.shape[1] != r:
+            raise RgcError("all projections in a batch share one rank")
+    kid = _KINDS[kind]
+    ks = (_i64 * n)(*[p.shape[0] for p in Ps])
+    sd = (_u64 * n)(*[s & 0xFFFFFFFFFFFFFFFF for s in seeds])
+    ptrs = (_vp * n)(*[p.data_ptr() for p in Ps])
+    ws = workspace or default_workspace(dev)
+    wp, wn = ws.get(lib.rgc_sample_projections_workspace_size(kid, n, ks, r))
+    _check(lib.rgc_sample_projections(kid, n, sd, ks, r, ptrs, wp, wn, _stream(dev)))
+    return Ps
 
 
 def rgc_project(X: torch.Tensor, P: torch.Tensor, out: torch.Tensor | None = None,
@@ -190,6 +221,65 @@ def rgc_accumulate(D: torch.Tensor, XP: torch.Tensor, C: torch.Tensor, workspace
     wp, wn = ws.get(lib.rgc_accumulate_workspace_size(T, d, r))
     _check(lib.rgc_accumulate(D.data_ptr(), ldd, XP.data_ptr(), C.data_ptr(), T, d, r, wp, wn, _stream(dev)))
     return C
+
+
+def _ptrs(ts):
+    return (_vp * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def _i64s(vals):
+    return (_i64 * len(vals))(*vals)
+
+
+def rgc_project_batch(Xs, Ps, outs=None, workspace: Workspace | None = None):
+    """XPs[m] = bf16(Xs[m] Ps[m]) for all m in one launch (one rank, one token count)."""
+    lib = load_library()
+    n = len(Xs)
+    if n == 0:
+        return []
+    dev = _need_gpu(*Xs, *Ps)
+    T = Xs[0].shape[0]
+    r = Ps[0].shape[1]
+    ldxs, ks = [], []
+    for x, p in zip(Xs, Ps):
+        ldxs.append(_rows(x, torch.bfloat16, "X"))
+        _dense(p, torch.bfloat16, "P")
+        if x.shape[0] != T or p.shape[1] != r or p.shape[0] != x.shape[1]:
+            raise RgcError("batch items must share T and r, with P of shape (X.shape[1], r)")
+        ks.append(x.shape[1])
+    if outs is None:
+        outs = [torch.empty((T, r), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    for o in outs:
+        _dense(o, torch.bfloat16, "XP")
+    ws = workspace or default_workspace(dev)
+    wp, wn = ws.get(lib.rgc_project_batch_workspace_size(n, _i64s(ks), T, r))
+    _check(lib.rgc_project_batch(n, _ptrs(Xs), _i64s(ldxs), _i64s(ks), _ptrs(Ps), _ptrs(outs), T, r, wp, wn,
+                                 _stream(dev)))
+    return outs
+
+
+def rgc_accumulate_batch(Ds, XPs, Cs, workspace: Workspace | None = None):
+    """Cs[m] += Ds[m]^T XPs[m] for all m in one launch (one rank, one token count)."""
+    lib = load_library()
+    n = len(Ds)
+    if n == 0:
+        return Cs
+    dev = _need_gpu(*Ds, *XPs, *Cs)
+    T = Ds[0].shape[0]
+    r = XPs[0].shape[1]
+    ldds, ds = [], []
+    for dd, xp, c in zip(Ds, XPs, Cs):
+        ldds.append(_rows(dd, torch.bfloat16, "D"))
+        _dense(xp, torch.bfloat16, "XP")
+        _dense(c, torch.float32, "C")
+        if dd.shape[0] != T or tuple(xp.shape) != (T, r) or tuple(c.shape) != (dd.shape[1], r):
+            raise RgcError("batch items must share T and r: D T x d, XP T x r, C d x r")
+        ds.append(dd.shape[1])
+    ws = workspace or default_workspace(dev)
+    wp, wn = ws.get(lib.rgc_accumulate_batch_workspace_size(n, _i64s(ds), T, r))
+    _check(lib.rgc_accumulate_batch(n, _ptrs(Ds), _i64s(ldds), _i64s(ds), _ptrs(XPs), _ptrs(Cs), T, r, wp, wn,
+                                    _stream(dev)))
+    return Cs
 
 
 def rgc_apply(W: torch.Tensor, C: torch.Tensor, P: torch.Tensor, tau: float, seed: int,

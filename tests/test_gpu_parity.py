@@ -116,6 +116,18 @@ def test_qr_projection_bitexact(dev, k, r, seed):
     assert nbad <= 2
 
 
+def test_batched_projections_equal_single_draws(dev):
+    shapes = [(2048, 1), (1024, 2), (6144, 3), (2048, 2**40 + 4), (4096, 5)]
+    for kind in ("qr", "rademacher"):
+        ps = [torch.empty((k, 64), dtype=torch.bfloat16, device=dev) for k, _ in shapes]
+        rgc.rgc_sample_projections(kind, [s for _, s in shapes], ps)
+        singles = [rgc.rgc_sample_projection(kind, s, k, 64, device=dev).clone() for k, s in shapes]
+        _sync()
+        for a, b in zip(ps, singles):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    _sync()
+
+
 def test_projection_repeatable(dev):
     a = rgc.rgc_sample_projection("qr", 99, 2048, 64, device=dev).clone()
     b = rgc.rgc_sample_projection("qr", 99, 2048, 64, device=dev).clone()
@@ -160,6 +172,36 @@ def test_accumulate_parity(dev, T, d, r):
     err = rel_frobenius(c.cpu().numpy(), ref)
     assert err < 2e-3, err
     assert err < 1e-5, err  # fp32 accumulation: expect ~1e-6
+
+
+def test_project_batch_parity(dev):
+    """The projections of one block in one launch: q/k/v share an X, down has k = 6144."""
+    T, r = 1000, 64
+    xa = synth.normal_bf16((T, 2048), 1.0, seed=31)
+    xd = synth.normal_bf16((T, 6144 + 8), 1.0, seed=32)[:, :6144]
+    ks = [2048, 2048, 2048, 6144]
+    xs = [xa, xa, xa, xd]
+    ps = [synth.normal_bf16((k, r), 1.0, seed=40 + i) for i, k in enumerate(ks)]
+    outs = rgc.rgc_project_batch([x.to(dev) for x in xs], [p.to(dev) for p in ps])
+    _sync()
+    for x, p, o in zip(xs, ps, outs):
+        ref = orc.project(bits(x), bits(p))
+        abs_terms = np.abs(orc.bf16_to_f64(bits(x))) @ np.abs(orc.bf16_to_f64(bits(p)))
+        assert_sum_close(bits(o), ref, abs_terms, what="XP batch")
+
+
+def test_accumulate_batch_parity(dev):
+    T, r = 777, 128
+    ds = [2048, 1024, 1024, 6144, 264]
+    dds = [synth.normal_bf16((T, d), 1e-3, seed=50 + i) for i, d in enumerate(ds)]
+    xps = [synth.normal_bf16((T, r), 3.0, seed=60 + i) for i in range(len(ds))]
+    c0s = [synth.normal_f32((d, r), 1e-3, seed=70 + i) for i, d in enumerate(ds)]
+    cs = [c.clone().to(dev) for c in c0s]
+    rgc.rgc_accumulate_batch([d.to(dev) for d in dds], [x.to(dev) for x in xps], cs)
+    _sync()
+    for dd, xp, c0, c in zip(dds, xps, c0s, cs):
+        ref = orc.accumulate(c0.numpy(), bits(dd), bits(xp))
+        assert rel_frobenius(c.cpu().numpy(), ref) < 1e-5
 
 
 def test_accumulate_empty_microbatch_is_noop(dev):

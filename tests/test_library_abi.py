@@ -117,6 +117,21 @@ def test_projection_validation(lib):
     assert lib.rgc_sample_projection(0, 1, 1024, 64, FAKE + 8, None, 0, s) == ALIGN
 
 
+def test_batched_projection_validation(lib):
+    s = None
+    ks = (ctypes.c_int64 * 2)(1024, 2048)
+    seeds = (ctypes.c_uint64 * 2)(1, 2)
+    ps = (ctypes.c_void_p * 2)(FAKE, FAKE + 8)
+    assert lib.rgc_sample_projections(1, 17, seeds, ks, 64, ps, None, 0, s) == UNSUP  # n > 16
+    assert lib.rgc_sample_projections(1, 0, None, None, 64, None, None, 0, s) == OK
+    assert lib.rgc_sample_projections(1, 2, None, ks, 64, ps, None, 0, s) == NULL
+    assert lib.rgc_sample_projections(1, 2, seeds, ks, 64, ps, None, 0, s) == ALIGN  # second P misaligned
+    ps[1] = FAKE
+    assert lib.rgc_sample_projections(1, 2, seeds, ks, 64, ps, None, 0, s) == WS
+    need = lib.rgc_sample_projections_workspace_size(1, 2, ks, 64)
+    assert need == lib.rgc_sample_projection_workspace_size(1, 1024, 64) + lib.rgc_sample_projection_workspace_size(1, 2048, 64)
+
+
 def test_test_hooks_validation(lib):
     s = None
     assert lib.rgc_test_philox(0, -1, FAKE, FAKE, s) == SHAPE
