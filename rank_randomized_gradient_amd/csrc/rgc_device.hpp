@@ -14,13 +14,37 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
 
+// Global-memory loads at a byte offset from a base pointer. The explicit
+// global address space keeps them global loads (a base rebuilt from scalar
+// registers is otherwise a generic pointer, which turns them into flat
+// loads); a wave-uniform base then stays in scalar registers and the
+// per-lane offset takes one VGPR.
+#define RGC_GLOBAL __attribute__((address_space(1)))
+// The empty asm statement redefines the offset where it is used, so the
+// compiler cannot hoist its widening to 64 bits out of a loop; the address
+// then matches the scalar-base + 32-bit-VGPR-offset form of the load.
+template <typename V>
+__device__ __forceinline__ const RGC_GLOBAL V* global_at(const void* base, uint32_t off) {
+  asm volatile("" : "+v"(off));
+  return (const RGC_GLOBAL V*)((const RGC_GLOBAL char*)base + off);
+}
 // Streaming loads for data read exactly once (nontemporal hint).
-__device__ __forceinline__ u32x4v_t load_stream_16b(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4v_t*>(p));
+__device__ __forceinline__ u32x4v_t load_stream_16b(const void* base, uint32_t off) {
+  return __builtin_nontemporal_load(global_at<u32x4v_t>(base, off));
 }
-__device__ __forceinline__ u32x2v_t load_stream_8b(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x2v_t*>(p));
+__device__ __forceinline__ u32x2v_t load_stream_8b(const void* base, uint32_t off) {
+  return __builtin_nontemporal_load(global_at<u32x2v_t>(base, off));
 }
+// Loads for data that other workgroups read too (kept in cache).
+template <typename V>
+__device__ __forceinline__ V load_cached(const void* base, uint32_t off) {
+  return *global_at<V>(base, off);
+}
+
+// Index of the calling wave within its workgroup, as a wave-uniform (scalar)
+// value, so that branches on it and on values derived from it are scalar
+// branches rather than exec-masked ones.
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 struct u32x4 {
   uint32_t x, y, z, w;
@@ -111,22 +135,6 @@ __device__ __forceinline__ void transpose_8xcpl(const uint32_t (&rows)[8][(CPL +
       out[p] = pick_halves(rows[2 * p][c >> 1], rows[2 * p + 1][c >> 1], sel);
     }
   }
-}
-
-// Cross-workgroup completion: every wave publishes its earlier global stores
-// at device scope (release: they reach memory visible to all XCDs), one
-// thread takes a ticket, and only the workgroup that draws the last ticket
-// acquires (invalidates its stale cached lines) and goes on to read the
-// others' results. No workgroup ever waits for another.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t last_ticket) {
-  __shared__ uint32_t ticket;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (threadIdx.x == 0) ticket = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const bool last = ticket == last_ticket;
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
 }
 
 // Wave-wide sum of a double (64 lanes) with cross-lane shuffles.

@@ -5,7 +5,10 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <type_traits>
+
+#include <hip/hip_runtime.h>
 
 #include "../../include/rgc.h"
 #include "rgc_device.hpp"
@@ -15,6 +18,10 @@ namespace rgc {
 // Per-call limit on the tiled dimension (tokens for project, d for
 // accumulate); keeps every in-kernel offset within 32 bits.
 constexpr int64_t kMaxTiledDim = 65536;
+
+// Limit on the leading dimension of X and D: the kernels address a 64-token
+// (or 32-token) slab of rows with 32-bit byte offsets.
+constexpr int64_t kMaxLeadingDim = int64_t(1) << 24;
 
 // Tiling of the rank dimension r (a multiple of 16, at most 64, or a multiple
 // of 64 up to 256). A wave covers RPW rank columns in NG groups of GW columns;
@@ -58,6 +65,18 @@ bool dispatch_rank(int64_t r, F&& f) {
 
 inline bool aligned_to(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 inline bool aligned16(const void* p) { return aligned_to(p, 16); }
+
+// Compute units of the current device (cached per device; 256 if unknown).
+inline int device_compute_units() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  static std::atomic<int> cache[64];
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
 
 inline int env_int(const char* name, int dflt) {
   const char* v = getenv(name);

@@ -5,28 +5,37 @@
 // ([RGC] = page "Randomized Gradient Compression"; [LoGRA-S] = page "LoGRA:
 // Scaling LLM Reinforcement Learning with Low-Rank Gradient Sketches".)
 //
-// Both kernels put the rank dimension r on the MFMA's M side. Its operand
-// (P or XP) is read with a register transpose: a lane loads CPL consecutive r
-// columns for eight consecutive K rows and repacks them, so M-tile c row m
-// is r = base + CPL*m + c. With that ordering each lane's output is a
-// contiguous run of 4*CPL values of r, which is what makes the stores
-// (XP rows, C rows) contiguous.
+// Both are GEMMs with a long K (k, or tokens), a short M (the rank r) and an N
+// (tokens, or d) whose operand is read from HBM exactly once: the "stream"
+// operand (X or D) carries nearly all the bytes, the "rank" operand (P or XP)
+// is small and re-read from L2 by every N-tile. At r <= 128 they are
+// HBM-bound, so the design is about keeping enough stream bytes in flight:
 //
-// Both are HBM-bound at the ranks of interest (a few flops per byte), so the
-// loops are written for memory-level parallelism: every load is unconditional
-// (out-of-range rows are clamped to a valid address and their values zeroed),
-// addresses are 32-bit offsets from workgroup-uniform bases, and the next
-// K-step's loads are issued before the current step's MFMAs.
-//
-// Work is split over K (k for project, tokens for accumulate) first across the
-// waves of a workgroup (summed through LDS, each wave finishing the N-tiles it
-// owns) and then, when the output alone has too few tiles to fill the chip,
-// across workgroups: each writes an output-shaped fp32 partial and a second,
-// fully parallel launch sums the partials in split order. Both reductions
-// have a fixed order, so results are bit-reproducible. There is no
-// cross-workgroup signalling inside a launch: a device-scope release costs an
-// L2 writeback per wave on this part, which serializes across hundreds of
-// workgroups, while the launch boundary orders the partials for free.
+// * A wave computes a 64 (N) x RPW (r) tile: four 16x16 MFMA N-tiles per
+//   M-tile. A workgroup of NR x KS waves covers all of r and splits each
+//   K-block of 32*KS rows among its KS waves (summed through LDS at the end
+//   of a tile).
+// * The rank operand's register transpose puts r on the MFMA's M side: a lane
+//   loads CPL consecutive r columns for eight consecutive K rows and repacks
+//   them, so M-tile c row m is r = base + CPL*m + c and each lane's output is
+//   a contiguous run of 4*CPL values of r (contiguous C and XP stores). D is
+//   token-major, so it gets the same transpose on the N side: lane (n, g)
+//   reads d = 4n .. 4n+3 of eight tokens and N-tile c column n is d = 4n + c.
+// * Each wave keeps the loads of its next two K-steps in flight while it
+//   multiplies the current one (three register stages). Loads are
+//   unconditional: out-of-range rows are clamped to valid memory and zeroed
+//   only in the last, partial K-step; addresses are a scalar base plus a
+//   per-lane 32-bit offset that is fixed for the whole loop.
+// * Work is balanced across the chip at K-block granularity ("stream-K"):
+//   the (item, tile, K-block) units of the whole batch are cut into one
+//   contiguous range per workgroup, one workgroup per compute unit. A tile that lies inside one
+//   range is finished in place; a tile cut between ranges gets fp32 partials
+//   (at most two per workgroup) that a second launch sums in workgroup order.
+//   Every reduction has a fixed order, so results are bit-reproducible, and
+//   there is no signalling between workgroups inside a launch (a device-scope
+//   release costs an L2 writeback per wave on this part). Consecutive ranges
+//   are placed on the same XCD, so the tiles of one item share that XCD's L2
+//   for the rank operand.
 #include "rgc_internal.hpp"
 
 namespace rgc {
@@ -35,47 +44,95 @@ namespace rgc {
 // Shared pieces
 // ---------------------------------------------------------------------------
 
-// Raw (untransposed) M-side rows of one 32-row K-step: for each column group
-// q and row j = 0..7, the CPL columns the lane reads, packed in dwords.
+// A K-step covers 32 rows of the K dimension. Its operands are read through a
+// window of 32 rows [wb, wb + 32): in the steady state wb is the step's own
+// first row k0; for the last, partial step (and for prefetches past the end)
+// the window is moved back to end at the K extent, so that every row it
+// touches is valid memory, and rows outside [k0, end) are zeroed before use.
+// A K extent below 32 clamps the lanes' row offsets once, up front.
+__device__ __forceinline__ int64_t window_base(int64_t k0, int64_t end) {
+  return k0 + 32 <= end ? k0 : (end >= 32 ? end - 32 : 0);
+}
+
+// Rows of a window that are valid memory for a K extent `end`.
+__device__ __forceinline__ int64_t window_rows(int64_t end) { return end >= 32 ? 32 : end; }
+
+// Pins a wave-uniform value to scalar registers. Without it the compiler may
+// strength-reduce every load address of the K loop into its own 64-bit
+// per-lane induction variable, which costs two VGPRs per load in flight.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  return reinterpret_cast<const uint16_t*>(uniform_u64(reinterpret_cast<uint64_t>(p)));
+}
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) { return (int64_t)uniform_u64((uint64_t)v); }
+
+// Raw (untransposed) M-side rows of one K-step: for each column group q and
+// row j = 0..7, the CPL columns the lane reads, packed in dwords.
 template <int R>
 struct RankRows {
   static constexpr int W = (RankTraits<R>::CPL + 1) / 2;
   uint32_t v[RankTraits<R>::NG][8][W];
 };
 
-// Loads rows krow0 + 8g + j (j = 0..7) of a row-major bf16 matrix with
-// compile-time row stride R (src already points at the wave's first column),
-// columns q*GW + CPL*m .. +CPL-1, for a lane (m = lane % 16, g = lane / 16).
-// Rows >= nrows read row nrows-1 and are zeroed.
+// Per-lane byte offsets of eight rows, relative to a window's first row.
+struct RowOffsets {
+  uint32_t off[8];
+};
+
+// Rows 8g + j (j = 0..7) of a row-major bf16 matrix with row stride R, at
+// columns CPL*m (m = lane % 16, g = lane / 16), clamped into `rows` rows.
 template <int R>
-__device__ __forceinline__ void load_rank_rows(const uint16_t* __restrict__ src, int64_t krow0, int64_t nrows,
-                                               int lane, RankRows<R>& out) {
-  using Tr = RankTraits<R>;
-  constexpr int CPL = Tr::CPL;
+__device__ __forceinline__ RowOffsets rank_row_offsets(int lane, int64_t rows) {
+  constexpr int CPL = RankTraits<R>::CPL;
   const int m = lane & 15, g = lane >> 4;
-  const int64_t base_row = krow0 < nrows ? krow0 : nrows - 1;  // uniform
-  const uint16_t* base = src + base_row * R + CPL * m;
-  const int64_t room = nrows - 1 - base_row;  // rows available after base_row
+  RowOffsets o;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int64_t want = krow0 + 8 * g + j - base_row;
-    const bool ok = krow0 + 8 * g + j < nrows;
-    const uint32_t off = (uint32_t)((want < room ? want : room) * R);
+    const int64_t row = 8 * g + j < rows ? 8 * g + j : rows - 1;
+    o.off[j] = (uint32_t)((row * R + CPL * m) * 2);
+  }
+  return o;
+}
+
+// Loads a K-step's rank rows; `win` points at the window's first row and the
+// wave's first column. The rank operand is re-read by every N-tile, so these
+// loads keep the default (cached) policy.
+template <int R>
+__device__ __forceinline__ void load_rank_rows(const uint16_t* win, const RowOffsets& o, RankRows<R>& out) {
+  using Tr = RankTraits<R>;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
 #pragma unroll
     for (int q = 0; q < Tr::NG; ++q) {
-      const uint16_t* p = base + off + q * Tr::GW;
-      if constexpr (CPL == 4) {
-        const uint2 v = *reinterpret_cast<const uint2*>(p);
-        out.v[q][j][0] = ok ? v.x : 0u;
-        out.v[q][j][1] = ok ? v.y : 0u;
-      } else if constexpr (CPL == 2) {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
-        out.v[q][j][0] = ok ? v : 0u;
+      const uint32_t off = o.off[j] + q * Tr::GW * 2;
+      if constexpr (Tr::CPL == 4) {
+        const u32x2v_t v = load_cached<u32x2v_t>(win, off);
+        out.v[q][j][0] = v.x;
+        out.v[q][j][1] = v.y;
+      } else if constexpr (Tr::CPL == 2) {
+        out.v[q][j][0] = load_cached<uint32_t>(win, off);
       } else {
-        const uint32_t v = *p;
-        out.v[q][j][0] = ok ? v : 0u;
+        out.v[q][j][0] = load_cached<uint16_t>(win, off);
       }
     }
+}
+
+// Zeroes the rows of a window that lie outside [k0, end).
+template <int R>
+__device__ __forceinline__ void mask_rank_rows(int64_t wb, int64_t k0, int64_t end, int lane, RankRows<R>& rows) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t row = wb + 8 * g + j;
+    const bool ok = row >= k0 && row < end;
+#pragma unroll
+    for (int q = 0; q < RankTraits<R>::NG; ++q)
+#pragma unroll
+      for (int w = 0; w < RankRows<R>::W; ++w) rows.v[q][j][w] = ok ? rows.v[q][j][w] : 0u;
   }
 }
 
@@ -88,46 +145,59 @@ __device__ __forceinline__ void transpose_rank_rows(const RankRows<R>& rows, uin
     for (int c = 0; c < Tr::CPL; ++c) transpose_8xcpl<Tr::CPL>(rows.v[q], c, aop[q * Tr::CPL + c]);
 }
 
-// Gathers, for N-tile `nt` and column group q, the 4*CPL contiguous rank
-// values a lane owns: out[CPL*i + c] = acc[q*CPL + c][nt][i].
+// N-tiles (16 columns each) per wave, and the workgroup's N extent.
+constexpr int kNT = 4;
+constexpr int kTileN = 16 * kNT;
+
+// The register budget (at most 256 VGPRs + AGPRs per wave) and the LDS of
+// the wave reduction are sized so that two workgroups fit on a compute unit.
+constexpr int kWorkgroupsPerCU = 2;
+
+// K-steps in flight per wave: the loads of step s + kStages - 1 are issued
+// before step s is multiplied. The stage buffers are indexed with
+// compile-time constants in an unrolled loop, so rotating them costs no
+// register copies (and no early waits).
+// (Two for r = 48, whose rank operand takes three column groups of 16-bit
+// loads and would not fit three stages in the register budget.)
 template <int R>
-__device__ __forceinline__ void gather_rank_run(const f32x4_t (&acc)[RankTraits<R>::MT][4], int q, int nt,
-                                                float (&out)[4 * RankTraits<R>::CPL]) {
-  constexpr int CPL = RankTraits<R>::CPL;
-#pragma unroll
-  for (int c = 0; c < CPL; ++c)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[CPL * i + c] = acc[q * CPL + c][nt][i];
-}
+constexpr int stages() { return R == 48 ? 2 : 3; }
 
-__device__ __forceinline__ int g_of(int lane) { return lane >> 4; }
+template <int R>
+using AccTile = f32x4_t[RankTraits<R>::MT][kNT];
 
-// The four N-tiles of a wave's output are split among the KS waves that share
-// an r-slice: wave ks owns N-tiles nt with nt % KS == ks, and after the
-// reductions below it holds the finished sums for exactly those.
+// The N-tiles of a wave's output are split among the KS waves that share an
+// r-slice: wave ks owns N-tiles nt with nt % KS == ks, and after the
+// reduction below it holds the finished sums for exactly those.
 template <int KS>
 __device__ __forceinline__ constexpr bool owns_ntile(int nt, int ks) { return (nt % KS) == ks; }
 
+template <int R>
+constexpr int reduce_lds_floats() {
+  using Tr = RankTraits<R>;
+  return Tr::KS > 1 ? Tr::KS * Tr::NR * Tr::MT * kNT * 4 * 64 : 1;
+}
+
 // Sums the KS waves' accumulators through LDS: every wave stores all of its
 // tile, then each wave adds, for the N-tiles it owns, the KS copies in wave
-// order (fixed order, so the result does not depend on timing).
-// `lds` holds KS * NR * MT * 16 * 64 floats.
-template <int R, int KS>
-__device__ __forceinline__ void reduce_waves(f32x4_t (&acc)[RankTraits<R>::MT][4], float* lds, int rw, int ks,
-                                             int lane) {
+// order (fixed order, so the result does not depend on timing). The leading
+// barrier lets the LDS be reused from one tile to the next.
+template <int R>
+__device__ __forceinline__ void reduce_waves(AccTile<R>& acc, float* lds, int rw, int ks, int lane) {
   using Tr = RankTraits<R>;
-  constexpr int E = Tr::MT * 16;  // floats per lane
+  constexpr int KS = Tr::KS;
+  constexpr int E = Tr::MT * kNT * 4;  // floats per lane
   if constexpr (KS > 1) {
+    __syncthreads();
     float* mine = lds + (ks * Tr::NR + rw) * E * 64;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
       for (int mt = 0; mt < Tr::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mine[((nt * Tr::MT + mt) * 4 + i) * 64 + lane] = acc[mt][nt][i];
     __syncthreads();
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < kNT; ++nt) {
       if (!owns_ntile<KS>(nt, ks)) continue;
 #pragma unroll
       for (int mt = 0; mt < Tr::MT; ++mt)
@@ -145,340 +215,485 @@ __device__ __forceinline__ void reduce_waves(f32x4_t (&acc)[RankTraits<R>::MT][4
   }
 }
 
-// Writes the 4*CPL-wide rank runs of the N-tiles this wave owns to an fp32
-// row-major buffer with row stride R (an output-shaped split partial). Rows of
-// N-tile nt: TOKEN_ROWS (project) row0 + 16*nt + n, else (accumulate)
-// row0 + 4*n + nt.
-template <int R, int KS, bool TOKEN_ROWS>
-__device__ __forceinline__ void store_runs_f32(const f32x4_t (&acc)[RankTraits<R>::MT][4], float* __restrict__ out,
-                                               int64_t row0, int64_t nrows, int rbase, int ks, int lane) {
-  using Tr = RankTraits<R>;
-  const int n = lane & 15, g = lane >> 4;
+// Gathers, for N-tile `nt` and column group q, the 4*CPL contiguous rank
+// values a lane owns: out[CPL*i + c] = acc[q*CPL + c][nt][i], which are
+// r = base + q*GW + 4*CPL*g + (0 .. 4*CPL-1).
+template <int R>
+__device__ __forceinline__ void gather_rank_run(const AccTile<R>& acc, int q, int nt,
+                                                float (&out)[4 * RankTraits<R>::CPL]) {
+  constexpr int CPL = RankTraits<R>::CPL;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int64_t row = TOKEN_ROWS ? row0 + 16 * nt + n : row0 + 4 * n + nt;
-    if (!owns_ntile<KS>(nt, ks) || row >= nrows) continue;
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[CPL * i + c] = acc[q * CPL + c][nt][i];
+}
+
+// Calls f(row, q, run) for every N-tile this wave owns in a finished tile:
+// `row` is the tile-relative N index of the lane's column, row_of(nt, n),
+// and run holds the lane's 4*CPL consecutive rank values of column group q,
+// which start at r = rbase + q*GW + 4*CPL*g.
+template <int R, typename RowOf, typename F>
+__device__ __forceinline__ void for_owned_runs(const AccTile<R>& acc, int ks, int lane, RowOf row_of, F f) {
+  using Tr = RankTraits<R>;
+  const int n = lane & 15;
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) {
+    if (!owns_ntile<Tr::KS>(nt, ks)) continue;
 #pragma unroll
     for (int q = 0; q < Tr::NG; ++q) {
       float run[4 * Tr::CPL];
       gather_rank_run<R>(acc, q, nt, run);
-      float4* dst = reinterpret_cast<float4*>(out + row * R + rbase + q * Tr::GW + 4 * Tr::CPL * g);
-#pragma unroll
-      for (int v = 0; v < Tr::CPL; ++v) dst[v] = make_float4(run[4 * v], run[4 * v + 1], run[4 * v + 2], run[4 * v + 3]);
+      f(row_of(nt, n), q, run);
     }
   }
 }
 
+template <int CPL>
+__device__ __forceinline__ void store_run_f32(float* dst, const float (&run)[4 * CPL]) {
+#pragma unroll
+  for (int v = 0; v < CPL; ++v)
+    reinterpret_cast<float4*>(dst)[v] = make_float4(run[4 * v], run[4 * v + 1], run[4 * v + 2], run[4 * v + 3]);
+}
+
+template <int CPL>
+__device__ __forceinline__ void add_run_f32(float* dst, const float (&run)[4 * CPL]) {
+#pragma unroll
+  for (int v = 0; v < CPL; ++v) {
+    float4 old = reinterpret_cast<float4*>(dst)[v];
+    old.x += run[4 * v + 0];
+    old.y += run[4 * v + 1];
+    old.z += run[4 * v + 2];
+    old.w += run[4 * v + 3];
+    reinterpret_cast<float4*>(dst)[v] = old;
+  }
+}
+
+template <int CPL>
+__device__ __forceinline__ void store_run_bf16(uint16_t* dst, const float (&run)[4 * CPL]) {
+  uint32_t packed[2 * CPL];
+#pragma unroll
+  for (int e = 0; e < 2 * CPL; ++e) packed[e] = pack_bf16x2(f32_to_bf16_rne(run[2 * e]), f32_to_bf16_rne(run[2 * e + 1]));
+  if constexpr (CPL == 4) {
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    reinterpret_cast<uint4*>(dst)[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  } else if constexpr (CPL == 2) {
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  } else {
+    reinterpret_cast<uint2*>(dst)[0] = make_uint2(packed[0], packed[1]);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Work-item tables: one launch covers a list of independent matrices of one
-// rank (e.g. all projections of a transformer block). Workgroup b belongs to
-// the item whose [wg_begin, wg_begin') range holds b.
+// Work items and the stream-K schedule. One launch covers a list of
+// independent matrices of one rank (e.g. all projections of a transformer
+// block). Units are (item, N-tile, K-block) in that order; workgroup w takes
+// units [floor(w U / G), floor((w+1) U / G)).
 // ---------------------------------------------------------------------------
 constexpr int kMaxItems = 16;
+constexpr int kNumXcds = 8;
 
-__device__ __forceinline__ int item_of(const int* begin, int n, int b) {
+struct Schedule {
+  int n;                          // items
+  int G;                          // workgroups
+  int64_t U;                      // units
+  int64_t ubase[kMaxItems + 1];   // first unit of each item
+  int64_t nkb[kMaxItems];         // K-blocks per tile
+  int64_t tbase[kMaxItems + 1];   // first (batch-wide) tile index of each item
+  int64_t kext[kMaxItems];        // K extent
+  int64_t next[kMaxItems];        // N extent
+};
+
+__device__ __forceinline__ int64_t range_begin(const Schedule& s, int64_t w) { return w * s.U / s.G; }
+
+// The workgroup whose range holds unit u: the largest w with
+// range_begin(w) <= u.
+__device__ __forceinline__ int64_t range_of(const Schedule& s, int64_t u) { return ((u + 1) * s.G - 1) / s.U; }
+
+__device__ __forceinline__ int item_of_unit(const Schedule& s, int64_t u) {
   int m = 0;
-  while (m + 1 < n && b >= begin[m + 1]) ++m;
+  while (m + 1 < s.n && u >= s.ubase[m + 1]) ++m;
   return m;
 }
 
+__device__ __forceinline__ int item_of_tile(const Schedule& s, int64_t t) {
+  int m = 0;
+  while (m + 1 < s.n && t >= s.tbase[m + 1]) ++m;
+  return m;
+}
+
+// The hardware hands workgroups to the XCDs round-robin; this numbers them
+// so that each XCD gets a contiguous run of ranges.
+__device__ __forceinline__ int64_t logical_workgroup(int64_t b, int64_t G) {
+  const int64_t x = b % kNumXcds, pos = b / kNumXcds;
+  const int64_t q = G / kNumXcds, rem = G % kNumXcds;
+  return x * q + (x < rem ? x : rem) + pos;
+}
+
+// Partial slots: a workgroup's first segment (if it is a partial tile) goes
+// to slot 2w, its last (if partial and not also the first) to slot 2w + 1.
+__device__ __forceinline__ int64_t partial_slot(int64_t w, bool first_segment) {
+  return 2 * w + (first_segment ? 0 : 1);
+}
+
 struct ProjectBatch {
-  int n;
-  int64_t T, tiles;                 // tokens (shared) and 64-token tiles per item
-  int wg_begin[kMaxItems + 1];      // tiles * splits workgroups per item
+  Schedule s;
   const uint16_t* X[kMaxItems];
   int64_t ldx[kMaxItems];
-  int64_t k[kMaxItems];
   const uint16_t* P[kMaxItems];
   uint16_t* XP[kMaxItems];
-  int64_t kchunk[kMaxItems];
-  int splits[kMaxItems];
-  float* part[kMaxItems];           // splits x T x R fp32 when splits > 1
+  float* part;                    // 2 G slots of kTileN x R fp32
 };
 
 struct AccumulateBatch {
-  int n;
-  int64_t T, tchunk;                // tokens and tokens per split (shared)
-  int splits;
-  int wg_begin[kMaxItems + 1];      // tiles * splits workgroups per item
+  Schedule s;
   const uint16_t* D[kMaxItems];
   int64_t ldd[kMaxItems];
-  int64_t d[kMaxItems];
-  int64_t tiles[kMaxItems];
   const uint16_t* XP[kMaxItems];
   float* C[kMaxItems];
-  float* part[kMaxItems];           // splits x d x R fp32 when splits > 1
+  float* part;                    // 2 G slots of kTileN x R fp32
 };
 
-// ---------------------------------------------------------------------------
-// project: XP = bf16(X P)
-// Workgroup = (item, 64-token tile, k-split); its NR x KS waves take r-slices
-// x interleaved K-steps.
-// ---------------------------------------------------------------------------
-struct XRows {
-  uint32_t v[4][4];  // per N-tile: 8 consecutive k of one token (16 bytes)
-};
-
-__device__ __forceinline__ void load_x_rows(const uint16_t* __restrict__ X, int64_t ldx, int64_t T, int64_t tbase,
-                                            int64_t k0, int64_t kend, int lane, XRows& out) {
-  const int n = lane & 15, g = lane >> 4;
-  const int64_t kc = k0 + 8 * g;
-  const bool kok = kc < kend;
-  const int64_t kcl = kok ? kc : kend - 8;  // kend is a multiple of 8
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int64_t t = tbase + 16 * nt + n;
-    const bool ok = kok && t < T;
-    const int64_t tc = t < T ? t : T - 1;
-    const u32x4v_t v = load_stream_16b(X + tc * ldx + kcl);
-    out.v[nt][0] = ok ? v.x : 0u;
-    out.v[nt][1] = ok ? v.y : 0u;
-    out.v[nt][2] = ok ? v.z : 0u;
-    out.v[nt][3] = ok ? v.w : 0u;
-  }
-}
-
-template <int R>
-__global__ __launch_bounds__(256) void project_kernel(ProjectBatch pb) {
+// Runs the workgroup's range: for each segment (a run of K-blocks of one
+// tile) calls begin(m, tile), then load(stage, k0) / step(stage, k0, masked)
+// for its K-steps, then finish(m, tile, full, slot) with the tile's sums in
+// acc (reduced across the KS waves). Steps whose K-block lies wholly inside
+// the K extent run without any masking; only the epilogue, which holds the
+// last (possibly partial) K-block, checks.
+template <int R, typename Stage, typename Begin, typename Load, typename Step, typename Finish>
+__device__ __forceinline__ void run_range(const Schedule& s, int64_t w, int ks, float* lds, int rw, int lane,
+                                          AccTile<R>& acc, Begin begin, Load load, Step step, Finish finish) {
   using Tr = RankTraits<R>;
-  constexpr int KS = Tr::KS;
-  __shared__ float lds[KS > 1 ? KS * Tr::NR * Tr::MT * 16 * 64 : 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rw = wave % Tr::NR, ks = wave / Tr::NR;
-  const int rbase = rw * Tr::RPW;
-  const int n = lane & 15, g = lane >> 4;
-  const int m = item_of(pb.wg_begin, pb.n, blockIdx.x);
-  const int local = blockIdx.x - pb.wg_begin[m];
-  const int64_t T = pb.T;
-  const int64_t tbase = (int64_t)(local % pb.tiles) * 64;
-  const int split = (int)(local / pb.tiles);
-  const int splits = pb.splits[m];
-  const int64_t k = pb.k[m], kchunk = pb.kchunk[m];
-  const int64_t kbeg = split * kchunk;
-  const int64_t kend = kbeg + kchunk < k ? kbeg + kchunk : k;
-  const uint16_t* X = pb.X[m];
-  const int64_t ldx = pb.ldx[m];
-  const uint16_t* P = pb.P[m] + rbase;
-
-  f32x4_t acc[Tr::MT][4];
-#pragma unroll
-  for (int mt = 0; mt < Tr::MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  int64_t k0 = kbeg + 32 * ks;
-  RankRows<R> pa;
-  XRows xb;
-  load_rank_rows<R>(P, k0, kend, lane, pa);
-  load_x_rows(X, ldx, T, tbase, k0, kend, lane, xb);
-  for (; k0 < kend; k0 += 32 * KS) {
-    RankRows<R> pn;
-    XRows xn;
-    load_rank_rows<R>(P, k0 + 32 * KS, kend, lane, pn);
-    load_x_rows(X, ldx, T, tbase, k0 + 32 * KS, kend, lane, xn);
-    uint32_t aop[Tr::MT][4];
-    transpose_rank_rows<R>(pa, aop);
+  constexpr int64_t stride = 32 * Tr::KS;
+  const int64_t u0 = uniform_i64(range_begin(s, w)), u1 = uniform_i64(range_begin(s, w + 1));
+  constexpr int kStages = stages<R>();
+  Stage st[kStages];
+  for (int64_t u = u0; u < u1;) {
+    const int m = item_of_unit(s, u);
+    const int64_t nkb = s.nkb[m];
+    const int64_t tile = (u - s.ubase[m]) / nkb, kb0 = (u - s.ubase[m]) % nkb;
+    const int64_t tile_end = s.ubase[m] + (tile + 1) * nkb;
+    const int64_t seg_end = u1 < tile_end ? u1 : tile_end;
+    const int64_t kb1 = kb0 + (seg_end - u);
+    const int64_t kb_full = s.kext[m] / stride;  // K-blocks wholly inside the K extent
+    const int64_t nfull = (kb1 < kb_full ? kb1 : kb_full) - kb0;
+    begin(m, tile);
 #pragma unroll
     for (int mt = 0; mt < Tr::MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_16x16x32(aop[mt], xb.v[nt], acc[mt][nt]);
-    pa = pn;
-    xb = xn;
-  }
-
-  reduce_waves<R, KS>(acc, lds, rw, ks, lane);
-  if (splits > 1) {  // output-shaped fp32 partial (T x R) for the finishing pass
-    store_runs_f32<R, KS, true>(acc, pb.part[m] + (int64_t)split * T * R, tbase, T, rbase, ks, lane);
-    return;
-  }
-  uint16_t* XP = pb.XP[m];
+      for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // this wave's K-steps start at rows kb*32*KS + 32*ks, kb in [kb0, kb1)
+    const int64_t first = kb0 * stride + 32 * ks;
+    const int64_t nsteps = kb1 - kb0;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int64_t t = tbase + 16 * nt + n;
-    if (!owns_ntile<KS>(nt, ks) || t >= T) continue;
+    for (int v = 0; v + 1 < kStages; ++v) load(st[v], first + v * stride);
+    int64_t s0 = 0;
+    for (; s0 + kStages <= nfull; s0 += kStages) {
 #pragma unroll
-    for (int q = 0; q < Tr::NG; ++q) {
-      float run[4 * Tr::CPL];
-      gather_rank_run<R>(acc, q, nt, run);
-      uint16_t* dst = XP + t * R + rbase + q * Tr::GW + 4 * Tr::CPL * g;
-      uint32_t packed[2 * Tr::CPL];
-#pragma unroll
-      for (int e = 0; e < 2 * Tr::CPL; ++e)
-        packed[e] = pack_bf16x2(f32_to_bf16_rne(run[2 * e]), f32_to_bf16_rne(run[2 * e + 1]));
-      if constexpr (Tr::CPL == 4) {
-        reinterpret_cast<uint4*>(dst)[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        reinterpret_cast<uint4*>(dst)[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-      } else if constexpr (Tr::CPL == 2) {
-        reinterpret_cast<uint4*>(dst)[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      } else {
-        reinterpret_cast<uint2*>(dst)[0] = make_uint2(packed[0], packed[1]);
+      for (int v = 0; v < kStages; ++v) {
+        const int64_t k0 = first + (s0 + v) * stride;
+        load(st[(v + kStages - 1) % kStages], k0 + (kStages - 1) * stride);
+        // Keep each step's transposes and MFMAs between its own loads and
+        // the next step's: hoisting the next step's transposes (which the
+        // scheduler likes for ILP) would wait for data still in flight.
+        __builtin_amdgcn_sched_barrier(0);
+        step(st[v], k0, std::false_type{});
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // at most kStages steps remain: the stages hold steps s0 .. s0+kStages-2
+#pragma unroll
+    for (int v = 0; v < kStages; ++v) {
+      if (s0 + v >= nsteps) break;
+      const int64_t k0 = first + (s0 + v) * stride;
+      if (v == kStages - 1) load(st[v], k0);
+      step(st[v], k0, std::true_type{});
+    }
+    reduce_waves<R>(acc, lds, rw, ks, lane);
+    finish(m, tile, kb0 == 0 && kb1 == nkb, partial_slot(w, u == u0));
+    u = seg_end;
   }
 }
 
 // ---------------------------------------------------------------------------
-// accumulate: C += D^T XP
-// Workgroup = (item, 64-row d tile, token split); its NR x KS waves take
-// r-slices x interleaved 32-token steps. D is token-major, so its operand is
-// also transposed in registers: lane (n, g) reads 4 consecutive d for eight
-// tokens, and N-tile c column n is d = dbase + 4n + c.
+// project: XP = bf16(X P). N = tokens (N-tile nt column n is token
+// tbase + 16*nt + n), K = k.
+// ---------------------------------------------------------------------------
+struct XRows {
+  uint32_t v[kNT][4];  // per N-tile: 8 consecutive k of one token (16 bytes)
+};
+
+// Per-lane byte offsets, relative to (token tbase, window column), of the 16
+// bytes lane (n, g) reads for N-tile nt: token tbase + 16*nt + n (tokens past
+// T read token T-1; their outputs are never stored), k chunk 8g (clamped into
+// a window of `rows` valid columns; rows is a multiple of 8).
+struct XOffsets {
+  uint32_t off[kNT];
+};
+
+__device__ __forceinline__ XOffsets x_offsets(int lane, int64_t T, int64_t tbase, int64_t ldx, int64_t rows) {
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t kc = 8 * g + 8 <= rows ? 8 * g : rows - 8;
+  XOffsets o;
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) {
+    const int64_t t = tbase + 16 * nt + n;
+    const int64_t tc = t < T ? t : T - 1;
+    o.off[nt] = (uint32_t)(((tc - tbase) * ldx + kc) * 2);
+  }
+  return o;
+}
+
+__device__ __forceinline__ void load_x_rows(const uint16_t* win, const XOffsets& o, XRows& out) {
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) {
+    const u32x4v_t v = load_stream_16b(win, o.off[nt]);
+    out.v[nt][0] = v.x;
+    out.v[nt][1] = v.y;
+    out.v[nt][2] = v.z;
+    out.v[nt][3] = v.w;
+  }
+}
+
+// Zeroes the 8-wide k chunks of a window that lie outside [k0, end).
+__device__ __forceinline__ void mask_x_rows(int64_t wb, int64_t k0, int64_t end, int lane, XRows& x) {
+  const int64_t c0 = wb + 8 * (lane >> 4);
+  const bool ok = c0 >= k0 && c0 < end;
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x.v[nt][e] = ok ? x.v[nt][e] : 0u;
+}
+
+template <int R>
+__global__ __launch_bounds__(64 * RankTraits<R>::NR * RankTraits<R>::KS, kWorkgroupsPerCU) void project_kernel(
+    ProjectBatch pb) {
+  using Tr = RankTraits<R>;
+  __shared__ float lds[reduce_lds_floats<R>()];
+  const int lane = threadIdx.x & 63, wave = wave_index();
+  const int rw = wave % Tr::NR, ks = wave / Tr::NR;
+  const int rbase = rw * Tr::RPW;
+  const int g = lane >> 4;
+  const Schedule& s = pb.s;
+  const int64_t w = logical_workgroup(blockIdx.x, s.G);
+  const int64_t T = s.next[0];
+
+  struct Stage {
+    RankRows<R> p;
+    XRows x;
+  };
+  AccTile<R> acc;
+  int64_t kend = 0, tbase = 0;
+  const uint16_t* Xt = nullptr;
+  const uint16_t* P = nullptr;
+  RowOffsets po;
+  XOffsets xo;
+  auto begin = [&](int m, int64_t tile) {
+    kend = uniform_i64(s.kext[m]);
+    tbase = tile * kTileN;
+    const int64_t ldx = pb.ldx[m];
+    Xt = uniform_ptr(pb.X[m] + tbase * ldx);
+    P = uniform_ptr(pb.P[m] + rbase);
+    po = rank_row_offsets<R>(lane, window_rows(kend));
+    xo = x_offsets(lane, T, tbase, ldx, window_rows(kend));
+  };
+  auto load = [&](Stage& b, int64_t k0) {
+    const int64_t wb = window_base(k0, kend);
+    load_rank_rows<R>(uniform_ptr(P + wb * R), po, b.p);
+    load_x_rows(uniform_ptr(Xt + wb), xo, b.x);
+  };
+  auto step = [&](Stage& b, int64_t k0, auto masked) {
+    if (masked && k0 + 32 > kend) {  // the last, partial K-step (wave-uniform)
+      const int64_t wb = window_base(k0, kend);
+      mask_rank_rows<R>(wb, k0, kend, lane, b.p);
+      mask_x_rows(wb, k0, kend, lane, b.x);
+    }
+    uint32_t aop[Tr::MT][4];
+    transpose_rank_rows<R>(b.p, aop);
+#pragma unroll
+    for (int mt = 0; mt < Tr::MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = mfma_16x16x32(aop[mt], b.x.v[nt], acc[mt][nt]);
+  };
+  auto finish = [&](int m, int64_t tile, bool full, int64_t slot) {
+    const auto row_of = [](int nt, int n) { return 16 * nt + n; };
+    if (full) {
+      uint16_t* XP = pb.XP[m];
+      for_owned_runs<R>(acc, ks, lane, row_of, [&](int row, int q, const float (&run)[4 * Tr::CPL]) {
+        if (tbase + row < T)
+          store_run_bf16<Tr::CPL>(XP + (tbase + row) * R + rbase + q * Tr::GW + 4 * Tr::CPL * g, run);
+      });
+    } else {
+      float* part = pb.part + slot * (int64_t)kTileN * R;
+      for_owned_runs<R>(acc, ks, lane, row_of, [&](int row, int q, const float (&run)[4 * Tr::CPL]) {
+        store_run_f32<Tr::CPL>(part + row * R + rbase + q * Tr::GW + 4 * Tr::CPL * g, run);
+      });
+    }
+  };
+  run_range<R, Stage>(s, w, ks, lds, rw, lane, acc, begin, load, step, finish);
+}
+
+// ---------------------------------------------------------------------------
+// accumulate: C += D^T XP. N = d (N-tile c column n is d = dbase + 4n + c),
+// K = tokens.
 // ---------------------------------------------------------------------------
 struct DRows {
   uint32_t v[8][2];  // 8 tokens x 4 consecutive d (bf16 pairs)
 };
 
-__device__ __forceinline__ void load_d_rows(const uint16_t* __restrict__ Dm, int64_t ldd, int64_t t0, int64_t tend,
-                                            int64_t dcol, bool dvalid, int lane, DRows& out) {
+// Per-lane byte offsets, relative to the window's first token, of the 8
+// bytes lane (n, g) reads for token 8g + j (clamped into a window of `rows`
+// valid tokens) at columns dcol .. dcol+3.
+__device__ __forceinline__ RowOffsets d_offsets(int lane, int64_t ldd, int64_t dcol, int64_t rows) {
   const int g = lane >> 4;
-  const int64_t base_row = t0 < tend ? t0 : tend - 1;  // uniform
-  const uint16_t* base = Dm + base_row * ldd + dcol;
-  const int64_t room = tend - 1 - base_row;
+  RowOffsets o;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int64_t want = t0 + 8 * g + j - base_row;
-    const bool ok = dvalid && (t0 + 8 * g + j < tend);
-    const uint32_t off = (uint32_t)((want < room ? want : room) * ldd);
-    const u32x2v_t v = load_stream_8b(base + off);
-    out.v[j][0] = ok ? v.x : 0u;
-    out.v[j][1] = ok ? v.y : 0u;
+    const int64_t row = 8 * g + j < rows ? 8 * g + j : rows - 1;
+    o.off[j] = (uint32_t)((row * ldd + dcol) * 2);
+  }
+  return o;
+}
+
+__device__ __forceinline__ void load_d_rows(const uint16_t* win, const RowOffsets& o, DRows& out) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const u32x2v_t v = load_stream_8b(win, o.off[j]);
+    out.v[j][0] = v.x;
+    out.v[j][1] = v.y;
+  }
+}
+
+__device__ __forceinline__ void mask_d_rows(int64_t wb, int64_t t0, int64_t tend, int lane, DRows& rows) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t row = wb + 8 * g + j;
+    const bool ok = row >= t0 && row < tend;
+    rows.v[j][0] = ok ? rows.v[j][0] : 0u;
+    rows.v[j][1] = ok ? rows.v[j][1] : 0u;
   }
 }
 
 template <int R>
-__global__ __launch_bounds__(256) void accumulate_kernel(AccumulateBatch ab) {
+__global__ __launch_bounds__(64 * RankTraits<R>::NR * RankTraits<R>::KS, kWorkgroupsPerCU) void accumulate_kernel(
+    AccumulateBatch ab) {
   using Tr = RankTraits<R>;
-  constexpr int KS = Tr::KS;
-  __shared__ float lds[KS > 1 ? KS * Tr::NR * Tr::MT * 16 * 64 : 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float lds[reduce_lds_floats<R>()];
+  const int lane = threadIdx.x & 63, wave = wave_index();
   const int rw = wave % Tr::NR, ks = wave / Tr::NR;
   const int rbase = rw * Tr::RPW;
-  const int n = lane & 15;
-  const int m = item_of(ab.wg_begin, ab.n, blockIdx.x);
-  const int local = blockIdx.x - ab.wg_begin[m];
-  const int64_t tiles = ab.tiles[m];
-  const int64_t dbase = (int64_t)(local % tiles) * 64;
-  const int split = (int)(local / tiles);
-  const int64_t T = ab.T, d = ab.d[m];
-  const int64_t tbeg = split * ab.tchunk;
-  const int64_t tend = tbeg + ab.tchunk < T ? tbeg + ab.tchunk : T;
-  const bool dvalid = dbase + 4 * n < d;  // d % 4 == 0: a lane's 4 columns are all in or all out
-  const int64_t dcol = dvalid ? dbase + 4 * n : 0;
-  const uint16_t* Dm = ab.D[m];
-  const int64_t ldd = ab.ldd[m];
-  const uint16_t* XPm = ab.XP[m] + rbase;
+  const int n = lane & 15, g = lane >> 4;
+  const Schedule& s = ab.s;
+  const int64_t w = logical_workgroup(blockIdx.x, s.G);
+  const int64_t T = uniform_i64(s.kext[0]);
 
-  f32x4_t acc[Tr::MT][4];
-#pragma unroll
-  for (int mt = 0; mt < Tr::MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  int64_t t0 = tbeg + 32 * ks;
-  DRows db;
-  RankRows<R> xa;
-  load_d_rows(Dm, ldd, t0, tend, dcol, dvalid, lane, db);
-  load_rank_rows<R>(XPm, t0, tend, lane, xa);
-  for (; t0 < tend; t0 += 32 * KS) {
-    DRows dn;
-    RankRows<R> xn;
-    load_d_rows(Dm, ldd, t0 + 32 * KS, tend, dcol, dvalid, lane, dn);
-    load_rank_rows<R>(XPm, t0 + 32 * KS, tend, lane, xn);
+  struct Stage {
+    DRows d;
+    RankRows<R> x;
+  };
+  AccTile<R> acc;
+  int64_t dbase = 0, d = 0, ldd = 0;
+  const uint16_t* Dm = nullptr;
+  const uint16_t* XPm = nullptr;
+  RowOffsets xo, doff;
+  auto begin = [&](int m, int64_t tile) {
+    dbase = tile * kTileN;
+    d = s.next[m];
+    ldd = uniform_i64(ab.ldd[m]);
+    // d % 4 == 0: a lane's 4 columns are all in or all out. Lanes past d
+    // read columns 0..3 instead; their output columns are never stored.
+    const int64_t dcol = dbase + 4 * n < d ? dbase + 4 * n : 0;
+    Dm = uniform_ptr(ab.D[m]);
+    XPm = uniform_ptr(ab.XP[m] + rbase);
+    xo = rank_row_offsets<R>(lane, window_rows(T));
+    doff = d_offsets(lane, ldd, dcol, window_rows(T));
+  };
+  auto load = [&](Stage& b, int64_t t0) {
+    const int64_t wb = window_base(t0, T);
+    load_d_rows(uniform_ptr(Dm + wb * ldd), doff, b.d);
+    load_rank_rows<R>(uniform_ptr(XPm + wb * R), xo, b.x);
+  };
+  auto step = [&](Stage& b, int64_t t0, auto masked) {
+    if (masked && t0 + 32 > T) {  // the last, partial K-step (wave-uniform)
+      const int64_t wb = window_base(t0, T);
+      mask_d_rows(wb, t0, T, lane, b.d);
+      mask_rank_rows<R>(wb, t0, T, lane, b.x);
+    }
     uint32_t aop[Tr::MT][4];
-    transpose_rank_rows<R>(xa, aop);
-    uint32_t bop[4][4];
+    transpose_rank_rows<R>(b.x, aop);
+    uint32_t bop[kNT][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) transpose_8xcpl<4>(db.v, c, bop[c]);
+    for (int c = 0; c < kNT; ++c) transpose_8xcpl<4>(b.d.v, c, bop[c]);
 #pragma unroll
     for (int mt = 0; mt < Tr::MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_16x16x32(aop[mt], bop[nt], acc[mt][nt]);
-    db = dn;
-    xa = xn;
-  }
-
-  reduce_waves<R, KS>(acc, lds, rw, ks, lane);
-  if (!dvalid) return;
-  if (ab.splits > 1) {  // output-shaped fp32 partial (d x R) for the finishing pass
-    store_runs_f32<R, KS, false>(acc, ab.part[m] + (int64_t)split * d * R, dbase, d, rbase, ks, lane);
-    return;
-  }
-  float* C = ab.C[m];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    if (!owns_ntile<KS>(nt, ks)) continue;
-    const int64_t drow = dbase + 4 * n + nt;
-#pragma unroll
-    for (int q = 0; q < Tr::NG; ++q) {
-      float run[4 * Tr::CPL];
-      gather_rank_run<R>(acc, q, nt, run);
-      float* dst = C + drow * R + rbase + q * Tr::GW + 4 * Tr::CPL * g_of(lane);
-#pragma unroll
-      for (int v = 0; v < Tr::CPL; ++v) {
-        float4 old = reinterpret_cast<float4*>(dst)[v];
-        old.x += run[4 * v + 0];
-        old.y += run[4 * v + 1];
-        old.z += run[4 * v + 2];
-        old.w += run[4 * v + 3];
-        reinterpret_cast<float4*>(dst)[v] = old;
-      }
+      for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = mfma_16x16x32(aop[mt], bop[nt], acc[mt][nt]);
+  };
+  auto finish = [&](int m, int64_t tile, bool full, int64_t slot) {
+    const auto row_of = [](int c, int nn) { return 4 * nn + c; };
+    if (full) {
+      float* C = ab.C[m];
+      for_owned_runs<R>(acc, ks, lane, row_of, [&](int row, int q, const float (&run)[4 * Tr::CPL]) {
+        if (dbase + row < d) add_run_f32<Tr::CPL>(C + (dbase + row) * R + rbase + q * Tr::GW + 4 * Tr::CPL * g, run);
+      });
+    } else {
+      float* part = ab.part + slot * (int64_t)kTileN * R;
+      for_owned_runs<R>(acc, ks, lane, row_of, [&](int row, int q, const float (&run)[4 * Tr::CPL]) {
+        store_run_f32<Tr::CPL>(part + row * R + rbase + q * Tr::GW + 4 * Tr::CPL * g, run);
+      });
     }
-  }
+  };
+  run_range<R, Stage>(s, w, ks, lds, rw, lane, acc, begin, load, step, finish);
 }
 
 // ---------------------------------------------------------------------------
-// Finishing pass over split partials (fp32, output-shaped, `splits` slabs per
-// item): each thread sums four consecutive values over the splits in split
-// order, with a batch of splits' loads in flight, then rounds them to bf16
-// into XP (project) or adds them to C (accumulate). Workgroup b belongs to
-// the item whose [fin_begin, fin_begin') range holds b.
+// Finishing pass over the tiles that were cut between workgroups: workgroup
+// t takes batch-wide tile t, finds the ranges that cover it and sums their
+// partials in range order, then rounds into XP (project) or adds into C
+// (accumulate). Tiles inside one range return at once.
 // ---------------------------------------------------------------------------
 struct FinishBatch {
-  int n;
-  int fin_begin[kMaxItems + 1];
-  const float* part[kMaxItems];
-  int splits[kMaxItems];
-  int64_t count[kMaxItems];  // floats per slab
-  float* C[kMaxItems];       // accumulate targets
-  uint16_t* XP[kMaxItems];   // project targets
+  Schedule s;
+  const float* part;
+  float* C[kMaxItems];            // accumulate targets
+  uint16_t* XP[kMaxItems];        // project targets
 };
 
-template <bool TO_BF16>
-__global__ __launch_bounds__(256) void finish_splits_kernel(FinishBatch fb) {
-  const int m = item_of(fb.fin_begin, fb.n, blockIdx.x);
-  const int64_t e = ((int64_t)(blockIdx.x - fb.fin_begin[m]) * blockDim.x + threadIdx.x) * 4;
-  const int64_t count = fb.count[m];
-  const int splits = fb.splits[m];
-  const float* partials = fb.part[m];
-  if (e >= count) return;
-  constexpr int BATCH = 8;
-  f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < splits; s0 += BATCH) {
-    float4 v[BATCH];
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      const int sb = s0 + b < splits ? s0 + b : splits - 1;
-      v[b] = *reinterpret_cast<const float4*>(partials + (int64_t)sb * count + e);
+template <int R, bool TO_BF16>
+__global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
+  const Schedule& s = fb.s;
+  const int64_t t = blockIdx.x;
+  const int m = item_of_tile(s, t);
+  const int64_t tile = t - s.tbase[m];
+  const int64_t ts = s.ubase[m] + tile * s.nkb[m], te = ts + s.nkb[m];
+  const int64_t wa = range_of(s, ts), wb = range_of(s, te - 1);
+  if (wa == wb) return;
+  const int64_t left = s.next[m] - tile * kTileN;
+  const int64_t rows = left < kTileN ? left : kTileN;
+  constexpr int PER = 4;  // floats per thread and pass
+  for (int64_t e = (int64_t)threadIdx.x * PER; e < rows * R; e += 256 * PER) {
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t w = wa; w <= wb; ++w) {
+      // wa's share is its last segment when its range began in an earlier
+      // tile, else its first; every later range begins inside this tile
+      const bool first = !(w == wa && range_begin(s, wa) < ts);
+      const float4 v = *reinterpret_cast<const float4*>(fb.part + partial_slot(w, first) * (int64_t)kTileN * R + e);
+      const f32x4_t x = {v.x, v.y, v.z, v.w};
+      sum = (w == wa) ? x : sum + x;
     }
-#pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      if (s0 + b < splits) {
-        const f32x4_t x = {v[b].x, v[b].y, v[b].z, v[b].w};
-        sum = (s0 + b == 0) ? x : sum + x;
-      }
-    }
-  }
-  if constexpr (TO_BF16) {
-    const uint2 out = make_uint2(pack_bf16x2(f32_to_bf16_rne(sum[0]), f32_to_bf16_rne(sum[1])),
+    const int64_t out = tile * kTileN * R + e;
+    if constexpr (TO_BF16) {
+      const uint2 o = make_uint2(pack_bf16x2(f32_to_bf16_rne(sum[0]), f32_to_bf16_rne(sum[1])),
                                  pack_bf16x2(f32_to_bf16_rne(sum[2]), f32_to_bf16_rne(sum[3])));
-    *reinterpret_cast<uint2*>(fb.XP[m] + e) = out;
-  } else {
-    float4 old = *reinterpret_cast<float4*>(fb.C[m] + e);
-    old.x += sum[0];
-    old.y += sum[1];
-    old.z += sum[2];
-    old.w += sum[3];
-    *reinterpret_cast<float4*>(fb.C[m] + e) = old;
+      *reinterpret_cast<uint2*>(fb.XP[m] + out) = o;
+    } else {
+      float4 old = *reinterpret_cast<float4*>(fb.C[m] + out);
+      old.x += sum[0];
+      old.y += sum[1];
+      old.z += sum[2];
+      old.w += sum[3];
+      *reinterpret_cast<float4*>(fb.C[m] + out) = old;
+    }
   }
 }
 
@@ -487,173 +702,91 @@ __global__ __launch_bounds__(256) void finish_splits_kernel(FinishBatch fb) {
 // ---------------------------------------------------------------------------
 namespace {
 
-// Workgroups that keep all 256 compute units streaming (two resident
-// workgroups per compute unit).
-int target_workgroups() { return env_int("RGC_TARGET_WGS", 512); }
-
-inline size_t align256(size_t b) { return (b + 255) / 256 * 256; }
-
-// Project plan: every item gets a k-chunk of about the same size, so that all
-// workgroups carry similar bytes; the chunk shrinks (more splits) until the
-// launch has enough workgroups, within 64 splits per item.
-struct ProjectPlan {
-  int64_t tiles;
-  int64_t kchunk[kMaxItems];
-  int splits[kMaxItems];
-  int wg_begin[kMaxItems + 1];
-  size_t part_off[kMaxItems];
-  size_t ws_bytes;
-};
-
-template <int R>
-ProjectPlan project_plan(int n, const int64_t* ks, int64_t T) {
-  ProjectPlan p;
-  constexpr int step = 32 * RankTraits<R>::KS;
-  p.tiles = (T + 63) / 64;
-  int64_t kmax = 0;
-  for (int m = 0; m < n; ++m) kmax = ks[m] > kmax ? ks[m] : kmax;
-  int64_t chunk = ((kmax + step - 1) / step) * step;
-  for (;;) {
-    int64_t wgs = 0;
-    bool capped = false;
-    for (int m = 0; m < n; ++m) {
-      const int64_t sp = (ks[m] + chunk - 1) / chunk;
-      wgs += p.tiles * sp;
-      capped = capped || sp >= 64;
-    }
-    if (wgs >= target_workgroups() || chunk <= step || capped) break;
-    chunk = ((chunk / 2 + step - 1) / step) * step;
-  }
-  size_t off = 0;
-  p.wg_begin[0] = 0;
-  for (int m = 0; m < n; ++m) {
-    p.splits[m] = (int)((ks[m] + chunk - 1) / chunk);
-    p.kchunk[m] = chunk;
-    p.wg_begin[m + 1] = p.wg_begin[m] + (int)(p.tiles * p.splits[m]);
-    p.part_off[m] = off;
-    if (p.splits[m] > 1) off += align256((size_t)p.splits[m] * T * R * sizeof(float));
-  }
-  p.ws_bytes = off;
-  return p;
+// Workgroups per launch: one per compute unit. (Two fit, but measured on
+// the Qwen3-1.7B-shaped block one is faster: the second adds L2/request
+// pressure rather than hiding latency.)
+int64_t sketch_workgroups() {
+  const int forced = env_int("RGC_SKETCH_WGS", 0);
+  return forced > 0 ? forced : (int64_t)device_compute_units();
 }
 
-// Accumulate plan: one token split count for the whole batch, chosen so that
-// the launch has enough workgroups.
-struct AccumulatePlan {
-  int64_t tiles[kMaxItems];
-  int splits;
-  int64_t tchunk;
-  int wg_begin[kMaxItems + 1];
-  size_t part_off[kMaxItems];
-  size_t ws_bytes;
-};
-
+// The schedule for items with N extents ns[] and K extents ks[].
 template <int R>
-AccumulatePlan accumulate_plan(int n, const int64_t* ds, int64_t T) {
-  AccumulatePlan p;
-  constexpr int step = 32 * RankTraits<R>::KS;
-  int64_t total = 0;
+Schedule make_schedule(int n, const int64_t* ns, const int64_t* ks) {
+  Schedule s = {};
+  constexpr int64_t kblock = 32 * RankTraits<R>::KS;
+  s.n = n;
   for (int m = 0; m < n; ++m) {
-    p.tiles[m] = (ds[m] + 63) / 64;
-    total += p.tiles[m];
+    const int64_t tiles = (ns[m] + kTileN - 1) / kTileN;
+    s.nkb[m] = (ks[m] + kblock - 1) / kblock;
+    s.kext[m] = ks[m];
+    s.next[m] = ns[m];
+    s.ubase[m + 1] = s.ubase[m] + tiles * s.nkb[m];
+    s.tbase[m + 1] = s.tbase[m] + tiles;
   }
-  const int64_t ksteps = (T + step - 1) / step;
-  int64_t want = (target_workgroups() + total - 1) / (total > 0 ? total : 1);
-  if (want < 1) want = 1;
-  if (want > ksteps) want = ksteps > 0 ? ksteps : 1;
-  if (want > 64) want = 64;
-  p.tchunk = ((ksteps + want - 1) / want) * step;
-  p.splits = (int)((T + p.tchunk - 1) / (p.tchunk > 0 ? p.tchunk : 1));
-  if (p.splits < 1) p.splits = 1;
-  size_t off = 0;
-  p.wg_begin[0] = 0;
-  for (int m = 0; m < n; ++m) {
-    p.wg_begin[m + 1] = p.wg_begin[m] + (int)(p.tiles[m] * p.splits);
-    p.part_off[m] = off;
-    if (p.splits > 1) off += align256((size_t)p.splits * ds[m] * R * sizeof(float));
-  }
-  p.ws_bytes = off;
-  return p;
+  s.U = s.ubase[n];
+  const int64_t G = sketch_workgroups();
+  s.G = (int)(s.U < G ? s.U : G);
+  return s;
 }
 
-inline int finish_blocks(int64_t count) { return (int)((count / 4 + 255) / 256); }
+template <int R>
+size_t partial_bytes(const Schedule& s) {
+  return (size_t)2 * s.G * kTileN * R * sizeof(float);
+}
 
 template <int R>
 rgc_status_t project_launch(int n, const uint16_t* const* Xs, const int64_t* ldxs, const int64_t* ks,
-                            const uint16_t* const* Ps, uint16_t* const* XPs, int64_t T, void* ws, hipStream_t s) {
-  const ProjectPlan p = project_plan<R>(n, ks, T);
+                            const uint16_t* const* Ps, uint16_t* const* XPs, int64_t T, void* ws, hipStream_t st) {
+  int64_t ns[kMaxItems];
+  for (int m = 0; m < n; ++m) ns[m] = T;
   ProjectBatch pb = {};
+  pb.s = make_schedule<R>(n, ns, ks);
   FinishBatch fb = {};
-  pb.n = n;
-  pb.T = T;
-  pb.tiles = p.tiles;
-  fb.fin_begin[0] = 0;
+  fb.s = pb.s;
   for (int m = 0; m < n; ++m) {
     pb.X[m] = Xs[m];
     pb.ldx[m] = ldxs[m];
-    pb.k[m] = ks[m];
     pb.P[m] = Ps[m];
     pb.XP[m] = XPs[m];
-    pb.kchunk[m] = p.kchunk[m];
-    pb.splits[m] = p.splits[m];
-    pb.part[m] = p.splits[m] > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_off[m]) : nullptr;
-    pb.wg_begin[m] = p.wg_begin[m];
-    if (p.splits[m] > 1) {
-      const int f = fb.n++;
-      fb.part[f] = pb.part[m];
-      fb.splits[f] = p.splits[m];
-      fb.count[f] = T * R;
-      fb.XP[f] = XPs[m];
-      fb.fin_begin[f + 1] = fb.fin_begin[f] + finish_blocks(T * R);
-    }
+    fb.XP[m] = XPs[m];
   }
-  pb.wg_begin[n] = p.wg_begin[n];
-  hipLaunchKernelGGL(project_kernel<R>, dim3(p.wg_begin[n]), dim3(64 * RankTraits<R>::NR * RankTraits<R>::KS), 0, s,
-                     pb);
-  if (fb.n > 0) hipLaunchKernelGGL(finish_splits_kernel<true>, dim3(fb.fin_begin[fb.n]), dim3(256), 0, s, fb);
+  pb.part = static_cast<float*>(ws);
+  fb.part = pb.part;
+  hipLaunchKernelGGL(project_kernel<R>, dim3((unsigned)pb.s.G), dim3(64 * RankTraits<R>::NR * RankTraits<R>::KS), 0,
+                     st, pb);
+  hipLaunchKernelGGL((finish_tiles_kernel<R, true>), dim3((unsigned)pb.s.tbase[n]), dim3(256), 0, st, fb);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
 template <int R>
 rgc_status_t accumulate_launch(int n, const uint16_t* const* Ds, const int64_t* ldds, const int64_t* ds,
-                               const uint16_t* const* XPs, float* const* Cs, int64_t T, void* ws, hipStream_t s) {
-  const AccumulatePlan p = accumulate_plan<R>(n, ds, T);
+                               const uint16_t* const* XPs, float* const* Cs, int64_t T, void* ws, hipStream_t st) {
+  int64_t ks[kMaxItems];
+  for (int m = 0; m < n; ++m) ks[m] = T;
   AccumulateBatch ab = {};
+  ab.s = make_schedule<R>(n, ds, ks);
   FinishBatch fb = {};
-  ab.n = n;
-  ab.T = T;
-  ab.tchunk = p.tchunk;
-  ab.splits = p.splits;
-  fb.fin_begin[0] = 0;
+  fb.s = ab.s;
   for (int m = 0; m < n; ++m) {
     ab.D[m] = Ds[m];
     ab.ldd[m] = ldds[m];
-    ab.d[m] = ds[m];
-    ab.tiles[m] = p.tiles[m];
     ab.XP[m] = XPs[m];
     ab.C[m] = Cs[m];
-    ab.part[m] = p.splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_off[m]) : nullptr;
-    ab.wg_begin[m] = p.wg_begin[m];
-    if (p.splits > 1) {
-      fb.part[m] = ab.part[m];
-      fb.splits[m] = p.splits;
-      fb.count[m] = ds[m] * R;
-      fb.C[m] = Cs[m];
-      fb.fin_begin[m + 1] = fb.fin_begin[m] + finish_blocks(ds[m] * R);
-    }
+    fb.C[m] = Cs[m];
   }
-  ab.wg_begin[n] = p.wg_begin[n];
-  fb.n = p.splits > 1 ? n : 0;
-  hipLaunchKernelGGL(accumulate_kernel<R>, dim3(p.wg_begin[n]), dim3(64 * RankTraits<R>::NR * RankTraits<R>::KS), 0,
-                     s, ab);
-  if (fb.n > 0) hipLaunchKernelGGL(finish_splits_kernel<false>, dim3(fb.fin_begin[fb.n]), dim3(256), 0, s, fb);
+  ab.part = static_cast<float*>(ws);
+  fb.part = ab.part;
+  hipLaunchKernelGGL(accumulate_kernel<R>, dim3((unsigned)ab.s.G), dim3(64 * RankTraits<R>::NR * RankTraits<R>::KS), 0,
+                     st, ab);
+  hipLaunchKernelGGL((finish_tiles_kernel<R, false>), dim3((unsigned)ab.s.tbase[n]), dim3(256), 0, st, fb);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
 rgc_status_t check_project_item(const uint16_t* X, int64_t ldx, int64_t k, const uint16_t* P, const uint16_t* XP,
                                 int64_t T, int64_t r) {
   if (k <= 0 || r > k || ldx < k) return RGC_ERR_SHAPE;
-  if ((k % 8) != 0) return RGC_ERR_UNSUPPORTED;
+  if ((k % 8) != 0 || ldx > kMaxLeadingDim) return RGC_ERR_UNSUPPORTED;
   if (T == 0) return RGC_OK;
   if (!X || !P || !XP) return RGC_ERR_NULL;
   if (!aligned16(X) || !aligned16(P) || !aligned16(XP) || (ldx % 8) != 0) return RGC_ERR_ALIGN;
@@ -663,7 +796,7 @@ rgc_status_t check_project_item(const uint16_t* X, int64_t ldx, int64_t k, const
 rgc_status_t check_accumulate_item(const uint16_t* D, int64_t ldd, int64_t d, const uint16_t* XP, const float* C,
                                    int64_t T) {
   if (d <= 0 || ldd < d) return RGC_ERR_SHAPE;
-  if ((d % 8) != 0 || d > kMaxTiledDim) return RGC_ERR_UNSUPPORTED;
+  if ((d % 8) != 0 || d > kMaxTiledDim || ldd > kMaxLeadingDim) return RGC_ERR_UNSUPPORTED;
   if (T == 0) return RGC_OK;
   if (!D || !XP || !C) return RGC_ERR_NULL;
   if (!aligned16(D) || !aligned16(XP) || !aligned16(C) || (ldd % 8) != 0) return RGC_ERR_ALIGN;
@@ -679,8 +812,14 @@ extern "C" size_t rgc_project_batch_workspace_size(int64_t n, const int64_t* ks,
   if (n <= 0 || n > kMaxItems || !ks || T <= 0) return 0;
   for (int64_t m = 0; m < n; ++m)
     if (ks[m] <= 0) return 0;
+  int64_t ns[kMaxItems];
+  for (int64_t m = 0; m < n; ++m) ns[m] = T;
   size_t out = 0;
-  if (!dispatch_rank(r, [&](auto rc) { out = project_plan<decltype(rc)::value>((int)n, ks, T).ws_bytes; })) return 0;
+  if (!dispatch_rank(r, [&](auto rc) {
+        constexpr int R = decltype(rc)::value;
+        out = partial_bytes<R>(make_schedule<R>((int)n, ns, ks));
+      }))
+    return 0;
   return out;
 }
 
@@ -688,8 +827,14 @@ extern "C" size_t rgc_accumulate_batch_workspace_size(int64_t n, const int64_t* 
   if (n <= 0 || n > kMaxItems || !ds || T <= 0) return 0;
   for (int64_t m = 0; m < n; ++m)
     if (ds[m] <= 0) return 0;
+  int64_t ks[kMaxItems];
+  for (int64_t m = 0; m < n; ++m) ks[m] = T;
   size_t out = 0;
-  if (!dispatch_rank(r, [&](auto rc) { out = accumulate_plan<decltype(rc)::value>((int)n, ds, T).ws_bytes; })) return 0;
+  if (!dispatch_rank(r, [&](auto rc) {
+        constexpr int R = decltype(rc)::value;
+        out = partial_bytes<R>(make_schedule<R>((int)n, ds, ks));
+      }))
+    return 0;
   return out;
 }
 

@@ -140,8 +140,11 @@ def test_projection_repeatable(dev):
 # ---------------------------------------------------------------------------
 # Sketch contractions
 # ---------------------------------------------------------------------------
+# includes k < 32 (a single, short K window), k = 2056 (a short last k chunk)
+# and T < 64 (one partial token tile)
 PROJECT_CASES = [(256, 512, 16), (1000, 520, 48), (37, 2048, 64), (4096, 2048, 64), (300, 1024, 128),
-                 (129, 512, 192), (200, 2048, 256), (64, 512, 32), (4096, 6144, 64)]
+                 (129, 512, 192), (200, 2048, 256), (64, 512, 32), (4096, 6144, 64), (20, 24, 16),
+                 (100, 2056, 64), (7, 16, 16)]
 
 
 @pytest.mark.parametrize("T,k,r", PROJECT_CASES)
@@ -156,8 +159,11 @@ def test_project_parity(dev, T, k, r):
     assert rel_frobenius(orc.bf16_to_f64(bits(got)), orc.bf16_to_f64(ref)) < 2e-3
 
 
+# includes T < 32 (a single, short K window) and T = 4100 (a last token
+# split of 4 tokens)
 ACC_CASES = [(256, 256, 16), (1000, 1000, 48), (4096, 2048, 64), (77, 520, 128), (300, 264, 192),
-             (513, 1024, 256), (33, 64, 32), (4096, 6144, 64), (4096, 1024, 256)]
+             (513, 1024, 256), (33, 64, 32), (4096, 6144, 64), (4096, 1024, 256), (20, 72, 16), (5, 8, 64),
+             (4100, 256, 64)]
 
 
 @pytest.mark.parametrize("T,d,r", ACC_CASES)
