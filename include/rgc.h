@@ -156,7 +156,8 @@ rgc_status_t rgc_accumulate_batch(int64_t n, const uint16_t* const* Ds, const in
 
 /* ---- 4. Normalized update with stochastic rounding ------------------------ */
 
-/* Workspace bytes rgc_apply needs (norm partials and the step scalar). */
+/* Workspace bytes rgc_apply needs (per-workgroup norm partials and the step
+ * scalar). */
 size_t rgc_apply_workspace_size(int64_t d, int64_t k, int64_t r);
 
 /* W <- SR_bf16(W - s * H), H = C P^T, s = fp32(tau * ||W||_F / ||H||_F)
@@ -172,6 +173,19 @@ size_t rgc_apply_workspace_size(int64_t d, int64_t k, int64_t r);
 rgc_status_t rgc_apply(uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d,
                        int64_t k, int64_t r, float tau, uint64_t seed, float* stats, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* rgc_apply for n <= 16 matrices of one rank r (e.g. the projections of a
+ * block) in three launches: a norms sweep over all of them, one step scalar
+ * per matrix, an update sweep. Item m: W Ws[m] (ds[m] x ks[m], row stride
+ * ldws[m]), C Cs[m] (ds[m] x r), P Ps[m] (ks[m] x r), rounding seed seeds[m],
+ * stats NULL or stats[m] NULL or device float[4]. All arrays are HOST arrays
+ * of n entries; tau is shared. Each matrix gets exactly the bits that
+ * rgc_apply would give it alone. */
+size_t rgc_apply_batch_workspace_size(int64_t n, const int64_t* ds, const int64_t* ks, int64_t r);
+rgc_status_t rgc_apply_batch(int64_t n, uint16_t* const* Ws, const int64_t* ldws, const float* const* Cs,
+                             const uint16_t* const* Ps, const int64_t* ds, const int64_t* ks, int64_t r,
+                             float tau, const uint64_t* seeds, float* const* stats, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* ---- Test hooks (same library; used by the parity tests) ----------------- */
 

@@ -3,106 +3,215 @@
 //
 //   W <- SR_bf16(W - s * H),  H = C P^T,  s = tau * ||W||_F / ||H||_F
 //
-// H is never written to memory. Each wave rebuilds 16 rows x 64 columns of it
-// at a time on MFMA (M = columns of W from rows of P, N = rows of W from rows
-// of C, K = r), with C split into a bf16 high part and a bf16 remainder so that
-// H carries ~16 bits of C's mantissa. The page rebuilds H 128 rows at a time;
-// here the height is 64 rows per workgroup (the result does not depend on it).
+// H is never written to memory. It is rebuilt 64 columns at a time on MFMA
+// (M = columns of W from rows of P, N = rows of W from rows of C, K = r), with
+// C split into a bf16 high part and a bf16 remainder so that H carries ~16
+// bits of C's mantissa. The page rebuilds H 128 rows at a time; here a
+// workgroup rebuilds 128 rows (64 for r > 64) x 64 columns per step (the
+// result does not depend on the tile shape).
 //
-// Two sweeps over W:
-//   sweep 1 reads W and rebuilds H to get sum(w^2) and sum(h^2) (fp64 per lane,
-//           fixed-order reductions across lanes and waves), one partial pair
-//           per workgroup (at most a few hundred workgroups);
-//   sweep 2 first sums those partials in a fixed order in every workgroup (all
-//           get the identical s and skip flag, with no signalling between
-//           workgroups), then reads W again, rebuilds the same H (same code,
-//           same order), forms v = fp32(w - fp32(s*h)) and rounds
+// One batch (e.g. all projections of a block) takes three launches:
+//   norms:  every workgroup streams its share of one matrix's W, rebuilds the
+//           same H tiles and writes one (sum w^2, sum h^2) pair (fp64 per
+//           lane, fixed-order reductions across lanes and waves);
+//   scale:  one workgroup per matrix sums that matrix's pairs in workgroup
+//           order and forms s = fp32(tau ||W|| / ||H||), or the skip flag when
+//           ||H|| is zero or not finite or s is not finite;
+//   update: every workgroup reads its matrix's s, rebuilds its H tiles again
+//           (same code, same order), forms v = fp32(w - fp32(s h)) and rounds
 //           stochastically with 16 bits per element from Philox4x32-10 keyed
 //           on (seed, row, column).
+// Each matrix gets one workgroup per twelve tiles (its own shape alone
+// decides, so a matrix gets the same bits alone or in a batch), and each
+// workgroup serves one matrix. Within a workgroup the W and P tiles two steps
+// ahead are loaded while the current one is processed (P goes through
+// registers into LDS, where the four waves share it).
 //
 // Lane layout of a tile: M-tile t row m stands for column
 // jb + 16*(m/4) + 4*t + (m%4), which gives lane (g = lane/16, n = lane%16) the
-// 16 consecutive columns jb + 16g .. +15 of row ib + n, i.e. two 16-byte loads
-// of W and two Philox calls (8 columns each) per lane per tile.
+// 16 consecutive columns jb + 16g .. +15 of its row in each N-tile, i.e. two
+// 16-byte loads of W and two Philox calls (8 columns each).
 #include "rgc_internal.hpp"
 
 namespace rgc {
 
 enum ApplyMode { kModeNorms = 0, kModeUpdate = 1, kModeReconstruct = 2 };
 
-constexpr int kApplyRowsPerWG = 64;  // 4 waves x 16 rows
-constexpr int kApplyColsPerTile = 64;
+constexpr int kApplyCols = 64;     // columns per tile
+constexpr int kApplyWaves = 4;
+constexpr int kApplyMaxItems = 16;
 
-// The C side of the tile product for the 16 rows a wave owns: K-step q holds
+template <int R>
+struct ApplyTraits {
+  static constexpr int KQ = (R + 31) / 32;              // K-steps of 32 over r
+  static constexpr int NTW = R <= 64 ? 2 : 1;           // 16-row N-tiles per wave
+  static constexpr int RW = 16 * NTW;                   // rows per wave
+  static constexpr int ROWS = kApplyWaves * RW;         // rows per workgroup tile
+  static constexpr int RP = 32 * KQ + 8;                // LDS row pitch of the P tile (bf16)
+  static constexpr int PCHUNKS = kApplyCols * R / 8;    // 16-byte chunks of a P tile
+  static constexpr int PCPT = (PCHUNKS + 255) / 256;    // chunks per thread
+};
+
+struct ApplyItem {
+  uint16_t* W;
+  int64_t ldw;
+  const float* C;
+  const uint16_t* P;
+  int64_t d, k;
+  int64_t ctiles;  // column tiles per row block
+  int64_t units;   // row blocks x column tiles
+  uint64_t seed;
+  float* stats;
+};
+
+struct ApplyBatch {
+  int n;
+  float tau;
+  int wbase[kApplyMaxItems + 1];  // workgroups [wbase[m], wbase[m+1]) serve item m
+  ApplyItem it[kApplyMaxItems];
+  double* partials;               // 2 per workgroup of the norms sweep
+  float* scale;                   // per item: s, flag
+  float* H;                       // reconstruct target (test hook)
+};
+
+__device__ __forceinline__ int apply_item_of(const ApplyBatch& b, int w) {
+  int m = 0;
+  while (m + 1 < b.n && w >= b.wbase[m + 1]) ++m;
+  return m;
+}
+
+// The C side of the MFMA for the rows of one N-tile: K-step q holds
 // C[i][32q + 8g .. +7] as bf16 high parts and bf16 remainders.
 template <int R>
 struct RowOperand {
-  static constexpr int KQ = (R + 31) / 32;
-  uint32_t hi[KQ][4];
-  uint32_t lo[KQ][4];
+  uint32_t hi[ApplyTraits<R>::NTW][ApplyTraits<R>::KQ][4];
+  uint32_t lo[ApplyTraits<R>::NTW][ApplyTraits<R>::KQ][4];
 };
 
 template <int R>
-__device__ __forceinline__ void load_row_operand(const float* __restrict__ C, int64_t d, int64_t i, int g,
+__device__ __forceinline__ void load_row_operand(const float* __restrict__ C, int64_t d, int64_t row0, int lane,
                                                  RowOperand<R>& op) {
+  using Tr = ApplyTraits<R>;
+  const int n = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int q = 0; q < RowOperand<R>::KQ; ++q) {
-    const int c0 = 32 * q + 8 * g;
-    float v[8];
-    if (i < d && c0 < R) {
-      const float4 a = *reinterpret_cast<const float4*>(C + i * R + c0);
-      const float4 b = *reinterpret_cast<const float4*>(C + i * R + c0 + 4);
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
+  for (int nt = 0; nt < Tr::NTW; ++nt) {
+    const int64_t i = row0 + 16 * nt + n;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    }
+    for (int q = 0; q < Tr::KQ; ++q) {
+      const int c0 = 32 * q + 8 * g;
+      float v[8];
+      if (i < d && c0 < R) {
+        const float4 a = *reinterpret_cast<const float4*>(C + i * R + c0);
+        const float4 b = *reinterpret_cast<const float4*>(C + i * R + c0 + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      } else {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t h0 = f32_to_bf16_rne(v[2 * p]), h1 = f32_to_bf16_rne(v[2 * p + 1]);
-      const uint32_t l0 = f32_to_bf16_rne(v[2 * p] - bf16_bits_to_f32(h0));
-      const uint32_t l1 = f32_to_bf16_rne(v[2 * p + 1] - bf16_bits_to_f32(h1));
-      op.hi[q][p] = pack_bf16x2(h0, h1);
-      op.lo[q][p] = pack_bf16x2(l0, l1);
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t h0 = f32_to_bf16_rne(v[2 * p]), h1 = f32_to_bf16_rne(v[2 * p + 1]);
+        const uint32_t l0 = f32_to_bf16_rne(v[2 * p] - bf16_bits_to_f32(h0));
+        const uint32_t l1 = f32_to_bf16_rne(v[2 * p + 1] - bf16_bits_to_f32(h1));
+        op.hi[nt][q][p] = pack_bf16x2(h0, h1);
+        op.lo[nt][q][p] = pack_bf16x2(l0, l1);
+      }
     }
   }
 }
 
-// h[x] = H[ib + n][jb + 16g + x], x = 0..15, for this lane.
+// Per-step buffers: this thread's share of the next P tile and this lane's W
+// values (two 16-byte chunks per N-tile).
 template <int R>
-__device__ __forceinline__ void rebuild_tile(const uint16_t* __restrict__ P, int64_t k, int64_t jb,
-                                             const RowOperand<R>& rop, int lane, float (&h)[16]) {
-  const int m = lane & 15, g = lane >> 4;
-  f32x4_t acc[4];
+struct TileRegs {
+  uint4 p[ApplyTraits<R>::PCPT];
+  uint4 w[ApplyTraits<R>::NTW][2];
+};
+
+// Issues the loads of tile (row0, jb): the P rows jb .. jb+63 (clamped to
+// k-1; zeroed when written to LDS) and, unless NORM-only reconstruction, the
+// lane's W chunks (rows clamped to d-1, chunks clamped to k-8; such values
+// are never stored or counted).
+template <int R, int MODE>
+__device__ __forceinline__ void load_tile(const ApplyItem& it, int64_t row0, int64_t jb, int wave, int lane,
+                                          TileRegs<R>& t) {
+  using Tr = ApplyTraits<R>;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < Tr::PCPT; ++c) {
+    const int chunk = (int)threadIdx.x + 256 * c;
+    const int jl = chunk / (R / 8), part = chunk % (R / 8);
+    int64_t j = jb + jl;
+    j = j < it.k ? j : it.k - 1;
+    if (chunk < Tr::PCHUNKS) t.p[c] = *reinterpret_cast<const uint4*>(it.P + j * R + 8 * part);
+  }
+  if constexpr (MODE != kModeReconstruct) {
+    const int n = lane & 15, g = lane >> 4;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int64_t j = jb + 16 * (m >> 2) + 4 * t + (m & 3);
+    for (int nt = 0; nt < Tr::NTW; ++nt) {
+      int64_t i = row0 + Tr::RW * wave + 16 * nt + n;
+      i = i < it.d ? i : it.d - 1;
 #pragma unroll
-    for (int q = 0; q < RowOperand<R>::KQ; ++q) {
-      const int c0 = 32 * q + 8 * g;
-      uint32_t a[4] = {0u, 0u, 0u, 0u};
-      if (j < k && c0 < R) {
-        const uint4 v = *reinterpret_cast<const uint4*>(P + j * R + c0);
-        a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w;
+      for (int half = 0; half < 2; ++half) {
+        int64_t jj = jb + 16 * g + 8 * half;
+        jj = jj < it.k ? jj : it.k - 8;
+        t.w[nt][half] = *reinterpret_cast<const uint4*>(it.W + i * it.ldw + jj);
       }
-      acc[t] = mfma_16x16x32(a, rop.hi[q], acc[t]);
-      acc[t] = mfma_16x16x32(a, rop.lo[q], acc[t]);
     }
   }
+}
+
+// Writes this thread's share of the P tile into an LDS buffer (rows past k
+// and rank columns past R as zeros).
+template <int R>
+__device__ __forceinline__ void stage_p(const TileRegs<R>& t, int64_t jb, int64_t k, uint16_t* lds_p) {
+  using Tr = ApplyTraits<R>;
+#pragma unroll
+  for (int c = 0; c < Tr::PCPT; ++c) {
+    const int chunk = (int)threadIdx.x + 256 * c;
+    if (chunk < Tr::PCHUNKS) {
+      const int jl = chunk / (R / 8), part = chunk % (R / 8);
+      const uint4 v = jb + jl < k ? t.p[c] : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(lds_p + jl * Tr::RP + 8 * part) = v;
+    }
+  }
+  if constexpr (32 * Tr::KQ > R) {  // zero the rank columns R .. 32*KQ-1 once per tile
+    constexpr int pad = 32 * Tr::KQ - R;
+    for (int e = threadIdx.x; e < kApplyCols * pad; e += 256) lds_p[(e / pad) * Tr::RP + R + e % pad] = 0;
+  }
+}
+
+// h[nt][x] = H[row(nt)][jb + 16g + x], x = 0..15, from the P tile in LDS.
+template <int R>
+__device__ __forceinline__ void rebuild_tile(const uint16_t* lds_p, const RowOperand<R>& rop, int lane,
+                                             float (&h)[ApplyTraits<R>::NTW][16]) {
+  using Tr = ApplyTraits<R>;
+  const int m = lane & 15, g = lane >> 4;
+  f32x4_t acc[4][Tr::NTW];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) h[4 * t + e] = acc[t][e];
-}
-
-__device__ __forceinline__ void load_w16(const uint16_t* p, uint32_t (&w)[8]) {
-  const uint4 a = reinterpret_cast<const uint4*>(p)[0];
-  const uint4 b = reinterpret_cast<const uint4*>(p)[1];
-  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    for (int nt = 0; nt < Tr::NTW; ++nt) acc[t][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int jl = 16 * (m >> 2) + 4 * t + (m & 3);
+#pragma unroll
+    for (int q = 0; q < Tr::KQ; ++q) {
+      const uint4 v = *reinterpret_cast<const uint4*>(lds_p + jl * Tr::RP + 32 * q + 8 * g);
+      const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int nt = 0; nt < Tr::NTW; ++nt) {
+        acc[t][nt] = mfma_16x16x32(a, rop.hi[nt][q], acc[t][nt]);
+        acc[t][nt] = mfma_16x16x32(a, rop.lo[nt][q], acc[t][nt]);
+      }
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < Tr::NTW; ++nt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[nt][4 * t + e] = acc[t][nt][e];
 }
 
 // Rounding bits for row i, columns 8*cb .. 8*cb+7: word (x/2), low half for
@@ -113,130 +222,121 @@ __device__ __forceinline__ void rounding_words(uint64_t seed, int64_t i, int64_t
   words[0] = o.x; words[1] = o.y; words[2] = o.z; words[3] = o.w;
 }
 
-// Fixed-order sum of sweep 1's partials (thread t holds partials t, t+256, ...
-// in order; then a butterfly within each wave and the waves in order), and the
-// step s = fp32(tau * ||W|| / ||H||); flag = 1 when ||H|| is zero or not finite
-// or s is not finite (then s = 0).
-__device__ __forceinline__ void step_from_partials(const double* __restrict__ partials, int nparts, float tau, int wave,
-                                                   int lane, float& s, uint32_t& flag, double& nw, double& nh) {
-  __shared__ double red[2][4];
-  double aw = 0.0, ah = 0.0;
-  for (int b = threadIdx.x; b < nparts; b += blockDim.x) {
-    aw += partials[2 * b];
-    ah += partials[2 * b + 1];
-  }
-  aw = wave_sum(aw);
-  ah = wave_sum(ah);
-  if (lane == 0) {
-    red[0][wave] = aw;
-    red[1][wave] = ah;
-  }
-  __syncthreads();
-  const double tw = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
-  const double th = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
-  nw = sqrt(tw);
-  nh = sqrt(th);
-  s = 0.f;
-  flag = 0u;
-  if (!(nh > 0.0) || !isfinite(nh)) {
-    flag = 1u;
-  } else {
-    s = (float)((double)tau * nw / nh);
-    if (!isfinite(s)) {
-      s = 0.f;
-      flag = 1u;
-    }
-  }
-}
-
+// Two resident workgroups per compute unit, or one at r > 128 (the row
+// operand and the P tile alone take most of a wave's registers there).
 template <int R, int MODE>
-__global__ __launch_bounds__(256) void apply_kernel(uint16_t* __restrict__ W, int64_t ldw, const float* __restrict__ C,
-                                                    const uint16_t* __restrict__ P, int64_t d, int64_t k,
-                                                    int tiles_per_wg, float tau, uint64_t seed,
-                                                    float* __restrict__ stats, double* __restrict__ partials,
-                                                    int nparts, float* __restrict__ Hout) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch b) {
+  using Tr = ApplyTraits<R>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_p[3][kApplyCols * Tr::RP];
+  __shared__ double red[2][kApplyWaves];
+  const int lane = threadIdx.x & 63, wave = wave_index();
   const int n = lane & 15, g = lane >> 4;
-  const int64_t i = (int64_t)blockIdx.x * kApplyRowsPerWG + 16 * wave + n;
-  const int64_t col_tiles = (k + kApplyColsPerTile - 1) / kApplyColsPerTile;
-  const int64_t tile0 = (int64_t)blockIdx.y * tiles_per_wg;
+  const int w = blockIdx.x;
+  const int m = apply_item_of(b, w);
+  const ApplyItem& it = b.it[m];
+  const int64_t wl = w - b.wbase[m], gm = b.wbase[m + 1] - b.wbase[m];
+  const int64_t u0 = wl * it.units / gm, u1 = (wl + 1) * it.units / gm;
 
   float s = 0.f;
   if constexpr (MODE == kModeUpdate) {
-    // Every workgroup sums sweep 1's partials in the same fixed order, so all
-    // compute the identical step s; workgroup 0 reports it.
-    uint32_t flag;
-    double nw, nh;
-    step_from_partials(partials, nparts, tau, wave, lane, s, flag, nw, nh);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0 && stats) {
-      stats[0] = (float)nw;
-      stats[1] = (float)nh;
-      stats[2] = s;
-      stats[3] = (float)flag;
-    }
-    if (flag) return;  // zero or non-finite step: leave W untouched
+    s = b.scale[2 * m];
+    if (b.scale[2 * m + 1] != 0.f) return;  // zero or non-finite step: W stays as it is
   }
 
-  RowOperand<R> rop;
-  load_row_operand<R>(C, d, i, g, rop);
-
   double sw = 0.0, sh = 0.0;
-  for (int tt = 0; tt < tiles_per_wg; ++tt) {
-    const int64_t tile = tile0 + tt;
-    if (tile >= col_tiles) break;
-    const int64_t jb = tile * kApplyColsPerTile;
-    float h[16];
-    rebuild_tile<R>(P, k, jb, rop, lane, h);
-    const int64_t j0 = jb + 16 * g;
-    if (i >= d) continue;
-    if constexpr (MODE == kModeReconstruct) {
+  RowOperand<R> rop;
+  int64_t rb_loaded = -1;
+
+  auto tile_at = [&](int64_t u, int64_t& row0, int64_t& jb) {
+    row0 = (u / it.ctiles) * Tr::ROWS;
+    jb = (u % it.ctiles) * kApplyCols;
+  };
+  auto load_unit = [&](int64_t u, TileRegs<R>& t) {
+    int64_t row0, jb;
+    tile_at(u < u1 ? u : u1 - 1, row0, jb);  // past the range: reload the last tile (never used)
+    load_tile<R, MODE>(it, row0, jb, wave, lane, t);
+  };
+  auto stage_unit = [&](int64_t u, const TileRegs<R>& t, uint16_t* buf) {
+    int64_t row0, jb;
+    tile_at(u < u1 ? u : u1 - 1, row0, jb);
+    stage_p<R>(t, jb, it.k, buf);
+  };
+  auto process = [&](int64_t u, const TileRegs<R>& t, const uint16_t* buf) {
+    int64_t row0, jb;
+    tile_at(u, row0, jb);
+    const int64_t rb = row0 / Tr::ROWS;
+    if (rb != rb_loaded) {  // wave-uniform: a new row block
+      load_row_operand<R>(it.C, it.d, row0 + Tr::RW * wave, lane, rop);
+      rb_loaded = rb;
+    }
+    float h[Tr::NTW][16];
+    rebuild_tile<R>(buf, rop, lane, h);
+#pragma unroll
+    for (int nt = 0; nt < Tr::NTW; ++nt) {
+      const int64_t i = row0 + Tr::RW * wave + 16 * nt + n;
+      if (i >= it.d) continue;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        if (j0 + 8 * half >= k) continue;
-        float4* dst = reinterpret_cast<float4*>(Hout + i * k + j0 + 8 * half);
-        dst[0] = make_float4(h[8 * half + 0], h[8 * half + 1], h[8 * half + 2], h[8 * half + 3]);
-        dst[1] = make_float4(h[8 * half + 4], h[8 * half + 5], h[8 * half + 6], h[8 * half + 7]);
-      }
-    } else if constexpr (MODE == kModeNorms) {
+        const int64_t jj = jb + 16 * g + 8 * half;
+        if (jj >= it.k) continue;
+        const float* hv = &h[nt][8 * half];
+        if constexpr (MODE == kModeReconstruct) {
+          float4* dst = reinterpret_cast<float4*>(b.H + i * it.k + jj);
+          dst[0] = make_float4(hv[0], hv[1], hv[2], hv[3]);
+          dst[1] = make_float4(hv[4], hv[5], hv[6], hv[7]);
+        } else {
+          const uint4 wv = t.w[nt][half];
+          const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+          if constexpr (MODE == kModeNorms) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        if (j0 + 8 * half >= k) continue;
-        const uint4 wv = *reinterpret_cast<const uint4*>(W + i * ldw + j0 + 8 * half);
-        const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+            for (int p = 0; p < 4; ++p) {
+              const double w0 = (double)bf16_bits_to_f32(wd[p] & 0xFFFFu);
+              const double w1 = (double)bf16_bits_to_f32(wd[p] >> 16);
+              const double h0 = (double)hv[2 * p], h1 = (double)hv[2 * p + 1];
+              sw += w0 * w0 + w1 * w1;
+              sh += h0 * h0 + h1 * h1;
+            }
+          } else {
+            uint32_t rw[4];
+            rounding_words(it.seed, i, jj >> 3, rw);
+            uint32_t out[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const double w0 = (double)bf16_bits_to_f32(wd[p] & 0xFFFFu);
-          const double w1 = (double)bf16_bits_to_f32(wd[p] >> 16);
-          const double h0 = (double)h[8 * half + 2 * p], h1 = (double)h[8 * half + 2 * p + 1];
-          sw += w0 * w0 + w1 * w1;
-          sh += h0 * h0 + h1 * h1;
+            for (int p = 0; p < 4; ++p) {
+              const float w0 = bf16_bits_to_f32(wd[p] & 0xFFFFu), w1 = bf16_bits_to_f32(wd[p] >> 16);
+              const float sh0 = s * hv[2 * p], sh1 = s * hv[2 * p + 1];
+              const float v0 = w0 - sh0, v1 = w1 - sh1;
+              out[p] = pack_bf16x2(f32_to_bf16_sr(v0, rw[p] & 0xFFFFu), f32_to_bf16_sr(v1, rw[p] >> 16));
+            }
+            *reinterpret_cast<uint4*>(it.W + i * it.ldw + jj) = make_uint4(out[0], out[1], out[2], out[3]);
+          }
         }
       }
-    } else {
+    }
+  };
+
+  // Software pipeline over the workgroup's tiles, three deep, unrolled by
+  // three so that the register and LDS buffers keep fixed roles. At the top
+  // of tile u: W(u) was loaded two tiles ago, P(u) is in LDS buffer u%3, and
+  // P(u+1) was loaded to registers one tile ago. Tile u then issues the loads
+  // of tile u+2, processes u, and stages P(u+1) into LDS for the next tile.
+  // The barrier before each tile publishes the staged P and guarantees that
+  // the buffer being overwritten (read two tiles earlier) is free.
+  TileRegs<R> t3[3];
+  load_unit(u0, t3[0]);
+  load_unit(u0 + 1, t3[1]);
+  stage_unit(u0, t3[0], lds_p[0]);
+  for (int64_t u = u0; u < u1; u += 3) {
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int64_t jj = j0 + 8 * half;
-        if (jj >= k) continue;
-        uint4* wp = reinterpret_cast<uint4*>(W + i * ldw + jj);
-        const uint4 wv = *wp;
-        const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
-        uint32_t rw[4];
-        rounding_words(seed, i, jj >> 3, rw);
-        uint32_t out[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const float w0 = bf16_bits_to_f32(wd[p] & 0xFFFFu), w1 = bf16_bits_to_f32(wd[p] >> 16);
-          const float sh0 = s * h[8 * half + 2 * p], sh1 = s * h[8 * half + 2 * p + 1];
-          const float v0 = w0 - sh0, v1 = w1 - sh1;
-          out[p] = pack_bf16x2(f32_to_bf16_sr(v0, rw[p] & 0xFFFFu), f32_to_bf16_sr(v1, rw[p] >> 16));
-        }
-        *wp = make_uint4(out[0], out[1], out[2], out[3]);
-      }
+    for (int v = 0; v < 3; ++v) {
+      if (u + v >= u1) break;
+      load_unit(u + v + 2, t3[(v + 2) % 3]);
+      __syncthreads();
+      process(u + v, t3[v], lds_p[v]);
+      stage_unit(u + v + 1, t3[(v + 1) % 3], lds_p[(v + 1) % 3]);
     }
   }
 
   if constexpr (MODE == kModeNorms) {
-    __shared__ double red[2][4];
     sw = wave_sum(sw);
     sh = wave_sum(sh);
     if (lane == 0) {
@@ -245,10 +345,54 @@ __global__ __launch_bounds__(256) void apply_kernel(uint16_t* __restrict__ W, in
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-      const int64_t bid = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-      partials[2 * bid] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
-      partials[2 * bid + 1] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
+      b.partials[2 * w] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+      b.partials[2 * w + 1] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
     }
+  }
+}
+
+// Per item: fixed-order sum of its norms partials (thread t holds partials
+// t, t+256, ... in order; then a butterfly within each wave and the waves in
+// order), and s = fp32(tau * ||W|| / ||H||); flag = 1 when ||H|| is zero or
+// not finite or s is not finite (then s = 0).
+__global__ __launch_bounds__(256) void apply_scale_kernel(ApplyBatch b) {
+  __shared__ double red[2][4];
+  const int m = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int w0 = b.wbase[m], w1 = b.wbase[m + 1];
+  double aw = 0.0, ah = 0.0;
+  for (int w = w0 + (int)threadIdx.x; w < w1; w += 256) {
+    aw += b.partials[2 * w];
+    ah += b.partials[2 * w + 1];
+  }
+  aw = wave_sum(aw);
+  ah = wave_sum(ah);
+  if (lane == 0) {
+    red[0][wave] = aw;
+    red[1][wave] = ah;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  const double nw = sqrt(((red[0][0] + red[0][1]) + red[0][2]) + red[0][3]);
+  const double nh = sqrt(((red[1][0] + red[1][1]) + red[1][2]) + red[1][3]);
+  float s = 0.f, flag = 0.f;
+  if (!(nh > 0.0) || !isfinite(nh)) {
+    flag = 1.f;
+  } else {
+    s = (float)((double)b.tau * nw / nh);
+    if (!isfinite(s)) {
+      s = 0.f;
+      flag = 1.f;
+    }
+  }
+  b.scale[2 * m] = s;
+  b.scale[2 * m + 1] = flag;
+  float* st = b.it[m].stats;
+  if (st) {
+    st[0] = (float)nw;
+    st[1] = (float)nh;
+    st[2] = s;
+    st[3] = flag;
   }
 }
 
@@ -281,55 +425,87 @@ __global__ void philox_kernel(uint64_t seed, int64_t n, const uint32_t* __restri
 
 namespace {
 
-struct ApplyPlan {
-  int64_t row_blocks, col_tiles;
-  int tiles_per_wg;
-  int64_t col_groups;
-};
+// Workgroups per matrix: one per kApplyUnitsPerWG tiles, a function of the
+// matrix's own shape only, so that a matrix gets the same partition (and so
+// the same norm sums and bits) alone or in any batch. Twelve tiles of 128 x
+// 64 give the Qwen3-1.7B-shaped block 512 workgroups, two per compute unit.
+constexpr int64_t kApplyUnitsPerWG = 12;
 
-// Grid over (64-row blocks) x (groups of 64-column tiles) with at most
-// `target` workgroups.
-ApplyPlan apply_plan(int64_t d, int64_t k, int64_t target) {
-  ApplyPlan p;
-  p.row_blocks = (d + kApplyRowsPerWG - 1) / kApplyRowsPerWG;
-  p.col_tiles = (k + kApplyColsPerTile - 1) / kApplyColsPerTile;
-  int64_t tpw = (p.row_blocks * p.col_tiles + target - 1) / target;
-  if (tpw < 1) tpw = 1;
-  if (tpw > p.col_tiles) tpw = p.col_tiles;
-  p.tiles_per_wg = (int)tpw;
-  p.col_groups = (p.col_tiles + tpw - 1) / tpw;
-  return p;
+template <int R>
+void apply_plan(ApplyBatch& b, int n, const int64_t* ds, const int64_t* ks) {
+  using Tr = ApplyTraits<R>;
+  const int forced = env_int("RGC_APPLY_UNITS", 0);
+  const int64_t per = forced > 0 ? forced : kApplyUnitsPerWG;
+  b.wbase[0] = 0;
+  for (int m = 0; m < n; ++m) {
+    b.it[m].ctiles = (ks[m] + kApplyCols - 1) / kApplyCols;
+    b.it[m].units = (ds[m] + Tr::ROWS - 1) / Tr::ROWS * b.it[m].ctiles;
+    b.wbase[m + 1] = b.wbase[m] + (int)((b.it[m].units + per - 1) / per);
+  }
+  b.n = n;
 }
-// Sweep 1 writes one partial per workgroup and every sweep-2 workgroup reads
-// them all, so sweep 1's grid stays small; sweep 2's is sized for the chip.
-ApplyPlan norms_plan(int64_t d, int64_t k) { return apply_plan(d, k, env_int("RGC_NORM_WGS", 256)); }
-ApplyPlan update_plan(int64_t d, int64_t k) { return apply_plan(d, k, env_int("RGC_APPLY_WGS", 1024)); }
 
-size_t apply_ws(int64_t d, int64_t k) {
-  const ApplyPlan p = norms_plan(d, k);
-  return (size_t)p.row_blocks * p.col_groups * 2 * sizeof(double);
+size_t apply_ws_bytes(int workgroups) {
+  return (size_t)((2 * workgroups * sizeof(double) + 255) / 256 * 256) + 2 * kApplyMaxItems * sizeof(float);
 }
 
 template <int R>
-rgc_status_t apply_launch(uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d, int64_t k,
-                          float tau, uint64_t seed, float* stats, void* ws, hipStream_t s) {
-  const ApplyPlan p1 = norms_plan(d, k), p2 = update_plan(d, k);
-  double* partials = static_cast<double*>(ws);
-  const int nparts = (int)(p1.row_blocks * p1.col_groups);
-  hipLaunchKernelGGL((apply_kernel<R, kModeNorms>), dim3((unsigned)p1.row_blocks, (unsigned)p1.col_groups), dim3(256),
-                     0, s, W, ldw, C, P, d, k, p1.tiles_per_wg, tau, seed, nullptr, partials, nparts, nullptr);
-  hipLaunchKernelGGL((apply_kernel<R, kModeUpdate>), dim3((unsigned)p2.row_blocks, (unsigned)p2.col_groups), dim3(256),
-                     0, s, W, ldw, C, P, d, k, p2.tiles_per_wg, tau, seed, stats, partials, nparts, nullptr);
+size_t apply_ws_for(int n, const int64_t* ds, const int64_t* ks) {
+  ApplyBatch b = {};
+  apply_plan<R>(b, n, ds, ks);
+  return apply_ws_bytes(b.wbase[n]);
+}
+
+template <int R>
+rgc_status_t apply_launch(int n, uint16_t* const* Ws, const int64_t* ldws, const float* const* Cs,
+                          const uint16_t* const* Ps, const int64_t* ds, const int64_t* ks, float tau,
+                          const uint64_t* seeds, float* const* stats, void* ws, hipStream_t st) {
+  ApplyBatch b = {};
+  apply_plan<R>(b, n, ds, ks);
+  b.tau = tau;
+  for (int m = 0; m < n; ++m) {
+    b.it[m].W = Ws[m];
+    b.it[m].ldw = ldws[m];
+    b.it[m].C = Cs[m];
+    b.it[m].P = Ps[m];
+    b.it[m].d = ds[m];
+    b.it[m].k = ks[m];
+    b.it[m].seed = seeds[m];
+    b.it[m].stats = stats ? stats[m] : nullptr;
+  }
+  const int G = b.wbase[n];
+  b.partials = static_cast<double*>(ws);
+  b.scale = reinterpret_cast<float*>(static_cast<char*>(ws) + (apply_ws_bytes(G) - 2 * kApplyMaxItems * sizeof(float)));
+  hipLaunchKernelGGL((apply_kernel<R, kModeNorms>), dim3((unsigned)G), dim3(256), 0, st, b);
+  hipLaunchKernelGGL(apply_scale_kernel, dim3((unsigned)n), dim3(256), 0, st, b);
+  hipLaunchKernelGGL((apply_kernel<R, kModeUpdate>), dim3((unsigned)G), dim3(256), 0, st, b);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
 template <int R>
-rgc_status_t reconstruct_launch(const float* C, const uint16_t* P, float* H, int64_t d, int64_t k, hipStream_t s) {
-  const ApplyPlan p = update_plan(d, k);
-  dim3 grid((unsigned)p.row_blocks, (unsigned)p.col_groups);
-  hipLaunchKernelGGL((apply_kernel<R, kModeReconstruct>), grid, dim3(256), 0, s, nullptr, k, C, P, d, k,
-                     p.tiles_per_wg, 0.f, 0ull, nullptr, nullptr, 0, H);
+rgc_status_t reconstruct_launch(const float* C, const uint16_t* P, float* H, int64_t d, int64_t k, hipStream_t st) {
+  ApplyBatch b = {};
+  apply_plan<R>(b, 1, &d, &k);
+  b.it[0].C = C;
+  b.it[0].P = P;
+  b.it[0].d = d;
+  b.it[0].k = k;
+  b.H = H;
+  hipLaunchKernelGGL((apply_kernel<R, kModeReconstruct>), dim3((unsigned)b.wbase[1]), dim3(256), 0, st, b);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+}
+
+rgc_status_t check_apply_shape(int64_t ldw, int64_t d, int64_t k, int64_t r) {
+  return (d <= 0 || k <= 0 || r > k || ldw < k) ? RGC_ERR_SHAPE : RGC_OK;
+}
+
+rgc_status_t check_apply_item(const uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d,
+                              int64_t k, const float* stats) {
+  if ((d % 8) != 0 || (k % 8) != 0) return RGC_ERR_UNSUPPORTED;
+  if (!W || !C || !P) return RGC_ERR_NULL;
+  if (!aligned16(W) || !aligned16(C) || !aligned16(P) || (ldw % 8) != 0) return RGC_ERR_ALIGN;
+  if (stats && !aligned_to(stats, 4)) return RGC_ERR_ALIGN;
+  return RGC_OK;
 }
 
 }  // namespace
@@ -337,27 +513,50 @@ rgc_status_t reconstruct_launch(const float* C, const uint16_t* P, float* H, int
 
 using namespace rgc;
 
+extern "C" size_t rgc_apply_batch_workspace_size(int64_t n, const int64_t* ds, const int64_t* ks, int64_t r) {
+  if (n <= 0 || n > kApplyMaxItems || !ds || !ks || !rank_supported(r)) return 0;
+  for (int64_t m = 0; m < n; ++m)
+    if (ds[m] <= 0 || ks[m] <= 0) return 0;
+  size_t out = 0;
+  dispatch_rank(r, [&](auto rc) { out = apply_ws_for<decltype(rc)::value>((int)n, ds, ks); });
+  return out;
+}
+
+extern "C" rgc_status_t rgc_apply_batch(int64_t n, uint16_t* const* Ws, const int64_t* ldws, const float* const* Cs,
+                                        const uint16_t* const* Ps, const int64_t* ds, const int64_t* ks, int64_t r,
+                                        float tau, const uint64_t* seeds, float* const* stats, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  if (n < 0 || r <= 0) return RGC_ERR_SHAPE;
+  if (n > kApplyMaxItems) return RGC_ERR_UNSUPPORTED;
+  if (n == 0) return RGC_OK;
+  if (!Ws || !ldws || !Cs || !Ps || !ds || !ks || !seeds) return RGC_ERR_NULL;
+  for (int64_t m = 0; m < n; ++m)
+    if (check_apply_shape(ldws[m], ds[m], ks[m], r) != RGC_OK) return RGC_ERR_SHAPE;
+  if (!rank_supported(r)) return RGC_ERR_UNSUPPORTED;
+  for (int64_t m = 0; m < n; ++m) {
+    const rgc_status_t st = check_apply_item(Ws[m], ldws[m], Cs[m], Ps[m], ds[m], ks[m], stats ? stats[m] : nullptr);
+    if (st != RGC_OK) return st;
+  }
+  const size_t need = rgc_apply_batch_workspace_size(n, ds, ks, r);
+  if (!ws || ws_bytes < need) return RGC_ERR_WORKSPACE;
+  if (!aligned_to(ws, 256)) return RGC_ERR_ALIGN;
+  rgc_status_t st = RGC_OK;
+  dispatch_rank(r, [&](auto rc) {
+    st = apply_launch<decltype(rc)::value>((int)n, Ws, ldws, Cs, Ps, ds, ks, tau, seeds, stats, ws,
+                                           static_cast<hipStream_t>(stream));
+  });
+  return st;
+}
+
 extern "C" size_t rgc_apply_workspace_size(int64_t d, int64_t k, int64_t r) {
-  if (d <= 0 || k <= 0 || !rank_supported(r)) return 0;
-  return apply_ws(d, k);
+  return rgc_apply_batch_workspace_size(1, &d, &k, r);
 }
 
 extern "C" rgc_status_t rgc_apply(uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d, int64_t k,
                                   int64_t r, float tau, uint64_t seed, float* stats, void* ws, size_t ws_bytes,
                                   void* stream) {
-  if (d <= 0 || k <= 0 || r <= 0 || r > k || ldw < k) return RGC_ERR_SHAPE;
-  if (!rank_supported(r) || (d % 8) != 0 || (k % 8) != 0) return RGC_ERR_UNSUPPORTED;
-  if (!W || !C || !P) return RGC_ERR_NULL;
-  if (!aligned16(W) || !aligned16(C) || !aligned16(P) || (ldw % 8) != 0) return RGC_ERR_ALIGN;
-  if (stats && !aligned_to(stats, 4)) return RGC_ERR_ALIGN;
-  const size_t need = apply_ws(d, k);
-  if (!ws || ws_bytes < need) return RGC_ERR_WORKSPACE;
-  if (!aligned_to(ws, 256)) return RGC_ERR_ALIGN;
-  rgc_status_t st = RGC_OK;
-  dispatch_rank(r, [&](auto rc) {
-    st = apply_launch<decltype(rc)::value>(W, ldw, C, P, d, k, tau, seed, stats, ws, static_cast<hipStream_t>(stream));
-  });
-  return st;
+  if (d <= 0 || k <= 0 || r <= 0) return RGC_ERR_SHAPE;
+  return rgc_apply_batch(1, &W, &ldw, &C, &P, &d, &k, r, tau, &seed, &stats, ws, ws_bytes, stream);
 }
 
 extern "C" rgc_status_t rgc_test_reconstruct(const float* C, const uint16_t* P, float* H, int64_t d, int64_t k,

@@ -51,6 +51,10 @@ SIGNATURES = {
                                             ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64, _i64, _vp, _sz, _vp]),
     "rgc_accumulate": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
     "rgc_apply_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "rgc_apply_batch_workspace_size": (_sz, [_i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i64]),
+    "rgc_apply_batch": (ctypes.c_int, [_i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_vp),
+                                       ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i64, _f32,
+                                       ctypes.POINTER(_u64), ctypes.POINTER(_vp), _vp, _sz, _vp]),
     "rgc_apply": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _f32, _u64, _vp, _vp, _sz, _vp]),
     "rgc_test_philox": (ctypes.c_int, [_u64, _i64, _vp, _vp, _vp]),
     "rgc_test_stochastic_round": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _u64, _vp]),
@@ -305,6 +309,48 @@ def rgc_apply(W: torch.Tensor, C: torch.Tensor, P: torch.Tensor, tau: float, see
     _check(lib.rgc_apply(W.data_ptr(), ldw, C.data_ptr(), P.data_ptr(), d, k, r, float(tau),
                          seed & 0xFFFFFFFFFFFFFFFF, sp, wp, wn, _stream(dev)))
     return W
+
+
+def rgc_apply_batch(Ws, Cs, Ps, tau: float, seeds, stats=None, workspace: Workspace | None = None):
+    """rgc_apply for several matrices of one rank in three launches (one seed
+    per matrix; stats: None or a list of device float[4] tensors or Nones)."""
+    lib = load_library()
+    n = len(Ws)
+    if n == 0:
+        return Ws
+    if len(Cs) != n or len(Ps) != n or len(seeds) != n or (stats is not None and len(stats) != n):
+        raise RgcError("Ws, Cs, Ps, seeds (and stats) must have the same length")
+    dev = _need_gpu(*Ws, *Cs, *Ps)
+    r = Cs[0].shape[1]
+    ldws, ds, ks = [], [], []
+    for W, C, P in zip(Ws, Cs, Ps):
+        ldws.append(_rows(W, torch.bfloat16, "W"))
+        _dense(C, torch.float32, "C")
+        _dense(P, torch.bfloat16, "P")
+        d, k = W.shape
+        if tuple(C.shape) != (d, r) or tuple(P.shape) != (k, r):
+            raise RgcError("batch items must share r: W d x k, C d x r, P k x r")
+        ds.append(d)
+        ks.append(k)
+    sps = None
+    if stats is not None:
+        vals = []
+        for st in stats:
+            if st is None:
+                vals.append(None)
+                continue
+            _need_gpu(st)
+            _dense(st, torch.float32, "stats")
+            if st.numel() < 4:
+                raise RgcError("stats needs 4 floats")
+            vals.append(st.data_ptr())
+        sps = (_vp * n)(*vals)
+    seeds_arr = (_u64 * n)(*[s & 0xFFFFFFFFFFFFFFFF for s in seeds])
+    ws = workspace or default_workspace(dev)
+    wp, wn = ws.get(lib.rgc_apply_batch_workspace_size(n, _i64s(ds), _i64s(ks), r))
+    _check(lib.rgc_apply_batch(n, _ptrs(Ws), _i64s(ldws), _ptrs(Cs), _ptrs(Ps), _i64s(ds), _i64s(ks), r,
+                               float(tau), seeds_arr, sps, wp, wn, _stream(dev)))
+    return Ws
 
 
 # ---- test hooks -------------------------------------------------------------

@@ -315,6 +315,47 @@ def test_apply_is_deterministic_and_seeded(dev):
     assert not np.array_equal(outs[0], outs[2])
 
 
+def test_apply_batch_matches_single_applies(dev):
+    """One batched call over a block's shapes gives every matrix exactly the
+    bits (and stats) of its own rgc_apply, and matches the oracle."""
+    r, tau = 64, 1e-3
+    shapes = [(2048, 2048), (1024, 2048), (6144, 2048), (2048, 6144), (264, 520)]
+    items = [_apply_inputs(d, k, r, 40 + i) for i, (d, k) in enumerate(shapes)]
+    seeds = [(5 << 32) | i for i in range(len(shapes))]
+    wb = [w.clone().to(dev) for w, _, _ in items]
+    cs = [c.to(dev) for _, c, _ in items]
+    ps = [p.to(dev) for _, _, p in items]
+    stats_b = [torch.zeros(4, device=dev) for _ in shapes]
+    rgc.rgc_apply_batch(wb, cs, ps, tau, seeds, stats=stats_b)
+    for i, (w, c, p) in enumerate(items):
+        ws_ = w.clone().to(dev)
+        st = torch.zeros(4, device=dev)
+        rgc.rgc_apply(ws_, cs[i], ps[i], tau, seeds[i], stats=st)
+        _sync()
+        assert np.array_equal(bits(ws_), bits(wb[i])), shapes[i]
+        assert torch.equal(st, stats_b[i])
+    d, k = shapes[-1]
+    w, c, p = items[-1]
+    ref_w, ref_stats = orc.apply_update(bits(w), c.numpy(), bits(p), tau, seeds[-1])
+    np.testing.assert_allclose(stats_b[-1].cpu().numpy()[:3], ref_stats[:3], rtol=1e-5)
+    abs_terms = np.abs(c.numpy().astype(np.float64)) @ np.abs(orc.bf16_to_f64(bits(p))).T
+    assert_update_close(bits(wb[-1]), ref_w, ref_stats[2], abs_terms, what="W batch")
+
+
+def test_apply_batch_skips_only_flagged_matrix(dev):
+    r = 16
+    items = [_apply_inputs(256, 512, r, 50), _apply_inputs(256, 512, r, 51)]
+    wb = [w.clone().to(dev) for w, _, _ in items]
+    cs = [torch.zeros(256, r, device=dev), items[1][1].to(dev)]  # first sketch is zero
+    ps = [p.to(dev) for _, _, p in items]
+    stats = [torch.zeros(4, device=dev), torch.zeros(4, device=dev)]
+    rgc.rgc_apply_batch(wb, cs, ps, 1e-3, [1, 2], stats=stats)
+    _sync()
+    assert np.array_equal(bits(wb[0]), bits(items[0][0]))
+    assert stats[0].cpu().numpy()[3] == 1 and stats[1].cpu().numpy()[3] == 0
+    assert not np.array_equal(bits(wb[1]), bits(items[1][0]))
+
+
 # ---------------------------------------------------------------------------
 # End to end: the small single-layer case (d=256, k=512, r=16, 4 x 256 tokens)
 # ---------------------------------------------------------------------------

@@ -55,7 +55,8 @@ def test_workspace_queries(lib):
     assert qr >= 2 * 2048 * 64 * 8
     assert lib.rgc_sample_projection_workspace_size(1, 2048, 256) == 0  # QR limited to r <= 128
     assert lib.rgc_accumulate_workspace_size(4096, 2048, 64) >= 0
-    assert lib.rgc_apply_workspace_size(2048, 2048, 64) >= 4096
+    small = lib.rgc_apply_workspace_size(2048, 2048, 64)  # per-workgroup norm partials + step scalars
+    assert small > 0 and lib.rgc_apply_workspace_size(8192, 8192, 64) > small
     assert lib.rgc_apply_workspace_size(2048, 2048, 40) == 0  # unsupported rank
 
 
@@ -106,6 +107,33 @@ def test_apply_validation(lib):
     assert lib.rgc_apply(FAKE, 256, FAKE, FAKE, 64, 256, 16, f, 0, FAKE + 2, FAKE, 1 << 20, s) == ALIGN
     assert lib.rgc_apply(FAKE, 256, FAKE, FAKE, 64, 256, 16, f, 0, None, None, 0, s) == WS
     assert lib.rgc_apply(FAKE, 256, FAKE, FAKE, 64, 256, 16, f, 0, None, FAKE + 64, 1 << 20, s) == ALIGN
+
+
+def test_apply_batch_validation(lib):
+    s = None
+    f = ctypes.c_float(1e-3)
+    n = 2
+    ws_ = (ctypes.c_void_p * n)(FAKE, FAKE)
+    cs = (ctypes.c_void_p * n)(FAKE, FAKE)
+    ps = (ctypes.c_void_p * n)(FAKE, FAKE)
+    lds = (ctypes.c_int64 * n)(256, 512)
+    ds = (ctypes.c_int64 * n)(64, 128)
+    ks = (ctypes.c_int64 * n)(256, 512)
+    seeds = (ctypes.c_uint64 * n)(1, 2)
+    need = lib.rgc_apply_batch_workspace_size(n, ds, ks, 64)
+    assert need > 0
+    assert lib.rgc_apply_batch(0, None, None, None, None, None, None, 64, f, None, None, None, 0, s) == OK
+    assert lib.rgc_apply_batch(17, ws_, lds, cs, ps, ds, ks, 64, f, seeds, None, FAKE, need, s) == UNSUP
+    assert lib.rgc_apply_batch(n, ws_, lds, cs, ps, ds, ks, 64, f, None, None, FAKE, need, s) == NULL  # seeds
+    bad_ld = (ctypes.c_int64 * n)(256, 500)
+    assert lib.rgc_apply_batch(n, ws_, bad_ld, cs, ps, ds, ks, 64, f, seeds, None, FAKE, need, s) == SHAPE
+    assert lib.rgc_apply_batch(n, ws_, lds, cs, ps, ds, ks, 80, f, seeds, None, FAKE, need, s) == UNSUP
+    bad_c = (ctypes.c_void_p * n)(FAKE, FAKE + 4)
+    assert lib.rgc_apply_batch(n, ws_, lds, bad_c, ps, ds, ks, 64, f, seeds, None, FAKE, need, s) == ALIGN
+    assert lib.rgc_apply_batch(n, ws_, lds, cs, ps, ds, ks, 64, f, seeds, None, FAKE, need - 8, s) == WS
+    # a matrix's workspace share does not depend on the rest of the batch
+    one = lib.rgc_apply_workspace_size(64, 256, 64)
+    assert 0 < one <= need
 
 
 def test_projection_validation(lib):
