@@ -40,6 +40,7 @@ enum ApplyMode { kModeNorms = 0, kModeUpdate = 1, kModeReconstruct = 2 };
 constexpr int kApplyCols = 64;     // columns per tile
 constexpr int kApplyWaves = 4;
 constexpr int kApplyMaxItems = 16;
+constexpr int64_t kMaxApplyDim = int64_t(1) << 30;  // d and k
 
 template <int R>
 struct ApplyTraits {
@@ -130,32 +131,32 @@ struct TileRegs {
 };
 
 // Issues the loads of tile (row0, jb): the P rows jb .. jb+63 (clamped to
-// k-1; zeroed when written to LDS) and, unless NORM-only reconstruction, the
+// k-1; zeroed when written to LDS) and, except for reconstruction, the
 // lane's W chunks (rows clamped to d-1, chunks clamped to k-8; such values
 // are never stored or counted).
 template <int R, int MODE>
-__device__ __forceinline__ void load_tile(const ApplyItem& it, int64_t row0, int64_t jb, int wave, int lane,
+__device__ __forceinline__ void load_tile(const ApplyItem& it, int row0, int jb, int wave, int lane,
                                           TileRegs<R>& t) {
   using Tr = ApplyTraits<R>;
+  const int k = (int)it.k, d = (int)it.d;
 #pragma unroll
   for (int c = 0; c < Tr::PCPT; ++c) {
     const int chunk = (int)threadIdx.x + 256 * c;
     const int jl = chunk / (R / 8), part = chunk % (R / 8);
-    int64_t j = jb + jl;
-    j = j < it.k ? j : it.k - 1;
-    if (chunk < Tr::PCHUNKS) t.p[c] = *reinterpret_cast<const uint4*>(it.P + j * R + 8 * part);
+    const int j = jb + jl < k ? jb + jl : k - 1;
+    if (chunk < Tr::PCHUNKS) t.p[c] = *reinterpret_cast<const uint4*>(it.P + (int64_t)j * R + 8 * part);
   }
   if constexpr (MODE != kModeReconstruct) {
     const int n = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int nt = 0; nt < Tr::NTW; ++nt) {
-      int64_t i = row0 + Tr::RW * wave + 16 * nt + n;
-      i = i < it.d ? i : it.d - 1;
+      int i = row0 + Tr::RW * wave + 16 * nt + n;
+      i = i < d ? i : d - 1;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        int64_t jj = jb + 16 * g + 8 * half;
-        jj = jj < it.k ? jj : it.k - 8;
-        t.w[nt][half] = *reinterpret_cast<const uint4*>(it.W + i * it.ldw + jj);
+        int jj = jb + 16 * g + 8 * half;
+        jj = jj < k ? jj : k - 8;
+        t.w[nt][half] = *reinterpret_cast<const uint4*>(it.W + (int64_t)i * it.ldw + jj);
       }
     }
   }
@@ -164,7 +165,7 @@ __device__ __forceinline__ void load_tile(const ApplyItem& it, int64_t row0, int
 // Writes this thread's share of the P tile into an LDS buffer (rows past k
 // and rank columns past R as zeros).
 template <int R>
-__device__ __forceinline__ void stage_p(const TileRegs<R>& t, int64_t jb, int64_t k, uint16_t* lds_p) {
+__device__ __forceinline__ void stage_p(const TileRegs<R>& t, int jb, int k, uint16_t* lds_p) {
   using Tr = ApplyTraits<R>;
 #pragma unroll
   for (int c = 0; c < Tr::PCPT; ++c) {
@@ -245,57 +246,76 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
 
   double sw = 0.0, sh = 0.0;
   RowOperand<R> rop;
-  int64_t rb_loaded = -1;
+  int rb_loaded = -1;
+  const int d = (int)it.d, k = (int)it.k, ctiles = (int)it.ctiles;
 
-  auto tile_at = [&](int64_t u, int64_t& row0, int64_t& jb) {
-    row0 = (u / it.ctiles) * Tr::ROWS;
-    jb = (u % it.ctiles) * kApplyCols;
+  // Tile cursors (row block, column tile), advanced one tile at a time; past
+  // the range they stay on the last tile (reloaded, never used).
+  struct Cursor {
+    int64_t u;
+    int rb, ct;
   };
-  auto load_unit = [&](int64_t u, TileRegs<R>& t) {
-    int64_t row0, jb;
-    tile_at(u < u1 ? u : u1 - 1, row0, jb);  // past the range: reload the last tile (never used)
-    load_tile<R, MODE>(it, row0, jb, wave, lane, t);
+  auto cursor_at = [&](int64_t u) {
+    Cursor c;
+    c.u = u;
+    c.rb = (int)(u / ctiles);
+    c.ct = (int)(u % ctiles);
+    return c;
   };
-  auto stage_unit = [&](int64_t u, const TileRegs<R>& t, uint16_t* buf) {
-    int64_t row0, jb;
-    tile_at(u < u1 ? u : u1 - 1, row0, jb);
-    stage_p<R>(t, jb, it.k, buf);
+  auto advance = [&](Cursor& c) {
+    if (c.u + 1 < u1) {
+      if (++c.ct == ctiles) {
+        c.ct = 0;
+        ++c.rb;
+      }
+    }
+    ++c.u;
   };
-  auto process = [&](int64_t u, const TileRegs<R>& t, const uint16_t* buf) {
-    int64_t row0, jb;
-    tile_at(u, row0, jb);
-    const int64_t rb = row0 / Tr::ROWS;
-    if (rb != rb_loaded) {  // wave-uniform: a new row block
+  auto load_at = [&](const Cursor& c, TileRegs<R>& t) {
+    load_tile<R, MODE>(it, c.rb * Tr::ROWS, c.ct * kApplyCols, wave, lane, t);
+  };
+  auto stage_at = [&](const Cursor& c, const TileRegs<R>& t, uint16_t* buf) {
+    stage_p<R>(t, c.ct * kApplyCols, k, buf);
+  };
+  auto process = [&](const Cursor& c, const TileRegs<R>& t, const uint16_t* buf) {
+    const int row0 = c.rb * Tr::ROWS, jb = c.ct * kApplyCols;
+    if (c.rb != rb_loaded) {  // wave-uniform: a new row block
       load_row_operand<R>(it.C, it.d, row0 + Tr::RW * wave, lane, rop);
-      rb_loaded = rb;
+      rb_loaded = c.rb;
     }
     float h[Tr::NTW][16];
     rebuild_tile<R>(buf, rop, lane, h);
+    // Every lane does the arithmetic; only the stores (and the norm sums)
+    // depend on whether its element lies inside W.
 #pragma unroll
     for (int nt = 0; nt < Tr::NTW; ++nt) {
-      const int64_t i = row0 + Tr::RW * wave + 16 * nt + n;
-      if (i >= it.d) continue;
+      const int i = row0 + Tr::RW * wave + 16 * nt + n;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int64_t jj = jb + 16 * g + 8 * half;
-        if (jj >= it.k) continue;
+        const int jj = jb + 16 * g + 8 * half;
+        const bool inside = i < d && jj < k;
         const float* hv = &h[nt][8 * half];
         if constexpr (MODE == kModeReconstruct) {
-          float4* dst = reinterpret_cast<float4*>(b.H + i * it.k + jj);
-          dst[0] = make_float4(hv[0], hv[1], hv[2], hv[3]);
-          dst[1] = make_float4(hv[4], hv[5], hv[6], hv[7]);
+          if (inside) {
+            float4* dst = reinterpret_cast<float4*>(b.H + (int64_t)i * k + jj);
+            dst[0] = make_float4(hv[0], hv[1], hv[2], hv[3]);
+            dst[1] = make_float4(hv[4], hv[5], hv[6], hv[7]);
+          }
         } else {
           const uint4 wv = t.w[nt][half];
           const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
           if constexpr (MODE == kModeNorms) {
+            double pw = 0.0, ph = 0.0;
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
               const double w0 = (double)bf16_bits_to_f32(wd[p] & 0xFFFFu);
               const double w1 = (double)bf16_bits_to_f32(wd[p] >> 16);
               const double h0 = (double)hv[2 * p], h1 = (double)hv[2 * p + 1];
-              sw += w0 * w0 + w1 * w1;
-              sh += h0 * h0 + h1 * h1;
+              pw += w0 * w0 + w1 * w1;
+              ph += h0 * h0 + h1 * h1;
             }
+            sw += inside ? pw : 0.0;
+            sh += inside ? ph : 0.0;
           } else {
             uint32_t rw[4];
             rounding_words(it.seed, i, jj >> 3, rw);
@@ -307,7 +327,8 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
               const float v0 = w0 - sh0, v1 = w1 - sh1;
               out[p] = pack_bf16x2(f32_to_bf16_sr(v0, rw[p] & 0xFFFFu), f32_to_bf16_sr(v1, rw[p] >> 16));
             }
-            *reinterpret_cast<uint4*>(it.W + i * it.ldw + jj) = make_uint4(out[0], out[1], out[2], out[3]);
+            if (inside)
+              *reinterpret_cast<uint4*>(it.W + (int64_t)i * it.ldw + jj) = make_uint4(out[0], out[1], out[2], out[3]);
           }
         }
       }
@@ -322,17 +343,25 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
   // The barrier before each tile publishes the staged P and guarantees that
   // the buffer being overwritten (read two tiles earlier) is free.
   TileRegs<R> t3[3];
-  load_unit(u0, t3[0]);
-  load_unit(u0 + 1, t3[1]);
-  stage_unit(u0, t3[0], lds_p[0]);
+  Cursor cp = cursor_at(u0);  // tile being processed
+  Cursor cs = cp;             // tile whose P is staged next
+  advance(cs);
+  Cursor cl = cs;             // tile whose loads are issued next
+  advance(cl);
+  load_at(cp, t3[0]);
+  load_at(cs, t3[1]);
+  stage_at(cp, t3[0], lds_p[0]);
   for (int64_t u = u0; u < u1; u += 3) {
 #pragma unroll
     for (int v = 0; v < 3; ++v) {
       if (u + v >= u1) break;
-      load_unit(u + v + 2, t3[(v + 2) % 3]);
+      load_at(cl, t3[(v + 2) % 3]);
       __syncthreads();
-      process(u + v, t3[v], lds_p[v]);
-      stage_unit(u + v + 1, t3[(v + 1) % 3], lds_p[(v + 1) % 3]);
+      process(cp, t3[v], lds_p[v]);
+      stage_at(cs, t3[(v + 1) % 3], lds_p[(v + 1) % 3]);
+      advance(cp);
+      advance(cs);
+      advance(cl);
     }
   }
 
@@ -501,7 +530,8 @@ rgc_status_t check_apply_shape(int64_t ldw, int64_t d, int64_t k, int64_t r) {
 
 rgc_status_t check_apply_item(const uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d,
                               int64_t k, const float* stats) {
-  if ((d % 8) != 0 || (k % 8) != 0) return RGC_ERR_UNSUPPORTED;
+  // element indices are 32-bit inside the kernels
+  if ((d % 8) != 0 || (k % 8) != 0 || d > kMaxApplyDim || k > kMaxApplyDim) return RGC_ERR_UNSUPPORTED;
   if (!W || !C || !P) return RGC_ERR_NULL;
   if (!aligned16(W) || !aligned16(C) || !aligned16(P) || (ldw % 8) != 0) return RGC_ERR_ALIGN;
   if (stats && !aligned_to(stats, 4)) return RGC_ERR_ALIGN;

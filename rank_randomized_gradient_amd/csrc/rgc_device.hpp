@@ -80,19 +80,23 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 // fp32 -> bf16, round to nearest even; NaN becomes a quiet NaN keeping its sign.
+// (Written as selects, not branches, so that it stays branch-free per lane.)
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   const uint32_t b = __float_as_uint(f);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (b >> 16) | 0x40u;
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+  const uint32_t rounded = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+  return (b & 0x7FFFFFFFu) > 0x7F800000u ? ((b >> 16) | 0x40u) : rounded;
 }
 
 // Stochastic rounding fp32 -> bf16 with 16 random bits: the random integer is
 // added to the dropped low half, so the kept half rounds up with probability
 // (low half) / 2^16. Infinities are kept, NaN becomes a quiet NaN.
+// (Selects, not branches: the sum is formed for every input and discarded for
+// infinities and NaNs.)
 __device__ __forceinline__ uint32_t f32_to_bf16_sr(float f, uint32_t r16) {
   const uint32_t b = __float_as_uint(f);
-  if ((b & 0x7F800000u) == 0x7F800000u) return (b & 0x007FFFFFu) ? ((b >> 16) | 0x40u) : (b >> 16);
-  return (b + r16) >> 16;
+  const uint32_t rounded = (b + r16) >> 16;
+  const uint32_t special = (b & 0x007FFFFFu) ? ((b >> 16) | 0x40u) : (b >> 16);
+  return (b & 0x7F800000u) == 0x7F800000u ? special : rounded;
 }
 
 // Two bf16 packed in a dword, element 0 in the low half.
