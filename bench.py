@@ -43,7 +43,48 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB three times (a plain copy kernel of "
+                         "known size, for calibrating the profiler's HBM byte counters)")
     return ap.parse_args()
+
+
+# Sources the accumulate kernel is built from; the HBM traffic recorded from
+# profiler counters is reported only while they are unchanged.
+KERNEL_SOURCES = ["rank_randomized_gradient_amd/csrc/rgc_sketch.hip", "rank_randomized_gradient_amd/csrc/rgc_device.hpp",
+                  "rank_randomized_gradient_amd/csrc/rgc_internal.hpp"]
+TRAFFIC_RECORD = "profiles/traffic_accumulate_qwen3_1p7b_block_r64.md"
+
+
+def sources_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per accumulate launch measured with rocprofv3 counters (see the
+    record for the commands and the copy-kernel scaling), or None when the
+    record is missing or was taken from different kernel sources."""
+    path = os.path.join(ROOT, TRAFFIC_RECORD)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.lstrip().startswith("- "):
+                key, _, val = line.strip()[2:].partition(":")
+                fields[key.strip()] = val.strip().strip("`")
+    if fields.get("sources_sha256") != sources_digest():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def step_seed(step: int, m: int) -> int:
@@ -178,8 +219,17 @@ def main():
     roofline = None
     if kern:
         a = kern["accumulate"]
-        roofline = {"kernel": "accumulate_kernel<64>", "bound": "hbm", "achieved": round(a["GBs"], 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(a["hbm_frac"], 4), "traffic": None}
+        roofline = {"kernel": "rgc_accumulate_batch (accumulate_kernel<64> + finish_tiles_kernel<64,false>)",
+                    "bound": "hbm", "achieved": round(a["GBs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(a["hbm_frac"], 4), "traffic": recorded_traffic(),
+                    "algorithmic_bytes_per_launch": acc_bytes // n_mb}
+
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu_baseline:
