@@ -16,7 +16,8 @@
 //   factor   U1 = chol(G1)^-1
 //   gram     Q1 = A U1 (stored), partial Grams of Q1
 //   reduce   G2 = Q1^T Q1
-//   factor   U2 = chol(G2)^-1
+//   factor   U2 = chol(G2)^-1 (G2 is the identity up to rounding, so this is
+//            the first-order expansion I - S unless some |G2 - I| >= 1e-7)
 //   gram     P = bf16(fp32(sqrt(k/r) * Q1 U2))
 // Cholesky factors have a positive diagonal, so Q is the unique factor with
 // the standard sign correction; the second pass restores orthogonality to
@@ -308,6 +309,33 @@ __global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double
       a[i][j] = (l < R && c < R && c >= l) ? G[l * R + c] : 0.0;
       if (l == 0 && c < R) rowbuf[0][c] = a[i][j];
     }
+  if (second) {
+    // G2 = Q1^T Q1 is the identity up to rounding (|G2 - I| ~ 1e-15 for the
+    // Gaussian matrices here). For G2 = I + E, chol(G2) = I + S with S the
+    // upper triangle of E (diagonal halved) up to O(|E|^2), and its inverse
+    // is I - S up to O(|E|^2): below 1e-14 when every |E| < 1e-7, so the
+    // elimination below is skipped. Otherwise it runs as for G1.
+    bool far = false;
+#pragma unroll
+    for (int i = 0; i < T32; ++i)
+#pragma unroll
+      for (int j = 0; j < T32; ++j) {
+        const int l = ty + 32 * i, c = tx + 32 * j;
+        if (l < R && c < R && c >= l) far = far || !(fabs(a[i][j] - (c == l ? 1.0 : 0.0)) < 1e-7);
+      }
+    if (!__syncthreads_or(far)) {
+      if (tid == 0) b.status[m][second] = 0u;
+#pragma unroll
+      for (int i = 0; i < T32; ++i)
+#pragma unroll
+        for (int j = 0; j < T32; ++j) {
+          const int l = ty + 32 * i, c = tx + 32 * j;
+          if (l >= R || c >= R) continue;
+          U[l * R + c] = c < l ? 0.0 : (c == l ? 1.0 - 0.5 * (a[i][j] - 1.0) : -a[i][j]);
+        }
+      return;
+    }
+  }
   for (int j = 0; j < R; ++j) {
     __syncthreads();
     const double* rb = rowbuf[j & 1];
