@@ -287,11 +287,13 @@ __global__ __launch_bounds__(256) void qr_gram_reduce_kernel(QrBatch b, double* 
 // keeps elements (ty + 32a, tx + 32c) in registers: the symmetric Schur
 // complement in the upper triangle and L^-1 (unit diagonal implied) in the
 // strictly lower one. Only the pivot row travels through LDS, double
-// buffered, so each column costs one barrier.
+// buffered, together with its reciprocal pivot, so each column costs one
+// barrier and no division on the critical path of the other threads.
 template <int R>
 __global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double* __restrict__ G_all, int second) {
-  constexpr int T32 = (R + 31) / 32;
+  constexpr int TT = (R + 31) / 32;
   __shared__ double rowbuf[2][R];
+  __shared__ double rinv[2];
   __shared__ double diag[R];
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
@@ -299,15 +301,15 @@ __global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double
   double* U = second ? b.U2[m] : b.U1[m];
   const double* G = G_all + (int64_t)m * R * R;
 
-  // 2. elimination with register-resident elements
-  double a[T32][T32];
+  double a[TT][TT];
 #pragma unroll
-  for (int i = 0; i < T32; ++i)
+  for (int i = 0; i < TT; ++i)
 #pragma unroll
-    for (int j = 0; j < T32; ++j) {
+    for (int j = 0; j < TT; ++j) {
       const int l = ty + 32 * i, c = tx + 32 * j;
       a[i][j] = (l < R && c < R && c >= l) ? G[l * R + c] : 0.0;
       if (l == 0 && c < R) rowbuf[0][c] = a[i][j];
+      if (l == 0 && c == 0) rinv[0] = 1.0 / a[i][j];
     }
   if (second) {
     // G2 = Q1^T Q1 is the identity up to rounding (|G2 - I| ~ 1e-15 for the
@@ -317,18 +319,18 @@ __global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double
     // elimination below is skipped. Otherwise it runs as for G1.
     bool far = false;
 #pragma unroll
-    for (int i = 0; i < T32; ++i)
+    for (int i = 0; i < TT; ++i)
 #pragma unroll
-      for (int j = 0; j < T32; ++j) {
+      for (int j = 0; j < TT; ++j) {
         const int l = ty + 32 * i, c = tx + 32 * j;
         if (l < R && c < R && c >= l) far = far || !(fabs(a[i][j] - (c == l ? 1.0 : 0.0)) < 1e-7);
       }
     if (!__syncthreads_or(far)) {
       if (tid == 0) b.status[m][second] = 0u;
 #pragma unroll
-      for (int i = 0; i < T32; ++i)
+      for (int i = 0; i < TT; ++i)
 #pragma unroll
-        for (int j = 0; j < T32; ++j) {
+        for (int j = 0; j < TT; ++j) {
           const int l = ty + 32 * i, c = tx + 32 * j;
           if (l >= R || c >= R) continue;
           U[l * R + c] = c < l ? 0.0 : (c == l ? 1.0 - 0.5 * (a[i][j] - 1.0) : -a[i][j]);
@@ -339,14 +341,14 @@ __global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double
   for (int j = 0; j < R; ++j) {
     __syncthreads();
     const double* rb = rowbuf[j & 1];
-    const double inv = 1.0 / rb[j];
+    const double inv = rinv[j & 1];
 #pragma unroll
-    for (int i = 0; i < T32; ++i) {
+    for (int i = 0; i < TT; ++i) {
       const int l = ty + 32 * i;
       if (l <= j || l >= R) continue;
       const double f = rb[l] * inv;  // G(l, j) / G(j, j), from the symmetric upper copy
 #pragma unroll
-      for (int jj = 0; jj < T32; ++jj) {
+      for (int jj = 0; jj < TT; ++jj) {
         const int c = tx + 32 * jj;
         if (c >= R) continue;
         if (c >= l || c < j) a[i][jj] -= f * rb[c];
@@ -354,18 +356,19 @@ __global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double
       }
       if (l == j + 1) {
 #pragma unroll
-        for (int jj = 0; jj < T32; ++jj) {
+        for (int jj = 0; jj < TT; ++jj) {
           const int c = tx + 32 * jj;
           if (c < R) rowbuf[(j + 1) & 1][c] = a[i][jj];
+          if (c == l) rinv[(j + 1) & 1] = 1.0 / a[i][jj];
         }
       }
     }
   }
-  // 3. U[x][y] = E(y, x) / sqrt(D_y) above the diagonal, 1 / sqrt(D_y) on it
+  // U[x][y] = E(y, x) / sqrt(D_y) above the diagonal, 1 / sqrt(D_y) on it
 #pragma unroll
-  for (int i = 0; i < T32; ++i)
+  for (int i = 0; i < TT; ++i)
 #pragma unroll
-    for (int j = 0; j < T32; ++j) {
+    for (int j = 0; j < TT; ++j) {
       const int l = ty + 32 * i, c = tx + 32 * j;
       if (l < R && c == l) diag[l] = a[i][j];
     }
@@ -376,9 +379,9 @@ __global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double
     b.status[m][second] = ok ? 0u : 1u;
   }
 #pragma unroll
-  for (int i = 0; i < T32; ++i)
+  for (int i = 0; i < TT; ++i)
 #pragma unroll
-    for (int j = 0; j < T32; ++j) {
+    for (int j = 0; j < TT; ++j) {
       const int l = ty + 32 * i, c = tx + 32 * j;
       if (l >= R || c >= R || c > l) continue;
       const double rs = 1.0 / sqrt(diag[l]);
