@@ -10,28 +10,29 @@ import numpy as np
 import torch
 
 
-def _gen(seed: int) -> torch.Generator:
-    g = torch.Generator(device="cpu")
+def _gen(seed: int, device="cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
     g.manual_seed(int(seed) & 0x7FFFFFFFFFFFFFFF)
     return g
 
 
-def normal_bf16(shape, std: float, seed: int) -> torch.Tensor:
-    """N(0, std^2) rounded to bf16 (CPU tensor)."""
-    x = torch.randn(*shape, generator=_gen(seed), dtype=torch.float32)
+def normal_bf16(shape, std: float, seed: int, device="cpu") -> torch.Tensor:
+    """N(0, std^2) rounded to bf16, drawn on `device` (large workloads draw on
+    the GPU and copy the bits to the host for the oracle)."""
+    x = torch.randn(*shape, generator=_gen(seed, device), dtype=torch.float32, device=device)
     return (x * std).to(torch.bfloat16)
 
 
-def student_t_bf16(shape, nu: float, seed: int) -> torch.Tensor:
+def student_t_bf16(shape, nu: float, seed: int, device="cpu") -> torch.Tensor:
     """Student-t with nu degrees of freedom scaled to unit variance (nu > 2), bf16."""
-    g = _gen(seed)
-    z = torch.randn(*shape, generator=g, dtype=torch.float64)
+    g = _gen(seed, device)
+    z = torch.randn(*shape, generator=g, dtype=torch.float32, device=device)
     # chi-square(nu) as a sum of nu squared normals (nu integer here)
-    chi = torch.zeros(*shape, dtype=torch.float64)
+    chi = torch.zeros(*shape, dtype=torch.float32, device=device)
     for _ in range(int(nu)):
-        chi += torch.randn(*shape, generator=g, dtype=torch.float64) ** 2
+        chi += torch.randn(*shape, generator=g, dtype=torch.float32, device=device) ** 2
     t = z / torch.sqrt(chi / nu)
-    return (t * np.sqrt((nu - 2.0) / nu)).to(torch.bfloat16)
+    return (t * float(np.sqrt((nu - 2.0) / nu))).to(torch.bfloat16)
 
 
 def normal_f32(shape, std: float, seed: int) -> torch.Tensor:
