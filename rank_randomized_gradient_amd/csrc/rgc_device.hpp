@@ -41,6 +41,59 @@ __device__ __forceinline__ V load_cached(const void* base, uint32_t off) {
   return *global_at<V>(base, off);
 }
 
+// ---------------------------------------------------------------------------
+// Staging through LDS.
+//
+// dma_16b_*: each lane copies the 16 bytes at base + voff (global) into LDS;
+// lane l's bytes land at lds_addr + 16*l (lds_addr is wave-uniform and goes
+// to M0). The copy does not pass through VGPRs. It is issued from inline asm
+// on purpose: the compiler, seeing the builtin, conservatively waits for
+// every outstanding copy before any LDS read, which would serialize a
+// multi-stage pipeline. Completion is therefore tracked by hand: a copy
+// counts in the wave's vector-memory counter until its bytes are in LDS, and
+// these counters retire loads in issue order, so wait_vmcnt<N>() returns once
+// all but the N most recent of the wave's loads are done. Other waves see the
+// bytes after a workgroup barrier that follows that wait.
+//
+// The leading s_nop 4 supplies wait states that the compiler cannot insert
+// into inline asm: a vector memory instruction that reads an SGPR as its base
+// needs five wait states after a VALU instruction wrote that SGPR (the
+// compiler reloads spilled SGPRs with v_readlane right before the asm), and
+// a copy into LDS needs one after M0 was written (the compiler writes M0 for
+// the "{m0}" operand right before the asm). Without them the copy may use a
+// stale base address.
+#define RGC_LDS __attribute__((address_space(3)))
+__device__ __forceinline__ void dma_16b_stream(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "{m0}"(lds_addr) : "memory");
+}
+__device__ __forceinline__ void dma_16b_cached(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier for LDS handoff: the wave's own LDS reads are complete
+// before it arrives (so a stage read in the previous step may be refilled
+// after the barrier). No memory fence beyond that: the copies it orders are
+// waited for explicitly with wait_vmcnt.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Transposing LDS read of 16-bit elements (ds_read_b64_tr_b16). Within each
+// group of 16 lanes, lane c supplies the address of an 8-byte chunk (four
+// elements); lane i receives, as its element j (j = 0..3), element i % 4 of
+// the chunk addressed by lane 4j + i / 4 of its group. With the chunks of a
+// 4 x 16 block laid out row-major (chunk 4j + q = row j, columns 4q..4q+3),
+// lane i therefore gets column i of rows 0..3: the MFMA operand layout for a
+// K-major (token-major) matrix. Returned as two dwords, element 0 in the low
+// half of dword 0.
+__device__ __forceinline__ u32x2v_t lds_read_tr16(const RGC_LDS char* p) {
+  typedef short i16x4_t __attribute__((ext_vector_type(4)));
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((RGC_LDS i16x4_t*)p);
+  return __builtin_bit_cast(u32x2v_t, v);
+}
+
 // Index of the calling wave within its workgroup, as a wave-uniform (scalar)
 // value, so that branches on it and on values derived from it are scalar
 // branches rather than exec-masked ones.

@@ -48,6 +48,15 @@ inline bool rank_supported(int64_t r) {
 template <int V>
 using IntC = std::integral_constant<int, V>;
 
+// Calls f(IntC<i>{}) for i = B .. E-1 (a loop whose index is a constant expression).
+template <int B, int E, typename F>
+__host__ __device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IntC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Calls f(IntC<r>{}) for a supported rank; returns false otherwise.
 template <typename F>
 bool dispatch_rank(int64_t r, F&& f) {

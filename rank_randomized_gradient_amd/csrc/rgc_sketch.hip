@@ -295,6 +295,7 @@ constexpr int kNumXcds = 8;
 struct Schedule {
   int n;                          // items
   int G;                          // workgroups
+  int64_t tile_n;                 // N extent of a tile
   int64_t U;                      // units
   int64_t ubase[kMaxItems + 1];   // first unit of each item
   int64_t nkb[kMaxItems];         // K-blocks per tile
@@ -533,124 +534,270 @@ __global__ __launch_bounds__(64 * RankTraits<R>::NR * RankTraits<R>::KS, kWorkgr
 }
 
 // ---------------------------------------------------------------------------
-// accumulate: C += D^T XP. N = d (N-tile c column n is d = dbase + 4n + c),
-// K = tokens.
+// accumulate: C += D^T XP, staged through LDS. N = d, K = tokens.
+//
+// A workgroup tile is TILE = 64*WN columns of d by all R columns of r; its
+// four waves split it WN ways along d and WR ways along r (WN * WR = 4), so
+// every wave multiplies a 64 (d) x RW (r) block. A K-step is 32 tokens: the
+// step's D slab (32 x TILE) and XP slab (32 x R) are copied from memory
+// straight into an LDS stage by all four waves in 1 KB pieces, S stages
+// ahead; each wave then reads its MFMA operands from the stage with
+// transposing reads, so both token-major operands arrive in MFMA layout
+// without register shuffles, and the XP slab is fetched once per workgroup.
+//
+// LDS layout of a stage: blocks of 4 tokens x 16 columns (128 bytes, four
+// rows of four 8-byte chunks). Block (tq, b) of the D slab (b = 16-column
+// block of the tile) sits at 128 * (tq * NDB + b); the XP slab's block
+// (tq, b) at D_BYTES + 128 * (tq * NRB + b). Copy c fills blocks 8c .. 8c+7:
+// lane l reads token (l % 8) / 2 of block 8c + l / 8, columns 8 * (l % 2)
+// .. +7, which are exactly the 16 bytes that land at 16 * l.
 // ---------------------------------------------------------------------------
-struct DRows {
-  uint32_t v[8][2];  // 8 tokens x 4 consecutive d (bf16 pairs)
-};
-
-// Per-lane byte offsets, relative to the window's first token, of the 8
-// bytes lane (n, g) reads for token 8g + j (clamped into a window of `rows`
-// valid tokens) at columns dcol .. dcol+3.
-__device__ __forceinline__ RowOffsets d_offsets(int lane, int64_t ldd, int64_t dcol, int64_t rows) {
-  const int g = lane >> 4;
-  RowOffsets o;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t row = 8 * g + j < rows ? 8 * g + j : rows - 1;
-    o.off[j] = (uint32_t)((row * ldd + dcol) * 2);
-  }
-  return o;
-}
-
-__device__ __forceinline__ void load_d_rows(const uint16_t* win, const RowOffsets& o, DRows& out) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const u32x2v_t v = load_stream_8b(win, o.off[j]);
-    out.v[j][0] = v.x;
-    out.v[j][1] = v.y;
-  }
-}
-
-__device__ __forceinline__ void mask_d_rows(int64_t wb, int64_t t0, int64_t tend, int lane, DRows& rows) {
-  const int g = lane >> 4;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t row = wb + 8 * g + j;
-    const bool ok = row >= t0 && row < tend;
-    rows.v[j][0] = ok ? rows.v[j][0] : 0u;
-    rows.v[j][1] = ok ? rows.v[j][1] : 0u;
-  }
-}
+constexpr int kAccStages = 6;
 
 template <int R>
-__global__ __launch_bounds__(64 * RankTraits<R>::NR * RankTraits<R>::KS, kWorkgroupsPerCU) void accumulate_kernel(
-    AccumulateBatch ab) {
-  using Tr = RankTraits<R>;
-  __shared__ float lds[reduce_lds_floats<R>()];
+struct AccShape {
+  static constexpr int WR = R <= 64 ? 1 : (R == 128 ? 2 : 4);  // waves along r
+  static constexpr int WN = 4 / WR;                              // waves along d
+  static constexpr int RW = R / WR;                              // r per wave
+  static constexpr int MT = RW / 16;                             // MFMA M-tiles per wave
+  static constexpr int TILE = 64 * WN;                           // d per workgroup tile
+  static constexpr int NDB = TILE / 16;                          // D copies per stage
+  static constexpr int NRB = R / 16;                             // XP copies per stage
+  static constexpr int NI = NDB + NRB;
+  static constexpr int D_BYTES = 1024 * NDB;
+  static constexpr int STAGE = 1024 * NI;
+  static constexpr int S = kAccStages;
+  static constexpr int NV_LO = NI / 4, NV_HI = (NI + 3) / 4;  // copies per wave (waves below NI % 4 take one more)
+  static_assert(RW % 16 == 0 && RW <= 64, "rank split");
+  static_assert(S * STAGE <= 160 * 1024, "LDS");
+  static_assert((S - 1) * NV_HI <= 63, "vector memory counter");
+};
+
+template <int R>
+__global__ __launch_bounds__(256, kWorkgroupsPerCU) void accumulate_kernel(AccumulateBatch ab) {
+  using Sh = AccShape<R>;
+  constexpr int S = Sh::S;
+  __shared__ __attribute__((aligned(1024))) char smem[S * Sh::STAGE];
   const int lane = threadIdx.x & 63, wave = wave_index();
-  const int rw = wave % Tr::NR, ks = wave / Tr::NR;
-  const int rbase = rw * Tr::RPW;
-  const int n = lane & 15, g = lane >> 4;
+  const int wn = wave % Sh::WN, rw = wave / Sh::WN;
+  const int g = lane >> 4, li = lane & 15;
   const Schedule& s = ab.s;
   const int64_t w = logical_workgroup(blockIdx.x, s.G);
   const int64_t T = uniform_i64(s.kext[0]);
+  const int64_t u0 = uniform_i64(range_begin(s, w)), u1 = uniform_i64(range_begin(s, w + 1));
+  const int64_t rows = window_rows(T);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(RGC_LDS char*)smem;
+  const bool more = wave < Sh::NI % 4;  // this wave issues NV_HI copies per stage (else NV_LO)
 
-  struct Stage {
-    DRows d;
-    RankRows<R> x;
-  };
-  AccTile<R> acc;
-  int64_t dbase = 0, d = 0, ldd = 0;
-  const uint16_t* Dm = nullptr;
-  const uint16_t* XPm = nullptr;
-  RowOffsets xo, doff;
-  auto begin = [&](int m, int64_t tile) {
-    dbase = tile * kTileN;
-    d = s.next[m];
-    ldd = uniform_i64(ab.ldd[m]);
-    // d % 4 == 0: a lane's 4 columns are all in or all out. Lanes past d
-    // read columns 0..3 instead; their output columns are never stored.
-    const int64_t dcol = dbase + 4 * n < d ? dbase + 4 * n : 0;
-    Dm = uniform_ptr(ab.D[m]);
-    XPm = uniform_ptr(ab.XP[m] + rbase);
-    xo = rank_row_offsets<R>(lane, window_rows(T));
-    doff = d_offsets(lane, ldd, dcol, window_rows(T));
-  };
-  auto load = [&](Stage& b, int64_t t0) {
-    const int64_t wb = window_base(t0, T);
-    load_d_rows(uniform_ptr(Dm + wb * ldd), doff, b.d);
-    load_rank_rows<R>(uniform_ptr(XPm + wb * R), xo, b.x);
-  };
-  auto step = [&](Stage& b, int64_t t0, auto masked) {
-    if (masked && t0 + 32 > T) {  // the last, partial K-step (wave-uniform)
-      const int64_t wb = window_base(t0, T);
-      mask_d_rows(wb, t0, T, lane, b.d);
-      mask_rank_rows<R>(wb, t0, T, lane, b.x);
+  // ---- the copy side: a cursor over this workgroup's units, S - 1 ahead
+  uint32_t voff[Sh::NV_HI];
+  auto set_offsets = [&](int m, int64_t tile) {
+    const int64_t d = s.next[m], ldd = ab.ldd[m], dbase = tile * Sh::TILE;
+    const int j = (lane & 7) >> 1, half = lane & 1;
+#pragma unroll
+    for (int v = 0; v < Sh::NV_HI; ++v) {
+      const int c = wave + 4 * v;
+      if (c < Sh::NDB) {
+        const int blk = 8 * c + (lane >> 3);
+        int64_t t = 4 * (blk / Sh::NDB) + j;
+        t = t < rows ? t : rows - 1;
+        int64_t col = dbase + 16 * (blk % Sh::NDB) + 8 * half;
+        col = col < d ? col : d - 8;  // past d: any valid chunk (its columns are never stored)
+        voff[v] = (uint32_t)((t * ldd + col) * 2);
+      } else {
+        const int blk = 8 * (c - Sh::NDB) + (lane >> 3);
+        int64_t t = 4 * (blk / Sh::NRB) + j;
+        t = t < rows ? t : rows - 1;
+        voff[v] = (uint32_t)((t * R + 16 * (blk % Sh::NRB) + 8 * half) * 2);
+      }
     }
-    uint32_t aop[Tr::MT][4];
-    transpose_rank_rows<R>(b.x, aop);
-    uint32_t bop[kNT][4];
-#pragma unroll
-    for (int c = 0; c < kNT; ++c) transpose_8xcpl<4>(b.d.v, c, bop[c]);
-#pragma unroll
-    for (int mt = 0; mt < Tr::MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = mfma_16x16x32(aop[mt], bop[nt], acc[mt][nt]);
   };
-  auto finish = [&](int m, int64_t tile, bool full, int64_t slot) {
-    const auto row_of = [](int c, int nn) { return 4 * nn + c; };
-    if (full) {
-      float* C = ab.C[m];
-      for_owned_runs<R>(acc, ks, lane, row_of, [&](int row, int q, const float (&run)[4 * Tr::CPL]) {
-        if (dbase + row < d) add_run_f32<Tr::CPL>(C + (dbase + row) * R + rbase + q * Tr::GW + 4 * Tr::CPL * g, run);
-      });
+  const int m0 = item_of_unit(s, u0);
+  const int64_t tile0 = (u0 - s.ubase[m0]) / s.nkb[m0], k0 = (u0 - s.ubase[m0]) % s.nkb[m0];
+  // per-item constants of the copy cursor, reloaded when it moves to the next item
+  int lm = m0;
+  int64_t ltile = tile0, lk = k0, lu = u0;
+  int64_t l_nkb = 0, l_tiles = 0, l_ldd = 0;
+  const uint16_t* l_D = nullptr;
+  const uint16_t* l_XP = nullptr;
+  auto enter_item = [&](int m) {
+    l_nkb = uniform_i64(s.nkb[m]);
+    l_tiles = uniform_i64(s.tbase[m + 1] - s.tbase[m]);
+    l_ldd = uniform_i64(ab.ldd[m]);
+    l_D = uniform_ptr(ab.D[m]);
+    l_XP = uniform_ptr(ab.XP[m]);
+  };
+  if (u0 < u1) {
+    enter_item(lm);
+    set_offsets(lm, ltile);
+  }
+  uint32_t lslot = 0;  // stage of unit lu
+  auto issue = [&]() {
+    const int64_t wb = window_base(lk * 32, T);
+    const uint16_t* Db = uniform_ptr(l_D + wb * l_ldd);
+    const uint16_t* Xb = uniform_ptr(l_XP + wb * R);
+    const uint32_t st = lds0 + lslot * Sh::STAGE;
+    static_for<0, Sh::NV_HI>([&](auto vc) {
+      constexpr int v = decltype(vc)::value;
+      // copy c = wave + 4v: a D copy if c < NDB, an XP copy if NDB <= c < NI
+      const int c = wave + 4 * v;
+      if constexpr (4 * v + 3 < Sh::NDB) {
+        dma_16b_stream(Db, voff[v], st + 1024 * c);
+      } else if constexpr (4 * v >= Sh::NDB && 4 * v + 3 < Sh::NI) {
+        dma_16b_cached(Xb, voff[v], st + 1024 * c);
+      } else {
+        if (c < Sh::NDB)
+          dma_16b_stream(Db, voff[v], st + 1024 * c);
+        else if (c < Sh::NI)
+          dma_16b_cached(Xb, voff[v], st + 1024 * c);
+      }
+    });
+    ++lu;
+    lslot = lslot + 1 == S ? 0 : lslot + 1;
+    if (++lk == l_nkb) {
+      lk = 0;
+      if (++ltile == l_tiles) {
+        ltile = 0;
+        ++lm;
+        if (lu < u1) enter_item(lm);
+      }
+      if (lu < u1) set_offsets(lm, ltile);
+    }
+  };
+
+  // ---- the compute side
+  f32x4_t acc[Sh::MT][4];
+  using Acc = f32x4_t[Sh::MT][4];
+  auto finish = [&](const Acc& res, int m, int64_t tile, bool full, int64_t slot) {
+    const int64_t d = s.next[m], dbase = tile * Sh::TILE;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int64_t row = 64 * wn + 16 * nt + li;  // tile-relative d
+#pragma unroll
+      for (int mt = 0; mt < Sh::MT; ++mt) {
+        const int rcol = rw * Sh::RW + 16 * mt + 4 * g;
+        const f32x4_t v = res[mt][nt];
+        if (full) {
+          // the tile lies inside this workgroup's range: one add per element,
+          // no other writer in this launch
+          if (dbase + row < d) {
+            float* c = ab.C[m] + (dbase + row) * R + rcol;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) unsafeAtomicAdd(c + e, v[e]);
+          }
+        } else {
+          float* p = ab.part + slot * Sh::TILE * R + row * R + rcol;
+          *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int v = 0; v + 1 < S; ++v)
+    if (lu < u1) issue();
+
+  // The first segment's sums are kept in registers and stored after the
+  // range's last segment: a store issued while copies are in flight counts
+  // in the same counter as the copies, so the next wait would drain the
+  // whole pipeline. Later segments (each a whole tile or the range's last
+  // piece) are stored as they finish.
+  f32x4_t keep[Sh::MT][4];
+  bool kept = false, kept_full = false;
+  int64_t kept_tile = tile0;
+
+  uint32_t cslot = 0;  // stage of unit u
+  int cm = m0;
+  int64_t ctile = tile0, ck = k0;
+  for (int64_t u = u0; u < u1;) {
+    // one segment: K-steps ck .. of tile (cm, ctile), up to the tile's end or the range's
+    const int64_t c_nkb = uniform_i64(s.nkb[cm]);
+    const int64_t seg_kb0 = ck;
+    const int64_t seg_end = u + (c_nkb - ck) < u1 ? u + (c_nkb - ck) : u1;
+    const bool tile_end = u + (c_nkb - ck) <= u1;
+#pragma unroll
+    for (int mt = 0; mt < Sh::MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (; u < seg_end; ++u, ++ck) {
+      if (u + S - 2 < u1) {
+        if (more)
+          wait_vmcnt<(S - 2) * Sh::NV_HI>();
+        else
+          wait_vmcnt<(S - 2) * Sh::NV_LO>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      lds_barrier();
+      if (lu < u1) issue();
+
+      const RGC_LDS char* st = (const RGC_LDS char*)smem + cslot * Sh::STAGE;
+      cslot = cslot + 1 == S ? 0 : cslot + 1;
+      uint32_t a[Sh::MT][4], b[4][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int mt = 0; mt < Sh::MT; ++mt) {
+          const u32x2v_t v =
+              lds_read_tr16(st + Sh::D_BYTES + 128 * ((2 * g + h) * Sh::NRB + rw * Sh::MT + mt) + 8 * li);
+          a[mt][2 * h] = v.x;
+          a[mt][2 * h + 1] = v.y;
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const u32x2v_t v = lds_read_tr16(st + 128 * ((2 * g + h) * Sh::NDB + 4 * wn + nt) + 8 * li);
+          b[nt][2 * h] = v.x;
+          b[nt][2 * h + 1] = v.y;
+        }
+      }
+      const int64_t t0 = ck * 32;
+      if (t0 + 32 > T) {
+        // the last, partial step: the stage holds tokens wb .. wb+31 (wb <= t0);
+        // K slot 8g + 2p (+1) of this lane is token wb + 8g + 2p (+1)
+        const int64_t wb = window_base(t0, T);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int64_t tk = wb + 8 * g + 2 * p;
+          const uint32_t keep =
+              (tk >= t0 && tk < T ? 0x0000FFFFu : 0u) | (tk + 1 >= t0 && tk + 1 < T ? 0xFFFF0000u : 0u);
+#pragma unroll
+          for (int mt = 0; mt < Sh::MT; ++mt) a[mt][p] &= keep;
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < Sh::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_16x16x32(a[mt], b[nt], acc[mt][nt]);
+    }
+    const bool first_seg = seg_kb0 == k0 && ctile == tile0 && cm == m0;
+    if (first_seg && u < u1) {
+#pragma unroll
+      for (int mt = 0; mt < Sh::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) keep[mt][nt] = acc[mt][nt];
+      kept = true;
+      kept_full = seg_kb0 == 0 && tile_end;
+      kept_tile = ctile;
     } else {
-      float* part = ab.part + slot * (int64_t)kTileN * R;
-      for_owned_runs<R>(acc, ks, lane, row_of, [&](int row, int q, const float (&run)[4 * Tr::CPL]) {
-        store_run_f32<Tr::CPL>(part + row * R + rbase + q * Tr::GW + 4 * Tr::CPL * g, run);
-      });
+      finish(acc, cm, ctile, seg_kb0 == 0 && tile_end, partial_slot(w, first_seg));
     }
-  };
-  run_range<R, Stage>(s, w, ks, lds, rw, lane, acc, begin, load, step, finish);
+    if (tile_end) {
+      ck = 0;
+      if (++ctile == uniform_i64(s.tbase[cm + 1] - s.tbase[cm])) {
+        ctile = 0;
+        ++cm;
+      }
+    }
+  }
+  if (kept) finish(keep, m0, kept_tile, kept_full, partial_slot(w, true));
 }
 
 // ---------------------------------------------------------------------------
 // Finishing pass over the tiles that were cut between workgroups: workgroup
-// t takes batch-wide tile t, finds the ranges that cover it and sums their
-// partials in range order, then rounds into XP (project) or adds into C
-// (accumulate). Tiles inside one range return at once.
+// (c, t) takes values 1024c .. 1024c+1023 of batch-wide tile t, finds the
+// ranges that cover the tile and sums their partials in range order, then
+// rounds into XP (project) or adds into C (accumulate). Tiles inside one
+// range return at once.
 // ---------------------------------------------------------------------------
 struct FinishBatch {
   Schedule s;
@@ -662,26 +809,29 @@ struct FinishBatch {
 template <int R, bool TO_BF16>
 __global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
   const Schedule& s = fb.s;
-  const int64_t t = blockIdx.x;
+  const int64_t t = blockIdx.y;
   const int m = item_of_tile(s, t);
   const int64_t tile = t - s.tbase[m];
   const int64_t ts = s.ubase[m] + tile * s.nkb[m], te = ts + s.nkb[m];
   const int64_t wa = range_of(s, ts), wb = range_of(s, te - 1);
   if (wa == wb) return;
-  const int64_t left = s.next[m] - tile * kTileN;
-  const int64_t rows = left < kTileN ? left : kTileN;
-  constexpr int PER = 4;  // floats per thread and pass
-  for (int64_t e = (int64_t)threadIdx.x * PER; e < rows * R; e += 256 * PER) {
+  const int64_t tn = s.tile_n;
+  const int64_t left = s.next[m] - tile * tn;
+  const int64_t rows = left < tn ? left : tn;
+  constexpr int PER = 4;  // floats per thread
+  {
+    const int64_t e = (int64_t)blockIdx.x * (256 * PER) + threadIdx.x * PER;
+    if (e >= rows * R) return;
     f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
     for (int64_t w = wa; w <= wb; ++w) {
       // wa's share is its last segment when its range began in an earlier
       // tile, else its first; every later range begins inside this tile
       const bool first = !(w == wa && range_begin(s, wa) < ts);
-      const float4 v = *reinterpret_cast<const float4*>(fb.part + partial_slot(w, first) * (int64_t)kTileN * R + e);
+      const float4 v = *reinterpret_cast<const float4*>(fb.part + partial_slot(w, first) * tn * R + e);
       const f32x4_t x = {v.x, v.y, v.z, v.w};
       sum = (w == wa) ? x : sum + x;
     }
-    const int64_t out = tile * kTileN * R + e;
+    const int64_t out = tile * tn * R + e;
     if constexpr (TO_BF16) {
       const uint2 o = make_uint2(pack_bf16x2(f32_to_bf16_rne(sum[0]), f32_to_bf16_rne(sum[1])),
                                  pack_bf16x2(f32_to_bf16_rne(sum[2]), f32_to_bf16_rne(sum[3])));
@@ -711,13 +861,12 @@ int64_t sketch_workgroups() {
 }
 
 // The schedule for items with N extents ns[] and K extents ks[].
-template <int R>
-Schedule make_schedule(int n, const int64_t* ns, const int64_t* ks) {
+Schedule make_schedule(int n, const int64_t* ns, const int64_t* ks, int64_t tile_n, int64_t kblock) {
   Schedule s = {};
-  constexpr int64_t kblock = 32 * RankTraits<R>::KS;
   s.n = n;
+  s.tile_n = tile_n;
   for (int m = 0; m < n; ++m) {
-    const int64_t tiles = (ns[m] + kTileN - 1) / kTileN;
+    const int64_t tiles = (ns[m] + tile_n - 1) / tile_n;
     s.nkb[m] = (ks[m] + kblock - 1) / kblock;
     s.kext[m] = ks[m];
     s.next[m] = ns[m];
@@ -732,7 +881,23 @@ Schedule make_schedule(int n, const int64_t* ns, const int64_t* ks) {
 
 template <int R>
 size_t partial_bytes(const Schedule& s) {
-  return (size_t)2 * s.G * kTileN * R * sizeof(float);
+  return (size_t)2 * s.G * s.tile_n * R * sizeof(float);
+}
+
+// One finishing workgroup per 1024 values of a tile (x) and per tile (y).
+template <int R>
+dim3 finish_grid(const Schedule& s) {
+  return dim3((unsigned)((s.tile_n * R + 1023) / 1024), (unsigned)s.tbase[s.n]);
+}
+
+template <int R>
+Schedule project_schedule(int n, const int64_t* ns, const int64_t* ks) {
+  return make_schedule(n, ns, ks, kTileN, 32 * RankTraits<R>::KS);
+}
+
+template <int R>
+Schedule accumulate_schedule(int n, const int64_t* ns, const int64_t* ks) {
+  return make_schedule(n, ns, ks, AccShape<R>::TILE, 32);
 }
 
 template <int R>
@@ -741,7 +906,7 @@ rgc_status_t project_launch(int n, const uint16_t* const* Xs, const int64_t* ldx
   int64_t ns[kMaxItems];
   for (int m = 0; m < n; ++m) ns[m] = T;
   ProjectBatch pb = {};
-  pb.s = make_schedule<R>(n, ns, ks);
+  pb.s = project_schedule<R>(n, ns, ks);
   FinishBatch fb = {};
   fb.s = pb.s;
   for (int m = 0; m < n; ++m) {
@@ -755,7 +920,7 @@ rgc_status_t project_launch(int n, const uint16_t* const* Xs, const int64_t* ldx
   fb.part = pb.part;
   hipLaunchKernelGGL(project_kernel<R>, dim3((unsigned)pb.s.G), dim3(64 * RankTraits<R>::NR * RankTraits<R>::KS), 0,
                      st, pb);
-  hipLaunchKernelGGL((finish_tiles_kernel<R, true>), dim3((unsigned)pb.s.tbase[n]), dim3(256), 0, st, fb);
+  hipLaunchKernelGGL((finish_tiles_kernel<R, true>), finish_grid<R>(pb.s), dim3(256), 0, st, fb);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
@@ -765,7 +930,7 @@ rgc_status_t accumulate_launch(int n, const uint16_t* const* Ds, const int64_t* 
   int64_t ks[kMaxItems];
   for (int m = 0; m < n; ++m) ks[m] = T;
   AccumulateBatch ab = {};
-  ab.s = make_schedule<R>(n, ds, ks);
+  ab.s = accumulate_schedule<R>(n, ds, ks);
   FinishBatch fb = {};
   fb.s = ab.s;
   for (int m = 0; m < n; ++m) {
@@ -777,10 +942,16 @@ rgc_status_t accumulate_launch(int n, const uint16_t* const* Ds, const int64_t* 
   }
   ab.part = static_cast<float*>(ws);
   fb.part = ab.part;
-  hipLaunchKernelGGL(accumulate_kernel<R>, dim3((unsigned)ab.s.G), dim3(64 * RankTraits<R>::NR * RankTraits<R>::KS), 0,
-                     st, ab);
-  hipLaunchKernelGGL((finish_tiles_kernel<R, false>), dim3((unsigned)ab.s.tbase[n]), dim3(256), 0, st, fb);
+  hipLaunchKernelGGL(accumulate_kernel<R>, dim3((unsigned)ab.s.G), dim3(256), 0, st, ab);
+  hipLaunchKernelGGL((finish_tiles_kernel<R, false>), finish_grid<R>(ab.s), dim3(256), 0, st, fb);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+}
+
+template <int R>
+size_t accumulate_workspace(int n, const int64_t* ds, int64_t T) {
+  int64_t ks[kMaxItems];
+  for (int m = 0; m < n; ++m) ks[m] = T;
+  return partial_bytes<R>(accumulate_schedule<R>(n, ds, ks));
 }
 
 rgc_status_t check_project_item(const uint16_t* X, int64_t ldx, int64_t k, const uint16_t* P, const uint16_t* XP,
@@ -817,7 +988,7 @@ extern "C" size_t rgc_project_batch_workspace_size(int64_t n, const int64_t* ks,
   size_t out = 0;
   if (!dispatch_rank(r, [&](auto rc) {
         constexpr int R = decltype(rc)::value;
-        out = partial_bytes<R>(make_schedule<R>((int)n, ns, ks));
+        out = partial_bytes<R>(project_schedule<R>((int)n, ns, ks));
       }))
     return 0;
   return out;
@@ -827,12 +998,10 @@ extern "C" size_t rgc_accumulate_batch_workspace_size(int64_t n, const int64_t* 
   if (n <= 0 || n > kMaxItems || !ds || T <= 0) return 0;
   for (int64_t m = 0; m < n; ++m)
     if (ds[m] <= 0) return 0;
-  int64_t ks[kMaxItems];
-  for (int64_t m = 0; m < n; ++m) ks[m] = T;
   size_t out = 0;
   if (!dispatch_rank(r, [&](auto rc) {
         constexpr int R = decltype(rc)::value;
-        out = partial_bytes<R>(make_schedule<R>((int)n, ds, ks));
+        out = accumulate_workspace<R>((int)n, ds, T);
       }))
     return 0;
   return out;
