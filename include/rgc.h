@@ -44,7 +44,7 @@
  *   - Shape limits: r is one of 16, 32, 48, 64, 128, 192, 256 (QR
  *     projections: r <= 128); d and k are multiples of 8; T >= 0 (T = 0 is a
  *     no-op); T and d at most 65536 per call; leading dimensions are
- *     multiples of 8 elements and at most 2^24 (RGC_ERR_UNSUPPORTED above);
+ *     multiples of 8 elements and at most 2^23 (RGC_ERR_UNSUPPORTED above);
  *     for rgc_apply, d and k at most 2^30;
  *     tensor base pointers are 16-byte aligned.
  */

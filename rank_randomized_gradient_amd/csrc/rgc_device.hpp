@@ -1,6 +1,7 @@
-// Device helpers shared by the gfx950 kernels of the sketch library:
-// the Philox4x32-10 counter generator, bf16 bit helpers, the bf16 MFMA
-// wrapper and the register transposes that feed token-major operands to it.
+// Device helpers shared by the gfx950 kernels of the sketch library: the
+// global-to-LDS copies and transposing LDS reads of the staged contractions,
+// the Philox4x32-10 counter generator, bf16 bit helpers and the bf16 MFMA
+// wrapper.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,33 +14,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2v_t __attribute__((ext_vector_type(2)));
-
-// Global-memory loads at a byte offset from a base pointer. The explicit
-// global address space keeps them global loads (a base rebuilt from scalar
-// registers is otherwise a generic pointer, which turns them into flat
-// loads); a wave-uniform base then stays in scalar registers and the
-// per-lane offset takes one VGPR.
-#define RGC_GLOBAL __attribute__((address_space(1)))
-// The empty asm statement redefines the offset where it is used, so the
-// compiler cannot hoist its widening to 64 bits out of a loop; the address
-// then matches the scalar-base + 32-bit-VGPR-offset form of the load.
-template <typename V>
-__device__ __forceinline__ const RGC_GLOBAL V* global_at(const void* base, uint32_t off) {
-  asm volatile("" : "+v"(off));
-  return (const RGC_GLOBAL V*)((const RGC_GLOBAL char*)base + off);
-}
-// Streaming loads for data read exactly once (nontemporal hint).
-__device__ __forceinline__ u32x4v_t load_stream_16b(const void* base, uint32_t off) {
-  return __builtin_nontemporal_load(global_at<u32x4v_t>(base, off));
-}
-__device__ __forceinline__ u32x2v_t load_stream_8b(const void* base, uint32_t off) {
-  return __builtin_nontemporal_load(global_at<u32x2v_t>(base, off));
-}
-// Loads for data that other workgroups read too (kept in cache).
-template <typename V>
-__device__ __forceinline__ V load_cached(const void* base, uint32_t off) {
-  return *global_at<V>(base, off);
-}
 
 // ---------------------------------------------------------------------------
 // Staging through LDS.
@@ -155,15 +129,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_sr(float f, uint32_t r16) {
 // Two bf16 packed in a dword, element 0 in the low half.
 __device__ __forceinline__ uint32_t pack_bf16x2(uint32_t lo, uint32_t hi) { return (lo & 0xFFFFu) | (hi << 16); }
 
-// v_perm_b32 selectors: low halves of (a, b) -> (a.lo, b.lo); high halves likewise.
-constexpr uint32_t kSelLo = 0x05040100u;
-constexpr uint32_t kSelHi = 0x07060302u;
-// Returns a dword whose low half is the selected half of `first` and whose
-// high half is the selected half of `second`.
-__device__ __forceinline__ uint32_t pick_halves(uint32_t first, uint32_t second, uint32_t sel) {
-  return __builtin_amdgcn_perm(second, first, sel);
-}
-
 // D = A B + C for one 16x16 output tile with K = 32 (bf16 in, fp32 out).
 // Lane l supplies A row (l % 16) and B column (l % 16), each with the eight
 // consecutive K values 8*(l/16) .. 8*(l/16)+7 packed as four bf16 pairs;
@@ -174,24 +139,6 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const uint32_t (&a)[4], const u
   u4v bv = {b[0], b[1], b[2], b[3]};
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv),
                                                  c, 0, 0, 0);
-}
-
-// Register transpose for token-major operands. A lane has read, for eight
-// consecutive tokens j = 0..7, CPL consecutive bf16 columns of one row each
-// (rows[j] holds them: one dword per two columns). For column c it returns the
-// eight tokens of that column packed as four bf16 pairs (token 2p in the low
-// half of dword p): the MFMA operand of "column c".
-template <int CPL>
-__device__ __forceinline__ void transpose_8xcpl(const uint32_t (&rows)[8][(CPL + 1) / 2], int c, uint32_t (&out)[4]) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    if constexpr (CPL == 1) {
-      out[p] = pack_bf16x2(rows[2 * p][0], rows[2 * p + 1][0]);
-    } else {
-      const uint32_t sel = (c & 1) ? kSelHi : kSelLo;
-      out[p] = pick_halves(rows[2 * p][c >> 1], rows[2 * p + 1][c >> 1], sel);
-    }
-  }
 }
 
 // Wave-wide sum of a double (64 lanes) with cross-lane shuffles.

@@ -19,27 +19,10 @@ namespace rgc {
 // accumulate); keeps every in-kernel offset within 32 bits.
 constexpr int64_t kMaxTiledDim = 65536;
 
-// Limit on the leading dimension of X and D: the kernels address a 64-token
-// (or 32-token) slab of rows with 32-bit byte offsets.
-constexpr int64_t kMaxLeadingDim = int64_t(1) << 24;
-
-// Tiling of the rank dimension r (a multiple of 16, at most 64, or a multiple
-// of 64 up to 256). A wave covers RPW rank columns in NG groups of GW columns;
-// each lane reads CPL adjacent columns per row of a group (CPL = 4 when the
-// group is 64 wide). NR waves cover all of r; KS waves split the K loop
-// inside a workgroup so that it has four waves when r is small.
-template <int R>
-struct RankTraits {
-  static_assert(R % 16 == 0 && R >= 16 && R <= 256, "rank");
-  static constexpr int CPL = (R % 64 == 0) ? 4 : ((R % 32 == 0) ? 2 : 1);
-  static constexpr int RPW = (R <= 64) ? R : 64;
-  static constexpr int NR = R / RPW;
-  static constexpr int GW = 16 * CPL;
-  static constexpr int NG = RPW / GW;
-  static constexpr int MT = RPW / 16;
-  static constexpr int KS = (NR == 1) ? 4 : (NR == 2 ? 2 : 1);
-  static_assert(RPW % GW == 0 && R % RPW == 0, "rank tiling");
-};
+// Limit on the leading dimension of X and D: the kernels address a tile of
+// up to 256 rows (project) or a 32-row window (accumulate) with 32-bit
+// per-lane byte offsets, so 256 * 2^23 * 2 bytes must fit in 32 bits.
+constexpr int64_t kMaxLeadingDim = int64_t(1) << 23;
 
 inline bool rank_supported(int64_t r) {
   return r == 16 || r == 32 || r == 48 || r == 64 || r == 128 || r == 192 || r == 256;

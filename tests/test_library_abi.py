@@ -79,7 +79,7 @@ def test_project_validation(lib):
     assert lib.rgc_project(FAKE, 2048, FAKE, FAKE, 4096, 2048, 64, None, 0, s) == WS
     assert lib.rgc_project(FAKE, 2048, FAKE, FAKE, 4096, 2048, 64, FAKE, need - 1, s) == WS
     assert lib.rgc_project(FAKE, 2048, FAKE, FAKE, 4096, 2048, 64, FAKE + 16, need, s) == ALIGN
-    assert lib.rgc_project(FAKE, (1 << 24) + 8, FAKE, FAKE, 16, 64, 16, None, 0, s) == UNSUP  # ldx > 2^24
+    assert lib.rgc_project(FAKE, (1 << 23) + 8, FAKE, FAKE, 16, 64, 16, None, 0, s) == UNSUP  # ldx > 2^23
 
 
 def test_accumulate_validation(lib):
@@ -94,7 +94,7 @@ def test_accumulate_validation(lib):
     assert need > 0
     assert lib.rgc_accumulate(FAKE, 2048, FAKE, FAKE, 4096, 2048, 64, FAKE, need - 4, s) == WS
     assert lib.rgc_accumulate(FAKE, 1 << 20, FAKE, FAKE, 4096, 1 << 20, 64, FAKE, need, s) == UNSUP  # d > limit
-    assert lib.rgc_accumulate(FAKE, (1 << 24) + 8, FAKE, FAKE, 16, 256, 16, None, 0, s) == UNSUP  # ldd > 2^24
+    assert lib.rgc_accumulate(FAKE, (1 << 23) + 8, FAKE, FAKE, 16, 256, 16, None, 0, s) == UNSUP  # ldd > 2^23
 
 
 def test_apply_validation(lib):
