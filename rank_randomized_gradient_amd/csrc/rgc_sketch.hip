@@ -42,18 +42,18 @@ namespace rgc {
 // K windows
 // ---------------------------------------------------------------------------
 
-// A K-step covers 32 rows of the K dimension. Its operands are read through a
-// window of 32 rows [wb, wb + 32): in the steady state wb is the step's own
-// first row k0; for the last, partial step the window is moved back to end
-// at the K extent, so that every row it touches is valid memory, and rows
-// outside [k0, end) are zeroed before use. A K extent below 32 clamps the
-// rows once, up front.
-__device__ __forceinline__ int64_t window_base(int64_t k0, int64_t end) {
-  return k0 + 32 <= end ? k0 : (end >= 32 ? end - 32 : 0);
+// A K-step covers KS rows of the K dimension (32 or 64). Its operands are
+// read through a window of KS rows [wb, wb + KS): in the steady state wb is
+// the step's own first row k0; for the last, partial step the window is
+// moved back to end at the K extent, so that every row it touches is valid
+// memory, and rows outside [k0, end) are zeroed before use. A K extent
+// below KS clamps the rows once, up front.
+__device__ __forceinline__ int64_t window_base(int64_t k0, int64_t end, int64_t ks) {
+  return k0 + ks <= end ? k0 : (end >= ks ? end - ks : 0);
 }
 
 // Rows of a window that are valid memory for a K extent `end`.
-__device__ __forceinline__ int64_t window_rows(int64_t end) { return end >= 32 ? 32 : end; }
+__device__ __forceinline__ int64_t window_rows(int64_t end, int64_t ks) { return end >= ks ? ks : end; }
 
 // Pins a wave-uniform value to scalar registers.
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
@@ -66,11 +66,12 @@ __device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
 }
 __device__ __forceinline__ int64_t uniform_i64(int64_t v) { return (int64_t)uniform_u64((uint64_t)v); }
 
-// K-slot keep mask of a partial step: the stage holds K rows wb .. wb+31;
-// dword p of a lane's operand holds K slots 8g + 2p and 8g + 2p + 1 (low and
-// high half). Returns the halves whose rows lie in [k0, end).
-__device__ __forceinline__ uint32_t kslot_keep(int64_t wb, int64_t k0, int64_t end, int g, int p) {
-  const int64_t k = wb + 8 * g + 2 * p;
+// K-slot keep mask of a partial step: the stage holds K rows wb .. wb+KS-1;
+// in K-half kh, dword p of a lane's operand holds rows 32kh + 8g + 2p and
+// 32kh + 8g + 2p + 1 (low and high half). Returns the halves whose rows lie
+// in [k0, end).
+__device__ __forceinline__ uint32_t kslot_keep(int64_t wb, int kh, int64_t k0, int64_t end, int g, int p) {
+  const int64_t k = wb + 32 * kh + 8 * g + 2 * p;
   return (k >= k0 && k < end ? 0x0000FFFFu : 0u) | (k + 1 >= k0 && k + 1 < end ? 0xFFFF0000u : 0u);
 }
 
@@ -130,6 +131,9 @@ __device__ __forceinline__ int64_t partial_slot(int64_t w, bool first_segment) {
 // ---------------------------------------------------------------------------
 // Stage geometry and the pipeline shared by both contractions.
 //
+// A step of KS = 32 KH rows is multiplied as KH K-halves of 32 (one MFMA K
+// extent each).
+//
 // Rank-operand layout in a stage (after the stream slab): blocks of 4 K rows
 // x 16 r columns (128 bytes, four rows of four 8-byte chunks); block (kq, b)
 // sits at STREAM + 128 * (kq * NRB + b). Rank copy c fills blocks 8c ..
@@ -140,27 +144,29 @@ __device__ __forceinline__ int64_t partial_slot(int64_t w, bool first_segment) {
 // ---------------------------------------------------------------------------
 constexpr int kStages = 6;
 
-template <int R>
+template <int R, int KH>
 struct StageShape {
   static constexpr int WR = R <= 64 ? 1 : (R == 128 ? 2 : 4);  // waves along r
   static constexpr int WN = 4 / WR;                              // waves along N
   static constexpr int RW = R / WR;                              // r per wave
   static constexpr int MT = RW / 16;                             // MFMA M-tiles per wave
   static constexpr int TILE = 64 * WN;                           // N per workgroup tile
-  static constexpr int NSC = TILE / 16;                          // stream copies per stage (1 KB each)
-  static constexpr int NRB = R / 16;                             // rank copies per stage
-  static constexpr int NI = NSC + NRB;
+  static constexpr int KS = 32 * KH;                             // K rows per step
+  static constexpr int NSC = TILE * KH / 16;                     // stream copies per stage (1 KB each)
+  static constexpr int NRB = R / 16;                             // 16-column rank blocks
+  static constexpr int NRC = KH * NRB;                           // rank copies per stage
+  static constexpr int NI = NSC + NRC;
   static constexpr int STREAM = 1024 * NSC;                      // stream slab bytes
   static constexpr int STAGE = 1024 * NI;
-  static constexpr int S = kStages;
+  static constexpr int S = kStages * STAGE <= 160 * 1024 ? kStages : 160 * 1024 / STAGE;
   static constexpr int NV_LO = NI / 4, NV_HI = (NI + 3) / 4;  // copies per wave (waves below NI % 4 take one more)
   static_assert(RW % 16 == 0 && RW <= 64, "rank split");
-  static_assert(S * STAGE <= 160 * 1024, "LDS");
+  static_assert(S >= 3 && S * STAGE <= 160 * 1024, "LDS");
   static_assert((S - 1) * NV_HI <= 63, "vector memory counter");
 };
 
 template <int R>
-using AccTile = f32x4_t[StageShape<R>::MT][4];
+using AccTile = f32x4_t[StageShape<R, 1>::MT][4];
 
 // Runs a workgroup's range of units. The policy supplies what differs
 // between the two contractions:
@@ -171,13 +177,13 @@ using AccTile = f32x4_t[StageShape<R>::MT][4];
 //   stream_offset(m, tile, c, lane, rows)  per-lane byte offset of stream copy c
 //   stream_base(m, tile, wb)               wave-uniform base of the window at K row wb
 //   rank_base(m)                           the item's rank operand
-//   read_b(stage, wn, g, li, b)            the B operands of the wave's four N-tiles
-//   mask_b(b, wb, k0, end, g)              zero B's K slots outside [k0, end)
+//   read_b(stage, kh, wn, g, li, b)        the B operands of the wave's four N-tiles, K-half kh
+//   mask_b(b, wb, kh, k0, end, g)          zero B's K slots outside [k0, end)
 //   store(res, m, tile, full, slot, wn, rw, g, li)
-template <int R, typename Policy>
+template <int R, int KH, typename Policy>
 __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, char* smem) {
-  using Sh = StageShape<R>;
-  constexpr int S = Sh::S, MT = Sh::MT;
+  using Sh = StageShape<R, KH>;
+  constexpr int S = Sh::S, MT = Sh::MT, KS = Sh::KS;
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int wn = wave % Sh::WN, rw = wave / Sh::WN;
   const int g = lane >> 4, li = lane & 15;
@@ -202,7 +208,7 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
     pol.enter_item(m);
   };
   auto set_offsets = [&](int m, int64_t tile) {
-    const int64_t rows = window_rows(l_kext);
+    const int64_t rows = window_rows(l_kext, KS);
 #pragma unroll
     for (int v = 0; v < Sh::NV_HI; ++v) {
       const int c = wave + 4 * v;
@@ -222,7 +228,7 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
   }
   uint32_t lslot = 0;  // stage of unit lu
   auto issue = [&]() {
-    const int64_t wb = window_base(lk * 32, l_kext);
+    const int64_t wb = window_base(lk * KS, l_kext, KS);
     const uint16_t* Sb = uniform_ptr(pol.stream_base(lm, ltile, wb));
     const uint16_t* Rb = uniform_ptr(l_rank + wb * R);
     const uint32_t st = lds0 + lslot * Sh::STAGE;
@@ -295,33 +301,37 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
 
       const RGC_LDS char* st = (const RGC_LDS char*)smem + cslot * Sh::STAGE;
       cslot = cslot + 1 == S ? 0 : cslot + 1;
-      uint32_t a[MT][4], b[4][4];
+      const int64_t t0 = ck * KS;
+      const bool partial = t0 + KS > c_kext;  // the tile's last, partial step
+      const int64_t wb = window_base(t0, c_kext, KS);
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int kh = 0; kh < KH; ++kh) {
+        uint32_t a[MT][4], b[4][4];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const u32x2v_t v =
-              lds_read_tr16(st + Sh::STREAM + 128 * ((2 * g + h) * Sh::NRB + rw * MT + mt) + 8 * li);
-          a[mt][2 * h] = v.x;
-          a[mt][2 * h + 1] = v.y;
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const u32x2v_t v = lds_read_tr16(st + Sh::STREAM +
+                                             128 * ((8 * kh + 2 * g + h) * Sh::NRB + rw * MT + mt) + 8 * li);
+            a[mt][2 * h] = v.x;
+            a[mt][2 * h + 1] = v.y;
+          }
+        pol.read_b(st, kh, wn, g, li, b);
+        if (partial) {
+          // zero both operands outside [t0, end)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t keep_p = kslot_keep(wb, kh, t0, c_kext, g, p);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) a[mt][p] &= keep_p;
+          }
+          pol.mask_b(b, wb, kh, t0, c_kext, g);
         }
-      pol.read_b(st, wn, g, li, b);
-      const int64_t t0 = ck * 32;
-      if (t0 + 32 > c_kext) {
-        // the last, partial step of the tile: zero both operands outside [t0, end)
-        const int64_t wb = window_base(t0, c_kext);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const uint32_t keep_p = kslot_keep(wb, t0, c_kext, g, p);
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) a[mt][p] &= keep_p;
-        }
-        pol.mask_b(b, wb, t0, c_kext, g);
+          for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_16x16x32(a[mt], b[nt], acc[mt][nt]);
       }
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_16x16x32(a[mt], b[nt], acc[mt][nt]);
     }
     const bool first_seg = seg_kb0 == k0 && ctile == tile0 && cm == m0;
     if (first_seg && u < u1) {
@@ -347,15 +357,18 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
 }
 
 // ---------------------------------------------------------------------------
-// project: XP = bf16(X P). N = tokens, K = k.
+// project: XP = bf16(X P). N = tokens, K = k, steps of 64 k (two K-halves),
+// so that every copy reads whole 128-byte rows of X.
 //
-// Stream copy c holds 16 tokens x 32 k (64 bytes per token) of the tile:
-// lane l reads token 16c + l / 4, k chunk q (8 values) such that its 16
-// bytes land at 16 * (4 * (l / 4) + (q + l / 16) % 4). The B operand of
-// lane (n, g) for N-tile nt is token 16nt + n, k = 8g .. 8g+7: one 16-byte
-// read, and the rotation by (l / 16) spreads the 16 lanes of a group over
-// all LDS banks.
+// Stream copy c holds 8 tokens x 64 k (128 bytes per token) of the tile:
+// lane l reads token 8c + l / 8, k chunk q (8 values) such that its 16
+// bytes land at 16 * (8 * (l / 8) + (q + l / 16 + 4 (c % 2)) % 8). The B
+// operand of lane (n, g) for N-tile nt in K-half kh is token 16nt + n,
+// k = 32kh + 8g .. +7: one 16-byte read; the rotations spread the 16 lanes
+// of a group over all LDS banks.
 // ---------------------------------------------------------------------------
+constexpr int kProjectKH = 2;
+
 struct ProjectBatch {
   Schedule s;
   const uint16_t* X[kMaxItems];
@@ -367,7 +380,7 @@ struct ProjectBatch {
 
 template <int R>
 struct ProjectPolicy {
-  using Sh = StageShape<R>;
+  using Sh = StageShape<R, kProjectKH>;
   const ProjectBatch& pb;
   int64_t ldx = 0, T = 0;  // of the copy cursor's item
   __device__ void enter_item(int m) {
@@ -379,28 +392,31 @@ struct ProjectPolicy {
     return pb.X[m] + tile * Sh::TILE * ldx + wb;
   }
   __device__ uint32_t stream_offset(int m, int64_t tile, int c, int lane, int64_t rows) const {
-    const int tl = lane >> 2;
-    const int q = ((lane & 3) - (tl >> 2)) & 3;  // k chunk whose bytes land at 16 * lane
-    int64_t t = 16 * c + tl;
+    const int tl = lane >> 3;
+    const int q = ((lane & 7) - (tl >> 1) - 4 * (c & 1)) & 7;  // k chunk whose bytes land at 16 * lane
+    int64_t t = 8 * c + tl;
     const int64_t tmax = T - 1 - tile * Sh::TILE;  // tokens past T read the last one (never stored)
     t = t < tmax ? t : tmax;
     int64_t kc = 8 * q;
     kc = kc + 8 <= rows ? kc : rows - 8;  // rows is a multiple of 8
     return (uint32_t)((t * ldx + kc) * 2);
   }
-  __device__ void read_b(const RGC_LDS char* st, int wn, int g, int li, uint32_t (&b)[4][4]) const {
+  __device__ void read_b(const RGC_LDS char* st, int kh, int wn, int g, int li, uint32_t (&b)[4][4]) const {
+    const int t = li & 7, half = li >> 3;
+    const int sigma = (4 * kh + g + (t >> 1) + 4 * half) & 7;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const u32x4v_t v = *(const RGC_LDS u32x4v_t*)(st + 1024 * (4 * wn + nt) + 16 * (4 * li + ((g + (li >> 2)) & 3)));
+      const int c = 2 * (4 * wn + nt) + half;
+      const u32x4v_t v = *(const RGC_LDS u32x4v_t*)(st + 1024 * c + 16 * (8 * t + sigma));
       b[nt][0] = v.x;
       b[nt][1] = v.y;
       b[nt][2] = v.z;
       b[nt][3] = v.w;
     }
   }
-  __device__ void mask_b(uint32_t (&b)[4][4], int64_t wb, int64_t k0, int64_t end, int g) const {
+  __device__ void mask_b(uint32_t (&b)[4][4], int64_t wb, int kh, int64_t k0, int64_t end, int g) const {
     // a lane's 8 K slots are one k chunk: all inside [k0, end) or all outside
-    const int64_t k = wb + 8 * g;
+    const int64_t k = wb + 32 * kh + 8 * g;
     const uint32_t keep = k >= k0 && k < end ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
@@ -433,9 +449,10 @@ struct ProjectPolicy {
 
 template <int R>
 __global__ __launch_bounds__(256, 1) void project_kernel(ProjectBatch pb) {
-  __shared__ __attribute__((aligned(1024))) char smem[StageShape<R>::S * StageShape<R>::STAGE];
+  using Sh = StageShape<R, kProjectKH>;
+  __shared__ __attribute__((aligned(1024))) char smem[Sh::S * Sh::STAGE];
   ProjectPolicy<R> pol{pb};
-  staged_pipeline<R>(pb.s, pol, smem);
+  staged_pipeline<R, kProjectKH>(pb.s, pol, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -458,7 +475,7 @@ struct AccumulateBatch {
 
 template <int R>
 struct AccumulatePolicy {
-  using Sh = StageShape<R>;
+  using Sh = StageShape<R, 1>;
   const AccumulateBatch& ab;
   int64_t ldd = 0, d = 0;  // of the copy cursor's item
   __device__ void enter_item(int m) {
@@ -475,20 +492,20 @@ struct AccumulatePolicy {
     col = col < d ? col : d - 8;  // past d: any valid chunk (its columns are never stored)
     return (uint32_t)((t * ldd + col) * 2);
   }
-  __device__ void read_b(const RGC_LDS char* st, int wn, int g, int li, uint32_t (&b)[4][4]) const {
+  __device__ void read_b(const RGC_LDS char* st, int kh, int wn, int g, int li, uint32_t (&b)[4][4]) const {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const u32x2v_t v = lds_read_tr16(st + 128 * ((2 * g + h) * Sh::NSC + 4 * wn + nt) + 8 * li);
+        const u32x2v_t v = lds_read_tr16(st + 128 * ((8 * kh + 2 * g + h) * Sh::NSC + 4 * wn + nt) + 8 * li);
         b[nt][2 * h] = v.x;
         b[nt][2 * h + 1] = v.y;
       }
   }
-  __device__ void mask_b(uint32_t (&b)[4][4], int64_t wb, int64_t k0, int64_t end, int g) const {
+  __device__ void mask_b(uint32_t (&b)[4][4], int64_t wb, int kh, int64_t k0, int64_t end, int g) const {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const uint32_t keep = kslot_keep(wb, k0, end, g, p);
+      const uint32_t keep = kslot_keep(wb, kh, k0, end, g, p);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) b[nt][p] &= keep;
     }
@@ -521,9 +538,10 @@ struct AccumulatePolicy {
 
 template <int R>
 __global__ __launch_bounds__(256, 1) void accumulate_kernel(AccumulateBatch ab) {
-  __shared__ __attribute__((aligned(1024))) char smem[StageShape<R>::S * StageShape<R>::STAGE];
+  using Sh = StageShape<R, 1>;
+  __shared__ __attribute__((aligned(1024))) char smem[Sh::S * Sh::STAGE];
   AccumulatePolicy<R> pol{ab};
-  staged_pipeline<R>(ab.s, pol, smem);
+  staged_pipeline<R, 1>(ab.s, pol, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -626,12 +644,12 @@ dim3 finish_grid(const Schedule& s) {
 
 template <int R>
 Schedule project_schedule(int n, const int64_t* ns, const int64_t* ks) {
-  return make_schedule(n, ns, ks, StageShape<R>::TILE, 32);
+  return make_schedule(n, ns, ks, StageShape<R, kProjectKH>::TILE, StageShape<R, kProjectKH>::KS);
 }
 
 template <int R>
 Schedule accumulate_schedule(int n, const int64_t* ns, const int64_t* ks) {
-  return make_schedule(n, ns, ks, StageShape<R>::TILE, 32);
+  return make_schedule(n, ns, ks, StageShape<R, 1>::TILE, StageShape<R, 1>::KS);
 }
 
 template <int R>
