@@ -122,71 +122,58 @@ __device__ __forceinline__ void load_row_operand(const float* __restrict__ C, in
   }
 }
 
-// Per-step buffers: this thread's share of the next P tile and this lane's W
-// values (two 16-byte chunks per N-tile).
-template <int R>
-struct TileRegs {
-  uint4 p[ApplyTraits<R>::PCPT];
-  uint4 w[ApplyTraits<R>::NTW][2];
+// ---------------------------------------------------------------------------
+// The sweeps are software pipelines over the workgroup's tiles: each tile's
+// W rows (ROWS x 64 bf16) and P rows (64 x R bf16) are copied from memory
+// straight into an LDS stage (1 KB copies that bypass the VGPRs, spread over
+// the four waves), S - 1 tiles ahead of the tile being processed.
+//
+// W stage layout: copy c holds tile rows 8c .. 8c+7 (128 bytes each); lane l
+// reads row 8c + l / 8, 8-column chunk q such that its 16 bytes land at
+// 16 * (8 * (l / 8) + (q + (l / 8) / 2 + 4 (c % 2)) % 8). A lane's two
+// chunks of its row (columns 16g .. 16g+15) are then two 16-byte reads, and
+// the rotations spread the 16 rows a wave reads at once over all banks.
+//
+// P stage layout: the 64 P rows of the tile row-major (2R bytes each) with
+// the 16-byte chunks of row jl rotated by f(jl) (bank spreading for the
+// A-operand reads, whose 16 lanes read 16 different rows).
+// ---------------------------------------------------------------------------
+// Two workgroups per compute unit with three stages each: the update's
+// per-tile arithmetic (the H rebuild on MFMA, Philox, rounding) is heavy
+// enough that a second workgroup's waves overlapping it pay more than deeper
+// staging (measured on the Qwen3-1.7B-shaped block). At r > 128 the P rows
+// make a stage too large for two, so one workgroup takes up to six.
+
+template <int R, int MODE>
+struct ApplyShape {
+  using Tr = ApplyTraits<R>;
+  static constexpr int WC = MODE == kModeReconstruct ? 0 : Tr::ROWS / 8;  // W copies per stage
+  static constexpr int CH = R / 8;                                          // 16-byte chunks per P row
+  static constexpr int PC = 64 * CH / 64;                                   // P copies per stage (= R / 8)
+  static constexpr int NI = WC + PC;
+  static constexpr int PBASE = 1024 * WC;
+  static constexpr int STAGE = 1024 * NI;
+  static constexpr int PER_CU = R > 128 ? 1 : 2;                          // resident workgroups per compute unit
+  static constexpr int LDS_MAX = (PER_CU == 2 ? 79 : 159) * 1024;        // room for the norm reduction
+  static constexpr int SMAX = PER_CU == 2 ? 3 : 6;
+  static constexpr int S = SMAX * STAGE <= LDS_MAX ? SMAX : LDS_MAX / STAGE;
+  static constexpr int NV_LO = NI / 4, NV_HI = (NI + 3) / 4;
+  static_assert(S >= 3 && S * STAGE <= LDS_MAX, "LDS");
+  static_assert((S - 1) * NV_HI <= 63, "vector memory counter");
 };
 
-// Issues the loads of tile (row0, jb): the P rows jb .. jb+63 (clamped to
-// k-1; zeroed when written to LDS) and, except for reconstruction, the
-// lane's W chunks (rows clamped to d-1, chunks clamped to k-8; such values
-// are never stored or counted).
-template <int R, int MODE>
-__device__ __forceinline__ void load_tile(const ApplyItem& it, int row0, int jb, int wave, int lane,
-                                          TileRegs<R>& t) {
-  using Tr = ApplyTraits<R>;
-  const int k = (int)it.k, d = (int)it.d;
-#pragma unroll
-  for (int c = 0; c < Tr::PCPT; ++c) {
-    const int chunk = (int)threadIdx.x + 256 * c;
-    const int jl = chunk / (R / 8), part = chunk % (R / 8);
-    const int j = jb + jl < k ? jb + jl : k - 1;
-    if (chunk < Tr::PCHUNKS) t.p[c] = *reinterpret_cast<const uint4*>(it.P + (int64_t)j * R + 8 * part);
-  }
-  if constexpr (MODE != kModeReconstruct) {
-    const int n = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int nt = 0; nt < Tr::NTW; ++nt) {
-      int i = row0 + Tr::RW * wave + 16 * nt + n;
-      i = i < d ? i : d - 1;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        int jj = jb + 16 * g + 8 * half;
-        jj = jj < k ? jj : k - 8;
-        t.w[nt][half] = *reinterpret_cast<const uint4*>(it.W + (int64_t)i * it.ldw + jj);
-      }
-    }
-  }
+// Chunk rotation of P row jl in the stage.
+template <int CH>
+__device__ __forceinline__ int p_rotation(int jl) {
+  return CH <= 8 ? (2 * (jl >> 4) + ((jl & 3) >> 1)) : (4 * (jl >> 4) + (jl & 3));
 }
 
-// Writes this thread's share of the P tile into an LDS buffer (rows past k
-// and rank columns past R as zeros).
+// h[nt][x] = H[row(nt)][jb + 16g + x], x = 0..15, from the P rows in LDS.
 template <int R>
-__device__ __forceinline__ void stage_p(const TileRegs<R>& t, int jb, int k, uint16_t* lds_p) {
-  using Tr = ApplyTraits<R>;
-#pragma unroll
-  for (int c = 0; c < Tr::PCPT; ++c) {
-    const int chunk = (int)threadIdx.x + 256 * c;
-    if (chunk < Tr::PCHUNKS) {
-      const int jl = chunk / (R / 8), part = chunk % (R / 8);
-      const uint4 v = jb + jl < k ? t.p[c] : make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(lds_p + jl * Tr::RP + 8 * part) = v;
-    }
-  }
-  if constexpr (32 * Tr::KQ > R) {  // zero the rank columns R .. 32*KQ-1 once per tile
-    constexpr int pad = 32 * Tr::KQ - R;
-    for (int e = threadIdx.x; e < kApplyCols * pad; e += 256) lds_p[(e / pad) * Tr::RP + R + e % pad] = 0;
-  }
-}
-
-// h[nt][x] = H[row(nt)][jb + 16g + x], x = 0..15, from the P tile in LDS.
-template <int R>
-__device__ __forceinline__ void rebuild_tile(const uint16_t* lds_p, const RowOperand<R>& rop, int lane,
+__device__ __forceinline__ void rebuild_tile(const RGC_LDS char* pst, const RowOperand<R>& rop, int lane,
                                              float (&h)[ApplyTraits<R>::NTW][16]) {
   using Tr = ApplyTraits<R>;
+  constexpr int CH = R / 8;
   const int m = lane & 15, g = lane >> 4;
   f32x4_t acc[4][Tr::NTW];
 #pragma unroll
@@ -196,10 +183,18 @@ __device__ __forceinline__ void rebuild_tile(const uint16_t* lds_p, const RowOpe
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int jl = 16 * (m >> 2) + 4 * t + (m & 3);
+    const int rot = p_rotation<CH>(jl);
 #pragma unroll
     for (int q = 0; q < Tr::KQ; ++q) {
-      const uint4 v = *reinterpret_cast<const uint4*>(lds_p + jl * Tr::RP + 32 * q + 8 * g);
-      const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+      const int ch = 4 * q + g;  // rank columns 32q + 8g .. +7
+      uint32_t a[4] = {0u, 0u, 0u, 0u};
+      if (32 * q + 32 <= R || ch < CH) {  // columns past R are zero (r = 48)
+        const u32x4v_t v = *(const RGC_LDS u32x4v_t*)(pst + jl * (2 * R) + 16 * ((ch + rot) % CH));
+        a[0] = v.x;
+        a[1] = v.y;
+        a[2] = v.z;
+        a[3] = v.w;
+      }
 #pragma unroll
       for (int nt = 0; nt < Tr::NTW; ++nt) {
         acc[t][nt] = mfma_16x16x32(a, rop.hi[nt][q], acc[t][nt]);
@@ -223,12 +218,19 @@ __device__ __forceinline__ void rounding_words(uint64_t seed, int64_t i, int64_t
   words[0] = o.x; words[1] = o.y; words[2] = o.z; words[3] = o.w;
 }
 
-// Two resident workgroups per compute unit, or one at r > 128 (the row
-// operand and the P tile alone take most of a wave's registers there).
+// Tiles are addressed from an origin (wrow, wcol) that keeps the whole
+// ROWS x 64 stage inside W (and the 64 P rows inside P): the tile's own
+// origin, shifted back at the last row block or column tile. The lanes then
+// work in stage coordinates (row wrow + r, column wcol + c) and only the
+// elements the tile owns (rows row0 .. row0+ROWS-1, columns jb .. jb+63, and
+// inside W) are stored or counted. Matrices with fewer than ROWS rows or 64
+// columns use origin 0 and clamp the copied rows and columns instead.
 template <int R, int MODE>
-__global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch b) {
+__global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch b) {  // ApplyShape::PER_CU
   using Tr = ApplyTraits<R>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_p[3][kApplyCols * Tr::RP];
+  using Sh = ApplyShape<R, MODE>;
+  constexpr int S = Sh::S;
+  __shared__ __attribute__((aligned(1024))) char smem[S * Sh::STAGE];
   __shared__ double red[2][kApplyWaves];
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int n = lane & 15, g = lane >> 4;
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
   const int m = apply_item_of(b, w);
   const ApplyItem& it = b.it[m];
   const int64_t wl = w - b.wbase[m], gm = b.wbase[m + 1] - b.wbase[m];
-  const int64_t u0 = wl * it.units / gm, u1 = (wl + 1) * it.units / gm;
+  const int64_t u0 = uniform_i64(wl * it.units / gm), u1 = uniform_i64((wl + 1) * it.units / gm);
 
   float s = 0.f;
   if constexpr (MODE == kModeUpdate) {
@@ -246,54 +248,99 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
 
   double sw = 0.0, sh = 0.0;
   RowOperand<R> rop;
-  int rb_loaded = -1;
+  int rop_row = -1;  // first row of the loaded row operand
   const int d = (int)it.d, k = (int)it.k, ctiles = (int)it.ctiles;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(RGC_LDS char*)smem;
+  const bool more = wave < Sh::NI % 4;
+  auto origin = [&](int64_t u, int& row0, int& jb, int& wrow, int& wcol) {
+    row0 = (int)(u / ctiles) * Tr::ROWS;
+    jb = (int)(u % ctiles) * kApplyCols;
+    wrow = row0 + Tr::ROWS <= d ? row0 : (d >= Tr::ROWS ? d - Tr::ROWS : 0);
+    wcol = jb + kApplyCols <= k ? jb : (k >= kApplyCols ? k - kApplyCols : 0);
+  };
 
-  // Tile cursors (row block, column tile), advanced one tile at a time; past
-  // the range they stay on the last tile (reloaded, never used).
-  struct Cursor {
-    int64_t u;
-    int rb, ct;
-  };
-  auto cursor_at = [&](int64_t u) {
-    Cursor c;
-    c.u = u;
-    c.rb = (int)(u / ctiles);
-    c.ct = (int)(u % ctiles);
-    return c;
-  };
-  auto advance = [&](Cursor& c) {
-    if (c.u + 1 < u1) {
-      if (++c.ct == ctiles) {
-        c.ct = 0;
-        ++c.rb;
-      }
+  // ---- copies: per-lane byte offsets from the tile origin (fixed)
+  uint32_t voff[Sh::NV_HI];
+#pragma unroll
+  for (int v = 0; v < Sh::NV_HI; ++v) {
+    const int c = wave + 4 * v;
+    if (c < Sh::WC) {
+      const int t = lane >> 3;
+      const int q = ((lane & 7) - (t >> 1) - 4 * (c & 1)) & 7;
+      const int row = 8 * c + t < d ? 8 * c + t : d - 1;
+      const int col = 8 * q + 8 <= k ? 8 * q : k - 8;
+      voff[v] = (uint32_t)(((int64_t)row * it.ldw + col) * 2);
+    } else {
+      const int e = 64 * (c - Sh::WC) + lane;
+      const int jr = e / Sh::CH, sig = e % Sh::CH;
+      const int ch = ((sig - p_rotation<Sh::CH>(jr)) % Sh::CH + Sh::CH) % Sh::CH;
+      const int prow = jr < k ? jr : k - 1;
+      voff[v] = (uint32_t)(((int64_t)prow * R + 8 * ch) * 2);
     }
-    ++c.u;
+  }
+  int64_t lu = u0;
+  uint32_t lslot = 0;
+  auto issue = [&]() {
+    int row0, jb, wrow, wcol;
+    origin(lu, row0, jb, wrow, wcol);
+    const uint16_t* Wb = uniform_ptr(it.W + (int64_t)wrow * it.ldw + wcol);
+    const uint16_t* Pb = uniform_ptr(it.P + (int64_t)wcol * R);
+    const uint32_t st = lds0 + lslot * Sh::STAGE;
+    static_for<0, Sh::NV_HI>([&](auto vc) {
+      constexpr int v = decltype(vc)::value;
+      const int c = wave + 4 * v;  // a W copy if c < WC, a P copy if WC <= c < NI
+      if constexpr (4 * v + 3 < Sh::WC) {
+        dma_16b_stream(Wb, voff[v], st + 1024 * c);
+      } else if constexpr (4 * v >= Sh::WC && 4 * v + 3 < Sh::NI) {
+        dma_16b_cached(Pb, voff[v], st + 1024 * c);
+      } else {
+        if (c < Sh::WC)
+          dma_16b_stream(Wb, voff[v], st + 1024 * c);
+        else if (c < Sh::NI)
+          dma_16b_cached(Pb, voff[v], st + 1024 * c);
+      }
+    });
+    ++lu;
+    lslot = lslot + 1 == S ? 0 : lslot + 1;
   };
-  auto load_at = [&](const Cursor& c, TileRegs<R>& t) {
-    load_tile<R, MODE>(it, c.rb * Tr::ROWS, c.ct * kApplyCols, wave, lane, t);
-  };
-  auto stage_at = [&](const Cursor& c, const TileRegs<R>& t, uint16_t* buf) {
-    stage_p<R>(t, c.ct * kApplyCols, k, buf);
-  };
-  auto process = [&](const Cursor& c, const TileRegs<R>& t, const uint16_t* buf) {
-    const int row0 = c.rb * Tr::ROWS, jb = c.ct * kApplyCols;
-    if (c.rb != rb_loaded) {  // wave-uniform: a new row block
-      load_row_operand<R>(it.C, it.d, row0 + Tr::RW * wave, lane, rop);
-      rb_loaded = c.rb;
+#pragma unroll
+  for (int v = 0; v + 1 < S; ++v)
+    if (lu < u1) issue();
+
+  uint32_t cslot = 0;
+  for (int64_t u = u0; u < u1; ++u) {
+    if (u + S - 2 < u1) {
+      if (more)
+        wait_vmcnt<(S - 2) * Sh::NV_HI>();
+      else
+        wait_vmcnt<(S - 2) * Sh::NV_LO>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    if (lu < u1) issue();
+    const RGC_LDS char* st = (const RGC_LDS char*)smem + cslot * Sh::STAGE;
+    cslot = cslot + 1 == S ? 0 : cslot + 1;
+
+    int row0, jb, wrow, wcol;
+    origin(u, row0, jb, wrow, wcol);
+    if (wrow != rop_row) {  // wave-uniform: new rows
+      load_row_operand<R>(it.C, it.d, wrow + Tr::RW * wave, lane, rop);
+      rop_row = wrow;
     }
     float h[Tr::NTW][16];
-    rebuild_tile<R>(buf, rop, lane, h);
+    rebuild_tile<R>(st + Sh::PBASE, rop, lane, h);
     // Every lane does the arithmetic; only the stores (and the norm sums)
-    // depend on whether its element lies inside W.
+    // depend on whether the tile owns its element.
 #pragma unroll
     for (int nt = 0; nt < Tr::NTW; ++nt) {
-      const int i = row0 + Tr::RW * wave + 16 * nt + n;
+      const int r = Tr::RW * wave + 16 * nt + n;  // stage row
+      const int i = wrow + r;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int jj = jb + 16 * g + 8 * half;
-        const bool inside = i < d && jj < k;
+        const int cs = 16 * g + 8 * half;  // stage column of the lane's 8-column chunk
+        const int jj = wcol + cs;
+        const bool inside = i >= row0 && i < d && jj >= jb && jj < k;
         const float* hv = &h[nt][8 * half];
         if constexpr (MODE == kModeReconstruct) {
           if (inside) {
@@ -302,7 +349,9 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
             dst[1] = make_float4(hv[4], hv[5], hv[6], hv[7]);
           }
         } else {
-          const uint4 wv = t.w[nt][half];
+          const int c = r >> 3, t = r & 7, q = cs >> 3;
+          const u32x4v_t wv =
+              *(const RGC_LDS u32x4v_t*)(st + 1024 * c + 16 * (8 * t + ((q + (t >> 1) + 4 * (c & 1)) & 7)));
           const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
           if constexpr (MODE == kModeNorms) {
             double pw = 0.0, ph = 0.0;
@@ -333,37 +382,8 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
         }
       }
     }
-  };
-
-  // Software pipeline over the workgroup's tiles, three deep, unrolled by
-  // three so that the register and LDS buffers keep fixed roles. At the top
-  // of tile u: W(u) was loaded two tiles ago, P(u) is in LDS buffer u%3, and
-  // P(u+1) was loaded to registers one tile ago. Tile u then issues the loads
-  // of tile u+2, processes u, and stages P(u+1) into LDS for the next tile.
-  // The barrier before each tile publishes the staged P and guarantees that
-  // the buffer being overwritten (read two tiles earlier) is free.
-  TileRegs<R> t3[3];
-  Cursor cp = cursor_at(u0);  // tile being processed
-  Cursor cs = cp;             // tile whose P is staged next
-  advance(cs);
-  Cursor cl = cs;             // tile whose loads are issued next
-  advance(cl);
-  load_at(cp, t3[0]);
-  load_at(cs, t3[1]);
-  stage_at(cp, t3[0], lds_p[0]);
-  for (int64_t u = u0; u < u1; u += 3) {
-#pragma unroll
-    for (int v = 0; v < 3; ++v) {
-      if (u + v >= u1) break;
-      load_at(cl, t3[(v + 2) % 3]);
-      __syncthreads();
-      process(cp, t3[v], lds_p[v]);
-      stage_at(cs, t3[(v + 1) % 3], lds_p[(v + 1) % 3]);
-      advance(cp);
-      advance(cs);
-      advance(cl);
-    }
   }
+  wait_vmcnt<0>();
 
   if constexpr (MODE == kModeNorms) {
     sw = wave_sum(sw);
@@ -456,9 +476,10 @@ namespace {
 
 // Workgroups per matrix: one per kApplyUnitsPerWG tiles, a function of the
 // matrix's own shape only, so that a matrix gets the same partition (and so
-// the same norm sums and bits) alone or in any batch. Twelve tiles of 128 x
-// 64 give the Qwen3-1.7B-shaped block 512 workgroups, two per compute unit.
-constexpr int64_t kApplyUnitsPerWG = 12;
+// the same norm sums and bits) alone or in any batch. Eight tiles of 128 x
+// 64 give the Qwen3-1.7B-shaped block 768 workgroups (two resident per
+// compute unit); measured faster than 4, 6, 10, 16 or 24 tiles.
+constexpr int64_t kApplyUnitsPerWG = 8;
 
 template <int R>
 void apply_plan(ApplyBatch& b, int n, const int64_t* ds, const int64_t* ks) {
@@ -530,8 +551,10 @@ rgc_status_t check_apply_shape(int64_t ldw, int64_t d, int64_t k, int64_t r) {
 
 rgc_status_t check_apply_item(const uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d,
                               int64_t k, const float* stats) {
-  // element indices are 32-bit inside the kernels
-  if ((d % 8) != 0 || (k % 8) != 0 || d > kMaxApplyDim || k > kMaxApplyDim) return RGC_ERR_UNSUPPORTED;
+  // element indices are 32-bit inside the kernels, and so are the byte
+  // offsets of a tile's rows from its origin
+  if ((d % 8) != 0 || (k % 8) != 0 || d > kMaxApplyDim || k > kMaxApplyDim || ldw > kMaxLeadingDim)
+    return RGC_ERR_UNSUPPORTED;
   if (!W || !C || !P) return RGC_ERR_NULL;
   if (!aligned16(W) || !aligned16(C) || !aligned16(P) || (ldw % 8) != 0) return RGC_ERR_ALIGN;
   if (stats && !aligned_to(stats, 4)) return RGC_ERR_ALIGN;

@@ -68,6 +68,17 @@ __device__ __forceinline__ u32x2v_t lds_read_tr16(const RGC_LDS char* p) {
   return __builtin_bit_cast(u32x2v_t, v);
 }
 
+// Pins a wave-uniform value to scalar registers.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  return reinterpret_cast<const uint16_t*>(uniform_u64(reinterpret_cast<uint64_t>(p)));
+}
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) { return (int64_t)uniform_u64((uint64_t)v); }
+
 // Index of the calling wave within its workgroup, as a wave-uniform (scalar)
 // value, so that branches on it and on values derived from it are scalar
 // branches rather than exec-masked ones.

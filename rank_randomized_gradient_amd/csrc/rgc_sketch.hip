@@ -55,17 +55,6 @@ __device__ __forceinline__ int64_t window_base(int64_t k0, int64_t end, int64_t 
 // Rows of a window that are valid memory for a K extent `end`.
 __device__ __forceinline__ int64_t window_rows(int64_t end, int64_t ks) { return end >= ks ? ks : end; }
 
-// Pins a wave-uniform value to scalar registers.
-__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
-  return reinterpret_cast<const uint16_t*>(uniform_u64(reinterpret_cast<uint64_t>(p)));
-}
-__device__ __forceinline__ int64_t uniform_i64(int64_t v) { return (int64_t)uniform_u64((uint64_t)v); }
-
 // K-slot keep mask of a partial step: the stage holds K rows wb .. wb+KS-1;
 // in K-half kh, dword p of a lane's operand holds rows 32kh + 8g + 2p and
 // 32kh + 8g + 2p + 1 (low and high half). Returns the halves whose rows lie
