@@ -3,34 +3,36 @@
 //
 //   W <- SR_bf16(W - s * H),  H = C P^T,  s = tau * ||W||_F / ||H||_F
 //
-// H is never written to memory. It is rebuilt 64 columns at a time on MFMA
-// (M = columns of W from rows of P, N = rows of W from rows of C, K = r), with
-// C split into a bf16 high part and a bf16 remainder so that H carries ~16
-// bits of C's mantissa. The page rebuilds H 128 rows at a time; here a
-// workgroup rebuilds 128 rows (64 for r > 64) x 64 columns per step (the
-// result does not depend on the tile shape).
+// H is never written to memory. The update rebuilds it 64 columns at a time
+// on MFMA (M = columns of W from rows of P, N = rows of W from rows of C,
+// K = r), with C split into a bf16 high part and a bf16 remainder so that H
+// carries ~16 bits of C's mantissa. The page rebuilds H 128 rows at a time;
+// here a workgroup rebuilds 128 rows (64 for r > 64) x 64 columns per step
+// (the result does not depend on the tile shape).
 //
 // One batch (e.g. all projections of a block) takes three launches:
-//   norms:  every workgroup streams its share of one matrix's W, rebuilds the
-//           same H tiles and writes one (sum w^2, sum h^2) pair (fp64 per
-//           lane, fixed-order reductions across lanes and waves);
-//   scale:  one workgroup per matrix sums that matrix's pairs in workgroup
+//   norms:  sum w^2 over W, and ||H||^2. For r <= 64, ||H||_F^2 =
+//           tr((C^T C)(P^T P)) (the Frobenius norm of a product through
+//           the two r x r Gram matrices), so W is only streamed and squared
+//           while a few workgroups per matrix form partial Gram matrices of
+//           C and of P. For r > 64 the Gram partials would be too large to
+//           reduce in one workgroup; there every workgroup streams its share
+//           of W and rebuilds the same H tiles as the update. Either way the
+//           partials are fp64 (Gram partials fp32) with fixed-order
+//           reductions across lanes and waves;
+//   scale:  one workgroup per matrix sums that matrix's partials in a fixed
 //           order and forms s = fp32(tau ||W|| / ||H||), or the skip flag when
 //           ||H|| is zero or not finite or s is not finite;
-//   update: every workgroup reads its matrix's s, rebuilds its H tiles again
-//           (same code, same order), forms v = fp32(w - fp32(s h)) and rounds
-//           stochastically with 16 bits per element from Philox4x32-10 keyed
-//           on (seed, row, column).
-// Each matrix gets one workgroup per twelve tiles (its own shape alone
-// decides, so a matrix gets the same bits alone or in a batch), and each
-// workgroup serves one matrix. Within a workgroup the W and P tiles two steps
-// ahead are loaded while the current one is processed (P goes through
-// registers into LDS, where the four waves share it).
+//   update: every workgroup reads its matrix's s, rebuilds its H tiles, forms
+//           v = fp32(w - fp32(s h)) and rounds stochastically with 16 bits
+//           per element from Philox4x32-10 keyed on (seed, row, column).
+// Each matrix gets its own workgroups in every launch, as many as its own
+// shape alone decides, so a matrix gets the same bits alone or in a batch.
 //
 // Lane layout of a tile: M-tile t row m stands for column
 // jb + 16*(m/4) + 4*t + (m%4), which gives lane (g = lane/16, n = lane%16) the
 // 16 consecutive columns jb + 16g .. +15 of its row in each N-tile, i.e. two
-// 16-byte loads of W and two Philox calls (8 columns each).
+// 16-byte reads of W and two Philox calls (8 columns each).
 #include "rgc_internal.hpp"
 
 namespace rgc {
@@ -41,6 +43,7 @@ constexpr int kApplyCols = 64;     // columns per tile
 constexpr int kApplyWaves = 4;
 constexpr int kApplyMaxItems = 16;
 constexpr int64_t kMaxApplyDim = int64_t(1) << 30;  // d and k
+constexpr int64_t kMaxApplyElems = int64_t(1) << 38;  // d * k (workgroup counts stay within int)
 
 template <int R>
 struct ApplyTraits {
@@ -68,10 +71,19 @@ struct ApplyItem {
 struct ApplyBatch {
   int n;
   float tau;
-  int wbase[kApplyMaxItems + 1];  // workgroups [wbase[m], wbase[m+1]) serve item m
+  int wbase[kApplyMaxItems + 1];  // update (and rebuild-norms) workgroups [wbase[m], wbase[m+1]) serve item m
+  // Gram-form norms launch (r <= 64): Gram workgroups [gbase[m], gbase[m+1])
+  // (the first ncg[m] over rows of C, the rest over rows of P), then W-stream
+  // workgroups gbase[n] + [sbase[m], sbase[m+1]).
+  int gbase[kApplyMaxItems + 1];
+  int sbase[kApplyMaxItems + 1];
+  int ncg[kApplyMaxItems];
   ApplyItem it[kApplyMaxItems];
-  double* partials;               // 2 per workgroup of the norms sweep
-  float* scale;                   // per item: s, flag
+  double* partials;               // rebuild norms: 2 per workgroup; Gram norms: 1 per W-stream workgroup
+  float* gram;                    // Gram norms: GramShape::NE floats per Gram workgroup
+  double* hpairs;                 // Gram norms: per item, kGramMaxPairs block-pair terms of ||H||^2
+  double* wnorm2;                 // Gram norms: per item, ||W||^2
+  float* scale;                   // rebuild norms: per item s, flag
   float* H;                       // reconstruct target (test hook)
 };
 
@@ -79,6 +91,47 @@ __device__ __forceinline__ int apply_item_of(const ApplyBatch& b, int w) {
   int m = 0;
   while (m + 1 < b.n && w >= b.wbase[m + 1]) ++m;
   return m;
+}
+
+// Ranks whose norms take the Gram form (below).
+template <int R>
+constexpr bool kGramNorms = R <= 64;
+
+template <int R>
+struct GramShape {
+  static constexpr int NB = R / 16;
+  static constexpr int NP = NB * (NB + 1) / 2;  // block pairs a <= b
+  static constexpr int NE = NP * 256;           // floats per Gram partial
+  // 32-row steps per wave of a Gram workgroup: 512 rows per workgroup keeps
+  // its share of the stream (128 KB of C at r = 64) near that of a W-stream
+  // workgroup, and the step count (each step waits for one load round) low.
+  static constexpr int STEPS = 4;
+  static constexpr int64_t ROWS = (int64_t)STEPS * 32 * kApplyWaves;
+};
+constexpr int kGramMaxPairs = 10;  // NP at r = 64
+
+// s = fp32(tau * ||W|| / ||H||) from the squared norms; flag = 1 (and s = 0)
+// when ||H|| is zero or not finite or s is not finite. stats (if not null)
+// receive {||W||, ||H||, s, flag}.
+__device__ __forceinline__ void step_scale(float tau, double nw2, double nh2, float& s, float& flag, float* stats) {
+  const double nw = sqrt(nw2), nh = sqrt(nh2);
+  s = 0.f;
+  flag = 0.f;
+  if (!(nh > 0.0) || !isfinite(nh)) {
+    flag = 1.f;
+  } else {
+    s = (float)((double)tau * nw / nh);
+    if (!isfinite(s)) {
+      s = 0.f;
+      flag = 1.f;
+    }
+  }
+  if (stats) {
+    stats[0] = (float)nw;
+    stats[1] = (float)nh;
+    stats[2] = s;
+    stats[3] = flag;
+  }
 }
 
 // The C side of the MFMA for the rows of one N-tile: K-step q holds
@@ -241,7 +294,7 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
   const int64_t u0 = uniform_i64(wl * it.units / gm), u1 = uniform_i64((wl + 1) * it.units / gm);
 
   float s = 0.f;
-  if constexpr (MODE == kModeUpdate) {
+  if constexpr (MODE == kModeUpdate && !kGramNorms<R>) {
     s = b.scale[2 * m];
     if (b.scale[2 * m + 1] != 0.f) return;  // zero or non-finite step: W stays as it is
   }
@@ -306,6 +359,19 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
 #pragma unroll
   for (int v = 0; v + 1 < S; ++v)
     if (lu < u1) issue();
+
+  if constexpr (MODE == kModeUpdate && kGramNorms<R>) {
+    // s from the item's norm terms while the first copies are in flight: the
+    // same fixed-order sums in every wave of every workgroup of the item
+    // (a butterfly gives every lane the same sum), so all agree on s.
+    const double hp = lane < GramShape<R>::NP ? b.hpairs[m * kGramMaxPairs + lane] : 0.0;
+    float flag;
+    step_scale(b.tau, b.wnorm2[m], wave_sum(hp), s, flag, wl == 0 && threadIdx.x == 0 ? it.stats : nullptr);
+    if (flag != 0.f) {  // zero or non-finite step: W stays as it is
+      wait_vmcnt<0>();
+      return;
+    }
+  }
 
   uint32_t cslot = 0;
   for (int64_t u = u0; u < u1; ++u) {
@@ -400,20 +466,244 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
   }
 }
 
-// Per item: fixed-order sum of its norms partials (thread t holds partials
-// t, t+256, ... in order; then a butterfly within each wave and the waves in
-// order), and s = fp32(tau * ||W|| / ||H||); flag = 1 when ||H|| is zero or
-// not finite or s is not finite (then s = 0).
-__global__ __launch_bounds__(256) void apply_scale_kernel(ApplyBatch b) {
-  __shared__ double red[2][4];
-  const int m = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int w0 = b.wbase[m], w1 = b.wbase[m + 1];
-  double aw = 0.0, ah = 0.0;
-  for (int w = w0 + (int)threadIdx.x; w < w1; w += 256) {
-    aw += b.partials[2 * w];
-    ah += b.partials[2 * w + 1];
+// ---------------------------------------------------------------------------
+// Gram-form norms (r <= 64).
+//
+// ||H||_F^2 = ||C P^T||_F^2 = tr(P C^T C P^T) = sum_ab (C^T C)_ab (P^T P)_ab.
+// C^T C is formed from C's bf16 high parts and remainders with all four
+// products (so only C's own two-term rounding, about 2^-18 relative and of
+// either sign, enters), P^T P from P's bf16 values (exact products), both
+// with fp32 MFMA sums over at most a few hundred rows per wave and fp64 sums
+// across workgroups. The result equals the H-based norm up to rounding. A C
+// whose squares leave the fp32 range (|c| above ~1e19) gives a non-finite
+// Gram and the update is skipped as for a non-finite ||H||.
+//
+// Lane layout: the r columns are relabelled so that block a (a < NB = r/16),
+// position x stands for column NB*x + a. Lane l (x = l % 16, g = l / 16)
+// reads the NB consecutive values NB*x .. NB*x + NB - 1 of each of its rows
+// 8g .. 8g+7 of a 32-row step, which for every block a is the MFMA operand of
+// row x with K = those 8 rows, both as A and as B. Block pair (a, b), a <= b,
+// accumulates the 16 x 16 block (a, b) of the relabelled Gram matrix. C and P
+// are relabelled alike, so the sum of the elementwise product is unchanged;
+// off-diagonal pairs count twice (the blocks (b, a) are their transposes).
+// ---------------------------------------------------------------------------
+// 16-byte chunks of W per W-stream workgroup (128 KB).
+constexpr int64_t kWStreamChunks = 8192;
+
+// The values one lane reads in one 32-row step: rows 8g .. 8g+7, columns
+// NB*x .. NB*x + NB - 1 (raw bits: fp32 for C, bf16 for P; 0 past row1).
+template <int NB>
+struct GramRows {
+  uint32_t v[8][NB];
+};
+
+template <int NB>
+__device__ __forceinline__ void load_gram_rows(const float* __restrict__ src, int64_t base, int64_t row1, int x,
+                                               int g, GramRows<NB>& o) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t row = base + 8 * g + e;
+    const float* p = src + row * (16 * NB) + NB * x;
+    if (row < row1) {
+      if constexpr (NB == 4) {
+        const uint4 a = *reinterpret_cast<const uint4*>(p);
+        o.v[e][0] = a.x; o.v[e][1] = a.y; o.v[e][2] = a.z; o.v[e][3] = a.w;
+      } else if constexpr (NB == 2) {
+        const uint2 a = *reinterpret_cast<const uint2*>(p);
+        o.v[e][0] = a.x; o.v[e][1] = a.y;
+      } else {
+#pragma unroll
+        for (int c = 0; c < NB; ++c) o.v[e][c] = __float_as_uint(p[c]);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NB; ++c) o.v[e][c] = 0u;
+    }
   }
+}
+
+template <int NB>
+__device__ __forceinline__ void load_gram_rows(const uint16_t* __restrict__ src, int64_t base, int64_t row1, int x,
+                                               int g, GramRows<NB>& o) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int64_t row = base + 8 * g + e;
+    const uint16_t* p = src + row * (16 * NB) + NB * x;
+    if (row < row1) {
+      if constexpr (NB == 4) {
+        const uint2 a = *reinterpret_cast<const uint2*>(p);
+        o.v[e][0] = a.x & 0xFFFFu; o.v[e][1] = a.x >> 16; o.v[e][2] = a.y & 0xFFFFu; o.v[e][3] = a.y >> 16;
+      } else if constexpr (NB == 2) {
+        const uint32_t a = *reinterpret_cast<const uint32_t*>(p);
+        o.v[e][0] = a & 0xFFFFu; o.v[e][1] = a >> 16;
+      } else {
+#pragma unroll
+        for (int c = 0; c < NB; ++c) o.v[e][c] = p[c];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NB; ++c) o.v[e][c] = 0u;
+    }
+  }
+}
+
+// One 32-row step: MFMA operands of every block from the lane's rows (C: bf16
+// high part and remainder of each fp32 value, all four products; P: the bf16
+// values), accumulated into the block pairs a <= b.
+template <int NB, bool TWO_TERM>
+__device__ __forceinline__ void gram_step(const GramRows<NB>& rw, f32x4_t (&acc)[NB * (NB + 1) / 2]) {
+  uint32_t hi[NB][4], lo[NB][4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int a = 0; a < NB; ++a) {
+      if constexpr (TWO_TERM) {
+        const float v0 = __uint_as_float(rw.v[2 * p][a]), v1 = __uint_as_float(rw.v[2 * p + 1][a]);
+        const uint32_t h0 = f32_to_bf16_rne(v0), h1 = f32_to_bf16_rne(v1);
+        hi[a][p] = pack_bf16x2(h0, h1);
+        lo[a][p] = pack_bf16x2(f32_to_bf16_rne(v0 - bf16_bits_to_f32(h0)), f32_to_bf16_rne(v1 - bf16_bits_to_f32(h1)));
+      } else {
+        hi[a][p] = pack_bf16x2(rw.v[2 * p][a], rw.v[2 * p + 1][a]);
+        lo[a][p] = 0u;
+      }
+    }
+  int q = 0;
+#pragma unroll
+  for (int a = 0; a < NB; ++a)
+#pragma unroll
+    for (int c = a; c < NB; ++c) {
+      acc[q] = mfma_16x16x32(hi[a], hi[c], acc[q]);
+      if constexpr (TWO_TERM) {
+        acc[q] = mfma_16x16x32(hi[a], lo[c], acc[q]);
+        acc[q] = mfma_16x16x32(lo[a], hi[c], acc[q]);
+        acc[q] = mfma_16x16x32(lo[a], lo[c], acc[q]);
+      }
+      ++q;
+    }
+}
+
+// Partial Gram matrix of rows [row0, row1) (at most ROWS) of the row-major
+// rows x R matrix src (C in fp32 with TWO_TERM, P in bf16 without), written
+// as NE floats: out[pair * 256 + 64 j + lane] = entry j of the lane's 16 x 16
+// MFMA output for block pair `pair`, summed over the four waves in wave
+// order. Wave w takes the steps at rows row0 + 32 w + 128 s; each step's
+// loads are issued before the previous step's MFMAs.
+template <int R, bool TWO_TERM, typename T>
+__device__ void gram_partial(const T* __restrict__ src, int64_t row0, int64_t row1, float* __restrict__ out,
+                             float* red) {
+  using Gs = GramShape<R>;
+  constexpr int NB = Gs::NB, NP = Gs::NP, NE = Gs::NE;
+  const int lane = threadIdx.x & 63, wave = wave_index();
+  const int x = lane & 15, g = lane >> 4;
+  f32x4_t acc[NP];
+#pragma unroll
+  for (int q = 0; q < NP; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  GramRows<NB> cur, nxt;
+  load_gram_rows<NB>(src, row0 + 32 * wave, row1, x, g, cur);
+#pragma unroll
+  for (int st = 0; st < Gs::STEPS; ++st) {
+    if (st + 1 < Gs::STEPS) load_gram_rows<NB>(src, row0 + 32 * wave + 128 * (st + 1), row1, x, g, nxt);
+    gram_step<NB, TWO_TERM>(cur, acc);
+    if (st + 1 < Gs::STEPS) cur = nxt;
+  }
+#pragma unroll
+  for (int q = 0; q < NP; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) red[(wave * NP + q) * 256 + 64 * j + lane] = acc[q][j];
+  __syncthreads();
+  for (int e = threadIdx.x; e < NE; e += 256)
+    out[e] = ((red[e] + red[NE + e]) + red[2 * NE + e]) + red[3 * NE + e];
+}
+
+// Sum of squares of the 16-byte chunks [c0, c1) of W (row-major d x k, row
+// stride ldw; chunk c is columns 8 (c % (k/8)) .. +7 of row c / (k/8)):
+// fp32 per chunk (the squares of bf16 values are exact in fp32), fp64 across
+// chunks, lanes and waves; returned in thread 0.
+__device__ double wstream_sumsq(const uint16_t* __restrict__ W, int64_t ldw, int64_t k, int64_t c0, int64_t c1,
+                                double* red) {
+  constexpr int U = 8;
+  const int lane = threadIdx.x & 63, wave = wave_index();
+  const int cpr = (int)(k >> 3);
+  const int dr = 256 / cpr, dc = 256 % cpr;  // per 256 chunks: whole rows and remainder
+  int64_t c = c0 + threadIdx.x;
+  int row = (int)(c / cpr), col = (int)(c % cpr);
+  double acc = 0.0;
+  for (; c < c1; c += 256 * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v[u] = c + 256 * u < c1 ? *reinterpret_cast<const uint4*>(W + (int64_t)row * ldw + 8 * col)
+                              : make_uint4(0u, 0u, 0u, 0u);
+      col += dc;
+      row += dr;
+      const bool wrap = col >= cpr;
+      col -= wrap ? cpr : 0;
+      row += wrap ? 1 : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      float sq = 0.f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float w0 = bf16_bits_to_f32(wd[p] & 0xFFFFu), w1 = bf16_bits_to_f32(wd[p] >> 16);
+        sq += w0 * w0;
+        sq += w1 * w1;
+      }
+      acc += (double)sq;
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) red[wave] = acc;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+__device__ __forceinline__ int item_of(const int* base, int n, int w) {
+  int m = 0;
+  while (m + 1 < n && w >= base[m + 1]) ++m;
+  return m;
+}
+
+// The norms launch for r <= 64: Gram workgroups first, then W-stream ones.
+template <int R>
+__global__ __launch_bounds__(256) void gram_norms_kernel(ApplyBatch b) {
+  using Gs = GramShape<R>;
+  __shared__ __attribute__((aligned(16))) float red[4 * Gs::NE];
+  const int w = blockIdx.x;
+  const int ng = b.gbase[b.n];
+  if (w < ng) {
+    const int m = item_of(b.gbase, b.n, w);
+    const ApplyItem& it = b.it[m];
+    const int l = w - b.gbase[m];
+    float* out = b.gram + (int64_t)w * Gs::NE;
+    if (l < b.ncg[m]) {
+      const int64_t r0 = l * Gs::ROWS, r1 = r0 + Gs::ROWS < it.d ? r0 + Gs::ROWS : it.d;
+      gram_partial<R, true>(it.C, r0, r1, out, red);
+    } else {
+      const int64_t r0 = (l - b.ncg[m]) * Gs::ROWS, r1 = r0 + Gs::ROWS < it.k ? r0 + Gs::ROWS : it.k;
+      gram_partial<R, false>(it.P, r0, r1, out, red);
+    }
+    return;
+  }
+  const int sw = w - ng;
+  const int m = item_of(b.sbase, b.n, sw);
+  const ApplyItem& it = b.it[m];
+  const int64_t total = it.d * (it.k >> 3);
+  const int64_t c0 = (sw - b.sbase[m]) * kWStreamChunks;
+  const int64_t c1 = c0 + kWStreamChunks < total ? c0 + kWStreamChunks : total;
+  const double sq = wstream_sumsq(it.W, it.ldw, it.k, c0, c1, reinterpret_cast<double*>(red));
+  if (threadIdx.x == 0) b.partials[sw] = sq;
+}
+
+// Per item: the scale launches sum its norms partials in a fixed order (each
+// thread its share in order, passed here as aw and ah; then a butterfly
+// within each wave and the waves in order) and form s = fp32(tau * ||W|| /
+// ||H||); flag = 1 when ||H|| is zero or not finite or s is not finite (then
+// s = 0).
+__device__ __forceinline__ void finish_scale(const ApplyBatch& b, int m, double aw, double ah) {
+  __shared__ double red[2][4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   aw = wave_sum(aw);
   ah = wave_sum(ah);
   if (lane == 0) {
@@ -422,27 +712,74 @@ __global__ __launch_bounds__(256) void apply_scale_kernel(ApplyBatch b) {
   }
   __syncthreads();
   if (threadIdx.x != 0) return;
-  const double nw = sqrt(((red[0][0] + red[0][1]) + red[0][2]) + red[0][3]);
-  const double nh = sqrt(((red[1][0] + red[1][1]) + red[1][2]) + red[1][3]);
-  float s = 0.f, flag = 0.f;
-  if (!(nh > 0.0) || !isfinite(nh)) {
-    flag = 1.f;
-  } else {
-    s = (float)((double)b.tau * nw / nh);
-    if (!isfinite(s)) {
-      s = 0.f;
-      flag = 1.f;
-    }
-  }
+  const double nw2 = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+  const double nh2 = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
+  float s, flag;
+  step_scale(b.tau, nw2, nh2, s, flag, b.it[m].stats);
   b.scale[2 * m] = s;
   b.scale[2 * m + 1] = flag;
-  float* st = b.it[m].stats;
-  if (st) {
-    st[0] = (float)nw;
-    st[1] = (float)nh;
-    st[2] = s;
-    st[3] = flag;
+}
+
+__global__ __launch_bounds__(256) void apply_scale_kernel(ApplyBatch b) {
+  const int m = blockIdx.x;
+  double aw = 0.0, ah = 0.0;
+  for (int w = b.wbase[m] + (int)threadIdx.x; w < b.wbase[m + 1]; w += 256) {
+    aw += b.partials[2 * w];
+    ah += b.partials[2 * w + 1];
   }
+  finish_scale(b, m, aw, ah);
+}
+
+// Gram form, one workgroup per (item, block pair): thread t sums entry
+// pair * 256 + t of the item's C Gram partials and of its P Gram partials in
+// partial order (fp64), and the workgroup writes sum over its entries of
+// G * M, times 2 for an off-diagonal pair. Pair 0's workgroup also sums the
+// item's W-stream partials into ||W||^2.
+template <int R>
+__global__ __launch_bounds__(256) void gram_reduce_kernel(ApplyBatch b) {
+  using Gs = GramShape<R>;
+  __shared__ double red[2][4];
+  const int m = blockIdx.x / Gs::NP, q = blockIdx.x % Gs::NP;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = 256 * q + (int)threadIdx.x;
+  const float* gc = b.gram + (int64_t)b.gbase[m] * Gs::NE + e;
+  const int nc = b.ncg[m], np = b.gbase[m + 1] - b.gbase[m] - nc;
+  const float* gp = gc + (int64_t)nc * Gs::NE;
+  constexpr int U = 8;  // loads in flight per thread
+  double G = 0.0, M = 0.0;
+  for (int u = 0; u < nc; u += U) {
+    float v[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) v[i] = u + i < nc ? gc[(int64_t)(u + i) * Gs::NE] : 0.f;
+#pragma unroll
+    for (int i = 0; i < U; ++i) G += (double)v[i];
+  }
+  for (int u = 0; u < np; u += U) {
+    float v[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) v[i] = u + i < np ? gp[(int64_t)(u + i) * Gs::NE] : 0.f;
+#pragma unroll
+    for (int i = 0; i < U; ++i) M += (double)v[i];
+  }
+  int pq = q, a = 0;  // pairs are listed (a, c) for a = 0.., c = a .. NB-1
+  while (pq >= Gs::NB - a) {
+    pq -= Gs::NB - a;
+    ++a;
+  }
+  double th = (pq == 0 ? 1.0 : 2.0) * G * M;
+  double tw = 0.0;
+  if (q == 0)
+    for (int w = b.sbase[m] + (int)threadIdx.x; w < b.sbase[m + 1]; w += 256) tw += b.partials[w];
+  th = wave_sum(th);
+  tw = wave_sum(tw);
+  if (lane == 0) {
+    red[0][wave] = th;
+    red[1][wave] = tw;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  b.hpairs[m * kGramMaxPairs + q] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+  if (q == 0) b.wnorm2[m] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
 }
 
 // ---------------------------------------------------------------------------
@@ -495,15 +832,58 @@ void apply_plan(ApplyBatch& b, int n, const int64_t* ds, const int64_t* ks) {
   b.n = n;
 }
 
-size_t apply_ws_bytes(int workgroups) {
-  return (size_t)((2 * workgroups * sizeof(double) + 255) / 256 * 256) + 2 * kApplyMaxItems * sizeof(float);
+// Gram-form norms launch: per matrix ceil(d / ROWS) C-Gram and
+// ceil(k / ROWS) P-Gram workgroups, and one W-stream workgroup per
+// kWStreamChunks 16-byte chunks of W.
+template <int R>
+void gram_plan(ApplyBatch& b, int n, const int64_t* ds, const int64_t* ks) {
+  using Gs = GramShape<R>;
+  b.gbase[0] = 0;
+  b.sbase[0] = 0;
+  for (int m = 0; m < n; ++m) {
+    b.ncg[m] = (int)((ds[m] + Gs::ROWS - 1) / Gs::ROWS);
+    b.gbase[m + 1] = b.gbase[m] + b.ncg[m] + (int)((ks[m] + Gs::ROWS - 1) / Gs::ROWS);
+    b.sbase[m + 1] = b.sbase[m] + (int)((ds[m] * (ks[m] / 8) + kWStreamChunks - 1) / kWStreamChunks);
+  }
+}
+
+// Workspace: norm partials (fp64), then Gram partials (fp32), then the
+// per-item Gram-form terms (fp64: block pairs, ||W||^2), then (s, flag) per
+// item, each part 256-byte aligned.
+struct ApplyWorkspace {
+  size_t gram_off, hpairs_off, wnorm2_off, scale_off, total;
+};
+
+template <int R>
+ApplyWorkspace apply_ws_layout(const ApplyBatch& b) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  ApplyWorkspace l;
+  size_t part = 0, gram = 0;
+  if constexpr (kGramNorms<R>) {
+    part = (size_t)b.sbase[b.n] * sizeof(double);
+    gram = (size_t)b.gbase[b.n] * GramShape<R>::NE * sizeof(float);
+  } else {
+    part = 2 * (size_t)b.wbase[b.n] * sizeof(double);
+  }
+  l.gram_off = up(part);
+  l.hpairs_off = l.gram_off + up(gram);
+  l.wnorm2_off = l.hpairs_off + up(kApplyMaxItems * kGramMaxPairs * sizeof(double));
+  l.scale_off = l.wnorm2_off + up(kApplyMaxItems * sizeof(double));
+  l.total = l.scale_off + up(2 * kApplyMaxItems * sizeof(float));
+  return l;
+}
+
+template <int R>
+void apply_plan_all(ApplyBatch& b, int n, const int64_t* ds, const int64_t* ks) {
+  apply_plan<R>(b, n, ds, ks);
+  if constexpr (kGramNorms<R>) gram_plan<R>(b, n, ds, ks);
 }
 
 template <int R>
 size_t apply_ws_for(int n, const int64_t* ds, const int64_t* ks) {
   ApplyBatch b = {};
-  apply_plan<R>(b, n, ds, ks);
-  return apply_ws_bytes(b.wbase[n]);
+  apply_plan_all<R>(b, n, ds, ks);
+  return apply_ws_layout<R>(b).total;
 }
 
 template <int R>
@@ -511,7 +891,7 @@ rgc_status_t apply_launch(int n, uint16_t* const* Ws, const int64_t* ldws, const
                           const uint16_t* const* Ps, const int64_t* ds, const int64_t* ks, float tau,
                           const uint64_t* seeds, float* const* stats, void* ws, hipStream_t st) {
   ApplyBatch b = {};
-  apply_plan<R>(b, n, ds, ks);
+  apply_plan_all<R>(b, n, ds, ks);
   b.tau = tau;
   for (int m = 0; m < n; ++m) {
     b.it[m].W = Ws[m];
@@ -524,10 +904,19 @@ rgc_status_t apply_launch(int n, uint16_t* const* Ws, const int64_t* ldws, const
     b.it[m].stats = stats ? stats[m] : nullptr;
   }
   const int G = b.wbase[n];
+  const ApplyWorkspace l = apply_ws_layout<R>(b);
   b.partials = static_cast<double*>(ws);
-  b.scale = reinterpret_cast<float*>(static_cast<char*>(ws) + (apply_ws_bytes(G) - 2 * kApplyMaxItems * sizeof(float)));
-  hipLaunchKernelGGL((apply_kernel<R, kModeNorms>), dim3((unsigned)G), dim3(256), 0, st, b);
-  hipLaunchKernelGGL(apply_scale_kernel, dim3((unsigned)n), dim3(256), 0, st, b);
+  b.gram = reinterpret_cast<float*>(static_cast<char*>(ws) + l.gram_off);
+  b.hpairs = reinterpret_cast<double*>(static_cast<char*>(ws) + l.hpairs_off);
+  b.wnorm2 = reinterpret_cast<double*>(static_cast<char*>(ws) + l.wnorm2_off);
+  b.scale = reinterpret_cast<float*>(static_cast<char*>(ws) + l.scale_off);
+  if constexpr (kGramNorms<R>) {
+    hipLaunchKernelGGL(gram_norms_kernel<R>, dim3((unsigned)(b.gbase[n] + b.sbase[n])), dim3(256), 0, st, b);
+    hipLaunchKernelGGL(gram_reduce_kernel<R>, dim3((unsigned)(n * GramShape<R>::NP)), dim3(256), 0, st, b);
+  } else {
+    hipLaunchKernelGGL((apply_kernel<R, kModeNorms>), dim3((unsigned)G), dim3(256), 0, st, b);
+    hipLaunchKernelGGL(apply_scale_kernel, dim3((unsigned)n), dim3(256), 0, st, b);
+  }
   hipLaunchKernelGGL((apply_kernel<R, kModeUpdate>), dim3((unsigned)G), dim3(256), 0, st, b);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
@@ -553,7 +942,8 @@ rgc_status_t check_apply_item(const uint16_t* W, int64_t ldw, const float* C, co
                               int64_t k, const float* stats) {
   // element indices are 32-bit inside the kernels, and so are the byte
   // offsets of a tile's rows from its origin
-  if ((d % 8) != 0 || (k % 8) != 0 || d > kMaxApplyDim || k > kMaxApplyDim || ldw > kMaxLeadingDim)
+  if ((d % 8) != 0 || (k % 8) != 0 || d > kMaxApplyDim || k > kMaxApplyDim || ldw > kMaxLeadingDim ||
+      d * k > kMaxApplyElems)
     return RGC_ERR_UNSUPPORTED;
   if (!W || !C || !P) return RGC_ERR_NULL;
   if (!aligned16(W) || !aligned16(C) || !aligned16(P) || (ldw % 8) != 0) return RGC_ERR_ALIGN;

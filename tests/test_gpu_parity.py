@@ -293,6 +293,35 @@ def test_apply_parity(dev, d, k, r):
     assert np.count_nonzero(bits(wg) != bits(w)) > 0.1 * d * k
 
 
+@pytest.mark.parametrize("d,k,r,pad", [(1032, 24, 16, 8), (2056, 4104, 48, 24), (264, 12808, 64, 8),
+                                       (776, 136, 32, 16), (136, 1048, 128, 8)])
+def test_apply_parity_row_stride_and_chunking(dev, d, k, r, pad):
+    """W as a view with row stride k + pad; shapes whose norms split into
+    several C-row and P-row chunks with ragged ends, and W chunks that start
+    mid-row (k = 24, 136: fewer than 256 chunks of 8 per row)."""
+    w, c, p = _apply_inputs(d, k, r, 21)
+    full = synth.normal_bf16((d, k + pad), 0.02, seed=22)
+    off = 8 if pad >= 16 else 0  # keeps W 16-byte aligned
+    full[:, off:off + k] = w
+    fg = full.clone().to(dev)
+    wg = fg[:, off:off + k]
+    seed, tau = 0x5151 + k, 1e-3
+    stats = torch.zeros(4, device=dev)
+    rgc.rgc_apply(wg, c.to(dev), p.to(dev), tau, seed, stats=stats)
+    _sync()
+    ref_w, ref_stats = orc.apply_update(bits(w), c.numpy(), bits(p), tau, seed)
+    st = stats.cpu().numpy()
+    assert st[3] == 0 and ref_stats[3] == 0
+    np.testing.assert_allclose(st[:3], ref_stats[:3], rtol=1e-5)
+    abs_terms = np.abs(c.numpy().astype(np.float64)) @ np.abs(orc.bf16_to_f64(bits(p))).T
+    assert_update_close(bits(wg.contiguous()), ref_w, ref_stats[2], abs_terms, what=f"W {d}x{k}x{r}+{pad}")
+    # the padding columns are untouched
+    got_full = bits(fg)
+    ref_full = bits(full)
+    assert np.array_equal(got_full[:, :off], ref_full[:, :off])
+    assert np.array_equal(got_full[:, off + k:], ref_full[:, off + k:])
+
+
 def test_apply_zero_sketch_leaves_weights(dev):
     d, k, r = 256, 512, 16
     w, _, p = _apply_inputs(d, k, r, 4)
