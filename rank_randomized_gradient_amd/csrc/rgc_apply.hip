@@ -301,13 +301,17 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
 
   double sw = 0.0, sh = 0.0;
   RowOperand<R> rop;
+  uint16_t* wrowp[Tr::NTW];  // update: start of the lane's W row in each N-tile
   int rop_row = -1;  // first row of the loaded row operand
   const int d = (int)it.d, k = (int)it.k, ctiles = (int)it.ctiles;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(RGC_LDS char*)smem;
   const bool more = wave < Sh::NI % 4;
-  auto origin = [&](int64_t u, int& row0, int& jb, int& wrow, int& wcol) {
-    row0 = (int)(u / ctiles) * Tr::ROWS;
-    jb = (int)(u % ctiles) * kApplyCols;
+  // Tiles run in unit order, unit = row block * ctiles + column tile; the
+  // copy cursor (lrb, lct) and the compute cursor (crb, cct) step through
+  // (row block, column tile) without dividing.
+  auto origin = [&](int rb, int ct, int& row0, int& jb, int& wrow, int& wcol) {
+    row0 = rb * Tr::ROWS;
+    jb = ct * kApplyCols;
     wrow = row0 + Tr::ROWS <= d ? row0 : (d >= Tr::ROWS ? d - Tr::ROWS : 0);
     wcol = jb + kApplyCols <= k ? jb : (k >= kApplyCols ? k - kApplyCols : 0);
   };
@@ -332,10 +336,17 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
     }
   }
   int64_t lu = u0;
+  int lrb = __builtin_amdgcn_readfirstlane((int)(u0 / ctiles));
+  int lct = __builtin_amdgcn_readfirstlane((int)(u0 - (int64_t)lrb * ctiles));
+  int crb = lrb, cct = lct;
   uint32_t lslot = 0;
   auto issue = [&]() {
     int row0, jb, wrow, wcol;
-    origin(lu, row0, jb, wrow, wcol);
+    origin(lrb, lct, row0, jb, wrow, wcol);
+    if (++lct == ctiles) {
+      lct = 0;
+      ++lrb;
+    }
     const uint16_t* Wb = uniform_ptr(it.W + (int64_t)wrow * it.ldw + wcol);
     const uint16_t* Pb = uniform_ptr(it.P + (int64_t)wcol * R);
     const uint32_t st = lds0 + lslot * Sh::STAGE;
@@ -389,10 +400,21 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
     cslot = cslot + 1 == S ? 0 : cslot + 1;
 
     int row0, jb, wrow, wcol;
-    origin(u, row0, jb, wrow, wcol);
+    origin(crb, cct, row0, jb, wrow, wcol);
+    if (++cct == ctiles) {
+      cct = 0;
+      ++crb;
+    }
     if (wrow != rop_row) {  // wave-uniform: new rows
       load_row_operand<R>(it.C, it.d, wrow + Tr::RW * wave, lane, rop);
       rop_row = wrow;
+      if constexpr (MODE == kModeUpdate) {
+#pragma unroll
+        for (int nt = 0; nt < Tr::NTW; ++nt) {
+          const int i = wrow + Tr::RW * wave + 16 * nt + n;
+          wrowp[nt] = it.W + (int64_t)(i < d ? i : d - 1) * it.ldw;
+        }
+      }
     }
     float h[Tr::NTW][16];
     rebuild_tile<R>(st + Sh::PBASE, rop, lane, h);
@@ -437,13 +459,12 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
             uint32_t out[4];
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-              const float w0 = bf16_bits_to_f32(wd[p] & 0xFFFFu), w1 = bf16_bits_to_f32(wd[p] >> 16);
+              const float w0 = __uint_as_float(wd[p] << 16), w1 = __uint_as_float(wd[p] & 0xFFFF0000u);
               const float sh0 = s * hv[2 * p], sh1 = s * hv[2 * p + 1];
               const float v0 = w0 - sh0, v1 = w1 - sh1;
-              out[p] = pack_bf16x2(f32_to_bf16_sr(v0, rw[p] & 0xFFFFu), f32_to_bf16_sr(v1, rw[p] >> 16));
+              out[p] = f32x2_to_bf16x2_sr(v0, v1, rw[p]);
             }
-            if (inside)
-              *reinterpret_cast<uint4*>(it.W + (int64_t)i * it.ldw + jj) = make_uint4(out[0], out[1], out[2], out[3]);
+            if (inside) *reinterpret_cast<uint4*>(wrowp[nt] + jj) = make_uint4(out[0], out[1], out[2], out[3]);
           }
         }
       }

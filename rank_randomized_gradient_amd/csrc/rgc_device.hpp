@@ -104,9 +104,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
     const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
     u32x4 n;
-    n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+    n.x = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c.y, k0, 0x96);  // three-way xor
     n.y = (uint32_t)p1;
-    n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+    n.z = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c.w, k1, 0x96);
     n.w = (uint32_t)p0;
     c = n;
     k0 += 0x9E3779B9u;
@@ -127,14 +127,20 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 // Stochastic rounding fp32 -> bf16 with 16 random bits: the random integer is
 // added to the dropped low half, so the kept half rounds up with probability
-// (low half) / 2^16. Infinities are kept, NaN becomes a quiet NaN.
-// (Selects, not branches: the sum is formed for every input and discarded for
-// infinities and NaNs.)
-__device__ __forceinline__ uint32_t f32_to_bf16_sr(float f, uint32_t r16) {
+// (low half) / 2^16. NaN becomes a quiet NaN keeping its sign. Infinities need
+// no case of their own: their low half is zero, so the sum never carries.
+// sr_keep returns the 32-bit word whose high half is the result.
+// (Selects, not branches: both words are formed for every input.)
+__device__ __forceinline__ uint32_t sr_keep(float f, uint32_t r16) {
   const uint32_t b = __float_as_uint(f);
-  const uint32_t rounded = (b + r16) >> 16;
-  const uint32_t special = (b & 0x007FFFFFu) ? ((b >> 16) | 0x40u) : (b >> 16);
-  return (b & 0x7F800000u) == 0x7F800000u ? special : rounded;
+  return __builtin_isnan(f) ? (b | 0x00400000u) : b + r16;
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_sr(float f, uint32_t r16) { return sr_keep(f, r16) >> 16; }
+// Two stochastically rounded values packed in a dword (v0 in the low half),
+// with the random halves of one word: low half for v0, high half for v1.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_sr(float v0, float v1, uint32_t rword) {
+  // byte select: result bytes 0, 1 = bytes 2, 3 of the first word, bytes 2, 3 = bytes 2, 3 of the second
+  return __builtin_amdgcn_perm(sr_keep(v1, rword >> 16), sr_keep(v0, rword & 0xFFFFu), 0x07060302u);
 }
 
 // Two bf16 packed in a dword, element 0 in the low half.

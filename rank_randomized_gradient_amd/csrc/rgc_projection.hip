@@ -11,7 +11,7 @@
 // matrices of one rank at once (each launch covers every matrix, so the
 // latency-bound steps are paid once per batch, not once per matrix):
 //   fill     A = Box-Muller normals from Philox
-//   gram     partial Grams of A over 128-row blocks
+//   gram     partial Grams of A over 64-row blocks
 //   reduce   G1 = A^T A (partials summed in block order)
 //   factor   U1 = chol(G1)^-1
 //   gram     Q1 = A U1 (stored), partial Grams of Q1
@@ -60,7 +60,7 @@ __global__ void rademacher_kernel(uint16_t* __restrict__ P, int64_t k, int r, ui
 // CholeskyQR2, batched over up to kQrMaxBatch matrices of one rank R <= 128.
 // ---------------------------------------------------------------------------
 constexpr int kQrMaxBatch = 16;
-constexpr int kQrBlockRows = 128;  // rows per Gram / multiply workgroup
+constexpr int kQrBlockRows = 64;  // rows per Gram / multiply workgroup (more workgroups than compute units for the 1.7B-block shapes)
 constexpr int kQrSub = 16;         // rows staged in LDS at a time
 constexpr double kTwoPi = 6.283185307179586;  // 2*pi rounded to double
 
@@ -72,12 +72,12 @@ struct QrBatch {
   uint16_t* P[kQrMaxBatch];
   double* A[kQrMaxBatch];     // k x R Gaussian
   double* Q1[kQrMaxBatch];    // k x R after the first pass
-  double* part[kQrMaxBatch];  // one R x R partial Gram per 128-row block
+  double* part[kQrMaxBatch];  // one R x R partial Gram per 64-row block
   double* U1[kQrMaxBatch];
   double* U2[kQrMaxBatch];
   uint32_t* status[kQrMaxBatch];
   int fill_begin[kQrMaxBatch + 1];   // workgroup prefix of the Gaussian fill
-  int block_begin[kQrMaxBatch + 1];  // workgroup prefix of the 128-row blocks
+  int block_begin[kQrMaxBatch + 1];  // workgroup prefix of the 64-row blocks
 };
 
 __device__ __forceinline__ int batch_item(const int* begin, int n, int b) {
@@ -117,14 +117,14 @@ __global__ __launch_bounds__(256) void gauss_fill_kernel(QrBatch b) {
   for (int e = 0; e < 4; ++e) dst[e] = z[e];
 }
 
-// Rows staged in LDS at a time: a whole 128-row block when U (R x R) and the
+// Rows staged in LDS at a time: a whole 64-row block when U (R x R) and the
 // rows fit together, else 16 (R = 128).
 template <int R>
 struct QrTile {
   static constexpr int SUB = R <= 64 ? kQrBlockRows : 16;
 };
 
-// One 128-row block of one matrix, staged through LDS (all at once when it fits).
+// One 64-row block of one matrix, staged through LDS (all at once when it fits).
 //   MODE 0: partial Gram of A.
 //   MODE 1: Q1 = A U1 (stored), then partial Gram of Q1.
 //   MODE 2: P = bf16(fp32(scale * Q1 U2)).
