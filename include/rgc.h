@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define RGC_ABI_VERSION 1
+#define RGC_ABI_VERSION 2
 
 typedef enum {
   RGC_OK = 0,
@@ -67,7 +67,8 @@ typedef enum {
   RGC_ERR_UNSUPPORTED = 3, /* r or d/k outside the supported set (see above) */
   RGC_ERR_ALIGN = 4,       /* a base pointer or leading dimension is misaligned */
   RGC_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the query */
-  RGC_ERR_HIP = 6          /* a kernel launch failed */
+  RGC_ERR_HIP = 6,         /* a kernel launch failed */
+  RGC_ERR_VALUE = 7        /* a scalar argument is not finite */
 } rgc_status_t;
 
 typedef enum {
@@ -189,6 +190,47 @@ rgc_status_t rgc_apply_batch(int64_t n, uint16_t* const* Ws, const int64_t* ldws
                              const uint16_t* const* Ps, const int64_t* ds, const int64_t* ks, int64_t r,
                              float tau, const uint64_t* seeds, float* const* stats, void* ws,
                              size_t ws_bytes, void* stream);
+
+/* ---- The fixed-scale update ([LoGRA-M], "Minimal Causal Code") -----------
+ *
+ * W <- SR_bf16(W - alpha * H), H = C P^T: the tutorial's plain-SGD update
+ * W -= alpha*eta*(U @ A) with U = S (the sketch, here C) and A = P^T, the
+ * step alpha*eta passed as one fp32 scalar `alpha` chosen by the caller (the
+ * pages' KL-based step controller stays with the caller). No norms are taken
+ * and nothing is skipped: the update runs in one launch, with the same H
+ * tiles, pre-rounding value v = fp32(w - fp32(alpha*h)) and rounding bits as
+ * rgc_apply (so rgc_apply_scaled with alpha = the s that rgc_apply reports in
+ * stats[2] gives rgc_apply's bits). The pages do not say how LoGRA rounds its
+ * bf16 weights; this library keeps no fp32 copy and rounds stochastically as
+ * for [RGC]. A non-finite alpha returns RGC_ERR_VALUE; non-finite values in C
+ * give non-finite weights, as the dense update would. No workspace. */
+rgc_status_t rgc_apply_scaled(uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d,
+                              int64_t k, int64_t r, float alpha, uint64_t seed, void* stream);
+
+/* rgc_apply_scaled for n <= 16 matrices of one rank r in one launch; alphas
+ * and the other arrays are HOST arrays of n entries (as rgc_apply_batch). */
+rgc_status_t rgc_apply_scaled_batch(int64_t n, uint16_t* const* Ws, const int64_t* ldws,
+                                    const float* const* Cs, const uint16_t* const* Ps,
+                                    const int64_t* ds, const int64_t* ks, int64_t r,
+                                    const float* alphas, const uint64_t* seeds, void* stream);
+
+/* ---- Applying a received sketch from its projection seed ------------------
+ *
+ * The receiving side of a policy update ([LoGRA-S], Key Contributions item 2;
+ * [LoGRA-M], "Why Refreshing the Projection Enables New Update Directions"):
+ * only the d x r factor and the projection seed travel; the receiver
+ * regenerates P (k x r, `kind`, `proj_seed`) in the workspace and applies the
+ * update. mode RGC_UPDATE_NORMALIZED: rgc_apply with tau = `step` (stats as
+ * there, may be NULL); RGC_UPDATE_SCALED: rgc_apply_scaled with alpha = `step`
+ * (stats must be NULL). Given the same W, C, seeds and step, the result is bit
+ * for bit what the sender computes with its own P. */
+typedef enum { RGC_UPDATE_NORMALIZED = 0, RGC_UPDATE_SCALED = 1 } rgc_update_mode_t;
+
+size_t rgc_apply_from_seed_workspace_size(rgc_proj_kind_t kind, int64_t d, int64_t k, int64_t r);
+rgc_status_t rgc_apply_from_seed(rgc_update_mode_t mode, rgc_proj_kind_t kind, uint64_t proj_seed,
+                                 uint16_t* W, int64_t ldw, const float* C, int64_t d, int64_t k,
+                                 int64_t r, float step, uint64_t seed, float* stats, void* ws,
+                                 size_t ws_bytes, void* stream);
 
 /* ---- Test hooks (same library; used by the parity tests) ----------------- */
 

@@ -323,6 +323,22 @@ def apply_update(w_bits: np.ndarray, c: np.ndarray, p_bits: np.ndarray, tau: flo
     return stochastic_round(v, rounding_bits(seed, d, k)), stats
 
 
+def apply_scaled(w_bits: np.ndarray, c: np.ndarray, p_bits: np.ndarray, alpha, seed: int) -> np.ndarray:
+    """W <- SR_bf16(W - alpha H), H = C P^T: the fixed-step update.
+
+    [LoGRA-M, "Minimal Causal Code"]: W -= alpha * eta * (U @ A), with U = S
+    for plain SGD on the sketch (C here) and A = P^T; the caller passes the
+    product alpha*eta as one fp32 scalar. Readings: the pages do not say how
+    LoGRA rounds bf16 weights; the same stochastic rounding and bit stream as
+    apply_update are used, and the pre-rounding value is formed exactly as
+    there, v = fp32(w - fp32(alpha * h)). No norms, nothing skipped.
+    """
+    h32 = reconstruct(c, p_bits).astype(np.float32)
+    v = pre_round_values(w_bits, h32, np.float32(alpha))
+    d, k = np.shape(w_bits)
+    return stochastic_round(v, rounding_bits(seed, d, k))
+
+
 def pre_round_values(w_bits: np.ndarray, h32: np.ndarray, s) -> np.ndarray:
     """v = fp32(w - fp32(s * h)) elementwise, no fused multiply-add."""
     w32 = bf16_to_f64(w_bits).astype(np.float32)

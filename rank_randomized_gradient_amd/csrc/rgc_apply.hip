@@ -33,6 +33,8 @@
 // jb + 16*(m/4) + 4*t + (m%4), which gives lane (g = lane/16, n = lane%16) the
 // 16 consecutive columns jb + 16g .. +15 of its row in each N-tile, i.e. two
 // 16-byte reads of W and two Philox calls (8 columns each).
+#include <cmath>
+
 #include "rgc_internal.hpp"
 
 namespace rgc {
@@ -66,10 +68,12 @@ struct ApplyItem {
   int64_t units;   // row blocks x column tiles
   uint64_t seed;
   float* stats;
+  float alpha;  // fixed-scale update: the caller's step
 };
 
 struct ApplyBatch {
   int n;
+  int fixed;  // 1: fixed-scale update (s = it.alpha, no norms, never skipped)
   float tau;
   int wbase[kApplyMaxItems + 1];  // update (and rebuild-norms) workgroups [wbase[m], wbase[m+1]) serve item m
   // Gram-form norms launch (r <= 64): Gram workgroups [gbase[m], gbase[m+1])
@@ -294,9 +298,13 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
   const int64_t u0 = uniform_i64(wl * it.units / gm), u1 = uniform_i64((wl + 1) * it.units / gm);
 
   float s = 0.f;
-  if constexpr (MODE == kModeUpdate && !kGramNorms<R>) {
-    s = b.scale[2 * m];
-    if (b.scale[2 * m + 1] != 0.f) return;  // zero or non-finite step: W stays as it is
+  if constexpr (MODE == kModeUpdate) {
+    if (b.fixed) {
+      s = it.alpha;
+    } else if constexpr (!kGramNorms<R>) {
+      s = b.scale[2 * m];
+      if (b.scale[2 * m + 1] != 0.f) return;  // zero or non-finite step: W stays as it is
+    }
   }
 
   double sw = 0.0, sh = 0.0;
@@ -372,15 +380,17 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
     if (lu < u1) issue();
 
   if constexpr (MODE == kModeUpdate && kGramNorms<R>) {
-    // s from the item's norm terms while the first copies are in flight: the
-    // same fixed-order sums in every wave of every workgroup of the item
-    // (a butterfly gives every lane the same sum), so all agree on s.
-    const double hp = lane < GramShape<R>::NP ? b.hpairs[m * kGramMaxPairs + lane] : 0.0;
-    float flag;
-    step_scale(b.tau, b.wnorm2[m], wave_sum(hp), s, flag, wl == 0 && threadIdx.x == 0 ? it.stats : nullptr);
-    if (flag != 0.f) {  // zero or non-finite step: W stays as it is
-      wait_vmcnt<0>();
-      return;
+    if (!b.fixed) {
+      // s from the item's norm terms while the first copies are in flight: the
+      // same fixed-order sums in every wave of every workgroup of the item
+      // (a butterfly gives every lane the same sum), so all agree on s.
+      const double hp = lane < GramShape<R>::NP ? b.hpairs[m * kGramMaxPairs + lane] : 0.0;
+      float flag;
+      step_scale(b.tau, b.wnorm2[m], wave_sum(hp), s, flag, wl == 0 && threadIdx.x == 0 ? it.stats : nullptr);
+      if (flag != 0.f) {  // zero or non-finite step: W stays as it is
+        wait_vmcnt<0>();
+        return;
+      }
     }
   }
 
@@ -910,10 +920,12 @@ size_t apply_ws_for(int n, const int64_t* ds, const int64_t* ks) {
 template <int R>
 rgc_status_t apply_launch(int n, uint16_t* const* Ws, const int64_t* ldws, const float* const* Cs,
                           const uint16_t* const* Ps, const int64_t* ds, const int64_t* ks, float tau,
-                          const uint64_t* seeds, float* const* stats, void* ws, hipStream_t st) {
+                          const uint64_t* seeds, float* const* stats, void* ws, hipStream_t st,
+                          const float* alphas = nullptr) {
   ApplyBatch b = {};
   apply_plan_all<R>(b, n, ds, ks);
   b.tau = tau;
+  b.fixed = alphas ? 1 : 0;
   for (int m = 0; m < n; ++m) {
     b.it[m].W = Ws[m];
     b.it[m].ldw = ldws[m];
@@ -923,8 +935,13 @@ rgc_status_t apply_launch(int n, uint16_t* const* Ws, const int64_t* ldws, const
     b.it[m].k = ks[m];
     b.it[m].seed = seeds[m];
     b.it[m].stats = stats ? stats[m] : nullptr;
+    b.it[m].alpha = alphas ? alphas[m] : 0.f;
   }
   const int G = b.wbase[n];
+  if (alphas) {  // fixed scale: the update sweep alone, no workspace
+    hipLaunchKernelGGL((apply_kernel<R, kModeUpdate>), dim3((unsigned)G), dim3(256), 0, st, b);
+    return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+  }
   const ApplyWorkspace l = apply_ws_layout<R>(b);
   b.partials = static_cast<double*>(ws);
   b.gram = reinterpret_cast<float*>(static_cast<char*>(ws) + l.gram_off);
@@ -973,6 +990,17 @@ rgc_status_t check_apply_item(const uint16_t* W, int64_t ldw, const float* C, co
 }
 
 }  // namespace
+
+rgc_status_t apply_validate(const uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d, int64_t k,
+                            int64_t r, bool scaled, float step, const float* stats) {
+  if (check_apply_shape(ldw, d, k, r) != RGC_OK) return RGC_ERR_SHAPE;
+  if (!rank_supported(r)) return RGC_ERR_UNSUPPORTED;
+  const rgc_status_t st = check_apply_item(W, ldw, C, P, d, k, stats);
+  if (st != RGC_OK) return st;
+  if (scaled && !std::isfinite(step)) return RGC_ERR_VALUE;
+  return RGC_OK;
+}
+
 }  // namespace rgc
 
 using namespace rgc;
@@ -1021,6 +1049,36 @@ extern "C" rgc_status_t rgc_apply(uint16_t* W, int64_t ldw, const float* C, cons
                                   void* stream) {
   if (d <= 0 || k <= 0 || r <= 0) return RGC_ERR_SHAPE;
   return rgc_apply_batch(1, &W, &ldw, &C, &P, &d, &k, r, tau, &seed, &stats, ws, ws_bytes, stream);
+}
+
+extern "C" rgc_status_t rgc_apply_scaled_batch(int64_t n, uint16_t* const* Ws, const int64_t* ldws,
+                                               const float* const* Cs, const uint16_t* const* Ps, const int64_t* ds,
+                                               const int64_t* ks, int64_t r, const float* alphas,
+                                               const uint64_t* seeds, void* stream) {
+  if (n < 0 || r <= 0) return RGC_ERR_SHAPE;
+  if (n > kApplyMaxItems) return RGC_ERR_UNSUPPORTED;
+  if (n == 0) return RGC_OK;
+  if (!Ws || !ldws || !Cs || !Ps || !ds || !ks || !alphas || !seeds) return RGC_ERR_NULL;
+  for (int64_t m = 0; m < n; ++m)
+    if (check_apply_shape(ldws[m], ds[m], ks[m], r) != RGC_OK) return RGC_ERR_SHAPE;
+  if (!rank_supported(r)) return RGC_ERR_UNSUPPORTED;
+  for (int64_t m = 0; m < n; ++m) {
+    const rgc_status_t st = check_apply_item(Ws[m], ldws[m], Cs[m], Ps[m], ds[m], ks[m], nullptr);
+    if (st != RGC_OK) return st;
+    if (!std::isfinite(alphas[m])) return RGC_ERR_VALUE;
+  }
+  rgc_status_t st = RGC_OK;
+  dispatch_rank(r, [&](auto rc) {
+    st = apply_launch<decltype(rc)::value>((int)n, Ws, ldws, Cs, Ps, ds, ks, 0.f, seeds, nullptr, nullptr,
+                                           static_cast<hipStream_t>(stream), alphas);
+  });
+  return st;
+}
+
+extern "C" rgc_status_t rgc_apply_scaled(uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d,
+                                         int64_t k, int64_t r, float alpha, uint64_t seed, void* stream) {
+  if (d <= 0 || k <= 0 || r <= 0) return RGC_ERR_SHAPE;
+  return rgc_apply_scaled_batch(1, &W, &ldw, &C, &P, &d, &k, r, &alpha, &seed, stream);
 }
 
 extern "C" rgc_status_t rgc_test_reconstruct(const float* C, const uint16_t* P, float* H, int64_t d, int64_t k,

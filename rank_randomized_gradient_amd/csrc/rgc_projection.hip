@@ -491,6 +491,11 @@ size_t batch_ws(rgc_proj_kind_t kind, int64_t n, const int64_t* ks, int64_t r) {
 }
 
 }  // namespace
+
+rgc_status_t sample_validate(rgc_proj_kind_t kind, int64_t k, int64_t r, const uint16_t* P) {
+  return check_item(kind, k, r, P);
+}
+
 }  // namespace rgc
 
 using namespace rgc;

@@ -9,6 +9,9 @@ Names mirror the C ABI in include/rgc.h:
   rgc_project(X, P)                         -> XP = bf16(X P)
   rgc_accumulate(D, XP, C)                  C += D^T XP (in place)
   rgc_apply(W, C, P, tau, seed)             W <- SR(W - tau ||W|| H / ||H||) (in place)
+  rgc_apply_scaled(W, C, P, alpha, seed)    W <- SR(W - alpha H) (in place)
+  rgc_apply_from_seed(mode, kind, proj_seed, W, C, step, seed)
+                                            P regenerated from its seed, then one of the two
 """
 from __future__ import annotations
 
@@ -24,6 +27,9 @@ LIB_PATH = os.path.join(_PKG_DIR, "librgc.so")
 RGC_PROJ_RADEMACHER = 0
 RGC_PROJ_QR_GAUSSIAN = 1
 _KINDS = {"rademacher": RGC_PROJ_RADEMACHER, "qr": RGC_PROJ_QR_GAUSSIAN}
+RGC_UPDATE_NORMALIZED = 0
+RGC_UPDATE_SCALED = 1
+_MODES = {"normalized": RGC_UPDATE_NORMALIZED, "scaled": RGC_UPDATE_SCALED}
 
 _i64 = ctypes.c_int64
 _u64 = ctypes.c_uint64
@@ -56,6 +62,13 @@ SIGNATURES = {
                                        ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i64, _f32,
                                        ctypes.POINTER(_u64), ctypes.POINTER(_vp), _vp, _sz, _vp]),
     "rgc_apply": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _f32, _u64, _vp, _vp, _sz, _vp]),
+    "rgc_apply_scaled": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _f32, _u64, _vp]),
+    "rgc_apply_scaled_batch": (ctypes.c_int, [_i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_vp),
+                                              ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i64,
+                                              ctypes.POINTER(_f32), ctypes.POINTER(_u64), _vp]),
+    "rgc_apply_from_seed_workspace_size": (_sz, [ctypes.c_int, _i64, _i64, _i64]),
+    "rgc_apply_from_seed": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _u64, _vp, _i64, _vp, _i64, _i64, _i64, _f32,
+                                           _u64, _vp, _vp, _sz, _vp]),
     "rgc_test_philox": (ctypes.c_int, [_u64, _i64, _vp, _vp, _vp]),
     "rgc_test_stochastic_round": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _u64, _vp]),
     "rgc_test_reconstruct": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
@@ -351,6 +364,75 @@ def rgc_apply_batch(Ws, Cs, Ps, tau: float, seeds, stats=None, workspace: Worksp
     _check(lib.rgc_apply_batch(n, _ptrs(Ws), _i64s(ldws), _ptrs(Cs), _ptrs(Ps), _i64s(ds), _i64s(ks), r,
                                float(tau), seeds_arr, sps, wp, wn, _stream(dev)))
     return Ws
+
+
+def _apply_items(Ws, Cs, Ps):
+    r = Cs[0].shape[1]
+    ldws, ds, ks = [], [], []
+    for W, C, P in zip(Ws, Cs, Ps):
+        ldws.append(_rows(W, torch.bfloat16, "W"))
+        _dense(C, torch.float32, "C")
+        _dense(P, torch.bfloat16, "P")
+        d, k = W.shape
+        if tuple(C.shape) != (d, r) or tuple(P.shape) != (k, r):
+            raise RgcError("items must share r: W d x k, C d x r, P k x r")
+        ds.append(d)
+        ks.append(k)
+    return r, ldws, ds, ks
+
+
+def rgc_apply_scaled_batch(Ws, Cs, Ps, alphas, seeds):
+    """W <- SR(W - alpha H) for several matrices of one rank in one launch."""
+    lib = load_library()
+    n = len(Ws)
+    if n == 0:
+        return Ws
+    if len(Cs) != n or len(Ps) != n or len(alphas) != n or len(seeds) != n:
+        raise RgcError("Ws, Cs, Ps, alphas and seeds must have the same length")
+    dev = _need_gpu(*Ws, *Cs, *Ps)
+    r, ldws, ds, ks = _apply_items(Ws, Cs, Ps)
+    alphas_arr = (_f32 * n)(*[float(a) for a in alphas])
+    seeds_arr = (_u64 * n)(*[s & 0xFFFFFFFFFFFFFFFF for s in seeds])
+    _check(lib.rgc_apply_scaled_batch(n, _ptrs(Ws), _i64s(ldws), _ptrs(Cs), _ptrs(Ps), _i64s(ds), _i64s(ks), r,
+                                      alphas_arr, seeds_arr, _stream(dev)))
+    return Ws
+
+
+def rgc_apply_scaled(W: torch.Tensor, C: torch.Tensor, P: torch.Tensor, alpha: float, seed: int) -> torch.Tensor:
+    lib = load_library()
+    dev = _need_gpu(W, C, P)
+    r, ldws, ds, ks = _apply_items([W], [C], [P])
+    _check(lib.rgc_apply_scaled(W.data_ptr(), ldws[0], C.data_ptr(), P.data_ptr(), ds[0], ks[0], r, float(alpha),
+                                seed & 0xFFFFFFFFFFFFFFFF, _stream(dev)))
+    return W
+
+
+def rgc_apply_from_seed(mode: str, kind: str, proj_seed: int, W: torch.Tensor, C: torch.Tensor, step: float,
+                        seed: int, stats: torch.Tensor | None = None,
+                        workspace: Workspace | None = None) -> torch.Tensor:
+    """Regenerates P (kind, proj_seed) in the workspace and applies the update
+    (mode "normalized": tau = step; "scaled": alpha = step)."""
+    lib = load_library()
+    dev = _need_gpu(W, C)
+    ldw = _rows(W, torch.bfloat16, "W")
+    _dense(C, torch.float32, "C")
+    d, k = W.shape
+    r = C.shape[1]
+    if C.shape[0] != d:
+        raise RgcError("shapes must be W: d x k, C: d x r")
+    sp = None
+    if stats is not None:
+        _need_gpu(stats)
+        _dense(stats, torch.float32, "stats")
+        if stats.numel() < 4:
+            raise RgcError("stats needs 4 floats")
+        sp = stats.data_ptr()
+    ws = workspace or default_workspace(dev)
+    wp, wn = ws.get(lib.rgc_apply_from_seed_workspace_size(_KINDS[kind], d, k, r))
+    _check(lib.rgc_apply_from_seed(_MODES[mode], _KINDS[kind], proj_seed & 0xFFFFFFFFFFFFFFFF, W.data_ptr(), ldw,
+                                   C.data_ptr(), d, k, r, float(step), seed & 0xFFFFFFFFFFFFFFFF, sp, wp, wn,
+                                   _stream(dev)))
+    return W
 
 
 # ---- test hooks -------------------------------------------------------------

@@ -1,0 +1,141 @@
+"""GPU parity of the fixed-step update and of the update applied from a
+projection seed, through the C ABI.
+
+  * rgc_apply_scaled / rgc_apply_scaled_batch: W <- SR_bf16(W - alpha C P^T)
+    ([LoGRA-M], "Minimal Causal Code") against the oracle's apply_scaled, with
+    the bar of the normalized update: every element within 1 bf16 ulp plus
+    alpha * 2^-15 * sum_a |c_ia p_ja|, at most 1e-4 of the elements differing.
+  * alpha = the normalized update's own step s reproduces rgc_apply's bits.
+  * rgc_apply_from_seed: a receiver that only has C and the projection seed
+    ends with exactly the sender's weights ([LoGRA-S], Key Contributions 2).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from rank_randomized_gradient_amd import rgc, synth
+from parity_tools import assert_update_close
+
+pytestmark = pytest.mark.gpu
+
+bits = synth.to_numpy_bits
+from_bits = synth.from_numpy_bits
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rgc.load_library()
+    return torch.device("cuda", 0)
+
+
+def _inputs(d, k, r, seed):
+    w = synth.normal_bf16((d, k), 0.02, seed=seed)
+    c = synth.normal_f32((d, r), 1e-2, seed=seed + 1)
+    p = orc.qr_projection(seed, k, r) if r <= 128 else orc.rademacher_projection(seed, k, r)
+    return w, c, from_bits(p)
+
+
+def _abs_terms(c, p):
+    return np.abs(c.numpy().astype(np.float64)) @ np.abs(orc.bf16_to_f64(bits(p))).T
+
+
+@pytest.mark.parametrize("d,k,r,alpha", [(256, 512, 16, 3e-3), (1000, 520, 48, 1e-3), (2048, 2048, 64, 2e-4),
+                                         (264, 1024, 128, 5e-3), (128, 2048, 256, 1e-3), (6144, 2048, 64, -4e-4)])
+def test_scaled_update_parity(dev, d, k, r, alpha):
+    w, c, p = _inputs(d, k, r, 61)
+    seed = 0x1234 + d
+    wg = w.clone().to(dev)
+    rgc.rgc_apply_scaled(wg, c.to(dev), p.to(dev), alpha, seed)
+    torch.cuda.synchronize()
+    ref = orc.apply_scaled(bits(w), c.numpy(), bits(p), np.float32(alpha), seed)
+    assert_update_close(bits(wg), ref, alpha, _abs_terms(c, p), what=f"W {d}x{k}x{r}")
+    assert np.count_nonzero(bits(wg) != bits(w)) > 0.05 * d * k
+
+
+def test_scaled_update_strided_weights(dev):
+    d, k, r, pad, alpha = 520, 1040, 64, 24, 1e-3
+    w, c, p = _inputs(d, k, r, 62)
+    full = synth.normal_bf16((d, k + pad), 0.02, seed=63)
+    full[:, 8:8 + k] = w
+    fg = full.clone().to(dev)
+    rgc.rgc_apply_scaled(fg[:, 8:8 + k], c.to(dev), p.to(dev), alpha, 5)
+    torch.cuda.synchronize()
+    ref = orc.apply_scaled(bits(w), c.numpy(), bits(p), np.float32(alpha), 5)
+    got = bits(fg)
+    assert_update_close(np.ascontiguousarray(got[:, 8:8 + k]), ref, alpha, _abs_terms(c, p), what="strided W")
+    assert np.array_equal(got[:, :8], bits(full)[:, :8]) and np.array_equal(got[:, 8 + k:], bits(full)[:, 8 + k:])
+
+
+def test_scaled_update_at_normalized_step_gives_normalized_bits(dev):
+    for d, k, r in [(2048, 2048, 64), (264, 1024, 128)]:
+        w, c, p = _inputs(d, k, r, 64)
+        cg, pg = c.to(dev), p.to(dev)
+        w1, w2 = w.clone().to(dev), w.clone().to(dev)
+        stats = torch.zeros(4, device=dev)
+        rgc.rgc_apply(w1, cg, pg, 1e-3, 99, stats=stats)
+        torch.cuda.synchronize()
+        s = float(stats.cpu().numpy()[2])
+        rgc.rgc_apply_scaled(w2, cg, pg, s, 99)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(w1), bits(w2)), (d, k, r)
+
+
+def test_scaled_batch_matches_single_calls(dev):
+    r = 64
+    shapes = [(2048, 2048), (1024, 2048), (6144, 2048), (2048, 6144), (264, 520)]
+    items = [_inputs(d, k, r, 70 + i) for i, (d, k) in enumerate(shapes)]
+    alphas = [1e-3, 2e-3, -5e-4, 1e-4, 3e-3]
+    seeds = [(7 << 32) | i for i in range(len(shapes))]
+    wb = [w.clone().to(dev) for w, _, _ in items]
+    cs = [c.to(dev) for _, c, _ in items]
+    ps = [p.to(dev) for _, _, p in items]
+    rgc.rgc_apply_scaled_batch(wb, cs, ps, alphas, seeds)
+    for i, (w, _, _) in enumerate(items):
+        one = w.clone().to(dev)
+        rgc.rgc_apply_scaled(one, cs[i], ps[i], alphas[i], seeds[i])
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(one), bits(wb[i])), shapes[i]
+
+
+def test_zero_step_keeps_weights(dev):
+    w, c, p = _inputs(512, 1024, 64, 80)
+    wg = w.clone().to(dev)
+    rgc.rgc_apply_scaled(wg, c.to(dev), p.to(dev), 0.0, 3)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(wg), bits(w))
+
+
+@pytest.mark.parametrize("kind,mode,d,k,r", [("qr", "normalized", 2048, 1024, 64), ("qr", "scaled", 1032, 2056, 128),
+                                             ("rademacher", "normalized", 1024, 2048, 256),
+                                             ("rademacher", "scaled", 512, 512, 16)])
+def test_apply_from_seed_matches_sender(dev, kind, mode, d, k, r):
+    """Sender: draws P, accumulates, applies. Receiver: gets C and the seeds only."""
+    w = synth.normal_bf16((d, k), 0.02, seed=90)
+    c = synth.normal_f32((d, r), 1e-2, seed=91).to(dev)
+    proj_seed, sr_seed, step = (3 << 32) | 17, 0xBEEF, 1e-3
+    p = rgc.rgc_sample_projection(kind, proj_seed, k, r, device=dev)
+    sender, receiver = w.clone().to(dev), w.clone().to(dev)
+    st_s, st_r = torch.zeros(4, device=dev), torch.zeros(4, device=dev)
+    if mode == "normalized":
+        rgc.rgc_apply(sender, c, p, step, sr_seed, stats=st_s)
+        rgc.rgc_apply_from_seed(mode, kind, proj_seed, receiver, c, step, sr_seed, stats=st_r)
+    else:
+        rgc.rgc_apply_scaled(sender, c, p, step, sr_seed)
+        rgc.rgc_apply_from_seed(mode, kind, proj_seed, receiver, c, step, sr_seed)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(sender), bits(receiver))
+    assert torch.equal(st_s, st_r)
+    assert np.count_nonzero(bits(receiver) != bits(w)) > 0.05 * d * k
+    # and the receiver's result matches the oracle's update with the oracle's own P
+    ref_p = orc.sample_projection(kind, proj_seed, k, r)
+    if mode == "normalized":
+        ref, _ = orc.apply_update(bits(w), c.cpu().numpy(), ref_p, step, sr_seed)
+    else:
+        ref = orc.apply_scaled(bits(w), c.cpu().numpy(), ref_p, np.float32(step), sr_seed)
+    # (QR P may differ from the oracle's at rounding-boundary elements; the update bar absorbs it)
+    abs_terms = np.abs(c.cpu().numpy().astype(np.float64)) @ np.abs(orc.bf16_to_f64(ref_p)).T
+    s = float(st_r.cpu().numpy()[2]) if mode == "normalized" else step
+    assert_update_close(bits(receiver), ref, s, abs_terms, what=f"receiver {kind} {mode}")

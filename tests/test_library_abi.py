@@ -13,7 +13,7 @@ from rank_randomized_gradient_amd import rgc
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rgc.h")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, VALUE = 0, 1, 2, 3, 4, 5, 7
 FAKE = 0x10000  # an aligned address that is never dereferenced: every call below fails validation first
 
 
@@ -44,8 +44,8 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
-        assert lib.rgc_status_string(s)
+    for s in range(8):
+        assert b"unknown" not in lib.rgc_status_string(s)
     assert b"unknown" in lib.rgc_status_string(99)
 
 
@@ -134,6 +134,53 @@ def test_apply_batch_validation(lib):
     # a matrix's workspace share does not depend on the rest of the batch
     one = lib.rgc_apply_workspace_size(64, 256, 64)
     assert 0 < one <= need
+
+
+def test_scaled_apply_validation(lib):
+    s = None
+    f = ctypes.c_float(1e-3)
+    assert lib.rgc_apply_scaled(FAKE, 255, FAKE, FAKE, 64, 256, 16, f, 0, s) == SHAPE
+    assert lib.rgc_apply_scaled(FAKE, 256, FAKE, FAKE, 64, 256, 272, f, 0, s) == SHAPE  # r > k
+    assert lib.rgc_apply_scaled(FAKE, 256, FAKE, FAKE, 60, 256, 16, f, 0, s) == UNSUP
+    assert lib.rgc_apply_scaled(FAKE, 256, FAKE, None, 64, 256, 16, f, 0, s) == NULL
+    assert lib.rgc_apply_scaled(FAKE + 8, 256, FAKE, FAKE, 64, 256, 16, f, 0, s) == ALIGN
+    for bad in (float("nan"), float("inf"), -float("inf")):
+        assert lib.rgc_apply_scaled(FAKE, 256, FAKE, FAKE, 64, 256, 16, ctypes.c_float(bad), 0, s) == VALUE
+    n = 2
+    ws_ = (ctypes.c_void_p * n)(FAKE, FAKE)
+    lds = (ctypes.c_int64 * n)(256, 512)
+    ds = (ctypes.c_int64 * n)(64, 128)
+    ks = (ctypes.c_int64 * n)(256, 512)
+    seeds = (ctypes.c_uint64 * n)(1, 2)
+    alphas = (ctypes.c_float * n)(1e-3, float("nan"))
+    assert lib.rgc_apply_scaled_batch(0, None, None, None, None, None, None, 64, None, None, s) == OK
+    assert lib.rgc_apply_scaled_batch(n, ws_, lds, ws_, ws_, ds, ks, 64, None, seeds, s) == NULL
+    assert lib.rgc_apply_scaled_batch(n, ws_, lds, ws_, ws_, ds, ks, 64, alphas, seeds, s) == VALUE
+    assert lib.rgc_apply_scaled_batch(17, ws_, lds, ws_, ws_, ds, ks, 64, alphas, seeds, s) == UNSUP
+
+
+def test_apply_from_seed_validation(lib):
+    s = None
+    f = ctypes.c_float(1e-3)
+    need = lib.rgc_apply_from_seed_workspace_size(1, 2048, 1024, 64)
+    # the regenerated P (bf16) plus the larger of the sampling and update scratch
+    assert need >= 1024 * 64 * 2 + lib.rgc_sample_projection_workspace_size(1, 1024, 64)
+    assert need >= 1024 * 64 * 2 + lib.rgc_apply_workspace_size(2048, 1024, 64)
+    assert lib.rgc_apply_from_seed_workspace_size(1, 2048, 1024, 256) == 0  # QR limited to r <= 128
+    assert lib.rgc_apply_from_seed_workspace_size(0, 2048, 1024, 256) > 1024 * 256 * 2
+    args = lambda mode=0, kind=1, W=FAKE, ldw=1024, C=FAKE, d=2048, r=64, step=f, stats=None, ws=FAKE, n=need: (
+        mode, kind, 5, W, ldw, C, d, 1024, r, step, 7, stats, ws, n, s)
+    assert lib.rgc_apply_from_seed(*args(mode=2)) == UNSUP
+    assert lib.rgc_apply_from_seed(*args(mode=1, stats=FAKE)) == UNSUP  # stats only with the normalized update
+    assert lib.rgc_apply_from_seed(*args(ldw=1000)) == SHAPE
+    assert lib.rgc_apply_from_seed(*args(r=2048)) == SHAPE  # r > k
+    assert lib.rgc_apply_from_seed(*args(ws=None)) == WS
+    assert lib.rgc_apply_from_seed(*args(n=need - 256)) == WS
+    assert lib.rgc_apply_from_seed(*args(ws=FAKE + 128)) == ALIGN
+    assert lib.rgc_apply_from_seed(*args(kind=1, r=256, n=1 << 30)) == UNSUP  # QR at r = 256
+    assert lib.rgc_apply_from_seed(*args(C=None)) == NULL
+    assert lib.rgc_apply_from_seed(*args(d=2044)) == UNSUP
+    assert lib.rgc_apply_from_seed(*args(mode=1, step=ctypes.c_float(float("nan")))) == VALUE
 
 
 def test_projection_validation(lib):
