@@ -11,14 +11,17 @@
 // matrices of one rank at once (each launch covers every matrix, so the
 // latency-bound steps are paid once per batch, not once per matrix):
 //   fill     A = Box-Muller normals from Philox
-//   gram     partial Grams of A over 64-row blocks
+//   gram     partial Grams of A over 64-row (r = 128: 128-row) blocks
 //   reduce   G1 = A^T A (partials summed in block order)
 //   factor   U1 = chol(G1)^-1
-//   gram     Q1 = A U1 (stored), partial Grams of Q1
+//   gram     Q1 = A U1 (stored), partial Grams of Q1, and P = bf16(fp32(
+//            sqrt(k/r) * Q1)) as a candidate
 //   reduce   G2 = Q1^T Q1
 //   factor   U2 = chol(G2)^-1 (G2 is the identity up to rounding, so this is
 //            the first-order expansion I - S unless some |G2 - I| >= 1e-7)
-//   gram     P = bf16(fp32(sqrt(k/r) * Q1 U2))
+//   gram     P = bf16(fp32(sqrt(k/r) * Q1 U2)), skipped (the candidate kept)
+//            when every |G2 - I| < 1e-14, as it is for well-conditioned
+//            Gaussian matrices
 // Cholesky factors have a positive diagonal, so Q is the unique factor with
 // the standard sign correction; the second pass restores orthogonality to
 // fp64 accuracy. Every reduction has a fixed order, so P is bit-reproducible.
@@ -60,9 +63,17 @@ __global__ void rademacher_kernel(uint16_t* __restrict__ P, int64_t k, int r, ui
 // CholeskyQR2, batched over up to kQrMaxBatch matrices of one rank R <= 128.
 // ---------------------------------------------------------------------------
 constexpr int kQrMaxBatch = 16;
-constexpr int kQrBlockRows = 64;  // rows per Gram / multiply workgroup (more workgroups than compute units for the 1.7B-block shapes)
+// Rows per Gram / multiply workgroup: 64 up to r = 64 (two workgroups fit a
+// compute unit); 128 at r = 128, where a workgroup's LDS (U alone is 128 KB)
+// fills a compute unit, so that the workgroups of a block's projections stay
+// within one round over the compute units.
+constexpr int qr_block_rows(int64_t r) { return r <= 64 ? 64 : 128; }
 constexpr int kQrSub = 16;         // rows staged in LDS at a time
 constexpr double kTwoPi = 6.283185307179586;  // 2*pi rounded to double
+// When every entry of Q1^T Q1 - I is below this, Q1 (U2 = I - S, |S| below it
+// too) already equals the second pass's Q to ~1e-14, far inside the bf16
+// rounding of P, and the P written from Q1 by the first multiply is kept.
+constexpr double kQrFinalTol = 1e-14;
 
 struct QrBatch {
   int n;
@@ -72,12 +83,14 @@ struct QrBatch {
   uint16_t* P[kQrMaxBatch];
   double* A[kQrMaxBatch];     // k x R Gaussian
   double* Q1[kQrMaxBatch];    // k x R after the first pass
-  double* part[kQrMaxBatch];  // one R x R partial Gram per 64-row block
+  double* part[kQrMaxBatch];  // one R x R partial Gram per row block
   double* U1[kQrMaxBatch];
   double* U2[kQrMaxBatch];
+  // status[m]: [0], [1] = factorization failed in pass 1, 2; [2] = the first
+  // pass is already orthonormal to kQrFinalTol, so P from it is final
   uint32_t* status[kQrMaxBatch];
   int fill_begin[kQrMaxBatch + 1];   // workgroup prefix of the Gaussian fill
-  int block_begin[kQrMaxBatch + 1];  // workgroup prefix of the 64-row blocks
+  int block_begin[kQrMaxBatch + 1];  // workgroup prefix of the row blocks
 };
 
 __device__ __forceinline__ int batch_item(const int* begin, int n, int b) {
@@ -121,12 +134,12 @@ __global__ __launch_bounds__(256) void gauss_fill_kernel(QrBatch b) {
 // rows fit together, else 16 (R = 128).
 template <int R>
 struct QrTile {
-  static constexpr int SUB = R <= 64 ? kQrBlockRows : 16;
+  static constexpr int SUB = R <= 64 ? qr_block_rows(R) : 16;
 };
 
-// One 64-row block of one matrix, staged through LDS (all at once when it fits).
+// One row block of one matrix, staged through LDS (all at once when it fits).
 //   MODE 0: partial Gram of A.
-//   MODE 1: Q1 = A U1 (stored), then partial Gram of Q1.
+//   MODE 1: Q1 = A U1 (stored, with the candidate P from it), then partial Gram of Q1.
 //   MODE 2: P = bf16(fp32(scale * Q1 U2)).
 // Thread (tx, ty) (16 x 16) owns Gram entries (ty + 16a, tx + 16c) and, in the
 // multiply, rows ty + 16i of the staged rows at columns tx + 16v. U is dense
@@ -141,9 +154,13 @@ __global__ __launch_bounds__(256) void qr_block_kernel(QrBatch b) {
   const int m = batch_item(b.block_begin, b.n, blockIdx.x);
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int64_t k = b.k[m];
-  const int64_t rbeg = (int64_t)(blockIdx.x - b.block_begin[m]) * kQrBlockRows;
-  const int64_t rend = rbeg + kQrBlockRows < k ? rbeg + kQrBlockRows : k;
+  constexpr int64_t BR = qr_block_rows(R);
+  const int64_t rbeg = (int64_t)(blockIdx.x - b.block_begin[m]) * BR;
+  const int64_t rend = rbeg + BR < k ? rbeg + BR : k;
   const double* src = MODE == 2 ? b.Q1[m] : b.A[m];
+  if constexpr (MODE == 2) {
+    if (b.status[m][2] != 0u) return;  // P from the first pass is final
+  }
   if constexpr (MODE != 0) {
     // R*R/256 loads per thread, all issued before the first LDS store
     const double* U = MODE == 1 ? b.U1[m] : b.U2[m];
@@ -217,7 +234,10 @@ __global__ __launch_bounds__(256) void qr_block_kernel(QrBatch b) {
           const int64_t row = r0 + ty + 16 * i;
           if (row >= rend) continue;
 #pragma unroll
-          for (int v = 0; v < TU; ++v) b.Q1[m][row * R + tx + 16 * v] = y[i][v];
+          for (int v = 0; v < TU; ++v) {
+            b.Q1[m][row * R + tx + 16 * v] = y[i][v];
+            b.P[m][row * R + tx + 16 * v] = (uint16_t)f32_to_bf16_rne((float)(b.scale[m] * y[i][v]));
+          }
         }
         __syncthreads();  // everyone is done reading the staged rows
 #pragma unroll
@@ -277,27 +297,39 @@ __global__ __launch_bounds__(256) void qr_gram_reduce_kernel(QrBatch b, double* 
   G_all[(int64_t)m * R * R + e] = sum;
 }
 
-// One workgroup (1024 threads) per matrix: U = chol(G)^-1 (upper triangular,
+// One workgroup (NT x NT threads) per matrix: U = chol(G)^-1 (upper triangular,
 // zeros below) from the summed Gram G (upper triangle).
 //
 // U comes from one Gaussian elimination of [G | I] without pivoting (stable
 // for symmetric positive definite G): with G = L D L^T (L unit lower), the
 // eliminated left block is D L^T and the right block is L^-1, so
-// R = D^1/2 L^T and R^-1 = L^-T D^-1/2. Thread (ty, tx) of a 32 x 32 grid
-// keeps elements (ty + 32a, tx + 32c) in registers: the symmetric Schur
+// R = D^1/2 L^T and R^-1 = L^-T D^-1/2. Thread (ty, tx) of an NT x NT grid
+// keeps elements (ty + NT a, tx + NT c) in registers: the symmetric Schur
 // complement in the upper triangle and L^-1 (unit diagonal implied) in the
 // strictly lower one. Only the pivot row travels through LDS, double
 // buffered, together with its reciprocal pivot, so each column costs one
 // barrier and no division on the critical path of the other threads.
 template <int R>
-__global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double* __restrict__ G_all, int second) {
-  constexpr int TT = (R + 31) / 32;
+struct QrFactorShape {
+  // NT x NT threads, each holding TT x TT elements. (16 x 16 threads at
+  // r = 64, with cheaper barriers but four times the per-thread work per
+  // column, measured twice as slow.)
+  static constexpr int NT = 32;
+  static constexpr int TT = (R + NT - 1) / NT;
+  static constexpr int THREADS = NT * NT;
+};
+
+template <int R>
+__global__ __launch_bounds__(QrFactorShape<R>::THREADS) void qr_factor_kernel(QrBatch b, const double* __restrict__ G_all,
+                                                                             int second) {
+  constexpr int NT = QrFactorShape<R>::NT;
+  constexpr int TT = QrFactorShape<R>::TT;
   __shared__ double rowbuf[2][R];
   __shared__ double rinv[2];
   __shared__ double diag[R];
   const int m = blockIdx.x;
   const int tid = threadIdx.x;
-  const int tx = tid & 31, ty = tid >> 5;
+  const int tx = tid % NT, ty = tid / NT;
   double* U = second ? b.U2[m] : b.U1[m];
   const double* G = G_all + (int64_t)m * R * R;
 
@@ -306,7 +338,7 @@ __global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double
   for (int i = 0; i < TT; ++i)
 #pragma unroll
     for (int j = 0; j < TT; ++j) {
-      const int l = ty + 32 * i, c = tx + 32 * j;
+      const int l = ty + NT * i, c = tx + NT * j;
       a[i][j] = (l < R && c < R && c >= l) ? G[l * R + c] : 0.0;
       if (l == 0 && c < R) rowbuf[0][c] = a[i][j];
       if (l == 0 && c == 0) rinv[0] = 1.0 / a[i][j];
@@ -317,21 +349,29 @@ __global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double
     // upper triangle of E (diagonal halved) up to O(|E|^2), and its inverse
     // is I - S up to O(|E|^2): below 1e-14 when every |E| < 1e-7, so the
     // elimination below is skipped. Otherwise it runs as for G1.
-    bool far = false;
+    bool far = false, above_final = false;
 #pragma unroll
     for (int i = 0; i < TT; ++i)
 #pragma unroll
       for (int j = 0; j < TT; ++j) {
-        const int l = ty + 32 * i, c = tx + 32 * j;
-        if (l < R && c < R && c >= l) far = far || !(fabs(a[i][j] - (c == l ? 1.0 : 0.0)) < 1e-7);
+        const int l = ty + NT * i, c = tx + NT * j;
+        if (l < R && c < R && c >= l) {
+          const double e = fabs(a[i][j] - (c == l ? 1.0 : 0.0));
+          far = far || !(e < 1e-7);
+          above_final = above_final || !(e < kQrFinalTol);
+        }
       }
+    const bool keep_first = !__syncthreads_or(above_final);
     if (!__syncthreads_or(far)) {
-      if (tid == 0) b.status[m][second] = 0u;
+      if (tid == 0) {
+        b.status[m][second] = 0u;
+        b.status[m][2] = keep_first ? 1u : 0u;
+      }
 #pragma unroll
       for (int i = 0; i < TT; ++i)
 #pragma unroll
         for (int j = 0; j < TT; ++j) {
-          const int l = ty + 32 * i, c = tx + 32 * j;
+          const int l = ty + NT * i, c = tx + NT * j;
           if (l >= R || c >= R) continue;
           U[l * R + c] = c < l ? 0.0 : (c == l ? 1.0 - 0.5 * (a[i][j] - 1.0) : -a[i][j]);
         }
@@ -344,12 +384,12 @@ __global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double
     const double inv = rinv[j & 1];
 #pragma unroll
     for (int i = 0; i < TT; ++i) {
-      const int l = ty + 32 * i;
+      const int l = ty + NT * i;
       if (l <= j || l >= R) continue;
       const double f = rb[l] * inv;  // G(l, j) / G(j, j), from the symmetric upper copy
 #pragma unroll
       for (int jj = 0; jj < TT; ++jj) {
-        const int c = tx + 32 * jj;
+        const int c = tx + NT * jj;
         if (c >= R) continue;
         if (c >= l || c < j) a[i][jj] -= f * rb[c];
         else if (c == j) a[i][jj] = -f;  // E(l, j) = 0 - f * E(j, j)
@@ -357,7 +397,7 @@ __global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double
       if (l == j + 1) {
 #pragma unroll
         for (int jj = 0; jj < TT; ++jj) {
-          const int c = tx + 32 * jj;
+          const int c = tx + NT * jj;
           if (c < R) rowbuf[(j + 1) & 1][c] = a[i][jj];
           if (c == l) rinv[(j + 1) & 1] = 1.0 / a[i][jj];
         }
@@ -369,7 +409,7 @@ __global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double
   for (int i = 0; i < TT; ++i)
 #pragma unroll
     for (int j = 0; j < TT; ++j) {
-      const int l = ty + 32 * i, c = tx + 32 * j;
+      const int l = ty + NT * i, c = tx + NT * j;
       if (l < R && c == l) diag[l] = a[i][j];
     }
   __syncthreads();
@@ -377,12 +417,13 @@ __global__ __launch_bounds__(1024) void qr_factor_kernel(QrBatch b, const double
     bool ok = true;
     for (int c = 0; c < R; ++c) ok = ok && (diag[c] > 0.0) && isfinite(diag[c]);
     b.status[m][second] = ok ? 0u : 1u;
+    if (second) b.status[m][2] = 0u;
   }
 #pragma unroll
   for (int i = 0; i < TT; ++i)
 #pragma unroll
     for (int j = 0; j < TT; ++j) {
-      const int l = ty + 32 * i, c = tx + 32 * j;
+      const int l = ty + NT * i, c = tx + NT * j;
       if (l >= R || c >= R || c > l) continue;
       const double rs = 1.0 / sqrt(diag[l]);
       if (c == l) {
@@ -403,7 +444,7 @@ struct QrItemLayout {
 
 QrItemLayout qr_item_layout(int64_t k, int64_t r) {
   QrItemLayout l;
-  l.blocks = (int)((k + kQrBlockRows - 1) / kQrBlockRows);
+  l.blocks = (int)((k + qr_block_rows(r) - 1) / qr_block_rows(r));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -415,7 +456,7 @@ QrItemLayout qr_item_layout(int64_t k, int64_t r) {
   l.part = take((size_t)l.blocks * r * r * sizeof(double));
   l.u1 = take((size_t)r * r * sizeof(double));
   l.u2 = take((size_t)r * r * sizeof(double));
-  l.status = take(2 * sizeof(uint32_t));
+  l.status = take(3 * sizeof(uint32_t));
   l.total = off;
   return l;
 }
@@ -452,10 +493,10 @@ rgc_status_t qr_launch(int n, const uint64_t* seeds, const int64_t* ks, uint16_t
   hipLaunchKernelGGL((qr_block_kernel<R, 0>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   const dim3 red_grid((unsigned)((R * R + 255) / 256), (unsigned)n);
   hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
-  hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(1024), 0, s, b, G_all, 0);
+  hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(QrFactorShape<R>::THREADS), 0, s, b, G_all, 0);
   hipLaunchKernelGGL((qr_block_kernel<R, 1>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
-  hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(1024), 0, s, b, G_all, 1);
+  hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(QrFactorShape<R>::THREADS), 0, s, b, G_all, 1);
   hipLaunchKernelGGL((qr_block_kernel<R, 2>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
