@@ -70,7 +70,7 @@ def assert_update_close(got_bits, ref_bits, s, abs_terms, rel_h=2.0**-15, max_mi
     return frac
 
 
-def qr_margin_mismatches(got_bits, seed, k, r):
+def qr_margin_mismatches(got_bits, seed, k, r, rel=1e-12):
     """Number of QR projection elements that differ from the oracle's; each
     difference must sit where the oracle's fp64 pre-rounding value is within
     1e-12 (relative) of a rounding boundary, so that either neighbour is a
@@ -81,8 +81,8 @@ def qr_margin_mismatches(got_bits, seed, k, r):
     bad = np.argwhere(got_bits != ref)
     for i, j in bad:
         v = ref_pre[i, j]
-        lo = orc.f64_to_bf16_via_f32(np.array([v * (1 - 1e-12)]))[0]
-        hi = orc.f64_to_bf16_via_f32(np.array([v * (1 + 1e-12)]))[0]
+        lo = orc.f64_to_bf16_via_f32(np.array([v * (1 - rel)]))[0]
+        hi = orc.f64_to_bf16_via_f32(np.array([v * (1 + rel)]))[0]
         assert got_bits[i, j] in (lo, hi), (i, j, v, hex(got_bits[i, j]), hex(ref[i, j]))
     return len(bad)
 

@@ -107,6 +107,22 @@ def test_qr_projection_bitexact(dev, k, r, seed):
     assert nbad <= 2
 
 
+@pytest.mark.parametrize("k,r,seed", [(64, 64, 1), (128, 64, 2), (128, 128, 3), (96, 48, 4), (32, 16, 5)])
+def test_qr_projection_near_square(dev, k, r, seed):
+    """k close to r: the Gaussian is far less well conditioned, so the first
+    CholeskyQR pass is not orthonormal to 1e-14 and the second pass's multiply
+    runs. Both sides are backward stable, so their Q differ by about
+    cond(A) * 1e-16; the margin is widened to 1e-10 accordingly."""
+    got = rgc.rgc_sample_projection("qr", seed, k, r, device=dev)
+    _sync()
+    a = orc.gaussian_matrix(seed, k, r)
+    assert np.linalg.cond(a) < 1e5
+    nbad = _qr_margin_ok(bits(got), seed, k, r, rel=1e-10)
+    assert nbad <= 2
+    pv = orc.bf16_to_f64(bits(got))
+    np.testing.assert_allclose(pv.T @ pv, (k / r) * np.eye(r), atol=2e-2 * k / r)
+
+
 def test_batched_projections_equal_single_draws(dev):
     shapes = [(2048, 1), (1024, 2), (6144, 3), (2048, 2**40 + 4), (4096, 5)]
     for kind in ("qr", "rademacher"):
