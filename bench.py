@@ -121,7 +121,12 @@ def main():
     D = [normal((T, d), 1e-3) for _, d, _, _ in mats]
     W = [normal((d, k), 0.02) for _, d, k, _ in mats]
     P = [torch.empty((k, r), dtype=torch.bfloat16, device=dev) for _, _, k, _ in mats]
-    C = [torch.zeros((d, r), dtype=torch.float32, device=dev) for _, d, _, _ in mats]
+    # the 7 sketches are views of one buffer, so that zeroing them is one launch
+    c_all = torch.zeros(sum(d for _, d, _, _ in mats) * r, dtype=torch.float32, device=dev)
+    C, off = [], 0
+    for _, d, _, _ in mats:
+        C.append(c_all[off:off + d * r].view(d, r))
+        off += d * r
     XP = [torch.empty((mb, r), dtype=torch.bfloat16, device=dev) for _ in mats]
     ws = rgc.Workspace(dev)
     torch.cuda.synchronize()
@@ -143,8 +148,7 @@ def main():
 
     def one_step(step):
         sample_all(step)
-        for m in range(len(mats)):
-            C[m].zero_()
+        c_all.zero_()
         for i in range(n_mb):
             project_mb(i)
             accumulate_mb(i)
