@@ -1,0 +1,98 @@
+"""A bf16 linear layer trained through the sketch instead of a dense weight gradient.
+
+[RGC, "How it works"] (page "Randomized Gradient Compression"): the forward
+keeps X P instead of X; the backward adds D^T (X P) to an fp32 sketch C while
+the input gradient D W flows on as usual; after the step's microbatches the
+weights take the normalized update with stochastic rounding and a new P is
+drawn. [LoGRA-M, "Minimal Causal Code"] (page "LoGRA: Low-Rank Gradient
+Sketches") runs the same loop with a caller-chosen step (`apply_update(...,
+alpha=...)`).
+
+The sketch steps run in the library's kernels (rgc_project in the forward,
+rgc_accumulate in the backward, rgc_apply / rgc_apply_scaled at the update,
+rgc_sample_projection for P). The layer's own products Y = X W^T and
+dX = D W are the model's dense GEMMs and stay with torch. W never receives a
+.grad: the sketch replaces it.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import rgc
+
+
+class SketchedLinearFunction(torch.autograd.Function):
+    """Y = X W^T; saves XP = X P (T x r), not X; backward: dX = D W and C += D^T XP."""
+
+    @staticmethod
+    def forward(ctx, x, weight, proj, sketch, workspace):
+        x2 = x.reshape(-1, x.shape[-1])
+        if not x2.is_contiguous():
+            x2 = x2.contiguous()
+        y = torch.nn.functional.linear(x2, weight)
+        xp = rgc.rgc_project(x2, proj, workspace=workspace)
+        ctx.save_for_backward(xp, weight)
+        ctx.sketch = sketch
+        ctx.workspace = workspace
+        ctx.in_shape = x.shape
+        return y.reshape(*x.shape[:-1], weight.shape[0])
+
+    @staticmethod
+    def backward(ctx, dy):
+        xp, weight = ctx.saved_tensors
+        d2 = dy.reshape(-1, dy.shape[-1])
+        if d2.dtype != torch.bfloat16:
+            d2 = d2.to(torch.bfloat16)
+        if not d2.is_contiguous():
+            d2 = d2.contiguous()
+        rgc.rgc_accumulate(d2, xp, ctx.sketch, workspace=ctx.workspace)
+        dx = (d2 @ weight).reshape(ctx.in_shape) if ctx.needs_input_grad[0] else None
+        return dx, None, None, None, None
+
+
+class SketchedLinear(torch.nn.Module):
+    """out x in bf16 linear layer (no bias) with a rank-r sketch in place of its gradient.
+
+    Per update: begin_update(seed) draws P and zeroes C; every microbatch's
+    forward/backward adds its D^T (X P) to C; apply_update(...) changes the
+    weights in place. P and C live on the layer (k x r bf16 and d x r fp32).
+    """
+
+    def __init__(self, in_features: int, out_features: int, rank: int, kind: str = "qr", device=None,
+                 weight: torch.Tensor | None = None):
+        super().__init__()
+        device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        if weight is None:
+            weight = torch.empty((out_features, in_features), dtype=torch.bfloat16, device=device)
+            torch.nn.init.normal_(weight, std=0.02)
+        if tuple(weight.shape) != (out_features, in_features) or weight.dtype != torch.bfloat16:
+            raise rgc.RgcError("weight must be a bf16 out_features x in_features tensor")
+        self.weight = torch.nn.Parameter(weight.to(device), requires_grad=False)
+        self.rank, self.kind = rank, kind
+        self.register_buffer("proj", torch.empty((in_features, rank), dtype=torch.bfloat16, device=device))
+        self.register_buffer("sketch", torch.zeros((out_features, rank), dtype=torch.float32, device=device))
+        self.workspace = rgc.Workspace(device)
+        self.proj_seed = None
+
+    def begin_update(self, proj_seed: int) -> None:
+        """Draws P from its seed (fixed for the whole accumulation) and zeroes C."""
+        rgc.rgc_sample_projection(self.kind, proj_seed, self.weight.shape[1], self.rank, out=self.proj,
+                                  workspace=self.workspace)
+        self.sketch.zero_()
+        self.proj_seed = proj_seed
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if self.proj_seed is None:
+            raise rgc.RgcError("begin_update(seed) must draw the projection before the first forward")
+        return SketchedLinearFunction.apply(x, self.weight, self.proj, self.sketch, self.workspace)
+
+    def apply_update(self, seed: int, tau: float | None = None, alpha: float | None = None,
+                     stats: torch.Tensor | None = None) -> None:
+        """Normalized update with tau [RGC], or the fixed step alpha [LoGRA-M]; one of the two."""
+        if (tau is None) == (alpha is None):
+            raise rgc.RgcError("give exactly one of tau (normalized update) or alpha (fixed step)")
+        w = self.weight.data
+        if tau is not None:
+            rgc.rgc_apply(w, self.sketch, self.proj, tau, seed, stats=stats, workspace=self.workspace)
+        else:
+            rgc.rgc_apply_scaled(w, self.sketch, self.proj, alpha, seed)

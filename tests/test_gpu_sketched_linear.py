@@ -1,0 +1,81 @@
+"""The sketched linear layer: forward keeps X P instead of X, backward adds
+D^T (X P) to the sketch and passes D W on, the update matches the oracle's
+(the small single-layer case: d = 256, k = 512, r = 16, 4 x 256 tokens)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from rank_randomized_gradient_amd import SketchedLinear, rgc, synth
+from parity_tools import assert_update_close, rel_frobenius
+
+pytestmark = pytest.mark.gpu
+
+bits = synth.to_numpy_bits
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    rgc.load_library()
+    return torch.device("cuda", 0)
+
+
+@pytest.mark.parametrize("mode", ["normalized", "scaled"])
+def test_sketched_linear_training_step(dev, mode):
+    d, k, r, mb, n_mb, seed = 256, 512, 16, 256, 4, 0
+    x = synth.normal_bf16((mb * n_mb, k), 1.0, seed=1000)
+    dd = synth.normal_bf16((mb * n_mb, d), 0.1, seed=1001)
+    w = synth.normal_bf16((d, k), 0.02, seed=1002)
+    layer = SketchedLinear(k, d, r, kind="qr", device=dev, weight=w.clone())
+    layer.begin_update(seed)
+    xg, dg = x.to(dev), dd.to(dev)
+    for i in range(n_mb):
+        xi = xg[i * mb:(i + 1) * mb].view(2, mb // 2, k).clone().requires_grad_(True)  # a (batch, seq, k) input
+        y = layer(xi)
+        assert y.shape == (2, mb // 2, d)
+        # the layer keeps X P (tokens x r), never X (tokens x k)
+        saved = y.grad_fn.saved_tensors
+        assert all(t.shape[-1] != k or t.shape[0] == d for t in saved)
+        assert any(tuple(t.shape) == (mb, r) for t in saved)
+        dyi = dg[i * mb:(i + 1) * mb].view(2, mb // 2, d)
+        y.backward(dyi)
+        # input gradient D W against an fp32 reference on the CPU
+        ref_dx = dyi.float().cpu().reshape(mb, d) @ w.float()
+        got_dx = xi.grad.float().cpu().reshape(mb, k)
+        assert rel_frobenius(got_dx.numpy(), ref_dx.numpy()) < 1e-2
+    assert layer.weight.grad is None
+    torch.cuda.synchronize()
+    # C and P against the oracle's loop
+    p_ref = orc.qr_projection(seed, k, r)
+    assert np.array_equal(bits(layer.proj), p_ref)
+    c_ref = np.zeros((d, r), dtype=np.float32)
+    for i in range(n_mb):
+        c_ref = orc.accumulate(c_ref, bits(dd[i * mb:(i + 1) * mb]), orc.project(bits(x[i * mb:(i + 1) * mb]), p_ref))
+    c = layer.sketch.cpu().numpy()
+    assert rel_frobenius(c, c_ref) < 2e-3
+    abs_terms = np.abs(c.astype(np.float64)) @ np.abs(orc.bf16_to_f64(p_ref)).T
+    if mode == "normalized":
+        stats = torch.zeros(4, device=dev)
+        layer.apply_update(seed, tau=1e-3, stats=stats)
+        torch.cuda.synchronize()
+        ref_w, ref_stats = orc.apply_update(bits(w), c, p_ref, 1e-3, seed)
+        s = ref_stats[2]
+        np.testing.assert_allclose(stats.cpu().numpy()[:3], ref_stats[:3], rtol=1e-5)
+    else:
+        # a step of the size the normalized update takes here (s ~ 1e-6 for this
+        # sketch): the update then moves each weight by a small fraction of itself
+        s = np.float32(2e-6)
+        layer.apply_update(seed, alpha=float(s))
+        torch.cuda.synchronize()
+        ref_w = orc.apply_scaled(bits(w), c, p_ref, s, seed)
+    assert_update_close(bits(layer.weight.data), ref_w, s, abs_terms, what=f"layer update ({mode})")
+
+
+def test_sketched_linear_requires_a_projection(dev):
+    layer = SketchedLinear(512, 256, 16, device=dev)
+    with pytest.raises(rgc.RgcError):
+        layer(torch.zeros(4, 512, dtype=torch.bfloat16, device=dev))
+    with pytest.raises(rgc.RgcError):
+        layer.apply_update(0, tau=1e-3, alpha=1e-3)
