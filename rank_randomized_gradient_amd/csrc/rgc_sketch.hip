@@ -560,25 +560,39 @@ __global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
   const int64_t left = s.next[m] - tile * tn;
   const int64_t rows = left < tn ? left : tn;
   constexpr int PER = 4;  // floats per thread
+  constexpr int MAXP = 8;  // partial loads in flight at once
   {
     const int64_t e = (int64_t)blockIdx.x * (256 * PER) + threadIdx.x * PER;
     if (e >= rows * R) return;
-    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t w = wa; w <= wb; ++w) {
-      // wa's share is its last segment when its range began in an earlier
-      // tile, else its first; every later range begins inside this tile
-      const bool first = !(w == wa && range_begin(s, wa) < ts);
-      const float4 v = *reinterpret_cast<const float4*>(fb.part + partial_slot(w, first) * tn * R + e);
-      const f32x4_t x = {v.x, v.y, v.z, v.w};
-      sum = (w == wa) ? x : sum + x;
-    }
     const int64_t out = tile * tn * R + e;
+    float4 old = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (!TO_BF16) old = *reinterpret_cast<const float4*>(fb.C[m] + out);
+    f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+    // The partials of up to MAXP ranges are loaded together, then summed in
+    // range order (the order, and so the bits, of a one-at-a-time sum).
+    for (int64_t w0 = wa; w0 <= wb; w0 += MAXP) {
+      float4 v[MAXP];
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i) {
+        const int64_t w = w0 + i;
+        // wa's share is its last segment when its range began in an earlier
+        // tile, else its first; every later range begins inside this tile
+        const bool first = !(w == wa && range_begin(s, wa) < ts);
+        v[i] = w <= wb ? *reinterpret_cast<const float4*>(fb.part + partial_slot(w, first) * tn * R + e)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < MAXP; ++i) {
+        const int64_t w = w0 + i;
+        const f32x4_t x = {v[i].x, v[i].y, v[i].z, v[i].w};
+        if (w <= wb) sum = (w == wa) ? x : sum + x;
+      }
+    }
     if constexpr (TO_BF16) {
       const uint2 o = make_uint2(pack_bf16x2(f32_to_bf16_rne(sum[0]), f32_to_bf16_rne(sum[1])),
                                  pack_bf16x2(f32_to_bf16_rne(sum[2]), f32_to_bf16_rne(sum[3])));
       *reinterpret_cast<uint2*>(fb.XP[m] + out) = o;
     } else {
-      float4 old = *reinterpret_cast<float4*>(fb.C[m] + out);
       old.x += sum[0];
       old.y += sum[1];
       old.z += sum[2];
