@@ -68,6 +68,8 @@ constexpr int kQrMaxBatch = 16;
 // fills a compute unit, so that the workgroups of a block's projections stay
 // within one round over the compute units.
 constexpr int qr_block_rows(int64_t r) { return r <= 64 ? 64 : 128; }
+// r <= 64 (multiples of 16): block steps on fp64 MFMA (qr_block_mfma_kernel).
+constexpr bool kQrBlockMfma = true;
 constexpr int kQrSub = 16;         // rows staged in LDS at a time
 constexpr double kTwoPi = 6.283185307179586;  // 2*pi rounded to double
 // When every entry of Q1^T Q1 - I is below this, Q1 (U2 = I - S, |S| below it
@@ -271,6 +273,116 @@ __global__ __launch_bounds__(256) void qr_block_kernel(QrBatch b) {
     for (int a = 0; a < TU; ++a)
 #pragma unroll
       for (int c = 0; c < TU; ++c) out[(ty + 16 * a) * R + tx + 16 * c] = acc[a][c];
+  }
+}
+
+// The same three block steps for r <= 64 on fp64 MFMA (v_mfma_f64_16x16x4_f64):
+// operands come straight from the staged rows, so the products no longer
+// wait on one LDS read per multiply-add. A 16 x 16 x 4 product takes, in lane
+// l, A[l % 16][l / 16] and B[l / 16][l % 16] and returns D[4 i + l / 16][l % 16]
+// in its register i = 0..3 (rows interleaved over the lane groups; measured
+// with a probe). Wave w owns row tile w of a multiply (the 64 staged rows are
+// four tiles of 16) and row tile w of a Gram (r / 16 <= 4 tiles).
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+template <int R, int MODE>
+__global__ __launch_bounds__(256) void qr_block_mfma_kernel(QrBatch b) {
+  static_assert(R <= 64 && R % 16 == 0, "r <= 64");
+  constexpr int BR = qr_block_rows(R);  // 64
+  constexpr int NT = R / 16;
+  constexpr int LD = R + 1;             // padded row pitch (doubles)
+  __shared__ double rows[BR][LD];
+  __shared__ double u[MODE == 0 ? 1 : R][MODE == 0 ? 1 : LD];
+  const int m = batch_item(b.block_begin, b.n, blockIdx.x);
+  const int lane = threadIdx.x & 63, wave = wave_index();
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t k = b.k[m];
+  const int64_t rbeg = (int64_t)(blockIdx.x - b.block_begin[m]) * BR;
+  const int64_t rend = rbeg + BR < k ? rbeg + BR : k;
+  if constexpr (MODE == 2) {
+    if (b.status[m][2] != 0u) return;  // P from the first pass is final
+  }
+  const double* src = MODE == 2 ? b.Q1[m] : b.A[m];
+  {
+    // every load issued before the first LDS store; rows past the end read
+    // a valid row and are zeroed
+    constexpr int NS = BR * R / 256, NU = MODE == 0 ? 0 : R * R / 256;
+    double sv[NS], uv[NU > 0 ? NU : 1];
+#pragma unroll
+    for (int e = 0; e < NS; ++e) {
+      const int t = threadIdx.x + 256 * e;
+      const int64_t row = rbeg + t / R;
+      sv[e] = src[(row < rend ? row : rend - 1) * R + t % R];
+    }
+    if constexpr (MODE != 0) {
+      const double* U = MODE == 1 ? b.U1[m] : b.U2[m];
+#pragma unroll
+      for (int e = 0; e < NU; ++e) uv[e] = U[threadIdx.x + 256 * e];
+    }
+#pragma unroll
+    for (int e = 0; e < NS; ++e) {
+      const int t = threadIdx.x + 256 * e;
+      rows[t / R][t % R] = rbeg + t / R < rend ? sv[e] : 0.0;
+    }
+    if constexpr (MODE != 0) {
+#pragma unroll
+      for (int e = 0; e < NU; ++e) {
+        const int t = threadIdx.x + 256 * e;
+        u[t / R][t % R] = uv[e];
+      }
+    }
+  }
+  __syncthreads();
+  if constexpr (MODE != 0) {
+    // Y = rows U: row tile `wave`, all column tiles
+    f64x4_t y[NT];
+#pragma unroll
+    for (int tc = 0; tc < NT; ++tc) y[tc] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int kk = 0; kk < R / 4; ++kk) {
+      const double a = rows[16 * wave + li][4 * kk + lg];
+#pragma unroll
+      for (int tc = 0; tc < NT; ++tc)
+        y[tc] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, u[4 * kk + lg][16 * tc + li], y[tc], 0, 0, 0);
+    }
+    const double scale = b.scale[m];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int lr = 16 * wave + 4 * i + lg;
+      const int64_t row = rbeg + lr;
+      if (row >= rend) continue;
+#pragma unroll
+      for (int tc = 0; tc < NT; ++tc) {
+        const int col = 16 * tc + li;
+        if constexpr (MODE == 1) b.Q1[m][row * R + col] = y[tc][i];
+        b.P[m][row * R + col] = (uint16_t)f32_to_bf16_rne((float)(scale * y[tc][i]));
+      }
+    }
+    if constexpr (MODE == 2) return;
+    __syncthreads();  // every wave is done reading the staged rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int tc = 0; tc < NT; ++tc) rows[16 * wave + 4 * i + lg][16 * tc + li] = y[tc][i];  // 0 past the end
+    __syncthreads();
+  }
+  // partial Gram of the staged rows: row tile `wave`, all column tiles
+  if (wave < NT) {
+    f64x4_t acc[NT];
+#pragma unroll
+    for (int tj = 0; tj < NT; ++tj) acc[tj] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int kk = 0; kk < BR / 4; ++kk) {
+      const double a = rows[4 * kk + lg][16 * wave + li];
+#pragma unroll
+      for (int tj = 0; tj < NT; ++tj)
+        acc[tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, rows[4 * kk + lg][16 * tj + li], acc[tj], 0, 0, 0);
+    }
+    double* out = b.part[m] + (int64_t)(blockIdx.x - b.block_begin[m]) * R * R;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int tj = 0; tj < NT; ++tj) out[(16 * wave + 4 * i + lg) * R + 16 * tj + li] = acc[tj][i];
   }
 }
 
@@ -490,14 +602,23 @@ rgc_status_t qr_launch(int n, const uint64_t* seeds, const int64_t* ks, uint16_t
     off += l.total;
   }
   hipLaunchKernelGGL((gauss_fill_kernel<R>), dim3(b.fill_begin[n]), dim3(256), 0, s, b);
-  hipLaunchKernelGGL((qr_block_kernel<R, 0>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
+  if constexpr (R <= 64 && R % 16 == 0 && kQrBlockMfma)
+    hipLaunchKernelGGL((qr_block_mfma_kernel<R, 0>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
+  else
+    hipLaunchKernelGGL((qr_block_kernel<R, 0>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   const dim3 red_grid((unsigned)((R * R + 255) / 256), (unsigned)n);
   hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
   hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(QrFactorShape<R>::THREADS), 0, s, b, G_all, 0);
-  hipLaunchKernelGGL((qr_block_kernel<R, 1>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
+  if constexpr (R <= 64 && R % 16 == 0 && kQrBlockMfma)
+    hipLaunchKernelGGL((qr_block_mfma_kernel<R, 1>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
+  else
+    hipLaunchKernelGGL((qr_block_kernel<R, 1>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
   hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(QrFactorShape<R>::THREADS), 0, s, b, G_all, 1);
-  hipLaunchKernelGGL((qr_block_kernel<R, 2>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
+  if constexpr (R <= 64 && R % 16 == 0 && kQrBlockMfma)
+    hipLaunchKernelGGL((qr_block_mfma_kernel<R, 2>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
+  else
+    hipLaunchKernelGGL((qr_block_kernel<R, 2>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
