@@ -276,7 +276,8 @@ __global__ __launch_bounds__(256) void qr_block_kernel(QrBatch b) {
   }
 }
 
-// The same three block steps for r <= 64 on fp64 MFMA (v_mfma_f64_16x16x4_f64):
+// The same three block steps for r <= 64 on fp64 MFMA (v_mfma_f64_16x16x4_f64),
+// the first one also drawing the Gaussian rows of its block (no fill launch):
 // operands come straight from the staged rows, so the products no longer
 // wait on one LDS read per multiply-add. A 16 x 16 x 4 product takes, in lane
 // l, A[l % 16][l / 16] and B[l / 16][l % 16] and returns D[4 i + l / 16][l % 16]
@@ -303,7 +304,26 @@ __global__ __launch_bounds__(256) void qr_block_mfma_kernel(QrBatch b) {
     if (b.status[m][2] != 0u) return;  // P from the first pass is final
   }
   const double* src = MODE == 2 ? b.Q1[m] : b.A[m];
-  {
+  if constexpr (MODE == 0) {
+    // The Gaussian rows are drawn here (as the fill kernel draws them: four
+    // columns per Philox call) into LDS and into A for the first multiply.
+    constexpr int NQ = BR * (R / 4) / 256;
+#pragma unroll
+    for (int e = 0; e < NQ; ++e) {
+      const int t = threadIdx.x + 256 * e;
+      const int lr = t / (R / 4), q = t % (R / 4);
+      const int64_t row = rbeg + lr;
+      double z[4] = {0.0, 0.0, 0.0, 0.0};
+      if (row < rend) {
+        gaussian4(b.seed[m], row, q, z);
+        double* dst = b.A[m] + row * R + 4 * q;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) dst[x] = z[x];
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) rows[lr][4 * q + x] = z[x];
+    }
+  } else {
     // every load issued before the first LDS store; rows past the end read
     // a valid row and are zeroed
     constexpr int NS = BR * R / 256, NU = MODE == 0 ? 0 : R * R / 256;
@@ -601,7 +621,9 @@ rgc_status_t qr_launch(int n, const uint64_t* seeds, const int64_t* ks, uint16_t
     b.block_begin[m + 1] = b.block_begin[m] + l.blocks;
     off += l.total;
   }
-  hipLaunchKernelGGL((gauss_fill_kernel<R>), dim3(b.fill_begin[n]), dim3(256), 0, s, b);
+  // (r <= 64: the first block step draws the Gaussian itself)
+  if constexpr (!(R <= 64 && R % 16 == 0 && kQrBlockMfma))
+    hipLaunchKernelGGL((gauss_fill_kernel<R>), dim3(b.fill_begin[n]), dim3(256), 0, s, b);
   if constexpr (R <= 64 && R % 16 == 0 && kQrBlockMfma)
     hipLaunchKernelGGL((qr_block_mfma_kernel<R, 0>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   else
