@@ -32,8 +32,29 @@ BLOCK_1P7B = [  # name, d (out), k (in), input activation
     ("o", 2048, 2048, "attn_out"), ("gate", 6144, 2048, "mlp_in"), ("up", 6144, 2048, "mlp_in"),
     ("down", 2048, 6144, "mlp_act"),
 ]
-WORKLOAD = {"name": "qwen3-1.7b-block", "matrices": BLOCK_1P7B, "r": 64, "kind": "qr", "tokens": 32768,
-            "microbatch": 4096, "tau": 1e-3}
+LAYER_8B = [  # one layer of the Qwen3-8B-shaped projection set
+    ("q", 4096, 4096, "attn_in"), ("k", 1024, 4096, "attn_in"), ("v", 1024, 4096, "attn_in"),
+    ("o", 4096, 4096, "attn_out"), ("gate", 12288, 4096, "mlp_in"), ("up", 12288, 4096, "mlp_in"),
+    ("down", 4096, 12288, "mlp_act"),
+]
+# The default is the bench line; the others measure the remaining workload shapes (same fields, their own name).
+#   refresh: a new projection every step (QR, drawn inside the timed step); else drawn once (fixed Rademacher)
+#   x_dist:  "normal" or "t4" (Student-t with 4 degrees of freedom scaled to unit variance)
+WORKLOADS = {
+    "qwen3-1.7b-block": {"desc": "qwen3-1.7b-block 7 projections, r=64 QR, 32768 tokens in 8x4096",
+                         "matrices": BLOCK_1P7B, "r": 64, "kind": "qr", "refresh": True, "tokens": 32768,
+                         "microbatch": 4096, "tau": 1e-3, "x_dist": "normal"},
+    "qwen3-1.7b-block-r256": {"desc": "qwen3-1.7b-block 7 projections, r=256 fixed Rademacher, 65536 tokens in 16x4096",
+                              "matrices": BLOCK_1P7B, "r": 256, "kind": "rademacher", "refresh": False,
+                              "tokens": 65536, "microbatch": 4096, "tau": 1e-3, "x_dist": "normal"},
+    "square-4096": {"desc": "square layer 4096x4096, r=64 QR new per update, 131072 tokens in 32x4096",
+                    "matrices": [("w", 4096, 4096, "x")], "r": 64, "kind": "qr", "refresh": True, "tokens": 131072,
+                    "microbatch": 4096, "tau": 1e-3, "x_dist": "t4"},
+    "qwen3-8b-layer": {"desc": "one qwen3-8b-shaped layer (7 projections), r=128 QR, 32768 tokens in 8x4096",
+                       "matrices": LAYER_8B, "r": 128, "kind": "qr", "refresh": True, "tokens": 32768,
+                       "microbatch": 4096, "tau": 1e-3, "x_dist": "normal"},
+}
+WORKLOAD = WORKLOADS["qwen3-1.7b-block"]
 
 
 def parse():
@@ -41,6 +62,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3-1.7b-block", choices=sorted(WORKLOADS),
+                    help="the bench line is the default; the others measure the remaining workload shapes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -104,7 +127,8 @@ def main():
     rgc.load_library()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    wl = WORKLOAD
+    wl = WORKLOADS[args.workload]
+    default_wl = args.workload == "qwen3-1.7b-block"
     r, T, mb = wl["r"], wl["tokens"], wl["microbatch"]
     n_mb = T // mb
     mats = wl["matrices"]
@@ -116,8 +140,16 @@ def main():
     def normal(shape, std):
         return (torch.randn(*shape, generator=g, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
 
-    acts = {"attn_in": 2048, "attn_out": 2048, "mlp_in": 2048, "mlp_act": 6144}
-    X = {name: normal((T, width), 1.0) for name, width in acts.items()}
+    def t4(shape):
+        # Student-t, 4 degrees of freedom: Z / sqrt(chi2_4 / 4), scaled by 1/sqrt(2) to unit variance
+        z = torch.randn(*shape, generator=g, device=dev)
+        chi2 = sum(torch.randn(*shape, generator=g, device=dev) ** 2 for _ in range(4))
+        return (z / torch.sqrt(chi2 / 4) / 2 ** 0.5).to(torch.bfloat16)
+
+    acts = {}
+    for _, _, k, src in mats:
+        acts[src] = k
+    X = {name: (t4((T, width)) if wl["x_dist"] == "t4" else normal((T, width), 1.0)) for name, width in acts.items()}
     D = [normal((T, d), 1e-3) for _, d, _, _ in mats]
     W = [normal((d, k), 0.02) for _, d, k, _ in mats]
     P = [torch.empty((k, r), dtype=torch.bfloat16, device=dev) for _, _, k, _ in mats]
@@ -135,6 +167,9 @@ def main():
         # all projections of the block in one batched call (same bits as one call per matrix)
         rgc.rgc_sample_projections(wl["kind"], [step_seed(step, m) for m in range(len(mats))], P, workspace=ws)
 
+    if not wl["refresh"]:
+        sample_all(0)  # a fixed projection, drawn once
+
     def project_mb(i):
         # the 7 projections of microbatch i in one launch (q/k/v and gate/up share their X)
         rgc.rgc_project_batch([X[src][i * mb:(i + 1) * mb] for _, _, _, src in mats], P, outs=XP, workspace=ws)
@@ -147,7 +182,8 @@ def main():
         rgc.rgc_apply_batch(W, C, P, wl["tau"], [step_seed(step, m) for m in range(len(mats))], workspace=ws)
 
     def one_step(step):
-        sample_all(step)
+        if wl["refresh"]:
+            sample_all(step)
         c_all.zero_()
         for i in range(n_mb):
             project_mb(i)
@@ -210,7 +246,8 @@ def main():
             "apply": {"s_per_step": per_step["apply"], "launches_per_step": 1,
                       "avg_us": 1e6 * per_step["apply"],
                       "GBs": app_bytes / per_step["apply"] / 1e9},
-            "sample_projection": {"s_per_step": per_step["sample_projection"], "launches_per_step": 1,
+            "sample_projection": {"s_per_step": per_step["sample_projection"],
+                                  "launches_per_step": 1 if wl["refresh"] else 0,
                                   "avg_us": 1e6 * per_step["sample_projection"],
                                   "GBs": smp_bytes / per_step["sample_projection"] / 1e9},
         }
@@ -223,9 +260,10 @@ def main():
     roofline = None
     if kern:
         a = kern["accumulate"]
-        roofline = {"kernel": "rgc_accumulate_batch (accumulate_kernel<64> + finish_tiles_kernel<64,false>)",
+        roofline = {"kernel": f"rgc_accumulate_batch (accumulate_kernel<{r}> + finish_tiles_kernel<{r},false>)",
                     "bound": "hbm", "achieved": round(a["GBs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(a["hbm_frac"], 4), "traffic": recorded_traffic(),
+                    "frac": round(a["hbm_frac"], 4),
+                    "traffic": recorded_traffic() if default_wl else None,
                     "algorithmic_bytes_per_launch": acc_bytes // n_mb}
 
     if args.copy_mib > 0:
@@ -236,7 +274,7 @@ def main():
         torch.cuda.synchronize()
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and default_wl:
         cpu = cpu_baseline(X, D, W, mats, wl)
 
     out = {
@@ -252,8 +290,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "qwen3-1.7b-block 7 projections, r=64 QR, 32768 tokens in 8x4096",
-                   "r": r, "tokens_per_step": T, "microbatch": mb, "projection": "qr-gaussian", "tau": wl["tau"]},
+        "config": {"workload": wl["desc"], "r": r, "tokens_per_step": T, "microbatch": mb,
+                   "projection": "qr-gaussian" if wl["kind"] == "qr" else "rademacher, fixed", "tau": wl["tau"]},
         "sketch_accumulate_TFLOPs": round(kern["accumulate"]["TFLOPs"], 2) if kern else None,
         "sketch_accumulate_frac_bf16_peak": round(kern["accumulate"]["mfma_frac"], 4) if kern else None,
         "fused_apply_GBs": round(kern["apply"]["GBs"], 1) if kern else None,

@@ -132,10 +132,18 @@ __device__ __forceinline__ int64_t partial_slot(int64_t w, bool first_segment) {
 // 4kq+3: four K slots of the A operand.
 // ---------------------------------------------------------------------------
 constexpr int kStages = 6;
+constexpr int kWavesR256 = 2;  // waves along r at r = 256
+constexpr int kWavesR128 = 1;  // waves along r at r = 128
 
+// Waves along r: r <= 64 and r = 128 one (the N tile is 256 wide; at r = 128
+// each wave holds 128 ranks, 8 M-tiles); r = 256 two, each again with 128
+// ranks, so that the N tile is 128 wide and the rank operand is re-read half
+// as often as with four waves of 64 ranks; r = 192 four. (Measured on the
+// 1.7B block at r = 256 and the 8B layer at r = 128 against the previous
+// split, which gave every wave at most 64 ranks.)
 template <int R, int KH>
 struct StageShape {
-  static constexpr int WR = R <= 64 ? 1 : (R == 128 ? 2 : 4);  // waves along r
+  static constexpr int WR = R <= 64 ? 1 : (R == 128 ? kWavesR128 : (R == 256 ? kWavesR256 : 4));
   static constexpr int WN = 4 / WR;                              // waves along N
   static constexpr int RW = R / WR;                              // r per wave
   static constexpr int MT = RW / 16;                             // MFMA M-tiles per wave
@@ -149,7 +157,7 @@ struct StageShape {
   static constexpr int STAGE = 1024 * NI;
   static constexpr int S = kStages * STAGE <= 160 * 1024 ? kStages : 160 * 1024 / STAGE;
   static constexpr int NV_LO = NI / 4, NV_HI = (NI + 3) / 4;  // copies per wave (waves below NI % 4 take one more)
-  static_assert(RW % 16 == 0 && RW <= 64, "rank split");
+  static_assert(RW % 16 == 0 && RW <= 128, "rank split");
   static_assert(S >= 3 && S * STAGE <= 160 * 1024, "LDS");
   static_assert((S - 1) * NV_HI <= 63, "vector memory counter");
 };
@@ -254,8 +262,11 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
   // range's last segment: a store issued while copies are in flight counts
   // in the same counter as the copies, so the next wait would drain the
   // whole pipeline. Later segments (each a whole tile or the range's last
-  // piece) are stored as they finish.
-  f32x4_t keep[MT][4];
+  // piece) are stored as they finish. With 8 M-tiles per wave (r = 256 on
+  // two waves along r) the accumulate has no room for a second set of sums
+  // (it spilled), so there its first segment is stored as it finishes too.
+  constexpr bool KEEP_FIRST = MT <= 4 || Policy::kKeepLargeFirst;
+  f32x4_t keep[KEEP_FIRST ? MT : 1][4];
   bool kept = false, kept_full = false;
   int64_t kept_tile = tile0;
 
@@ -323,11 +334,13 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
       }
     }
     const bool first_seg = seg_kb0 == k0 && ctile == tile0 && cm == m0;
-    if (first_seg && u < u1) {
+    if (KEEP_FIRST && first_seg && u < u1) {
+      if constexpr (KEEP_FIRST) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) keep[mt][nt] = acc[mt][nt];
+          for (int nt = 0; nt < 4; ++nt) keep[mt][nt] = acc[mt][nt];
+      }
       kept = true;
       kept_full = seg_kb0 == 0 && tile_end;
       kept_tile = ctile;
@@ -342,7 +355,9 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
       }
     }
   }
-  if (kept) pol.store(keep, m0, kept_tile, kept_full, partial_slot(w, true), wn, rw, g, li);
+  if constexpr (KEEP_FIRST) {
+    if (kept) pol.store(keep, m0, kept_tile, kept_full, partial_slot(w, true), wn, rw, g, li);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -370,6 +385,7 @@ struct ProjectBatch {
 template <int R>
 struct ProjectPolicy {
   using Sh = StageShape<R, kProjectKH>;
+  static constexpr bool kKeepLargeFirst = true;
   const ProjectBatch& pb;
   int64_t ldx = 0, T = 0;  // of the copy cursor's item
   __device__ void enter_item(int m) {
@@ -465,6 +481,7 @@ struct AccumulateBatch {
 template <int R>
 struct AccumulatePolicy {
   using Sh = StageShape<R, 1>;
+  static constexpr bool kKeepLargeFirst = false;
   const AccumulateBatch& ab;
   int64_t ldd = 0, d = 0;  // of the copy cursor's item
   __device__ void enter_item(int m) {
