@@ -63,13 +63,14 @@ __global__ void rademacher_kernel(uint16_t* __restrict__ P, int64_t k, int r, ui
 // CholeskyQR2, batched over up to kQrMaxBatch matrices of one rank R <= 128.
 // ---------------------------------------------------------------------------
 constexpr int kQrMaxBatch = 16;
-// Rows per Gram / multiply workgroup: 64 up to r = 64 (two workgroups fit a
-// compute unit); 128 at r = 128, where a workgroup's LDS (U alone is 128 KB)
-// fills a compute unit, so that the workgroups of a block's projections stay
-// within one round over the compute units.
-constexpr int qr_block_rows(int64_t r) { return r <= 64 ? 64 : 128; }
-// r <= 64 (multiples of 16): block steps on fp64 MFMA (qr_block_mfma_kernel).
 constexpr bool kQrBlockMfma = true;
+// Rows per Gram / multiply workgroup: 64 (the MFMA block steps stage only
+// U's upper tiles, so r = 128 fits 64 staged rows beside them; the VALU
+// steps, kept for kQrBlockMfma = false, stage all of U and take 128 rows at
+// r = 128 so that a block's workgroups stay within one round).
+constexpr int qr_block_rows(int64_t r) { return kQrBlockMfma || r <= 64 ? 64 : 128; }
+// r a multiple of 16 (every QR rank): block steps on fp64 MFMA (qr_block_mfma_kernel).
+
 constexpr int kQrSub = 16;         // rows staged in LDS at a time
 constexpr double kTwoPi = 6.283185307179586;  // 2*pi rounded to double
 // When every entry of Q1^T Q1 - I is below this, Q1 (U2 = I - S, |S| below it
@@ -276,24 +277,32 @@ __global__ __launch_bounds__(256) void qr_block_kernel(QrBatch b) {
   }
 }
 
-// The same three block steps for r <= 64 on fp64 MFMA (v_mfma_f64_16x16x4_f64),
+// The same three block steps on fp64 MFMA (v_mfma_f64_16x16x4_f64),
 // the first one also drawing the Gaussian rows of its block (no fill launch):
 // operands come straight from the staged rows, so the products no longer
 // wait on one LDS read per multiply-add. A 16 x 16 x 4 product takes, in lane
 // l, A[l % 16][l / 16] and B[l / 16][l % 16] and returns D[4 i + l / 16][l % 16]
 // in its register i = 0..3 (rows interleaved over the lane groups; measured
 // with a probe). Wave w owns row tile w of a multiply (the 64 staged rows are
-// four tiles of 16) and row tile w of a Gram (r / 16 <= 4 tiles).
+// four tiles of 16) and row tiles w, w + 4 of a Gram. U is upper triangular:
+// only its 16 x 16 tiles on and above the diagonal are staged (tile (rt, tc),
+// rt <= tc, at slot tc (tc + 1) / 2 + rt, rows padded to 17), which is what
+// lets r = 128 stage U beside the rows, and the multiply skips the zero tiles.
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kUTilePitch = 17;                     // doubles per staged U tile row
+constexpr int kUTileSize = 16 * kUTilePitch;        // doubles per staged U tile
+__host__ __device__ constexpr int utile_slot(int rt, int tc) { return tc * (tc + 1) / 2 + rt; }
 
 template <int R, int MODE>
 __global__ __launch_bounds__(256) void qr_block_mfma_kernel(QrBatch b) {
-  static_assert(R <= 64 && R % 16 == 0, "r <= 64");
+  static_assert(R <= 128 && R % 16 == 0, "r <= 128, multiple of 16");
   constexpr int BR = qr_block_rows(R);  // 64
+  static_assert(BR == 64, "four row tiles, one per wave");
   constexpr int NT = R / 16;
   constexpr int LD = R + 1;             // padded row pitch (doubles)
   __shared__ double rows[BR][LD];
-  __shared__ double u[MODE == 0 ? 1 : R][MODE == 0 ? 1 : LD];
+  __shared__ double u[MODE == 0 ? 1 : NT * (NT + 1) / 2 * kUTileSize];
   const int m = batch_item(b.block_begin, b.n, blockIdx.x);
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int li = lane & 15, lg = lane >> 4;
@@ -348,7 +357,8 @@ __global__ __launch_bounds__(256) void qr_block_mfma_kernel(QrBatch b) {
 #pragma unroll
       for (int e = 0; e < NU; ++e) {
         const int t = threadIdx.x + 256 * e;
-        u[t / R][t % R] = uv[e];
+        const int a = t / R, c = t % R;
+        if (a / 16 <= c / 16) u[utile_slot(a / 16, c / 16) * kUTileSize + (a % 16) * kUTilePitch + c % 16] = uv[e];
       }
     }
   }
@@ -361,9 +371,12 @@ __global__ __launch_bounds__(256) void qr_block_mfma_kernel(QrBatch b) {
 #pragma unroll
     for (int kk = 0; kk < R / 4; ++kk) {
       const double a = rows[16 * wave + li][4 * kk + lg];
+      const int rt = kk / 4;  // U's row tile; tiles left of the diagonal are zero
 #pragma unroll
       for (int tc = 0; tc < NT; ++tc)
-        y[tc] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, u[4 * kk + lg][16 * tc + li], y[tc], 0, 0, 0);
+        if (tc >= rt)
+          y[tc] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+              a, u[utile_slot(rt, tc) * kUTileSize + (4 * kk + lg - 16 * rt) * kUTilePitch + li], y[tc], 0, 0, 0);
     }
     const double scale = b.scale[m];
 #pragma unroll
@@ -386,14 +399,17 @@ __global__ __launch_bounds__(256) void qr_block_mfma_kernel(QrBatch b) {
       for (int tc = 0; tc < NT; ++tc) rows[16 * wave + 4 * i + lg][16 * tc + li] = y[tc][i];  // 0 past the end
     __syncthreads();
   }
-  // partial Gram of the staged rows: row tile `wave`, all column tiles
-  if (wave < NT) {
+  // partial Gram of the staged rows: row tiles wave, wave + 4, all column tiles
+#pragma unroll
+  for (int pass = 0; pass < (NT + 3) / 4; ++pass) {
+    const int ti = wave + 4 * pass;
+    if (ti >= NT) break;
     f64x4_t acc[NT];
 #pragma unroll
     for (int tj = 0; tj < NT; ++tj) acc[tj] = f64x4_t{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int kk = 0; kk < BR / 4; ++kk) {
-      const double a = rows[4 * kk + lg][16 * wave + li];
+      const double a = rows[4 * kk + lg][16 * ti + li];
 #pragma unroll
       for (int tj = 0; tj < NT; ++tj)
         acc[tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, rows[4 * kk + lg][16 * tj + li], acc[tj], 0, 0, 0);
@@ -402,7 +418,7 @@ __global__ __launch_bounds__(256) void qr_block_mfma_kernel(QrBatch b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int tj = 0; tj < NT; ++tj) out[(16 * wave + 4 * i + lg) * R + 16 * tj + li] = acc[tj][i];
+      for (int tj = 0; tj < NT; ++tj) out[(16 * ti + 4 * i + lg) * R + 16 * tj + li] = acc[tj][i];
   }
 }
 
@@ -622,22 +638,22 @@ rgc_status_t qr_launch(int n, const uint64_t* seeds, const int64_t* ks, uint16_t
     off += l.total;
   }
   // (r <= 64: the first block step draws the Gaussian itself)
-  if constexpr (!(R <= 64 && R % 16 == 0 && kQrBlockMfma))
+  if constexpr (!(R % 16 == 0 && kQrBlockMfma))
     hipLaunchKernelGGL((gauss_fill_kernel<R>), dim3(b.fill_begin[n]), dim3(256), 0, s, b);
-  if constexpr (R <= 64 && R % 16 == 0 && kQrBlockMfma)
+  if constexpr (R % 16 == 0 && kQrBlockMfma)
     hipLaunchKernelGGL((qr_block_mfma_kernel<R, 0>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   else
     hipLaunchKernelGGL((qr_block_kernel<R, 0>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   const dim3 red_grid((unsigned)((R * R + 255) / 256), (unsigned)n);
   hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
   hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(QrFactorShape<R>::THREADS), 0, s, b, G_all, 0);
-  if constexpr (R <= 64 && R % 16 == 0 && kQrBlockMfma)
+  if constexpr (R % 16 == 0 && kQrBlockMfma)
     hipLaunchKernelGGL((qr_block_mfma_kernel<R, 1>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   else
     hipLaunchKernelGGL((qr_block_kernel<R, 1>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
   hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(QrFactorShape<R>::THREADS), 0, s, b, G_all, 1);
-  if constexpr (R <= 64 && R % 16 == 0 && kQrBlockMfma)
+  if constexpr (R % 16 == 0 && kQrBlockMfma)
     hipLaunchKernelGGL((qr_block_mfma_kernel<R, 2>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   else
     hipLaunchKernelGGL((qr_block_kernel<R, 2>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
