@@ -11,15 +11,15 @@
 // (the result does not depend on the tile shape).
 //
 // One batch (e.g. all projections of a block) takes three launches:
-//   norms:  sum w^2 over W, and ||H||^2. For r <= 64, ||H||_F^2 =
+//   norms:  sum w^2 over W, and ||H||^2. For r <= 128, ||H||_F^2 =
 //           tr((C^T C)(P^T P)) (the Frobenius norm of a product through
 //           the two r x r Gram matrices), so W is only streamed and squared
 //           while a few workgroups per matrix form partial Gram matrices of
-//           C and of P. For r > 64 the Gram partials would be too large to
-//           reduce in one workgroup; there every workgroup streams its share
-//           of W and rebuilds the same H tiles as the update. Either way the
-//           partials are fp64 (Gram partials fp32) with fixed-order
-//           reductions across lanes and waves;
+//           C and of P. For r > 128 the Gram partials (136 block pairs)
+//           would not fit a workgroup's registers; there every workgroup
+//           streams its share of W and rebuilds the same H tiles as the
+//           update. Either way the partials are fp64 (Gram partials fp32)
+//           with fixed-order reductions across lanes and waves;
 //   scale:  one workgroup per matrix sums that matrix's partials in a fixed
 //           order and forms s = fp32(tau ||W|| / ||H||), or the skip flag when
 //           ||H|| is zero or not finite or s is not finite;
@@ -76,7 +76,7 @@ struct ApplyBatch {
   int fixed;  // 1: fixed-scale update (s = it.alpha, no norms, never skipped)
   float tau;
   int wbase[kApplyMaxItems + 1];  // update (and rebuild-norms) workgroups [wbase[m], wbase[m+1]) serve item m
-  // Gram-form norms launch (r <= 64): Gram workgroups [gbase[m], gbase[m+1])
+  // Gram-form norms launch (r <= 128): Gram workgroups [gbase[m], gbase[m+1])
   // (the first ncg[m] over rows of C, the rest over rows of P), then W-stream
   // workgroups gbase[n] + [sbase[m], sbase[m+1]).
   int gbase[kApplyMaxItems + 1];
@@ -99,7 +99,7 @@ __device__ __forceinline__ int apply_item_of(const ApplyBatch& b, int w) {
 
 // Ranks whose norms take the Gram form (below).
 template <int R>
-constexpr bool kGramNorms = R <= 64;
+constexpr bool kGramNorms = R <= 128;
 
 template <int R>
 struct GramShape {
@@ -112,7 +112,7 @@ struct GramShape {
   static constexpr int STEPS = 4;
   static constexpr int64_t ROWS = (int64_t)STEPS * 32 * kApplyWaves;
 };
-constexpr int kGramMaxPairs = 10;  // NP at r = 64
+constexpr int kGramMaxPairs = 36;  // NP at r = 128
 
 // s = fp32(tau * ||W|| / ||H||) from the squared norms; flag = 1 (and s = 0)
 // when ||H|| is zero or not finite or s is not finite. stats (if not null)
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
 }
 
 // ---------------------------------------------------------------------------
-// Gram-form norms (r <= 64).
+// Gram-form norms (r <= 128).
 //
 // ||H||_F^2 = ||C P^T||_F^2 = tr(P C^T C P^T) = sum_ab (C^T C)_ab (P^T P)_ab.
 // C^T C is formed from C's bf16 high parts and remainders with all four
@@ -536,7 +536,11 @@ __device__ __forceinline__ void load_gram_rows(const float* __restrict__ src, in
     const int64_t row = base + 8 * g + e;
     const float* p = src + row * (16 * NB) + NB * x;
     if (row < row1) {
-      if constexpr (NB == 4) {
+      if constexpr (NB == 8) {
+        const uint4 a = *reinterpret_cast<const uint4*>(p), c = *reinterpret_cast<const uint4*>(p + 4);
+        o.v[e][0] = a.x; o.v[e][1] = a.y; o.v[e][2] = a.z; o.v[e][3] = a.w;
+        o.v[e][4] = c.x; o.v[e][5] = c.y; o.v[e][6] = c.z; o.v[e][7] = c.w;
+      } else if constexpr (NB == 4) {
         const uint4 a = *reinterpret_cast<const uint4*>(p);
         o.v[e][0] = a.x; o.v[e][1] = a.y; o.v[e][2] = a.z; o.v[e][3] = a.w;
       } else if constexpr (NB == 2) {
@@ -561,7 +565,11 @@ __device__ __forceinline__ void load_gram_rows(const uint16_t* __restrict__ src,
     const int64_t row = base + 8 * g + e;
     const uint16_t* p = src + row * (16 * NB) + NB * x;
     if (row < row1) {
-      if constexpr (NB == 4) {
+      if constexpr (NB == 8) {
+        const uint4 a = *reinterpret_cast<const uint4*>(p);
+        o.v[e][0] = a.x & 0xFFFFu; o.v[e][1] = a.x >> 16; o.v[e][2] = a.y & 0xFFFFu; o.v[e][3] = a.y >> 16;
+        o.v[e][4] = a.z & 0xFFFFu; o.v[e][5] = a.z >> 16; o.v[e][6] = a.w & 0xFFFFu; o.v[e][7] = a.w >> 16;
+      } else if constexpr (NB == 4) {
         const uint2 a = *reinterpret_cast<const uint2*>(p);
         o.v[e][0] = a.x & 0xFFFFu; o.v[e][1] = a.x >> 16; o.v[e][2] = a.y & 0xFFFFu; o.v[e][3] = a.y >> 16;
       } else if constexpr (NB == 2) {
@@ -637,13 +645,21 @@ __device__ void gram_partial(const T* __restrict__ src, int64_t row0, int64_t ro
     gram_step<NB, TWO_TERM>(cur, acc);
     if (st + 1 < Gs::STEPS) cur = nxt;
   }
+  // waves add their sums into one slab in wave order: ((w0 + w1) + w2) + w3
 #pragma unroll
-  for (int q = 0; q < NP; ++q)
+  for (int w = 0; w < kApplyWaves; ++w) {
+    if (wave == w) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) red[(wave * NP + q) * 256 + 64 * j + lane] = acc[q][j];
-  __syncthreads();
-  for (int e = threadIdx.x; e < NE; e += 256)
-    out[e] = ((red[e] + red[NE + e]) + red[2 * NE + e]) + red[3 * NE + e];
+      for (int q = 0; q < NP; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float* e = red + q * 256 + 64 * j + lane;
+          *e = w == 0 ? acc[q][j] : *e + acc[q][j];
+        }
+    }
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < NE; e += 256) out[e] = red[e];
 }
 
 // Sum of squares of the 16-byte chunks [c0, c1) of W (row-major d x k, row
@@ -696,11 +712,11 @@ __device__ __forceinline__ int item_of(const int* base, int n, int w) {
   return m;
 }
 
-// The norms launch for r <= 64: Gram workgroups first, then W-stream ones.
+// The norms launch for r <= 128: Gram workgroups first, then W-stream ones.
 template <int R>
 __global__ __launch_bounds__(256) void gram_norms_kernel(ApplyBatch b) {
   using Gs = GramShape<R>;
-  __shared__ __attribute__((aligned(16))) float red[4 * Gs::NE];
+  __shared__ __attribute__((aligned(16))) float red[Gs::NE];
   const int w = blockIdx.x;
   const int ng = b.gbase[b.n];
   if (w < ng) {
