@@ -158,14 +158,14 @@ rgc_status_t rgc_accumulate_batch(int64_t n, const uint16_t* const* Ds, const in
 
 /* ---- 4. Normalized update with stochastic rounding ------------------------ */
 
-/* Workspace bytes rgc_apply needs (per-workgroup norm partials, for r <= 64
+/* Workspace bytes rgc_apply needs (per-workgroup norm partials, for r <= 128
  * also partial Gram matrices, and the step scalar). */
 size_t rgc_apply_workspace_size(int64_t d, int64_t k, int64_t r);
 
 /* W <- SR_bf16(W - s * H), H = C P^T, s = fp32(tau * ||W||_F / ||H||_F)
  * [RGC, "How it works"]. W: d x k bf16 (row stride ldw >= k), updated in place;
  * C: d x r fp32; P: k x r bf16. H is rebuilt tile by tile in registers (MFMA,
- * C split into two bf16 terms) and never written to memory. For r <= 64,
+ * C split into two bf16 terms) and never written to memory. For r <= 128,
  * ||H||_F^2 is taken as sum((C^T C) o (P^T P)) (equal to it up to rounding);
  * a C whose squares overflow fp32 then reads as a non-finite ||H||. The pre-rounding
  * value is v = fp32(w - fp32(s*h)) (no fused multiply-add); stochastic
