@@ -163,32 +163,66 @@ def main():
     ws = rgc.Workspace(dev)
     torch.cuda.synchronize()
 
-    def sample_all(step):
+    # The projections of step s depend only on their seeds, so they are drawn one
+    # step ahead on a second stream (default priority), overlapping step s - 1;
+    # two sets of P buffers, ordered by events. Every timed step still draws
+    # exactly one set (the first timed step's set is drawn during the warm-up).
+    s_main = torch.cuda.current_stream(dev)
+    s_side = torch.cuda.Stream(device=dev)
+    ws_side = rgc.Workspace(dev)
+    Pb = [P, [torch.empty_like(p) for p in P]]
+    ev_ready, ev_free = [None, None], [None, None]
+
+    def sample_all(step, Ps=None, workspace=None):
         # all projections of the block in one batched call (same bits as one call per matrix)
-        rgc.rgc_sample_projections(wl["kind"], [step_seed(step, m) for m in range(len(mats))], P, workspace=ws)
+        rgc.rgc_sample_projections(wl["kind"], [step_seed(step, m) for m in range(len(mats))],
+                                   Ps if Ps is not None else P, workspace=workspace or ws)
+
+    def draw_ahead(step):
+        buf = step % 2
+        with torch.cuda.stream(s_side):
+            if ev_free[buf] is not None:
+                s_side.wait_event(ev_free[buf])  # the step that last read this set is done
+            sample_all(step, Pb[buf], ws_side)
+            ev = torch.cuda.Event()
+            ev.record(s_side)
+            ev_ready[buf] = ev
 
     if not wl["refresh"]:
         sample_all(0)  # a fixed projection, drawn once
 
-    def project_mb(i):
+    def project_mb(i, Ps=None):
         # the 7 projections of microbatch i in one launch (q/k/v and gate/up share their X)
-        rgc.rgc_project_batch([X[src][i * mb:(i + 1) * mb] for _, _, _, src in mats], P, outs=XP, workspace=ws)
+        rgc.rgc_project_batch([X[src][i * mb:(i + 1) * mb] for _, _, _, src in mats], Ps if Ps is not None else P,
+                              outs=XP, workspace=ws)
 
     def accumulate_mb(i):
         rgc.rgc_accumulate_batch([D[m][i * mb:(i + 1) * mb] for m in range(len(mats))], XP, C, workspace=ws)
 
-    def apply_all(step):
+    def apply_all(step, Ps=None):
         # the 7 updates in one batched call (norms sweep, step scalars, update sweep)
-        rgc.rgc_apply_batch(W, C, P, wl["tau"], [step_seed(step, m) for m in range(len(mats))], workspace=ws)
+        rgc.rgc_apply_batch(W, C, Ps if Ps is not None else P, wl["tau"],
+                            [step_seed(step, m) for m in range(len(mats))], workspace=ws)
 
     def one_step(step):
+        Ps = P
         if wl["refresh"]:
-            sample_all(step)
+            buf = step % 2
+            if ev_ready[buf] is None:
+                draw_ahead(step)
+            s_main.wait_event(ev_ready[buf])
+            ev_ready[buf] = None
+            draw_ahead(step + 1)
+            Ps = Pb[buf]
         c_all.zero_()
         for i in range(n_mb):
-            project_mb(i)
+            project_mb(i, Ps)
             accumulate_mb(i)
-        apply_all(step)
+        apply_all(step, Ps)
+        if wl["refresh"]:
+            ev = torch.cuda.Event()
+            ev.record(s_main)
+            ev_free[step % 2] = ev
 
     for s in range(args.warmup):
         one_step(s)
@@ -200,6 +234,7 @@ def main():
     start.record()
     for s in range(args.steps):
         one_step(args.warmup + s)
+    torch.cuda.current_stream(dev).wait_stream(s_side)  # the last draw ends inside the timed region
     end.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
