@@ -7,7 +7,7 @@
 // on MFMA (M = columns of W from rows of P, N = rows of W from rows of C,
 // K = r), with C split into a bf16 high part and a bf16 remainder so that H
 // carries ~16 bits of C's mantissa. The page rebuilds H 128 rows at a time;
-// here a workgroup rebuilds 128 rows (64 for r > 64) x 64 columns per step
+// here a workgroup rebuilds 128 rows (64 at r = 128) x 64 columns per step
 // (the result does not depend on the tile shape).
 //
 // One batch (e.g. all projections of a block) takes three launches:
@@ -50,7 +50,11 @@ constexpr int64_t kMaxApplyElems = int64_t(1) << 38;  // d * k (workgroup counts
 template <int R>
 struct ApplyTraits {
   static constexpr int KQ = (R + 31) / 32;              // K-steps of 32 over r
-  static constexpr int NTW = R <= 64 ? 2 : 1;           // 16-row N-tiles per wave
+  // 16-row N-tiles per wave: two (128-row tiles) except at r = 128, whose
+  // 128-row stage would leave one workgroup per compute unit; at r > 128 that
+  // is the case anyway, and the taller tile halves the P rows re-read per W
+  // byte (measured on the Qwen3-1.7B-shaped block at r = 256: 253 -> 205 us)
+  static constexpr int NTW = R == 128 ? 1 : 2;
   static constexpr int RW = 16 * NTW;                   // rows per wave
   static constexpr int ROWS = kApplyWaves * RW;         // rows per workgroup tile
   static constexpr int RP = 32 * KQ + 8;                // LDS row pitch of the P tile (bf16)
