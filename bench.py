@@ -240,6 +240,21 @@ def main():
     ms_per_step = start.elapsed_time(end) / args.steps
     tokens_per_s = T / (ms_per_step / 1e3)
 
+    # the spread of single steps (a second pass, an event pair around each step)
+    single = []
+    for s in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        one_step(args.warmup + args.steps + s)
+        torch.cuda.current_stream(dev).wait_stream(s_side)
+        b.record()
+        torch.cuda.synchronize()
+        single.append(a.elapsed_time(b))
+    single.sort()
+    step_spread = {"min": round(single[0], 4), "median": round(single[len(single) // 2], 4),
+                   "max": round(single[-1], 4)}
+
     # ---- per-entry-point timing ---------------------------------------------------
     # HIP events on the launch stream around K repetitions of one step's calls of
     # a single entry point, issued back to back (an event pair around every
@@ -320,6 +335,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "single_step_ms": step_spread,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
