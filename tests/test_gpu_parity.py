@@ -270,7 +270,9 @@ def test_sketch_is_deterministic(dev):
 # Update
 # ---------------------------------------------------------------------------
 APPLY_CASES = [(256, 512, 16), (1000, 520, 48), (2048, 2048, 64), (264, 1024, 128), (128, 2048, 256),
-               (64, 512, 192), (6144, 2048, 64), (2048, 6144, 64), (1024, 2048, 256)]
+               (64, 512, 192), (6144, 2048, 64), (2048, 6144, 64), (1024, 2048, 256),
+               # ragged row blocks and column tiles at r > 128 (128-row tiles) and r = 128 (64-row tiles)
+               (1000, 520, 256), (264, 1048, 192), (1096, 2056, 128)]
 
 
 def _apply_inputs(d, k, r, seed):
@@ -310,7 +312,7 @@ def test_apply_parity(dev, d, k, r):
 
 
 @pytest.mark.parametrize("d,k,r,pad", [(1032, 24, 16, 8), (2056, 4104, 48, 24), (264, 12808, 64, 8),
-                                       (776, 136, 32, 16), (136, 1048, 128, 8)])
+                                       (776, 136, 32, 16), (136, 1048, 128, 8), (200, 1040, 256, 16)])
 def test_apply_parity_row_stride_and_chunking(dev, d, k, r, pad):
     """W as a view with row stride k + pad; shapes whose norms split into
     several C-row and P-row chunks with ragged ends, and W chunks that start

@@ -43,7 +43,8 @@ def _abs_terms(c, p):
 
 
 @pytest.mark.parametrize("d,k,r,alpha", [(256, 512, 16, 3e-3), (1000, 520, 48, 1e-3), (2048, 2048, 64, 2e-4),
-                                         (264, 1024, 128, 5e-3), (128, 2048, 256, 1e-3), (6144, 2048, 64, -4e-4)])
+                                         (264, 1024, 128, 5e-3), (128, 2048, 256, 1e-3), (6144, 2048, 64, -4e-4),
+                                         (1000, 520, 256, 2e-3), (264, 1048, 192, 1e-3)])
 def test_scaled_update_parity(dev, d, k, r, alpha):
     w, c, p = _inputs(d, k, r, 61)
     seed = 0x1234 + d
