@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3-1.7b-block", choices=sorted(WORKLOADS),
                     help="the bench line is the default; the others measure the remaining workload shapes")
+    ap.add_argument("--carried-norm", action="store_true",
+                    help="the step applies with ||W|| carried from the previous update (rgc_apply_carried_batch: "
+                         "W read once per apply); streamed from W once before the warm-up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -199,7 +202,20 @@ def main():
     def accumulate_mb(i):
         rgc.rgc_accumulate_batch([D[m][i * mb:(i + 1) * mb] for m in range(len(mats))], XP, C, workspace=ws)
 
+    wnorm2 = torch.zeros(len(mats), dtype=torch.float64, device=dev)
+    carried = {"fresh": True}
+
+    def apply_carried(step, Ps=None):
+        # the 7 updates with ||W||^2 carried in wnorm2 (streamed from W on the first call)
+        rgc.rgc_apply_carried_batch(W, C, Ps if Ps is not None else P, wl["tau"],
+                                    [step_seed(step, m) for m in range(len(mats))], wnorm2,
+                                    fresh=carried["fresh"], workspace=ws)
+        carried["fresh"] = False
+
     def apply_all(step, Ps=None):
+        if args.carried_norm:
+            apply_carried(step, Ps)
+            return
         # the 7 updates in one batched call (norms sweep, step scalars, update sweep)
         rgc.rgc_apply_batch(W, C, Ps if Ps is not None else P, wl["tau"],
                             [step_seed(step, m) for m in range(len(mats))], workspace=ws)
@@ -277,12 +293,16 @@ def main():
             "accumulate": time_op(lambda s: [accumulate_mb(i) for i in range(n_mb)]),
             "apply": time_op(lambda s: apply_all(s)),
         }
+        if not args.carried_norm:
+            apply_carried(0)  # the first call streams ||W||; the timed ones carry it
+        per_step["apply_carried"] = time_op(lambda s: apply_carried(s))
         # algorithmic work per step (bytes and flops), per entry point
         acc_bytes = sum(2 * mb * d + 2 * mb * r + 8 * d * r for _, d, _, _ in mats) * n_mb
         acc_flops = sum(2 * mb * d * r for _, d, _, _ in mats) * n_mb
         prj_bytes = sum(2 * mb * k + 2 * mb * r + 2 * k * r for _, _, k, _ in mats) * n_mb
         prj_flops = sum(2 * mb * k * r for _, _, k, _ in mats) * n_mb
         app_bytes = sum(6 * d * k + 8 * d * r + 4 * k * r for _, d, k, _ in mats)
+        appc_bytes = sum(4 * d * k + 8 * d * r + 4 * k * r for _, d, k, _ in mats)  # W read once
         smp_bytes = sum(2 * k * r for _, _, k, _ in mats)
         kern = {
             "accumulate": {"s_per_step": per_step["accumulate"], "launches_per_step": n_mb,
@@ -295,7 +315,10 @@ def main():
                         "TFLOPs": prj_flops / per_step["project"] / 1e12},
             "apply": {"s_per_step": per_step["apply"], "launches_per_step": 1,
                       "avg_us": 1e6 * per_step["apply"],
-                      "GBs": app_bytes / per_step["apply"] / 1e9},
+                      "GBs": (appc_bytes if args.carried_norm else app_bytes) / per_step["apply"] / 1e9},
+            "apply_carried": {"s_per_step": per_step["apply_carried"], "launches_per_step": 1,
+                              "avg_us": 1e6 * per_step["apply_carried"],
+                              "GBs": appc_bytes / per_step["apply_carried"] / 1e9},
             "sample_projection": {"s_per_step": per_step["sample_projection"],
                                   "launches_per_step": 1 if wl["refresh"] else 0,
                                   "avg_us": 1e6 * per_step["sample_projection"],
@@ -342,7 +365,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl["desc"], "r": r, "tokens_per_step": T, "microbatch": mb,
-                   "projection": "qr-gaussian" if wl["kind"] == "qr" else "rademacher, fixed", "tau": wl["tau"]},
+                   "projection": "qr-gaussian" if wl["kind"] == "qr" else "rademacher, fixed", "tau": wl["tau"],
+                   "weight_norm": "carried from the previous update" if args.carried_norm else "streamed from W"},
         "sketch_accumulate_TFLOPs": round(kern["accumulate"]["TFLOPs"], 2) if kern else None,
         "sketch_accumulate_frac_bf16_peak": round(kern["accumulate"]["mfma_frac"], 4) if kern else None,
         "fused_apply_GBs": round(kern["apply"]["GBs"], 1) if kern else None,

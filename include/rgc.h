@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define RGC_ABI_VERSION 2
+#define RGC_ABI_VERSION 3
 
 typedef enum {
   RGC_OK = 0,
@@ -190,6 +190,40 @@ rgc_status_t rgc_apply_batch(int64_t n, uint16_t* const* Ws, const int64_t* ldws
                              const uint16_t* const* Ps, const int64_t* ds, const int64_t* ks, int64_t r,
                              float tau, const uint64_t* seeds, float* const* stats, void* ws,
                              size_t ws_bytes, void* stream);
+
+/* ---- The normalized update with a carried ||W|| --------------------------
+ *
+ * rgc_apply's update ([RGC], "How it works") where ||W||_F^2 is not streamed
+ * from W but carried over from the previous update, which summed the squares
+ * of the bf16 weights as it wrote them: the apply then reads W once and
+ * writes it once (4dk bytes instead of 6dk). The step uses the same formula
+ * and the same rounding bits as rgc_apply; its ||W|| is the same number up to
+ * the order of the fp64 sum, so s can differ from rgc_apply's in its last
+ * bit.
+ * wnorm2: device double[n] (8-byte aligned), owned by the caller. fresh != 0:
+ *   on entry its contents are ignored and ||W||^2 is streamed from W as in
+ *   rgc_apply (first call, or after W changed outside these calls); fresh ==
+ *   0: on entry wnorm2[m] must hold ||W_m||_F^2 of the weights as they stand,
+ *   normally as a previous call left it. On return wnorm2[m] holds
+ *   ||W'_m||_F^2 of the weights this call wrote (fp32 sums of eight squares,
+ *   fp64 across them, fixed order, so repeated calls give the same bits); a
+ *   skipped update (flag = 1) leaves W and the entry as they were (with
+ *   fresh != 0, the streamed ||W||^2). A value that does not match W is not
+ *   detected: the step is then scaled by the wrong norm.
+ * Other arguments, the workspace (rgc_apply_batch_workspace_size) and errors
+ * as rgc_apply_batch; wnorm2 NULL gives RGC_ERR_NULL. Four launches: the
+ * norms (at r <= 128 the Gram partials of C and P, plus the W stream only
+ * when fresh != 0), one step scalar per matrix, the update with the squares,
+ * one sum per matrix. At r > 128 the norms launch rebuilds H from the W tiles
+ * it reads, so there it reads W whatever fresh says. */
+rgc_status_t rgc_apply_carried_batch(int64_t n, uint16_t* const* Ws, const int64_t* ldws,
+                                     const float* const* Cs, const uint16_t* const* Ps, const int64_t* ds,
+                                     const int64_t* ks, int64_t r, float tau, const uint64_t* seeds,
+                                     float* const* stats, double* wnorm2, int fresh, void* ws,
+                                     size_t ws_bytes, void* stream);
+rgc_status_t rgc_apply_carried(uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d,
+                               int64_t k, int64_t r, float tau, uint64_t seed, float* stats,
+                               double* wnorm2, int fresh, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- The fixed-scale update ([LoGRA-M], "Minimal Causal Code") -----------
  *

@@ -323,6 +323,17 @@ def apply_update(w_bits: np.ndarray, c: np.ndarray, p_bits: np.ndarray, tau: flo
     return stochastic_round(v, rounding_bits(seed, d, k)), stats
 
 
+def weight_sumsq(w_bits: np.ndarray) -> float:
+    """||W||_F^2 of bf16 weights, summed in float64.
+
+    [RGC, "How it works"]: the normalized step scales by norm(W), read as the
+    Frobenius norm. An update that carries the norm to the next step hands on
+    the squared norm of the weights it wrote, which is this value of them.
+    """
+    w64 = bf16_to_f64(w_bits)
+    return float(np.sum(w64 * w64))
+
+
 def apply_scaled(w_bits: np.ndarray, c: np.ndarray, p_bits: np.ndarray, alpha, seed: int) -> np.ndarray:
     """W <- SR_bf16(W - alpha H), H = C P^T: the fixed-step update.
 

@@ -15,6 +15,8 @@ from .rgc import (  # noqa: F401
     rgc_accumulate_batch,
     rgc_apply,
     rgc_apply_batch,
+    rgc_apply_carried,
+    rgc_apply_carried_batch,
     rgc_apply_from_seed,
     rgc_apply_scaled,
     rgc_apply_scaled_batch,

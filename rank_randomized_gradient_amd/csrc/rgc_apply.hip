@@ -39,7 +39,15 @@
 
 namespace rgc {
 
-enum ApplyMode { kModeNorms = 0, kModeUpdate = 1, kModeReconstruct = 2 };
+// kModeUpdateCarry: the update that also sums the squares of the bf16
+// weights it writes (one fp64 partial per workgroup), for the carried norm.
+enum ApplyMode { kModeNorms = 0, kModeUpdate = 1, kModeReconstruct = 2, kModeUpdateCarry = 3 };
+
+// Where ||W||^2 comes from (ApplyBatch::carry): streamed from W by the norms
+// launch (kCarryNone, kCarryFresh) or the caller's value carried over from
+// the previous update (kCarryIn). With kCarryIn and kCarryFresh the caller's
+// buffer receives ||W'||^2 of the weights the update wrote.
+enum CarryMode { kCarryNone = 0, kCarryIn = 1, kCarryFresh = 2 };
 
 constexpr int kApplyCols = 64;     // columns per tile
 constexpr int kApplyWaves = 4;
@@ -78,6 +86,7 @@ struct ApplyItem {
 struct ApplyBatch {
   int n;
   int fixed;  // 1: fixed-scale update (s = it.alpha, no norms, never skipped)
+  int carry;  // CarryMode
   float tau;
   int wbase[kApplyMaxItems + 1];  // update (and rebuild-norms) workgroups [wbase[m], wbase[m+1]) serve item m
   // Gram-form norms launch (r <= 128): Gram workgroups [gbase[m], gbase[m+1])
@@ -90,8 +99,9 @@ struct ApplyBatch {
   double* partials;               // rebuild norms: 2 per workgroup; Gram norms: 1 per W-stream workgroup
   float* gram;                    // Gram norms: GramShape::NE floats per Gram workgroup
   double* hpairs;                 // Gram norms: per item, kGramMaxPairs block-pair terms of ||H||^2
-  double* wnorm2;                 // Gram norms: per item, ||W||^2
-  float* scale;                   // rebuild norms: per item s, flag
+  double* wnorm2;                 // per item, ||W||^2 (the caller's buffer when carrying)
+  float* scale;                   // per item s, flag (rebuild norms; Gram norms when carrying)
+  double* wpart;                  // carrying: per update workgroup, sum of the written weights' squares
   float* H;                       // reconstruct target (test hook)
 };
 
@@ -301,8 +311,9 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
   const int64_t wl = w - b.wbase[m], gm = b.wbase[m + 1] - b.wbase[m];
   const int64_t u0 = uniform_i64(wl * it.units / gm), u1 = uniform_i64((wl + 1) * it.units / gm);
 
+  constexpr bool UPD = MODE == kModeUpdate || MODE == kModeUpdateCarry;
   float s = 0.f;
-  if constexpr (MODE == kModeUpdate) {
+  if constexpr (UPD) {
     if (b.fixed) {
       s = it.alpha;
     } else if constexpr (!kGramNorms<R>) {
@@ -383,14 +394,21 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
   for (int v = 0; v + 1 < S; ++v)
     if (lu < u1) issue();
 
-  if constexpr (MODE == kModeUpdate && kGramNorms<R>) {
+  if constexpr (UPD && kGramNorms<R>) {
     if (!b.fixed) {
       // s from the item's norm terms while the first copies are in flight: the
       // same fixed-order sums in every wave of every workgroup of the item
       // (a butterfly gives every lane the same sum), so all agree on s.
       const double hp = lane < GramShape<R>::NP ? b.hpairs[m * kGramMaxPairs + lane] : 0.0;
       float flag;
-      step_scale(b.tau, b.wnorm2[m], wave_sum(hp), s, flag, wl == 0 && threadIdx.x == 0 ? it.stats : nullptr);
+      const bool lead = wl == 0 && threadIdx.x == 0;
+      step_scale(b.tau, b.wnorm2[m], wave_sum(hp), s, flag, lead ? it.stats : nullptr);
+      if constexpr (MODE == kModeUpdateCarry) {
+        if (lead) {  // read by the launch that sums the carried norm
+          b.scale[2 * m] = s;
+          b.scale[2 * m + 1] = flag;
+        }
+      }
       if (flag != 0.f) {  // zero or non-finite step: W stays as it is
         wait_vmcnt<0>();
         return;
@@ -422,7 +440,7 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
     if (wrow != rop_row) {  // wave-uniform: new rows
       load_row_operand<R>(it.C, it.d, wrow + Tr::RW * wave, lane, rop);
       rop_row = wrow;
-      if constexpr (MODE == kModeUpdate) {
+      if constexpr (UPD) {
 #pragma unroll
         for (int nt = 0; nt < Tr::NTW; ++nt) {
           const int i = wrow + Tr::RW * wave + 16 * nt + n;
@@ -479,6 +497,16 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
               out[p] = f32x2_to_bf16x2_sr(v0, v1, rw[p]);
             }
             if (inside) *reinterpret_cast<uint4*>(wrowp[nt] + jj) = make_uint4(out[0], out[1], out[2], out[3]);
+            if constexpr (MODE == kModeUpdateCarry) {
+              float sq = 0.f;
+#pragma unroll
+              for (int p = 0; p < 4; ++p) {
+                const float o0 = __uint_as_float(out[p] << 16), o1 = __uint_as_float(out[p] & 0xFFFF0000u);
+                sq += o0 * o0;
+                sq += o1 * o1;
+              }
+              sw += inside ? (double)sq : 0.0;
+            }
           }
         }
       }
@@ -486,6 +514,12 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
   }
   wait_vmcnt<0>();
 
+  if constexpr (MODE == kModeUpdateCarry) {
+    sw = wave_sum(sw);
+    if (lane == 0) red[0][wave] = sw;
+    __syncthreads();
+    if (threadIdx.x == 0) b.wpart[w] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+  }
   if constexpr (MODE == kModeNorms) {
     sw = wave_sum(sw);
     sh = wave_sum(sh);
@@ -763,8 +797,10 @@ __device__ __forceinline__ void finish_scale(const ApplyBatch& b, int m, double 
   }
   __syncthreads();
   if (threadIdx.x != 0) return;
-  const double nw2 = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+  double nw2 = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
   const double nh2 = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
+  if (b.carry == kCarryIn) nw2 = b.wnorm2[m];
+  if (b.carry == kCarryFresh) b.wnorm2[m] = nw2;
   float s, flag;
   step_scale(b.tau, nw2, nh2, s, flag, b.it[m].stats);
   b.scale[2 * m] = s;
@@ -819,7 +855,8 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(ApplyBatch b) {
   }
   double th = (pq == 0 ? 1.0 : 2.0) * G * M;
   double tw = 0.0;
-  if (q == 0)
+  const bool streamed = q == 0 && b.carry != kCarryIn;  // else ||W||^2 is the caller's carried value
+  if (streamed)
     for (int w = b.sbase[m] + (int)threadIdx.x; w < b.sbase[m + 1]; w += 256) tw += b.partials[w];
   th = wave_sum(th);
   tw = wave_sum(tw);
@@ -830,7 +867,23 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(ApplyBatch b) {
   __syncthreads();
   if (threadIdx.x != 0) return;
   b.hpairs[m * kGramMaxPairs + q] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
-  if (q == 0) b.wnorm2[m] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
+  if (streamed) b.wnorm2[m] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
+}
+
+// Carried norm, one workgroup per item: ||W'||^2 = the update workgroups'
+// partials summed in a fixed order (as in the scale launch), stored over the
+// item's ||W||^2. A skipped update leaves W, and so the value, as it is.
+__global__ __launch_bounds__(256) void carry_norm_kernel(ApplyBatch b) {
+  __shared__ double red[4];
+  const int m = blockIdx.x;
+  if (b.scale[2 * m + 1] != 0.f) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double a = 0.0;
+  for (int w = b.wbase[m] + (int)threadIdx.x; w < b.wbase[m + 1]; w += 256) a += b.wpart[w];
+  a = wave_sum(a);
+  if (lane == 0) red[wave] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) b.wnorm2[m] = ((red[0] + red[1]) + red[2]) + red[3];
 }
 
 // ---------------------------------------------------------------------------
@@ -900,9 +953,10 @@ void gram_plan(ApplyBatch& b, int n, const int64_t* ds, const int64_t* ks) {
 
 // Workspace: norm partials (fp64), then Gram partials (fp32), then the
 // per-item Gram-form terms (fp64: block pairs, ||W||^2), then (s, flag) per
-// item, each part 256-byte aligned.
+// item, then the carried norm's per-workgroup partials (fp64), each part
+// 256-byte aligned.
 struct ApplyWorkspace {
-  size_t gram_off, hpairs_off, wnorm2_off, scale_off, total;
+  size_t gram_off, hpairs_off, wnorm2_off, scale_off, wpart_off, total;
 };
 
 template <int R>
@@ -920,7 +974,8 @@ ApplyWorkspace apply_ws_layout(const ApplyBatch& b) {
   l.hpairs_off = l.gram_off + up(gram);
   l.wnorm2_off = l.hpairs_off + up(kApplyMaxItems * kGramMaxPairs * sizeof(double));
   l.scale_off = l.wnorm2_off + up(kApplyMaxItems * sizeof(double));
-  l.total = l.scale_off + up(2 * kApplyMaxItems * sizeof(float));
+  l.wpart_off = l.scale_off + up(2 * kApplyMaxItems * sizeof(float));
+  l.total = l.wpart_off + up((size_t)b.wbase[b.n] * sizeof(double));
   return l;
 }
 
@@ -941,11 +996,12 @@ template <int R>
 rgc_status_t apply_launch(int n, uint16_t* const* Ws, const int64_t* ldws, const float* const* Cs,
                           const uint16_t* const* Ps, const int64_t* ds, const int64_t* ks, float tau,
                           const uint64_t* seeds, float* const* stats, void* ws, hipStream_t st,
-                          const float* alphas = nullptr) {
+                          const float* alphas = nullptr, int carry = kCarryNone, double* wnorm2 = nullptr) {
   ApplyBatch b = {};
   apply_plan_all<R>(b, n, ds, ks);
   b.tau = tau;
   b.fixed = alphas ? 1 : 0;
+  b.carry = carry;
   for (int m = 0; m < n; ++m) {
     b.it[m].W = Ws[m];
     b.it[m].ldw = ldws[m];
@@ -966,16 +1022,24 @@ rgc_status_t apply_launch(int n, uint16_t* const* Ws, const int64_t* ldws, const
   b.partials = static_cast<double*>(ws);
   b.gram = reinterpret_cast<float*>(static_cast<char*>(ws) + l.gram_off);
   b.hpairs = reinterpret_cast<double*>(static_cast<char*>(ws) + l.hpairs_off);
-  b.wnorm2 = reinterpret_cast<double*>(static_cast<char*>(ws) + l.wnorm2_off);
+  b.wnorm2 = carry != kCarryNone ? wnorm2 : reinterpret_cast<double*>(static_cast<char*>(ws) + l.wnorm2_off);
   b.scale = reinterpret_cast<float*>(static_cast<char*>(ws) + l.scale_off);
+  b.wpart = reinterpret_cast<double*>(static_cast<char*>(ws) + l.wpart_off);
   if constexpr (kGramNorms<R>) {
-    hipLaunchKernelGGL(gram_norms_kernel<R>, dim3((unsigned)(b.gbase[n] + b.sbase[n])), dim3(256), 0, st, b);
+    // with a carried ||W|| the launch holds the Gram workgroups alone
+    const int nw = carry == kCarryIn ? 0 : b.sbase[n];
+    hipLaunchKernelGGL(gram_norms_kernel<R>, dim3((unsigned)(b.gbase[n] + nw)), dim3(256), 0, st, b);
     hipLaunchKernelGGL(gram_reduce_kernel<R>, dim3((unsigned)(n * GramShape<R>::NP)), dim3(256), 0, st, b);
   } else {
     hipLaunchKernelGGL((apply_kernel<R, kModeNorms>), dim3((unsigned)G), dim3(256), 0, st, b);
     hipLaunchKernelGGL(apply_scale_kernel, dim3((unsigned)n), dim3(256), 0, st, b);
   }
-  hipLaunchKernelGGL((apply_kernel<R, kModeUpdate>), dim3((unsigned)G), dim3(256), 0, st, b);
+  if (carry == kCarryNone) {
+    hipLaunchKernelGGL((apply_kernel<R, kModeUpdate>), dim3((unsigned)G), dim3(256), 0, st, b);
+  } else {
+    hipLaunchKernelGGL((apply_kernel<R, kModeUpdateCarry>), dim3((unsigned)G), dim3(256), 0, st, b);
+    hipLaunchKernelGGL(carry_norm_kernel, dim3((unsigned)n), dim3(256), 0, st, b);
+  }
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
@@ -1058,6 +1122,43 @@ extern "C" rgc_status_t rgc_apply_batch(int64_t n, uint16_t* const* Ws, const in
                                            static_cast<hipStream_t>(stream));
   });
   return st;
+}
+
+extern "C" rgc_status_t rgc_apply_carried_batch(int64_t n, uint16_t* const* Ws, const int64_t* ldws,
+                                                const float* const* Cs, const uint16_t* const* Ps, const int64_t* ds,
+                                                const int64_t* ks, int64_t r, float tau, const uint64_t* seeds,
+                                                float* const* stats, double* wnorm2, int fresh, void* ws,
+                                                size_t ws_bytes, void* stream) {
+  if (n < 0 || r <= 0) return RGC_ERR_SHAPE;
+  if (n > kApplyMaxItems) return RGC_ERR_UNSUPPORTED;
+  if (n == 0) return RGC_OK;
+  if (!Ws || !ldws || !Cs || !Ps || !ds || !ks || !seeds || !wnorm2) return RGC_ERR_NULL;
+  for (int64_t m = 0; m < n; ++m)
+    if (check_apply_shape(ldws[m], ds[m], ks[m], r) != RGC_OK) return RGC_ERR_SHAPE;
+  if (!rank_supported(r)) return RGC_ERR_UNSUPPORTED;
+  for (int64_t m = 0; m < n; ++m) {
+    const rgc_status_t st = check_apply_item(Ws[m], ldws[m], Cs[m], Ps[m], ds[m], ks[m], stats ? stats[m] : nullptr);
+    if (st != RGC_OK) return st;
+  }
+  if (!aligned_to(wnorm2, 8)) return RGC_ERR_ALIGN;
+  const size_t need = rgc_apply_batch_workspace_size(n, ds, ks, r);
+  if (!ws || ws_bytes < need) return RGC_ERR_WORKSPACE;
+  if (!aligned_to(ws, 256)) return RGC_ERR_ALIGN;
+  rgc_status_t st = RGC_OK;
+  dispatch_rank(r, [&](auto rc) {
+    st = apply_launch<decltype(rc)::value>((int)n, Ws, ldws, Cs, Ps, ds, ks, tau, seeds, stats, ws,
+                                           static_cast<hipStream_t>(stream), nullptr,
+                                           fresh ? kCarryFresh : kCarryIn, wnorm2);
+  });
+  return st;
+}
+
+extern "C" rgc_status_t rgc_apply_carried(uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d,
+                                          int64_t k, int64_t r, float tau, uint64_t seed, float* stats,
+                                          double* wnorm2, int fresh, void* ws, size_t ws_bytes, void* stream) {
+  if (d <= 0 || k <= 0 || r <= 0) return RGC_ERR_SHAPE;
+  return rgc_apply_carried_batch(1, &W, &ldw, &C, &P, &d, &k, r, tau, &seed, &stats, wnorm2, fresh, ws, ws_bytes,
+                                 stream);
 }
 
 extern "C" size_t rgc_apply_workspace_size(int64_t d, int64_t k, int64_t r) {

@@ -10,6 +10,8 @@ Names mirror the C ABI in include/rgc.h:
   rgc_accumulate(D, XP, C)                  C += D^T XP (in place)
   rgc_apply(W, C, P, tau, seed)             W <- SR(W - tau ||W|| H / ||H||) (in place)
   rgc_apply_scaled(W, C, P, alpha, seed)    W <- SR(W - alpha H) (in place)
+  rgc_apply_carried(W, C, P, tau, seed, wnorm2, fresh)
+                                            rgc_apply with ||W||^2 carried between calls
   rgc_apply_from_seed(mode, kind, proj_seed, W, C, step, seed)
                                             P regenerated from its seed, then one of the two
 """
@@ -66,6 +68,12 @@ SIGNATURES = {
     "rgc_apply_scaled_batch": (ctypes.c_int, [_i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_vp),
                                               ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i64,
                                               ctypes.POINTER(_f32), ctypes.POINTER(_u64), _vp]),
+    "rgc_apply_carried_batch": (ctypes.c_int, [_i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_vp),
+                                               ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i64,
+                                               _f32, ctypes.POINTER(_u64), ctypes.POINTER(_vp), _vp, ctypes.c_int,
+                                               _vp, _sz, _vp]),
+    "rgc_apply_carried": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _f32, _u64, _vp, _vp, ctypes.c_int,
+                                         _vp, _sz, _vp]),
     "rgc_apply_from_seed_workspace_size": (_sz, [ctypes.c_int, _i64, _i64, _i64]),
     "rgc_apply_from_seed": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _u64, _vp, _i64, _vp, _i64, _i64, _i64, _f32,
                                            _u64, _vp, _vp, _sz, _vp]),
@@ -364,6 +372,66 @@ def rgc_apply_batch(Ws, Cs, Ps, tau: float, seeds, stats=None, workspace: Worksp
     _check(lib.rgc_apply_batch(n, _ptrs(Ws), _i64s(ldws), _ptrs(Cs), _ptrs(Ps), _i64s(ds), _i64s(ks), r,
                                float(tau), seeds_arr, sps, wp, wn, _stream(dev)))
     return Ws
+
+
+def _stats_ptrs(stats, n):
+    if stats is None:
+        return None
+    vals = []
+    for st in stats:
+        if st is None:
+            vals.append(None)
+            continue
+        _need_gpu(st)
+        _dense(st, torch.float32, "stats")
+        if st.numel() < 4:
+            raise RgcError("stats needs 4 floats")
+        vals.append(st.data_ptr())
+    return (_vp * n)(*vals)
+
+
+def rgc_apply_carried_batch(Ws, Cs, Ps, tau: float, seeds, wnorm2: torch.Tensor, fresh: bool, stats=None,
+                            workspace: Workspace | None = None):
+    """rgc_apply_batch with ||W||^2 carried in wnorm2 (device float64, n values):
+    fresh=True streams it from W first; on return wnorm2 holds ||W'||^2 of
+    the weights written, for the next call with fresh=False."""
+    lib = load_library()
+    n = len(Ws)
+    if n == 0:
+        return Ws
+    if len(Cs) != n or len(Ps) != n or len(seeds) != n or (stats is not None and len(stats) != n):
+        raise RgcError("Ws, Cs, Ps, seeds (and stats) must have the same length")
+    dev = _need_gpu(*Ws, *Cs, *Ps, wnorm2)
+    _dense(wnorm2, torch.float64, "wnorm2")
+    if wnorm2.numel() < n:
+        raise RgcError("wnorm2 needs one float64 per matrix")
+    r, ldws, ds, ks = _apply_items(Ws, Cs, Ps)
+    sps = _stats_ptrs(stats, n)
+    seeds_arr = (_u64 * n)(*[s & 0xFFFFFFFFFFFFFFFF for s in seeds])
+    ws = workspace or default_workspace(dev)
+    wp, wn = ws.get(lib.rgc_apply_batch_workspace_size(n, _i64s(ds), _i64s(ks), r))
+    _check(lib.rgc_apply_carried_batch(n, _ptrs(Ws), _i64s(ldws), _ptrs(Cs), _ptrs(Ps), _i64s(ds), _i64s(ks), r,
+                                       float(tau), seeds_arr, sps, wnorm2.data_ptr(), 1 if fresh else 0, wp, wn,
+                                       _stream(dev)))
+    return Ws
+
+
+def rgc_apply_carried(W: torch.Tensor, C: torch.Tensor, P: torch.Tensor, tau: float, seed: int,
+                      wnorm2: torch.Tensor, fresh: bool, stats: torch.Tensor | None = None,
+                      workspace: Workspace | None = None) -> torch.Tensor:
+    lib = load_library()
+    dev = _need_gpu(W, C, P, wnorm2)
+    _dense(wnorm2, torch.float64, "wnorm2")
+    if wnorm2.numel() < 1:
+        raise RgcError("wnorm2 needs one float64")
+    r, ldws, ds, ks = _apply_items([W], [C], [P])
+    sps = _stats_ptrs(None if stats is None else [stats], 1)
+    ws = workspace or default_workspace(dev)
+    wp, wn = ws.get(lib.rgc_apply_workspace_size(ds[0], ks[0], r))
+    _check(lib.rgc_apply_carried(W.data_ptr(), ldws[0], C.data_ptr(), P.data_ptr(), ds[0], ks[0], r, float(tau),
+                                 seed & 0xFFFFFFFFFFFFFFFF, None if sps is None else sps[0], wnorm2.data_ptr(),
+                                 1 if fresh else 0, wp, wn, _stream(dev)))
+    return W
 
 
 def _apply_items(Ws, Cs, Ps):

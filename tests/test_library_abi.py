@@ -159,6 +159,37 @@ def test_scaled_apply_validation(lib):
     assert lib.rgc_apply_scaled_batch(17, ws_, lds, ws_, ws_, ds, ks, 64, alphas, seeds, s) == UNSUP
 
 
+def test_carried_apply_validation(lib):
+    s = None
+    f = ctypes.c_float(1e-3)
+    need = lib.rgc_apply_workspace_size(64, 256, 16)
+    # the workspace holds one fp64 partial per update workgroup for the carried norm
+    assert need >= 8 * 2
+    args = lambda W=FAKE, ldw=256, C=FAKE, d=64, r=16, wn=FAKE, fresh=0, ws=FAKE, n=need: (
+        W, ldw, C, FAKE, d, 256, r, f, 7, None, wn, fresh, ws, n, s)
+    assert lib.rgc_apply_carried(*args(ldw=255)) == SHAPE
+    assert lib.rgc_apply_carried(*args(r=272)) == SHAPE  # r > k
+    assert lib.rgc_apply_carried(*args(d=60)) == UNSUP
+    assert lib.rgc_apply_carried(*args(wn=None)) == NULL
+    assert lib.rgc_apply_carried(*args(C=None, fresh=1)) == NULL
+    assert lib.rgc_apply_carried(*args(wn=FAKE + 4)) == ALIGN
+    assert lib.rgc_apply_carried(*args(ws=None)) == WS
+    assert lib.rgc_apply_carried(*args(n=need - 8)) == WS
+    assert lib.rgc_apply_carried(*args(ws=FAKE + 128)) == ALIGN
+    n = 2
+    ws_ = (ctypes.c_void_p * n)(FAKE, FAKE)
+    lds = (ctypes.c_int64 * n)(256, 512)
+    ds = (ctypes.c_int64 * n)(64, 128)
+    ks = (ctypes.c_int64 * n)(256, 512)
+    seeds = (ctypes.c_uint64 * n)(1, 2)
+    assert lib.rgc_apply_carried_batch(0, None, None, None, None, None, None, 64, f, None, None, None, 0, None, 0,
+                                       s) == OK
+    assert lib.rgc_apply_carried_batch(n, ws_, lds, ws_, ws_, ds, ks, 64, f, seeds, None, None, 1, FAKE, 1 << 30,
+                                       s) == NULL
+    assert lib.rgc_apply_carried_batch(17, ws_, lds, ws_, ws_, ds, ks, 64, f, seeds, None, FAKE, 0, FAKE, 1 << 30,
+                                       s) == UNSUP
+
+
 def test_apply_from_seed_validation(lib):
     s = None
     f = ctypes.c_float(1e-3)
