@@ -56,10 +56,16 @@ class SketchedLinear(torch.nn.Module):
     Per update: begin_update(seed) draws P and zeroes C; every microbatch's
     forward/backward adds its D^T (X P) to C; apply_update(...) changes the
     weights in place. P and C live on the layer (k x r bf16 and d x r fp32).
+
+    carry_norm=True: the normalized update hands ||W||^2 of the weights it
+    writes to the next one (rgc_apply_carried), so each later update reads W
+    once. The value is refreshed from W after a fixed-step update and after
+    invalidate_weight_norm(), which a caller that changes the weights by other
+    means must call.
     """
 
     def __init__(self, in_features: int, out_features: int, rank: int, kind: str = "qr", device=None,
-                 weight: torch.Tensor | None = None):
+                 weight: torch.Tensor | None = None, carry_norm: bool = False):
         super().__init__()
         device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         if weight is None:
@@ -73,6 +79,13 @@ class SketchedLinear(torch.nn.Module):
         self.register_buffer("sketch", torch.zeros((out_features, rank), dtype=torch.float32, device=device))
         self.workspace = rgc.Workspace(device)
         self.proj_seed = None
+        self.carry_norm = carry_norm
+        self.register_buffer("weight_norm2", torch.zeros(1, dtype=torch.float64, device=device))
+        self._norm_fresh = True  # weight_norm2 does not hold ||W||^2 yet
+
+    def invalidate_weight_norm(self) -> None:
+        """The weights changed outside apply_update: the next update streams ||W|| again."""
+        self._norm_fresh = True
 
     def begin_update(self, proj_seed: int) -> None:
         """Draws P from its seed (fixed for the whole accumulation) and zeroes C."""
@@ -92,7 +105,12 @@ class SketchedLinear(torch.nn.Module):
         if (tau is None) == (alpha is None):
             raise rgc.RgcError("give exactly one of tau (normalized update) or alpha (fixed step)")
         w = self.weight.data
-        if tau is not None:
+        if tau is not None and self.carry_norm:
+            rgc.rgc_apply_carried(w, self.sketch, self.proj, tau, seed, self.weight_norm2, fresh=self._norm_fresh,
+                                  stats=stats, workspace=self.workspace)
+            self._norm_fresh = False
+        elif tau is not None:
             rgc.rgc_apply(w, self.sketch, self.proj, tau, seed, stats=stats, workspace=self.workspace)
         else:
             rgc.rgc_apply_scaled(w, self.sketch, self.proj, alpha, seed)
+            self._norm_fresh = True

@@ -79,3 +79,38 @@ def test_sketched_linear_requires_a_projection(dev):
         layer(torch.zeros(4, 512, dtype=torch.bfloat16, device=dev))
     with pytest.raises(rgc.RgcError):
         layer.apply_update(0, tau=1e-3, alpha=1e-3)
+
+
+def test_sketched_linear_carried_norm_matches_plain(dev):
+    """Two layers on the same inputs over four updates, one carrying ||W||
+    between its normalized updates (with a fixed-step update in between,
+    after which the norm is streamed again): the same step s up to its last
+    bit, and with an equal s the same weights."""
+    d, k, r, mb = 512, 1024, 64, 512
+    w = synth.normal_bf16((d, k), 0.02, seed=2002)
+    plain = SketchedLinear(k, d, r, kind="qr", device=dev, weight=w.clone())
+    carry = SketchedLinear(k, d, r, kind="qr", device=dev, weight=w.clone(), carry_norm=True)
+    for u, how in enumerate(["tau", "tau", "alpha", "tau"]):
+        x = synth.normal_bf16((mb, k), 1.0, seed=2100 + u).to(dev).requires_grad_(True)
+        dy = synth.normal_bf16((mb, d), 0.1, seed=2200 + u).to(dev)
+        stats = []
+        for layer in (plain, carry):
+            layer.begin_update(300 + u)
+            layer(x).backward(dy)
+            st = torch.zeros(4, device=dev)
+            if how == "tau":
+                layer.apply_update(400 + u, tau=1e-3, stats=st)
+            else:
+                layer.apply_update(400 + u, alpha=2e-6)
+            stats.append(st)
+        torch.cuda.synchronize()
+        if how == "tau":
+            sa, sb = (np.float32(s.cpu().numpy()[2]) for s in stats)
+            assert sa > 0
+            ulps = abs(int(sa.view(np.int32)) - int(sb.view(np.int32)))
+            assert ulps <= 1, (u, sa, sb)
+            if ulps:
+                carry.weight.data.copy_(plain.weight.data)
+                carry.invalidate_weight_norm()
+                continue
+        assert torch.equal(plain.weight.data, carry.weight.data), f"update {u}"
