@@ -674,9 +674,28 @@ Schedule project_schedule(int n, const int64_t* ns, const int64_t* ks) {
   return make_schedule(n, ns, ks, StageShape<R, kProjectKH>::TILE, StageShape<R, kProjectKH>::KS);
 }
 
+// When every tile has the same K-steps (one token count for all items, as in
+// the accumulate) and p >= 2 whole copies of the tile list fill at least 90%
+// of the workgroups, the schedule takes p x tiles workgroups: every range
+// then lies inside one tile and every tile has exactly p partials, instead
+// of ranges that straddle tile ends and leave up to two partials each
+// (measured on the Qwen3-1.7B-shaped block, 80 tiles: 240 workgroups 41.3 us
+// against 256 workgroups 42.9 us per accumulate call). A forced workgroup
+// count is kept as it is.
+void align_ranges_to_tiles(Schedule& s) {
+  if (env_int("RGC_SKETCH_WGS", 0) > 0) return;
+  const int64_t tiles = s.tbase[s.n];
+  for (int m = 1; m < s.n; ++m)
+    if (s.nkb[m] != s.nkb[0]) return;
+  const int64_t p = s.G / tiles;
+  if (p >= 2 && p <= s.nkb[0] && 10 * p * tiles >= 9 * (int64_t)s.G) s.G = (int)(p * tiles);
+}
+
 template <int R>
 Schedule accumulate_schedule(int n, const int64_t* ns, const int64_t* ks) {
-  return make_schedule(n, ns, ks, StageShape<R, 1>::TILE, StageShape<R, 1>::KS);
+  Schedule s = make_schedule(n, ns, ks, StageShape<R, 1>::TILE, StageShape<R, 1>::KS);
+  align_ranges_to_tiles(s);
+  return s;
 }
 
 template <int R>
