@@ -27,7 +27,8 @@
 //   (accumulate: D is token-major).
 // * Work is balanced across the chip at K-step granularity ("stream-K"):
 //   the (item, tile, K-step) units of the whole batch are cut into one
-//   contiguous range per workgroup, one workgroup per compute unit. A tile
+//   contiguous range per workgroup, about one workgroup per compute unit
+//   (the host-side schedule below says how many). A tile
 //   that lies inside one range is finished in place; a tile cut between
 //   ranges gets fp32 partials (at most two per workgroup) that a second
 //   launch sums in workgroup order. Every reduction has a fixed order, so
