@@ -217,6 +217,24 @@ def test_accumulate_batch_parity(dev):
         assert rel_frobenius(c.cpu().numpy(), ref) < 1e-5
 
 
+def test_accumulate_batch_ranges_aligned_to_tiles(dev):
+    """The Qwen3-1.7B-shaped block's seven d (80 tiles of 256 columns) at a
+    ragged token count: 63 K-steps per tile, the last one 16 tokens, so that
+    the schedule cuts every tile into exactly three ranges (240 workgroups on
+    a 256-CU part) and each tile's last range ends in the partial step."""
+    T, r = 2000, 64
+    ds = [2048, 1024, 1024, 2048, 6144, 6144, 2048]
+    dds = [synth.normal_bf16((T, d), 1e-3, seed=150 + i) for i, d in enumerate(ds)]
+    xps = [synth.normal_bf16((T, r), 3.0, seed=160 + i) for i in range(len(ds))]
+    c0s = [synth.normal_f32((d, r), 1e-3, seed=170 + i) for i, d in enumerate(ds)]
+    cs = [c.clone().to(dev) for c in c0s]
+    rgc.rgc_accumulate_batch([d.to(dev) for d in dds], [x.to(dev) for x in xps], cs)
+    _sync()
+    for dd, xp, c0, c in zip(dds, xps, c0s, cs):
+        ref = orc.accumulate(c0.numpy(), bits(dd), bits(xp))
+        assert rel_frobenius(c.cpu().numpy(), ref) < 1e-5
+
+
 @pytest.mark.parametrize("wgs", [1, 3])
 def test_sketch_batches_with_whole_tiles_per_workgroup(dev, monkeypatch, wgs):
     """Few workgroups: each range holds whole tiles, ends in later items, and
