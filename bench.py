@@ -60,7 +60,7 @@ WORKLOAD = WORKLOADS["qwen3-1.7b-block"]
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3-1.7b-block", choices=sorted(WORKLOADS),
                     help="the bench line is the default; the others measure the remaining workload shapes")
