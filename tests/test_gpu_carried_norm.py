@@ -108,8 +108,9 @@ def test_carried_chain_matches_plain_apply(dev, d, k, r):
             fresh = True
 
 
-def test_carried_skip_keeps_weights_and_value(dev):
-    d, k, r = 512, 1024, 64
+@pytest.mark.parametrize("r", [64, 256])  # Gram-form norms; rebuilt norms and the scale launch
+def test_carried_skip_keeps_weights_and_value(dev, r):
+    d, k = 512, 1024
     w, p = _w_p(d, k, r, 8)
     wg = w.clone().to(dev)
     zero = torch.zeros(d, r, device=dev)
