@@ -37,6 +37,9 @@
  *     initialisation and are dead after the call's kernels complete, so one
  *     workspace can serve any sequence of calls ordered on a stream; calls
  *     that may run concurrently need separate workspaces.
+ *   - Results depend only on the arguments and the device's compute-unit
+ *     count (which sets the work partition and so the fp32 summation order);
+ *     no environment variable or other process state changes them.
  *   - Arguments are validated on the host before anything is enqueued; on any
  *     error nothing is launched and no buffer changes. Conditions that are only
  *     known on the device (a zero sketch, non-finite values) are reported
@@ -279,6 +282,24 @@ rgc_status_t rgc_test_philox(uint64_t seed, int64_t n, const uint32_t* ctr, uint
 rgc_status_t rgc_test_stochastic_round(const float* v, uint16_t* out, int64_t rows, int64_t cols,
                                        int64_t ld, int64_t row0, int64_t col0, uint64_t seed,
                                        void* stream);
+
+/* rgc_project_batch (contraction 0) and rgc_accumulate_batch (contraction 1)
+ * with the number of workgroups given by the caller (workgroups > 0) instead
+ * of chosen from the shapes and the device. The partition decides the fp32
+ * summation order, so results may differ in their last bits from the product
+ * calls'; tests use it to force ranges of whole tiles that cross item
+ * boundaries. Arguments, validation and errors otherwise as the product
+ * calls; workgroups <= 0 gives RGC_ERR_SHAPE (the query returns 0). */
+size_t rgc_test_sketch_workspace_size(int contraction, int64_t workgroups, int64_t n, const int64_t* widths,
+                                      int64_t T, int64_t r);
+rgc_status_t rgc_test_project_batch_wgs(int64_t workgroups, int64_t n, const uint16_t* const* Xs,
+                                        const int64_t* ldxs, const int64_t* ks, const uint16_t* const* Ps,
+                                        uint16_t* const* XPs, int64_t T, int64_t r, void* ws, size_t ws_bytes,
+                                        void* stream);
+rgc_status_t rgc_test_accumulate_batch_wgs(int64_t workgroups, int64_t n, const uint16_t* const* Ds,
+                                           const int64_t* ldds, const int64_t* ds, const uint16_t* const* XPs,
+                                           float* const* Cs, int64_t T, int64_t r, void* ws, size_t ws_bytes,
+                                           void* stream);
 
 /* H = C P^T in fp32 through the apply kernel's tile code (d x k, row stride k). */
 rgc_status_t rgc_test_reconstruct(const float* C, const uint16_t* P, float* H, int64_t d,

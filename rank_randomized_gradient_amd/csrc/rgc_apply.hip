@@ -925,8 +925,7 @@ constexpr int64_t kApplyUnitsPerWG = 8;
 template <int R>
 void apply_plan(ApplyBatch& b, int n, const int64_t* ds, const int64_t* ks) {
   using Tr = ApplyTraits<R>;
-  const int forced = env_int("RGC_APPLY_UNITS", 0);
-  const int64_t per = forced > 0 ? forced : kApplyUnitsPerWG;
+  const int64_t per = kApplyUnitsPerWG;
   b.wbase[0] = 0;
   for (int m = 0; m < n; ++m) {
     b.it[m].ctiles = (ks[m] + kApplyCols - 1) / kApplyCols;

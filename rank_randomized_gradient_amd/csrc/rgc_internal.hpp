@@ -70,11 +70,4 @@ inline int device_compute_units() {
   return v;
 }
 
-inline int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  if (!v || !*v) return dflt;
-  int x = atoi(v);
-  return x > 0 ? x : dflt;
-}
-
 }  // namespace rgc

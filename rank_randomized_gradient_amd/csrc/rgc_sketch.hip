@@ -632,16 +632,19 @@ namespace {
 // ranges pay their pipeline fill and their split-tile partials on little
 // work (measured on one 4096 x 4096 matrix with 4096-token microbatches:
 // 1.49 against 1.62 ms per step).
+// `forced` > 0 replaces this choice (the test hooks only: the partition
+// decides the fp32 summation order, so the product calls never take it from
+// anything but the shapes and the device).
 constexpr int64_t kMinUnitsPerWorkgroup = 16;
-int64_t sketch_workgroups(int64_t units) {
-  const int forced = env_int("RGC_SKETCH_WGS", 0);
+int64_t sketch_workgroups(int64_t units, int64_t forced) {
   if (forced > 0) return forced;
   const int64_t cus = device_compute_units();
   return units < kMinUnitsPerWorkgroup * cus ? (cus + 1) / 2 : cus;
 }
 
 // The schedule for items with N extents ns[] and K extents ks[].
-Schedule make_schedule(int n, const int64_t* ns, const int64_t* ks, int64_t tile_n, int64_t kblock) {
+Schedule make_schedule(int n, const int64_t* ns, const int64_t* ks, int64_t tile_n, int64_t kblock,
+                       int64_t forced) {
   Schedule s = {};
   s.n = n;
   s.tile_n = tile_n;
@@ -654,7 +657,7 @@ Schedule make_schedule(int n, const int64_t* ns, const int64_t* ks, int64_t tile
     s.tbase[m + 1] = s.tbase[m] + tiles;
   }
   s.U = s.ubase[n];
-  const int64_t G = sketch_workgroups(s.U);
+  const int64_t G = sketch_workgroups(s.U, forced);
   s.G = (int)(s.U < G ? s.U : G);
   return s;
 }
@@ -671,8 +674,8 @@ dim3 finish_grid(const Schedule& s) {
 }
 
 template <int R>
-Schedule project_schedule(int n, const int64_t* ns, const int64_t* ks) {
-  return make_schedule(n, ns, ks, StageShape<R, kProjectKH>::TILE, StageShape<R, kProjectKH>::KS);
+Schedule project_schedule(int n, const int64_t* ns, const int64_t* ks, int64_t forced) {
+  return make_schedule(n, ns, ks, StageShape<R, kProjectKH>::TILE, StageShape<R, kProjectKH>::KS, forced);
 }
 
 // When every tile has the same K-steps (one token count for all items, as in
@@ -683,8 +686,8 @@ Schedule project_schedule(int n, const int64_t* ns, const int64_t* ks) {
 // (measured on the Qwen3-1.7B-shaped block, 80 tiles: 240 workgroups 41.3 us
 // against 256 workgroups 42.9 us per accumulate call). A forced workgroup
 // count is kept as it is.
-void align_ranges_to_tiles(Schedule& s) {
-  if (env_int("RGC_SKETCH_WGS", 0) > 0) return;
+void align_ranges_to_tiles(Schedule& s, int64_t forced) {
+  if (forced > 0) return;
   const int64_t tiles = s.tbase[s.n];
   for (int m = 1; m < s.n; ++m)
     if (s.nkb[m] != s.nkb[0]) return;
@@ -693,19 +696,20 @@ void align_ranges_to_tiles(Schedule& s) {
 }
 
 template <int R>
-Schedule accumulate_schedule(int n, const int64_t* ns, const int64_t* ks) {
-  Schedule s = make_schedule(n, ns, ks, StageShape<R, 1>::TILE, StageShape<R, 1>::KS);
-  align_ranges_to_tiles(s);
+Schedule accumulate_schedule(int n, const int64_t* ns, const int64_t* ks, int64_t forced) {
+  Schedule s = make_schedule(n, ns, ks, StageShape<R, 1>::TILE, StageShape<R, 1>::KS, forced);
+  align_ranges_to_tiles(s, forced);
   return s;
 }
 
 template <int R>
 rgc_status_t project_launch(int n, const uint16_t* const* Xs, const int64_t* ldxs, const int64_t* ks,
-                            const uint16_t* const* Ps, uint16_t* const* XPs, int64_t T, void* ws, hipStream_t st) {
+                            const uint16_t* const* Ps, uint16_t* const* XPs, int64_t T, void* ws, hipStream_t st,
+                            int64_t forced) {
   int64_t ns[kMaxItems];
   for (int m = 0; m < n; ++m) ns[m] = T;
   ProjectBatch pb = {};
-  pb.s = project_schedule<R>(n, ns, ks);
+  pb.s = project_schedule<R>(n, ns, ks, forced);
   FinishBatch fb = {};
   fb.s = pb.s;
   for (int m = 0; m < n; ++m) {
@@ -724,11 +728,12 @@ rgc_status_t project_launch(int n, const uint16_t* const* Xs, const int64_t* ldx
 
 template <int R>
 rgc_status_t accumulate_launch(int n, const uint16_t* const* Ds, const int64_t* ldds, const int64_t* ds,
-                               const uint16_t* const* XPs, float* const* Cs, int64_t T, void* ws, hipStream_t st) {
+                               const uint16_t* const* XPs, float* const* Cs, int64_t T, void* ws, hipStream_t st,
+                               int64_t forced) {
   int64_t ks[kMaxItems];
   for (int m = 0; m < n; ++m) ks[m] = T;
   AccumulateBatch ab = {};
-  ab.s = accumulate_schedule<R>(n, ds, ks);
+  ab.s = accumulate_schedule<R>(n, ds, ks, forced);
   FinishBatch fb = {};
   fb.s = ab.s;
   for (int m = 0; m < n; ++m) {
@@ -746,10 +751,10 @@ rgc_status_t accumulate_launch(int n, const uint16_t* const* Ds, const int64_t* 
 }
 
 template <int R>
-size_t accumulate_workspace(int n, const int64_t* ds, int64_t T) {
+size_t accumulate_workspace(int n, const int64_t* ds, int64_t T, int64_t forced) {
   int64_t ks[kMaxItems];
   for (int m = 0; m < n; ++m) ks[m] = T;
-  return partial_bytes<R>(accumulate_schedule<R>(n, ds, ks));
+  return partial_bytes<R>(accumulate_schedule<R>(n, ds, ks, forced));
 }
 
 rgc_status_t check_project_item(const uint16_t* X, int64_t ldx, int64_t k, const uint16_t* P, const uint16_t* XP,
@@ -777,7 +782,9 @@ rgc_status_t check_accumulate_item(const uint16_t* D, int64_t ldd, int64_t d, co
 
 using namespace rgc;
 
-extern "C" size_t rgc_project_batch_workspace_size(int64_t n, const int64_t* ks, int64_t T, int64_t r) {
+namespace {
+
+size_t project_ws_impl(int64_t n, const int64_t* ks, int64_t T, int64_t r, int64_t forced) {
   if (n <= 0 || n > kMaxItems || !ks || T <= 0) return 0;
   for (int64_t m = 0; m < n; ++m)
     if (ks[m] <= 0) return 0;
@@ -786,28 +793,28 @@ extern "C" size_t rgc_project_batch_workspace_size(int64_t n, const int64_t* ks,
   size_t out = 0;
   if (!dispatch_rank(r, [&](auto rc) {
         constexpr int R = decltype(rc)::value;
-        out = partial_bytes<R>(project_schedule<R>((int)n, ns, ks));
+        out = partial_bytes<R>(project_schedule<R>((int)n, ns, ks, forced));
       }))
     return 0;
   return out;
 }
 
-extern "C" size_t rgc_accumulate_batch_workspace_size(int64_t n, const int64_t* ds, int64_t T, int64_t r) {
+size_t accumulate_ws_impl(int64_t n, const int64_t* ds, int64_t T, int64_t r, int64_t forced) {
   if (n <= 0 || n > kMaxItems || !ds || T <= 0) return 0;
   for (int64_t m = 0; m < n; ++m)
     if (ds[m] <= 0) return 0;
   size_t out = 0;
   if (!dispatch_rank(r, [&](auto rc) {
         constexpr int R = decltype(rc)::value;
-        out = accumulate_workspace<R>((int)n, ds, T);
+        out = accumulate_workspace<R>((int)n, ds, T, forced);
       }))
     return 0;
   return out;
 }
 
-extern "C" rgc_status_t rgc_project_batch(int64_t n, const uint16_t* const* Xs, const int64_t* ldxs,
-                                          const int64_t* ks, const uint16_t* const* Ps, uint16_t* const* XPs,
-                                          int64_t T, int64_t r, void* ws, size_t ws_bytes, void* stream) {
+rgc_status_t project_batch_impl(int64_t n, const uint16_t* const* Xs, const int64_t* ldxs, const int64_t* ks,
+                                const uint16_t* const* Ps, uint16_t* const* XPs, int64_t T, int64_t r, void* ws,
+                                size_t ws_bytes, void* stream, int64_t forced) {
   if (n < 0 || T < 0 || r <= 0) return RGC_ERR_SHAPE;
   if (n > kMaxItems || !rank_supported(r) || T > kMaxTiledDim) return RGC_ERR_UNSUPPORTED;
   if (n == 0 || T == 0) return RGC_OK;
@@ -816,19 +823,20 @@ extern "C" rgc_status_t rgc_project_batch(int64_t n, const uint16_t* const* Xs, 
     const rgc_status_t st = check_project_item(Xs[m], ldxs[m], ks[m], Ps[m], XPs[m], T, r);
     if (st != RGC_OK) return st;
   }
-  const size_t need = rgc_project_batch_workspace_size(n, ks, T, r);
+  const size_t need = project_ws_impl(n, ks, T, r, forced);
   if (need > 0 && (!ws || ws_bytes < need)) return RGC_ERR_WORKSPACE;
   if (need > 0 && !aligned_to(ws, 256)) return RGC_ERR_ALIGN;
   rgc_status_t st = RGC_OK;
   dispatch_rank(r, [&](auto rc) {
-    st = project_launch<decltype(rc)::value>((int)n, Xs, ldxs, ks, Ps, XPs, T, ws, static_cast<hipStream_t>(stream));
+    st = project_launch<decltype(rc)::value>((int)n, Xs, ldxs, ks, Ps, XPs, T, ws, static_cast<hipStream_t>(stream),
+                                             forced);
   });
   return st;
 }
 
-extern "C" rgc_status_t rgc_accumulate_batch(int64_t n, const uint16_t* const* Ds, const int64_t* ldds,
-                                             const int64_t* ds, const uint16_t* const* XPs, float* const* Cs,
-                                             int64_t T, int64_t r, void* ws, size_t ws_bytes, void* stream) {
+rgc_status_t accumulate_batch_impl(int64_t n, const uint16_t* const* Ds, const int64_t* ldds, const int64_t* ds,
+                                   const uint16_t* const* XPs, float* const* Cs, int64_t T, int64_t r, void* ws,
+                                   size_t ws_bytes, void* stream, int64_t forced) {
   if (n < 0 || T < 0 || r <= 0) return RGC_ERR_SHAPE;
   if (n > kMaxItems || !rank_supported(r)) return RGC_ERR_UNSUPPORTED;
   if (n == 0 || T == 0) return RGC_OK;
@@ -837,14 +845,37 @@ extern "C" rgc_status_t rgc_accumulate_batch(int64_t n, const uint16_t* const* D
     const rgc_status_t st = check_accumulate_item(Ds[m], ldds[m], ds[m], XPs[m], Cs[m], T);
     if (st != RGC_OK) return st;
   }
-  const size_t need = rgc_accumulate_batch_workspace_size(n, ds, T, r);
+  const size_t need = accumulate_ws_impl(n, ds, T, r, forced);
   if (need > 0 && (!ws || ws_bytes < need)) return RGC_ERR_WORKSPACE;
   if (need > 0 && !aligned_to(ws, 256)) return RGC_ERR_ALIGN;
   rgc_status_t st = RGC_OK;
   dispatch_rank(r, [&](auto rc) {
-    st = accumulate_launch<decltype(rc)::value>((int)n, Ds, ldds, ds, XPs, Cs, T, ws, static_cast<hipStream_t>(stream));
+    st = accumulate_launch<decltype(rc)::value>((int)n, Ds, ldds, ds, XPs, Cs, T, ws,
+                                                static_cast<hipStream_t>(stream), forced);
   });
   return st;
+}
+
+}  // namespace
+
+extern "C" size_t rgc_project_batch_workspace_size(int64_t n, const int64_t* ks, int64_t T, int64_t r) {
+  return project_ws_impl(n, ks, T, r, 0);
+}
+
+extern "C" size_t rgc_accumulate_batch_workspace_size(int64_t n, const int64_t* ds, int64_t T, int64_t r) {
+  return accumulate_ws_impl(n, ds, T, r, 0);
+}
+
+extern "C" rgc_status_t rgc_project_batch(int64_t n, const uint16_t* const* Xs, const int64_t* ldxs,
+                                          const int64_t* ks, const uint16_t* const* Ps, uint16_t* const* XPs,
+                                          int64_t T, int64_t r, void* ws, size_t ws_bytes, void* stream) {
+  return project_batch_impl(n, Xs, ldxs, ks, Ps, XPs, T, r, ws, ws_bytes, stream, 0);
+}
+
+extern "C" rgc_status_t rgc_accumulate_batch(int64_t n, const uint16_t* const* Ds, const int64_t* ldds,
+                                             const int64_t* ds, const uint16_t* const* XPs, float* const* Cs,
+                                             int64_t T, int64_t r, void* ws, size_t ws_bytes, void* stream) {
+  return accumulate_batch_impl(n, Ds, ldds, ds, XPs, Cs, T, r, ws, ws_bytes, stream, 0);
 }
 
 extern "C" size_t rgc_project_workspace_size(int64_t T, int64_t k, int64_t r) {
@@ -865,4 +896,30 @@ extern "C" rgc_status_t rgc_accumulate(const uint16_t* D, int64_t ldd, const uin
                                        int64_t d, int64_t r, void* ws, size_t ws_bytes, void* stream) {
   if (T < 0 || d <= 0 || r <= 0) return RGC_ERR_SHAPE;
   return rgc_accumulate_batch(1, &D, &ldd, &d, &XP, &C, T, r, ws, ws_bytes, stream);
+}
+
+// Test hooks: the batched contractions with the workgroup count given by the
+// caller (> 0) instead of chosen from the shapes, so that tests can force
+// ranges of whole tiles that cross item boundaries.
+extern "C" size_t rgc_test_sketch_workspace_size(int contraction, int64_t workgroups, int64_t n,
+                                                 const int64_t* widths, int64_t T, int64_t r) {
+  if (workgroups <= 0) return 0;
+  return contraction == 0 ? project_ws_impl(n, widths, T, r, workgroups)
+                          : accumulate_ws_impl(n, widths, T, r, workgroups);
+}
+
+extern "C" rgc_status_t rgc_test_project_batch_wgs(int64_t workgroups, int64_t n, const uint16_t* const* Xs,
+                                                   const int64_t* ldxs, const int64_t* ks,
+                                                   const uint16_t* const* Ps, uint16_t* const* XPs, int64_t T,
+                                                   int64_t r, void* ws, size_t ws_bytes, void* stream) {
+  if (workgroups <= 0) return RGC_ERR_SHAPE;
+  return project_batch_impl(n, Xs, ldxs, ks, Ps, XPs, T, r, ws, ws_bytes, stream, workgroups);
+}
+
+extern "C" rgc_status_t rgc_test_accumulate_batch_wgs(int64_t workgroups, int64_t n, const uint16_t* const* Ds,
+                                                      const int64_t* ldds, const int64_t* ds,
+                                                      const uint16_t* const* XPs, float* const* Cs, int64_t T,
+                                                      int64_t r, void* ws, size_t ws_bytes, void* stream) {
+  if (workgroups <= 0) return RGC_ERR_SHAPE;
+  return accumulate_batch_impl(n, Ds, ldds, ds, XPs, Cs, T, r, ws, ws_bytes, stream, workgroups);
 }

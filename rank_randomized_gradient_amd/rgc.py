@@ -80,6 +80,13 @@ SIGNATURES = {
     "rgc_test_philox": (ctypes.c_int, [_u64, _i64, _vp, _vp, _vp]),
     "rgc_test_stochastic_round": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _u64, _vp]),
     "rgc_test_reconstruct": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "rgc_test_sketch_workspace_size": (_sz, [ctypes.c_int, _i64, _i64, ctypes.POINTER(_i64), _i64, _i64]),
+    "rgc_test_project_batch_wgs": (ctypes.c_int, [_i64, _i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64),
+                                                  ctypes.POINTER(_i64), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                                  _i64, _i64, _vp, _sz, _vp]),
+    "rgc_test_accumulate_batch_wgs": (ctypes.c_int, [_i64, _i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64),
+                                                     ctypes.POINTER(_i64), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                                     _i64, _i64, _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -536,3 +543,40 @@ def rgc_test_reconstruct(C: torch.Tensor, P: torch.Tensor) -> torch.Tensor:
     H = torch.empty((d, k), dtype=torch.float32, device=dev)
     _check(lib.rgc_test_reconstruct(C.data_ptr(), P.data_ptr(), H.data_ptr(), d, k, r, _stream(dev)))
     return H
+
+
+def rgc_test_project_batch_wgs(workgroups: int, Xs, Ps):
+    """rgc_project_batch with a caller-given workgroup count (test hook)."""
+    lib = load_library()
+    n = len(Xs)
+    dev = _need_gpu(*Xs, *Ps)
+    T, r = Xs[0].shape[0], Ps[0].shape[1]
+    ldxs = [_rows(x, torch.bfloat16, "X") for x in Xs]
+    ks = [x.shape[1] for x in Xs]
+    for p in Ps:
+        _dense(p, torch.bfloat16, "P")
+    outs = [torch.empty((T, r), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    nbytes = lib.rgc_test_sketch_workspace_size(0, workgroups, n, _i64s(ks), T, r)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.rgc_test_project_batch_wgs(workgroups, n, _ptrs(Xs), _i64s(ldxs), _i64s(ks), _ptrs(Ps), _ptrs(outs),
+                                          T, r, ws.data_ptr(), ws.numel(), _stream(dev)))
+    return outs
+
+
+def rgc_test_accumulate_batch_wgs(workgroups: int, Ds, XPs, Cs):
+    """rgc_accumulate_batch with a caller-given workgroup count (test hook)."""
+    lib = load_library()
+    n = len(Ds)
+    dev = _need_gpu(*Ds, *XPs, *Cs)
+    T, r = Ds[0].shape[0], XPs[0].shape[1]
+    ldds = [_rows(d, torch.bfloat16, "D") for d in Ds]
+    ds = [d.shape[1] for d in Ds]
+    for x in XPs:
+        _dense(x, torch.bfloat16, "XP")
+    for c in Cs:
+        _dense(c, torch.float32, "C")
+    nbytes = lib.rgc_test_sketch_workspace_size(1, workgroups, n, _i64s(ds), T, r)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib.rgc_test_accumulate_batch_wgs(workgroups, n, _ptrs(Ds), _i64s(ldds), _i64s(ds), _ptrs(XPs),
+                                             _ptrs(Cs), T, r, ws.data_ptr(), ws.numel(), _stream(dev)))
+    return Cs

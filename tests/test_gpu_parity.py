@@ -236,21 +236,21 @@ def test_accumulate_batch_ranges_aligned_to_tiles(dev):
 
 
 @pytest.mark.parametrize("wgs", [1, 3])
-def test_sketch_batches_with_whole_tiles_per_workgroup(dev, monkeypatch, wgs):
-    """Few workgroups: each range holds whole tiles, ends in later items, and
-    the first segment's sums are stored after the last one (ragged d and T)."""
-    monkeypatch.setenv("RGC_SKETCH_WGS", str(wgs))
+def test_sketch_batches_with_whole_tiles_per_workgroup(dev, wgs):
+    """Few workgroups (forced through the test hooks): each range holds whole
+    tiles, ends in later items, and the first segment's sums are stored after
+    the last one (ragged d and T)."""
     T, r = 300, 64
     ds = [512, 8, 264]
     dds = [synth.normal_bf16((T, d), 1e-3, seed=80 + i) for i, d in enumerate(ds)]
     xps = [synth.normal_bf16((T, r), 3.0, seed=90 + i) for i in range(len(ds))]
     c0s = [synth.normal_f32((d, r), 1e-3, seed=95 + i) for i, d in enumerate(ds)]
     cs = [c.clone().to(dev) for c in c0s]
-    rgc.rgc_accumulate_batch([d.to(dev) for d in dds], [x.to(dev) for x in xps], cs)
+    rgc.rgc_test_accumulate_batch_wgs(wgs, [d.to(dev) for d in dds], [x.to(dev) for x in xps], cs)
     ks = [512, 72, 264]  # r <= k; 72 ends in a partial 32-wide step
     xs = [synth.normal_bf16((T, k), 1.0, seed=100 + i) for i, k in enumerate(ks)]
     ps = [synth.normal_bf16((k, r), 1.0, seed=110 + i) for i, k in enumerate(ks)]
-    outs = rgc.rgc_project_batch([x.to(dev) for x in xs], [p.to(dev) for p in ps])
+    outs = rgc.rgc_test_project_batch_wgs(wgs, [x.to(dev) for x in xs], [p.to(dev) for p in ps])
     _sync()
     for dd, xp, c0, c in zip(dds, xps, c0s, cs):
         assert rel_frobenius(c.cpu().numpy(), orc.accumulate(c0.numpy(), bits(dd), bits(xp))) < 1e-5
