@@ -10,8 +10,8 @@
 // Gaussian k x r matrix. Q is computed by CholeskyQR2 in fp64, for a batch of
 // matrices of one rank at once (each launch covers every matrix, so the
 // latency-bound steps are paid once per batch, not once per matrix):
-//   fill     A = Box-Muller normals from Philox
-//   gram     partial Grams of A over 64-row (r = 128: 128-row) blocks
+//   gram     A = Box-Muller normals from Philox (stored), partial Grams of A
+//            over 64-row blocks
 //   reduce   G1 = A^T A (partials summed in block order)
 //   factor   U1 = chol(G1)^-1
 //   gram     Q1 = A U1 (stored), partial Grams of Q1, and P = bf16(fp32(
@@ -25,6 +25,9 @@
 // Cholesky factors have a positive diagonal, so Q is the unique factor with
 // the standard sign correction; the second pass restores orthogonality to
 // fp64 accuracy. Every reduction has a fixed order, so P is bit-reproducible.
+// A Gram matrix that is not numerically positive definite (it does not happen
+// for Gaussian matrices with k >= r in practice) makes its factor all NaN, so
+// the P of that matrix is all NaN and an update computed from it is skipped.
 #include <math.h>
 #include <string.h>
 
@@ -63,15 +66,9 @@ __global__ void rademacher_kernel(uint16_t* __restrict__ P, int64_t k, int r, ui
 // CholeskyQR2, batched over up to kQrMaxBatch matrices of one rank R <= 128.
 // ---------------------------------------------------------------------------
 constexpr int kQrMaxBatch = 16;
-constexpr bool kQrBlockMfma = true;
-// Rows per Gram / multiply workgroup: 64 (the MFMA block steps stage only
-// U's upper tiles, so r = 128 fits 64 staged rows beside them; the VALU
-// steps, kept for kQrBlockMfma = false, stage all of U and take 128 rows at
-// r = 128 so that a block's workgroups stay within one round).
-constexpr int qr_block_rows(int64_t r) { return kQrBlockMfma || r <= 64 ? 64 : 128; }
-// r a multiple of 16 (every QR rank): block steps on fp64 MFMA (qr_block_mfma_kernel).
+// Rows per Gram / multiply workgroup: four row tiles of 16, one per wave.
+constexpr int kQrBlockRows = 64;
 
-constexpr int kQrSub = 16;         // rows staged in LDS at a time
 constexpr double kTwoPi = 6.283185307179586;  // 2*pi rounded to double
 // When every entry of Q1^T Q1 - I is below this, Q1 (U2 = I - S, |S| below it
 // too) already equals the second pass's Q to ~1e-14, far inside the bf16
@@ -92,7 +89,6 @@ struct QrBatch {
   // status[m]: [0], [1] = factorization failed in pass 1, 2; [2] = the first
   // pass is already orthonormal to kQrFinalTol, so P from it is final
   uint32_t* status[kQrMaxBatch];
-  int fill_begin[kQrMaxBatch + 1];   // workgroup prefix of the Gaussian fill
   int block_begin[kQrMaxBatch + 1];  // workgroup prefix of the row blocks
 };
 
@@ -118,167 +114,10 @@ __device__ __forceinline__ void gaussian4(uint64_t seed, int64_t i, int q, doubl
   }
 }
 
-// A = Gaussian, one thread per (row, 4 columns).
-template <int R>
-__global__ __launch_bounds__(256) void gauss_fill_kernel(QrBatch b) {
-  const int m = batch_item(b.fill_begin, b.n, blockIdx.x);
-  const int64_t idx = (int64_t)(blockIdx.x - b.fill_begin[m]) * blockDim.x + threadIdx.x;
-  if (idx >= b.k[m] * (R / 4)) return;
-  const int64_t i = idx / (R / 4);
-  const int q = (int)(idx % (R / 4));
-  double z[4];
-  gaussian4(b.seed[m], i, q, z);
-  double* dst = b.A[m] + i * R + 4 * q;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) dst[e] = z[e];
-}
-
-// Rows staged in LDS at a time: a whole 64-row block when U (R x R) and the
-// rows fit together, else 16 (R = 128).
-template <int R>
-struct QrTile {
-  static constexpr int SUB = R <= 64 ? qr_block_rows(R) : 16;
-};
-
-// One row block of one matrix, staged through LDS (all at once when it fits).
-//   MODE 0: partial Gram of A.
-//   MODE 1: Q1 = A U1 (stored, with the candidate P from it), then partial Gram of Q1.
+// The three block steps on fp64 MFMA (v_mfma_f64_16x16x4_f64):
+//   MODE 0: draw the Gaussian rows of the block (into A and LDS), partial Gram of A;
+//   MODE 1: Q1 = A U1 (stored, with the candidate P from it), partial Gram of Q1;
 //   MODE 2: P = bf16(fp32(scale * Q1 U2)).
-// Thread (tx, ty) (16 x 16) owns Gram entries (ty + 16a, tx + 16c) and, in the
-// multiply, rows ty + 16i of the staged rows at columns tx + 16v. U is dense
-// with zeros below the diagonal, so the multiply needs no triangular test.
-template <int R, int MODE>
-__global__ __launch_bounds__(256) void qr_block_kernel(QrBatch b) {
-  constexpr int TU = R / 16;
-  constexpr int SUB = QrTile<R>::SUB;
-  constexpr int RI = SUB / 16;  // staged rows per thread in the multiply
-  __shared__ double rows[SUB][R + 1];  // +1: rows read by different lanes sit on different banks
-  __shared__ double u[MODE == 0 ? 1 : R][MODE == 0 ? 1 : R];
-  const int m = batch_item(b.block_begin, b.n, blockIdx.x);
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const int64_t k = b.k[m];
-  constexpr int64_t BR = qr_block_rows(R);
-  const int64_t rbeg = (int64_t)(blockIdx.x - b.block_begin[m]) * BR;
-  const int64_t rend = rbeg + BR < k ? rbeg + BR : k;
-  const double* src = MODE == 2 ? b.Q1[m] : b.A[m];
-  if constexpr (MODE == 2) {
-    if (b.status[m][2] != 0u) return;  // P from the first pass is final
-  }
-  if constexpr (MODE != 0) {
-    // R*R/256 loads per thread, all issued before the first LDS store
-    const double* U = MODE == 1 ? b.U1[m] : b.U2[m];
-    constexpr int NU = R * R / 256;
-    double uv[NU];
-#pragma unroll
-    for (int e = 0; e < NU; ++e) uv[e] = U[threadIdx.x + 256 * e];
-#pragma unroll
-    for (int e = 0; e < NU; ++e) {
-      const int t = threadIdx.x + 256 * e;
-      u[t / R][t % R] = uv[e];
-    }
-  }
-  double acc[TU][TU];
-#pragma unroll
-  for (int a = 0; a < TU; ++a)
-#pragma unroll
-    for (int c = 0; c < TU; ++c) acc[a][c] = 0.0;
-
-  for (int64_t r0 = rbeg; r0 < rend; r0 += SUB) {
-    __syncthreads();
-    {
-      // SUB*R/256 loads per thread (rows clamped to a valid one, then zeroed),
-      // all issued before the first LDS store
-      constexpr int NS = SUB * R / 256;
-      double sv[NS];
-#pragma unroll
-      for (int e = 0; e < NS; ++e) {
-        const int t = threadIdx.x + 256 * e;
-        const int64_t row = r0 + t / R;
-        sv[e] = src[(row < rend ? row : rend - 1) * R + t % R];
-      }
-#pragma unroll
-      for (int e = 0; e < NS; ++e) {
-        const int t = threadIdx.x + 256 * e;
-        rows[t / R][t % R] = r0 + t / R < rend ? sv[e] : 0.0;
-      }
-    }
-    __syncthreads();
-    if constexpr (MODE != 0) {
-      double y[RI][TU];
-#pragma unroll
-      for (int i = 0; i < RI; ++i)
-#pragma unroll
-        for (int v = 0; v < TU; ++v) y[i][v] = 0.0;
-#pragma unroll 2
-      for (int a = 0; a < R; ++a) {
-        double x[RI], w[TU];
-#pragma unroll
-        for (int i = 0; i < RI; ++i) x[i] = rows[ty + 16 * i][a];
-#pragma unroll
-        for (int v = 0; v < TU; ++v) w[v] = u[a][tx + 16 * v];
-#pragma unroll
-        for (int i = 0; i < RI; ++i)
-#pragma unroll
-          for (int v = 0; v < TU; ++v) y[i][v] += x[i] * w[v];
-      }
-      if constexpr (MODE == 2) {
-#pragma unroll
-        for (int i = 0; i < RI; ++i) {
-          const int64_t row = r0 + ty + 16 * i;
-          if (row >= rend) continue;
-#pragma unroll
-          for (int v = 0; v < TU; ++v)
-            b.P[m][row * R + tx + 16 * v] = (uint16_t)f32_to_bf16_rne((float)(b.scale[m] * y[i][v]));
-        }
-        continue;
-      } else {
-#pragma unroll
-        for (int i = 0; i < RI; ++i) {
-          const int64_t row = r0 + ty + 16 * i;
-          if (row >= rend) continue;
-#pragma unroll
-          for (int v = 0; v < TU; ++v) {
-            b.Q1[m][row * R + tx + 16 * v] = y[i][v];
-            b.P[m][row * R + tx + 16 * v] = (uint16_t)f32_to_bf16_rne((float)(b.scale[m] * y[i][v]));
-          }
-        }
-        __syncthreads();  // everyone is done reading the staged rows
-#pragma unroll
-        for (int i = 0; i < RI; ++i) {
-          const bool in = r0 + ty + 16 * i < rend;
-#pragma unroll
-          for (int v = 0; v < TU; ++v) rows[ty + 16 * i][tx + 16 * v] = in ? y[i][v] : 0.0;
-        }
-        __syncthreads();
-      }
-    }
-    if constexpr (MODE != 2) {
-      const int nr = (int)(rend - r0 < SUB ? rend - r0 : SUB);
-#pragma unroll 4
-      for (int lr = 0; lr < nr; ++lr) {
-        double x[TU], w[TU];
-#pragma unroll
-        for (int a = 0; a < TU; ++a) x[a] = rows[lr][ty + 16 * a];
-#pragma unroll
-        for (int c = 0; c < TU; ++c) w[c] = rows[lr][tx + 16 * c];
-#pragma unroll
-        for (int a = 0; a < TU; ++a)
-#pragma unroll
-          for (int c = 0; c < TU; ++c) acc[a][c] += x[a] * w[c];
-      }
-    }
-  }
-  if constexpr (MODE != 2) {
-    double* out = b.part[m] + (int64_t)(blockIdx.x - b.block_begin[m]) * R * R;
-#pragma unroll
-    for (int a = 0; a < TU; ++a)
-#pragma unroll
-      for (int c = 0; c < TU; ++c) out[(ty + 16 * a) * R + tx + 16 * c] = acc[a][c];
-  }
-}
-
-// The same three block steps on fp64 MFMA (v_mfma_f64_16x16x4_f64),
-// the first one also drawing the Gaussian rows of its block (no fill launch):
 // operands come straight from the staged rows, so the products no longer
 // wait on one LDS read per multiply-add. A 16 x 16 x 4 product takes, in lane
 // l, A[l % 16][l / 16] and B[l / 16][l % 16] and returns D[4 i + l / 16][l % 16]
@@ -297,7 +136,7 @@ __host__ __device__ constexpr int utile_slot(int rt, int tc) { return tc * (tc +
 template <int R, int MODE>
 __global__ __launch_bounds__(256) void qr_block_mfma_kernel(QrBatch b) {
   static_assert(R <= 128 && R % 16 == 0, "r <= 128, multiple of 16");
-  constexpr int BR = qr_block_rows(R);  // 64
+  constexpr int BR = kQrBlockRows;
   static_assert(BR == 64, "four row tiles, one per wave");
   constexpr int NT = R / 16;
   constexpr int LD = R + 1;             // padded row pitch (doubles)
@@ -314,8 +153,8 @@ __global__ __launch_bounds__(256) void qr_block_mfma_kernel(QrBatch b) {
   }
   const double* src = MODE == 2 ? b.Q1[m] : b.A[m];
   if constexpr (MODE == 0) {
-    // The Gaussian rows are drawn here (as the fill kernel draws them: four
-    // columns per Philox call) into LDS and into A for the first multiply.
+    // The Gaussian rows are drawn here (four columns per Philox call) into
+    // LDS and into A for the first multiply.
     constexpr int NQ = BR * (R / 4) / 256;
 #pragma unroll
     for (int e = 0; e < NQ; ++e) {
@@ -560,13 +399,22 @@ __global__ __launch_bounds__(QrFactorShape<R>::THREADS) void qr_factor_kernel(Qr
       const int l = ty + NT * i, c = tx + NT * j;
       if (l < R && c == l) diag[l] = a[i][j];
     }
-  __syncthreads();
+  // A pivot that is not positive and finite means G is not numerically
+  // positive definite: the whole factor is then NaN (and so is P).
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < TT; ++i)
+#pragma unroll
+    for (int j = 0; j < TT; ++j) {
+      const int l = ty + NT * i, c = tx + NT * j;
+      if (l < R && c == l) bad = bad || !(a[i][j] > 0.0 && isfinite(a[i][j]));
+    }
+  const bool failed = __syncthreads_or(bad) != 0;
   if (tid == 0) {
-    bool ok = true;
-    for (int c = 0; c < R; ++c) ok = ok && (diag[c] > 0.0) && isfinite(diag[c]);
-    b.status[m][second] = ok ? 0u : 1u;
+    b.status[m][second] = failed ? 1u : 0u;
     if (second) b.status[m][2] = 0u;
   }
+  const double nan = __builtin_nan("");
 #pragma unroll
   for (int i = 0; i < TT; ++i)
 #pragma unroll
@@ -575,10 +423,10 @@ __global__ __launch_bounds__(QrFactorShape<R>::THREADS) void qr_factor_kernel(Qr
       if (l >= R || c >= R || c > l) continue;
       const double rs = 1.0 / sqrt(diag[l]);
       if (c == l) {
-        U[l * R + l] = rs;
+        U[l * R + l] = failed ? nan : rs;
       } else {
-        U[c * R + l] = a[i][j] * rs;
-        U[l * R + c] = 0.0;
+        U[c * R + l] = failed ? nan : a[i][j] * rs;
+        U[l * R + c] = failed ? nan : 0.0;
       }
     }
 }
@@ -592,7 +440,7 @@ struct QrItemLayout {
 
 QrItemLayout qr_item_layout(int64_t k, int64_t r) {
   QrItemLayout l;
-  l.blocks = (int)((k + qr_block_rows(r) - 1) / qr_block_rows(r));
+  l.blocks = (int)((k + kQrBlockRows - 1) / kQrBlockRows);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -619,7 +467,6 @@ rgc_status_t qr_launch(int n, const uint64_t* seeds, const int64_t* ks, uint16_t
   // the n summed Gram matrices first, then each item's buffers
   double* G_all = reinterpret_cast<double*>(base);
   size_t off = qr_gram_bytes(n, R);
-  b.fill_begin[0] = 0;
   b.block_begin[0] = 0;
   for (int m = 0; m < n; ++m) {
     const QrItemLayout l = qr_item_layout(ks[m], R);
@@ -633,30 +480,17 @@ rgc_status_t qr_launch(int n, const uint64_t* seeds, const int64_t* ks, uint16_t
     b.U1[m] = reinterpret_cast<double*>(base + off + l.u1);
     b.U2[m] = reinterpret_cast<double*>(base + off + l.u2);
     b.status[m] = reinterpret_cast<uint32_t*>(base + off + l.status);
-    b.fill_begin[m + 1] = b.fill_begin[m] + (int)((ks[m] * (R / 4) + 255) / 256);
     b.block_begin[m + 1] = b.block_begin[m] + l.blocks;
     off += l.total;
   }
-  // (r <= 64: the first block step draws the Gaussian itself)
-  if constexpr (!(R % 16 == 0 && kQrBlockMfma))
-    hipLaunchKernelGGL((gauss_fill_kernel<R>), dim3(b.fill_begin[n]), dim3(256), 0, s, b);
-  if constexpr (R % 16 == 0 && kQrBlockMfma)
-    hipLaunchKernelGGL((qr_block_mfma_kernel<R, 0>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
-  else
-    hipLaunchKernelGGL((qr_block_kernel<R, 0>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   const dim3 red_grid((unsigned)((R * R + 255) / 256), (unsigned)n);
+  hipLaunchKernelGGL((qr_block_mfma_kernel<R, 0>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
   hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(QrFactorShape<R>::THREADS), 0, s, b, G_all, 0);
-  if constexpr (R % 16 == 0 && kQrBlockMfma)
-    hipLaunchKernelGGL((qr_block_mfma_kernel<R, 1>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
-  else
-    hipLaunchKernelGGL((qr_block_kernel<R, 1>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
+  hipLaunchKernelGGL((qr_block_mfma_kernel<R, 1>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
   hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(QrFactorShape<R>::THREADS), 0, s, b, G_all, 1);
-  if constexpr (R % 16 == 0 && kQrBlockMfma)
-    hipLaunchKernelGGL((qr_block_mfma_kernel<R, 2>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
-  else
-    hipLaunchKernelGGL((qr_block_kernel<R, 2>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
+  hipLaunchKernelGGL((qr_block_mfma_kernel<R, 2>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
