@@ -59,9 +59,13 @@ class SketchedLinear(torch.nn.Module):
 
     carry_norm=True: the normalized update hands ||W||^2 of the weights it
     writes to the next one (rgc_apply_carried), so each later update reads W
-    once. The value is refreshed from W after a fixed-step update and after
-    invalidate_weight_norm(), which a caller that changes the weights by other
-    means must call.
+    once. The value is streamed from W again (fresh) after a fixed-step
+    update, after load_state_dict, whenever the weight's version counter moved
+    since the last carried update (any torch in-place op on the Parameter,
+    e.g. `with torch.no_grad(): layer.weight.copy_(...)`), and after
+    invalidate_weight_norm(). Writes that bypass the version counter
+    (through `weight.data`, or raw pointers) are not seen: a caller making
+    them must call invalidate_weight_norm().
     """
 
     def __init__(self, in_features: int, out_features: int, rank: int, kind: str = "qr", device=None,
@@ -82,9 +86,18 @@ class SketchedLinear(torch.nn.Module):
         self.carry_norm = carry_norm
         self.register_buffer("weight_norm2", torch.zeros(1, dtype=torch.float64, device=device))
         self._norm_fresh = True  # weight_norm2 does not hold ||W||^2 yet
+        self._norm_version = None  # the weight's version counter when weight_norm2 was last written
 
     def invalidate_weight_norm(self) -> None:
         """The weights changed outside apply_update: the next update streams ||W|| again."""
+        self._norm_fresh = True
+
+    def _norm_is_stale(self) -> bool:
+        return self._norm_fresh or self._norm_version != self.weight._version
+
+    def _load_from_state_dict(self, *args, **kwargs):
+        # the loaded weights (and a loaded weight_norm2) need not match each other
+        super()._load_from_state_dict(*args, **kwargs)
         self._norm_fresh = True
 
     def begin_update(self, proj_seed: int) -> None:
@@ -106,9 +119,11 @@ class SketchedLinear(torch.nn.Module):
             raise rgc.RgcError("give exactly one of tau (normalized update) or alpha (fixed step)")
         w = self.weight.data
         if tau is not None and self.carry_norm:
-            rgc.rgc_apply_carried(w, self.sketch, self.proj, tau, seed, self.weight_norm2, fresh=self._norm_fresh,
+            rgc.rgc_apply_carried(w, self.sketch, self.proj, tau, seed, self.weight_norm2, fresh=self._norm_is_stale(),
                                   stats=stats, workspace=self.workspace)
+            # the library writes W through its pointer, which leaves the version counter as it is
             self._norm_fresh = False
+            self._norm_version = self.weight._version
         elif tau is not None:
             rgc.rgc_apply(w, self.sketch, self.proj, tau, seed, stats=stats, workspace=self.workspace)
         else:

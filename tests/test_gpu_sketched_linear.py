@@ -114,3 +114,41 @@ def test_sketched_linear_carried_norm_matches_plain(dev):
                 carry.invalidate_weight_norm()
                 continue
         assert torch.equal(plain.weight.data, carry.weight.data), f"update {u}"
+
+
+@pytest.mark.parametrize("how", ["copy", "load_state_dict"])
+def test_sketched_linear_carried_norm_sees_weight_changes(dev, how):
+    """Weights replaced between carried updates through the Parameter (an
+    in-place copy, or load_state_dict): the next update streams ||W|| again
+    without an explicit invalidate_weight_norm(), so it equals the plain
+    layer's update bit for bit (same ||W||, same s, same weights)."""
+    d, k, r, mb = 256, 512, 16, 256
+    w = synth.normal_bf16((d, k), 0.02, seed=3002)
+    w2 = synth.normal_bf16((d, k), 0.05, seed=3003).to(dev)
+    plain = SketchedLinear(k, d, r, kind="qr", device=dev, weight=w.clone())
+    carry = SketchedLinear(k, d, r, kind="qr", device=dev, weight=w.clone(), carry_norm=True)
+    for u in range(2):
+        x = synth.normal_bf16((mb, k), 1.0, seed=3100 + u).to(dev)
+        dy = synth.normal_bf16((mb, d), 0.1, seed=3200 + u).to(dev)
+        stats = []
+        for layer in (plain, carry):
+            layer.begin_update(500 + u)
+            layer(x).backward(dy)
+            st = torch.zeros(4, device=dev)
+            layer.apply_update(600 + u, tau=1e-3, stats=st)
+            stats.append(st)
+        torch.cuda.synchronize()
+        if u == 1:
+            assert torch.equal(stats[0], stats[1])
+            assert torch.equal(plain.weight.data, carry.weight.data)
+        # replace both layers' weights by the same new values
+        with torch.no_grad():
+            plain.weight.copy_(w2)
+        if how == "copy":
+            with torch.no_grad():
+                carry.weight.copy_(w2)
+        else:
+            sd = carry.state_dict()
+            sd["weight"] = w2.clone()
+            sd["weight_norm2"] = torch.zeros(1, dtype=torch.float64, device=dev)  # a norm that does not match
+            carry.load_state_dict(sd)
