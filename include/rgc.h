@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define RGC_ABI_VERSION 3
+#define RGC_ABI_VERSION 4
 
 typedef enum {
   RGC_OK = 0,
@@ -71,7 +71,8 @@ typedef enum {
   RGC_ERR_ALIGN = 4,       /* a base pointer or leading dimension is misaligned */
   RGC_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the query */
   RGC_ERR_HIP = 6,         /* a kernel launch failed */
-  RGC_ERR_VALUE = 7        /* a scalar argument is not finite */
+  RGC_ERR_VALUE = 7,       /* a scalar argument is not finite */
+  RGC_ERR_SCRATCH = 8      /* rgc_apply_noalloc: more scratch needed than its static buffer holds */
 } rgc_status_t;
 
 typedef enum {
@@ -193,6 +194,27 @@ rgc_status_t rgc_apply_batch(int64_t n, uint16_t* const* Ws, const int64_t* ldws
                              const uint16_t* const* Ps, const int64_t* ds, const int64_t* ks, int64_t r,
                              float tau, const uint64_t* seeds, float* const* stats, void* ws,
                              size_t ws_bytes, void* stream);
+
+/* ---- The normalized update without a workspace ---------------------------
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. Computes
+ * exactly what rgc_apply computes (same kernels, same partition, same bits),
+ * with rgc_apply's workspace taken from a static device buffer of
+ * RGC_NOALLOC_SCRATCH_BYTES bytes that the library holds on each device it
+ * runs on, for as long as it stays loaded. The call allocates nothing.
+ * - Calls whose workspace (rgc_apply_workspace_size(d, k, r)) would exceed
+ *   that buffer return RGC_ERR_SCRATCH before anything is enqueued; with
+ *   8 MiB this holds e.g. every matrix up to 32768 x 32768 at r <= 128.
+ * - Every call on one device shares the buffer: calls that may overlap on one
+ *   device (different streams without ordering, or concurrent host threads)
+ *   race and must not be made; calls ordered on one stream are fine.
+ * - `stream` must belong to the current device (RGC_ERR_UNSUPPORTED
+ *   otherwise); the first call on a device looks the buffer's address up.
+ * Arguments, stats and the other errors as rgc_apply. */
+#define RGC_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+rgc_status_t rgc_apply_noalloc(uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d,
+                               int64_t k, int64_t r, float tau, uint64_t seed, float* stats, void* stream);
 
 /* ---- The normalized update with a carried ||W|| --------------------------
  *

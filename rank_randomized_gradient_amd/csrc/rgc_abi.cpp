@@ -17,6 +17,7 @@ extern "C" const char* rgc_status_string(rgc_status_t status) {
     case RGC_ERR_WORKSPACE: return "workspace missing or too small";
     case RGC_ERR_HIP: return "HIP kernel launch failed";
     case RGC_ERR_VALUE: return "a scalar argument is not finite";
+    case RGC_ERR_SCRATCH: return "the call needs more scratch than the library's static buffer holds";
   }
   return "unknown status";
 }

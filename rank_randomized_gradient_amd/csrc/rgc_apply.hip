@@ -34,6 +34,7 @@
 // 16 consecutive columns jb + 16g .. +15 of its row in each N-tile, i.e. two
 // 16-byte reads of W and two Philox calls (8 columns each).
 #include <cmath>
+#include <mutex>
 
 #include "rgc_internal.hpp"
 
@@ -1235,4 +1236,56 @@ extern "C" rgc_status_t rgc_test_philox(uint64_t seed, int64_t n, const uint32_t
   hipLaunchKernelGGL(philox_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
                      seed, n, ctr, out);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// The normalized update for callers that cannot allocate (code under HIP
+// graph capture, tight serving loops, harnesses that forbid allocation):
+// rgc_apply with its workspace in a static device array instead of a caller
+// buffer. Each device holds its own copy of the array (for as long as the
+// library stays loaded); every call on a device shares it, so such calls must
+// not overlap on one device. The workspace needs no initialisation (every
+// partial is written before it is read), so nothing is cleared between calls.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_addr[kMaxScratchDevices];  // device address of `scratch` on each device, looked up once
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device with the device current; the stream must belong to it.
+rgc_status_t scratch_for(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return RGC_ERR_HIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return RGC_ERR_HIP;
+    if (sdev != dev) return RGC_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RGC_ERR_HIP;
+    scratch_addr[dev] = p;
+  }
+  *out = scratch_addr[dev];
+  return RGC_OK;
+}
+
+}  // namespace
+
+extern "C" rgc_status_t rgc_apply_noalloc(uint16_t* W, int64_t ldw, const float* C, const uint16_t* P, int64_t d,
+                                          int64_t k, int64_t r, float tau, uint64_t seed, float* stats,
+                                          void* stream) {
+  rgc_status_t st = apply_validate(W, ldw, C, P, d, k, r, false, 0.f, stats);
+  if (st != RGC_OK) return st;
+  const size_t need = rgc_apply_workspace_size(d, k, r);
+  if (need == 0 || need > kNoAllocScratchBytes) return RGC_ERR_SCRATCH;
+  void* ptr = nullptr;
+  st = scratch_for(static_cast<hipStream_t>(stream), &ptr);
+  if (st != RGC_OK) return st;
+  return rgc_apply(W, ldw, C, P, d, k, r, tau, seed, stats, ptr, kNoAllocScratchBytes, stream);
 }

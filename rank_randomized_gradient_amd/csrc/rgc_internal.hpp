@@ -24,6 +24,9 @@ constexpr int64_t kMaxTiledDim = 65536;
 // per-lane byte offsets, so 256 * 2^23 * 2 bytes must fit in 32 bits.
 constexpr int64_t kMaxLeadingDim = int64_t(1) << 23;
 
+// Bytes of the static device scratch behind rgc_apply_noalloc.
+constexpr size_t kNoAllocScratchBytes = RGC_NOALLOC_SCRATCH_BYTES;
+
 inline bool rank_supported(int64_t r) {
   return r == 16 || r == 32 || r == 48 || r == 64 || r == 128 || r == 192 || r == 256;
 }

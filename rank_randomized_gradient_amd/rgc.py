@@ -65,6 +65,7 @@ SIGNATURES = {
                                        ctypes.POINTER(_u64), ctypes.POINTER(_vp), _vp, _sz, _vp]),
     "rgc_apply": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _f32, _u64, _vp, _vp, _sz, _vp]),
     "rgc_apply_scaled": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _f32, _u64, _vp]),
+    "rgc_apply_noalloc": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _f32, _u64, _vp, _vp]),
     "rgc_apply_scaled_batch": (ctypes.c_int, [_i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_vp),
                                               ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i64,
                                               ctypes.POINTER(_f32), ctypes.POINTER(_u64), _vp]),
@@ -336,6 +337,31 @@ def rgc_apply(W: torch.Tensor, C: torch.Tensor, P: torch.Tensor, tau: float, see
     wp, wn = ws.get(lib.rgc_apply_workspace_size(d, k, r))
     _check(lib.rgc_apply(W.data_ptr(), ldw, C.data_ptr(), P.data_ptr(), d, k, r, float(tau),
                          seed & 0xFFFFFFFFFFFFFFFF, sp, wp, wn, _stream(dev)))
+    return W
+
+
+def rgc_apply_noalloc(W: torch.Tensor, C: torch.Tensor, P: torch.Tensor, tau: float, seed: int,
+                      stats: torch.Tensor | None = None) -> torch.Tensor:
+    """rgc_apply without a workspace: the library's static device scratch is
+    used instead (no device allocation on any path of this call)."""
+    lib = load_library()
+    dev = _need_gpu(W, C, P)
+    ldw = _rows(W, torch.bfloat16, "W")
+    _dense(C, torch.float32, "C")
+    _dense(P, torch.bfloat16, "P")
+    d, k = W.shape
+    r = C.shape[1]
+    if tuple(C.shape) != (d, r) or tuple(P.shape) != (k, r):
+        raise RgcError("shapes must be W: d x k, C: d x r, P: k x r")
+    sp = None
+    if stats is not None:
+        _need_gpu(stats)
+        _dense(stats, torch.float32, "stats")
+        if stats.numel() < 4:
+            raise RgcError("stats needs 4 floats")
+        sp = stats.data_ptr()
+    _check(lib.rgc_apply_noalloc(W.data_ptr(), ldw, C.data_ptr(), P.data_ptr(), d, k, r, float(tau),
+                                 seed & 0xFFFFFFFFFFFFFFFF, sp, _stream(dev)))
     return W
 
 

@@ -44,7 +44,7 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         assert b"unknown" not in lib.rgc_status_string(s)
     assert b"unknown" in lib.rgc_status_string(99)
 
@@ -255,3 +255,16 @@ def test_binding_refuses_cpu_tensors():
     p = torch.zeros(64, 16, dtype=torch.bfloat16)
     with pytest.raises(rgc.RgcError):
         rgc.rgc_project(x, p)
+
+
+def test_noalloc_rejects_oversized_calls_before_any_launch(lib):
+    """rgc_apply_noalloc: a call whose workspace exceeds the static scratch
+    returns RGC_ERR_SCRATCH on the host (no HIP call is made before it)."""
+    SCRATCH = 8
+    assert lib.rgc_apply_workspace_size(65536, 65536, 128) > (8 << 20)
+    assert lib.rgc_apply_noalloc(FAKE, 65536, FAKE, FAKE, 65536, 65536, 128, 1e-3, 1, None, None) == SCRATCH
+    assert b"scratch" in lib.rgc_status_string(SCRATCH)
+    # the ordinary argument errors come first, as in rgc_apply
+    assert lib.rgc_apply_noalloc(FAKE, 63, FAKE, FAKE, 16, 64, 16, 1e-3, 1, None, None) == SHAPE
+    assert lib.rgc_apply_noalloc(None, 64, FAKE, FAKE, 16, 64, 16, 1e-3, 1, None, None) == NULL
+    assert lib.rgc_apply_noalloc(FAKE, 64, FAKE, FAKE, 16, 64, 40, 1e-3, 1, None, None) == UNSUP
