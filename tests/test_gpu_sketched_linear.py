@@ -128,7 +128,7 @@ def test_sketched_linear_carried_norm_sees_weight_changes(dev, how):
     plain = SketchedLinear(k, d, r, kind="qr", device=dev, weight=w.clone())
     carry = SketchedLinear(k, d, r, kind="qr", device=dev, weight=w.clone(), carry_norm=True)
     for u in range(2):
-        x = synth.normal_bf16((mb, k), 1.0, seed=3100 + u).to(dev)
+        x = synth.normal_bf16((mb, k), 1.0, seed=3100 + u).to(dev).requires_grad_(True)
         dy = synth.normal_bf16((mb, d), 0.1, seed=3200 + u).to(dev)
         stats = []
         for layer in (plain, carry):
