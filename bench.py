@@ -1,23 +1,32 @@
 """Benchmark of the sketch hot path on one MI355X.
 
-One step = the whole path for one training step of one Qwen3-1.7B-shaped
-block (q 2048->2048, k and v 2048->1024, o 2048->2048, gate and up
-2048->6144, down 6144->2048; W is out x in), rank 64, QR-of-Gaussian
-projections redrawn every step, 32768 tokens in 8 microbatches of 4096:
+The bench line is one training step of the full Qwen3-8B-shaped projection
+set: 36 layers x 7 matrices (q and o 4096->4096, k and v 4096->1024, gate
+and up 4096->12288, down 12288->4096; W is out x in), all 252 weight matrices
+(12.9 GiB of bf16) resident in HBM, rank 128, QR-of-Gaussian projections
+redrawn every step, 32768 tokens in 8 microbatches of 4096. Per layer:
 
-  rgc_sample_projections (QR, the 7 matrices in one batched call)
+  rgc_sample_projections (QR, the layer's 7 matrices in one batched call;
+                          drawn one step ahead on a second stream)
   8 x (rgc_project_batch + rgc_accumulate_batch), each covering the 7 matrices
   rgc_apply_batch over the 7 matrices (tau = 1e-3)
 
-Inputs are synthetic and resident in HBM before timing: X ~ N(0,1) (shared by
-q/k/v and by gate/up, as in the real block), D ~ N(0, 1e-3^2), W ~ N(0, 0.02^2),
-all bf16. Prints one JSON line (see the fields below).
+Layers run one after another (layer-major). Inputs are synthetic and resident
+in HBM before timing: one set of X ~ N(0,1) activations (shared by q/k/v and
+by gate/up, as in the real block) and D ~ N(0, 1e-3^2) output gradients,
+reused by every layer (a set is 4.2 GB, far above the 256 MB Infinity Cache,
+and a layer reads it all between two reads of the same bytes); every layer
+has its own W ~ N(0, 0.02^2), sketches and projections. Prints one JSON line.
+
+--workload selects the other workload shapes (same fields).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
+import platform
 import sys
 import time
 
@@ -37,32 +46,46 @@ LAYER_8B = [  # one layer of the Qwen3-8B-shaped projection set
     ("o", 4096, 4096, "attn_out"), ("gate", 12288, 4096, "mlp_in"), ("up", 12288, 4096, "mlp_in"),
     ("down", 4096, 12288, "mlp_act"),
 ]
-# The default is the bench line; the others measure the remaining workload shapes (same fields, their own name).
-#   refresh: a new projection every step (QR, drawn inside the timed step); else drawn once (fixed Rademacher)
+#   layers:  layers of the set, each with its own W, sketches and projections
+#   refresh: a new projection every step (QR, drawn one step ahead); else drawn once (fixed Rademacher)
 #   x_dist:  "normal" or "t4" (Student-t with 4 degrees of freedom scaled to unit variance)
 WORKLOADS = {
+    "qwen3-8b": {"desc": "qwen3-8b-shaped projection set, 36 layers x 7 matrices (12.9 GiB bf16 W resident), "
+                         "r=128 QR redrawn every step, 32768 tokens in 8x4096",
+                 "matrices": LAYER_8B, "layers": 36, "r": 128, "kind": "qr", "refresh": True, "tokens": 32768,
+                 "microbatch": 4096, "tau": 1e-3, "x_dist": "normal", "cfg": 5},
+    "qwen3-8b-layer": {"desc": "one layer of the qwen3-8b-shaped set (7 matrices), r=128 QR, 32768 tokens in 8x4096",
+                       "matrices": LAYER_8B, "layers": 1, "r": 128, "kind": "qr", "refresh": True, "tokens": 32768,
+                       "microbatch": 4096, "tau": 1e-3, "x_dist": "normal", "cfg": 5},
     "qwen3-1.7b-block": {"desc": "qwen3-1.7b-block 7 projections, r=64 QR, 32768 tokens in 8x4096",
-                         "matrices": BLOCK_1P7B, "r": 64, "kind": "qr", "refresh": True, "tokens": 32768,
-                         "microbatch": 4096, "tau": 1e-3, "x_dist": "normal"},
-    "qwen3-1.7b-block-r256": {"desc": "qwen3-1.7b-block 7 projections, r=256 fixed Rademacher, 65536 tokens in 16x4096",
-                              "matrices": BLOCK_1P7B, "r": 256, "kind": "rademacher", "refresh": False,
-                              "tokens": 65536, "microbatch": 4096, "tau": 1e-3, "x_dist": "normal"},
+                         "matrices": BLOCK_1P7B, "layers": 1, "r": 64, "kind": "qr", "refresh": True,
+                         "tokens": 32768, "microbatch": 4096, "tau": 1e-3, "x_dist": "normal", "cfg": 2},
+    "qwen3-1.7b-block-r256": {"desc": "qwen3-1.7b-block 7 projections, r=256 fixed Rademacher, 65536 tokens in "
+                                      "16x4096", "matrices": BLOCK_1P7B, "layers": 1, "r": 256, "kind": "rademacher",
+                              "refresh": False, "tokens": 65536, "microbatch": 4096, "tau": 1e-3,
+                              "x_dist": "normal", "cfg": 3},
     "square-4096": {"desc": "square layer 4096x4096, r=64 QR new per update, 131072 tokens in 32x4096",
-                    "matrices": [("w", 4096, 4096, "x")], "r": 64, "kind": "qr", "refresh": True, "tokens": 131072,
-                    "microbatch": 4096, "tau": 1e-3, "x_dist": "t4"},
-    "qwen3-8b-layer": {"desc": "one qwen3-8b-shaped layer (7 projections), r=128 QR, 32768 tokens in 8x4096",
-                       "matrices": LAYER_8B, "r": 128, "kind": "qr", "refresh": True, "tokens": 32768,
-                       "microbatch": 4096, "tau": 1e-3, "x_dist": "normal"},
+                    "matrices": [("w", 4096, 4096, "x")], "layers": 1, "r": 64, "kind": "qr", "refresh": True,
+                    "tokens": 131072, "microbatch": 4096, "tau": 1e-3, "x_dist": "t4", "cfg": 4},
 }
-WORKLOAD = WORKLOADS["qwen3-1.7b-block"]
+DEFAULT_WORKLOAD = "qwen3-8b"
+
+# HBM traffic of the roofline kernel, measured with rocprofv3 counters; each
+# record is used only while the sources it was taken from are unchanged.
+TRAFFIC_RECORDS = {
+    "qwen3-8b": "profiles/traffic_accumulate_qwen3_8b_r128.md",
+    "qwen3-1.7b-block": "profiles/traffic_accumulate_qwen3_1p7b_block_r64.md",
+}
+KERNEL_SOURCES = ["rank_randomized_gradient_amd/csrc/rgc_sketch.hip", "rank_randomized_gradient_amd/csrc/rgc_device.hpp",
+                  "rank_randomized_gradient_amd/csrc/rgc_internal.hpp"]
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="qwen3-1.7b-block", choices=sorted(WORKLOADS),
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS),
                     help="the bench line is the default; the others measure the remaining workload shapes")
     ap.add_argument("--carried-norm", action="store_true",
                     help="the step applies with ||W|| carried from the previous update (rgc_apply_carried_batch: "
@@ -75,13 +98,6 @@ def parse():
     return ap.parse_args()
 
 
-# Sources the accumulate kernel is built from; the HBM traffic recorded from
-# profiler counters is reported only while they are unchanged.
-KERNEL_SOURCES = ["rank_randomized_gradient_amd/csrc/rgc_sketch.hip", "rank_randomized_gradient_amd/csrc/rgc_device.hpp",
-                  "rank_randomized_gradient_amd/csrc/rgc_internal.hpp"]
-TRAFFIC_RECORD = "profiles/traffic_accumulate_qwen3_1p7b_block_r64.md"
-
-
 def sources_digest() -> str:
     import hashlib
 
@@ -92,15 +108,15 @@ def sources_digest() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per accumulate launch measured with rocprofv3 counters (see the
-    record for the commands and the copy-kernel scaling), or None when the
+def recorded_traffic(workload: str):
+    """HBM bytes per accumulate launch measured with rocprofv3 counters (the
+    record gives the commands and the copy-kernel scaling), or None when the
     record is missing or was taken from different kernel sources."""
-    path = os.path.join(ROOT, TRAFFIC_RECORD)
-    if not os.path.exists(path):
+    rel = TRAFFIC_RECORDS.get(workload)
+    if rel is None or not os.path.exists(os.path.join(ROOT, rel)):
         return None
     fields = {}
-    with open(path) as f:
+    with open(os.path.join(ROOT, rel)) as f:
         for line in f:
             if ":" in line and line.lstrip().startswith("- "):
                 key, _, val = line.strip()[2:].partition(":")
@@ -113,28 +129,109 @@ def recorded_traffic():
         return None
 
 
-def step_seed(step: int, m: int) -> int:
-    return (2 << 32) | (step << 8) | m
+def step_seed(cfg: int, step: int, layer: int, m: int) -> int:
+    return (cfg << 56) | ((step & 0xFFFFFFFF) << 24) | (layer << 8) | m
+
+
+class Calls:
+    """The library calls of one step, marshalled once: every call below is a
+    ctypes call with argument arrays built up front (the seeds arrays are
+    rewritten in place before each use). Validation still runs in the library
+    on every call; only Python's per-call marshalling is hoisted."""
+
+    def __init__(self, rgc, lib, wl, X, D, W, P_sets, C, XP, ws_main, ws_side, s_main, s_side):
+        import torch
+
+        self.rgc, self.lib = rgc, lib
+        mats, r, mb = wl["matrices"], wl["r"], wl["microbatch"]
+        n, L = len(mats), wl["layers"]
+        self.n, self.L, self.n_mb = n, L, wl["tokens"] // mb
+        i64, vp, u64, f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_float
+        arr = lambda t, vals: (t * len(vals))(*vals)  # noqa: E731
+        self.kind = rgc.RGC_PROJ_QR_GAUSSIAN if wl["kind"] == "qr" else rgc.RGC_PROJ_RADEMACHER
+        ks = [k for _, _, k, _ in mats]
+        ds = [d for _, d, _, _ in mats]
+        self.ks_arr, self.ds_arr = arr(i64, ks), arr(i64, ds)
+        self.r, self.mb, self.tau = r, mb, float(wl["tau"])
+        self.sm, self.ss = vp(s_main.cuda_stream), vp(s_side.cuda_stream)
+        # workspaces: the largest query of any call on each stream
+        need_main = max(lib.rgc_project_batch_workspace_size(n, self.ks_arr, mb, r),
+                        lib.rgc_accumulate_batch_workspace_size(n, self.ds_arr, mb, r),
+                        lib.rgc_apply_batch_workspace_size(n, self.ds_arr, self.ks_arr, r),
+                        lib.rgc_sample_projections_workspace_size(self.kind, n, self.ks_arr, r))
+        need_side = lib.rgc_sample_projections_workspace_size(self.kind, n, self.ks_arr, r)
+        self.wm = (vp(ws_main.get(need_main)[0].value), need_main)
+        self.wsd = (vp(ws_side.get(need_side)[0].value), need_side) if need_side else (vp(0), 0)
+        self.seeds = [arr(u64, [0] * n) for _ in range(L)]
+        self.p_ptrs = [[arr(vp, [p.data_ptr() for p in P_sets[b][l]]) for l in range(L)] for b in range(len(P_sets))]
+        self.w_ptrs = [arr(vp, [w.data_ptr() for w in W[l]]) for l in range(L)]
+        self.ldw = arr(i64, ks)
+        self.c_ptrs = [arr(vp, [c.data_ptr() for c in C[l]]) for l in range(L)]
+        self.xp_ptrs = arr(vp, [x.data_ptr() for x in XP])
+        self.x_ptrs, self.ldx, self.d_ptrs, self.ldd = [], None, [], None
+        for i in range(self.n_mb):
+            xs = [X[src][i * mb:(i + 1) * mb] for _, _, _, src in mats]
+            dd = [D[m][i * mb:(i + 1) * mb] for m in range(n)]
+            self.x_ptrs.append(arr(vp, [x.data_ptr() for x in xs]))
+            self.d_ptrs.append(arr(vp, [x.data_ptr() for x in dd]))
+            self.ldx = arr(i64, [x.stride(0) for x in xs])
+            self.ldd = arr(i64, [x.stride(0) for x in dd])
+        self.step_seeds = arr(u64, [0] * n)
+        self.wnorm2 = [torch.zeros(n, dtype=torch.float64, device=X[mats[0][3]].device) for _ in range(L)]
+        self.carried_fresh = [True] * L
+
+    def sample(self, cfg, step, layer, pbuf, side):
+        for m in range(self.n):
+            self.seeds[layer][m] = step_seed(cfg, step, layer, m)
+        ws, stream = (self.wsd, self.ss) if side else (self.wm, self.sm)
+        self.rgc._check(self.lib.rgc_sample_projections(self.kind, self.n, self.seeds[layer], self.ks_arr, self.r,
+                                                        self.p_ptrs[pbuf][layer], ws[0], ws[1], stream))
+
+    def project(self, pbuf, layer, i):
+        self.rgc._check(self.lib.rgc_project_batch(self.n, self.x_ptrs[i], self.ldx, self.ks_arr,
+                                                   self.p_ptrs[pbuf][layer], self.xp_ptrs, self.mb, self.r,
+                                                   self.wm[0], self.wm[1], self.sm))
+
+    def accumulate(self, layer, i):
+        self.rgc._check(self.lib.rgc_accumulate_batch(self.n, self.d_ptrs[i], self.ldd, self.ds_arr, self.xp_ptrs,
+                                                      self.c_ptrs[layer], self.mb, self.r, self.wm[0], self.wm[1],
+                                                      self.sm))
+
+    def apply(self, cfg, step, pbuf, layer, carried=False):
+        for m in range(self.n):
+            self.step_seeds[m] = step_seed(cfg, step, layer, m) ^ (1 << 23)
+        if carried:
+            fresh = 1 if self.carried_fresh[layer] else 0
+            self.carried_fresh[layer] = False
+            self.rgc._check(self.lib.rgc_apply_carried_batch(
+                self.n, self.w_ptrs[layer], self.ldw, self.c_ptrs[layer], self.p_ptrs[pbuf][layer], self.ds_arr,
+                self.ks_arr, self.r, ctypes.c_float(self.tau), self.step_seeds, None,
+                ctypes.c_void_p(self.wnorm2[layer].data_ptr()), fresh, self.wm[0], self.wm[1], self.sm))
+            return
+        self.rgc._check(self.lib.rgc_apply_batch(self.n, self.w_ptrs[layer], self.ldw, self.c_ptrs[layer],
+                                                 self.p_ptrs[pbuf][layer], self.ds_arr, self.ks_arr, self.r,
+                                                 ctypes.c_float(self.tau), self.step_seeds, None, self.wm[0],
+                                                 self.wm[1], self.sm))
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (got --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
     import torch
 
     from rank_randomized_gradient_amd import rgc
 
-    rgc.load_library()
+    lib = rgc.load_library()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     wl = WORKLOADS[args.workload]
-    default_wl = args.workload == "qwen3-1.7b-block"
-    r, T, mb = wl["r"], wl["tokens"], wl["microbatch"]
+    cfg, r, T, mb, L = wl["cfg"], wl["r"], wl["tokens"], wl["microbatch"], wl["layers"]
     n_mb = T // mb
     mats = wl["matrices"]
+    n = len(mats)
 
     # ---- synthetic inputs, resident in HBM ------------------------------------
     g = torch.Generator(device=dev)
@@ -154,76 +251,60 @@ def main():
         acts[src] = k
     X = {name: (t4((T, width)) if wl["x_dist"] == "t4" else normal((T, width), 1.0)) for name, width in acts.items()}
     D = [normal((T, d), 1e-3) for _, d, _, _ in mats]
-    W = [normal((d, k), 0.02) for _, d, k, _ in mats]
-    P = [torch.empty((k, r), dtype=torch.bfloat16, device=dev) for _, _, k, _ in mats]
-    # the 7 sketches are views of one buffer, so that zeroing them is one launch
-    c_all = torch.zeros(sum(d for _, d, _, _ in mats) * r, dtype=torch.float32, device=dev)
-    C, off = [], 0
-    for _, d, _, _ in mats:
-        C.append(c_all[off:off + d * r].view(d, r))
-        off += d * r
+    W = [[normal((d, k), 0.02) for _, d, k, _ in mats] for _ in range(L)]
+    # two sets of projections (drawn one step ahead) per layer
+    P_sets = [[[torch.empty((k, r), dtype=torch.bfloat16, device=dev) for _, _, k, _ in mats] for _ in range(L)]
+              for _ in range(2 if wl["refresh"] else 1)]
+    # each layer's 7 sketches are views of one buffer, so that zeroing them is one launch
+    c_layer = [torch.zeros(sum(d for _, d, _, _ in mats) * r, dtype=torch.float32, device=dev) for _ in range(L)]
+    C = []
+    for l in range(L):
+        views, off = [], 0
+        for _, d, _, _ in mats:
+            views.append(c_layer[l][off:off + d * r].view(d, r))
+            off += d * r
+        C.append(views)
     XP = [torch.empty((mb, r), dtype=torch.bfloat16, device=dev) for _ in mats]
-    ws = rgc.Workspace(dev)
+    s_main = torch.cuda.current_stream(dev)
+    s_side = torch.cuda.Stream(device=dev)  # default priority
+    calls = Calls(rgc, lib, wl, X, D, W, P_sets, C, XP, rgc.Workspace(dev), rgc.Workspace(dev), s_main, s_side)
     torch.cuda.synchronize()
 
     # The projections of step s depend only on their seeds, so they are drawn one
-    # step ahead on a second stream (default priority), overlapping step s - 1;
-    # two sets of P buffers, ordered by events. Every timed step still draws
-    # exactly one set (the first timed step's set is drawn during the warm-up).
-    s_main = torch.cuda.current_stream(dev)
-    s_side = torch.cuda.Stream(device=dev)
-    ws_side = rgc.Workspace(dev)
-    Pb = [P, [torch.empty_like(p) for p in P]]
+    # step ahead on the second stream, overlapping step s - 1; two sets of P
+    # buffers, ordered by events. Every timed step still draws exactly one set
+    # (the first timed step's set is drawn during the warm-up).
     ev_ready, ev_free = [None, None], [None, None]
-
-    def sample_all(step, Ps=None, workspace=None):
-        # all projections of the block in one batched call (same bits as one call per matrix)
-        rgc.rgc_sample_projections(wl["kind"], [step_seed(step, m) for m in range(len(mats))],
-                                   Ps if Ps is not None else P, workspace=workspace or ws)
 
     def draw_ahead(step):
         buf = step % 2
         with torch.cuda.stream(s_side):
             if ev_free[buf] is not None:
                 s_side.wait_event(ev_free[buf])  # the step that last read this set is done
-            sample_all(step, Pb[buf], ws_side)
+            for l in range(L):
+                calls.sample(cfg, step, l, buf, side=True)
             ev = torch.cuda.Event()
             ev.record(s_side)
             ev_ready[buf] = ev
 
     if not wl["refresh"]:
-        sample_all(0)  # a fixed projection, drawn once
+        for l in range(L):
+            calls.sample(cfg, 0, l, 0, side=False)  # a fixed projection, drawn once
 
-    def project_mb(i, Ps=None):
-        # the 7 projections of microbatch i in one launch (q/k/v and gate/up share their X)
-        rgc.rgc_project_batch([X[src][i * mb:(i + 1) * mb] for _, _, _, src in mats], Ps if Ps is not None else P,
-                              outs=XP, workspace=ws)
+    pairs = {"project": [], "accumulate": [], "apply": []}  # event pairs around calls, when timing inside steps
 
-    def accumulate_mb(i):
-        rgc.rgc_accumulate_batch([D[m][i * mb:(i + 1) * mb] for m in range(len(mats))], XP, C, workspace=ws)
-
-    wnorm2 = torch.zeros(len(mats), dtype=torch.float64, device=dev)
-    carried = {"fresh": True}
-
-    def apply_carried(step, Ps=None):
-        # the 7 updates with ||W||^2 carried in wnorm2 (streamed from W on the first call)
-        rgc.rgc_apply_carried_batch(W, C, Ps if Ps is not None else P, wl["tau"],
-                                    [step_seed(step, m) for m in range(len(mats))], wnorm2,
-                                    fresh=carried["fresh"], workspace=ws)
-        carried["fresh"] = False
-
-    def apply_all(step, Ps=None):
-        if args.carried_norm:
-            apply_carried(step, Ps)
+    def timed(name, fn, on):
+        if not on:
+            fn()
             return
-        # the 7 updates in one batched call (norms sweep, step scalars, update sweep)
-        rgc.rgc_apply_batch(W, C, Ps if Ps is not None else P, wl["tau"],
-                            [step_seed(step, m) for m in range(len(mats))], workspace=ws)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        pairs[name].append((a, b))
 
-    acc_pairs = []  # (start, end) events around accumulate calls, when timing them inside steps
-
-    def one_step(step, time_accumulate=False):
-        Ps = P
+    def one_step(step, time_calls=False):
+        buf = 0
         if wl["refresh"]:
             buf = step % 2
             if ev_ready[buf] is None:
@@ -231,23 +312,16 @@ def main():
             s_main.wait_event(ev_ready[buf])
             ev_ready[buf] = None
             draw_ahead(step + 1)
-            Ps = Pb[buf]
-        c_all.zero_()
-        for i in range(n_mb):
-            project_mb(i, Ps)
-            if time_accumulate:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                accumulate_mb(i)
-                b.record()
-                acc_pairs.append((a, b))
-            else:
-                accumulate_mb(i)
-        apply_all(step, Ps)
+        for l in range(L):
+            c_layer[l].zero_()
+            for i in range(n_mb):
+                timed("project", lambda: calls.project(buf, l, i), time_calls)
+                timed("accumulate", lambda: calls.accumulate(l, i), time_calls)
+            timed("apply", lambda: calls.apply(cfg, step, buf, l, args.carried_norm), time_calls)
         if wl["refresh"]:
             ev = torch.cuda.Event()
             ev.record(s_main)
-            ev_free[step % 2] = ev
+            ev_free[buf] = ev
 
     for s in range(args.warmup):
         one_step(s)
@@ -259,11 +333,12 @@ def main():
     start.record()
     for s in range(args.steps):
         one_step(args.warmup + s)
-    torch.cuda.current_stream(dev).wait_stream(s_side)  # the last draw ends inside the timed region
+    s_main.wait_stream(s_side)  # the last draw ends inside the timed region
     end.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
     tokens_per_s = T / (ms_per_step / 1e3)
+    base = args.warmup + args.steps
 
     # the spread of single steps (a second pass, an event pair around each step)
     single = []
@@ -271,33 +346,41 @@ def main():
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record()
-        one_step(args.warmup + args.steps + s)
-        torch.cuda.current_stream(dev).wait_stream(s_side)
+        one_step(base + s)
+        s_main.wait_stream(s_side)
         b.record()
         torch.cuda.synchronize()
         single.append(a.elapsed_time(b))
     single.sort()
     step_spread = {"min": round(single[0], 4), "median": round(single[len(single) // 2], 4),
                    "max": round(single[-1], 4)}
+    base += args.steps
 
-    # the accumulate's duration inside steps (the roofline's kernel): a third pass
-    # of K steps like the timed ones, with an event pair on the launch stream
-    # around each rgc_accumulate_batch call
-    acc_in_step_s = None
+    # algorithmic work per launch (bytes and flops), per entry point
+    acc_bytes = sum(2 * mb * d + 2 * mb * r + 8 * d * r for _, d, _, _ in mats)
+    acc_flops = sum(2 * mb * d * r for _, d, _, _ in mats)
+    prj_bytes = sum(2 * mb * k + 2 * mb * r + 2 * k * r for _, _, k, _ in mats)
+    prj_flops = sum(2 * mb * k * r for _, _, k, _ in mats)
+    app_bytes = sum(6 * d * k + 8 * d * r + 4 * k * r for _, d, k, _ in mats)
+    appc_bytes = sum(4 * d * k + 8 * d * r + 4 * k * r for _, d, k, _ in mats)  # W read once
+    smp_bytes = sum(2 * k * r for _, _, k, _ in mats)
+    app_launch_bytes = appc_bytes if args.carried_norm else app_bytes
+
+    # each call's duration inside steps: a third pass of K steps like the timed
+    # ones, with an event pair on the launch stream around every batched call
+    kern, in_step = {}, {}
     if not args.no_kernel_timing:
         torch.cuda.synchronize()
         for s in range(args.steps):
-            one_step(args.warmup + 2 * args.steps + s, time_accumulate=True)
-        torch.cuda.current_stream(dev).wait_stream(s_side)
+            one_step(base + s, time_calls=True)
+        s_main.wait_stream(s_side)
         torch.cuda.synchronize()
-        acc_in_step_s = sum(a.elapsed_time(b) for a, b in acc_pairs) * 1e-3 / len(acc_pairs)
+        base += args.steps
+        for name, prs in pairs.items():
+            in_step[name] = sum(a.elapsed_time(b) for a, b in prs) * 1e-3 / len(prs)  # seconds per call
 
-    # ---- per-entry-point timing ---------------------------------------------------
-    # HIP events on the launch stream around K repetitions of one step's calls of
-    # a single entry point, issued back to back (an event pair around every
-    # microsecond-scale launch would time the event packets, not the kernels).
-    kern = {}
-    if not args.no_kernel_timing:
+        # Per-entry-point timing back to back: HIP events on the launch stream
+        # around K repetitions of one step's calls of a single entry point.
         def time_op(fn):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
@@ -309,61 +392,59 @@ def main():
             return a.elapsed_time(b) * 1e-3 / args.steps  # seconds per step
 
         per_step = {
-            "sample_projection": time_op(lambda s: sample_all(s)),
-            "project": time_op(lambda s: [project_mb(i) for i in range(n_mb)]),
-            "accumulate": time_op(lambda s: [accumulate_mb(i) for i in range(n_mb)]),
-            "apply": time_op(lambda s: apply_all(s)),
+            "sample_projection": time_op(lambda s: [calls.sample(cfg, base + s, l, 0, side=False) for l in range(L)]),
+            "project": time_op(lambda s: [calls.project(0, l, i) for l in range(L) for i in range(n_mb)]),
+            "accumulate": time_op(lambda s: [calls.accumulate(l, i) for l in range(L) for i in range(n_mb)]),
+            "apply": time_op(lambda s: [calls.apply(cfg, base + s, 0, l, args.carried_norm) for l in range(L)]),
         }
         if not args.carried_norm:
-            apply_carried(0)  # the first call streams ||W||; the timed ones carry it
-        per_step["apply_carried"] = time_op(lambda s: apply_carried(s))
-        # algorithmic work per step (bytes and flops), per entry point
-        acc_bytes = sum(2 * mb * d + 2 * mb * r + 8 * d * r for _, d, _, _ in mats) * n_mb
-        acc_flops = sum(2 * mb * d * r for _, d, _, _ in mats) * n_mb
-        prj_bytes = sum(2 * mb * k + 2 * mb * r + 2 * k * r for _, _, k, _ in mats) * n_mb
-        prj_flops = sum(2 * mb * k * r for _, _, k, _ in mats) * n_mb
-        app_bytes = sum(6 * d * k + 8 * d * r + 4 * k * r for _, d, k, _ in mats)
-        appc_bytes = sum(4 * d * k + 8 * d * r + 4 * k * r for _, d, k, _ in mats)  # W read once
-        smp_bytes = sum(2 * k * r for _, _, k, _ in mats)
-        kern = {
-            "accumulate": {"s_per_step": per_step["accumulate"], "launches_per_step": n_mb,
-                           "avg_us": 1e6 * per_step["accumulate"] / n_mb,
-                           "avg_us_in_step": 1e6 * acc_in_step_s,
-                           "GBs_in_step": acc_bytes / n_mb / acc_in_step_s / 1e9,
-                           "TFLOPs_in_step": acc_flops / n_mb / acc_in_step_s / 1e12,
-                           "GBs": acc_bytes / per_step["accumulate"] / 1e9,
-                           "TFLOPs": acc_flops / per_step["accumulate"] / 1e12},
-            "project": {"s_per_step": per_step["project"], "launches_per_step": n_mb,
-                        "avg_us": 1e6 * per_step["project"] / n_mb,
-                        "GBs": prj_bytes / per_step["project"] / 1e9,
-                        "TFLOPs": prj_flops / per_step["project"] / 1e12},
-            "apply": {"s_per_step": per_step["apply"], "launches_per_step": 1,
-                      "avg_us": 1e6 * per_step["apply"],
-                      "GBs": (appc_bytes if args.carried_norm else app_bytes) / per_step["apply"] / 1e9},
-            "apply_carried": {"s_per_step": per_step["apply_carried"], "launches_per_step": 1,
-                              "avg_us": 1e6 * per_step["apply_carried"],
-                              "GBs": appc_bytes / per_step["apply_carried"] / 1e9},
-            "sample_projection": {"s_per_step": per_step["sample_projection"],
-                                  "launches_per_step": 1 if wl["refresh"] else 0,
-                                  "avg_us": 1e6 * per_step["sample_projection"],
-                                  "GBs": smp_bytes / per_step["sample_projection"] / 1e9},
-        }
-        for v in kern.values():
-            v["hbm_frac"] = v["GBs"] / HBM_PEAK_GBS
-        kern["accumulate"]["mfma_frac"] = kern["accumulate"]["TFLOPs"] / BF16_PEAK_TFLOPS
-        kern["project"]["mfma_frac"] = kern["project"]["TFLOPs"] / BF16_PEAK_TFLOPS
+            for l in range(L):
+                calls.apply(cfg, base, 0, l, carried=True)  # the first call streams ||W||; the timed ones carry it
+        per_step["apply_carried"] = time_op(lambda s: [calls.apply(cfg, base + s, 0, l, True) for l in range(L)])
+        launches = {"project": L * n_mb, "accumulate": L * n_mb, "apply": L, "apply_carried": L,
+                    "sample_projection": L}
+        work = {"project": (prj_bytes, prj_flops), "accumulate": (acc_bytes, acc_flops),
+                "apply": (app_launch_bytes, 0), "apply_carried": (appc_bytes, 0), "sample_projection": (smp_bytes, 0)}
+        for name, sps in per_step.items():
+            by, fl = work[name]
+            avg = sps / launches[name]
+            e = {"launches_per_step": launches[name], "avg_us": 1e6 * avg, "GBs": by / avg / 1e9}
+            if fl:
+                e["TFLOPs"] = fl / avg / 1e12
+            if name in in_step:
+                t = in_step[name]
+                e.update({"avg_us_in_step": 1e6 * t, "GBs_in_step": by / t / 1e9})
+                if fl:
+                    e["TFLOPs_in_step"] = fl / t / 1e12
+                    ai = fl / by
+                    bound = min(BF16_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
+                    e["arith_intensity"] = ai
+                    e["frac_bounding_roofline_in_step"] = (fl / t / 1e12) / bound
+            e["hbm_frac"] = e.get("GBs_in_step", e["GBs"]) / HBM_PEAK_GBS
+            kern[name] = e
+        if not wl["refresh"]:
+            kern["sample_projection"]["launches_per_step"] = 0
 
-    # dominant kernel: the accumulate (the metric's named contraction); HBM-bound at r = 64.
-    # achieved = algorithmic bytes per launch / the launch's mean duration inside the steps
+    # dominant kernel: the entry point with the most time inside a step.
+    # achieved = algorithmic bytes per launch / the launch's mean duration inside steps
     roofline = None
-    if kern:
-        achieved = acc_bytes / n_mb / acc_in_step_s / 1e9
-        roofline = {"kernel": f"rgc_accumulate_batch (accumulate_kernel<{r}> + finish_tiles_kernel<{r},false>)",
-                    "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "launch_us_in_step": round(1e6 * acc_in_step_s, 2),
-                    "traffic": recorded_traffic() if default_wl else None,
-                    "algorithmic_bytes_per_launch": acc_bytes // n_mb}
+    if in_step:
+        share = {nm: in_step[nm] * (L * n_mb if nm != "apply" else L) for nm in in_step}
+        dom = max(share, key=share.get)
+        by, fl = work[dom]
+        t = in_step[dom]
+        kernels = {"accumulate": f"rgc_accumulate_batch (accumulate_kernel<{r}> + finish_tiles_kernel<{r},false>)",
+                   "project": f"rgc_project_batch (project_kernel<{r}> + finish_tiles_kernel<{r},true>)",
+                   "apply": "rgc_apply_batch (norms, scale, update launches)"}
+        achieved = by / t / 1e9
+        roofline = {"kernel": kernels[dom], "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "launch_us_in_step": round(1e6 * t, 2),
+                    "traffic": recorded_traffic(args.workload) if dom == "accumulate" else None,
+                    "algorithmic_bytes_per_launch": by,
+                    "step_time_share": round(share[dom] / (ms_per_step * 1e-3), 4)}
+        if fl:
+            roofline["arith_intensity_flop_per_byte"] = round(fl / by, 1)
 
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -373,9 +454,11 @@ def main():
         torch.cuda.synchronize()
 
     cpu = None
-    if not args.no_cpu_baseline and default_wl:
-        cpu = cpu_baseline(X, D, W, mats, wl)
+    if not args.no_cpu_baseline and args.workload == DEFAULT_WORKLOAD:
+        cpu = cpu_baseline(X, D, W[0], mats, wl)
 
+    acc = kern.get("accumulate", {})
+    app = kern.get("apply", {})
     out = {
         "metric": "sketch-accumulate TFLOP/s + fused-apply HBM GB/s (% roofline), tokens/s/step",
         "value": round(tokens_per_s, 1),
@@ -390,14 +473,16 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl["desc"], "r": r, "tokens_per_step": T, "microbatch": mb,
-                   "projection": "qr-gaussian" if wl["kind"] == "qr" else "rademacher, fixed", "tau": wl["tau"],
-                   "weight_norm": "carried from the previous update" if args.carried_norm else "streamed from W"},
-        "sketch_accumulate_TFLOPs": round(kern["accumulate"]["TFLOPs_in_step"], 2) if kern else None,
-        "sketch_accumulate_frac_bf16_peak": round(kern["accumulate"]["TFLOPs_in_step"] / BF16_PEAK_TFLOPS, 4)
-        if kern else None,
-        "fused_apply_GBs": round(kern["apply"]["GBs"], 1) if kern else None,
-        "fused_apply_frac_hbm_peak": round(kern["apply"]["hbm_frac"], 4) if kern else None,
+        "config": {"workload": wl["desc"], "layers": L, "matrices_per_layer": n, "r": r, "tokens_per_step": T,
+                   "microbatch": mb, "projection": "qr-gaussian" if wl["kind"] == "qr" else "rademacher, fixed",
+                   "tau": wl["tau"],
+                   "weight_norm": "carried from the previous update" if args.carried_norm else "streamed from W",
+                   "resident_weight_GiB": round(sum(w.numel() * 2 for ws_ in W for w in ws_) / 2**30, 2)},
+        "sketch_accumulate_TFLOPs": round(acc["TFLOPs_in_step"], 2) if acc else None,
+        "sketch_accumulate_frac_bf16_peak": round(acc["TFLOPs_in_step"] / BF16_PEAK_TFLOPS, 4) if acc else None,
+        "sketch_accumulate_frac_bounding_roofline": round(acc["frac_bounding_roofline_in_step"], 4) if acc else None,
+        "fused_apply_GBs": round(app["GBs_in_step"], 1) if app else None,
+        "fused_apply_frac_hbm_peak": round(app["GBs_in_step"] / HBM_PEAK_GBS, 4) if app else None,
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kern.items()},
@@ -406,43 +491,71 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _blas() -> tuple[str, int]:
+    try:
+        from threadpoolctl import threadpool_info
+
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            i = info[0]
+            return f"{i.get('internal_api', '?')} {i.get('version', '')}".strip(), int(i.get("num_threads", 1))
+    except Exception:
+        pass
+    return "unknown", len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(X, D, W, mats, wl):
-    """The CPU oracle, untuned, on a bounded sample of the same workload: all 7
-    QR projections, one 4096-token microbatch of project + accumulate for all 7
-    matrices, and all 7 applies; the step time is extrapolated to 8 microbatches."""
+    """The CPU oracle, untuned, on a bounded sample of the same workload (one
+    layer's share): the layer's 7 QR projections, one 4096-token microbatch of
+    project + accumulate for all 7 matrices, and the applies of the three
+    smallest matrices (q, k, v), whose time is scaled by weight elements to
+    all 7. The step time is extrapolated to 8 microbatches and 36 layers."""
     import numpy as np
 
     import oracle as orc
     from rank_randomized_gradient_amd import synth
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    r, mb = wl["r"], wl["microbatch"]
+    r, mb, L = wl["r"], wl["microbatch"], wl["layers"]
     n_mb = wl["tokens"] // mb
     bits = synth.to_numpy_bits
     xs = {name: bits(x[:mb]) for name, x in X.items()}
     ds = [bits(d[:mb]) for d in D]
-    ws = [bits(w) for w in W]
     t0 = time.perf_counter()
-    ps = [orc.qr_projection(step_seed(0, m), k, r) for m, (_, _, k, _) in enumerate(mats)]
+    ps = [orc.qr_projection(step_seed(wl["cfg"], 0, 0, m), k, r) for m, (_, _, k, _) in enumerate(mats)]
     t1 = time.perf_counter()
     cs = []
     for m, (_, d, k, src) in enumerate(mats):
         c = np.zeros((d, r), np.float32)
         cs.append(orc.accumulate(c, ds[m], orc.project(xs[src], ps[m])))
     t2 = time.perf_counter()
-    for m in range(len(mats)):
-        orc.apply_update(ws[m], cs[m], ps[m], wl["tau"], step_seed(0, m))
+    sample_m = sorted(range(len(mats)), key=lambda m: mats[m][1] * mats[m][2])[:3]
+    for m in sample_m:
+        orc.apply_update(bits(W[m]), cs[m], ps[m], wl["tau"], step_seed(wl["cfg"], 0, 0, m))
     t3 = time.perf_counter()
-    step_s = (t1 - t0) + n_mb * (t2 - t1) + (t3 - t2)
-    return {"value": round(wl["tokens"] / step_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"7 QR projections + 1 of {n_mb} microbatches (project+accumulate, 7 matrices) + 7 applies, "
-                      f"measured {t3 - t0:.1f}s; step time = projections + {n_mb} x microbatch + applies "
-                      f"= {step_s:.1f}s"}
+    el_all = sum(d * k for _, d, k, _ in mats)
+    el_sample = sum(mats[m][1] * mats[m][2] for m in sample_m)
+    apply_s = (t3 - t2) * el_all / el_sample
+    layer_s = (t1 - t0) + n_mb * (t2 - t1) + apply_s
+    step_s = L * layer_s
+    blas, threads = _blas()
+    return {"value": round(wl["tokens"] / step_s, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(), "blas": blas,
+            "sample": f"one layer's share: 7 QR projections ({t1 - t0:.1f}s) + 1 of {n_mb} microbatches "
+                      f"(project+accumulate, 7 matrices, {t2 - t1:.1f}s) + the applies of q, k, v "
+                      f"({t3 - t2:.1f}s, x{el_all / el_sample:.2f} by weight elements for all 7); "
+                      f"step = {L} x (projections + {n_mb} x microbatch + applies) = {step_s:.0f}s "
+                      f"(extrapolated x{L} layers)"}
 
 
 if __name__ == "__main__":
