@@ -44,8 +44,8 @@
  *     error nothing is launched and no buffer changes. Conditions that are only
  *     known on the device (a zero sketch, non-finite values) are reported
  *     through `stats` (rgc_apply).
- *   - Shape limits: r is one of 16, 32, 48, 64, 128, 192, 256 (QR
- *     projections: r <= 128); d and k are multiples of 8; T >= 0 (T = 0 is a
+ *   - Shape limits: r is any multiple of 16 up to 256 (QR projections: up
+ *     to 128); d and k are multiples of 8; T >= 0 (T = 0 is a
  *     no-op); T and d at most 65536 per call; leading dimensions are
  *     multiples of 8 elements and at most 2^23 (RGC_ERR_UNSUPPORTED above);
  *     for rgc_apply, d and k at most 2^30 and d*k at most 2^38;
@@ -67,7 +67,7 @@ typedef enum {
   RGC_OK = 0,
   RGC_ERR_NULL = 1,        /* a required pointer is NULL */
   RGC_ERR_SHAPE = 2,       /* a dimension is negative, r > k, or ld < width */
-  RGC_ERR_UNSUPPORTED = 3, /* r or d/k outside the supported set (see above) */
+  RGC_ERR_UNSUPPORTED = 3, /* r or d/k outside the supported set (see the shape limits) */
   RGC_ERR_ALIGN = 4,       /* a base pointer or leading dimension is misaligned */
   RGC_ERR_WORKSPACE = 5,   /* workspace missing or smaller than the query */
   RGC_ERR_HIP = 6,         /* a kernel launch failed */

@@ -59,11 +59,12 @@ constexpr int64_t kMaxApplyElems = int64_t(1) << 38;  // d * k (workgroup counts
 template <int R>
 struct ApplyTraits {
   static constexpr int KQ = (R + 31) / 32;              // K-steps of 32 over r
-  // 16-row N-tiles per wave: two (128-row tiles) except at r = 128, whose
-  // 128-row stage would leave one workgroup per compute unit; at r > 128 that
-  // is the case anyway, and the taller tile halves the P rows re-read per W
-  // byte (measured on the Qwen3-1.7B-shaped block at r = 256: 253 -> 205 us)
-  static constexpr int NTW = R == 128 ? 1 : 2;
+  // 16-row N-tiles per wave: two (128-row tiles) except for 64 < r <= 128,
+  // whose 128-row stage would leave one workgroup per compute unit; at r >
+  // 128 that is the case anyway, and the taller tile halves the P rows
+  // re-read per W byte (measured on the Qwen3-1.7B-shaped block at r = 256:
+  // 253 -> 205 us)
+  static constexpr int NTW = R > 64 && R <= 128 ? 1 : 2;
   static constexpr int RW = 16 * NTW;                   // rows per wave
   static constexpr int ROWS = kApplyWaves * RW;         // rows per workgroup tile
   static constexpr int RP = 32 * KQ + 8;                // LDS row pitch of the P tile (bf16)

@@ -27,9 +27,10 @@ constexpr int64_t kMaxLeadingDim = int64_t(1) << 23;
 // Bytes of the static device scratch behind rgc_apply_noalloc.
 constexpr size_t kNoAllocScratchBytes = RGC_NOALLOC_SCRATCH_BYTES;
 
-inline bool rank_supported(int64_t r) {
-  return r == 16 || r == 32 || r == 48 || r == 64 || r == 128 || r == 192 || r == 256;
-}
+// Ranks of the MFMA-tiled kernels: every multiple of 16 up to 256.
+inline bool rank_tiled(int64_t r) { return r >= 16 && r <= 256 && r % 16 == 0; }
+
+inline bool rank_supported(int64_t r) { return rank_tiled(r); }
 
 template <int V>
 using IntC = std::integral_constant<int, V>;
@@ -43,19 +44,19 @@ __host__ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Calls f(IntC<r>{}) for a supported rank; returns false otherwise.
+// Calls f(IntC<r>{}) for a tiled rank (a multiple of 16 up to 256); returns
+// false otherwise.
 template <typename F>
 bool dispatch_rank(int64_t r, F&& f) {
-  switch (r) {
-    case 16: f(IntC<16>{}); return true;
-    case 32: f(IntC<32>{}); return true;
-    case 48: f(IntC<48>{}); return true;
-    case 64: f(IntC<64>{}); return true;
-    case 128: f(IntC<128>{}); return true;
-    case 192: f(IntC<192>{}); return true;
-    case 256: f(IntC<256>{}); return true;
-    default: return false;
-  }
+  bool done = false;
+  static_for<1, 17>([&](auto q) {
+    constexpr int R = 16 * decltype(q)::value;
+    if (r == R) {
+      f(IntC<R>{});
+      done = true;
+    }
+  });
+  return done;
 }
 
 inline bool aligned_to(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }

@@ -494,7 +494,7 @@ rgc_status_t qr_launch(int n, const uint64_t* seeds, const int64_t* ks, uint16_t
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
-bool qr_rank_supported(int64_t r) { return r == 16 || r == 32 || r == 48 || r == 64 || r == 128; }
+bool qr_rank_supported(int64_t r) { return r >= 16 && r <= 128 && r % 16 == 0; }
 
 uint32_t rademacher_magnitude(int64_t r) {
   // a = bf16(fp32(1/sqrt(r))), both roundings to nearest even
@@ -566,14 +566,12 @@ extern "C" rgc_status_t rgc_sample_projections(rgc_proj_kind_t kind, int64_t n, 
   const size_t need = batch_ws(kind, n, ks, r);
   if (!ws || ws_bytes < need) return RGC_ERR_WORKSPACE;
   if (!aligned_to(ws, 256)) return RGC_ERR_ALIGN;
-  switch (r) {
-    case 16: return qr_launch<16>((int)n, seeds, ks, Ps, ws, s);
-    case 32: return qr_launch<32>((int)n, seeds, ks, Ps, ws, s);
-    case 48: return qr_launch<48>((int)n, seeds, ks, Ps, ws, s);
-    case 64: return qr_launch<64>((int)n, seeds, ks, Ps, ws, s);
-    case 128: return qr_launch<128>((int)n, seeds, ks, Ps, ws, s);
-    default: return RGC_ERR_UNSUPPORTED;
-  }
+  rgc_status_t st = RGC_ERR_UNSUPPORTED;
+  static_for<1, 9>([&](auto q) {
+    constexpr int R = 16 * decltype(q)::value;
+    if (r == R) st = qr_launch<R>((int)n, seeds, ks, Ps, ws, s);
+  });
+  return st;
 }
 
 extern "C" rgc_status_t rgc_sample_projection(rgc_proj_kind_t kind, uint64_t seed, int64_t k, int64_t r, uint16_t* P,

@@ -133,18 +133,23 @@ __device__ __forceinline__ int64_t partial_slot(int64_t w, bool first_segment) {
 // 4kq+3: four K slots of the A operand.
 // ---------------------------------------------------------------------------
 constexpr int kStages = 6;
-constexpr int kWavesR256 = 2;  // waves along r at r = 256
-constexpr int kWavesR128 = 1;  // waves along r at r = 128
 
-// Waves along r: r <= 64 and r = 128 one (the N tile is 256 wide; at r = 128
-// each wave holds 128 ranks, 8 M-tiles); r = 256 two, each again with 128
-// ranks, so that the N tile is 128 wide and the rank operand is re-read half
-// as often as with four waves of 64 ranks; r = 192 four. (Measured on the
-// 1.7B block at r = 256 and the 8B layer at r = 128 against the previous
-// split, which gave every wave at most 64 ranks.)
+// Compute width of the rank operand for a rank of RM columns (a multiple of
+// 16): RM itself, except above 128 with an odd number of 16-column blocks
+// (144, 176, 208, 240), which take one more block so that two waves can split
+// them. The extra block is filled with a copy of a real block and never
+// multiplied or stored.
+__host__ __device__ constexpr int sketch_width(int RM) { return RM > 128 && (RM / 16) % 2 == 1 ? RM + 16 : RM; }
+
+// Waves along r: up to 128 ranks one (the N tile is 256 wide, each wave holds
+// all ranks, up to 8 M-tiles); above 128 two, each with half the ranks, so
+// that the N tile is 128 wide and the rank operand is re-read half as often
+// as with four waves of a quarter; 192 four. (Measured on the 1.7B block at
+// r = 256 and the 8B layer at r = 128 against the previous split, which gave
+// every wave at most 64 ranks.)
 template <int R, int KH>
 struct StageShape {
-  static constexpr int WR = R <= 64 ? 1 : (R == 128 ? kWavesR128 : (R == 256 ? kWavesR256 : 4));
+  static constexpr int WR = R <= 128 ? 1 : (R == 192 ? 4 : 2);
   static constexpr int WN = 4 / WR;                              // waves along N
   static constexpr int RW = R / WR;                              // r per wave
   static constexpr int MT = RW / 16;                             // MFMA M-tiles per wave
@@ -178,8 +183,10 @@ using AccTile = f32x4_t[StageShape<R, 1>::MT][4];
 //   read_b(stage, kh, wn, g, li, b)        the B operands of the wave's four N-tiles, K-half kh
 //   mask_b(b, wb, kh, k0, end, g)          zero B's K slots outside [k0, end)
 //   store(res, m, tile, full, slot, wn, rw, g, li)
-template <int R, int KH, typename Policy>
+template <int RM, int KH, typename Policy>
 __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, char* smem) {
+  constexpr int R = sketch_width(RM);  // compute width; RM columns are in memory (row stride RM)
+  constexpr int NRB_MEM = RM / 16;     // rank blocks that exist in memory
   using Sh = StageShape<R, KH>;
   constexpr int S = Sh::S, MT = Sh::MT, KS = Sh::KS;
   const int lane = threadIdx.x & 63, wave = wave_index();
@@ -216,7 +223,9 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
         const int blk = 8 * (c - Sh::NSC) + (lane >> 3);
         int64_t kr = 4 * (blk / Sh::NRB) + ((lane & 7) >> 1);
         kr = kr < rows ? kr : rows - 1;
-        voff[v] = (uint32_t)((kr * R + 16 * (blk % Sh::NRB) + 8 * (lane & 1)) * 2);
+        int rb = blk % Sh::NRB;
+        rb = rb < NRB_MEM ? rb : NRB_MEM - 1;  // a padding block copies a real one (never multiplied)
+        voff[v] = (uint32_t)((kr * RM + 16 * rb + 8 * (lane & 1)) * 2);
       }
     }
   };
@@ -228,7 +237,7 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
   auto issue = [&]() {
     const int64_t wb = window_base(lk * KS, l_kext, KS);
     const uint16_t* Sb = uniform_ptr(pol.stream_base(lm, ltile, wb));
-    const uint16_t* Rb = uniform_ptr(l_rank + wb * R);
+    const uint16_t* Rb = uniform_ptr(l_rank + wb * RM);
     const uint32_t st = lds0 + lslot * Sh::STAGE;
     static_for<0, Sh::NV_HI>([&](auto vc) {
       constexpr int v = decltype(vc)::value;
@@ -329,9 +338,11 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
           pol.mask_b(b, wb, kh, t0, c_kext, g);
         }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+          if (R != RM && rw * MT + mt >= NRB_MEM) continue;  // padding block (wave-uniform)
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_16x16x32(a[mt], b[nt], acc[mt][nt]);
+        }
       }
     }
     const bool first_seg = seg_kb0 == k0 && ctile == tile0 && cm == m0;
@@ -383,8 +394,9 @@ struct ProjectBatch {
   float* part;                    // 2 G slots of TILE x R fp32
 };
 
-template <int R>
+template <int RM>
 struct ProjectPolicy {
+  static constexpr int R = sketch_width(RM);
   using Sh = StageShape<R, kProjectKH>;
   static constexpr bool kKeepLargeFirst = true;
   const ProjectBatch& pb;
@@ -436,12 +448,13 @@ struct ProjectPolicy {
       const int64_t row = 64 * wn + 16 * nt + li;  // tile-relative token
 #pragma unroll
       for (int mt = 0; mt < Sh::MT; ++mt) {
+        if (R != RM && rw * Sh::RW + 16 * mt >= RM) continue;  // padding block
         const int rcol = rw * Sh::RW + 16 * mt + 4 * g;
         const f32x4_t v = res[mt][nt];
         if (full) {
           const int64_t t = tile * Sh::TILE + row;
           if (t < pb.s.next[m])
-            *reinterpret_cast<uint2*>(pb.XP[m] + t * R + rcol) =
+            *reinterpret_cast<uint2*>(pb.XP[m] + t * RM + rcol) =
                 make_uint2(pack_bf16x2(f32_to_bf16_rne(v[0]), f32_to_bf16_rne(v[1])),
                            pack_bf16x2(f32_to_bf16_rne(v[2]), f32_to_bf16_rne(v[3])));
         } else {
@@ -453,12 +466,12 @@ struct ProjectPolicy {
   }
 };
 
-template <int R>
+template <int RM>
 __global__ __launch_bounds__(256, 1) void project_kernel(ProjectBatch pb) {
-  using Sh = StageShape<R, kProjectKH>;
+  using Sh = StageShape<sketch_width(RM), kProjectKH>;
   __shared__ __attribute__((aligned(1024))) char smem[Sh::S * Sh::STAGE];
-  ProjectPolicy<R> pol{pb};
-  staged_pipeline<R, kProjectKH>(pb.s, pol, smem);
+  ProjectPolicy<RM> pol{pb};
+  staged_pipeline<RM, kProjectKH>(pb.s, pol, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -479,8 +492,9 @@ struct AccumulateBatch {
   float* part;                    // 2 G slots of TILE x R fp32
 };
 
-template <int R>
+template <int RM>
 struct AccumulatePolicy {
+  static constexpr int R = sketch_width(RM);
   using Sh = StageShape<R, 1>;
   static constexpr bool kKeepLargeFirst = false;
   const AccumulateBatch& ab;
@@ -524,13 +538,14 @@ struct AccumulatePolicy {
       const int64_t row = 64 * wn + 16 * nt + li;  // tile-relative d
 #pragma unroll
       for (int mt = 0; mt < Sh::MT; ++mt) {
+        if (R != RM && rw * Sh::RW + 16 * mt >= RM) continue;  // padding block
         const int rcol = rw * Sh::RW + 16 * mt + 4 * g;
         const f32x4_t v = res[mt][nt];
         if (full) {
           // the tile lies inside this workgroup's range: one add per element,
           // no other writer in this launch
           if (tile * Sh::TILE + row < ab.s.next[m]) {
-            float* c = ab.C[m] + (tile * Sh::TILE + row) * R + rcol;
+            float* c = ab.C[m] + (tile * Sh::TILE + row) * RM + rcol;
 #pragma unroll
             for (int e = 0; e < 4; ++e) unsafeAtomicAdd(c + e, v[e]);
           }
@@ -543,12 +558,12 @@ struct AccumulatePolicy {
   }
 };
 
-template <int R>
+template <int RM>
 __global__ __launch_bounds__(256, 1) void accumulate_kernel(AccumulateBatch ab) {
-  using Sh = StageShape<R, 1>;
+  using Sh = StageShape<sketch_width(RM), 1>;
   __shared__ __attribute__((aligned(1024))) char smem[Sh::S * Sh::STAGE];
-  AccumulatePolicy<R> pol{ab};
-  staged_pipeline<R, 1>(ab.s, pol, smem);
+  AccumulatePolicy<RM> pol{ab};
+  staged_pipeline<RM, 1>(ab.s, pol, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -565,8 +580,9 @@ struct FinishBatch {
   uint16_t* XP[kMaxItems];        // project targets
 };
 
-template <int R, bool TO_BF16>
+template <int RM, bool TO_BF16>
 __global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
+  constexpr int R = sketch_width(RM);  // partials are tile_n x R; outputs have row stride RM
   const Schedule& s = fb.s;
   const int64_t t = blockIdx.y;
   const int m = item_of_tile(s, t);
@@ -582,7 +598,8 @@ __global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
   {
     const int64_t e = (int64_t)blockIdx.x * (256 * PER) + threadIdx.x * PER;
     if (e >= rows * R) return;
-    const int64_t out = tile * tn * R + e;
+    if (R != RM && e % R >= RM) return;  // padding columns (a float4 never straddles RM)
+    const int64_t out = (tile * tn + e / R) * RM + e % R;
     float4 old = make_float4(0.f, 0.f, 0.f, 0.f);
     if constexpr (!TO_BF16) old = *reinterpret_cast<const float4*>(fb.C[m] + out);
     f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
@@ -662,20 +679,31 @@ Schedule make_schedule(int n, const int64_t* ns, const int64_t* ks, int64_t tile
   return s;
 }
 
-template <int R>
+template <int RM>
 size_t partial_bytes(const Schedule& s) {
-  return (size_t)2 * s.G * s.tile_n * R * sizeof(float);
+  return (size_t)2 * s.G * s.tile_n * sketch_width(RM) * sizeof(float);
+}
+
+// Whether some tile is cut between ranges (then the finishing launch runs).
+bool has_split_tiles(const Schedule& s) {
+  for (int m = 0; m < s.n; ++m)
+    for (int64_t t = 0; t < s.tbase[m + 1] - s.tbase[m]; ++t) {
+      const int64_t ts = s.ubase[m] + t * s.nkb[m], te = ts + s.nkb[m];
+      if (((ts + 1) * s.G - 1) / s.U != (te * s.G - 1) / s.U) return true;  // range_of(ts) != range_of(te - 1)
+    }
+  return false;
 }
 
 // One finishing workgroup per 1024 values of a tile (x) and per tile (y).
-template <int R>
+template <int RM>
 dim3 finish_grid(const Schedule& s) {
-  return dim3((unsigned)((s.tile_n * R + 1023) / 1024), (unsigned)s.tbase[s.n]);
+  return dim3((unsigned)((s.tile_n * sketch_width(RM) + 1023) / 1024), (unsigned)s.tbase[s.n]);
 }
 
-template <int R>
+template <int RM>
 Schedule project_schedule(int n, const int64_t* ns, const int64_t* ks, int64_t forced) {
-  return make_schedule(n, ns, ks, StageShape<R, kProjectKH>::TILE, StageShape<R, kProjectKH>::KS, forced);
+  using Sh = StageShape<sketch_width(RM), kProjectKH>;
+  return make_schedule(n, ns, ks, Sh::TILE, Sh::KS, forced);
 }
 
 // When every tile has the same K-steps (one token count for all items, as in
@@ -695,9 +723,10 @@ void align_ranges_to_tiles(Schedule& s, int64_t forced) {
   if (p >= 2 && p <= s.nkb[0] && 10 * p * tiles >= 9 * (int64_t)s.G) s.G = (int)(p * tiles);
 }
 
-template <int R>
+template <int RM>
 Schedule accumulate_schedule(int n, const int64_t* ns, const int64_t* ks, int64_t forced) {
-  Schedule s = make_schedule(n, ns, ks, StageShape<R, 1>::TILE, StageShape<R, 1>::KS, forced);
+  using Sh = StageShape<sketch_width(RM), 1>;
+  Schedule s = make_schedule(n, ns, ks, Sh::TILE, Sh::KS, forced);
   align_ranges_to_tiles(s, forced);
   return s;
 }
@@ -722,7 +751,8 @@ rgc_status_t project_launch(int n, const uint16_t* const* Xs, const int64_t* ldx
   pb.part = static_cast<float*>(ws);
   fb.part = pb.part;
   hipLaunchKernelGGL(project_kernel<R>, dim3((unsigned)pb.s.G), dim3(256), 0, st, pb);
-  hipLaunchKernelGGL((finish_tiles_kernel<R, true>), finish_grid<R>(pb.s), dim3(256), 0, st, fb);
+  if (has_split_tiles(pb.s))
+    hipLaunchKernelGGL((finish_tiles_kernel<R, true>), finish_grid<R>(pb.s), dim3(256), 0, st, fb);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
@@ -746,7 +776,8 @@ rgc_status_t accumulate_launch(int n, const uint16_t* const* Ds, const int64_t* 
   ab.part = static_cast<float*>(ws);
   fb.part = ab.part;
   hipLaunchKernelGGL(accumulate_kernel<R>, dim3((unsigned)ab.s.G), dim3(256), 0, st, ab);
-  hipLaunchKernelGGL((finish_tiles_kernel<R, false>), finish_grid<R>(ab.s), dim3(256), 0, st, fb);
+  if (has_split_tiles(ab.s))
+    hipLaunchKernelGGL((finish_tiles_kernel<R, false>), finish_grid<R>(ab.s), dim3(256), 0, st, fb);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 

@@ -127,7 +127,7 @@ def test_apply_batch_validation(lib):
     assert lib.rgc_apply_batch(n, ws_, lds, cs, ps, ds, ks, 64, f, None, None, FAKE, need, s) == NULL  # seeds
     bad_ld = (ctypes.c_int64 * n)(256, 500)
     assert lib.rgc_apply_batch(n, ws_, bad_ld, cs, ps, ds, ks, 64, f, seeds, None, FAKE, need, s) == SHAPE
-    assert lib.rgc_apply_batch(n, ws_, lds, cs, ps, ds, ks, 80, f, seeds, None, FAKE, need, s) == UNSUP
+    assert lib.rgc_apply_batch(n, ws_, lds, cs, ps, ds, ks, 72, f, seeds, None, FAKE, need, s) == UNSUP
     bad_c = (ctypes.c_void_p * n)(FAKE, FAKE + 4)
     assert lib.rgc_apply_batch(n, ws_, lds, bad_c, ps, ds, ks, 64, f, seeds, None, FAKE, need, s) == ALIGN
     assert lib.rgc_apply_batch(n, ws_, lds, cs, ps, ds, ks, 64, f, seeds, None, FAKE, need - 8, s) == WS
