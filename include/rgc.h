@@ -44,8 +44,10 @@
  *     error nothing is launched and no buffer changes. Conditions that are only
  *     known on the device (a zero sketch, non-finite values) are reported
  *     through `stats` (rgc_apply).
- *   - Shape limits: r is any multiple of 16 up to 256 (QR projections: up
- *     to 128); d and k are multiples of 8; T >= 0 (T = 0 is a
+ *   - Shape limits: r is 4, 8 or any multiple of 16 up to 256 (QR
+ *     projections: 4, 8 or a multiple of 16 up to 128); ranks 4 and 8 run
+ *     small-rank kernels (VALU sums; H formed in fp32 in rank order, its norm
+ *     from fp64 Gram matrices); d and k are multiples of 8; T >= 0 (T = 0 is a
  *     no-op); T and d at most 65536 per call; leading dimensions are
  *     multiples of 8 elements and at most 2^23 (RGC_ERR_UNSUPPORTED above);
  *     for rgc_apply, d and k at most 2^30 and d*k at most 2^38;

@@ -104,6 +104,7 @@ struct ApplyBatch {
   double* wnorm2;                 // per item, ||W||^2 (the caller's buffer when carrying)
   float* scale;                   // per item s, flag (rebuild norms; Gram norms when carrying)
   double* wpart;                  // carrying: per update workgroup, sum of the written weights' squares
+  double* sgram;                  // ranks below 16: one fp64 Gram partial (upper triangle) per Gram workgroup
   float* H;                       // reconstruct target (test hook)
 };
 
@@ -889,6 +890,217 @@ __global__ __launch_bounds__(256) void carry_norm_kernel(ApplyBatch b) {
 }
 
 // ---------------------------------------------------------------------------
+// Ranks below one MFMA tile (r = 4, 8). Each element of H = C P^T has only r
+// terms, so it is formed on the VALU in fp32, in rank order with every
+// product and sum rounded separately: h = ((c0 p0 + c1 p1) + c2 p2) + ...
+// ||H||^2 comes from the Gram identity with fp64 Gram matrices of C and P
+// (products of fp32 or bf16 values are exact in fp64; fixed-order sums), and
+// ||W||^2 from the same W stream as the tiled ranks. The launches mirror the
+// tiled ones: norms (Gram and W-stream workgroups), one scale workgroup per
+// item, the update (or the reconstruction), and for a carried norm the
+// per-item sum of the written squares.
+// ---------------------------------------------------------------------------
+constexpr int64_t kSmallGramRows = 4096;      // rows of C or P per Gram workgroup
+constexpr int64_t kSmallUpdateChunks = 2048;  // 8-column chunks per update workgroup (8 per thread)
+
+template <int R>
+struct SmallShape {
+  static constexpr int NQ = R * (R + 1) / 2;  // upper-triangle entries of an R x R Gram matrix
+};
+
+template <int R>
+__device__ __forceinline__ void small_row(const float* __restrict__ C, int64_t row, double (&v)[R]) {
+#pragma unroll
+  for (int a = 0; a < R; a += 4) {
+    const float4 c = *reinterpret_cast<const float4*>(C + row * R + a);
+    v[a] = c.x; v[a + 1] = c.y; v[a + 2] = c.z; v[a + 3] = c.w;
+  }
+}
+template <int R>
+__device__ __forceinline__ void small_row(const uint16_t* __restrict__ P, int64_t row, double (&v)[R]) {
+  float f[R];
+  load_bf16_row<R>(P + row * R, f);
+#pragma unroll
+  for (int a = 0; a < R; ++a) v[a] = f[a];
+}
+
+// Upper triangle of the Gram matrix of rows [row0, row1) of src (R columns),
+// summed per thread over its rows in order, then lanes by butterfly and
+// waves in order; written by threads 0 .. NQ-1.
+template <int R, typename T>
+__device__ void small_gram_partial(const T* __restrict__ src, int64_t row0, int64_t row1, double* __restrict__ out,
+                                   double* red) {
+  constexpr int NQ = SmallShape<R>::NQ;
+  const int lane = threadIdx.x & 63, wave = wave_index();
+  double acc[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) acc[q] = 0.0;
+  for (int64_t row = row0 + threadIdx.x; row < row1; row += 256) {
+    double v[R];
+    small_row<R>(src, row, v);
+    int q = 0;
+#pragma unroll
+    for (int a = 0; a < R; ++a)
+#pragma unroll
+      for (int c = a; c < R; ++c) acc[q++] += v[a] * v[c];
+  }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const double t = wave_sum(acc[q]);
+    if (lane == 0) red[wave * NQ + q] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x < NQ) {
+    const int q = threadIdx.x;
+    out[q] = ((red[q] + red[NQ + q]) + red[2 * NQ + q]) + red[3 * NQ + q];
+  }
+}
+
+// Gram workgroups first (per item the C-row chunks, then the P-row chunks),
+// then the W-stream workgroups.
+template <int R>
+__global__ __launch_bounds__(256) void small_norms_kernel(ApplyBatch b) {
+  constexpr int NQ = SmallShape<R>::NQ;
+  __shared__ double red[4 * NQ];
+  const int w = blockIdx.x;
+  const int ng = b.gbase[b.n];
+  if (w < ng) {
+    const int m = item_of(b.gbase, b.n, w);
+    const ApplyItem& it = b.it[m];
+    const int l = w - b.gbase[m];
+    double* out = b.sgram + (int64_t)w * NQ;
+    if (l < b.ncg[m]) {
+      const int64_t r0 = l * kSmallGramRows, r1 = r0 + kSmallGramRows < it.d ? r0 + kSmallGramRows : it.d;
+      small_gram_partial<R>(it.C, r0, r1, out, red);
+    } else {
+      const int64_t r0 = (l - b.ncg[m]) * kSmallGramRows, r1 = r0 + kSmallGramRows < it.k ? r0 + kSmallGramRows : it.k;
+      small_gram_partial<R>(it.P, r0, r1, out, red);
+    }
+    return;
+  }
+  const int sw = w - ng;
+  const int m = item_of(b.sbase, b.n, sw);
+  const ApplyItem& it = b.it[m];
+  const int64_t total = it.d * (it.k >> 3);
+  const int64_t c0 = (sw - b.sbase[m]) * kWStreamChunks;
+  const int64_t c1 = c0 + kWStreamChunks < total ? c0 + kWStreamChunks : total;
+  const double sq = wstream_sumsq(it.W, it.ldw, it.k, c0, c1, red);
+  if (threadIdx.x == 0) b.partials[sw] = sq;
+}
+
+// One workgroup per item: the Gram partials summed entry by entry in
+// workgroup order, ||H||^2 = sum_ab G_ab M_ab (off-diagonal entries twice),
+// ||W||^2 from the W-stream partials (or carried), then s and the flag.
+template <int R>
+__global__ __launch_bounds__(256) void small_scale_kernel(ApplyBatch b) {
+  constexpr int NQ = SmallShape<R>::NQ;
+  const int m = blockIdx.x;
+  const int t = threadIdx.x;
+  double ah = 0.0;
+  if (t < NQ) {
+    const int nc = b.ncg[m], np = b.gbase[m + 1] - b.gbase[m] - nc;
+    const double* gc = b.sgram + (int64_t)b.gbase[m] * NQ + t;
+    const double* gp = gc + (int64_t)nc * NQ;
+    double G = 0.0, M = 0.0;
+    for (int i = 0; i < nc; ++i) G += gc[(int64_t)i * NQ];
+    for (int i = 0; i < np; ++i) M += gp[(int64_t)i * NQ];
+    int a = 0, q = t;  // entry t of the upper triangle is (a, a + q) after the loop
+    while (q >= R - a) {
+      q -= R - a;
+      ++a;
+    }
+    ah = (q == 0 ? 1.0 : 2.0) * G * M;
+  }
+  double aw = 0.0;
+  if (b.carry != kCarryIn)
+    for (int w = b.sbase[m] + t; w < b.sbase[m + 1]; w += 256) aw += b.partials[w];
+  finish_scale(b, m, aw, ah);
+}
+
+// One thread per 8-column chunk of a row (eight chunks per thread, a
+// workgroup per kSmallUpdateChunks chunks of one item): h of the chunk on the
+// VALU, then (MODE) the H store, or v = fp32(w - fp32(s h)) rounded
+// stochastically with the chunk's Philox word, as the tiled update rounds it.
+template <int R, int MODE>
+__global__ __launch_bounds__(256) void small_update_kernel(ApplyBatch b) {
+  const int w = blockIdx.x;
+  const int m = apply_item_of(b, w);
+  const ApplyItem& it = b.it[m];
+  constexpr bool UPD = MODE == kModeUpdate || MODE == kModeUpdateCarry;
+  float s = 0.f;
+  if constexpr (UPD) {
+    if (b.fixed) {
+      s = it.alpha;
+    } else {
+      s = b.scale[2 * m];
+      if (b.scale[2 * m + 1] != 0.f) return;  // zero or non-finite step: W stays as it is
+    }
+  }
+  const int64_t cpr = it.k >> 3;  // chunks per row
+  const int64_t total = it.d * cpr;
+  const int64_t c0 = (int64_t)(w - b.wbase[m]) * kSmallUpdateChunks;
+  double sw = 0.0;
+  for (int u = 0; u < (int)(kSmallUpdateChunks / 256); ++u) {
+    const int64_t c = c0 + u * 256 + threadIdx.x;
+    if (c >= total) break;
+    const int64_t i = c / cpr, j0 = 8 * (c - i * cpr);
+    float cv[R];
+#pragma unroll
+    for (int a = 0; a < R; a += 4) {
+      const float4 q = *reinterpret_cast<const float4*>(it.C + i * R + a);
+      cv[a] = q.x; cv[a + 1] = q.y; cv[a + 2] = q.z; cv[a + 3] = q.w;
+    }
+    float h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float p[R];
+      load_bf16_row<R>(it.P + (j0 + e) * R, p);
+      float acc = cv[0] * p[0];
+#pragma unroll
+      for (int a = 1; a < R; ++a) acc = acc + cv[a] * p[a];
+      h[e] = acc;
+    }
+    if constexpr (MODE == kModeReconstruct) {
+      float4* dst = reinterpret_cast<float4*>(b.H + i * it.k + j0);
+      dst[0] = make_float4(h[0], h[1], h[2], h[3]);
+      dst[1] = make_float4(h[4], h[5], h[6], h[7]);
+    } else {
+      uint16_t* wp = it.W + i * it.ldw + j0;
+      const uint4 wv = *reinterpret_cast<const uint4*>(wp);
+      const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+      uint32_t rw[4];
+      rounding_words(it.seed, i, j0 >> 3, rw);
+      uint32_t out[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float w0 = __uint_as_float(wd[p] << 16), w1 = __uint_as_float(wd[p] & 0xFFFF0000u);
+        const float sh0 = s * h[2 * p], sh1 = s * h[2 * p + 1];
+        out[p] = f32x2_to_bf16x2_sr(w0 - sh0, w1 - sh1, rw[p]);
+      }
+      *reinterpret_cast<uint4*>(wp) = make_uint4(out[0], out[1], out[2], out[3]);
+      if constexpr (MODE == kModeUpdateCarry) {
+        float sq = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float o0 = __uint_as_float(out[p] << 16), o1 = __uint_as_float(out[p] & 0xFFFF0000u);
+          sq += o0 * o0;
+          sq += o1 * o1;
+        }
+        sw += (double)sq;
+      }
+    }
+  }
+  if constexpr (MODE == kModeUpdateCarry) {
+    __shared__ double red[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    sw = wave_sum(sw);
+    if (lane == 0) red[wave] = sw;
+    __syncthreads();
+    if (threadIdx.x == 0) b.wpart[w] = ((red[0] + red[1]) + red[2]) + red[3];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Test hooks: the rounding stream and the Philox generator alone.
 // ---------------------------------------------------------------------------
 __global__ void stochastic_round_kernel(const float* __restrict__ v, uint16_t* __restrict__ out, int64_t rows,
@@ -1044,6 +1256,103 @@ rgc_status_t apply_launch(int n, uint16_t* const* Ws, const int64_t* ldws, const
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
+// Small ranks: update workgroups per kSmallUpdateChunks chunks of W, Gram
+// workgroups per kSmallGramRows rows of C and of P, W-stream workgroups as
+// for the tiled ranks. All functions of each matrix's own shape.
+template <int R>
+void small_plan(ApplyBatch& b, int n, const int64_t* ds, const int64_t* ks) {
+  b.n = n;
+  b.wbase[0] = b.gbase[0] = b.sbase[0] = 0;
+  for (int m = 0; m < n; ++m) {
+    const int64_t chunks = ds[m] * (ks[m] / 8);
+    b.wbase[m + 1] = b.wbase[m] + (int)((chunks + kSmallUpdateChunks - 1) / kSmallUpdateChunks);
+    b.ncg[m] = (int)((ds[m] + kSmallGramRows - 1) / kSmallGramRows);
+    b.gbase[m + 1] = b.gbase[m] + b.ncg[m] + (int)((ks[m] + kSmallGramRows - 1) / kSmallGramRows);
+    b.sbase[m + 1] = b.sbase[m] + (int)((chunks + kWStreamChunks - 1) / kWStreamChunks);
+  }
+}
+
+// Workspace: W-stream partials, Gram partials, ||W||^2, (s, flag), and the
+// carried norm's per-workgroup partials, each part 256-byte aligned.
+template <int R>
+ApplyWorkspace small_ws_layout(const ApplyBatch& b) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  ApplyWorkspace l;
+  l.gram_off = up((size_t)b.sbase[b.n] * sizeof(double));
+  l.hpairs_off = l.gram_off + up((size_t)b.gbase[b.n] * SmallShape<R>::NQ * sizeof(double));
+  l.wnorm2_off = l.hpairs_off;
+  l.scale_off = l.wnorm2_off + up(kApplyMaxItems * sizeof(double));
+  l.wpart_off = l.scale_off + up(2 * kApplyMaxItems * sizeof(float));
+  l.total = l.wpart_off + up((size_t)b.wbase[b.n] * sizeof(double));
+  return l;
+}
+
+template <int R>
+size_t small_ws_for(int n, const int64_t* ds, const int64_t* ks) {
+  ApplyBatch b = {};
+  small_plan<R>(b, n, ds, ks);
+  return small_ws_layout<R>(b).total;
+}
+
+template <int R>
+rgc_status_t small_apply_launch(int n, uint16_t* const* Ws, const int64_t* ldws, const float* const* Cs,
+                                const uint16_t* const* Ps, const int64_t* ds, const int64_t* ks, float tau,
+                                const uint64_t* seeds, float* const* stats, void* ws, hipStream_t st,
+                                const float* alphas = nullptr, int carry = kCarryNone, double* wnorm2 = nullptr) {
+  ApplyBatch b = {};
+  small_plan<R>(b, n, ds, ks);
+  b.tau = tau;
+  b.fixed = alphas ? 1 : 0;
+  b.carry = carry;
+  for (int m = 0; m < n; ++m) {
+    b.it[m].W = Ws[m];
+    b.it[m].ldw = ldws[m];
+    b.it[m].C = Cs[m];
+    b.it[m].P = Ps[m];
+    b.it[m].d = ds[m];
+    b.it[m].k = ks[m];
+    b.it[m].seed = seeds[m];
+    b.it[m].stats = stats ? stats[m] : nullptr;
+    b.it[m].alpha = alphas ? alphas[m] : 0.f;
+  }
+  const int G = b.wbase[n];
+  if (alphas) {
+    hipLaunchKernelGGL((small_update_kernel<R, kModeUpdate>), dim3((unsigned)G), dim3(256), 0, st, b);
+    return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+  }
+  const ApplyWorkspace l = small_ws_layout<R>(b);
+  char* base = static_cast<char*>(ws);
+  b.partials = reinterpret_cast<double*>(base);
+  b.sgram = reinterpret_cast<double*>(base + l.gram_off);
+  b.wnorm2 = carry != kCarryNone ? wnorm2 : reinterpret_cast<double*>(base + l.wnorm2_off);
+  b.scale = reinterpret_cast<float*>(base + l.scale_off);
+  b.wpart = reinterpret_cast<double*>(base + l.wpart_off);
+  const int nw = carry == kCarryIn ? 0 : b.sbase[n];  // with a carried ||W||, no W stream
+  hipLaunchKernelGGL(small_norms_kernel<R>, dim3((unsigned)(b.gbase[n] + nw)), dim3(256), 0, st, b);
+  hipLaunchKernelGGL(small_scale_kernel<R>, dim3((unsigned)n), dim3(256), 0, st, b);
+  if (carry == kCarryNone) {
+    hipLaunchKernelGGL((small_update_kernel<R, kModeUpdate>), dim3((unsigned)G), dim3(256), 0, st, b);
+  } else {
+    hipLaunchKernelGGL((small_update_kernel<R, kModeUpdateCarry>), dim3((unsigned)G), dim3(256), 0, st, b);
+    hipLaunchKernelGGL(carry_norm_kernel, dim3((unsigned)n), dim3(256), 0, st, b);
+  }
+  return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+}
+
+template <int R>
+rgc_status_t small_reconstruct_launch(const float* C, const uint16_t* P, float* H, int64_t d, int64_t k,
+                                      hipStream_t st) {
+  ApplyBatch b = {};
+  small_plan<R>(b, 1, &d, &k);
+  b.it[0].C = C;
+  b.it[0].P = P;
+  b.it[0].d = d;
+  b.it[0].k = k;
+  b.H = H;
+  hipLaunchKernelGGL((small_update_kernel<R, kModeReconstruct>), dim3((unsigned)b.wbase[1]), dim3(256), 0, st, b);
+  return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+}
+
 template <int R>
 rgc_status_t reconstruct_launch(const float* C, const uint16_t* P, float* H, int64_t d, int64_t k, hipStream_t st) {
   ApplyBatch b = {};
@@ -1095,6 +1404,7 @@ extern "C" size_t rgc_apply_batch_workspace_size(int64_t n, const int64_t* ds, c
   for (int64_t m = 0; m < n; ++m)
     if (ds[m] <= 0 || ks[m] <= 0) return 0;
   size_t out = 0;
+  if (dispatch_small_rank(r, [&](auto rc) { out = small_ws_for<decltype(rc)::value>((int)n, ds, ks); })) return out;
   dispatch_rank(r, [&](auto rc) { out = apply_ws_for<decltype(rc)::value>((int)n, ds, ks); });
   return out;
 }
@@ -1118,9 +1428,13 @@ extern "C" rgc_status_t rgc_apply_batch(int64_t n, uint16_t* const* Ws, const in
   if (!ws || ws_bytes < need) return RGC_ERR_WORKSPACE;
   if (!aligned_to(ws, 256)) return RGC_ERR_ALIGN;
   rgc_status_t st = RGC_OK;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (dispatch_small_rank(r, [&](auto rc) {
+        st = small_apply_launch<decltype(rc)::value>((int)n, Ws, ldws, Cs, Ps, ds, ks, tau, seeds, stats, ws, hs);
+      }))
+    return st;
   dispatch_rank(r, [&](auto rc) {
-    st = apply_launch<decltype(rc)::value>((int)n, Ws, ldws, Cs, Ps, ds, ks, tau, seeds, stats, ws,
-                                           static_cast<hipStream_t>(stream));
+    st = apply_launch<decltype(rc)::value>((int)n, Ws, ldws, Cs, Ps, ds, ks, tau, seeds, stats, ws, hs);
   });
   return st;
 }
@@ -1146,10 +1460,16 @@ extern "C" rgc_status_t rgc_apply_carried_batch(int64_t n, uint16_t* const* Ws, 
   if (!ws || ws_bytes < need) return RGC_ERR_WORKSPACE;
   if (!aligned_to(ws, 256)) return RGC_ERR_ALIGN;
   rgc_status_t st = RGC_OK;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int carry = fresh ? kCarryFresh : kCarryIn;
+  if (dispatch_small_rank(r, [&](auto rc) {
+        st = small_apply_launch<decltype(rc)::value>((int)n, Ws, ldws, Cs, Ps, ds, ks, tau, seeds, stats, ws, hs,
+                                                     nullptr, carry, wnorm2);
+      }))
+    return st;
   dispatch_rank(r, [&](auto rc) {
-    st = apply_launch<decltype(rc)::value>((int)n, Ws, ldws, Cs, Ps, ds, ks, tau, seeds, stats, ws,
-                                           static_cast<hipStream_t>(stream), nullptr,
-                                           fresh ? kCarryFresh : kCarryIn, wnorm2);
+    st = apply_launch<decltype(rc)::value>((int)n, Ws, ldws, Cs, Ps, ds, ks, tau, seeds, stats, ws, hs, nullptr,
+                                           carry, wnorm2);
   });
   return st;
 }
@@ -1190,9 +1510,14 @@ extern "C" rgc_status_t rgc_apply_scaled_batch(int64_t n, uint16_t* const* Ws, c
     if (!std::isfinite(alphas[m])) return RGC_ERR_VALUE;
   }
   rgc_status_t st = RGC_OK;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (dispatch_small_rank(r, [&](auto rc) {
+        st = small_apply_launch<decltype(rc)::value>((int)n, Ws, ldws, Cs, Ps, ds, ks, 0.f, seeds, nullptr, nullptr,
+                                                     hs, alphas);
+      }))
+    return st;
   dispatch_rank(r, [&](auto rc) {
-    st = apply_launch<decltype(rc)::value>((int)n, Ws, ldws, Cs, Ps, ds, ks, 0.f, seeds, nullptr, nullptr,
-                                           static_cast<hipStream_t>(stream), alphas);
+    st = apply_launch<decltype(rc)::value>((int)n, Ws, ldws, Cs, Ps, ds, ks, 0.f, seeds, nullptr, nullptr, hs, alphas);
   });
   return st;
 }
@@ -1210,9 +1535,10 @@ extern "C" rgc_status_t rgc_test_reconstruct(const float* C, const uint16_t* P, 
   if (!C || !P || !H) return RGC_ERR_NULL;
   if (!aligned16(C) || !aligned16(P) || !aligned16(H)) return RGC_ERR_ALIGN;
   rgc_status_t st = RGC_OK;
-  dispatch_rank(r, [&](auto rc) {
-    st = reconstruct_launch<decltype(rc)::value>(C, P, H, d, k, static_cast<hipStream_t>(stream));
-  });
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (dispatch_small_rank(r, [&](auto rc) { st = small_reconstruct_launch<decltype(rc)::value>(C, P, H, d, k, hs); }))
+    return st;
+  dispatch_rank(r, [&](auto rc) { st = reconstruct_launch<decltype(rc)::value>(C, P, H, d, k, hs); });
   return st;
 }
 

@@ -164,5 +164,31 @@ __device__ __forceinline__ double wave_sum(double v) {
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
+// The same for a float. A xor butterfly pairs the same two partial sums in
+// both lanes of every exchange, so all 64 lanes end with the same bits.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// R (4 or 8) consecutive bf16 values at p (8- or 16-byte aligned) as floats.
+template <int R>
+__device__ __forceinline__ void load_bf16_row(const uint16_t* p, float (&out)[R]) {
+  static_assert(R == 4 || R == 8, "small rank");
+  uint32_t w[R / 2];
+  if constexpr (R == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+#pragma unroll
+  for (int i = 0; i < R / 2; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
 
 }  // namespace rgc

@@ -30,7 +30,10 @@ constexpr size_t kNoAllocScratchBytes = RGC_NOALLOC_SCRATCH_BYTES;
 // Ranks of the MFMA-tiled kernels: every multiple of 16 up to 256.
 inline bool rank_tiled(int64_t r) { return r >= 16 && r <= 256 && r % 16 == 0; }
 
-inline bool rank_supported(int64_t r) { return rank_tiled(r); }
+// Ranks below one MFMA tile (4 and 8) take the small-rank kernels.
+inline bool rank_small(int64_t r) { return r == 4 || r == 8; }
+
+inline bool rank_supported(int64_t r) { return rank_tiled(r) || rank_small(r); }
 
 template <int V>
 using IntC = std::integral_constant<int, V>;
@@ -57,6 +60,15 @@ bool dispatch_rank(int64_t r, F&& f) {
     }
   });
   return done;
+}
+
+// Calls f(IntC<r>{}) for a small rank (4 or 8); returns false otherwise.
+template <typename F>
+bool dispatch_small_rank(int64_t r, F&& f) {
+  if (r == 4) f(IntC<4>{});
+  else if (r == 8) f(IntC<8>{});
+  else return false;
+  return true;
 }
 
 inline bool aligned_to(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }

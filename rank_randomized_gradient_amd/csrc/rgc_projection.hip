@@ -36,14 +36,15 @@
 namespace rgc {
 
 // ---------------------------------------------------------------------------
-// Rademacher: one thread per (row, 8 columns).
+// Rademacher: one thread per (row, 8 columns), or per row when r = 4.
 // ---------------------------------------------------------------------------
 __global__ void rademacher_kernel(uint16_t* __restrict__ P, int64_t k, int r, uint64_t seed, uint32_t mag) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int groups = r / 8;
+  const int per = r < 8 ? r : 8;  // columns per thread
+  const int groups = r / per;
   if (idx >= k * groups) return;
   const int64_t i = idx / groups;
-  const int j0 = (int)(idx % groups) * 8;
+  const int j0 = (int)(idx % groups) * per;
   u32x4 c = {(uint32_t)i, (uint32_t)(j0 >> 7), kTagRademacher, 0u};
   const u32x4 o = philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
   const uint32_t words[4] = {o.x, o.y, o.z, o.w};
@@ -59,7 +60,10 @@ __global__ void rademacher_kernel(uint16_t* __restrict__ P, int64_t k, int r, ui
     }
     out[p] = pack_bf16x2(hv[0], hv[1]);
   }
-  *reinterpret_cast<uint4*>(P + i * r + j0) = make_uint4(out[0], out[1], out[2], out[3]);
+  if (per == 8)
+    *reinterpret_cast<uint4*>(P + i * r + j0) = make_uint4(out[0], out[1], out[2], out[3]);
+  else
+    *reinterpret_cast<uint2*>(P + i * r + j0) = make_uint2(out[0], out[1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -259,6 +263,68 @@ __global__ __launch_bounds__(256) void qr_block_mfma_kernel(QrBatch b) {
 #pragma unroll
       for (int tj = 0; tj < NT; ++tj) out[(16 * ti + 4 * i + lg) * R + 16 * tj + li] = acc[tj][i];
   }
+}
+
+// The same three block steps for ranks below one MFMA tile (r = 4, 8), on
+// the fp64 VALU: one wave per 64-row block, one row per lane. The multiply
+// sums a = 0 .. c in order; the block's Gram entries are lane butterflies.
+template <int R, int MODE>
+__global__ __launch_bounds__(64) void qr_block_small_kernel(QrBatch b) {
+  static_assert(R == 4 || R == 8, "small rank");
+  const int m = batch_item(b.block_begin, b.n, blockIdx.x);
+  const int64_t k = b.k[m];
+  const int64_t rbeg = (int64_t)(blockIdx.x - b.block_begin[m]) * kQrBlockRows;
+  const int64_t rend = rbeg + kQrBlockRows < k ? rbeg + kQrBlockRows : k;
+  if constexpr (MODE == 2) {
+    if (b.status[m][2] != 0u) return;  // P from the first pass is final
+  }
+  const int64_t row = rbeg + threadIdx.x;
+  const bool in = row < rend;
+  double y[R];
+#pragma unroll
+  for (int c = 0; c < R; ++c) y[c] = 0.0;
+  if constexpr (MODE == 0) {
+    if (in) {
+#pragma unroll
+      for (int q = 0; q < R / 4; ++q) {
+        double z[4];
+        gaussian4(b.seed[m], row, q, z);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) y[4 * q + x] = z[x];
+      }
+#pragma unroll
+      for (int c = 0; c < R; ++c) b.A[m][row * R + c] = y[c];
+    }
+  } else {
+    const double* src = MODE == 2 ? b.Q1[m] : b.A[m];
+    const double* U = MODE == 1 ? b.U1[m] : b.U2[m];
+    double x[R];
+#pragma unroll
+    for (int a = 0; a < R; ++a) x[a] = in ? src[row * R + a] : 0.0;
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      double acc = 0.0;
+#pragma unroll
+      for (int a = 0; a <= c; ++a) acc += x[a] * U[a * R + c];
+      y[c] = acc;
+    }
+    if (in) {
+#pragma unroll
+      for (int c = 0; c < R; ++c) {
+        if constexpr (MODE == 1) b.Q1[m][row * R + c] = y[c];
+        b.P[m][row * R + c] = (uint16_t)f32_to_bf16_rne((float)(b.scale[m] * y[c]));
+      }
+    }
+    if constexpr (MODE == 2) return;
+  }
+  double* out = b.part[m] + (int64_t)(blockIdx.x - b.block_begin[m]) * R * R;
+#pragma unroll
+  for (int a = 0; a < R; ++a)
+#pragma unroll
+    for (int c = 0; c < R; ++c) {
+      const double v = wave_sum(y[a] * y[c]);
+      if (threadIdx.x == 0) out[a * R + c] = v;
+    }
 }
 
 // G = sum of a matrix's block partials in block order, upper triangle only
@@ -484,17 +550,25 @@ rgc_status_t qr_launch(int n, const uint64_t* seeds, const int64_t* ks, uint16_t
     off += l.total;
   }
   const dim3 red_grid((unsigned)((R * R + 255) / 256), (unsigned)n);
-  hipLaunchKernelGGL((qr_block_mfma_kernel<R, 0>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
+  const dim3 blocks((unsigned)b.block_begin[n]);
+  auto block_step = [&](auto mode) {
+    constexpr int MODE = decltype(mode)::value;
+    if constexpr (R < 16)
+      hipLaunchKernelGGL((qr_block_small_kernel<R, MODE>), blocks, dim3(64), 0, s, b);
+    else
+      hipLaunchKernelGGL((qr_block_mfma_kernel<R, MODE>), blocks, dim3(256), 0, s, b);
+  };
+  block_step(IntC<0>{});
   hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
   hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(QrFactorShape<R>::THREADS), 0, s, b, G_all, 0);
-  hipLaunchKernelGGL((qr_block_mfma_kernel<R, 1>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
+  block_step(IntC<1>{});
   hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
   hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(QrFactorShape<R>::THREADS), 0, s, b, G_all, 1);
-  hipLaunchKernelGGL((qr_block_mfma_kernel<R, 2>), dim3(b.block_begin[n]), dim3(256), 0, s, b);
+  block_step(IntC<2>{});
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
-bool qr_rank_supported(int64_t r) { return r >= 16 && r <= 128 && r % 16 == 0; }
+bool qr_rank_supported(int64_t r) { return rank_small(r) || (r >= 16 && r <= 128 && r % 16 == 0); }
 
 uint32_t rademacher_magnitude(int64_t r) {
   // a = bf16(fp32(1/sqrt(r))), both roundings to nearest even
@@ -557,7 +631,7 @@ extern "C" rgc_status_t rgc_sample_projections(rgc_proj_kind_t kind, int64_t n, 
   if (kind == RGC_PROJ_RADEMACHER) {
     const uint32_t mag = rademacher_magnitude(r);
     for (int64_t m = 0; m < n; ++m) {
-      const int64_t cnt = ks[m] * (r / 8);
+      const int64_t cnt = ks[m] * (r < 8 ? 1 : r / 8);  // threads of rademacher_kernel
       hipLaunchKernelGGL(rademacher_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, s, Ps[m], ks[m], (int)r,
                          seeds[m], mag);
     }
@@ -567,6 +641,8 @@ extern "C" rgc_status_t rgc_sample_projections(rgc_proj_kind_t kind, int64_t n, 
   if (!ws || ws_bytes < need) return RGC_ERR_WORKSPACE;
   if (!aligned_to(ws, 256)) return RGC_ERR_ALIGN;
   rgc_status_t st = RGC_ERR_UNSUPPORTED;
+  if (dispatch_small_rank(r, [&](auto rc) { st = qr_launch<decltype(rc)::value>((int)n, seeds, ks, Ps, ws, s); }))
+    return st;
   static_for<1, 9>([&](auto q) {
     constexpr int R = 16 * decltype(q)::value;
     if (r == R) st = qr_launch<R>((int)n, seeds, ks, Ps, ws, s);

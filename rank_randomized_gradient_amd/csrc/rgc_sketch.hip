@@ -638,9 +638,195 @@ __global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
 }
 
 // ---------------------------------------------------------------------------
+// Ranks below one MFMA tile (r = 4, 8): the rank operand rows are 8 or 16
+// bytes, so these contractions stream X or D with plain 16-byte loads and
+// sum on the VALU. Products of bf16 values are exact in fp32; the sums are
+// fp32 in a fixed order, so results are bit-reproducible.
+// ---------------------------------------------------------------------------
+struct SmallProjectBatch {
+  int n;
+  int64_t T;
+  const uint16_t* X[kMaxItems];
+  int64_t ldx[kMaxItems];
+  int64_t k[kMaxItems];
+  const uint16_t* P[kMaxItems];
+  uint16_t* XP[kMaxItems];
+};
+
+// One wave per token row: lane l sums the 8-value chunks l, l + 64, ... of
+// the row against the matching P rows, then a butterfly adds the 64 lane
+// sums; one rounding to bf16.
+template <int R>
+__global__ __launch_bounds__(256) void small_project_kernel(SmallProjectBatch b) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int m = (int)(row / b.T);
+  if (m >= b.n) return;
+  const int64_t t = row - (int64_t)m * b.T;
+  const uint16_t* __restrict__ x = b.X[m] + t * b.ldx[m];
+  const uint16_t* __restrict__ P = b.P[m];
+  const int64_t chunks = b.k[m] / 8;
+  float acc[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) acc[j] = 0.f;
+  for (int64_t c = lane; c < chunks; c += 64) {
+    const uint4 xv = *reinterpret_cast<const uint4*>(x + 8 * c);
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xe = __uint_as_float(e & 1 ? (xw[e / 2] & 0xFFFF0000u) : (xw[e / 2] << 16));
+      float p[R];
+      load_bf16_row<R>(P + (8 * c + e) * R, p);
+#pragma unroll
+      for (int j = 0; j < R; ++j) acc[j] += xe * p[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < R; ++j) acc[j] = wave_sum_f32(acc[j]);
+  if (lane == 0) {
+    uint32_t o[R / 2];
+#pragma unroll
+    for (int i = 0; i < R / 2; ++i) o[i] = pack_bf16x2(f32_to_bf16_rne(acc[2 * i]), f32_to_bf16_rne(acc[2 * i + 1]));
+    uint16_t* dst = b.XP[m] + t * R;
+    if constexpr (R == 4)
+      *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
+    else
+      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Tokens per partial sum of the small-rank accumulate.
+constexpr int kSmallTokenChunk = 128;
+
+struct SmallAccumulateBatch {
+  int n;
+  int64_t T;
+  int64_t chunks;                  // 8-column chunks of all items
+  int64_t cbase[kMaxItems + 1];    // first chunk of each item
+  const uint16_t* D[kMaxItems];
+  int64_t ldd[kMaxItems];
+  const uint16_t* XP[kMaxItems];
+  float* C[kMaxItems];
+  float* part;                     // per (token chunk, column chunk): 8 x R fp32
+};
+
+__device__ __forceinline__ int small_item(const int64_t* base, int n, int64_t c) {
+  int m = 0;
+  while (m + 1 < n && c >= base[m + 1]) ++m;
+  return m;
+}
+
+// Thread (column chunk, token chunk): the 8 x R sums of D[t][8c .. 8c+7] *
+// XP[t][0 .. R-1] over the chunk's tokens in order.
+template <int R>
+__global__ __launch_bounds__(256) void small_accumulate_kernel(SmallAccumulateBatch b) {
+  const int64_t gc = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gc >= b.chunks) return;
+  const int m = small_item(b.cbase, b.n, gc);
+  const int64_t cc = gc - b.cbase[m];
+  const int64_t t0 = (int64_t)blockIdx.y * kSmallTokenChunk;
+  const int64_t t1 = t0 + kSmallTokenChunk < b.T ? t0 + kSmallTokenChunk : b.T;
+  const uint16_t* __restrict__ D = b.D[m] + 8 * cc;
+  const uint16_t* __restrict__ XP = b.XP[m];
+  float acc[8][R];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int j = 0; j < R; ++j) acc[e][j] = 0.f;
+  for (int64_t t = t0; t < t1; ++t) {
+    const uint4 dv = *reinterpret_cast<const uint4*>(D + t * b.ldd[m]);
+    const uint32_t dw[4] = {dv.x, dv.y, dv.z, dv.w};
+    float xp[R];
+    load_bf16_row<R>(XP + t * R, xp);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float de = __uint_as_float(e & 1 ? (dw[e / 2] & 0xFFFF0000u) : (dw[e / 2] << 16));
+#pragma unroll
+      for (int j = 0; j < R; ++j) acc[e][j] += de * xp[j];
+    }
+  }
+  float4* out = reinterpret_cast<float4*>(b.part + ((int64_t)blockIdx.y * b.chunks + gc) * 8 * R);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int j = 0; j < R; j += 4) out[(e * R + j) / 4] = make_float4(acc[e][j], acc[e][j + 1], acc[e][j + 2], acc[e][j + 3]);
+}
+
+// Thread per C element: its token-chunk partials summed in chunk order, then
+// added to C (one writer per element).
+template <int R>
+__global__ __launch_bounds__(256) void small_accumulate_finish_kernel(SmallAccumulateBatch b, int tchunks) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t gc = idx / (8 * R);
+  if (gc >= b.chunks) return;
+  const int q = (int)(idx % (8 * R));
+  const int m = small_item(b.cbase, b.n, gc);
+  const int64_t cc = gc - b.cbase[m];
+  float sum = 0.f;
+  for (int tc = 0; tc < tchunks; ++tc) {
+    const float v = b.part[((int64_t)tc * b.chunks + gc) * 8 * R + q];
+    sum = tc == 0 ? v : sum + v;
+  }
+  float* c = b.C[m] + (8 * cc + q / R) * R + q % R;
+  *c += sum;
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 namespace {
+
+template <int R>
+rgc_status_t small_project_launch(int n, const uint16_t* const* Xs, const int64_t* ldxs, const int64_t* ks,
+                                  const uint16_t* const* Ps, uint16_t* const* XPs, int64_t T, hipStream_t st) {
+  SmallProjectBatch b = {};
+  b.n = n;
+  b.T = T;
+  for (int m = 0; m < n; ++m) {
+    b.X[m] = Xs[m];
+    b.ldx[m] = ldxs[m];
+    b.k[m] = ks[m];
+    b.P[m] = Ps[m];
+    b.XP[m] = XPs[m];
+  }
+  const int64_t rows = (int64_t)n * T;
+  hipLaunchKernelGGL(small_project_kernel<R>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, b);
+  return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+}
+
+int64_t small_token_chunks(int64_t T) { return (T + kSmallTokenChunk - 1) / kSmallTokenChunk; }
+
+template <int R>
+size_t small_accumulate_workspace(int n, const int64_t* ds, int64_t T) {
+  int64_t chunks = 0;
+  for (int m = 0; m < n; ++m) chunks += ds[m] / 8;
+  return (size_t)small_token_chunks(T) * chunks * 8 * R * sizeof(float);
+}
+
+template <int R>
+rgc_status_t small_accumulate_launch(int n, const uint16_t* const* Ds, const int64_t* ldds, const int64_t* ds,
+                                     const uint16_t* const* XPs, float* const* Cs, int64_t T, void* ws,
+                                     hipStream_t st) {
+  SmallAccumulateBatch b = {};
+  b.n = n;
+  b.T = T;
+  b.cbase[0] = 0;
+  for (int m = 0; m < n; ++m) {
+    b.D[m] = Ds[m];
+    b.ldd[m] = ldds[m];
+    b.XP[m] = XPs[m];
+    b.C[m] = Cs[m];
+    b.cbase[m + 1] = b.cbase[m] + ds[m] / 8;
+  }
+  b.chunks = b.cbase[n];
+  b.part = static_cast<float*>(ws);
+  const int64_t tchunks = small_token_chunks(T);
+  hipLaunchKernelGGL(small_accumulate_kernel<R>, dim3((unsigned)((b.chunks + 255) / 256), (unsigned)tchunks), dim3(256),
+                     0, st, b);
+  hipLaunchKernelGGL(small_accumulate_finish_kernel<R>, dim3((unsigned)((b.chunks * 8 * R + 255) / 256)), dim3(256), 0,
+                     st, b, (int)tchunks);
+  return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+}
 
 // Workgroups per launch: one per compute unit (two fit, but measured on the
 // Qwen3-1.7B-shaped block one is faster: the second adds L2/request pressure
@@ -819,6 +1005,7 @@ size_t project_ws_impl(int64_t n, const int64_t* ks, int64_t T, int64_t r, int64
   if (n <= 0 || n > kMaxItems || !ks || T <= 0) return 0;
   for (int64_t m = 0; m < n; ++m)
     if (ks[m] <= 0) return 0;
+  if (rank_small(r)) return 0;  // no partial sums
   int64_t ns[kMaxItems];
   for (int64_t m = 0; m < n; ++m) ns[m] = T;
   size_t out = 0;
@@ -835,6 +1022,8 @@ size_t accumulate_ws_impl(int64_t n, const int64_t* ds, int64_t T, int64_t r, in
   for (int64_t m = 0; m < n; ++m)
     if (ds[m] <= 0) return 0;
   size_t out = 0;
+  if (dispatch_small_rank(r, [&](auto rc) { out = small_accumulate_workspace<decltype(rc)::value>((int)n, ds, T); }))
+    return out;
   if (!dispatch_rank(r, [&](auto rc) {
         constexpr int R = decltype(rc)::value;
         out = accumulate_workspace<R>((int)n, ds, T, forced);
@@ -858,9 +1047,13 @@ rgc_status_t project_batch_impl(int64_t n, const uint16_t* const* Xs, const int6
   if (need > 0 && (!ws || ws_bytes < need)) return RGC_ERR_WORKSPACE;
   if (need > 0 && !aligned_to(ws, 256)) return RGC_ERR_ALIGN;
   rgc_status_t st = RGC_OK;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (dispatch_small_rank(r, [&](auto rc) {
+        st = small_project_launch<decltype(rc)::value>((int)n, Xs, ldxs, ks, Ps, XPs, T, hs);
+      }))
+    return st;
   dispatch_rank(r, [&](auto rc) {
-    st = project_launch<decltype(rc)::value>((int)n, Xs, ldxs, ks, Ps, XPs, T, ws, static_cast<hipStream_t>(stream),
-                                             forced);
+    st = project_launch<decltype(rc)::value>((int)n, Xs, ldxs, ks, Ps, XPs, T, ws, hs, forced);
   });
   return st;
 }
@@ -880,9 +1073,13 @@ rgc_status_t accumulate_batch_impl(int64_t n, const uint16_t* const* Ds, const i
   if (need > 0 && (!ws || ws_bytes < need)) return RGC_ERR_WORKSPACE;
   if (need > 0 && !aligned_to(ws, 256)) return RGC_ERR_ALIGN;
   rgc_status_t st = RGC_OK;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (dispatch_small_rank(r, [&](auto rc) {
+        st = small_accumulate_launch<decltype(rc)::value>((int)n, Ds, ldds, ds, XPs, Cs, T, ws, hs);
+      }))
+    return st;
   dispatch_rank(r, [&](auto rc) {
-    st = accumulate_launch<decltype(rc)::value>((int)n, Ds, ldds, ds, XPs, Cs, T, ws,
-                                                static_cast<hipStream_t>(stream), forced);
+    st = accumulate_launch<decltype(rc)::value>((int)n, Ds, ldds, ds, XPs, Cs, T, ws, hs, forced);
   });
   return st;
 }

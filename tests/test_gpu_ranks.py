@@ -1,9 +1,12 @@
-"""GPU parity at every supported rank: every multiple of 16 up to 256 (any
-rank r << min(d, k) [page "LoGRA: Low-Rank Gradient Sketches", "The Core
-Move"]). Ranks whose count of 16-column blocks is odd above 128 (144, 176,
-208, 240) run the sketch contractions at a padded compute width; 80, 96, 112
-take the one-wave split and the 64-row update tiles. Shapes are ragged (T,
-d, k not multiples of the tiles) so that every path through the edges runs.
+"""GPU parity at every supported rank: 4 and 8, and every multiple of 16 up
+to 256 (any rank r << min(d, k) [page "LoGRA: Low-Rank Gradient Sketches",
+"The Core Move"]; its rank sweep starts at 4 [page "LoGRA: Scaling LLM
+Reinforcement Learning with Low-Rank Gradient Sketches", "Main Findings"]).
+Ranks 4 and 8 run the small-rank kernels (VALU sums, fp64 Gram norms);
+ranks whose count of 16-column blocks is odd above 128 (144, 176, 208, 240)
+run the sketch contractions at a padded compute width; 80, 96, 112 take the
+one-wave split and the 64-row update tiles. Shapes are ragged (T, d, k not
+multiples of the tiles) so that every path through the edges runs.
 
 Bars as in test_gpu_parity.py: XP within 1 ulp + 2^-20 sum|xp| (<= 1e-3 of
 elements differing), C and H within 1e-5 / 2e-5 relative Frobenius, W within
@@ -22,7 +25,7 @@ pytestmark = pytest.mark.gpu
 
 bits = synth.to_numpy_bits
 from_bits = synth.from_numpy_bits
-RANKS = list(range(16, 257, 16))
+RANKS = [4, 8] + list(range(16, 257, 16))
 
 
 @pytest.fixture(scope="module")
@@ -136,3 +139,72 @@ def test_qr_every_rank(dev, r):
     got = rgc.rgc_sample_projection("qr", 200 + r, k, r, device=dev)
     torch.cuda.synchronize()
     assert qr_margin_mismatches(bits(got), 200 + r, k, r) <= 2
+
+
+@pytest.mark.parametrize("r", [4, 8, 16, 112, 144])
+def test_apply_carried_every_path(dev, r):
+    """Three carried updates (the first streams ||W||) through the small-rank,
+    Gram-form and rebuilt-norm paths: each rounds exactly the GPU's own h with
+    the reported s, and the carried value is the written weights' ||W||^2."""
+    d, k = 264, 1048
+    w, c, p = _apply_inputs(d, k, r, 13 * r)
+    cg, pg = c.to(dev), p.to(dev)
+    h32 = rgc.rgc_test_reconstruct(cg, pg).cpu().numpy()
+    wg = w.clone().to(dev)
+    wn2 = torch.zeros(1, dtype=torch.float64, device=dev)
+    prev = bits(w)
+    for u in range(3):
+        stats = torch.zeros(4, device=dev)
+        rgc.rgc_apply_carried(wg, cg, pg, 1e-3, 77 + u, wn2, fresh=(u == 0), stats=stats)
+        torch.cuda.synchronize()
+        st = stats.cpu().numpy()
+        _, ref_stats = orc.apply_update(prev, c.numpy(), bits(p), 1e-3, 77 + u)
+        np.testing.assert_allclose(st[:3], ref_stats[:3], rtol=1e-5)
+        got = bits(wg)
+        v = orc.pre_round_values(prev, h32, np.float32(st[2]))
+        assert np.array_equal(got, orc.stochastic_round(v, orc.rounding_bits(77 + u, d, k))), u
+        assert wn2.item() == pytest.approx(orc.weight_sumsq(got), rel=1e-6)
+        prev = got
+
+
+@pytest.mark.parametrize("r", [4, 8])
+def test_small_rank_zero_sketch_skips(dev, r):
+    d, k = 136, 520
+    w, _, p = _apply_inputs(d, k, r, 3)
+    wg = w.clone().to(dev)
+    stats = torch.full((4,), -1.0, device=dev)
+    rgc.rgc_apply(wg, torch.zeros(d, r, device=dev), p.to(dev), 1e-3, 1, stats=stats)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(wg), bits(w))
+    st = stats.cpu().numpy()
+    assert st[1] == 0 and st[2] == 0 and st[3] == 1
+
+
+@pytest.mark.parametrize("r", [4, 16, 64, 256])
+def test_logra_fixed_rademacher_loop(dev, r):
+    """The LoGRA loop at its sweep's ranks [page "LoGRA: Low-Rank Gradient
+    Sketches", "Minimal Causal Code"]: a Rademacher P from a seed, a sketch
+    accumulated over microbatches, the fixed-step update W -= alpha C P^T;
+    against the oracle's loop (P bit-exact, C within 1e-4, W within the
+    update bar)."""
+    d, k, T, mb, alpha, seed = 264, 1048, 512, 128, 2e-5, 31
+    x = synth.normal_bf16((T, k), 1.0, seed=r + 60)
+    dd = synth.normal_bf16((T, d), 1e-3, seed=r + 61)
+    w = synth.normal_bf16((d, k), 0.02, seed=r + 62)
+    p_ref = orc.rademacher_projection(seed, k, r)
+    c_ref = np.zeros((d, r), np.float32)
+    for i in range(0, T, mb):
+        c_ref = orc.accumulate(c_ref, bits(dd[i:i + mb]), orc.project(bits(x[i:i + mb]), p_ref))
+    w_ref = orc.apply_scaled(bits(w), c_ref, p_ref, np.float32(alpha), seed + 1)
+    p = rgc.rgc_sample_projection("rademacher", seed, k, r, device=dev)
+    c = torch.zeros(d, r, device=dev)
+    xg, dg = x.to(dev), dd.to(dev)
+    for i in range(0, T, mb):
+        rgc.rgc_accumulate(dg[i:i + mb], rgc.rgc_project(xg[i:i + mb], p), c)
+    wg = w.clone().to(dev)
+    rgc.rgc_apply_scaled(wg, c, p, alpha, seed + 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(p), p_ref)
+    assert rel_frobenius(c.cpu().numpy(), c_ref) < 1e-4
+    abs_terms = np.abs(c_ref.astype(np.float64)) @ np.abs(orc.bf16_to_f64(p_ref)).T
+    assert_update_close(bits(wg), w_ref, alpha, abs_terms, max_mismatch_frac=1e-3, what=f"LoGRA W r={r}")

@@ -268,3 +268,15 @@ def test_noalloc_rejects_oversized_calls_before_any_launch(lib):
     assert lib.rgc_apply_noalloc(FAKE, 63, FAKE, FAKE, 16, 64, 16, 1e-3, 1, None, None) == SHAPE
     assert lib.rgc_apply_noalloc(None, 64, FAKE, FAKE, 16, 64, 16, 1e-3, 1, None, None) == NULL
     assert lib.rgc_apply_noalloc(FAKE, 64, FAKE, FAKE, 16, 64, 40, 1e-3, 1, None, None) == UNSUP
+
+
+def test_small_ranks_are_supported(lib):
+    """Ranks 4 and 8 are accepted by every workspace query (nonzero where a
+    workspace is used); 12 is not a supported rank."""
+    assert lib.rgc_sample_projection_workspace_size(1, 2048, 4) > 0  # QR at r = 4
+    assert lib.rgc_sample_projection_workspace_size(1, 2048, 8) > 0
+    assert lib.rgc_accumulate_workspace_size(4096, 2048, 4) > 0
+    assert lib.rgc_apply_workspace_size(2048, 2048, 8) > 0
+    assert lib.rgc_apply_workspace_size(2048, 2048, 12) == 0
+    s = None
+    assert lib.rgc_project(FAKE, 64, FAKE, FAKE, 16, 64, 12, None, 0, s) == UNSUP
