@@ -139,6 +139,21 @@ rgc_status_t rgc_project_batch(int64_t n, const uint16_t* const* Xs, const int64
                                const uint16_t* const* Ps, uint16_t* const* XPs, int64_t T, int64_t r, void* ws,
                                size_t ws_bytes, void* stream);
 
+/* One pass over a shared X [RGC, "How it works": every projection of a layer
+ * keeps X P]: XPs[i] = bf16(X Ps[i]) for the n <= 4 projections of the
+ * matrices that read the same input X (a block's q, k and v; gate and up),
+ * with X streamed from memory once for all of them: the rank operand is the
+ * n projections side by side (n * r <= 256 ranks; r a multiple of 16). X: T
+ * x k bf16, row stride ldx; Ps[i]: k x r bf16; XPs[i]: T x r bf16; Ps and
+ * XPs are HOST arrays of n device pointers. Rounding as rgc_project (the
+ * fp32 summation order may differ). rgc_project_batch does not group items
+ * itself: on the Qwen3-shaped blocks the grouped schedule measured slower
+ * than one item per matrix (per-CU streaming, not the repeated X reads,
+ * bounds the project there). */
+size_t rgc_project_shared_workspace_size(int64_t n, int64_t T, int64_t k, int64_t r);
+rgc_status_t rgc_project_shared(int64_t n, const uint16_t* X, int64_t ldx, int64_t k, const uint16_t* const* Ps,
+                                uint16_t* const* XPs, int64_t T, int64_t r, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- 3. Sketch accumulation ----------------------------------------------- */
 
 /* Workspace bytes rgc_accumulate needs (split-token partial sums). */
@@ -324,6 +339,12 @@ rgc_status_t rgc_test_accumulate_batch_wgs(int64_t workgroups, int64_t n, const 
                                            const int64_t* ldds, const int64_t* ds, const uint16_t* const* XPs,
                                            float* const* Cs, int64_t T, int64_t r, void* ws, size_t ws_bytes,
                                            void* stream);
+
+/* rgc_project_shared with a caller-given workgroup count (as above). */
+size_t rgc_test_project_shared_workspace_size(int64_t workgroups, int64_t n, int64_t T, int64_t k, int64_t r);
+rgc_status_t rgc_test_project_shared_wgs(int64_t workgroups, int64_t n, const uint16_t* X, int64_t ldx, int64_t k,
+                                         const uint16_t* const* Ps, uint16_t* const* XPs, int64_t T, int64_t r,
+                                         void* ws, size_t ws_bytes, void* stream);
 
 /* H = C P^T in fp32 through the apply kernel's tile code (d x k, row stride k). */
 rgc_status_t rgc_test_reconstruct(const float* C, const uint16_t* P, float* H, int64_t d,

@@ -22,6 +22,7 @@ from .rgc import (  # noqa: F401
     rgc_apply_scaled_batch,
     rgc_project,
     rgc_project_batch,
+    rgc_project_shared,
     rgc_sample_projection,
     rgc_sample_projections,
     rgc_test_philox,

@@ -144,12 +144,12 @@ __host__ __device__ constexpr int sketch_width(int RM) { return RM > 128 && (RM 
 // Waves along r: up to 128 ranks one (the N tile is 256 wide, each wave holds
 // all ranks, up to 8 M-tiles); above 128 two, each with half the ranks, so
 // that the N tile is 128 wide and the rank operand is re-read half as often
-// as with four waves of a quarter; 192 four. (Measured on the 1.7B block at
-// r = 256 and the 8B layer at r = 128 against the previous split, which gave
-// every wave at most 64 ranks.)
+// as with four waves of a quarter. (Measured on the 1.7B block at r = 256
+// and the 8B layer at r = 128 against a split that gave every wave at most
+// 64 ranks.)
 template <int R, int KH>
 struct StageShape {
-  static constexpr int WR = R <= 128 ? 1 : (R == 192 ? 4 : 2);
+  static constexpr int WR = R <= 128 ? 1 : 2;
   static constexpr int WN = 4 / WR;                              // waves along N
   static constexpr int RW = R / WR;                              // r per wave
   static constexpr int MT = RW / 16;                             // MFMA M-tiles per wave
@@ -179,14 +179,24 @@ using AccTile = f32x4_t[StageShape<R, 1>::MT][4];
 //                                          the compute side never uses them)
 //   stream_offset(m, tile, c, lane, rows)  per-lane byte offset of stream copy c
 //   stream_base(m, tile, wb)               wave-uniform base of the window at K row wb
-//   rank_base(m)                           the item's rank operand
+//   rank_base(m, mi)                       rank operand of member mi of the item
 //   read_b(stage, kh, wn, g, li, b)        the B operands of the wave's four N-tiles, K-half kh
 //   mask_b(b, wb, kh, k0, end, g)          zero B's K slots outside [k0, end)
 //   store(res, m, tile, full, slot, wn, rw, g, li)
-template <int RM, int KH, typename Policy>
+//
+// An item may be a group of GM members that share the stream operand (the
+// project of several matrices that read the same X): the rank operand is then
+// the members' RM-column operands side by side, GM * RM columns in all, and
+// every stream slab in LDS is multiplied by all of them. In a stage the rank
+// blocks are laid out member by member (member mi's blocks (kq, b) at block
+// mi * 8 KH * NRB_ITEM + kq * NRB_ITEM + b), so that every 1 KB copy comes
+// from a single member's operand.
+template <int RM, int KH, typename Policy, int GM = 1>
 __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, char* smem) {
-  constexpr int R = sketch_width(RM);  // compute width; RM columns are in memory (row stride RM)
-  constexpr int NRB_MEM = RM / 16;     // rank blocks that exist in memory
+  constexpr int R = sketch_width(GM * RM);  // compute width; each member has RM columns (row stride RM)
+  constexpr int NRB_ITEM = RM / 16;         // rank blocks of one member
+  constexpr int NRB_MEM = GM * NRB_ITEM;    // rank blocks that exist in memory
+  constexpr int CPM = KH * NRB_ITEM;        // rank copies per member and stage
   using Sh = StageShape<R, KH>;
   constexpr int S = Sh::S, MT = Sh::MT, KS = Sh::KS;
   const int lane = threadIdx.x & 63, wave = wave_index();
@@ -203,13 +213,21 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
   int lm = m0;
   int64_t ltile = tile0, lk = k0, lu = u0;
   int64_t l_kext = 0, l_nkb = 0, l_tiles = 0;
-  const uint16_t* l_rank = nullptr;
+  const uint16_t* l_rank[GM];  // the members' rank operands
   uint32_t voff[Sh::NV_HI];
+  // the member and the copy within the member of rank copy cr (copies past the
+  // members, the padding, repeat the last one)
+  auto rank_copy = [&](int cr, int& mi, int& cl) {
+    cr = cr < NRB_MEM * KH ? cr : NRB_MEM * KH - 1;
+    mi = GM == 1 ? 0 : cr / CPM;
+    cl = cr - mi * CPM;
+  };
   auto enter_item = [&](int m) {
     l_kext = uniform_i64(s.kext[m]);
     l_nkb = uniform_i64(s.nkb[m]);
     l_tiles = uniform_i64(s.tbase[m + 1] - s.tbase[m]);
-    l_rank = uniform_ptr(pol.rank_base(m));
+#pragma unroll
+    for (int mi = 0; mi < GM; ++mi) l_rank[mi] = uniform_ptr(pol.rank_base(m, mi));
     pol.enter_item(m);
   };
   auto set_offsets = [&](int m, int64_t tile) {
@@ -220,12 +238,12 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
       if (c < Sh::NSC) {
         voff[v] = pol.stream_offset(m, tile, c, lane, rows);
       } else {
-        const int blk = 8 * (c - Sh::NSC) + (lane >> 3);
-        int64_t kr = 4 * (blk / Sh::NRB) + ((lane & 7) >> 1);
+        int mi = 0, cl = 0;
+        rank_copy(c - Sh::NSC, mi, cl);
+        const int blk = 8 * cl + (lane >> 3);  // block of member mi
+        int64_t kr = 4 * (blk / NRB_ITEM) + ((lane & 7) >> 1);
         kr = kr < rows ? kr : rows - 1;
-        int rb = blk % Sh::NRB;
-        rb = rb < NRB_MEM ? rb : NRB_MEM - 1;  // a padding block copies a real one (never multiplied)
-        voff[v] = (uint32_t)((kr * RM + 16 * rb + 8 * (lane & 1)) * 2);
+        voff[v] = (uint32_t)((kr * RM + 16 * (blk % NRB_ITEM) + 8 * (lane & 1)) * 2);
       }
     }
   };
@@ -237,11 +255,23 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
   auto issue = [&]() {
     const int64_t wb = window_base(lk * KS, l_kext, KS);
     const uint16_t* Sb = uniform_ptr(pol.stream_base(lm, ltile, wb));
-    const uint16_t* Rb = uniform_ptr(l_rank + wb * RM);
     const uint32_t st = lds0 + lslot * Sh::STAGE;
     static_for<0, Sh::NV_HI>([&](auto vc) {
       constexpr int v = decltype(vc)::value;
       const int c = wave + 4 * v;  // a stream copy if c < NSC, a rank copy if NSC <= c < NI
+      const uint16_t* Rb = nullptr;
+      if constexpr (4 * v + 3 >= Sh::NSC) {
+        if constexpr (GM == 1) {
+          Rb = uniform_ptr(l_rank[0] + wb * RM);
+        } else {
+          int mi = 0, cl = 0;  // the member this slot copies from (wave-uniform)
+          rank_copy(c - Sh::NSC, mi, cl);
+          const uint16_t* base = l_rank[0];
+#pragma unroll
+          for (int q = 1; q < GM; ++q) base = mi == q ? l_rank[q] : base;
+          Rb = uniform_ptr(base + wb * RM);
+        }
+      }
       if constexpr (4 * v + 3 < Sh::NSC) {
         dma_16b_stream(Sb, voff[v], st + 1024 * c);
       } else if constexpr (4 * v >= Sh::NSC && 4 * v + 3 < Sh::NI) {
@@ -321,8 +351,18 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            const u32x2v_t v = lds_read_tr16(st + Sh::STREAM +
-                                             128 * ((8 * kh + 2 * g + h) * Sh::NRB + rw * MT + mt) + 8 * li);
+            const int B = rw * MT + mt;  // rank block (wave-uniform)
+            // A padding block is never multiplied; with one member its read
+            // stays inside the stage (it reads some block of the stage), with
+            // several it would not, so it is skipped.
+            if (GM > 1 && R != RM * GM && B >= NRB_MEM) {
+              a[mt][2 * h] = a[mt][2 * h + 1] = 0u;
+              continue;
+            }
+            const int mi = GM == 1 ? 0 : B / NRB_ITEM;
+            const u32x2v_t v = lds_read_tr16(
+                st + Sh::STREAM + 128 * (mi * 8 * KH * NRB_ITEM + (8 * kh + 2 * g + h) * NRB_ITEM + B - mi * NRB_ITEM) +
+                8 * li);
             a[mt][2 * h] = v.x;
             a[mt][2 * h + 1] = v.y;
           }
@@ -339,7 +379,7 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          if (R != RM && rw * MT + mt >= NRB_MEM) continue;  // padding block (wave-uniform)
+          if (R != RM * GM && rw * MT + mt >= NRB_MEM) continue;  // padding block (wave-uniform)
 #pragma unroll
           for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_16x16x32(a[mt], b[nt], acc[mt][nt]);
         }
@@ -384,28 +424,33 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
 // of a group over all LDS banks.
 // ---------------------------------------------------------------------------
 constexpr int kProjectKH = 2;
+// Members of a project group: matrices that read the same X, projected in one
+// pass over it; at most 256 ranks in all.
+constexpr int kMaxGroup = 4;
 
 struct ProjectBatch {
-  Schedule s;
+  Schedule s;                     // one schedule item per group
   const uint16_t* X[kMaxItems];
   int64_t ldx[kMaxItems];
-  const uint16_t* P[kMaxItems];
-  uint16_t* XP[kMaxItems];
+  const uint16_t* P[kMaxItems][kMaxGroup];
+  uint16_t* XP[kMaxItems][kMaxGroup];
   float* part;                    // 2 G slots of TILE x R fp32
 };
 
-template <int RM>
+template <int RM, int GM>
 struct ProjectPolicy {
-  static constexpr int R = sketch_width(RM);
+  static constexpr int R = sketch_width(GM * RM);
+  static constexpr int NRB_ITEM = RM / 16;
   using Sh = StageShape<R, kProjectKH>;
-  static constexpr bool kKeepLargeFirst = true;
+  // a group's sums leave no room for a second set (measured: spills)
+  static constexpr bool kKeepLargeFirst = GM == 1;
   const ProjectBatch& pb;
   int64_t ldx = 0, T = 0;  // of the copy cursor's item
   __device__ void enter_item(int m) {
     ldx = uniform_i64(pb.ldx[m]);
     T = uniform_i64(pb.s.next[m]);
   }
-  __device__ const uint16_t* rank_base(int m) const { return pb.P[m]; }
+  __device__ const uint16_t* rank_base(int m, int mi) const { return pb.P[m][mi]; }
   __device__ const uint16_t* stream_base(int m, int64_t tile, int64_t wb) const {
     return pb.X[m] + tile * Sh::TILE * ldx + wb;
   }
@@ -448,13 +493,15 @@ struct ProjectPolicy {
       const int64_t row = 64 * wn + 16 * nt + li;  // tile-relative token
 #pragma unroll
       for (int mt = 0; mt < Sh::MT; ++mt) {
-        if (R != RM && rw * Sh::RW + 16 * mt >= RM) continue;  // padding block
+        const int B = rw * Sh::MT + mt;  // rank block
+        if (R != RM * GM && B >= GM * NRB_ITEM) continue;  // padding block
         const int rcol = rw * Sh::RW + 16 * mt + 4 * g;
         const f32x4_t v = res[mt][nt];
         if (full) {
           const int64_t t = tile * Sh::TILE + row;
+          const int mi = GM == 1 ? 0 : B / NRB_ITEM;
           if (t < pb.s.next[m])
-            *reinterpret_cast<uint2*>(pb.XP[m] + t * RM + rcol) =
+            *reinterpret_cast<uint2*>(pb.XP[m][mi] + t * RM + rcol - mi * RM) =
                 make_uint2(pack_bf16x2(f32_to_bf16_rne(v[0]), f32_to_bf16_rne(v[1])),
                            pack_bf16x2(f32_to_bf16_rne(v[2]), f32_to_bf16_rne(v[3])));
         } else {
@@ -466,12 +513,12 @@ struct ProjectPolicy {
   }
 };
 
-template <int RM>
+template <int RM, int GM>
 __global__ __launch_bounds__(256, 1) void project_kernel(ProjectBatch pb) {
-  using Sh = StageShape<sketch_width(RM), kProjectKH>;
+  using Sh = StageShape<sketch_width(GM * RM), kProjectKH>;
   __shared__ __attribute__((aligned(1024))) char smem[Sh::S * Sh::STAGE];
-  ProjectPolicy<RM> pol{pb};
-  staged_pipeline<RM, kProjectKH>(pb.s, pol, smem);
+  ProjectPolicy<RM, GM> pol{pb};
+  staged_pipeline<RM, kProjectKH, ProjectPolicy<RM, GM>, GM>(pb.s, pol, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -503,7 +550,7 @@ struct AccumulatePolicy {
     ldd = uniform_i64(ab.ldd[m]);
     d = uniform_i64(ab.s.next[m]);
   }
-  __device__ const uint16_t* rank_base(int m) const { return ab.XP[m]; }
+  __device__ const uint16_t* rank_base(int m, int) const { return ab.XP[m]; }
   __device__ const uint16_t* stream_base(int m, int64_t tile, int64_t wb) const { return ab.D[m] + wb * ldd; }
   __device__ uint32_t stream_offset(int m, int64_t tile, int c, int lane, int64_t rows) const {
     const int blk = 8 * c + (lane >> 3);
@@ -576,13 +623,13 @@ __global__ __launch_bounds__(256, 1) void accumulate_kernel(AccumulateBatch ab) 
 struct FinishBatch {
   Schedule s;
   const float* part;
-  float* C[kMaxItems];            // accumulate targets
-  uint16_t* XP[kMaxItems];        // project targets
+  float* C[kMaxItems];                    // accumulate targets
+  uint16_t* XP[kMaxItems][kMaxGroup];     // project targets (per group member)
 };
 
-template <int RM, bool TO_BF16>
+template <int RM, int GM, bool TO_BF16>
 __global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
-  constexpr int R = sketch_width(RM);  // partials are tile_n x R; outputs have row stride RM
+  constexpr int R = sketch_width(GM * RM);  // partials are tile_n x R; outputs have row stride RM
   const Schedule& s = fb.s;
   const int64_t t = blockIdx.y;
   const int m = item_of_tile(s, t);
@@ -598,8 +645,10 @@ __global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
   {
     const int64_t e = (int64_t)blockIdx.x * (256 * PER) + threadIdx.x * PER;
     if (e >= rows * R) return;
-    if (R != RM && e % R >= RM) return;  // padding columns (a float4 never straddles RM)
-    const int64_t out = (tile * tn + e / R) * RM + e % R;
+    const int col = (int)(e % R);
+    if (R != RM * GM && col >= RM * GM) return;  // padding columns (a float4 never straddles a member)
+    const int mi = col / RM;
+    const int64_t out = (tile * tn + e / R) * RM + col - mi * RM;
     float4 old = make_float4(0.f, 0.f, 0.f, 0.f);
     if constexpr (!TO_BF16) old = *reinterpret_cast<const float4*>(fb.C[m] + out);
     f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
@@ -626,7 +675,7 @@ __global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
     if constexpr (TO_BF16) {
       const uint2 o = make_uint2(pack_bf16x2(f32_to_bf16_rne(sum[0]), f32_to_bf16_rne(sum[1])),
                                  pack_bf16x2(f32_to_bf16_rne(sum[2]), f32_to_bf16_rne(sum[3])));
-      *reinterpret_cast<uint2*>(fb.XP[m] + out) = o;
+      *reinterpret_cast<uint2*>(fb.XP[m][mi] + out) = o;
     } else {
       old.x += sum[0];
       old.y += sum[1];
@@ -865,9 +914,9 @@ Schedule make_schedule(int n, const int64_t* ns, const int64_t* ks, int64_t tile
   return s;
 }
 
-template <int RM>
+template <int RM, int GM = 1>
 size_t partial_bytes(const Schedule& s) {
-  return (size_t)2 * s.G * s.tile_n * sketch_width(RM) * sizeof(float);
+  return (size_t)2 * s.G * s.tile_n * sketch_width(GM * RM) * sizeof(float);
 }
 
 // Whether some tile is cut between ranges (then the finishing launch runs).
@@ -881,14 +930,14 @@ bool has_split_tiles(const Schedule& s) {
 }
 
 // One finishing workgroup per 1024 values of a tile (x) and per tile (y).
-template <int RM>
+template <int RM, int GM = 1>
 dim3 finish_grid(const Schedule& s) {
-  return dim3((unsigned)((s.tile_n * sketch_width(RM) + 1023) / 1024), (unsigned)s.tbase[s.n]);
+  return dim3((unsigned)((s.tile_n * sketch_width(GM * RM) + 1023) / 1024), (unsigned)s.tbase[s.n]);
 }
 
-template <int RM>
+template <int RM, int GM = 1>
 Schedule project_schedule(int n, const int64_t* ns, const int64_t* ks, int64_t forced) {
-  using Sh = StageShape<sketch_width(RM), kProjectKH>;
+  using Sh = StageShape<sketch_width(GM * RM), kProjectKH>;
   return make_schedule(n, ns, ks, Sh::TILE, Sh::KS, forced);
 }
 
@@ -917,29 +966,116 @@ Schedule accumulate_schedule(int n, const int64_t* ns, const int64_t* ks, int64_
   return s;
 }
 
+// Groups of a launch: with `shared`, the matrices that read the same X (same
+// pointer, row stride and width) form groups of up to kMaxGroup members and
+// at most 256 ranks in all, each projected in one pass over X (rgc_project_
+// shared); otherwise every matrix is its own group (the batched project).
+// Groups of one size share a launch. (Grouping inside the batched project
+// was measured slower on the Qwen3-shaped blocks, 96 against 42 us per
+// microbatch at r = 64: per-size launches leave each workgroup a few K-steps
+// and many partial sums, and a group's P slabs take the LDS that would keep
+// more X in flight.)
+struct ProjectGroups {
+  int n = 0;                        // groups
+  int size[kMaxItems];              // members per group
+  int member[kMaxItems][kMaxGroup];  // batch index of each member
+};
+
+ProjectGroups project_groups(int n, const uint16_t* const* Xs, const int64_t* ldxs, const int64_t* ks, int64_t r,
+                             bool shared) {
+  ProjectGroups g;
+  const int cap = !shared ? 1 : ((int)(256 / r) < kMaxGroup ? (int)(256 / r) : kMaxGroup);
+  for (int m = 0; m < n; ++m) {
+    int gi = -1;
+    for (int q = 0; q < g.n && gi < 0; ++q) {
+      const int f = g.member[q][0];
+      if (Xs[f] == Xs[m] && ldxs[f] == ldxs[m] && ks[f] == ks[m] && g.size[q] < cap) gi = q;
+    }
+    if (gi < 0) {
+      gi = g.n++;
+      g.size[gi] = 0;
+    }
+    g.member[gi][g.size[gi]++] = m;
+  }
+  return g;
+}
+
+// The groups with GM members, as one launch's schedule items.
+template <int RM, int GM>
+rgc_status_t project_launch_groups(const ProjectGroups& gr, const uint16_t* const* Xs, const int64_t* ldxs,
+                                   const int64_t* ks, const uint16_t* const* Ps, uint16_t* const* XPs, int64_t T,
+                                   void* ws, hipStream_t st, int64_t forced) {
+  ProjectBatch pb = {};
+  FinishBatch fb = {};
+  int64_t ns[kMaxItems], kk[kMaxItems];
+  int n = 0;
+  for (int q = 0; q < gr.n; ++q) {
+    if (gr.size[q] != GM) continue;
+    const int f = gr.member[q][0];
+    pb.X[n] = Xs[f];
+    pb.ldx[n] = ldxs[f];
+    for (int i = 0; i < GM; ++i) {
+      pb.P[n][i] = Ps[gr.member[q][i]];
+      pb.XP[n][i] = XPs[gr.member[q][i]];
+      fb.XP[n][i] = XPs[gr.member[q][i]];
+    }
+    ns[n] = T;
+    kk[n] = ks[f];
+    ++n;
+  }
+  if (n == 0) return RGC_OK;
+  pb.s = project_schedule<RM, GM>(n, ns, kk, forced);
+  fb.s = pb.s;
+  pb.part = static_cast<float*>(ws);
+  fb.part = pb.part;
+  hipLaunchKernelGGL((project_kernel<RM, GM>), dim3((unsigned)pb.s.G), dim3(256), 0, st, pb);
+  if (has_split_tiles(pb.s)) {
+    const dim3 grid = finish_grid<RM, GM>(pb.s);
+    hipLaunchKernelGGL((finish_tiles_kernel<RM, GM, true>), grid, dim3(256), 0, st, fb);
+  }
+  return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+}
+
+// Calls f(IntC<GM>{}) for each group size GM (1 .. kMaxGroup) whose total
+// width GM * RM stays within 256 ranks.
+template <int RM, typename F>
+void for_group_sizes(F&& f) {
+  static_for<1, kMaxGroup + 1>([&](auto gm) {
+    constexpr int GM = decltype(gm)::value;
+    if constexpr (GM * RM <= 256) f(gm);
+  });
+}
+
 template <int R>
 rgc_status_t project_launch(int n, const uint16_t* const* Xs, const int64_t* ldxs, const int64_t* ks,
                             const uint16_t* const* Ps, uint16_t* const* XPs, int64_t T, void* ws, hipStream_t st,
-                            int64_t forced) {
-  int64_t ns[kMaxItems];
-  for (int m = 0; m < n; ++m) ns[m] = T;
-  ProjectBatch pb = {};
-  pb.s = project_schedule<R>(n, ns, ks, forced);
-  FinishBatch fb = {};
-  fb.s = pb.s;
-  for (int m = 0; m < n; ++m) {
-    pb.X[m] = Xs[m];
-    pb.ldx[m] = ldxs[m];
-    pb.P[m] = Ps[m];
-    pb.XP[m] = XPs[m];
-    fb.XP[m] = XPs[m];
-  }
-  pb.part = static_cast<float*>(ws);
-  fb.part = pb.part;
-  hipLaunchKernelGGL(project_kernel<R>, dim3((unsigned)pb.s.G), dim3(256), 0, st, pb);
-  if (has_split_tiles(pb.s))
-    hipLaunchKernelGGL((finish_tiles_kernel<R, true>), finish_grid<R>(pb.s), dim3(256), 0, st, fb);
-  return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+                            int64_t forced, bool shared = false) {
+  const ProjectGroups gr = project_groups(n, Xs, ldxs, ks, R, shared);
+  rgc_status_t res = RGC_OK;
+  for_group_sizes<R>([&](auto gm) {
+    if (res == RGC_OK) res = project_launch_groups<R, decltype(gm)::value>(gr, Xs, ldxs, ks, Ps, XPs, T, ws, st, forced);
+  });
+  return res;
+}
+
+// Workspace of a batched project, a bound that holds for any grouping of its
+// n items (the query does not see which items share an X): the largest
+// partial-sum area of a launch with groups of GM <= n members, at the
+// workgroup count of the schedule.
+template <int R>
+size_t project_workspace(int n, const int64_t* ks, int64_t T, int64_t forced, bool shared = false) {
+  size_t out = 0;
+  for_group_sizes<R>([&](auto gm) {
+    constexpr int GM = decltype(gm)::value;
+    if (GM > n || (GM > 1 && !shared)) return;
+    int64_t ns[kMaxItems];
+    for (int m = 0; m < n; ++m) ns[m] = T;
+    // the same items as one group each: at least as many units, so at least
+    // as many workgroups as any launch of the call with GM-member groups
+    const size_t b = partial_bytes<R, GM>(project_schedule<R, GM>(n, ns, ks, forced));
+    out = b > out ? b : out;
+  });
+  return out;
 }
 
 template <int R>
@@ -963,7 +1099,7 @@ rgc_status_t accumulate_launch(int n, const uint16_t* const* Ds, const int64_t* 
   fb.part = ab.part;
   hipLaunchKernelGGL(accumulate_kernel<R>, dim3((unsigned)ab.s.G), dim3(256), 0, st, ab);
   if (has_split_tiles(ab.s))
-    hipLaunchKernelGGL((finish_tiles_kernel<R, false>), finish_grid<R>(ab.s), dim3(256), 0, st, fb);
+    hipLaunchKernelGGL((finish_tiles_kernel<R, 1, false>), finish_grid<R>(ab.s), dim3(256), 0, st, fb);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
@@ -1006,13 +1142,8 @@ size_t project_ws_impl(int64_t n, const int64_t* ks, int64_t T, int64_t r, int64
   for (int64_t m = 0; m < n; ++m)
     if (ks[m] <= 0) return 0;
   if (rank_small(r)) return 0;  // no partial sums
-  int64_t ns[kMaxItems];
-  for (int64_t m = 0; m < n; ++m) ns[m] = T;
   size_t out = 0;
-  if (!dispatch_rank(r, [&](auto rc) {
-        constexpr int R = decltype(rc)::value;
-        out = partial_bytes<R>(project_schedule<R>((int)n, ns, ks, forced));
-      }))
+  if (!dispatch_rank(r, [&](auto rc) { out = project_workspace<decltype(rc)::value>((int)n, ks, T, forced); }))
     return 0;
   return out;
 }
@@ -1150,4 +1281,67 @@ extern "C" rgc_status_t rgc_test_accumulate_batch_wgs(int64_t workgroups, int64_
                                                       int64_t r, void* ws, size_t ws_bytes, void* stream) {
   if (workgroups <= 0) return RGC_ERR_SHAPE;
   return accumulate_batch_impl(n, Ds, ldds, ds, XPs, Cs, T, r, ws, ws_bytes, stream, workgroups);
+}
+
+// ---- one pass over a shared X ---------------------------------------------
+namespace {
+
+size_t project_shared_ws_impl(int64_t n, int64_t T, int64_t k, int64_t r, int64_t forced) {
+  if (n <= 0 || n > kMaxGroup || T <= 0 || k <= 0 || !rank_tiled(r) || n * r > 256) return 0;
+  int64_t ks[kMaxGroup];
+  for (int64_t m = 0; m < n; ++m) ks[m] = k;
+  size_t out = 0;
+  dispatch_rank(r, [&](auto rc) { out = project_workspace<decltype(rc)::value>((int)n, ks, T, forced, true); });
+  return out;
+}
+
+rgc_status_t project_shared_impl(int64_t n, const uint16_t* X, int64_t ldx, int64_t k, const uint16_t* const* Ps,
+                                 uint16_t* const* XPs, int64_t T, int64_t r, void* ws, size_t ws_bytes, void* stream,
+                                 int64_t forced) {
+  if (n < 0 || T < 0 || r <= 0 || k <= 0) return RGC_ERR_SHAPE;
+  if (n > kMaxGroup || !rank_tiled(r) || n * r > 256 || T > kMaxTiledDim) return RGC_ERR_UNSUPPORTED;
+  if (n == 0 || T == 0) return RGC_OK;
+  if (!Ps || !XPs) return RGC_ERR_NULL;
+  const uint16_t* Xs[kMaxGroup];
+  int64_t ldxs[kMaxGroup], ks[kMaxGroup];
+  for (int64_t m = 0; m < n; ++m) {
+    Xs[m] = X;
+    ldxs[m] = ldx;
+    ks[m] = k;
+    const rgc_status_t st = check_project_item(X, ldx, k, Ps[m], XPs[m], T, r);
+    if (st != RGC_OK) return st;
+  }
+  const size_t need = project_shared_ws_impl(n, T, k, r, forced);
+  if (need > 0 && (!ws || ws_bytes < need)) return RGC_ERR_WORKSPACE;
+  if (need > 0 && !aligned_to(ws, 256)) return RGC_ERR_ALIGN;
+  rgc_status_t st = RGC_OK;
+  dispatch_rank(r, [&](auto rc) {
+    st = project_launch<decltype(rc)::value>((int)n, Xs, ldxs, ks, Ps, XPs, T, ws, static_cast<hipStream_t>(stream),
+                                             forced, true);
+  });
+  return st;
+}
+
+}  // namespace
+
+extern "C" size_t rgc_project_shared_workspace_size(int64_t n, int64_t T, int64_t k, int64_t r) {
+  return project_shared_ws_impl(n, T, k, r, 0);
+}
+
+extern "C" rgc_status_t rgc_project_shared(int64_t n, const uint16_t* X, int64_t ldx, int64_t k,
+                                           const uint16_t* const* Ps, uint16_t* const* XPs, int64_t T, int64_t r,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  return project_shared_impl(n, X, ldx, k, Ps, XPs, T, r, ws, ws_bytes, stream, 0);
+}
+
+extern "C" size_t rgc_test_project_shared_workspace_size(int64_t workgroups, int64_t n, int64_t T, int64_t k,
+                                                         int64_t r) {
+  return workgroups > 0 ? project_shared_ws_impl(n, T, k, r, workgroups) : 0;
+}
+
+extern "C" rgc_status_t rgc_test_project_shared_wgs(int64_t workgroups, int64_t n, const uint16_t* X, int64_t ldx,
+                                                    int64_t k, const uint16_t* const* Ps, uint16_t* const* XPs,
+                                                    int64_t T, int64_t r, void* ws, size_t ws_bytes, void* stream) {
+  if (workgroups <= 0) return RGC_ERR_SHAPE;
+  return project_shared_impl(n, X, ldx, k, Ps, XPs, T, r, ws, ws_bytes, stream, workgroups);
 }

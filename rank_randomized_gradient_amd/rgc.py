@@ -82,6 +82,12 @@ SIGNATURES = {
     "rgc_test_stochastic_round": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _u64, _vp]),
     "rgc_test_reconstruct": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "rgc_test_sketch_workspace_size": (_sz, [ctypes.c_int, _i64, _i64, ctypes.POINTER(_i64), _i64, _i64]),
+    "rgc_project_shared_workspace_size": (_sz, [_i64, _i64, _i64, _i64]),
+    "rgc_project_shared": (ctypes.c_int, [_i64, _vp, _i64, _i64, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64, _i64,
+                                          _vp, _sz, _vp]),
+    "rgc_test_project_shared_workspace_size": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "rgc_test_project_shared_wgs": (ctypes.c_int, [_i64, _i64, _vp, _i64, _i64, ctypes.POINTER(_vp),
+                                                   ctypes.POINTER(_vp), _i64, _i64, _vp, _sz, _vp]),
     "rgc_test_project_batch_wgs": (ctypes.c_int, [_i64, _i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64),
                                                   ctypes.POINTER(_i64), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                                   _i64, _i64, _vp, _sz, _vp]),
@@ -288,6 +294,38 @@ def rgc_project_batch(Xs, Ps, outs=None, workspace: Workspace | None = None):
     wp, wn = ws.get(lib.rgc_project_batch_workspace_size(n, _i64s(ks), T, r))
     _check(lib.rgc_project_batch(n, _ptrs(Xs), _i64s(ldxs), _i64s(ks), _ptrs(Ps), _ptrs(outs), T, r, wp, wn,
                                  _stream(dev)))
+    return outs
+
+
+def rgc_project_shared(X: torch.Tensor, Ps, outs=None, workspace: Workspace | None = None, workgroups: int = 0):
+    """XPs[i] = bf16(X Ps[i]) for the projections of matrices that read the same
+    X, with X streamed once for all of them (n <= 4, n * r <= 256).
+    workgroups > 0 forces the workgroup count (test hook)."""
+    lib = load_library()
+    n = len(Ps)
+    if n == 0:
+        return []
+    dev = _need_gpu(X, *Ps)
+    ldx = _rows(X, torch.bfloat16, "X")
+    T, k = X.shape
+    r = Ps[0].shape[1]
+    for p in Ps:
+        _dense(p, torch.bfloat16, "P")
+        if tuple(p.shape) != (k, r):
+            raise RgcError("every P must be k x r with k = X.shape[1] and one rank r")
+    if outs is None:
+        outs = [torch.empty((T, r), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    for o in outs:
+        _dense(o, torch.bfloat16, "XP")
+    if workgroups > 0:
+        nbytes = lib.rgc_test_project_shared_workspace_size(workgroups, n, T, k, r)
+        buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        _check(lib.rgc_test_project_shared_wgs(workgroups, n, X.data_ptr(), ldx, k, _ptrs(Ps), _ptrs(outs), T, r,
+                                               buf.data_ptr(), buf.numel(), _stream(dev)))
+        return outs
+    ws = workspace or default_workspace(dev)
+    wp, wn = ws.get(lib.rgc_project_shared_workspace_size(n, T, k, r))
+    _check(lib.rgc_project_shared(n, X.data_ptr(), ldx, k, _ptrs(Ps), _ptrs(outs), T, r, wp, wn, _stream(dev)))
     return outs
 
 
