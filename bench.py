@@ -92,6 +92,10 @@ def parse():
                          "W read once per apply); streamed from W once before the warm-up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--probe", choices=["shared-x"], default=None,
+                    help="instead of the step: shared-x times rgc_project_shared against rgc_project_batch for the "
+                         "workload's matrices that read one X (--steps calls each; with --steps 1, one call each "
+                         "for counter runs) and prints one JSON line")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times (a plain copy kernel of "
                          "known size, for calibrating the profiler's HBM byte counters)")
@@ -228,6 +232,9 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     wl = WORKLOADS[args.workload]
+    if args.probe == "shared-x":
+        probe_shared_x(args, wl, rgc, torch, dev)
+        return
     cfg, r, T, mb, L = wl["cfg"], wl["r"], wl["tokens"], wl["microbatch"], wl["layers"]
     n_mb = T // mb
     mats = wl["matrices"]
@@ -488,6 +495,53 @@ def main():
                     for k, v in kern.items()},
         "cpu_baseline": cpu,
     }
+    print(json.dumps(out), flush=True)
+
+
+def probe_shared_x(args, wl, rgc, torch, dev):
+    """One microbatch of the workload's matrices that read one X (q/k/v,
+    gate/up): rgc_project_shared (X read once per group, up to 256 ranks a
+    group) against rgc_project_batch of the same matrices (X read once per
+    matrix). Times are HIP event pairs around --steps calls of each."""
+    r, mb, mats = wl["r"], wl["microbatch"], wl["matrices"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    groups = {}
+    for m, (_, _, k, src) in enumerate(mats):
+        groups.setdefault(src, []).append(m)
+    cap = max(1, min(4, 256 // r))
+    out = {"probe": "shared-x", "workload": wl["desc"], "r": r, "tokens": mb, "groups": []}
+    for src, members in groups.items():
+        if len(members) < 2:
+            continue
+        members = members[:cap]
+        k = mats[members[0]][2]
+        x = torch.randn(mb, k, generator=g, device=dev).to(torch.bfloat16)
+        ps = [(torch.randn(k, r, generator=g, device=dev) * 0.1).to(torch.bfloat16) for _ in members]
+        xps = [torch.empty(mb, r, dtype=torch.bfloat16, device=dev) for _ in members]
+        ws = rgc.Workspace(dev)
+        shared = lambda: rgc.rgc_project_shared(x, ps, outs=xps, workspace=ws)  # noqa: E731
+        batch = lambda: rgc.rgc_project_batch([x] * len(ps), ps, outs=xps, workspace=ws)  # noqa: E731
+        times = {}
+        for name, fn in (("shared", shared), ("batch", batch)):
+            if args.steps > 1:
+                for _ in range(3):
+                    fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(args.steps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            times[name] = round(a.elapsed_time(b) * 1e3 / args.steps, 2)
+        out["groups"].append({"input": src, "matrices": [mats[m][0] for m in members], "k": k,
+                              "unique_x_MB": round(2 * mb * k / 1e6, 1), "shared_us": times["shared"],
+                              "batch_us": times["batch"]})
+    if args.copy_mib > 0:
+        src_t = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(src_t).copy_(src_t)
+        torch.cuda.synchronize()
     print(json.dumps(out), flush=True)
 
 
