@@ -11,21 +11,19 @@
 // (the result does not depend on the tile shape).
 //
 // One batch (e.g. all projections of a block) takes three launches:
-//   norms:  sum w^2 over W, and ||H||^2. For r <= 128, ||H||_F^2 =
-//           tr((C^T C)(P^T P)) (the Frobenius norm of a product through
-//           the two r x r Gram matrices), so W is only streamed and squared
-//           while a few workgroups per matrix form partial Gram matrices of
-//           C and of P. For r > 128 the Gram partials (136 block pairs)
-//           would not fit a workgroup's registers; there every workgroup
-//           streams its share of W and rebuilds the same H tiles as the
-//           update. Either way the partials are fp64 (Gram partials fp32)
-//           with fixed-order reductions across lanes and waves;
-//   scale:  one workgroup per matrix sums that matrix's partials in a fixed
-//           order and forms s = fp32(tau ||W|| / ||H||), or the skip flag when
-//           ||H|| is zero or not finite or s is not finite;
-//   update: every workgroup reads its matrix's s, rebuilds its H tiles, forms
-//           v = fp32(w - fp32(s h)) and rounds stochastically with 16 bits
-//           per element from Philox4x32-10 keyed on (seed, row, column).
+//   norms:  sum w^2 over W, and ||H||^2 = tr((C^T C)(P^T P)) (the Frobenius
+//           norm of a product through the two r x r Gram matrices), so W is
+//           only streamed and squared while a few workgroups per matrix form
+//           partial Gram matrices of C and of P (above r = 128 in four
+//           groups of block pairs). The W partials are fp64, the Gram
+//           partials fp32, with fixed-order reductions across lanes and waves;
+//   reduce: one workgroup per (matrix, block pair) sums that pair's partials
+//           in a fixed order into one term of ||H||^2 (and ||W||^2);
+//   update: every wave forms s = fp32(tau ||W|| / ||H||) from its matrix's
+//           terms (the skip flag when ||H|| is zero or not finite or s is not
+//           finite), rebuilds its H tiles, forms v = fp32(w - fp32(s h)) and
+//           rounds stochastically with 16 bits per element from
+//           Philox4x32-10 keyed on (seed, row, column).
 // Each matrix gets its own workgroups in every launch, as many as its own
 // shape alone decides, so a matrix gets the same bits alone or in a batch.
 //
@@ -42,7 +40,7 @@ namespace rgc {
 
 // kModeUpdateCarry: the update that also sums the squares of the bf16
 // weights it writes (one fp64 partial per workgroup), for the carried norm.
-enum ApplyMode { kModeNorms = 0, kModeUpdate = 1, kModeReconstruct = 2, kModeUpdateCarry = 3 };
+enum ApplyMode { kModeUpdate = 1, kModeReconstruct = 2, kModeUpdateCarry = 3 };
 
 // Where ||W||^2 comes from (ApplyBatch::carry): streamed from W by the norms
 // launch (kCarryNone, kCarryFresh) or the caller's value carried over from
@@ -90,9 +88,9 @@ struct ApplyBatch {
   int fixed;  // 1: fixed-scale update (s = it.alpha, no norms, never skipped)
   int carry;  // CarryMode
   float tau;
-  int wbase[kApplyMaxItems + 1];  // update (and rebuild-norms) workgroups [wbase[m], wbase[m+1]) serve item m
-  // Gram-form norms launch (r <= 128): Gram workgroups [gbase[m], gbase[m+1])
-  // (the first ncg[m] over rows of C, the rest over rows of P), then W-stream
+  int wbase[kApplyMaxItems + 1];  // update workgroups [wbase[m], wbase[m+1]) serve item m
+  // Norms launch: Gram workgroups [gbase[m], gbase[m+1]) (per pair group,
+  // the first ncg[m] over rows of C, the rest over rows of P), then W-stream
   // workgroups gbase[n] + [sbase[m], sbase[m+1]).
   int gbase[kApplyMaxItems + 1];
   int sbase[kApplyMaxItems + 1];
@@ -114,22 +112,35 @@ __device__ __forceinline__ int apply_item_of(const ApplyBatch& b, int w) {
   return m;
 }
 
-// Ranks whose norms take the Gram form (below).
-template <int R>
-constexpr bool kGramNorms = R <= 128;
-
+// The Gram-form norms (below) work on 16-column blocks of C and P and their
+// NB (NB + 1) / 2 block pairs a <= c. A workgroup holds the sums of at most
+// 36 pairs (the registers of one wave), so above 8 blocks (r > 128) the pairs
+// are split into four groups: the pairs within the lower half of the blocks,
+// within the upper half, and the pairs across the halves in two groups (by
+// the first block). Group g covers the n0(g) blocks from lo0(g) and, for a
+// cross group, the n1(g) blocks from lo1(g).
 template <int R>
 struct GramShape {
   static constexpr int NB = R / 16;
-  static constexpr int NP = NB * (NB + 1) / 2;  // block pairs a <= b
-  static constexpr int NE = NP * 256;           // floats per Gram partial
+  static constexpr int NG = NB <= 8 ? 1 : 4;             // pair groups
+  static constexpr int H = NB <= 8 ? NB : (NB + 1) / 2;  // blocks of the lower half
+  static constexpr int U = NB - H, H2 = H / 2;
+  static constexpr int lo0(int g) { return g == 1 ? H : (g == 3 ? H2 : 0); }
+  static constexpr int n0(int g) { return NG == 1 ? NB : (g == 0 ? H : (g == 1 ? U : (g == 2 ? H2 : H - H2))); }
+  static constexpr int lo1(int) { return H; }
+  static constexpr int n1(int g) { return NG > 1 && g >= 2 ? U : 0; }
+  static constexpr int pairs(int g) { return n1(g) == 0 ? n0(g) * (n0(g) + 1) / 2 : n0(g) * n1(g); }
+  static constexpr int poff(int g) { return g == 0 ? 0 : poff(g - 1) + pairs(g - 1); }  // first pair of group g
+  static constexpr int NP = NB * (NB + 1) / 2;  // block pairs a <= c
+  static constexpr int NE = 36 * 256;           // floats per Gram partial (the pairs of a group)
   // 32-row steps per wave of a Gram workgroup: 512 rows per workgroup keeps
   // its share of the stream (128 KB of C at r = 64) near that of a W-stream
   // workgroup, and the step count (each step waits for one load round) low.
   static constexpr int STEPS = 4;
   static constexpr int64_t ROWS = (int64_t)STEPS * 32 * kApplyWaves;
+  static_assert(poff(NG) == NP, "the groups cover every block pair");
 };
-constexpr int kGramMaxPairs = 36;  // NP at r = 128
+constexpr int kGramMaxPairs = 136;  // NP at r = 256
 
 // s = fp32(tau * ||W|| / ||H||) from the squared norms; flag = 1 (and s = 0)
 // when ||H|| is zero or not finite or s is not finite. stats (if not null)
@@ -317,15 +328,10 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
   constexpr bool UPD = MODE == kModeUpdate || MODE == kModeUpdateCarry;
   float s = 0.f;
   if constexpr (UPD) {
-    if (b.fixed) {
-      s = it.alpha;
-    } else if constexpr (!kGramNorms<R>) {
-      s = b.scale[2 * m];
-      if (b.scale[2 * m + 1] != 0.f) return;  // zero or non-finite step: W stays as it is
-    }
+    if (b.fixed) s = it.alpha;
   }
 
-  double sw = 0.0, sh = 0.0;
+  double sw = 0.0;
   RowOperand<R> rop;
   uint16_t* wrowp[Tr::NTW];  // update: start of the lane's W row in each N-tile
   int rop_row = -1;  // first row of the loaded row operand
@@ -397,12 +403,14 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
   for (int v = 0; v + 1 < S; ++v)
     if (lu < u1) issue();
 
-  if constexpr (UPD && kGramNorms<R>) {
+  if constexpr (UPD) {
     if (!b.fixed) {
       // s from the item's norm terms while the first copies are in flight: the
       // same fixed-order sums in every wave of every workgroup of the item
-      // (a butterfly gives every lane the same sum), so all agree on s.
-      const double hp = lane < GramShape<R>::NP ? b.hpairs[m * kGramMaxPairs + lane] : 0.0;
+      // (each lane its terms lane, lane + 64, ... in order, then a butterfly,
+      // which gives every lane the same sum), so all agree on s.
+      double hp = 0.0;
+      for (int q = lane; q < GramShape<R>::NP; q += 64) hp += b.hpairs[m * kGramMaxPairs + q];
       float flag;
       const bool lead = wl == 0 && threadIdx.x == 0;
       step_scale(b.tau, b.wnorm2[m], wave_sum(hp), s, flag, lead ? it.stats : nullptr);
@@ -476,19 +484,7 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
           const u32x4v_t wv =
               *(const RGC_LDS u32x4v_t*)(st + 1024 * c + 16 * (8 * t + ((q + (t >> 1) + 4 * (c & 1)) & 7)));
           const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
-          if constexpr (MODE == kModeNorms) {
-            double pw = 0.0, ph = 0.0;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              const double w0 = (double)bf16_bits_to_f32(wd[p] & 0xFFFFu);
-              const double w1 = (double)bf16_bits_to_f32(wd[p] >> 16);
-              const double h0 = (double)hv[2 * p], h1 = (double)hv[2 * p + 1];
-              pw += w0 * w0 + w1 * w1;
-              ph += h0 * h0 + h1 * h1;
-            }
-            sw += inside ? pw : 0.0;
-            sh += inside ? ph : 0.0;
-          } else {
+          {
             uint32_t rw[4];
             rounding_words(it.seed, i, jj >> 3, rw);
             uint32_t out[4];
@@ -523,23 +519,10 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
     __syncthreads();
     if (threadIdx.x == 0) b.wpart[w] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
   }
-  if constexpr (MODE == kModeNorms) {
-    sw = wave_sum(sw);
-    sh = wave_sum(sh);
-    if (lane == 0) {
-      red[0][wave] = sw;
-      red[1][wave] = sh;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      b.partials[2 * w] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
-      b.partials[2 * w + 1] = ((red[1][0] + red[1][1]) + red[1][2]) + red[1][3];
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
-// Gram-form norms (r <= 128).
+// Gram-form norms.
 //
 // ||H||_F^2 = ||C P^T||_F^2 = tr(P C^T C P^T) = sum_ab (C^T C)_ab (P^T P)_ab.
 // C^T C is formed from C's bf16 high parts and remainders with all four
@@ -553,90 +536,111 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
 // Lane layout: the r columns are relabelled so that block a (a < NB = r/16),
 // position x stands for column NB*x + a. Lane l (x = l % 16, g = l / 16)
 // reads the NB consecutive values NB*x .. NB*x + NB - 1 of each of its rows
-// 8g .. 8g+7 of a 32-row step, which for every block a is the MFMA operand of
-// row x with K = those 8 rows, both as A and as B. Block pair (a, b), a <= b,
-// accumulates the 16 x 16 block (a, b) of the relabelled Gram matrix. C and P
-// are relabelled alike, so the sum of the elementwise product is unchanged;
-// off-diagonal pairs count twice (the blocks (b, a) are their transposes).
+// 8g .. 8g+7 of a 32-row step (those of its pair group's blocks), which for
+// every block a is the MFMA operand of row x with K = those 8 rows, both as A
+// and as B. Block pair (a, b), a <= b, accumulates the 16 x 16 block (a, b)
+// of the relabelled Gram matrix. C and P are relabelled alike, so the sum of
+// the elementwise product is unchanged; off-diagonal pairs count twice (the
+// blocks (b, a) are their transposes).
 // ---------------------------------------------------------------------------
 // 16-byte chunks of W per W-stream workgroup (128 KB).
 constexpr int64_t kWStreamChunks = 8192;
 
-// The values one lane reads in one 32-row step: rows 8g .. 8g+7, columns
-// NB*x .. NB*x + NB - 1 (raw bits: fp32 for C, bf16 for P; 0 past row1).
-template <int NB>
+// The values one lane reads in one 32-row step: rows 8g .. 8g+7 of the step,
+// for the NL blocks of its pair group (raw bits: fp32 for C, bf16 for P; 0
+// past row1). Slot s < N0 holds block LO0 + s, slot N0 + s block LO1 + s; the
+// value of block b in lane x is column NB x + b of the row.
+template <int NL>
 struct GramRows {
-  uint32_t v[8][NB];
+  uint32_t v[8][NL];
 };
 
-template <int NB>
-__device__ __forceinline__ void load_gram_rows(const float* __restrict__ src, int64_t base, int64_t row1, int x,
-                                               int g, GramRows<NB>& o) {
+// Blocks LO .. LO+N-1 of one row (p = the row's column NB x) into slots
+// S .. S+N-1, with vector loads where the alignment allows.
+template <int NB, int LO, int N, int S, int NL>
+__device__ __forceinline__ void load_range(const float* __restrict__ p, uint32_t (&v)[NL]) {
+  if constexpr (N > 0) {
+    if constexpr (NB % 4 == 0 && LO % 4 == 0 && N % 4 == 0) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int64_t row = base + 8 * g + e;
-    const float* p = src + row * (16 * NB) + NB * x;
-    if (row < row1) {
-      if constexpr (NB == 8) {
-        const uint4 a = *reinterpret_cast<const uint4*>(p), c = *reinterpret_cast<const uint4*>(p + 4);
-        o.v[e][0] = a.x; o.v[e][1] = a.y; o.v[e][2] = a.z; o.v[e][3] = a.w;
-        o.v[e][4] = c.x; o.v[e][5] = c.y; o.v[e][6] = c.z; o.v[e][7] = c.w;
-      } else if constexpr (NB == 4) {
-        const uint4 a = *reinterpret_cast<const uint4*>(p);
-        o.v[e][0] = a.x; o.v[e][1] = a.y; o.v[e][2] = a.z; o.v[e][3] = a.w;
-      } else if constexpr (NB == 2) {
-        const uint2 a = *reinterpret_cast<const uint2*>(p);
-        o.v[e][0] = a.x; o.v[e][1] = a.y;
-      } else {
+      for (int i = 0; i < N; i += 4) {
+        const uint4 a = *reinterpret_cast<const uint4*>(p + LO + i);
+        v[S + i] = a.x; v[S + i + 1] = a.y; v[S + i + 2] = a.z; v[S + i + 3] = a.w;
+      }
+    } else if constexpr (NB % 2 == 0 && LO % 2 == 0 && N % 2 == 0) {
 #pragma unroll
-        for (int c = 0; c < NB; ++c) o.v[e][c] = __float_as_uint(p[c]);
+      for (int i = 0; i < N; i += 2) {
+        const uint2 a = *reinterpret_cast<const uint2*>(p + LO + i);
+        v[S + i] = a.x; v[S + i + 1] = a.y;
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < NB; ++c) o.v[e][c] = 0u;
+      for (int i = 0; i < N; ++i) v[S + i] = __float_as_uint(p[LO + i]);
+    }
+  }
+}
+template <int NB, int LO, int N, int S, int NL>
+__device__ __forceinline__ void load_range(const uint16_t* __restrict__ p, uint32_t (&v)[NL]) {
+  if constexpr (N > 0) {
+    if constexpr (NB % 8 == 0 && LO % 8 == 0 && N % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < N; i += 8) {
+        const uint4 a = *reinterpret_cast<const uint4*>(p + LO + i);
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[S + i + 2 * j] = w[j] & 0xFFFFu;
+          v[S + i + 2 * j + 1] = w[j] >> 16;
+        }
+      }
+    } else if constexpr (NB % 4 == 0 && LO % 4 == 0 && N % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < N; i += 4) {
+        const uint2 a = *reinterpret_cast<const uint2*>(p + LO + i);
+        v[S + i] = a.x & 0xFFFFu; v[S + i + 1] = a.x >> 16; v[S + i + 2] = a.y & 0xFFFFu; v[S + i + 3] = a.y >> 16;
+      }
+    } else if constexpr (NB % 2 == 0 && LO % 2 == 0 && N % 2 == 0) {
+#pragma unroll
+      for (int i = 0; i < N; i += 2) {
+        const uint32_t a = *reinterpret_cast<const uint32_t*>(p + LO + i);
+        v[S + i] = a & 0xFFFFu; v[S + i + 1] = a >> 16;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) v[S + i] = p[LO + i];
     }
   }
 }
 
-template <int NB>
-__device__ __forceinline__ void load_gram_rows(const uint16_t* __restrict__ src, int64_t base, int64_t row1, int x,
-                                               int g, GramRows<NB>& o) {
+template <int NB, int LO0, int N0, int LO1, int N1, typename T>
+__device__ __forceinline__ void load_gram_rows(const T* __restrict__ src, int64_t base, int64_t row1, int x, int g,
+                                               GramRows<N0 + N1>& o) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int64_t row = base + 8 * g + e;
-    const uint16_t* p = src + row * (16 * NB) + NB * x;
     if (row < row1) {
-      if constexpr (NB == 8) {
-        const uint4 a = *reinterpret_cast<const uint4*>(p);
-        o.v[e][0] = a.x & 0xFFFFu; o.v[e][1] = a.x >> 16; o.v[e][2] = a.y & 0xFFFFu; o.v[e][3] = a.y >> 16;
-        o.v[e][4] = a.z & 0xFFFFu; o.v[e][5] = a.z >> 16; o.v[e][6] = a.w & 0xFFFFu; o.v[e][7] = a.w >> 16;
-      } else if constexpr (NB == 4) {
-        const uint2 a = *reinterpret_cast<const uint2*>(p);
-        o.v[e][0] = a.x & 0xFFFFu; o.v[e][1] = a.x >> 16; o.v[e][2] = a.y & 0xFFFFu; o.v[e][3] = a.y >> 16;
-      } else if constexpr (NB == 2) {
-        const uint32_t a = *reinterpret_cast<const uint32_t*>(p);
-        o.v[e][0] = a & 0xFFFFu; o.v[e][1] = a >> 16;
-      } else {
-#pragma unroll
-        for (int c = 0; c < NB; ++c) o.v[e][c] = p[c];
-      }
+      const T* p = src + row * (16 * NB) + NB * x;
+      load_range<NB, LO0, N0, 0>(p, o.v[e]);
+      load_range<NB, LO1, N1, N0>(p, o.v[e]);
     } else {
 #pragma unroll
-      for (int c = 0; c < NB; ++c) o.v[e][c] = 0u;
+      for (int c = 0; c < N0 + N1; ++c) o.v[e][c] = 0u;
     }
   }
 }
 
-// One 32-row step: MFMA operands of every block from the lane's rows (C: bf16
-// high part and remainder of each fp32 value, all four products; P: the bf16
-// values), accumulated into the block pairs a <= b.
-template <int NB, bool TWO_TERM>
-__device__ __forceinline__ void gram_step(const GramRows<NB>& rw, f32x4_t (&acc)[NB * (NB + 1) / 2]) {
-  uint32_t hi[NB][4], lo[NB][4];
+// One 32-row step: MFMA operands of the group's blocks from the lane's rows
+// (C: bf16 high part and remainder of each fp32 value, all four products; P:
+// the bf16 values), accumulated into the group's block pairs: with N1 = 0
+// the pairs (a, c), a <= c < N0, else the pairs (a, N0 + c), in a-major order.
+template <int N0, int N1, bool TWO_TERM>
+__device__ __forceinline__ void gram_step(const GramRows<N0 + N1>& rw,
+                                          f32x4_t (&acc)[N1 == 0 ? N0 * (N0 + 1) / 2 : N0 * N1]) {
+  constexpr int NL = N0 + N1;
+  uint32_t hi[NL][4], lo[NL][4];
 #pragma unroll
   for (int p = 0; p < 4; ++p)
 #pragma unroll
-    for (int a = 0; a < NB; ++a) {
+    for (int a = 0; a < NL; ++a) {
       if constexpr (TWO_TERM) {
         const float v0 = __uint_as_float(rw.v[2 * p][a]), v1 = __uint_as_float(rw.v[2 * p + 1][a]);
         const uint32_t h0 = f32_to_bf16_rne(v0), h1 = f32_to_bf16_rne(v1);
@@ -649,9 +653,9 @@ __device__ __forceinline__ void gram_step(const GramRows<NB>& rw, f32x4_t (&acc)
     }
   int q = 0;
 #pragma unroll
-  for (int a = 0; a < NB; ++a)
+  for (int a = 0; a < N0; ++a)
 #pragma unroll
-    for (int c = a; c < NB; ++c) {
+    for (int c = (N1 == 0 ? a : N0); c < (N1 == 0 ? N0 : NL); ++c) {
       acc[q] = mfma_16x16x32(hi[a], hi[c], acc[q]);
       if constexpr (TWO_TERM) {
         acc[q] = mfma_16x16x32(hi[a], lo[c], acc[q]);
@@ -663,27 +667,30 @@ __device__ __forceinline__ void gram_step(const GramRows<NB>& rw, f32x4_t (&acc)
 }
 
 // Partial Gram matrix of rows [row0, row1) (at most ROWS) of the row-major
-// rows x R matrix src (C in fp32 with TWO_TERM, P in bf16 without), written
-// as NE floats: out[pair * 256 + 64 j + lane] = entry j of the lane's 16 x 16
-// MFMA output for block pair `pair`, summed over the four waves in wave
-// order. Wave w takes the steps at rows row0 + 32 w + 128 s; each step's
-// loads are issued before the previous step's MFMAs.
-template <int R, bool TWO_TERM, typename T>
+// rows x R matrix src (C in fp32 with TWO_TERM, P in bf16 without), for the
+// block pairs of group GR, written as out[pair * 256 + 64 j + lane] = entry j
+// of the lane's 16 x 16 MFMA output for the group's pair `pair`, summed over
+// the four waves in wave order. Wave w takes the steps at rows row0 + 32 w +
+// 128 s; each step's loads are issued before the previous step's MFMAs.
+template <int R, bool TWO_TERM, int GR, typename T>
 __device__ void gram_partial(const T* __restrict__ src, int64_t row0, int64_t row1, float* __restrict__ out,
                              float* red) {
   using Gs = GramShape<R>;
-  constexpr int NB = Gs::NB, NP = Gs::NP, NE = Gs::NE;
+  constexpr int NB = Gs::NB;
+  constexpr int LO0 = Gs::lo0(GR), N0 = Gs::n0(GR), LO1 = Gs::lo1(GR), N1 = Gs::n1(GR);
+  constexpr int NPG = Gs::pairs(GR);
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int x = lane & 15, g = lane >> 4;
-  f32x4_t acc[NP];
+  f32x4_t acc[NPG];
 #pragma unroll
-  for (int q = 0; q < NP; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  GramRows<NB> cur, nxt;
-  load_gram_rows<NB>(src, row0 + 32 * wave, row1, x, g, cur);
+  for (int q = 0; q < NPG; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  GramRows<N0 + N1> cur, nxt;
+  load_gram_rows<NB, LO0, N0, LO1, N1>(src, row0 + 32 * wave, row1, x, g, cur);
 #pragma unroll
   for (int st = 0; st < Gs::STEPS; ++st) {
-    if (st + 1 < Gs::STEPS) load_gram_rows<NB>(src, row0 + 32 * wave + 128 * (st + 1), row1, x, g, nxt);
-    gram_step<NB, TWO_TERM>(cur, acc);
+    if (st + 1 < Gs::STEPS)
+      load_gram_rows<NB, LO0, N0, LO1, N1>(src, row0 + 32 * wave + 128 * (st + 1), row1, x, g, nxt);
+    gram_step<N0, N1, TWO_TERM>(cur, acc);
     if (st + 1 < Gs::STEPS) cur = nxt;
   }
   // waves add their sums into one slab in wave order: ((w0 + w1) + w2) + w3
@@ -691,7 +698,7 @@ __device__ void gram_partial(const T* __restrict__ src, int64_t row0, int64_t ro
   for (int w = 0; w < kApplyWaves; ++w) {
     if (wave == w) {
 #pragma unroll
-      for (int q = 0; q < NP; ++q)
+      for (int q = 0; q < NPG; ++q)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float* e = red + q * 256 + 64 * j + lane;
@@ -700,7 +707,7 @@ __device__ void gram_partial(const T* __restrict__ src, int64_t row0, int64_t ro
     }
     __syncthreads();
   }
-  for (int e = threadIdx.x; e < NE; e += 256) out[e] = red[e];
+  for (int e = threadIdx.x; e < NPG * 256; e += 256) out[e] = red[e];
 }
 
 // Sum of squares of the 16-byte chunks [c0, c1) of W (row-major d x k, row
@@ -753,7 +760,8 @@ __device__ __forceinline__ int item_of(const int* base, int n, int w) {
   return m;
 }
 
-// The norms launch for r <= 128: Gram workgroups first, then W-stream ones.
+// The norms launch: Gram workgroups first (per item and pair group, the
+// C-row chunks, then the P-row chunks), then the W-stream workgroups.
 template <int R>
 __global__ __launch_bounds__(256) void gram_norms_kernel(ApplyBatch b) {
   using Gs = GramShape<R>;
@@ -763,15 +771,21 @@ __global__ __launch_bounds__(256) void gram_norms_kernel(ApplyBatch b) {
   if (w < ng) {
     const int m = item_of(b.gbase, b.n, w);
     const ApplyItem& it = b.it[m];
+    const int per_group = (b.gbase[m + 1] - b.gbase[m]) / Gs::NG;  // C and P chunks of one group
     const int l = w - b.gbase[m];
+    const int grp = l / per_group, lc = l - grp * per_group;
     float* out = b.gram + (int64_t)w * Gs::NE;
-    if (l < b.ncg[m]) {
-      const int64_t r0 = l * Gs::ROWS, r1 = r0 + Gs::ROWS < it.d ? r0 + Gs::ROWS : it.d;
-      gram_partial<R, true>(it.C, r0, r1, out, red);
-    } else {
-      const int64_t r0 = (l - b.ncg[m]) * Gs::ROWS, r1 = r0 + Gs::ROWS < it.k ? r0 + Gs::ROWS : it.k;
-      gram_partial<R, false>(it.P, r0, r1, out, red);
-    }
+    static_for<0, Gs::NG>([&](auto gc) {
+      constexpr int GR = decltype(gc)::value;
+      if (grp != GR) return;
+      if (lc < b.ncg[m]) {
+        const int64_t r0 = lc * Gs::ROWS, r1 = r0 + Gs::ROWS < it.d ? r0 + Gs::ROWS : it.d;
+        gram_partial<R, true, GR>(it.C, r0, r1, out, red);
+      } else {
+        const int64_t r0 = (lc - b.ncg[m]) * Gs::ROWS, r1 = r0 + Gs::ROWS < it.k ? r0 + Gs::ROWS : it.k;
+        gram_partial<R, false, GR>(it.P, r0, r1, out, red);
+      }
+    });
     return;
   }
   const int sw = w - ng;
@@ -810,30 +824,22 @@ __device__ __forceinline__ void finish_scale(const ApplyBatch& b, int m, double 
   b.scale[2 * m + 1] = flag;
 }
 
-__global__ __launch_bounds__(256) void apply_scale_kernel(ApplyBatch b) {
-  const int m = blockIdx.x;
-  double aw = 0.0, ah = 0.0;
-  for (int w = b.wbase[m] + (int)threadIdx.x; w < b.wbase[m + 1]; w += 256) {
-    aw += b.partials[2 * w];
-    ah += b.partials[2 * w + 1];
-  }
-  finish_scale(b, m, aw, ah);
-}
-
-// Gram form, one workgroup per (item, block pair): thread t sums entry
-// pair * 256 + t of the item's C Gram partials and of its P Gram partials in
-// partial order (fp64), and the workgroup writes sum over its entries of
-// G * M, times 2 for an off-diagonal pair. Pair 0's workgroup also sums the
-// item's W-stream partials into ||W||^2.
+// Gram form, one workgroup per (item, block pair): thread t sums entry t of
+// the pair in the item's C Gram partials and in its P Gram partials (those
+// of the pair's group) in partial order (fp64), and the workgroup writes sum
+// over its entries of G * M, times 2 for an off-diagonal pair. Pair 0's
+// workgroup also sums the item's W-stream partials into ||W||^2.
 template <int R>
 __global__ __launch_bounds__(256) void gram_reduce_kernel(ApplyBatch b) {
   using Gs = GramShape<R>;
   __shared__ double red[2][4];
   const int m = blockIdx.x / Gs::NP, q = blockIdx.x % Gs::NP;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = 256 * q + (int)threadIdx.x;
-  const float* gc = b.gram + (int64_t)b.gbase[m] * Gs::NE + e;
-  const int nc = b.ncg[m], np = b.gbase[m + 1] - b.gbase[m] - nc;
+  int grp = 0;
+  while (grp + 1 < Gs::NG && q >= Gs::poff(grp + 1)) ++grp;
+  const int ql = q - Gs::poff(grp);  // the pair within its group
+  const int nc = b.ncg[m], np = (b.gbase[m + 1] - b.gbase[m]) / Gs::NG - nc;
+  const float* gc = b.gram + (int64_t)(b.gbase[m] + grp * (nc + np)) * Gs::NE + 256 * ql + threadIdx.x;
   const float* gp = gc + (int64_t)nc * Gs::NE;
   constexpr int U = 8;  // loads in flight per thread
   double G = 0.0, M = 0.0;
@@ -851,12 +857,18 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(ApplyBatch b) {
 #pragma unroll
     for (int i = 0; i < U; ++i) M += (double)v[i];
   }
-  int pq = q, a = 0;  // pairs are listed (a, c) for a = 0.., c = a .. NB-1
-  while (pq >= Gs::NB - a) {
-    pq -= Gs::NB - a;
-    ++a;
+  // a within-half group lists its pairs (a, c) for a = 0.., c = a .. n0-1
+  // (diagonal when c = a); a cross group has no diagonal pair
+  bool diag = false;
+  if (Gs::n1(grp) == 0) {
+    int pq = ql, a = 0;
+    while (pq >= Gs::n0(grp) - a) {
+      pq -= Gs::n0(grp) - a;
+      ++a;
+    }
+    diag = pq == 0;
   }
-  double th = (pq == 0 ? 1.0 : 2.0) * G * M;
+  double th = (diag ? 1.0 : 2.0) * G * M;
   double tw = 0.0;
   const bool streamed = q == 0 && b.carry != kCarryIn;  // else ||W||^2 is the caller's carried value
   if (streamed)
@@ -1149,8 +1161,8 @@ void apply_plan(ApplyBatch& b, int n, const int64_t* ds, const int64_t* ks) {
   b.n = n;
 }
 
-// Gram-form norms launch: per matrix ceil(d / ROWS) C-Gram and
-// ceil(k / ROWS) P-Gram workgroups, and one W-stream workgroup per
+// Gram-form norms launch: per matrix and pair group ceil(d / ROWS) C-Gram
+// and ceil(k / ROWS) P-Gram workgroups, and one W-stream workgroup per
 // kWStreamChunks 16-byte chunks of W.
 template <int R>
 void gram_plan(ApplyBatch& b, int n, const int64_t* ds, const int64_t* ks) {
@@ -1159,7 +1171,7 @@ void gram_plan(ApplyBatch& b, int n, const int64_t* ds, const int64_t* ks) {
   b.sbase[0] = 0;
   for (int m = 0; m < n; ++m) {
     b.ncg[m] = (int)((ds[m] + Gs::ROWS - 1) / Gs::ROWS);
-    b.gbase[m + 1] = b.gbase[m] + b.ncg[m] + (int)((ks[m] + Gs::ROWS - 1) / Gs::ROWS);
+    b.gbase[m + 1] = b.gbase[m] + Gs::NG * (b.ncg[m] + (int)((ks[m] + Gs::ROWS - 1) / Gs::ROWS));
     b.sbase[m + 1] = b.sbase[m] + (int)((ds[m] * (ks[m] / 8) + kWStreamChunks - 1) / kWStreamChunks);
   }
 }
@@ -1176,13 +1188,8 @@ template <int R>
 ApplyWorkspace apply_ws_layout(const ApplyBatch& b) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   ApplyWorkspace l;
-  size_t part = 0, gram = 0;
-  if constexpr (kGramNorms<R>) {
-    part = (size_t)b.sbase[b.n] * sizeof(double);
-    gram = (size_t)b.gbase[b.n] * GramShape<R>::NE * sizeof(float);
-  } else {
-    part = 2 * (size_t)b.wbase[b.n] * sizeof(double);
-  }
+  const size_t part = (size_t)b.sbase[b.n] * sizeof(double);
+  const size_t gram = (size_t)b.gbase[b.n] * GramShape<R>::NE * sizeof(float);
   l.gram_off = up(part);
   l.hpairs_off = l.gram_off + up(gram);
   l.wnorm2_off = l.hpairs_off + up(kApplyMaxItems * kGramMaxPairs * sizeof(double));
@@ -1195,7 +1202,7 @@ ApplyWorkspace apply_ws_layout(const ApplyBatch& b) {
 template <int R>
 void apply_plan_all(ApplyBatch& b, int n, const int64_t* ds, const int64_t* ks) {
   apply_plan<R>(b, n, ds, ks);
-  if constexpr (kGramNorms<R>) gram_plan<R>(b, n, ds, ks);
+  gram_plan<R>(b, n, ds, ks);
 }
 
 template <int R>
@@ -1238,15 +1245,10 @@ rgc_status_t apply_launch(int n, uint16_t* const* Ws, const int64_t* ldws, const
   b.wnorm2 = carry != kCarryNone ? wnorm2 : reinterpret_cast<double*>(static_cast<char*>(ws) + l.wnorm2_off);
   b.scale = reinterpret_cast<float*>(static_cast<char*>(ws) + l.scale_off);
   b.wpart = reinterpret_cast<double*>(static_cast<char*>(ws) + l.wpart_off);
-  if constexpr (kGramNorms<R>) {
-    // with a carried ||W|| the launch holds the Gram workgroups alone
-    const int nw = carry == kCarryIn ? 0 : b.sbase[n];
-    hipLaunchKernelGGL(gram_norms_kernel<R>, dim3((unsigned)(b.gbase[n] + nw)), dim3(256), 0, st, b);
-    hipLaunchKernelGGL(gram_reduce_kernel<R>, dim3((unsigned)(n * GramShape<R>::NP)), dim3(256), 0, st, b);
-  } else {
-    hipLaunchKernelGGL((apply_kernel<R, kModeNorms>), dim3((unsigned)G), dim3(256), 0, st, b);
-    hipLaunchKernelGGL(apply_scale_kernel, dim3((unsigned)n), dim3(256), 0, st, b);
-  }
+  // with a carried ||W|| the launch holds the Gram workgroups alone
+  const int nw = carry == kCarryIn ? 0 : b.sbase[n];
+  hipLaunchKernelGGL(gram_norms_kernel<R>, dim3((unsigned)(b.gbase[n] + nw)), dim3(256), 0, st, b);
+  hipLaunchKernelGGL(gram_reduce_kernel<R>, dim3((unsigned)(n * GramShape<R>::NP)), dim3(256), 0, st, b);
   if (carry == kCarryNone) {
     hipLaunchKernelGGL((apply_kernel<R, kModeUpdate>), dim3((unsigned)G), dim3(256), 0, st, b);
   } else {
