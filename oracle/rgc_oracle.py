@@ -238,6 +238,31 @@ def accumulate(c: np.ndarray, d_bits: np.ndarray, xp_bits: np.ndarray) -> np.nda
     return (np.asarray(c, dtype=np.float32).astype(np.float64) + prod).astype(np.float32)
 
 
+def layer_forward(x_bits: np.ndarray, w_bits: np.ndarray, p_bits) -> tuple:
+    """The layer's forward with its sketch projection: Y = X W^T (T x d) and
+    XP = X P (T x r), the activation kept in place of X [RGC, "How it works"].
+
+    W is d x k (out x in), so Y's column j is X times W's row j. Each output is
+    the exact float64 sum of the bf16 products, rounded once to fp32 and once to
+    bf16 (the layer's output dtype; the pages leave it open). p_bits None gives
+    (Y, None).
+    """
+    y = bf16_to_f64(x_bits) @ bf16_to_f64(w_bits).T
+    y_bits = f32_to_bf16_rne(y.astype(np.float32))
+    return y_bits, (project(x_bits, p_bits) if p_bits is not None else None)
+
+
+def layer_backward(d_bits: np.ndarray, w_bits: np.ndarray, xp_bits, c) -> tuple:
+    """The layer's backward with its sketch: the input gradient dX = D W (T x k;
+    D = dL/dY is T x d) flows on, and C gains D^T (X P) from the saved XP
+    [RGC, "How it works"] in place of the weight gradient D^T X. dX rounded as
+    Y in layer_forward; C as in accumulate. xp_bits None gives (dX, c).
+    """
+    dx = bf16_to_f64(d_bits) @ bf16_to_f64(w_bits)
+    dx_bits = f32_to_bf16_rne(dx.astype(np.float32))
+    return dx_bits, (accumulate(c, d_bits, xp_bits) if xp_bits is not None else c)
+
+
 def reconstruct(c: np.ndarray, p_bits: np.ndarray) -> np.ndarray:
     """H = C P^T in float64 (rank <= r) [RGC, "How it works"]; [LoGRA-M, low-rank section]."""
     return np.asarray(c, dtype=np.float32).astype(np.float64) @ bf16_to_f64(p_bits).T
