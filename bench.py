@@ -92,10 +92,12 @@ def parse():
                          "W read once per apply); streamed from W once before the warm-up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
-    ap.add_argument("--probe", choices=["shared-x"], default=None,
+    ap.add_argument("--probe", choices=["shared-x", "linear"], default=None,
                     help="instead of the step: shared-x times rgc_project_shared against rgc_project_batch for the "
-                         "workload's matrices that read one X (--steps calls each; with --steps 1, one call each "
-                         "for counter runs) and prints one JSON line")
+                         "workload's matrices that read one X; linear times the layer products with the sketch "
+                         "attached (rgc_linear_forward / rgc_linear_backward) against torch's GEMM plus the "
+                         "separate sketch call, per matrix of one layer (--steps calls each; with --steps 1, one "
+                         "call each for counter runs); either prints one JSON line")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times (a plain copy kernel of "
                          "known size, for calibrating the profiler's HBM byte counters)")
@@ -232,6 +234,9 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     wl = WORKLOADS[args.workload]
+    if args.probe == "linear":
+        probe_linear(args, wl, rgc, torch, dev)
+        return
     if args.probe == "shared-x":
         probe_shared_x(args, wl, rgc, torch, dev)
         return
@@ -538,6 +543,70 @@ def probe_shared_x(args, wl, rgc, torch, dev):
         out["groups"].append({"input": src, "matrices": [mats[m][0] for m in members], "k": k,
                               "unique_x_MB": round(2 * mb * k / 1e6, 1), "shared_us": times["shared"],
                               "batch_us": times["batch"]})
+    if args.copy_mib > 0:
+        src_t = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(src_t).copy_(src_t)
+        torch.cuda.synchronize()
+    print(json.dumps(out), flush=True)
+
+
+def probe_linear(args, wl, rgc, torch, dev):
+    """One microbatch through each matrix of one layer of the workload: the
+    forward [Y | XP] = X [W^T | P] as one rgc_linear_forward call against
+    torch's Y = X W^T (hipBLASLt) followed by rgc_project, and the backward
+    dX = D W with C += D^T XP as one rgc_linear_backward call against torch's
+    D W followed by rgc_accumulate; also the library's Y and dX alone (r = 0).
+    Times are HIP event pairs on the current stream around --steps calls."""
+    r, mb, mats = wl["r"], wl["microbatch"], wl["matrices"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    ws = rgc.Workspace(dev)
+    out = {"probe": "linear", "workload": wl["desc"], "r": r, "tokens": mb, "matrices": []}
+
+    def timed(fn):
+        if args.steps > 1:
+            for _ in range(2):
+                fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / args.steps
+
+    tot = {}
+    for name, d, k, _ in mats:
+        x = torch.randn(mb, k, generator=g, device=dev).to(torch.bfloat16)
+        w = (torch.randn(d, k, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        p = (torch.randn(k, r, generator=g, device=dev) / r ** 0.5).to(torch.bfloat16)
+        dd = (torch.randn(mb, d, generator=g, device=dev) * 1e-3).to(torch.bfloat16)
+        y = torch.empty(mb, d, dtype=torch.bfloat16, device=dev)
+        xp = torch.empty(mb, r, dtype=torch.bfloat16, device=dev)
+        dx = torch.empty(mb, k, dtype=torch.bfloat16, device=dev)
+        c = torch.zeros(d, r, device=dev)
+        flops = 2.0 * mb * d * k
+        t = {
+            "fwd_fused_us": timed(lambda: rgc.rgc_linear_forward(x, w, p, Y=y, XP=xp)),
+            "fwd_torch_plus_project_us": timed(lambda: (torch.matmul(x, w.t(), out=y),
+                                                        rgc.rgc_project(x, p, out=xp, workspace=ws))),
+            "fwd_lib_gemm_us": timed(lambda: rgc.rgc_linear_forward(x, w, Y=y)),
+            "fwd_torch_gemm_us": timed(lambda: torch.matmul(x, w.t(), out=y)),
+            "bwd_fused_us": timed(lambda: rgc.rgc_linear_backward(dd, w, xp, c, dX=dx, workspace=ws)),
+            "bwd_torch_plus_accumulate_us": timed(lambda: (torch.matmul(dd, w, out=dx),
+                                                           rgc.rgc_accumulate(dd, xp, c, workspace=ws))),
+            "bwd_lib_gemm_us": timed(lambda: rgc.rgc_linear_backward(dd, w, dX=dx)),
+            "bwd_torch_gemm_us": timed(lambda: torch.matmul(dd, w, out=dx)),
+        }
+        for key, v in t.items():
+            tot[key] = tot.get(key, 0.0) + v
+        row = {"matrix": name, "d": d, "k": k}
+        row.update({key: round(v, 2) for key, v in t.items()})
+        row["lib_gemm_TFLOPs"] = round(flops / t["fwd_lib_gemm_us"] / 1e6, 1)
+        row["torch_gemm_TFLOPs"] = round(flops / t["fwd_torch_gemm_us"] / 1e6, 1)
+        out["matrices"].append(row)
+    out["layer_total_us"] = {key: round(v, 1) for key, v in tot.items()}
     if args.copy_mib > 0:
         src_t = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         torch.empty_like(src_t).copy_(src_t)

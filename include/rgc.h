@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define RGC_ABI_VERSION 4
+#define RGC_ABI_VERSION 5
 
 typedef enum {
   RGC_OK = 0,
@@ -307,6 +307,53 @@ rgc_status_t rgc_apply_from_seed(rgc_update_mode_t mode, rgc_proj_kind_t kind, u
                                  uint16_t* W, int64_t ldw, const float* C, int64_t d, int64_t k,
                                  int64_t r, float step, uint64_t seed, float* stats, void* ws,
                                  size_t ws_bytes, void* stream);
+
+/* ---- The layer's own products either side of the sketch ------------------
+ *
+ * [RGC, "How it works"]: the forward keeps X P instead of X and the backward
+ * adds D^T (X P) to C; [LoGRA-M, "Minimal Causal Code"]: the projection
+ * belongs inside the layer's own products. These calls make the layer's
+ * dense products themselves on the library's kernels, with the sketch steps
+ * attached, so a layer needs no other GEMM:
+ *
+ * Forward: Y = bf16_rne(X W^T) and XP = bf16_rne(X P) from one tile grid
+ * over the output columns [d columns of Y | r columns of XP]: P's columns are
+ * one more column of tiles beside W's, so X is staged once per tile row for
+ * both and the projection adds no pass of its own over X.
+ *   X: T x k bf16, row stride ldx; W: d x k bf16 (out x in), row stride ldw;
+ *   P: k x r bf16 (row stride r); Y: T x d bf16, row stride ldy; XP: T x r
+ *   bf16 (row stride r). r = 0 (P and XP may then be NULL) computes Y alone.
+ *   Each output element is one fp32 sum over k in ascending order (MFMA
+ *   products of bf16), then one rounding: bit-reproducible. XP is equal to
+ *   rgc_project's up to the fp32 summation order. At r = 4 (narrower than
+ *   the kernel's 16-byte P chunks) XP comes from the small-rank project after
+ *   the grid, a second pass over X.
+ * The batched form takes HOST arrays of n <= 16 entries (one T, one r); items
+ * may share X (a block's q, k and v; gate and up). No workspace. */
+rgc_status_t rgc_linear_forward(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw,
+                                const uint16_t* P, uint16_t* Y, int64_t ldy, uint16_t* XP, int64_t T,
+                                int64_t d, int64_t k, int64_t r, void* stream);
+rgc_status_t rgc_linear_forward_batch(int64_t n, const uint16_t* const* Xs, const int64_t* ldxs,
+                                      const int64_t* ks, const uint16_t* const* Ws, const int64_t* ldws,
+                                      const int64_t* ds, const uint16_t* const* Ps, uint16_t* const* Ys,
+                                      const int64_t* ldys, uint16_t* const* XPs, int64_t T, int64_t r,
+                                      void* stream);
+
+/* Backward: dX = bf16_rne(D W) (T x k, row stride lddx; one fp32 sum over d
+ * in ascending order per element), then C += D^T XP exactly as
+ * rgc_accumulate does (same kernels, same bits), both enqueued by this one
+ * call on `stream`, the accumulate right after the dX grid while D is still
+ * in the last-level cache. D: T x d bf16, row stride ldd; W: d x k bf16, row
+ * stride ldw; XP: T x r bf16; C: d x r fp32. r = 0 (XP and C may then be
+ * NULL) computes dX alone. The workspace is rgc_accumulate's (query below).
+ * Both calls: d and k multiples of 8, ld* multiples of 8, 16-byte aligned
+ * pointers, r in {0, 4, 8, 16, 32, ..., 256} and r <= k, T <= 65536;
+ * RGC_ERR_SHAPE / _UNSUPPORTED / _ALIGN / _NULL / _WORKSPACE otherwise. */
+size_t rgc_linear_backward_workspace_size(int64_t T, int64_t d, int64_t k, int64_t r);
+rgc_status_t rgc_linear_backward(const uint16_t* D, int64_t ldd, const uint16_t* W, int64_t ldw,
+                                 const uint16_t* XP, float* C, uint16_t* dX, int64_t lddx, int64_t T,
+                                 int64_t d, int64_t k, int64_t r, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* ---- Test hooks (same library; used by the parity tests) ----------------- */
 

@@ -23,6 +23,9 @@ from .rgc import (  # noqa: F401
     rgc_project,
     rgc_project_batch,
     rgc_project_shared,
+    rgc_linear_forward,
+    rgc_linear_forward_batch,
+    rgc_linear_backward,
     rgc_sample_projection,
     rgc_sample_projections,
     rgc_test_philox,

@@ -10,7 +10,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "librgc.so")
-SOURCES = ["rgc_sketch.hip", "rgc_apply.hip", "rgc_projection.hip", "rgc_abi.cpp"]
+SOURCES = ["rgc_sketch.hip", "rgc_apply.hip", "rgc_projection.hip", "rgc_linear.hip", "rgc_abi.cpp"]
 
 # -ffp-contract=off: the update's pre-rounding value w - s*h and the Box-Muller
 # formulas are two separately rounded operations, never fused.

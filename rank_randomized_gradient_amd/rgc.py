@@ -14,6 +14,8 @@ Names mirror the C ABI in include/rgc.h:
                                             rgc_apply with ||W||^2 carried between calls
   rgc_apply_from_seed(mode, kind, proj_seed, W, C, step, seed)
                                             P regenerated from its seed, then one of the two
+  rgc_linear_forward(X, W, P)               (Y, XP) = (bf16(X W^T), bf16(X P)), one tile grid
+  rgc_linear_backward(D, W, XP, C)          dX = bf16(D W), then C += D^T XP
 """
 from __future__ import annotations
 
@@ -78,6 +80,14 @@ SIGNATURES = {
     "rgc_apply_from_seed_workspace_size": (_sz, [ctypes.c_int, _i64, _i64, _i64]),
     "rgc_apply_from_seed": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _u64, _vp, _i64, _vp, _i64, _i64, _i64, _f32,
                                            _u64, _vp, _vp, _sz, _vp]),
+    "rgc_linear_forward": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]),
+    "rgc_linear_forward_batch": (ctypes.c_int, [_i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64),
+                                                ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64),
+                                                ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_i64),
+                                                ctypes.POINTER(_vp), _i64, _i64, _vp]),
+    "rgc_linear_backward_workspace_size": (_sz, [_i64, _i64, _i64, _i64]),
+    "rgc_linear_backward": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _sz,
+                                           _vp]),
     "rgc_test_philox": (ctypes.c_int, [_u64, _i64, _vp, _vp, _vp]),
     "rgc_test_stochastic_round": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _u64, _vp]),
     "rgc_test_reconstruct": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
@@ -644,3 +654,96 @@ def rgc_test_accumulate_batch_wgs(workgroups: int, Ds, XPs, Cs):
     _check(lib.rgc_test_accumulate_batch_wgs(workgroups, n, _ptrs(Ds), _i64s(ldds), _i64s(ds), _ptrs(XPs),
                                              _ptrs(Cs), T, r, ws.data_ptr(), ws.numel(), _stream(dev)))
     return Cs
+
+
+def rgc_linear_forward(X: torch.Tensor, W: torch.Tensor, P: torch.Tensor | None = None,
+                       Y: torch.Tensor | None = None, XP: torch.Tensor | None = None):
+    """(Y, XP) = (bf16(X W^T), bf16(X P)) from one tile grid over [W^T | P]'s
+    columns; XP is None when P is None. X: T x k (row stride >= k), W: d x k,
+    P: k x r."""
+    lib = load_library()
+    dev = _need_gpu(X, W, *([P] if P is not None else []))
+    ldx = _rows(X, torch.bfloat16, "X")
+    ldw = _rows(W, torch.bfloat16, "W")
+    T, k = X.shape
+    d = W.shape[0]
+    if W.shape[1] != k:
+        raise RgcError("W must be d x k with k = X.shape[1]")
+    r = 0
+    if P is not None:
+        _dense(P, torch.bfloat16, "P")
+        if P.shape[0] != k:
+            raise RgcError("P must be k x r with k = X.shape[1]")
+        r = P.shape[1]
+        if XP is None:
+            XP = torch.empty((T, r), dtype=torch.bfloat16, device=dev)
+        _dense(XP, torch.bfloat16, "XP")
+    if Y is None:
+        Y = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    ldy = _rows(Y, torch.bfloat16, "Y")
+    _check(lib.rgc_linear_forward(X.data_ptr(), ldx, W.data_ptr(), ldw, P.data_ptr() if P is not None else None,
+                                  Y.data_ptr(), ldy, XP.data_ptr() if XP is not None else None, T, d, k, r,
+                                  _stream(dev)))
+    return Y, XP
+
+
+def rgc_linear_forward_batch(Xs, Ws, Ps=None):
+    """rgc_linear_forward for n <= 16 layers of one token count and one rank in
+    one launch (items may share X). Returns (Ys, XPs)."""
+    lib = load_library()
+    n = len(Xs)
+    if n == 0:
+        return [], []
+    dev = _need_gpu(*Xs, *Ws, *(Ps or []))
+    T = Xs[0].shape[0]
+    r = Ps[0].shape[1] if Ps else 0
+    ldxs, ldws, ks, ds = [], [], [], []
+    for m in range(n):
+        ldxs.append(_rows(Xs[m], torch.bfloat16, "X"))
+        ldws.append(_rows(Ws[m], torch.bfloat16, "W"))
+        if Xs[m].shape[0] != T or Ws[m].shape[1] != Xs[m].shape[1]:
+            raise RgcError("batch items must share T, with W of shape (d, X.shape[1])")
+        if Ps:
+            _dense(Ps[m], torch.bfloat16, "P")
+            if tuple(Ps[m].shape) != (Xs[m].shape[1], r):
+                raise RgcError("every P must be k x r with one rank r")
+        ks.append(Xs[m].shape[1])
+        ds.append(Ws[m].shape[0])
+    Ys = [torch.empty((T, d), dtype=torch.bfloat16, device=dev) for d in ds]
+    XPs = [torch.empty((T, r), dtype=torch.bfloat16, device=dev) for _ in range(n)] if Ps else None
+    _check(lib.rgc_linear_forward_batch(n, _ptrs(Xs), _i64s(ldxs), _i64s(ks), _ptrs(Ws), _i64s(ldws), _i64s(ds),
+                                        _ptrs(Ps) if Ps else None, _ptrs(Ys), _i64s(ds), _ptrs(XPs) if Ps else None,
+                                        T, r, _stream(dev)))
+    return Ys, XPs
+
+
+def rgc_linear_backward(D: torch.Tensor, W: torch.Tensor, XP: torch.Tensor | None = None,
+                        C: torch.Tensor | None = None, dX: torch.Tensor | None = None,
+                        workspace: Workspace | None = None) -> torch.Tensor:
+    """dX = bf16(D W); with XP and C also C += D^T XP (in place), in one call."""
+    lib = load_library()
+    if (XP is None) != (C is None):
+        raise RgcError("give both XP and C, or neither")
+    dev = _need_gpu(D, W, *([XP, C] if XP is not None else []))
+    ldd = _rows(D, torch.bfloat16, "D")
+    ldw = _rows(W, torch.bfloat16, "W")
+    T, d = D.shape
+    k = W.shape[1]
+    if W.shape[0] != d:
+        raise RgcError("W must be d x k with d = D.shape[1]")
+    r = 0
+    if XP is not None:
+        _dense(XP, torch.bfloat16, "XP")
+        _dense(C, torch.float32, "C")
+        r = XP.shape[1]
+        if XP.shape[0] != T or tuple(C.shape) != (d, r):
+            raise RgcError("shapes must be XP: T x r, C: d x r")
+    if dX is None:
+        dX = torch.empty((T, k), dtype=torch.bfloat16, device=dev)
+    lddx = _rows(dX, torch.bfloat16, "dX")
+    ws = workspace or default_workspace(dev)
+    wp, wn = ws.get(lib.rgc_linear_backward_workspace_size(T, d, k, r))
+    _check(lib.rgc_linear_backward(D.data_ptr(), ldd, W.data_ptr(), ldw, XP.data_ptr() if XP is not None else None,
+                                   C.data_ptr() if C is not None else None, dX.data_ptr(), lddx, T, d, k, r, wp, wn,
+                                   _stream(dev)))
+    return dX

@@ -8,11 +8,12 @@ drawn. [LoGRA-M, "Minimal Causal Code"] (page "LoGRA: Low-Rank Gradient
 Sketches") runs the same loop with a caller-chosen step (`apply_update(...,
 alpha=...)`).
 
-The sketch steps run in the library's kernels (rgc_project in the forward,
-rgc_accumulate in the backward, rgc_apply / rgc_apply_scaled at the update,
-rgc_sample_projection for P). The layer's own products Y = X W^T and
-dX = D W are the model's dense GEMMs and stay with torch. W never receives a
-.grad: the sketch replaces it.
+Every step runs in the library's kernels: the forward is one
+rgc_linear_forward call ([Y | XP] = X [W^T | P], one tile grid, so the
+projection adds no pass over X); the backward one rgc_linear_backward call
+(dX = D W, then C += D^T XP on the same stream); the update rgc_apply /
+rgc_apply_scaled / rgc_apply_carried; P from rgc_sample_projection. W never
+receives a .grad: the sketch replaces it.
 """
 from __future__ import annotations
 
@@ -22,15 +23,15 @@ from . import rgc
 
 
 class SketchedLinearFunction(torch.autograd.Function):
-    """Y = X W^T; saves XP = X P (T x r), not X; backward: dX = D W and C += D^T XP."""
+    """Y = X W^T and XP = X P from one call; saves XP (T x r), not X; backward:
+    dX = D W and C += D^T XP from one call (C alone when X needs no gradient)."""
 
     @staticmethod
     def forward(ctx, x, weight, proj, sketch, workspace):
         x2 = x.reshape(-1, x.shape[-1])
         if not x2.is_contiguous():
             x2 = x2.contiguous()
-        y = torch.nn.functional.linear(x2, weight)
-        xp = rgc.rgc_project(x2, proj, workspace=workspace)
+        y, xp = rgc.rgc_linear_forward(x2, weight, proj)
         ctx.save_for_backward(xp, weight)
         ctx.sketch = sketch
         ctx.workspace = workspace
@@ -45,8 +46,11 @@ class SketchedLinearFunction(torch.autograd.Function):
             d2 = d2.to(torch.bfloat16)
         if not d2.is_contiguous():
             d2 = d2.contiguous()
-        rgc.rgc_accumulate(d2, xp, ctx.sketch, workspace=ctx.workspace)
-        dx = (d2 @ weight).reshape(ctx.in_shape) if ctx.needs_input_grad[0] else None
+        if ctx.needs_input_grad[0]:
+            dx = rgc.rgc_linear_backward(d2, weight, xp, ctx.sketch, workspace=ctx.workspace).reshape(ctx.in_shape)
+        else:
+            rgc.rgc_accumulate(d2, xp, ctx.sketch, workspace=ctx.workspace)
+            dx = None
         return dx, None, None, None, None
 
 
