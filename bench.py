@@ -607,6 +607,31 @@ def probe_linear(args, wl, rgc, torch, dev):
         row["torch_gemm_TFLOPs"] = round(flops / t["fwd_torch_gemm_us"] / 1e6, 1)
         out["matrices"].append(row)
     out["layer_total_us"] = {key: round(v, 1) for key, v in tot.items()}
+    # the matrices that read one X, as one batched launch each (a block's q, k,
+    # v; gate and up) against torch's separate GEMMs plus rgc_project_batch
+    groups = {}
+    for m, (_, _, _, src) in enumerate(mats):
+        groups.setdefault(src, []).append(m)
+    out["shared_input_batches"] = []
+    for src, members in groups.items():
+        if len(members) < 2:
+            continue
+        k = mats[members[0]][2]
+        x = torch.randn(mb, k, generator=g, device=dev).to(torch.bfloat16)
+        ws_ = [(torch.randn(mats[m][1], k, generator=g, device=dev) * 0.02).to(torch.bfloat16) for m in members]
+        ps = [(torch.randn(k, r, generator=g, device=dev) / r ** 0.5).to(torch.bfloat16) for _ in members]
+        ys = [torch.empty(mb, mats[m][1], dtype=torch.bfloat16, device=dev) for m in members]
+        xps = [torch.empty(mb, r, dtype=torch.bfloat16, device=dev) for _ in members]
+
+        def torch_fwd():
+            for w_, y_ in zip(ws_, ys):
+                torch.matmul(x, w_.t(), out=y_)
+            rgc.rgc_project_batch([x] * len(ps), ps, outs=xps, workspace=ws)
+
+        out["shared_input_batches"].append({
+            "input": src, "matrices": [mats[m][0] for m in members],
+            "fwd_fused_batch_us": round(timed(lambda: rgc.rgc_linear_forward_batch([x] * len(ps), ws_, ps)), 2),
+            "fwd_torch_plus_project_batch_us": round(timed(torch_fwd), 2)})
     if args.copy_mib > 0:
         src_t = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         torch.empty_like(src_t).copy_(src_t)
