@@ -280,3 +280,43 @@ def test_small_ranks_are_supported(lib):
     assert lib.rgc_apply_workspace_size(2048, 2048, 12) == 0
     s = None
     assert lib.rgc_project(FAKE, 64, FAKE, FAKE, 16, 64, 12, None, 0, s) == UNSUP
+
+
+def test_linear_validation(lib):
+    """The layer products' host checks (nothing is launched: every call below
+    is rejected, or has no tokens)."""
+    s = None
+    fwd = lib.rgc_linear_forward
+    # X, ldx, W, ldw, P, Y, ldy, XP, T, d, k, r, stream
+    assert fwd(None, 64, None, 64, None, None, 64, None, 0, 64, 64, 16, s) == OK  # no tokens
+    assert fwd(FAKE, 64, FAKE, 64, FAKE, FAKE, 64, FAKE, -1, 64, 64, 16, s) == SHAPE
+    assert fwd(FAKE, 64, FAKE, 64, FAKE, FAKE, 64, FAKE, 16, 64, 16, 32, s) == SHAPE  # r > k
+    assert fwd(FAKE, 64, FAKE, 64, FAKE, FAKE, 64, FAKE, 16, 64, 64, 24, s) == UNSUP  # rank
+    assert fwd(FAKE, 64, FAKE, 64, FAKE, FAKE, 64, FAKE, 16, 64, 60, 16, s) == UNSUP  # k % 8
+    assert fwd(FAKE, 64, FAKE, 64, FAKE, FAKE, 64, FAKE, 16, 60, 64, 16, s) == UNSUP  # d % 8
+    assert fwd(FAKE, 64, FAKE, 64, FAKE, FAKE, 64, FAKE, 1 << 17, 64, 64, 16, s) == UNSUP  # T above the limit
+    assert fwd(FAKE, 64, FAKE, 64, None, FAKE, 64, FAKE, 16, 64, 64, 16, s) == NULL  # P
+    assert fwd(FAKE, 64, None, 64, FAKE, FAKE, 64, FAKE, 16, 64, 64, 16, s) == NULL  # W
+    assert fwd(FAKE + 2, 64, FAKE, 64, FAKE, FAKE, 64, FAKE, 16, 64, 64, 16, s) == ALIGN
+    assert fwd(FAKE, 68, FAKE, 64, FAKE, FAKE, 64, FAKE, 16, 64, 64, 16, s) == ALIGN  # ldx % 8
+    assert fwd(FAKE, 64, FAKE, 64, FAKE, FAKE, 60, FAKE, 16, 64, 64, 16, s) == SHAPE  # ldy < d
+    assert fwd(FAKE, (1 << 23) + 8, FAKE, 64, FAKE, FAKE, 64, FAKE, 16, 64, 64, 16, s) == UNSUP  # ldx > 2^23
+    bwd = lib.rgc_linear_backward
+    # D, ldd, W, ldw, XP, C, dX, lddx, T, d, k, r, ws, ws_bytes, stream
+    assert bwd(FAKE, 64, FAKE, 64, FAKE, FAKE, FAKE, 64, 16, 64, 64, 24, None, 0, s) == UNSUP
+    assert bwd(FAKE, 64, FAKE, 64, FAKE, FAKE, FAKE, 64, 16, 60, 64, 16, None, 0, s) == UNSUP  # d % 8
+    assert bwd(FAKE, 64, FAKE, 60, FAKE, FAKE, FAKE, 64, 16, 64, 60, 16, None, 0, s) == UNSUP  # k % 8
+    assert bwd(FAKE, 64, FAKE, 64, None, FAKE, FAKE, 64, 16, 64, 64, 16, None, 0, s) == NULL  # XP
+    assert bwd(FAKE, 64, FAKE, 64, FAKE, FAKE, FAKE, 60, 16, 64, 64, 16, None, 0, s) == SHAPE  # lddx < k
+    need = lib.rgc_linear_backward_workspace_size(4096, 2048, 2048, 64)
+    assert need == lib.rgc_accumulate_workspace_size(4096, 2048, 64) and need > 0
+    assert lib.rgc_linear_backward_workspace_size(4096, 2048, 2048, 0) == 0
+    assert bwd(FAKE, 2048, FAKE, 2048, FAKE, FAKE, FAKE, 2048, 4096, 2048, 2048, 64, FAKE, need - 8, s) == WS
+    assert bwd(FAKE, 2048, FAKE, 2048, FAKE, FAKE, FAKE, 2048, 4096, 2048, 2048, 64, FAKE + 16, need, s) == ALIGN
+
+
+def test_apply_rejects_widths_not_divisible_by_8(lib):
+    s = None
+    f = ctypes.c_float(1e-3)
+    assert lib.rgc_apply(FAKE, 260, FAKE, FAKE, 64, 260, 16, f, 0, None, FAKE, 1 << 20, s) == UNSUP  # k % 8
+    assert lib.rgc_apply(FAKE, 256, FAKE, FAKE, 68, 256, 16, f, 0, None, FAKE, 1 << 20, s) == UNSUP  # d % 8
