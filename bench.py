@@ -665,10 +665,10 @@ def _blas() -> tuple[str, int]:
 
 def cpu_baseline(X, D, W, mats, wl):
     """The CPU oracle, untuned, on a bounded sample of the same workload (one
-    layer's share): the layer's 7 QR projections, one 4096-token microbatch of
-    project + accumulate for all 7 matrices, and the applies of the three
-    smallest matrices (q, k, v), whose time is scaled by weight elements to
-    all 7. The step time is extrapolated to 8 microbatches and 36 layers."""
+    layer's share, about 10-15 s of CPU work): the layer's 7 QR projections,
+    one 4096-token microbatch of project + accumulate for all 7 matrices, and
+    the updates of all 7 matrices. The step time is extrapolated to 8
+    microbatches and 36 layers."""
     import numpy as np
 
     import oracle as orc
@@ -687,22 +687,18 @@ def cpu_baseline(X, D, W, mats, wl):
         c = np.zeros((d, r), np.float32)
         cs.append(orc.accumulate(c, ds[m], orc.project(xs[src], ps[m])))
     t2 = time.perf_counter()
-    sample_m = sorted(range(len(mats)), key=lambda m: mats[m][1] * mats[m][2])[:3]
-    for m in sample_m:
+    for m in range(len(mats)):
         orc.apply_update(bits(W[m]), cs[m], ps[m], wl["tau"], step_seed(wl["cfg"], 0, 0, m))
     t3 = time.perf_counter()
-    el_all = sum(d * k for _, d, k, _ in mats)
-    el_sample = sum(mats[m][1] * mats[m][2] for m in sample_m)
-    apply_s = (t3 - t2) * el_all / el_sample
-    layer_s = (t1 - t0) + n_mb * (t2 - t1) + apply_s
+    layer_s = (t1 - t0) + n_mb * (t2 - t1) + (t3 - t2)
     step_s = L * layer_s
     blas, threads = _blas()
     return {"value": round(wl["tokens"] / step_s, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "cpu_model": _cpu_model(), "blas": blas,
             "sample": f"one layer's share: 7 QR projections ({t1 - t0:.1f}s) + 1 of {n_mb} microbatches "
-                      f"(project+accumulate, 7 matrices, {t2 - t1:.1f}s) + the applies of q, k, v "
-                      f"({t3 - t2:.1f}s, x{el_all / el_sample:.2f} by weight elements for all 7); "
-                      f"step = {L} x (projections + {n_mb} x microbatch + applies) = {step_s:.0f}s "
+                      f"(project+accumulate, 7 matrices, {t2 - t1:.1f}s) + the updates of all 7 matrices "
+                      f"({t3 - t2:.1f}s); "
+                      f"step = {L} x (projections + {n_mb} x microbatch + updates) = {step_s:.0f}s "
                       f"(extrapolated x{L} layers)"}
 
 

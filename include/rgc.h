@@ -102,6 +102,10 @@ size_t rgc_sample_projection_workspace_size(rgc_proj_kind_t kind, int64_t k, int
  *   u = (w + 1/2) / 2^32; even column rho*cos, odd column rho*sin); then
  *   Q = A R^-1 with R upper triangular, diag(R) > 0 (CholeskyQR2, fp64);
  *   P = bf16(fp32(sqrt(k/r) * Q)). Needs a workspace (see the query).
+ *   If a Cholesky factorization fails (a Gram matrix that is not numerically
+ *   positive definite: for a Gaussian draw with k >= r practically never),
+ *   P is written as all NaN; every update from such a P is then skipped
+ *   (flag = 1 in its stats, W left bit-identical).
  * The same (kind, seed, k, r) always gives the same bits, on any device. */
 rgc_status_t rgc_sample_projection(rgc_proj_kind_t kind, uint64_t seed, int64_t k, int64_t r,
                                    uint16_t* P, void* ws, size_t ws_bytes, void* stream);
