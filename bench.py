@@ -104,6 +104,68 @@ def parse():
     return ap.parse_args()
 
 
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence: its
+    recording skips the system-scope release (an L2 writeback and invalidate)
+    that a default event performs, which otherwise stalls the next kernel by
+    ~10 us and so inflates per-call times measured between dependent launches.
+    Created through the HIP runtime that torch has loaded (the same instance
+    the library launches through)."""
+
+    _rt = None
+    FLAGS = 0x20000000  # hipEventDisableSystemFence (timing stays enabled)
+
+    @classmethod
+    def runtime(cls):
+        if cls._rt is None:
+            import ctypes
+
+            path = None
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64.so" in line:
+                        path = line.split()[-1]
+                        break
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded")
+            rt = ctypes.CDLL(path)
+            rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._rt = rt
+        return cls._rt
+
+    def __init__(self):
+        import ctypes
+
+        self.ev = ctypes.c_void_p()
+        if self.runtime().hipEventCreateWithFlags(ctypes.byref(self.ev), self.FLAGS) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        if self.runtime().hipEventRecord(self.ev, ctypes_stream(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, end) -> float:
+        import ctypes
+
+        ms = ctypes.c_float()
+        if self.runtime().hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self.ev and TimingEvent._rt is not None:
+            TimingEvent._rt.hipEventDestroy(self.ev)
+
+
+def ctypes_stream(stream):
+    import ctypes
+
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
 def sources_digest() -> str:
     import hashlib
 
@@ -303,19 +365,25 @@ def main():
         for l in range(L):
             calls.sample(cfg, 0, l, 0, side=False)  # a fixed projection, drawn once
 
-    pairs = {"project": [], "accumulate": [], "apply": []}  # event pairs around calls, when timing inside steps
+    # Event pairs around calls, when timing inside steps. An event recorded
+    # between two dependent launches delays the second by several us (its
+    # packet, even without a system fence), so a call's time inside steps is
+    # taken as a difference of brackets that each hold one such delay: pass
+    # "single" brackets every call alone, pass "pairs" every project with the
+    # accumulate that follows it, pass "tail" every layer's last accumulate
+    # with the apply that follows it. Then accumulate = pair - project alone,
+    # project = pair - accumulate alone, apply = tail - accumulate alone.
+    pairs = {k: [] for k in ("project", "accumulate", "apply", "pair", "tail")}
 
-    def timed(name, fn, on):
-        if not on:
+    def bracket(name, *fns):
+        a, b = TimingEvent(), TimingEvent()
+        a.record(s_main)
+        for fn in fns:
             fn()
-            return
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        fn()
-        b.record()
+        b.record(s_main)
         pairs[name].append((a, b))
 
-    def one_step(step, time_calls=False):
+    def one_step(step, mode=None):
         buf = 0
         if wl["refresh"]:
             buf = step % 2
@@ -327,9 +395,25 @@ def main():
         for l in range(L):
             c_layer[l].zero_()
             for i in range(n_mb):
-                timed("project", lambda: calls.project(buf, l, i), time_calls)
-                timed("accumulate", lambda: calls.accumulate(l, i), time_calls)
-            timed("apply", lambda: calls.apply(cfg, step, buf, l, args.carried_norm), time_calls)
+                prj = lambda: calls.project(buf, l, i)  # noqa: E731
+                acc = lambda: calls.accumulate(l, i)  # noqa: E731
+                if mode == "single":
+                    bracket("project", prj)
+                    bracket("accumulate", acc)
+                elif mode == "pairs":
+                    bracket("pair", prj, acc)
+                elif mode == "tail" and i == n_mb - 1:
+                    prj()
+                else:
+                    prj()
+                    acc()
+            app = lambda: calls.apply(cfg, step, buf, l, args.carried_norm)  # noqa: E731
+            if mode == "single":
+                bracket("apply", app)
+            elif mode == "tail":
+                bracket("tail", lambda: calls.accumulate(l, n_mb - 1), app)
+            else:
+                app()
         if wl["refresh"]:
             ev = torch.cuda.Event()
             ev.record(s_main)
@@ -378,18 +462,21 @@ def main():
     smp_bytes = sum(2 * k * r for _, _, k, _ in mats)
     app_launch_bytes = appc_bytes if args.carried_norm else app_bytes
 
-    # each call's duration inside steps: a third pass of K steps like the timed
-    # ones, with an event pair on the launch stream around every batched call
+    # each call's duration inside steps: three more passes of K steps like the
+    # timed ones, with event pairs on the launch stream (timing-only events
+    # without a system-scope fence) around calls or pairs of calls (above)
     kern, in_step = {}, {}
     if not args.no_kernel_timing:
-        torch.cuda.synchronize()
-        for s in range(args.steps):
-            one_step(base + s, time_calls=True)
-        s_main.wait_stream(s_side)
-        torch.cuda.synchronize()
-        base += args.steps
-        for name, prs in pairs.items():
-            in_step[name] = sum(a.elapsed_time(b) for a, b in prs) * 1e-3 / len(prs)  # seconds per call
+        for mode in ("single", "pairs", "tail"):
+            torch.cuda.synchronize()
+            for s in range(args.steps):
+                one_step(base + s, mode)
+            s_main.wait_stream(s_side)
+            torch.cuda.synchronize()
+            base += args.steps
+        mean = {name: sum(a.elapsed_ms(b) for a, b in prs) * 1e-3 / len(prs) for name, prs in pairs.items()}
+        in_step = {"accumulate": mean["pair"] - mean["project"], "project": mean["pair"] - mean["accumulate"],
+                   "apply": mean["tail"] - mean["accumulate"]}  # seconds per call
 
         # Per-entry-point timing back to back: HIP events on the launch stream
         # around K repetitions of one step's calls of a single entry point.
