@@ -367,7 +367,10 @@ rgc_status_t rgc_test_philox(uint64_t seed, int64_t n, const uint32_t* ctr, uint
                              void* stream);
 
 /* out[i][j] = SR(v[i][j]) with the rounding bits of weight element
- * (row0 + i, col0 + j) under `seed`, exactly as rgc_apply draws them.
+ * (row0 + i, col0 + j) under `seed`: the same bits rgc_apply draws, rounded
+ * here one element at a time (the update sweep rounds pairs and packs them
+ * with a byte permute; the parity tests pin the update's own written bits
+ * against the oracle separately).
  * v: rows x cols fp32 (row stride ld); out: rows x cols bf16 (row stride ld). */
 rgc_status_t rgc_test_stochastic_round(const float* v, uint16_t* out, int64_t rows, int64_t cols,
                                        int64_t ld, int64_t row0, int64_t col0, uint64_t seed,
