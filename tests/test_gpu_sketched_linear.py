@@ -7,7 +7,7 @@ import torch
 
 import oracle as orc
 from rank_randomized_gradient_amd import SketchedLinear, rgc, synth
-from parity_tools import assert_update_close, rel_frobenius
+from parity_tools import assert_sum_close, assert_update_close, qr_margin_mismatches, rel_frobenius
 
 pytestmark = pytest.mark.gpu
 
@@ -152,3 +152,36 @@ def test_sketched_linear_carried_norm_sees_weight_changes(dev, how):
             sd["weight"] = w2.clone()
             sd["weight_norm2"] = torch.zeros(1, dtype=torch.float64, device=dev)  # a norm that does not match
             carry.load_state_dict(sd)
+
+
+@pytest.mark.parametrize("r,kind", [(4, "rademacher"), (8, "qr"), (64, "qr")])
+def test_sketched_linear_every_forward_path(dev, r, kind):
+    """The layer at r = 4 (XP from the small-rank project after the tile
+    grid), r = 8 (XP as one more column of tiles) and r = 64 (XP as slices
+    inside Y's tiles): Y and dX against the oracle's layer products, the
+    sketch against the oracle's loop, the saved tensors XP and W only."""
+    d, k, mb, n_mb, seed = 264, 520, 300, 2, 7
+    w = synth.normal_bf16((d, k), 0.02, seed=4000 + r)
+    layer = SketchedLinear(k, d, r, kind=kind, device=dev, weight=w.clone())
+    layer.begin_update(seed)
+    p_ref = orc.sample_projection(kind, seed, k, r)
+    c_ref = np.zeros((d, r), np.float32)
+    for i in range(n_mb):
+        x = synth.normal_bf16((mb, k), 1.0, seed=4100 + 10 * r + i)
+        dy = synth.normal_bf16((mb, d), 0.1, seed=4200 + 10 * r + i)
+        xg = x.to(dev).requires_grad_(True)
+        y = layer(xg)
+        assert sorted(tuple(t.shape) for t in y.grad_fn.saved_tensors) == sorted([(mb, r), (d, k)])
+        y.backward(dy.to(dev))
+        torch.cuda.synchronize()
+        y_ref, xp_ref = orc.layer_forward(bits(x), bits(w), p_ref)
+        absy = np.abs(orc.bf16_to_f64(bits(x))) @ np.abs(orc.bf16_to_f64(bits(w))).T
+        assert_sum_close(bits(y.detach()), y_ref, absy, what=f"Y r={r}")
+        dx_ref, c_ref = orc.layer_backward(bits(dy), bits(w), xp_ref, c_ref)
+        absd = np.abs(orc.bf16_to_f64(bits(dy))) @ np.abs(orc.bf16_to_f64(bits(w)))
+        assert_sum_close(bits(xg.grad), dx_ref, absd, what=f"dX r={r}")
+    if kind == "rademacher":
+        assert np.array_equal(bits(layer.proj), p_ref)
+    else:
+        assert qr_margin_mismatches(bits(layer.proj), seed, k, r) <= 2
+    assert rel_frobenius(layer.sketch.cpu().numpy(), c_ref) < 1e-4
