@@ -8,8 +8,9 @@ error of a long sum; at most 1e-3 of the elements differing), C within 1e-5
 relative Frobenius and bit-identical to rgc_accumulate's. Y and dX are also
 checked against an fp32 torch reference (relative Frobenius < 4e-3, the
 bf16 output rounding). Shapes are ragged in every dimension: T, d, k not
-multiples of the 256 x 256 tile or of the 64-row K-step, K below one step,
-a single token row, strided X, Y and dX.
+multiples of the 256 x 256 tile or of the 32-row K-step, K below one step,
+a single token row, strided X, Y and dX; every rank through the forward
+(XP as slices inside Y's tiles, or as a column of tiles of its own).
 """
 import numpy as np
 import pytest
@@ -40,9 +41,9 @@ def _fp32_ref(a, b):
     return (a.float() @ b.float()).numpy()
 
 
-# (T, k, d, r): tile tails in T and d, K tails (72 = one step + 8, 40 < one
-# step, 1000), r = 0 (Y alone), 4 (XP from the small-rank project), 8 (a P
-# narrower than a block), up to 256
+# (T, k, d, r): tile tails in T and d, K tails (72 = two steps + 8, 40 = one
+# step + 8, 1000), r = 0 (Y alone), 4 (XP from the small-rank project), 8 (a
+# P narrower than a block: a column of tiles), up to 256
 SHAPES = [(300, 520, 264, 64), (256, 512, 512, 128), (77, 1000, 1048, 16), (513, 72, 136, 8),
           (1000, 2048, 520, 256), (1, 40, 8, 32), (129, 264, 776, 0), (600, 1048, 200, 4),
           (257, 64, 264, 48), (4096, 1024, 1024, 128)]
@@ -181,3 +182,20 @@ def test_rejects_bad_arguments(dev):
     with pytest.raises(rgc.RgcError):  # XP without C
         rgc.rgc_linear_backward(torch.zeros(16, 32, dtype=torch.bfloat16, device=dev), w,
                                 XP=torch.zeros(16, 16, dtype=torch.bfloat16, device=dev))
+
+
+@pytest.mark.parametrize("r", [16 * q for q in range(1, 17)])
+@pytest.mark.parametrize("d", [264, 1048])
+def test_forward_every_rank(dev, d, r):
+    """Every tiled rank through the forward, at two widths of Y: XP as slices
+    inside Y's tiles where a tile carries at most two (r <= 64 at d = 264,
+    r <= 160 at d = 1048), else as one more column of tiles."""
+    T, k = 300, 520
+    x = synth.normal_bf16((T, k), 1.0, seed=r + d)
+    w = synth.normal_bf16((d, k), 0.02, seed=r + d + 1)
+    p = synth.normal_bf16((k, r), 1.0, seed=r + d + 2)
+    y, xp = rgc.rgc_linear_forward(x.to(dev), w.to(dev), p.to(dev))
+    torch.cuda.synchronize()
+    y_ref, xp_ref = orc.layer_forward(bits(x), bits(w), bits(p))
+    assert_sum_close(bits(y), y_ref, _absprod(bits(x), bits(w).T), what=f"Y d={d} r={r}")
+    assert_sum_close(bits(xp), xp_ref, _absprod(bits(x), bits(p)), what=f"XP d={d} r={r}")
