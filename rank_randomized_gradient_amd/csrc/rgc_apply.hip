@@ -310,6 +310,18 @@ __device__ __forceinline__ void rounding_words(uint64_t seed, int64_t i, int64_t
 // elements the tile owns (rows row0 .. row0+ROWS-1, columns jb .. jb+63, and
 // inside W) are stored or counted. Matrices with fewer than ROWS rows or 64
 // columns use origin 0 and clamp the copied rows and columns instead.
+// The hardware hands workgroups to the eight XCDs round-robin; this numbers
+// them so that each XCD runs a contiguous run of workgroups (whole row blocks
+// of W), so that a row block's C rows are fetched into one XCD's L2, not into
+// all eight. The partition of the work over the numbers, and so every sum,
+// is unchanged.
+__device__ __forceinline__ int apply_logical_workgroup(int b, int G) {
+  constexpr int kXcds = 8;
+  const int x = b % kXcds, pos = b / kXcds;
+  const int q = G / kXcds, rem = G % kXcds;
+  return x * q + (x < rem ? x : rem) + pos;
+}
+
 template <int R, int MODE>
 __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch b) {  // ApplyShape::PER_CU
   using Tr = ApplyTraits<R>;
@@ -319,7 +331,7 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
   __shared__ double red[2][kApplyWaves];
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int n = lane & 15, g = lane >> 4;
-  const int w = blockIdx.x;
+  const int w = apply_logical_workgroup(blockIdx.x, gridDim.x);
   const int m = apply_item_of(b, w);
   const ApplyItem& it = b.it[m];
   const int64_t wl = w - b.wbase[m], gm = b.wbase[m + 1] - b.wbase[m];
