@@ -84,8 +84,8 @@ KERNEL_SOURCES = ["rank_randomized_gradient_amd/csrc/rgc_sketch.hip", "rank_rand
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS),
                     help="the bench line is the default; the others measure the remaining workload shapes")
     ap.add_argument("--carried-norm", action="store_true",
@@ -752,11 +752,11 @@ def _blas() -> tuple[str, int]:
 
 
 def cpu_baseline(X, D, W, mats, wl):
-    """The CPU oracle, untuned, on a bounded sample of the same workload (one
-    layer's share, about 10-15 s of CPU work): the layer's 7 QR projections,
-    one 4096-token microbatch of project + accumulate for all 7 matrices, and
-    the updates of all 7 matrices. The step time is extrapolated to 8
-    microbatches and 36 layers."""
+    """The CPU oracle, untuned, on a bounded sample of the same workload: one
+    full layer (about 15 s of CPU work): the layer's 7 QR projections, every
+    4096-token microbatch of project + accumulate for its 7 matrices, and the
+    updates of all 7 matrices. The step time is that layer's time x the
+    number of layers (labelled as an extrapolation)."""
     import numpy as np
 
     import oracle as orc
@@ -765,28 +765,32 @@ def cpu_baseline(X, D, W, mats, wl):
     r, mb, L = wl["r"], wl["microbatch"], wl["layers"]
     n_mb = wl["tokens"] // mb
     bits = synth.to_numpy_bits
-    xs = {name: bits(x[:mb]) for name, x in X.items()}
-    ds = [bits(d[:mb]) for d in D]
     t0 = time.perf_counter()
     ps = [orc.qr_projection(step_seed(wl["cfg"], 0, 0, m), k, r) for m, (_, _, k, _) in enumerate(mats)]
     t1 = time.perf_counter()
-    cs = []
-    for m, (_, d, k, src) in enumerate(mats):
-        c = np.zeros((d, r), np.float32)
-        cs.append(orc.accumulate(c, ds[m], orc.project(xs[src], ps[m])))
+    cs = [np.zeros((d, r), np.float32) for _, d, _, _ in mats]
+    t_mb = 0.0
+    for i in range(n_mb):
+        xs = {name: bits(x[i * mb:(i + 1) * mb]) for name, x in X.items()}  # host copies, not timed
+        ds = [bits(d[i * mb:(i + 1) * mb]) for d in D]
+        ta = time.perf_counter()
+        for m, (_, d, k, src) in enumerate(mats):
+            cs[m] = orc.accumulate(cs[m], ds[m], orc.project(xs[src], ps[m]))
+        t_mb += time.perf_counter() - ta
     t2 = time.perf_counter()
     for m in range(len(mats)):
         orc.apply_update(bits(W[m]), cs[m], ps[m], wl["tau"], step_seed(wl["cfg"], 0, 0, m))
     t3 = time.perf_counter()
-    layer_s = (t1 - t0) + n_mb * (t2 - t1) + (t3 - t2)
+    layer_s = (t1 - t0) + t_mb + (t3 - t2)
     step_s = L * layer_s
+    # the contractions' flops in the sample: project and accumulate per microbatch, H = C P^T per update
+    flops = sum(n_mb * (2 * mb * k * r + 2 * mb * d * r) + 2 * d * k * r for _, d, k, _ in mats)
     blas, threads = _blas()
     return {"value": round(wl["tokens"] / step_s, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "cpu_model": _cpu_model(), "blas": blas,
-            "sample": f"one layer's share: 7 QR projections ({t1 - t0:.1f}s) + 1 of {n_mb} microbatches "
-                      f"(project+accumulate, 7 matrices, {t2 - t1:.1f}s) + the updates of all 7 matrices "
-                      f"({t3 - t2:.1f}s); "
-                      f"step = {L} x (projections + {n_mb} x microbatch + updates) = {step_s:.0f}s "
+            "cpu_model": _cpu_model(), "blas": blas, "gflops": round(flops / layer_s / 1e9, 2),
+            "sample": f"one full layer: 7 QR projections ({t1 - t0:.1f}s) + {n_mb} microbatches of "
+                      f"project+accumulate for 7 matrices ({t_mb:.1f}s) + the updates of all 7 matrices "
+                      f"({t3 - t2:.1f}s) = {layer_s:.1f}s; step = {L} x that layer = {step_s:.0f}s "
                       f"(extrapolated x{L} layers)"}
 
 
