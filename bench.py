@@ -208,7 +208,7 @@ class Calls:
     rewritten in place before each use). Validation still runs in the library
     on every call; only Python's per-call marshalling is hoisted."""
 
-    def __init__(self, rgc, lib, wl, X, D, W, P_sets, C, XP, ws_main, ws_side, s_main, s_side):
+    def __init__(self, rgc, lib, wl, X, D, W, P_sets, C, XP, ws_main, ws_side, ws_acc, s_main, s_side):
         import torch
 
         self.rgc, self.lib = rgc, lib
@@ -230,6 +230,10 @@ class Calls:
                         lib.rgc_sample_projections_workspace_size(self.kind, n, self.ks_arr, r))
         need_side = lib.rgc_sample_projections_workspace_size(self.kind, n, self.ks_arr, r)
         self.wm = (vp(ws_main.get(need_main)[0].value), need_main)
+        # the accumulate's own workspace: it carries the split tiles' partial
+        # sums from a layer's first microbatch to its last (deferred finish)
+        need_acc = lib.rgc_accumulate_batch_workspace_size(n, self.ds_arr, mb, r)
+        self.wa = (vp(ws_acc.get(need_acc)[0].value if need_acc else 0), need_acc)
         self.wsd = (vp(ws_side.get(need_side)[0].value), need_side) if need_side else (vp(0), 0)
         self.seeds = [arr(u64, [0] * n) for _ in range(L)]
         self.p_ptrs = [[arr(vp, [p.data_ptr() for p in P_sets[b][l]]) for l in range(L)] for b in range(len(P_sets))]
@@ -262,9 +266,12 @@ class Calls:
                                                    self.wm[0], self.wm[1], self.sm))
 
     def accumulate(self, layer, i):
-        self.rgc._check(self.lib.rgc_accumulate_batch(self.n, self.d_ptrs[i], self.ldd, self.ds_arr, self.xp_ptrs,
-                                                      self.c_ptrs[layer], self.mb, self.r, self.wm[0], self.wm[1],
-                                                      self.sm))
+        # one accumulation per layer and step: the first microbatch writes the
+        # split tiles' partial slots, the last adds them into C
+        phase = (1 if i == 0 else 0) | (2 if i == self.n_mb - 1 else 0)
+        self.rgc._check(self.lib.rgc_accumulate_batch_deferred(
+            self.n, self.d_ptrs[i], self.ldd, self.ds_arr, self.xp_ptrs, self.c_ptrs[layer], self.mb, self.r,
+            self.wa[0], self.wa[1], phase, self.sm))
 
     def apply(self, cfg, step, pbuf, layer, carried=False):
         for m in range(self.n):
@@ -342,7 +349,8 @@ def main():
     XP = [torch.empty((mb, r), dtype=torch.bfloat16, device=dev) for _ in mats]
     s_main = torch.cuda.current_stream(dev)
     s_side = torch.cuda.Stream(device=dev)  # default priority
-    calls = Calls(rgc, lib, wl, X, D, W, P_sets, C, XP, rgc.Workspace(dev), rgc.Workspace(dev), s_main, s_side)
+    calls = Calls(rgc, lib, wl, X, D, W, P_sets, C, XP, rgc.Workspace(dev), rgc.Workspace(dev), rgc.Workspace(dev),
+                  s_main, s_side)
     torch.cuda.synchronize()
 
     # The projections of step s depend only on their seeds, so they are drawn one
@@ -374,15 +382,17 @@ def main():
     # accumulate that follows it, pass "tail" every layer's last accumulate
     # with the apply that follows it. Then accumulate = pair - project alone,
     # project = pair - accumulate alone, apply = tail - accumulate alone.
-    pairs = {k: [] for k in ("project", "accumulate", "apply", "pair", "tail")}
+    pairs = {k: [] for k in ("project", "accumulate", "accumulate_last", "apply", "pair", "tail")}
 
-    def bracket(name, *fns):
+    def bracket(name, *fns, also=None):
         a, b = TimingEvent(), TimingEvent()
         a.record(s_main)
         for fn in fns:
             fn()
         b.record(s_main)
         pairs[name].append((a, b))
+        if also:
+            pairs[also].append((a, b))
 
     def one_step(step, mode=None):
         buf = 0
@@ -400,7 +410,7 @@ def main():
                 acc = lambda: calls.accumulate(l, i)  # noqa: E731
                 if mode == "single":
                     bracket("project", prj)
-                    bracket("accumulate", acc)
+                    bracket("accumulate", acc, also="accumulate_last" if i == n_mb - 1 else None)
                 elif mode == "pairs":
                     bracket("pair", prj, acc)
                 elif mode == "tail" and i == n_mb - 1:
@@ -477,7 +487,7 @@ def main():
             base += args.steps
         mean = {name: sum(a.elapsed_ms(b) for a, b in prs) * 1e-3 / len(prs) for name, prs in pairs.items()}
         in_step = {"accumulate": mean["pair"] - mean["project"], "project": mean["pair"] - mean["accumulate"],
-                   "apply": mean["tail"] - mean["accumulate"]}  # seconds per call
+                   "apply": mean["tail"] - mean["accumulate_last"]}  # seconds per call
 
         # Per-entry-point timing back to back: HIP events on the launch stream
         # around K repetitions of one step's calls of a single entry point.
@@ -533,7 +543,8 @@ def main():
         dom = max(share, key=share.get)
         by, fl = work[dom]
         t = in_step[dom]
-        kernels = {"accumulate": f"rgc_accumulate_batch (accumulate_kernel<{r}> + finish_tiles_kernel<{r},false>)",
+        kernels = {"accumulate": f"rgc_accumulate_batch_deferred (accumulate_kernel<{r}> per call + "
+                                 f"finish_tiles_kernel<{r},false> on a layer's last of {n_mb} calls)",
                    "project": f"rgc_project_batch (project_kernel<{r}> + finish_tiles_kernel<{r},true>)",
                    "apply": "rgc_apply_batch (norms, scale, update launches)"}
         achieved = by / t / 1e9
@@ -576,6 +587,8 @@ def main():
         "config": {"workload": wl["desc"], "layers": L, "matrices_per_layer": n, "r": r, "tokens_per_step": T,
                    "microbatch": mb, "projection": "qr-gaussian" if wl["kind"] == "qr" else "rademacher, fixed",
                    "tau": wl["tau"],
+                   "accumulation": f"deferred: split-tile partials summed into C once per layer and step "
+                                   f"(after the last of {n_mb} microbatches)",
                    "weight_norm": "carried from the previous update" if args.carried_norm else "streamed from W",
                    "resident_weight_GiB": round(sum(w.numel() * 2 for ws_ in W for w in ws_) / 2**30, 2)},
         "sketch_accumulate_TFLOPs": round(acc["TFLOPs_in_step"], 2) if acc else None,

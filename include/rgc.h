@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define RGC_ABI_VERSION 5
+#define RGC_ABI_VERSION 6
 
 typedef enum {
   RGC_OK = 0,
@@ -180,6 +180,24 @@ size_t rgc_accumulate_batch_workspace_size(int64_t n, const int64_t* ds, int64_t
 rgc_status_t rgc_accumulate_batch(int64_t n, const uint16_t* const* Ds, const int64_t* ldds, const int64_t* ds,
                                   const uint16_t* const* XPs, float* const* Cs, int64_t T, int64_t r, void* ws,
                                   size_t ws_bytes, void* stream);
+
+/* Deferred form for the microbatches of one accumulation (the calls that add
+ * into the same Cs before the next update): the work split between
+ * workgroups leaves fp32 partial sums for some tiles, and here they stay in the
+ * workspace from call to call, added there, and reach C once, in the call that
+ * ends the accumulation, instead of in a finishing pass after every call.
+ * phase: bit 0 set = the first call of the accumulation, bit 1 set = the last;
+ * 3 = a single call (exactly rgc_accumulate_batch). C holds the full sum only
+ * after the last call; in between it holds part of it. Every call of one
+ * accumulation must have the same n, ds, T and r, run on the same device and
+ * use the same workspace, which no other call may use in between (its contents
+ * carry the partial sums; this is not checked). The sum differs from the
+ * per-call form's only in the fp32 addition order; it is bit-reproducible.
+ * Ranks 4 and 8 complete C in every call whatever the phase. */
+rgc_status_t rgc_accumulate_batch_deferred(int64_t n, const uint16_t* const* Ds, const int64_t* ldds,
+                                           const int64_t* ds, const uint16_t* const* XPs, float* const* Cs,
+                                           int64_t T, int64_t r, void* ws, size_t ws_bytes, int phase,
+                                           void* stream);
 
 /* ---- 4. Normalized update with stochastic rounding ------------------------ */
 
@@ -393,6 +411,10 @@ rgc_status_t rgc_test_accumulate_batch_wgs(int64_t workgroups, int64_t n, const 
                                            const int64_t* ldds, const int64_t* ds, const uint16_t* const* XPs,
                                            float* const* Cs, int64_t T, int64_t r, void* ws, size_t ws_bytes,
                                            void* stream);
+rgc_status_t rgc_test_accumulate_batch_deferred_wgs(int64_t workgroups, int64_t n, const uint16_t* const* Ds,
+                                                    const int64_t* ldds, const int64_t* ds,
+                                                    const uint16_t* const* XPs, float* const* Cs, int64_t T,
+                                                    int64_t r, void* ws, size_t ws_bytes, int phase, void* stream);
 
 /* rgc_project_shared with a caller-given workgroup count (as above). */
 size_t rgc_test_project_shared_workspace_size(int64_t workgroups, int64_t n, int64_t T, int64_t k, int64_t r);

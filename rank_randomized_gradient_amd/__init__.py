@@ -13,6 +13,7 @@ from .rgc import (  # noqa: F401
     load_library,
     rgc_accumulate,
     rgc_accumulate_batch,
+    rgc_accumulate_batch_deferred,
     rgc_apply,
     rgc_apply_batch,
     rgc_apply_carried,

@@ -537,6 +537,7 @@ struct AccumulateBatch {
   const uint16_t* XP[kMaxItems];
   float* C[kMaxItems];
   float* part;                    // 2 G slots of TILE x R fp32
+  int add_part;                   // 1: add the split tiles' partials to the slots (a later call of a deferred accumulation)
 };
 
 template <int RM>
@@ -598,7 +599,14 @@ struct AccumulatePolicy {
           }
         } else {
           float* p = ab.part + slot * Sh::TILE * R + row * R + rcol;
-          *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+          if (ab.add_part) {
+            // a deferred accumulation: this slot already holds the earlier
+            // calls' sums of the same segment (the same schedule every call)
+            const float4 o = *reinterpret_cast<const float4*>(p);
+            *reinterpret_cast<float4*>(p) = make_float4(o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]);
+          } else {
+            *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+          }
         }
       }
     }
@@ -1078,10 +1086,13 @@ size_t project_workspace(int n, const int64_t* ks, int64_t T, int64_t forced, bo
   return out;
 }
 
+// phase: bit 0 = the first call of an accumulation (the split tiles' slots are
+// written), bit 1 = the last (the finishing launch adds the slots into C);
+// 3 for a call that is both, the plain rgc_accumulate_batch.
 template <int R>
 rgc_status_t accumulate_launch(int n, const uint16_t* const* Ds, const int64_t* ldds, const int64_t* ds,
                                const uint16_t* const* XPs, float* const* Cs, int64_t T, void* ws, hipStream_t st,
-                               int64_t forced) {
+                               int64_t forced, int phase) {
   int64_t ks[kMaxItems];
   for (int m = 0; m < n; ++m) ks[m] = T;
   AccumulateBatch ab = {};
@@ -1096,9 +1107,10 @@ rgc_status_t accumulate_launch(int n, const uint16_t* const* Ds, const int64_t* 
     fb.C[m] = Cs[m];
   }
   ab.part = static_cast<float*>(ws);
+  ab.add_part = (phase & 1) ? 0 : 1;
   fb.part = ab.part;
   hipLaunchKernelGGL(accumulate_kernel<R>, dim3((unsigned)ab.s.G), dim3(256), 0, st, ab);
-  if (has_split_tiles(ab.s))
+  if ((phase & 2) && has_split_tiles(ab.s))
     hipLaunchKernelGGL((finish_tiles_kernel<R, 1, false>), finish_grid<R>(ab.s), dim3(256), 0, st, fb);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
@@ -1191,7 +1203,7 @@ rgc_status_t project_batch_impl(int64_t n, const uint16_t* const* Xs, const int6
 
 rgc_status_t accumulate_batch_impl(int64_t n, const uint16_t* const* Ds, const int64_t* ldds, const int64_t* ds,
                                    const uint16_t* const* XPs, float* const* Cs, int64_t T, int64_t r, void* ws,
-                                   size_t ws_bytes, void* stream, int64_t forced) {
+                                   size_t ws_bytes, void* stream, int64_t forced, int phase = 3) {
   if (n < 0 || T < 0 || r <= 0) return RGC_ERR_SHAPE;
   if (n > kMaxItems || !rank_supported(r)) return RGC_ERR_UNSUPPORTED;
   if (n == 0 || T == 0) return RGC_OK;
@@ -1210,7 +1222,7 @@ rgc_status_t accumulate_batch_impl(int64_t n, const uint16_t* const* Ds, const i
       }))
     return st;
   dispatch_rank(r, [&](auto rc) {
-    st = accumulate_launch<decltype(rc)::value>((int)n, Ds, ldds, ds, XPs, Cs, T, ws, hs, forced);
+    st = accumulate_launch<decltype(rc)::value>((int)n, Ds, ldds, ds, XPs, Cs, T, ws, hs, forced, phase);
   });
   return st;
 }
@@ -1235,6 +1247,14 @@ extern "C" rgc_status_t rgc_accumulate_batch(int64_t n, const uint16_t* const* D
                                              const int64_t* ds, const uint16_t* const* XPs, float* const* Cs,
                                              int64_t T, int64_t r, void* ws, size_t ws_bytes, void* stream) {
   return accumulate_batch_impl(n, Ds, ldds, ds, XPs, Cs, T, r, ws, ws_bytes, stream, 0);
+}
+
+extern "C" rgc_status_t rgc_accumulate_batch_deferred(int64_t n, const uint16_t* const* Ds, const int64_t* ldds,
+                                                      const int64_t* ds, const uint16_t* const* XPs, float* const* Cs,
+                                                      int64_t T, int64_t r, void* ws, size_t ws_bytes, int phase,
+                                                      void* stream) {
+  if (phase < 0 || phase > 3) return RGC_ERR_SHAPE;
+  return accumulate_batch_impl(n, Ds, ldds, ds, XPs, Cs, T, r, ws, ws_bytes, stream, 0, phase);
 }
 
 extern "C" size_t rgc_project_workspace_size(int64_t T, int64_t k, int64_t r) {
@@ -1281,6 +1301,15 @@ extern "C" rgc_status_t rgc_test_accumulate_batch_wgs(int64_t workgroups, int64_
                                                       int64_t r, void* ws, size_t ws_bytes, void* stream) {
   if (workgroups <= 0) return RGC_ERR_SHAPE;
   return accumulate_batch_impl(n, Ds, ldds, ds, XPs, Cs, T, r, ws, ws_bytes, stream, workgroups);
+}
+
+extern "C" rgc_status_t rgc_test_accumulate_batch_deferred_wgs(int64_t workgroups, int64_t n,
+                                                               const uint16_t* const* Ds, const int64_t* ldds,
+                                                               const int64_t* ds, const uint16_t* const* XPs,
+                                                               float* const* Cs, int64_t T, int64_t r, void* ws,
+                                                               size_t ws_bytes, int phase, void* stream) {
+  if (workgroups <= 0 || phase < 0 || phase > 3) return RGC_ERR_SHAPE;
+  return accumulate_batch_impl(n, Ds, ldds, ds, XPs, Cs, T, r, ws, ws_bytes, stream, workgroups, phase);
 }
 
 // ---- one pass over a shared X ---------------------------------------------

@@ -60,6 +60,13 @@ SIGNATURES = {
     "rgc_accumulate_batch": (ctypes.c_int, [_i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_i64),
                                             ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64, _i64, _vp, _sz, _vp]),
     "rgc_accumulate": (ctypes.c_int, [_vp, _i64, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "rgc_accumulate_batch_deferred": (ctypes.c_int, [_i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64),
+                                                     ctypes.POINTER(_i64), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                                     _i64, _i64, _vp, _sz, ctypes.c_int, _vp]),
+    "rgc_test_accumulate_batch_deferred_wgs": (ctypes.c_int, [_i64, _i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64),
+                                                              ctypes.POINTER(_i64), ctypes.POINTER(_vp),
+                                                              ctypes.POINTER(_vp), _i64, _i64, _vp, _sz, ctypes.c_int,
+                                                              _vp]),
     "rgc_apply_workspace_size": (_sz, [_i64, _i64, _i64]),
     "rgc_apply_batch_workspace_size": (_sz, [_i64, ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i64]),
     "rgc_apply_batch": (ctypes.c_int, [_i64, ctypes.POINTER(_vp), ctypes.POINTER(_i64), ctypes.POINTER(_vp),
@@ -360,6 +367,43 @@ def rgc_accumulate_batch(Ds, XPs, Cs, workspace: Workspace | None = None):
     wp, wn = ws.get(lib.rgc_accumulate_batch_workspace_size(n, _i64s(ds), T, r))
     _check(lib.rgc_accumulate_batch(n, _ptrs(Ds), _i64s(ldds), _i64s(ds), _ptrs(XPs), _ptrs(Cs), T, r, wp, wn,
                                     _stream(dev)))
+    return Cs
+
+
+def rgc_accumulate_batch_deferred(Ds, XPs, Cs, workspace: Workspace, first: bool, last: bool,
+                                  workgroups: int = 0):
+    """Cs[m] += Ds[m]^T XPs[m] as one call of an accumulation over several
+    microbatches whose split-tile partial sums stay in `workspace` between the
+    calls and reach C in the call with last=True. The workspace is required:
+    it carries state from the first call to the last, so no other call may
+    use it in between. workgroups > 0 forces the workgroup count (test hook;
+    the same count for every call of the accumulation)."""
+    lib = load_library()
+    n = len(Ds)
+    if n == 0:
+        return Cs
+    if workspace is None:
+        raise RgcError("a deferred accumulation needs its own workspace")
+    dev = _need_gpu(*Ds, *XPs, *Cs)
+    T = Ds[0].shape[0]
+    r = XPs[0].shape[1]
+    ldds, ds = [], []
+    for dd, xp, c in zip(Ds, XPs, Cs):
+        ldds.append(_rows(dd, torch.bfloat16, "D"))
+        _dense(xp, torch.bfloat16, "XP")
+        _dense(c, torch.float32, "C")
+        if dd.shape[0] != T or tuple(xp.shape) != (T, r) or tuple(c.shape) != (dd.shape[1], r):
+            raise RgcError("batch items must share T and r: D T x d, XP T x r, C d x r")
+        ds.append(dd.shape[1])
+    phase = (1 if first else 0) | (2 if last else 0)
+    if workgroups > 0:
+        wp, wn = workspace.get(lib.rgc_test_sketch_workspace_size(1, workgroups, n, _i64s(ds), T, r))
+        _check(lib.rgc_test_accumulate_batch_deferred_wgs(workgroups, n, _ptrs(Ds), _i64s(ldds), _i64s(ds),
+                                                          _ptrs(XPs), _ptrs(Cs), T, r, wp, wn, phase, _stream(dev)))
+        return Cs
+    wp, wn = workspace.get(lib.rgc_accumulate_batch_workspace_size(n, _i64s(ds), T, r))
+    _check(lib.rgc_accumulate_batch_deferred(n, _ptrs(Ds), _i64s(ldds), _i64s(ds), _ptrs(XPs), _ptrs(Cs), T, r, wp,
+                                             wn, phase, _stream(dev)))
     return Cs
 
 

@@ -320,3 +320,17 @@ def test_apply_rejects_widths_not_divisible_by_8(lib):
     f = ctypes.c_float(1e-3)
     assert lib.rgc_apply(FAKE, 260, FAKE, FAKE, 64, 260, 16, f, 0, None, FAKE, 1 << 20, s) == UNSUP  # k % 8
     assert lib.rgc_apply(FAKE, 256, FAKE, FAKE, 68, 256, 16, f, 0, None, FAKE, 1 << 20, s) == UNSUP  # d % 8
+
+
+def test_deferred_accumulate_validation(lib):
+    s = None
+    n = 1
+    dptr = (ctypes.c_void_p * n)(FAKE)
+    lds = (ctypes.c_int64 * n)(256)
+    ds = (ctypes.c_int64 * n)(256)
+    fn = lib.rgc_accumulate_batch_deferred
+    assert fn(n, dptr, lds, ds, dptr, dptr, 16, 64, None, 0, 4, s) == SHAPE  # phase out of range
+    assert fn(n, dptr, lds, ds, dptr, dptr, 16, 64, None, 0, -1, s) == SHAPE
+    assert fn(0, None, None, None, None, None, 16, 64, None, 0, 1, s) == OK
+    assert fn(n, dptr, lds, ds, dptr, dptr, 16, 72, None, 0, 1, s) == UNSUP  # rank
+
