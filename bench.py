@@ -177,10 +177,12 @@ def sources_digest() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per accumulate launch measured with rocprofv3 counters (the
-    record gives the commands and the copy-kernel scaling), or None when the
-    record is missing or was taken from different kernel sources."""
+def recorded_traffic(workload: str, key: str = "hbm_bytes_per_launch"):
+    """HBM bytes per launch (the accumulate's, or with key
+    project_hbm_bytes_per_launch the project's) measured with rocprofv3
+    counters (the record gives the commands and the copy-kernel scaling), or
+    None when the record is missing or was taken from different kernel
+    sources."""
     rel = TRAFFIC_RECORDS.get(workload)
     if rel is None or not os.path.exists(os.path.join(ROOT, rel)):
         return None
@@ -188,12 +190,12 @@ def recorded_traffic(workload: str):
     with open(os.path.join(ROOT, rel)) as f:
         for line in f:
             if ":" in line and line.lstrip().startswith("- "):
-                key, _, val = line.strip()[2:].partition(":")
-                fields[key.strip()] = val.strip().strip("`")
+                name, _, val = line.strip()[2:].partition(":")
+                fields[name.strip()] = val.strip().strip("`")
     if fields.get("sources_sha256") != sources_digest():
         return None
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields[key])
     except (KeyError, ValueError):
         return None
 
@@ -515,6 +517,17 @@ def main():
                     "sample_projection": L}
         work = {"project": (prj_bytes, prj_flops), "accumulate": (acc_bytes, acc_flops),
                 "apply": (app_launch_bytes, 0), "apply_carried": (appc_bytes, 0), "sample_projection": (smp_bytes, 0)}
+        # A difference of brackets can come out far below the back-to-back
+        # duration when something else stretches the brackets unevenly (a
+        # profiler that intercepts each dispatch does); a launch cannot run
+        # much faster inside a step than back to back, so such an estimate is
+        # dropped for the back-to-back mean and the entry says so.
+        rejected = []
+        for name in list(in_step):
+            b2b = per_step[name] / launches[name]
+            if in_step[name] < 0.8 * b2b:
+                rejected.append(name)
+                in_step[name] = b2b
         for name, sps in per_step.items():
             by, fl = work[name]
             avg = sps / launches[name]
@@ -524,6 +537,8 @@ def main():
             if name in in_step:
                 t = in_step[name]
                 e.update({"avg_us_in_step": 1e6 * t, "GBs_in_step": by / t / 1e9})
+                if name in rejected:
+                    e["in_step_estimate"] = "rejected (below 0.8 x back to back); back-to-back mean used"
                 if fl:
                     e["TFLOPs_in_step"] = fl / t / 1e12
                     ai = fl / by
@@ -551,7 +566,11 @@ def main():
         roofline = {"kernel": kernels[dom], "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "launch_us_in_step": round(1e6 * t, 2),
-                    "traffic": recorded_traffic(args.workload) if dom == "accumulate" else None,
+                    "launch_time_from": ("back-to-back mean (in-step estimate rejected)" if dom in rejected
+                                         else "in-step: difference of event-bracketed passes"),
+                    "traffic": (recorded_traffic(args.workload) if dom == "accumulate" else
+                                recorded_traffic(args.workload, "project_hbm_bytes_per_launch")
+                                if dom == "project" else None),
                     "algorithmic_bytes_per_launch": by,
                     "step_time_share": round(share[dom] / (ms_per_step * 1e-3), 4)}
         if fl:

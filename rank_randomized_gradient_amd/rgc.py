@@ -180,7 +180,10 @@ class Workspace:
     """Device scratch for the calls ordered on one stream, grown on demand.
 
     Workspace contents are dead after each call's kernels complete, so one
-    buffer serves every call ordered on a stream.
+    buffer serves every call ordered on a stream. The exception is a deferred
+    accumulation (rgc_accumulate_batch_deferred), whose partial sums live in
+    its workspace from the first call to the last: give it a Workspace of its
+    own.
     """
 
     def __init__(self, device: torch.device):
