@@ -10,18 +10,25 @@
 // Gaussian k x r matrix. Q is computed by CholeskyQR2 in fp64, for a batch of
 // matrices of one rank at once (each launch covers every matrix, so the
 // latency-bound steps are paid once per batch, not once per matrix):
-//   gram     A = Box-Muller normals from Philox (stored), partial Grams of A
-//            over 64-row blocks
-//   reduce   G1 = A^T A (partials summed in block order)
+//   draw     A = Box-Muller normals from Philox (stored; its own launch,
+//            one thread per four values, so that the fp64 transcendentals
+//            run at full occupancy)
+//   gram     partial Grams of A, one per workgroup of 128 rows (summed in
+//            registers over its two 64-row blocks)
+//   reduce   G1 = A^T A (partials summed in workgroup order)
 //   factor   U1 = chol(G1)^-1
-//   gram     Q1 = A U1 (stored), partial Grams of Q1, and P = bf16(fp32(
-//            sqrt(k/r) * Q1)) as a candidate
+//   gram     Q1 = A U1, partial Grams of Q1, and P = bf16(fp32(sqrt(k/r) *
+//            Q1)) as a candidate
 //   reduce   G2 = Q1^T Q1
 //   factor   U2 = chol(G2)^-1 (G2 is the identity up to rounding, so this is
 //            the first-order expansion I - S unless some |G2 - I| >= 1e-7)
-//   gram     P = bf16(fp32(sqrt(k/r) * Q1 U2)), skipped (the candidate kept)
+//   gram     P = bf16(fp32(sqrt(k/r) * Q1 U2)) with Q1 = A U1 formed again
+//            as in the pass before (same bits), skipped (the candidate kept)
 //            when every |G2 - I| < 1e-14, as it is for well-conditioned
 //            Gaussian matrices
+// Q1 is not stored at ranks of 16 and up (the third step, rarely run, forms
+// it again). Ranks 4 and 8 run one 64-row block per workgroup on the VALU,
+// drawing A in their first step and keeping Q1.
 // Cholesky factors have a positive diagonal, so Q is the unique factor with
 // the standard sign correction; the second pass restores orthogonality to
 // fp64 accuracy. Every reduction has a fixed order, so P is bit-reproducible.
@@ -70,8 +77,22 @@ __global__ void rademacher_kernel(uint16_t* __restrict__ P, int64_t k, int r, ui
 // CholeskyQR2, batched over up to kQrMaxBatch matrices of one rank R <= 128.
 // ---------------------------------------------------------------------------
 constexpr int kQrMaxBatch = 16;
-// Rows per Gram / multiply workgroup: four row tiles of 16, one per wave.
+// Rows per block of the Gram / multiply steps: four row tiles of 16, one per
+// wave.
 constexpr int kQrBlockRows = 64;
+// Blocks per workgroup of the fp64 MFMA steps: a workgroup sums its blocks'
+// Gram in registers and writes one partial, so the partials written and read
+// back per pass are half of one per block, and U is staged once per two
+// blocks. (More blocks per workgroup leave too few workgroups to fill the
+// chip for one transformer block's projections, and make each workgroup hold
+// its compute unit longer against other streams' launches.)
+constexpr int kQrGroupBlocks = 3;
+
+// Rows per workgroup of a block step at rank r (the small-rank steps run one
+// block per workgroup).
+__host__ __device__ constexpr int qr_group_rows(int64_t r) {
+  return r < 16 ? kQrBlockRows : kQrBlockRows * kQrGroupBlocks;
+}
 
 constexpr double kTwoPi = 6.283185307179586;  // 2*pi rounded to double
 // When every entry of Q1^T Q1 - I is below this, Q1 (U2 = I - S, |S| below it
@@ -86,14 +107,14 @@ struct QrBatch {
   double scale[kQrMaxBatch];
   uint16_t* P[kQrMaxBatch];
   double* A[kQrMaxBatch];     // k x R Gaussian
-  double* Q1[kQrMaxBatch];    // k x R after the first pass
-  double* part[kQrMaxBatch];  // one R x R partial Gram per row block
+  double* Q1[kQrMaxBatch];    // k x R after the first pass (ranks 4 and 8 only)
+  double* part[kQrMaxBatch];  // one R x R partial Gram per workgroup
   double* U1[kQrMaxBatch];
   double* U2[kQrMaxBatch];
   // status[m]: [0], [1] = factorization failed in pass 1, 2; [2] = the first
   // pass is already orthonormal to kQrFinalTol, so P from it is final
   uint32_t* status[kQrMaxBatch];
-  int block_begin[kQrMaxBatch + 1];  // workgroup prefix of the row blocks
+  int block_begin[kQrMaxBatch + 1];  // workgroup prefix (qr_group_rows rows per workgroup)
 };
 
 __device__ __forceinline__ int batch_item(const int* begin, int n, int b) {
@@ -118,150 +139,300 @@ __device__ __forceinline__ void gaussian4(uint64_t seed, int64_t i, int q, doubl
   }
 }
 
-// The three block steps on fp64 MFMA (v_mfma_f64_16x16x4_f64):
-//   MODE 0: draw the Gaussian rows of the block (into A and LDS), partial Gram of A;
-//   MODE 1: Q1 = A U1 (stored, with the candidate P from it), partial Gram of Q1;
-//   MODE 2: P = bf16(fp32(scale * Q1 U2)).
-// operands come straight from the staged rows, so the products no longer
-// wait on one LDS read per multiply-add. A 16 x 16 x 4 product takes, in lane
-// l, A[l % 16][l / 16] and B[l / 16][l % 16] and returns D[4 i + l / 16][l % 16]
-// in its register i = 0..3 (rows interleaved over the lane groups; measured
-// with a probe). Wave w owns row tile w of a multiply (the 64 staged rows are
-// four tiles of 16) and row tiles w, w + 4 of a Gram. U is upper triangular:
-// only its 16 x 16 tiles on and above the diagonal are staged (tile (rt, tc),
-// rt <= tc, at slot tc (tc + 1) / 2 + rt, rows padded to 17), which is what
-// lets r = 128 stage U beside the rows, and the multiply skips the zero tiles.
+// The Gaussian A of every matrix of the batch: one thread per row and four
+// columns (one Philox call), a grid row per matrix.
+template <int R>
+__global__ __launch_bounds__(256) void qr_gauss_kernel(QrBatch b) {
+  const int m = blockIdx.y;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (m >= b.n || t >= b.k[m] * (R / 4)) return;
+  const int64_t row = t / (R / 4);
+  const int q = (int)(t % (R / 4));
+  double z[4];
+  gaussian4(b.seed[m], row, q, z);
+  double2* dst = reinterpret_cast<double2*>(b.A[m] + row * R + 4 * q);
+  dst[0] = make_double2(z[0], z[1]);
+  dst[1] = make_double2(z[2], z[3]);
+}
+
+// The three block steps on fp64 MFMA (v_mfma_f64_16x16x4_f64), each
+// workgroup over up to kQrGroupBlocks blocks of 64 rows of one matrix:
+//   MODE 0: partial Gram of A;
+//   MODE 1: Q1 = A U1, the candidate P from Q1; partial Gram of Q1;
+//   MODE 2: Q1 = A U1 as in MODE 1, P = bf16(fp32(scale * Q1 U2)).
+// Operands come straight from the staged rows. A 16 x 16 x 4 product takes,
+// in lane l, A[l % 16][l / 16] and B[l / 16][l % 16] and returns
+// D[4 i + l / 16][l % 16] in its register i = 0..3 (rows interleaved over the
+// lane groups; measured with a probe). Wave w owns row tile w of a multiply
+// (the 64 staged rows are four tiles of 16). A Gram is symmetric and only its
+// upper triangle is summed later, so only the 16 x 16 tiles (ti, tj) with
+// ti <= tj are formed, numbered row by row, tile t by wave t % 4; each wave
+// keeps its tiles' sums in registers across the workgroup's blocks. U is
+// upper triangular: only its tiles on and above the diagonal are staged
+// (tile (rt, tc), rt <= tc, at slot tc (tc + 1) / 2 + rt, rows padded to 17),
+// which is what lets r = 128 stage U beside the rows, and the multiply skips
+// the zero tiles.
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kUTilePitch = 17;                     // doubles per staged U tile row
+// LDS pitches. The LDS serves 64 banks of 4 bytes, so a 64-bit read is free
+// of bank conflicts when each half-wave's 32 lanes cover all 64 banks.
+// The multiply reads its left operand as 16 rows x 4 columns (lane l: row
+// l % 16, column l / 16) and the Gram reads both operands as 4 rows x 16
+// columns; rows of 2 (mod 32) doubles serve the first, rows of 16 (mod 32)
+// doubles the second, so a block is staged at the pitch its reader needs.
+// U's tiles are read as 4 rows x 16 columns and are stored unpadded.
+constexpr int kUTilePitch = 16;                     // doubles per staged U tile row
 constexpr int kUTileSize = 16 * kUTilePitch;        // doubles per staged U tile
+__host__ __device__ constexpr int qr_gram_pitch(int R) { return R % 32 == 0 ? R + 16 : R; }
+__host__ __device__ constexpr int qr_mul_pitch(int R) { return R % 32 == 0 ? R + 2 : R + 18; }
 __host__ __device__ constexpr int utile_slot(int rt, int tc) { return tc * (tc + 1) / 2 + rt; }
 
+// Row and column tile of upper-triangle Gram tile t (row by row: row ti
+// holds the nt - ti tiles ti .. nt - 1).
+__device__ __forceinline__ void gram_tile(int t, int nt, int& ti, int& tj) {
+  int i = 0;
+  while (t >= nt - i) {
+    t -= nt - i;
+    ++i;
+  }
+  ti = i;
+  tj = i + t;
+}
+
+// Threads of a block-step workgroup: eight waves, two per SIMD, so that one
+// wave's products run while the other waits on LDS or a barrier.
+constexpr int kQrThreads = 512;
+constexpr int kQrWaves = kQrThreads / 64;
+
+// Stages the upper-triangle tiles of U (R x R, row-major) into LDS, 16 loads
+// in flight per thread at a time (few registers, so it can sit beside live
+// products).
+template <int R>
+__device__ __forceinline__ void qr_stage_u(double* u, const double* __restrict__ U) {
+  constexpr int CH = 16;
+#pragma unroll 1
+  for (int t0 = 0; t0 < R * R; t0 += kQrThreads * CH) {
+    double uv[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const int t = t0 + (int)threadIdx.x + kQrThreads * e;
+      uv[e] = t < R * R ? U[t] : 0.0;
+    }
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const int t = t0 + (int)threadIdx.x + kQrThreads * e;
+      if (t >= R * R) continue;
+      const int a = t / R, c = t % R;
+      if (a / 16 <= c / 16) u[utile_slot(a / 16, c / 16) * kUTileSize + (a % 16) * kUTilePitch + c % 16] = uv[e];
+    }
+  }
+}
+
+// Row and column of element e of a thread in a row-major block of R columns
+// that the workgroup's threads stride through (flat index threadIdx.x +
+// kQrThreads e), from the thread's own row q0 and column c0: one compare per
+// element instead of a division.
+template <int R>
+__device__ __forceinline__ void qr_flat_split(int q0, int c0, int e, int& row, int& col) {
+  const int d = kQrThreads * e / R, mm = kQrThreads * e % R;
+  const int c = c0 + mm;
+  row = q0 + d + (c >= R ? 1 : 0);
+  col = c >= R ? c - R : c;
+}
+
+// Workgroup barrier for LDS handoff only: this wave's LDS accesses are
+// complete when it arrives, and global loads stay in flight across it (the
+// next block's rows are fetched while the current block is multiplied).
+__device__ __forceinline__ void qr_lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Y = X U for the 16-row tile WR of a staged block (pitch LM) and the column
+// tiles tc = 2 j + H (j < NY), U's upper-triangle tiles staged in u.
+template <int R, int H>
+__device__ __forceinline__ void qr_multiply(const double* rows, const double* u, int wr, int li, int lg,
+                                            f64x4_t (&y)[(R / 16 + 1) / 2]) {
+  constexpr int NT = R / 16, NY = (NT + 1) / 2, LM = qr_mul_pitch(R);
+#pragma unroll
+  for (int j = 0; j < NY; ++j) y[j] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int kk = 0; kk < R / 4; ++kk) {
+    const double a = rows[(16 * wr + li) * LM + 4 * kk + lg];
+    const int rt = kk / 4;  // U's row tile; tiles left of the diagonal are zero
+#pragma unroll
+    for (int j = 0; j < NY; ++j) {
+      const int tc = 2 * j + H;
+      if (tc < NT && tc >= rt)
+        y[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+            a, u[utile_slot(rt, tc) * kUTileSize + (4 * kk + lg - 16 * rt) * kUTilePitch + li], y[j], 0, 0, 0);
+    }
+  }
+}
+
+// The three block steps on fp64 MFMA (v_mfma_f64_16x16x4_f64), each
+// workgroup over up to kQrGroupBlocks blocks of 64 rows of one matrix:
+//   MODE 0: partial Gram of A;
+//   MODE 1: Q1 = A U1, the candidate P from Q1; partial Gram of Q1;
+//   MODE 2: Q1 = A U1 as in MODE 1, P = bf16(fp32(scale * Q1 U2)).
+// Operands come straight from the staged rows. A 16 x 16 x 4 product takes,
+// in lane l, A[l % 16][l / 16] and B[l / 16][l % 16] and returns
+// D[4 i + l / 16][l % 16] in its register i = 0..3 (rows interleaved over the
+// lane groups; measured with a probe). In a multiply, wave w owns row tile
+// w % 4 of the block (64 rows, four tiles of 16) and the column tiles of
+// parity w / 4. A Gram is symmetric and only its upper triangle is summed
+// later, so only the 16 x 16 tiles (ti, tj) with ti <= tj are formed,
+// numbered row by row, tile t by wave t % 8; each wave keeps its tiles' sums
+// in registers across the workgroup's blocks. U is upper triangular: only its
+// tiles on and above the diagonal are staged (tile (rt, tc), rt <= tc, at
+// slot tc (tc + 1) / 2 + rt), which is what lets r = 128 stage U beside the
+// rows, and the multiply skips the zero tiles.
 template <int R, int MODE>
-__global__ __launch_bounds__(256) void qr_block_mfma_kernel(QrBatch b) {
+__global__ __launch_bounds__(kQrThreads) void qr_block_mfma_kernel(QrBatch b) {
   static_assert(R <= 128 && R % 16 == 0, "r <= 128, multiple of 16");
   constexpr int BR = kQrBlockRows;
-  static_assert(BR == 64, "four row tiles, one per wave");
-  constexpr int NT = R / 16;
-  constexpr int LD = R + 1;             // padded row pitch (doubles)
-  __shared__ double rows[BR][LD];
+  static_assert(BR == 64 && kQrWaves == 8, "four row tiles, two waves each");
+  constexpr int NT = R / 16, NY = (NT + 1) / 2;
+  constexpr int LG = qr_gram_pitch(R);            // row pitch of a block the Gram reads
+  constexpr int LM = qr_mul_pitch(R);             // row pitch of a block a multiply reads
+  constexpr int LA = MODE == 0 ? LG : LM;         // the pitch A is staged at
+  constexpr int NTT = NT * (NT + 1) / 2;          // upper-triangle Gram tiles
+  constexpr int PW = (NTT + kQrWaves - 1) / kQrWaves;  // Gram tiles per wave (at most)
+  constexpr int NS = BR * R / kQrThreads;         // staged doubles per thread and block
+  __shared__ double rows[BR * (LG > LM ? LG : LM)];
   __shared__ double u[MODE == 0 ? 1 : NT * (NT + 1) / 2 * kUTileSize];
   const int m = batch_item(b.block_begin, b.n, blockIdx.x);
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int li = lane & 15, lg = lane >> 4;
+  const int wr = wave % 4, wh = wave / 4;  // multiply: row tile and column-tile parity
   const int64_t k = b.k[m];
-  const int64_t rbeg = (int64_t)(blockIdx.x - b.block_begin[m]) * BR;
-  const int64_t rend = rbeg + BR < k ? rbeg + BR : k;
+  const int64_t gbeg = (int64_t)(blockIdx.x - b.block_begin[m]) * qr_group_rows(R);
+  const int64_t gend = gbeg + qr_group_rows(R) < k ? gbeg + qr_group_rows(R) : k;
   if constexpr (MODE == 2) {
     if (b.status[m][2] != 0u) return;  // P from the first pass is final
   }
-  const double* src = MODE == 2 ? b.Q1[m] : b.A[m];
-  if constexpr (MODE == 0) {
-    // The Gaussian rows are drawn here (four columns per Philox call) into
-    // LDS and into A for the first multiply.
-    constexpr int NQ = BR * (R / 4) / 256;
+  const double* __restrict__ A = b.A[m];
+  const double scale = b.scale[m];
+
+  int gti[PW], gtj[PW];
+  f64x4_t acc[PW];
 #pragma unroll
-    for (int e = 0; e < NQ; ++e) {
-      const int t = threadIdx.x + 256 * e;
-      const int lr = t / (R / 4), q = t % (R / 4);
-      const int64_t row = rbeg + lr;
-      double z[4] = {0.0, 0.0, 0.0, 0.0};
-      if (row < rend) {
-        gaussian4(b.seed[m], row, q, z);
-        double* dst = b.A[m] + row * R + 4 * q;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) dst[x] = z[x];
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x) rows[lr][4 * q + x] = z[x];
-    }
-  } else {
-    // every load issued before the first LDS store; rows past the end read
-    // a valid row and are zeroed
-    constexpr int NS = BR * R / 256, NU = MODE == 0 ? 0 : R * R / 256;
-    double sv[NS], uv[NU > 0 ? NU : 1];
+  for (int sl = 0; sl < PW; ++sl) {
+    gti[sl] = -1;
+    gtj[sl] = 0;
+    if (wave + kQrWaves * sl < NTT) gram_tile(wave + kQrWaves * sl, NT, gti[sl], gtj[sl]);
+    acc[sl] = f64x4_t{0.0, 0.0, 0.0, 0.0};
+  }
+  // The rows of A of a block are loaded into registers one block ahead:
+  // every load of the next block is issued before the current block's
+  // products, and stored to LDS when those are done. Rows past the end read a
+  // valid row and are zeroed.
+  // A block's rows are contiguous in A: thread element e is flat element
+  // threadIdx.x + kQrThreads e of the block, clamped to the last valid one.
+  const int q0 = (int)threadIdx.x / R, c0 = (int)threadIdx.x % R;
+  double sv[NS];
+  {
+    const double* blk = A + gbeg * R;
+    const int lim = (int)((gbeg + BR < gend ? gbeg + BR : gend) - gbeg) * R;
 #pragma unroll
     for (int e = 0; e < NS; ++e) {
-      const int t = threadIdx.x + 256 * e;
-      const int64_t row = rbeg + t / R;
-      sv[e] = src[(row < rend ? row : rend - 1) * R + t % R];
-    }
-    if constexpr (MODE != 0) {
-      const double* U = MODE == 1 ? b.U1[m] : b.U2[m];
-#pragma unroll
-      for (int e = 0; e < NU; ++e) uv[e] = U[threadIdx.x + 256 * e];
-    }
-#pragma unroll
-    for (int e = 0; e < NS; ++e) {
-      const int t = threadIdx.x + 256 * e;
-      rows[t / R][t % R] = rbeg + t / R < rend ? sv[e] : 0.0;
-    }
-    if constexpr (MODE != 0) {
-#pragma unroll
-      for (int e = 0; e < NU; ++e) {
-        const int t = threadIdx.x + 256 * e;
-        const int a = t / R, c = t % R;
-        if (a / 16 <= c / 16) u[utile_slot(a / 16, c / 16) * kUTileSize + (a % 16) * kUTilePitch + c % 16] = uv[e];
-      }
+      const int f = (int)threadIdx.x + kQrThreads * e;
+      sv[e] = blk[f < lim ? f : lim - 1];
     }
   }
-  __syncthreads();
-  if constexpr (MODE != 0) {
-    // Y = rows U: row tile `wave`, all column tiles
-    f64x4_t y[NT];
+  if constexpr (MODE == 1) qr_stage_u<R>(u, b.U1[m]);
+
+  for (int64_t rbeg = gbeg; rbeg < gend; rbeg += BR) {
+    const int64_t rend = rbeg + BR < gend ? rbeg + BR : gend;
+    qr_lds_barrier();  // the previous block's readers of rows (and u) are done
+    if constexpr (MODE == 2) qr_stage_u<R>(u, b.U1[m]);
+    {
+      const int lim = (int)(rend - rbeg) * R;
 #pragma unroll
-    for (int tc = 0; tc < NT; ++tc) y[tc] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int kk = 0; kk < R / 4; ++kk) {
-      const double a = rows[16 * wave + li][4 * kk + lg];
-      const int rt = kk / 4;  // U's row tile; tiles left of the diagonal are zero
-#pragma unroll
-      for (int tc = 0; tc < NT; ++tc)
-        if (tc >= rt)
-          y[tc] = __builtin_amdgcn_mfma_f64_16x16x4f64(
-              a, u[utile_slot(rt, tc) * kUTileSize + (4 * kk + lg - 16 * rt) * kUTilePitch + li], y[tc], 0, 0, 0);
-    }
-    const double scale = b.scale[m];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int lr = 16 * wave + 4 * i + lg;
-      const int64_t row = rbeg + lr;
-      if (row >= rend) continue;
-#pragma unroll
-      for (int tc = 0; tc < NT; ++tc) {
-        const int col = 16 * tc + li;
-        if constexpr (MODE == 1) b.Q1[m][row * R + col] = y[tc][i];
-        b.P[m][row * R + col] = (uint16_t)f32_to_bf16_rne((float)(scale * y[tc][i]));
+      for (int e = 0; e < NS; ++e) {
+        int lr, c;
+        qr_flat_split<R>(q0, c0, e, lr, c);
+        rows[lr * LA + c] = (int)threadIdx.x + kQrThreads * e < lim ? sv[e] : 0.0;
       }
     }
-    if constexpr (MODE == 2) return;
-    __syncthreads();  // every wave is done reading the staged rows
+    if (rbeg + BR < gend) {
+      const int64_t nbeg = rbeg + BR, nend = nbeg + BR < gend ? nbeg + BR : gend;
+      const double* blk = A + nbeg * R;
+      const int lim = (int)(nend - nbeg) * R;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int tc = 0; tc < NT; ++tc) rows[16 * wave + 4 * i + lg][16 * tc + li] = y[tc][i];  // 0 past the end
-    __syncthreads();
-  }
-  // partial Gram of the staged rows: row tiles wave, wave + 4, all column tiles
-#pragma unroll
-  for (int pass = 0; pass < (NT + 3) / 4; ++pass) {
-    const int ti = wave + 4 * pass;
-    if (ti >= NT) break;
-    f64x4_t acc[NT];
-#pragma unroll
-    for (int tj = 0; tj < NT; ++tj) acc[tj] = f64x4_t{0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-    for (int kk = 0; kk < BR / 4; ++kk) {
-      const double a = rows[4 * kk + lg][16 * ti + li];
-#pragma unroll
-      for (int tj = 0; tj < NT; ++tj)
-        acc[tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, rows[4 * kk + lg][16 * tj + li], acc[tj], 0, 0, 0);
+      for (int e = 0; e < NS; ++e) {
+        const int f = (int)threadIdx.x + kQrThreads * e;
+        sv[e] = blk[f < lim ? f : lim - 1];
+      }
     }
+    qr_lds_barrier();
+    if constexpr (MODE != 0) {
+      // Q1 rows = A rows U1: row tile wr, the column tiles of parity wh
+      f64x4_t y[NY];
+      if (wh == 0)
+        qr_multiply<R, 0>(rows, u, wr, li, lg, y);
+      else
+        qr_multiply<R, 1>(rows, u, wr, li, lg, y);
+      if constexpr (MODE == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t row = rbeg + 16 * wr + 4 * i + lg;
+          if (row >= rend) continue;
+#pragma unroll
+          for (int j = 0; j < NY; ++j) {
+            const int tc = 2 * j + wh;
+            if (tc < NT) b.P[m][row * R + 16 * tc + li] = (uint16_t)f32_to_bf16_rne((float)(scale * y[j][i]));
+          }
+        }
+      }
+      qr_lds_barrier();  // every wave is done reading the staged rows (and U1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NY; ++j) {  // 0 past the end; MODE 2 multiplies it again, MODE 1 takes its Gram
+          const int tc = 2 * j + wh;
+          if (tc < NT) rows[(16 * wr + 4 * i + lg) * (MODE == 2 ? LM : LG) + 16 * tc + li] = y[j][i];
+        }
+      if constexpr (MODE == 2) qr_stage_u<R>(u, b.U2[m]);
+      qr_lds_barrier();
+      if constexpr (MODE == 2) {
+        // P rows = scale * Q1 rows U2
+        if (wh == 0)
+          qr_multiply<R, 0>(rows, u, wr, li, lg, y);
+        else
+          qr_multiply<R, 1>(rows, u, wr, li, lg, y);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t row = rbeg + 16 * wr + 4 * i + lg;
+          if (row >= rend) continue;
+#pragma unroll
+          for (int j = 0; j < NY; ++j) {
+            const int tc = 2 * j + wh;
+            if (tc < NT) b.P[m][row * R + 16 * tc + li] = (uint16_t)f32_to_bf16_rne((float)(scale * y[j][i]));
+          }
+        }
+      }
+    }
+    if constexpr (MODE != 2) {
+      // the block's rows into this wave's upper-triangle Gram tiles
+#pragma unroll 4
+      for (int kk = 0; kk < BR / 4; ++kk)
+#pragma unroll
+        for (int sl = 0; sl < PW; ++sl)
+          if (gti[sl] >= 0)
+            acc[sl] = __builtin_amdgcn_mfma_f64_16x16x4f64(rows[(4 * kk + lg) * LG + 16 * gti[sl] + li],
+                                                           rows[(4 * kk + lg) * LG + 16 * gtj[sl] + li], acc[sl], 0,
+                                                           0, 0);
+    }
+  }
+  if constexpr (MODE != 2) {
     double* out = b.part[m] + (int64_t)(blockIdx.x - b.block_begin[m]) * R * R;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int sl = 0; sl < PW; ++sl) {
+      if (gti[sl] < 0) continue;
 #pragma unroll
-      for (int tj = 0; tj < NT; ++tj) out[(16 * ti + 4 * i + lg) * R + 16 * tj + li] = acc[tj][i];
+      for (int i = 0; i < 4; ++i) out[(16 * gti[sl] + 4 * i + lg) * R + 16 * gtj[sl] + li] = acc[sl][i];
+    }
   }
 }
 
@@ -506,7 +677,7 @@ struct QrItemLayout {
 
 QrItemLayout qr_item_layout(int64_t k, int64_t r) {
   QrItemLayout l;
-  l.blocks = (int)((k + kQrBlockRows - 1) / kQrBlockRows);
+  l.blocks = (int)((k + qr_group_rows(r) - 1) / qr_group_rows(r));  // workgroups of a block step
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -514,7 +685,7 @@ QrItemLayout qr_item_layout(int64_t k, int64_t r) {
     return at;
   };
   l.a = take((size_t)k * r * sizeof(double));
-  l.q1 = take((size_t)k * r * sizeof(double));
+  l.q1 = take(r < 16 ? (size_t)k * r * sizeof(double) : 0);  // the small-rank steps keep Q1
   l.part = take((size_t)l.blocks * r * r * sizeof(double));
   l.u1 = take((size_t)r * r * sizeof(double));
   l.u2 = take((size_t)r * r * sizeof(double));
@@ -556,8 +727,14 @@ rgc_status_t qr_launch(int n, const uint64_t* seeds, const int64_t* ks, uint16_t
     if constexpr (R < 16)
       hipLaunchKernelGGL((qr_block_small_kernel<R, MODE>), blocks, dim3(64), 0, s, b);
     else
-      hipLaunchKernelGGL((qr_block_mfma_kernel<R, MODE>), blocks, dim3(256), 0, s, b);
+      hipLaunchKernelGGL((qr_block_mfma_kernel<R, MODE>), blocks, dim3(kQrThreads), 0, s, b);
   };
+  if constexpr (R >= 16) {
+    int64_t kmax = 0;
+    for (int m = 0; m < n; ++m) kmax = ks[m] > kmax ? ks[m] : kmax;
+    hipLaunchKernelGGL((qr_gauss_kernel<R>), dim3((unsigned)((kmax * (R / 4) + 255) / 256), (unsigned)n), dim3(256),
+                       0, s, b);
+  }
   block_step(IntC<0>{});
   hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
   hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(QrFactorShape<R>::THREADS), 0, s, b, G_all, 0);

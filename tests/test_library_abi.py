@@ -52,7 +52,11 @@ def test_status_strings(lib):
 def test_workspace_queries(lib):
     assert lib.rgc_sample_projection_workspace_size(0, 2048, 64) == 0
     qr = lib.rgc_sample_projection_workspace_size(1, 2048, 64)
-    assert qr >= 2 * 2048 * 64 * 8
+    # r >= 16: the Gaussian (k x r fp64), the summed Gram, one partial Gram per workgroup of 192 rows,
+    # U1, U2 and flags; Q1 is formed again where it is needed rather than stored
+    assert 2048 * 64 * 8 + (2048 + 191) // 192 * 64 * 64 * 8 + 3 * 64 * 64 * 8 <= qr < 2 * 2048 * 64 * 8
+    # r = 4, 8: one partial per 64-row block, and the Gaussian and Q1 kept (k x r fp64 each)
+    assert lib.rgc_sample_projection_workspace_size(1, 2048, 8) >= 2 * 2048 * 8 * 8 + 2048 // 64 * 8 * 8 * 8
     assert lib.rgc_sample_projection_workspace_size(1, 2048, 256) == 0  # QR limited to r <= 128
     assert lib.rgc_accumulate_workspace_size(4096, 2048, 64) >= 0
     small = lib.rgc_apply_workspace_size(2048, 2048, 64)  # per-workgroup norm partials + step scalars
