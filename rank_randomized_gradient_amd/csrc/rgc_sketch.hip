@@ -581,6 +581,30 @@ struct AccumulatePolicy {
   }
   __device__ void store(const AccTile<R>& res, int m, int64_t tile, bool full, int64_t slot, int wn, int rw, int g,
                         int li) const {
+    if (!full && ab.add_part) {
+      // A deferred accumulation: this slot already holds the earlier calls'
+      // sums of the same segment (the same schedule every call). A load waits
+      // for every older memory operation of the wave, the copies in flight
+      // included, so the slot is read one N-tile (MT loads) at a time and each
+      // wait covers MT loads rather than one.
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int64_t row = 64 * wn + 16 * nt + li;  // tile-relative d
+        float* p = ab.part + slot * Sh::TILE * R + row * R + rw * Sh::RW + 4 * g;
+        float4 o[Sh::MT];
+#pragma unroll
+        for (int mt = 0; mt < Sh::MT; ++mt)
+          if (!(R != RM && rw * Sh::RW + 16 * mt >= RM)) o[mt] = *reinterpret_cast<const float4*>(p + 16 * mt);
+#pragma unroll
+        for (int mt = 0; mt < Sh::MT; ++mt) {
+          if (R != RM && rw * Sh::RW + 16 * mt >= RM) continue;  // padding block
+          const f32x4_t v = res[mt][nt];
+          *reinterpret_cast<float4*>(p + 16 * mt) =
+              make_float4(o[mt].x + v[0], o[mt].y + v[1], o[mt].z + v[2], o[mt].w + v[3]);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int64_t row = 64 * wn + 16 * nt + li;  // tile-relative d
@@ -599,14 +623,7 @@ struct AccumulatePolicy {
           }
         } else {
           float* p = ab.part + slot * Sh::TILE * R + row * R + rcol;
-          if (ab.add_part) {
-            // a deferred accumulation: this slot already holds the earlier
-            // calls' sums of the same segment (the same schedule every call)
-            const float4 o = *reinterpret_cast<const float4*>(p);
-            *reinterpret_cast<float4*>(p) = make_float4(o.x + v[0], o.y + v[1], o.z + v[2], o.w + v[3]);
-          } else {
-            *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-          }
+          *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
         }
       }
     }
