@@ -93,12 +93,13 @@ def parse():
                          "W read once per apply); streamed from W once before the warm-up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
-    ap.add_argument("--probe", choices=["shared-x", "linear"], default=None,
+    ap.add_argument("--probe", choices=["shared-x", "linear", "sample"], default=None,
                     help="instead of the step: shared-x times rgc_project_shared against rgc_project_batch for the "
                          "workload's matrices that read one X; linear times the layer products with the sketch "
                          "attached (rgc_linear_forward / rgc_linear_backward) against torch's GEMM plus the "
                          "separate sketch call, per matrix of one layer (--steps calls each; with --steps 1, one "
-                         "call each for counter runs); either prints one JSON line")
+                         "call each for counter runs); sample times one layer's projection sampling "
+                         "(rgc_sample_projections) back to back; each prints one JSON line")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB three times (a plain copy kernel of "
                          "known size, for calibrating the profiler's HBM byte counters)")
@@ -311,6 +312,9 @@ def main():
         return
     if args.probe == "shared-x":
         probe_shared_x(args, wl, rgc, torch, dev)
+        return
+    if args.probe == "sample":
+        probe_sample(args, wl, rgc, torch, dev)
         return
     cfg, r, T, mb, L = wl["cfg"], wl["r"], wl["tokens"], wl["microbatch"], wl["layers"]
     n_mb = T // mb
@@ -667,6 +671,30 @@ def probe_shared_x(args, wl, rgc, torch, dev):
         src_t = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
         torch.empty_like(src_t).copy_(src_t)
         torch.cuda.synchronize()
+    print(json.dumps(out), flush=True)
+
+
+def probe_sample(args, wl, rgc, torch, dev):
+    """The projection sampling of one layer of the workload alone: one
+    rgc_sample_projections call over the layer's matrices (the QR chain, or
+    the Rademacher draw), --steps calls back to back with fresh seeds, timed
+    with a HIP event pair; under rocprofv3 it gives the chain's kernel split."""
+    r, mats = wl["r"], wl["matrices"]
+    kind = "qr" if wl["kind"] == "qr" else "rademacher"
+    ps = [torch.empty((k, r), dtype=torch.bfloat16, device=dev) for _, _, k, _ in mats]
+    ws = rgc.Workspace(dev)
+    for i in range(3):
+        rgc.rgc_sample_projections(kind, [i * len(mats) + m for m in range(len(mats))], ps, workspace=ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(args.steps):
+        rgc.rgc_sample_projections(kind, [((i + 3) << 8) + m for m in range(len(mats))], ps, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    out = {"probe": "sample", "workload": wl["desc"], "kind": kind, "r": r, "matrices": len(mats),
+           "ks": [k for _, _, k, _ in mats], "calls": args.steps,
+           "us_per_call": round(a.elapsed_time(b) * 1e3 / args.steps, 2)}
     print(json.dumps(out), flush=True)
 
 
