@@ -668,6 +668,212 @@ __global__ __launch_bounds__(QrFactorShape<R>::THREADS) void qr_factor_kernel(Qr
     }
 }
 
+// Blocked U = chol(G)^-1 for R = 16 NT (ranks 16 .. 128), one workgroup of
+// four waves per matrix, the upper 16 x 16 tiles of G in LDS. With G = R^T R
+// (R upper triangular) and V_pp = R_pp^-1, for each block step p:
+//   diagonal  V_pp = chol(G_pp)^-1 of the current (Schur-complemented) G_pp,
+//             one wave, by eliminating [G_pp | I] as the unblocked factor
+//             does (lane (g, i): column i, rows g + 4 t);
+//   panel     R_pq = V_pp^T G_pq for q > p (fp64 MFMA);
+//   update    G_qq' -= R_pq^T R_pq' for p < q <= q' (fp64 MFMA).
+// Then U = R^-1 by block columns, each within one wave: U_qq = V_qq and
+// U_pq = -V_pp sum_{p < s <= q} R_ps U_sq for p = q - 1 .. 0, the U tiles
+// kept in registers in the MFMA result layout, which is also the layout of
+// a B operand. Only the diagonal steps are serial (16 pivots of one wave each);
+// the rest is 16 x 16 x 16 products. A pivot that is not positive and finite
+// makes the whole U NaN, as in the unblocked factor.
+constexpr int kFacPitch = 18;  // doubles per row of an LDS tile (reads of 16 rows x 4 columns hit distinct banks)
+constexpr int kFacTile = 16 * kFacPitch;
+
+template <int R>
+__global__ __launch_bounds__(256) void qr_factor_blocked_kernel(QrBatch b, const double* __restrict__ G_all,
+                                                                int second) {
+  static_assert(R % 16 == 0 && R <= 128, "tiled ranks");
+  constexpr int NT = R / 16, NTT = NT * (NT + 1) / 2;
+  __shared__ double gt[NTT * kFacTile];  // upper tiles of G, then of R
+  __shared__ double vt[NT * kFacTile];   // V_pp per diagonal block
+  __shared__ double yt[kFacTile];        // a diagonal step's L^-1, read transposed
+  __shared__ double dd[16];              // a diagonal step's pivots
+  __shared__ int fail_s;
+  const int m = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const int li = lane & 15, lg = lane >> 4;
+  double* U = second ? b.U2[m] : b.U1[m];
+  const double* G = G_all + (int64_t)m * R * R;
+
+  constexpr int NE = R * R / 256;  // elements of G per thread (element tid + 256 e)
+  if (second) {
+    // G2 = I + E (see the unblocked factor): U2 = I - S when every |E| < 1e-7.
+    // Every load is issued before the first is used.
+    double gv[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) gv[e] = G[tid + 256 * e];
+    bool far = false, above_final = false;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const int l = (tid + 256 * e) / R, c = (tid + 256 * e) % R;
+      if (c < l) continue;
+      const double err = fabs(gv[e] - (c == l ? 1.0 : 0.0));
+      far = far || !(err < 1e-7);
+      above_final = above_final || !(err < kQrFinalTol);
+    }
+    const bool keep_first = !__syncthreads_or(above_final);
+    if (!__syncthreads_or(far)) {
+      if (tid == 0) {
+        b.status[m][1] = 0u;
+        b.status[m][2] = keep_first ? 1u : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const int l = (tid + 256 * e) / R, c = (tid + 256 * e) % R;
+        const double a = gv[e];
+        U[tid + 256 * e] = c < l ? 0.0 : (c == l ? 1.0 - 0.5 * (a - 1.0) : -a);
+      }
+      return;
+    }
+  }
+
+  // the upper tiles of G (its lower triangle is not summed: diagonal tiles are
+  // mirrored), every load issued before the first LDS store
+  {
+    double gv[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const int l = (tid + 256 * e) / R, c = (tid + 256 * e) % R;
+      gv[e] = G[c >= l ? l * R + c : c * R + l];
+    }
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const int l = (tid + 256 * e) / R, c = (tid + 256 * e) % R;
+      if (l / 16 <= c / 16) gt[utile_slot(l / 16, c / 16) * kFacTile + (l % 16) * kFacPitch + c % 16] = gv[e];
+    }
+  }
+  if (tid == 0) fail_s = 0;
+  __syncthreads();
+
+  for (int p = 0; p < NT; ++p) {
+    if (wave == 0) {
+      // V_pp from the current G_pp: lane holds column li of rows lg + 4 t
+      double* tp = gt + utile_slot(p, p) * kFacTile;
+      double x[4], y[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        x[t] = tp[(lg + 4 * t) * kFacPitch + li];
+        y[t] = lg + 4 * t == li ? 1.0 : 0.0;
+      }
+      bool bad = false;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const double piv = __shfl(x[k / 4], 16 * (k % 4) + k);
+        bad = bad || !(piv > 0.0 && isfinite(piv));
+        const double inv = 1.0 / piv;
+        const double bk = __shfl(x[k / 4], 16 * (k % 4) + li);  // pivot row, column li
+        const double yk = __shfl(y[k / 4], 16 * (k % 4) + li);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const double bik = __shfl(x[t], 16 * lg + k);  // row lg + 4 t, pivot column
+          if (lg + 4 * t > k) {
+            const double f = bik * inv;
+            x[t] -= f * bk;
+            y[t] -= f * yk;
+          }
+        }
+      }
+      // V = L^-T D^-1/2: V[i][j] = L^-1[j][i] / sqrt(D_j) for i <= j
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        yt[(lg + 4 * t) * kFacPitch + li] = y[t];
+        if (lg + 4 * t == li) dd[li] = x[t];
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+      double* vp = vt + p * kFacTile;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int i = lg + 4 * t;
+        vp[i * kFacPitch + li] = i <= li ? yt[li * kFacPitch + i] / sqrt(dd[li]) : 0.0;
+      }
+      if (bad && lane == 0) fail_s = 1;
+    }
+    __syncthreads();
+    // panel: R_pq = V_pp^T G_pq, tile q by wave (q - p - 1) % 4
+    for (int q = p + 1 + wave; q < NT; q += 4) {
+      double* tq = gt + utile_slot(p, q) * kFacTile;
+      const double* vp = vt + p * kFacTile;
+      f64x4_t acc = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(vp[(4 * kk + lg) * kFacPitch + li],
+                                                    tq[(4 * kk + lg) * kFacPitch + li], acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tq[(4 * i + lg) * kFacPitch + li] = acc[i];
+    }
+    __syncthreads();
+    // update: G_qq' -= R_pq^T R_pq' over the upper tiles of the trailing block
+    const int nt2 = NT - p - 1;
+    for (int t = wave; t < nt2 * (nt2 + 1) / 2; t += 4) {
+      int a_, b_;
+      gram_tile(t, nt2, a_, b_);
+      const int q = p + 1 + a_, q2 = p + 1 + b_;
+      double* tc = gt + utile_slot(q, q2) * kFacTile;
+      const double* ra = gt + utile_slot(p, q) * kFacTile;
+      const double* rb = gt + utile_slot(p, q2) * kFacTile;
+      f64x4_t acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = tc[(4 * i + lg) * kFacPitch + li];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(-ra[(4 * kk + lg) * kFacPitch + li],
+                                                    rb[(4 * kk + lg) * kFacPitch + li], acc, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tc[(4 * i + lg) * kFacPitch + li] = acc[i];
+    }
+    __syncthreads();
+  }
+
+  if (fail_s) {
+    const double nan = __builtin_nan("");
+    for (int e = tid; e < R * R; e += 256) U[e] = nan;
+    if (tid == 0) {
+      b.status[m][second] = 1u;
+      if (second) b.status[m][2] = 0u;
+    }
+    return;
+  }
+  if (tid == 0) {
+    b.status[m][second] = 0u;
+    if (second) b.status[m][2] = 0u;
+  }
+  // U by block columns: column q by wave q % 4
+  static_for<0, NT>([&](auto qc) {
+    constexpr int q = decltype(qc)::value;
+    if (q % 4 != wave) return;
+    f64x4_t ures[q + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ures[q][i] = vt[q * kFacTile + (4 * i + lg) * kFacPitch + li];
+    static_for<0, q>([&](auto pc) {
+      constexpr int p = q - 1 - decltype(pc)::value;
+      f64x4_t sacc = f64x4_t{0.0, 0.0, 0.0, 0.0};
+      static_for<p + 1, q + 1>([&](auto sc) {
+        constexpr int s2 = decltype(sc)::value;
+        const double* rp = gt + utile_slot(p, s2) * kFacTile;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          sacc = __builtin_amdgcn_mfma_f64_16x16x4f64(rp[li * kFacPitch + 4 * kk + lg], ures[s2][kk], sacc, 0, 0, 0);
+      });
+      f64x4_t r = f64x4_t{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        r = __builtin_amdgcn_mfma_f64_16x16x4f64(-vt[p * kFacTile + li * kFacPitch + 4 * kk + lg], sacc[kk], r, 0, 0,
+                                                 0);
+      ures[p] = r;
+    });
+#pragma unroll
+    for (int p = 0; p < NT; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) U[(16 * p + 4 * i + lg) * R + 16 * q + li] = p <= q ? ures[p <= q ? p : q][i] : 0.0;
+  });
+}
+
 namespace {
 
 struct QrItemLayout {
@@ -735,12 +941,18 @@ rgc_status_t qr_launch(int n, const uint64_t* seeds, const int64_t* ks, uint16_t
     hipLaunchKernelGGL((qr_gauss_kernel<R>), dim3((unsigned)((kmax * (R / 4) + 255) / 256), (unsigned)n), dim3(256),
                        0, s, b);
   }
+  auto factor = [&](int second) {
+    if constexpr (R < 16)
+      hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(QrFactorShape<R>::THREADS), 0, s, b, G_all, second);
+    else
+      hipLaunchKernelGGL((qr_factor_blocked_kernel<R>), dim3(n), dim3(256), 0, s, b, G_all, second);
+  };
   block_step(IntC<0>{});
   hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
-  hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(QrFactorShape<R>::THREADS), 0, s, b, G_all, 0);
+  factor(0);
   block_step(IntC<1>{});
   hipLaunchKernelGGL((qr_gram_reduce_kernel<R>), red_grid, dim3(256), 0, s, b, G_all);
-  hipLaunchKernelGGL((qr_factor_kernel<R>), dim3(n), dim3(QrFactorShape<R>::THREADS), 0, s, b, G_all, 1);
+  factor(1);
   block_step(IntC<2>{});
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
