@@ -118,6 +118,17 @@ __device__ __forceinline__ int64_t partial_slot(int64_t w, bool first_segment) {
   return 2 * w + (first_segment ? 0 : 1);
 }
 
+// Layout of a partial slot (TILE x R fp32 of one segment) in store order: the
+// float4 that lane l of wave w holds for N-tile nt and M-tile mt sits at
+// float4 position ((w 4 + nt) MT + mt) 64 + l, so that each store instruction
+// writes 1 KB contiguously (a row-major tile took 16 rows x 64 bytes each).
+// It holds tile row 64 wn + 16 nt + l % 16 and columns rw RW + 16 mt +
+// 4 (l / 16) .. +3, with wn = w % WN and rw = w / WN.
+template <int MT>
+__host__ __device__ __forceinline__ int64_t slot_pos4(int w, int nt, int mt, int l) {
+  return ((int64_t)(w * 4 + nt) * MT + mt) * 64 + l;
+}
+
 // ---------------------------------------------------------------------------
 // Stage geometry and the pipeline shared by both contractions.
 //
@@ -505,8 +516,9 @@ struct ProjectPolicy {
                 make_uint2(pack_bf16x2(f32_to_bf16_rne(v[0]), f32_to_bf16_rne(v[1])),
                            pack_bf16x2(f32_to_bf16_rne(v[2]), f32_to_bf16_rne(v[3])));
         } else {
-          float* p = pb.part + slot * Sh::TILE * R + row * R + rcol;
-          *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+          reinterpret_cast<float4*>(pb.part + slot * Sh::TILE * R)[slot_pos4<Sh::MT>(rw * Sh::WN + wn, nt, mt,
+                                                                                     16 * g + li)] =
+              make_float4(v[0], v[1], v[2], v[3]);
         }
       }
     }
@@ -589,18 +601,17 @@ struct AccumulatePolicy {
       // wait covers MT loads rather than one.
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const int64_t row = 64 * wn + 16 * nt + li;  // tile-relative d
-        float* p = ab.part + slot * Sh::TILE * R + row * R + rw * Sh::RW + 4 * g;
+        float4* p = reinterpret_cast<float4*>(ab.part + slot * Sh::TILE * R) +
+                    slot_pos4<Sh::MT>(rw * Sh::WN + wn, nt, 0, 16 * g + li);
         float4 o[Sh::MT];
 #pragma unroll
         for (int mt = 0; mt < Sh::MT; ++mt)
-          if (!(R != RM && rw * Sh::RW + 16 * mt >= RM)) o[mt] = *reinterpret_cast<const float4*>(p + 16 * mt);
+          if (!(R != RM && rw * Sh::RW + 16 * mt >= RM)) o[mt] = p[64 * mt];
 #pragma unroll
         for (int mt = 0; mt < Sh::MT; ++mt) {
           if (R != RM && rw * Sh::RW + 16 * mt >= RM) continue;  // padding block
           const f32x4_t v = res[mt][nt];
-          *reinterpret_cast<float4*>(p + 16 * mt) =
-              make_float4(o[mt].x + v[0], o[mt].y + v[1], o[mt].z + v[2], o[mt].w + v[3]);
+          p[64 * mt] = make_float4(o[mt].x + v[0], o[mt].y + v[1], o[mt].z + v[2], o[mt].w + v[3]);
         }
       }
       return;
@@ -622,8 +633,9 @@ struct AccumulatePolicy {
             for (int e = 0; e < 4; ++e) unsafeAtomicAdd(c + e, v[e]);
           }
         } else {
-          float* p = ab.part + slot * Sh::TILE * R + row * R + rcol;
-          *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+          reinterpret_cast<float4*>(ab.part + slot * Sh::TILE * R)[slot_pos4<Sh::MT>(rw * Sh::WN + wn, nt, mt,
+                                                                                     16 * g + li)] =
+              make_float4(v[0], v[1], v[2], v[3]);
         }
       }
     }
@@ -665,15 +677,21 @@ __global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
   const int64_t tn = s.tile_n;
   const int64_t left = s.next[m] - tile * tn;
   const int64_t rows = left < tn ? left : tn;
-  constexpr int PER = 4;  // floats per thread
-  constexpr int MAXP = 8;  // partial loads in flight at once
+  using Sh = StageShape<R, 1>;  // the slot layout depends on R only (slot_pos4)
+  constexpr int MAXP = 8;        // partial loads in flight at once
   {
-    const int64_t e = (int64_t)blockIdx.x * (256 * PER) + threadIdx.x * PER;
-    if (e >= rows * R) return;
-    const int col = (int)(e % R);
+    // one float4 of the slots per thread, at the same store-order position in each
+    const int64_t q4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q4 >= tn * R / 4) return;
+    const int lane = (int)(q4 % 64);
+    const int64_t wq = q4 / 64;
+    const int mt = (int)(wq % Sh::MT), nt = (int)(wq / Sh::MT % 4), wv = (int)(wq / Sh::MT / 4);
+    const int64_t row = 64 * (wv % Sh::WN) + 16 * nt + (lane & 15);
+    const int col = (wv / Sh::WN) * Sh::RW + 16 * mt + 4 * (lane >> 4);
+    if (row >= rows) return;
     if (R != RM * GM && col >= RM * GM) return;  // padding columns (a float4 never straddles a member)
     const int mi = col / RM;
-    const int64_t out = (tile * tn + e / R) * RM + col - mi * RM;
+    const int64_t out = (tile * tn + row) * RM + col - mi * RM;
     float4 old = make_float4(0.f, 0.f, 0.f, 0.f);
     if constexpr (!TO_BF16) old = *reinterpret_cast<const float4*>(fb.C[m] + out);
     f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
@@ -687,7 +705,7 @@ __global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
         // wa's share is its last segment when its range began in an earlier
         // tile, else its first; every later range begins inside this tile
         const bool first = !(w == wa && range_begin(s, wa) < ts);
-        v[i] = w <= wb ? *reinterpret_cast<const float4*>(fb.part + partial_slot(w, first) * tn * R + e)
+        v[i] = w <= wb ? reinterpret_cast<const float4*>(fb.part + partial_slot(w, first) * tn * R)[q4]
                        : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
