@@ -384,6 +384,13 @@ rgc_status_t rgc_linear_backward(const uint16_t* D, int64_t ldd, const uint16_t*
 rgc_status_t rgc_test_philox(uint64_t seed, int64_t n, const uint32_t* ctr, uint32_t* out,
                              void* stream);
 
+/* out[i] = bf16(v[i]) rounded to nearest even for i < n: the conversion every
+ * kernel uses where it rounds to bf16 without randomness (XP, Y, dX, P, the
+ * high part and remainder of C in the update); NaN gives a quiet NaN with the
+ * input's sign and upper payload bits ((bits >> 16) | 0x40). v: device fp32,
+ * out: device bf16, n elements each; 0 <= n <= 2^31 (else RGC_ERR_SHAPE). */
+rgc_status_t rgc_test_round_nearest(const float* v, uint16_t* out, int64_t n, void* stream);
+
 /* out[i][j] = SR(v[i][j]) with the rounding bits of weight element
  * (row0 + i, col0 + j) under `seed`: the same bits rgc_apply draws, rounded
  * here one element at a time (the update sweep rounds pairs and packs them

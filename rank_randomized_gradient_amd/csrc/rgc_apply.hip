@@ -57,17 +57,17 @@ constexpr int64_t kMaxApplyElems = int64_t(1) << 38;  // d * k (workgroup counts
 template <int R>
 struct ApplyTraits {
   static constexpr int KQ = (R + 31) / 32;              // K-steps of 32 over r
-  // 16-row N-tiles per wave: two (128-row tiles) except for 64 < r <= 128,
-  // whose 128-row stage would leave one workgroup per compute unit; at r >
-  // 128 that is the case anyway, and the taller tile halves the P rows
-  // re-read per W byte (measured on the Qwen3-1.7B-shaped block at r = 256:
-  // 253 -> 205 us)
-  static constexpr int NTW = R > 64 && R <= 128 ? 1 : 2;
+  // Update sweeps: tiles of 128 rows. Up to r = 128 eight waves of one
+  // 16-row N-tile each, so that two workgroups (four waves per SIMD) overlap
+  // the per-tile arithmetic with the copies; above, four waves of two N-tiles
+  // (the P stage leaves one workgroup per compute unit anyway). The 128-row
+  // tile halves the P rows re-read per W byte against 64 rows (measured on
+  // the Qwen3-1.7B-shaped block at r = 256: 253 -> 205 us).
+  static constexpr int WAVES = R <= 128 ? 8 : kApplyWaves;  // waves of an update workgroup
+  static constexpr int NTW = R <= 128 ? 1 : 2;
   static constexpr int RW = 16 * NTW;                   // rows per wave
-  static constexpr int ROWS = kApplyWaves * RW;         // rows per workgroup tile
-  static constexpr int RP = 32 * KQ + 8;                // LDS row pitch of the P tile (bf16)
-  static constexpr int PCHUNKS = kApplyCols * R / 8;    // 16-byte chunks of a P tile
-  static constexpr int PCPT = (PCHUNKS + 255) / 256;    // chunks per thread
+  static constexpr int ROWS = WAVES * RW;               // rows per workgroup tile
+  static constexpr int THREADS = 64 * WAVES;
 };
 
 struct ApplyItem {
@@ -197,11 +197,10 @@ __device__ __forceinline__ void load_row_operand(const float* __restrict__ C, in
       }
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const uint32_t h0 = f32_to_bf16_rne(v[2 * p]), h1 = f32_to_bf16_rne(v[2 * p + 1]);
-        const uint32_t l0 = f32_to_bf16_rne(v[2 * p] - bf16_bits_to_f32(h0));
-        const uint32_t l1 = f32_to_bf16_rne(v[2 * p + 1] - bf16_bits_to_f32(h1));
-        op.hi[nt][q][p] = pack_bf16x2(h0, h1);
-        op.lo[nt][q][p] = pack_bf16x2(l0, l1);
+        const uint32_t hv = f32x2_to_bf16x2_rne(v[2 * p], v[2 * p + 1]);
+        op.hi[nt][q][p] = hv;
+        op.lo[nt][q][p] = f32x2_to_bf16x2_rne(v[2 * p] - __uint_as_float(hv << 16),
+                                              v[2 * p + 1] - __uint_as_float(hv & 0xFFFF0000u));
       }
     }
   }
@@ -223,11 +222,12 @@ __device__ __forceinline__ void load_row_operand(const float* __restrict__ C, in
 // the 16-byte chunks of row jl rotated by f(jl) (bank spreading for the
 // A-operand reads, whose 16 lanes read 16 different rows).
 // ---------------------------------------------------------------------------
-// Two workgroups per compute unit with three stages each: the update's
-// per-tile arithmetic (the H rebuild on MFMA, Philox, rounding) is heavy
-// enough that a second workgroup's waves overlapping it pay more than deeper
-// staging (measured on the Qwen3-1.7B-shaped block). At r > 128 the P rows
-// make a stage too large for two, so one workgroup takes up to six.
+// Two workgroups per compute unit with up to three stages each (two at r >
+// 80, where a stage passes 26 KB): the update's per-tile arithmetic (the H
+// rebuild on MFMA, Philox, rounding) is heavy enough that other waves
+// overlapping it pay more than deeper staging (measured on the Qwen3-1.7B-
+// shaped block and the Qwen3-8B-shaped layer). At r > 128 the P rows make a
+// stage too large for two, so one workgroup takes up to six.
 
 template <int R, int MODE>
 struct ApplyShape {
@@ -242,8 +242,8 @@ struct ApplyShape {
   static constexpr int LDS_MAX = (PER_CU == 2 ? 79 : 159) * 1024;        // room for the norm reduction
   static constexpr int SMAX = PER_CU == 2 ? 3 : 6;
   static constexpr int S = SMAX * STAGE <= LDS_MAX ? SMAX : LDS_MAX / STAGE;
-  static constexpr int NV_LO = NI / 4, NV_HI = (NI + 3) / 4;
-  static_assert(S >= 3 && S * STAGE <= LDS_MAX, "LDS");
+  static constexpr int NV_LO = NI / Tr::WAVES, NV_HI = (NI + Tr::WAVES - 1) / Tr::WAVES;  // copies per wave
+  static_assert(S >= 2 && S * STAGE <= LDS_MAX, "LDS");
   static_assert((S - 1) * NV_HI <= 63, "vector memory counter");
 };
 
@@ -323,12 +323,12 @@ __device__ __forceinline__ int apply_logical_workgroup(int b, int G) {
 }
 
 template <int R, int MODE>
-__global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch b) {  // ApplyShape::PER_CU
+__global__ __launch_bounds__(ApplyTraits<R>::THREADS, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch b) {  // PER_CU
   using Tr = ApplyTraits<R>;
   using Sh = ApplyShape<R, MODE>;
   constexpr int S = Sh::S;
   __shared__ __attribute__((aligned(1024))) char smem[S * Sh::STAGE];
-  __shared__ double red[2][kApplyWaves];
+  __shared__ double red[Tr::WAVES];
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int n = lane & 15, g = lane >> 4;
   const int w = apply_logical_workgroup(blockIdx.x, gridDim.x);
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
   int rop_row = -1;  // first row of the loaded row operand
   const int d = (int)it.d, k = (int)it.k, ctiles = (int)it.ctiles;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(RGC_LDS char*)smem;
-  const bool more = wave < Sh::NI % 4;
+  const bool more = wave < Sh::NI % Tr::WAVES;
   // Tiles run in unit order, unit = row block * ctiles + column tile; the
   // copy cursor (lrb, lct) and the compute cursor (crb, cct) step through
   // (row block, column tile) without dividing.
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
   uint32_t voff[Sh::NV_HI];
 #pragma unroll
   for (int v = 0; v < Sh::NV_HI; ++v) {
-    const int c = wave + 4 * v;
+    const int c = wave + Tr::WAVES * v;
     if (c < Sh::WC) {
       const int t = lane >> 3;
       const int q = ((lane & 7) - (t >> 1) - 4 * (c & 1)) & 7;
@@ -396,10 +396,10 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
     const uint32_t st = lds0 + lslot * Sh::STAGE;
     static_for<0, Sh::NV_HI>([&](auto vc) {
       constexpr int v = decltype(vc)::value;
-      const int c = wave + 4 * v;  // a W copy if c < WC, a P copy if WC <= c < NI
-      if constexpr (4 * v + 3 < Sh::WC) {
+      const int c = wave + Tr::WAVES * v;  // a W copy if c < WC, a P copy if WC <= c < NI
+      if constexpr (Tr::WAVES * v + Tr::WAVES - 1 < Sh::WC) {
         dma_16b_stream(Wb, voff[v], st + 1024 * c);
-      } else if constexpr (4 * v >= Sh::WC && 4 * v + 3 < Sh::NI) {
+      } else if constexpr (Tr::WAVES * v >= Sh::WC && Tr::WAVES * v + Tr::WAVES - 1 < Sh::NI) {
         dma_16b_cached(Pb, voff[v], st + 1024 * c);
       } else {
         if (c < Sh::WC)
@@ -527,9 +527,13 @@ __global__ __launch_bounds__(256, R > 128 ? 1 : 2) void apply_kernel(ApplyBatch 
 
   if constexpr (MODE == kModeUpdateCarry) {
     sw = wave_sum(sw);
-    if (lane == 0) red[0][wave] = sw;
+    if (lane == 0) red[wave] = sw;
     __syncthreads();
-    if (threadIdx.x == 0) b.wpart[w] = ((red[0][0] + red[0][1]) + red[0][2]) + red[0][3];
+    if (threadIdx.x == 0) {
+      double t = red[0];
+      for (int v = 1; v < Tr::WAVES; ++v) t += red[v];  // waves in order
+      b.wpart[w] = t;
+    }
   }
 }
 
@@ -655,9 +659,9 @@ __device__ __forceinline__ void gram_step(const GramRows<N0 + N1>& rw,
     for (int a = 0; a < NL; ++a) {
       if constexpr (TWO_TERM) {
         const float v0 = __uint_as_float(rw.v[2 * p][a]), v1 = __uint_as_float(rw.v[2 * p + 1][a]);
-        const uint32_t h0 = f32_to_bf16_rne(v0), h1 = f32_to_bf16_rne(v1);
-        hi[a][p] = pack_bf16x2(h0, h1);
-        lo[a][p] = pack_bf16x2(f32_to_bf16_rne(v0 - bf16_bits_to_f32(h0)), f32_to_bf16_rne(v1 - bf16_bits_to_f32(h1)));
+        const uint32_t hv = f32x2_to_bf16x2_rne(v0, v1);
+        hi[a][p] = hv;
+        lo[a][p] = f32x2_to_bf16x2_rne(v0 - __uint_as_float(hv << 16), v1 - __uint_as_float(hv & 0xFFFF0000u));
       } else {
         hi[a][p] = pack_bf16x2(rw.v[2 * p][a], rw.v[2 * p + 1][a]);
         lo[a][p] = 0u;
@@ -1125,7 +1129,8 @@ __global__ __launch_bounds__(256) void small_update_kernel(ApplyBatch b) {
 }
 
 // ---------------------------------------------------------------------------
-// Test hooks: the rounding stream and the Philox generator alone.
+// Test hooks: the rounding stream, the nearest-even conversion and the Philox
+// generator alone.
 // ---------------------------------------------------------------------------
 __global__ void stochastic_round_kernel(const float* __restrict__ v, uint16_t* __restrict__ out, int64_t rows,
                                         int64_t cols, int64_t ld, int64_t row0, int64_t col0, uint64_t seed) {
@@ -1138,6 +1143,11 @@ __global__ void stochastic_round_kernel(const float* __restrict__ v, uint16_t* _
   const uint32_t w = words[(J & 7) >> 1];
   const uint32_t r16 = (J & 1) ? (w >> 16) : (w & 0xFFFFu);
   out[i * ld + j] = (uint16_t)f32_to_bf16_sr(v[i * ld + j], r16);
+}
+
+__global__ void round_nearest_kernel(const float* __restrict__ v, uint16_t* __restrict__ out, int64_t n) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < n) out[idx] = (uint16_t)f32_to_bf16_rne(v[idx]);
 }
 
 __global__ void philox_kernel(uint64_t seed, int64_t n, const uint32_t* __restrict__ ctr, uint32_t* __restrict__ out) {
@@ -1153,21 +1163,27 @@ __global__ void philox_kernel(uint64_t seed, int64_t n, const uint32_t* __restri
 
 namespace {
 
-// Workgroups per matrix: one per kApplyUnitsPerWG tiles, a function of the
-// matrix's own shape only, so that a matrix gets the same partition (and so
-// the same norm sums and bits) alone or in any batch. Eight tiles of 128 x
-// 64 give the Qwen3-1.7B-shaped block 768 workgroups (two resident per
-// compute unit); measured faster than 4, 6, 10, 16 or 24 tiles.
+// Workgroups per matrix: one per 8 tiles, or per 16 tiles for a matrix of
+// at least 2048 tiles, a function of the matrix's own shape only, so that a
+// matrix gets the same partition (and so the same norm sums and bits) alone
+// or in any batch. Each workgroup loads and splits its C rows once per row
+// block it enters, so larger matrices take longer runs: on the Qwen3-8B-
+// shaped layer at r = 128 (2048-6144 tiles of 128 x 64 per matrix) 16 tiles
+// measured 330 -> 316 us against 8 (32: 315 us); the Qwen3-1.7B-shaped block
+// (512-1536 tiles per matrix at r = 64) is fastest with 8 (76 us; 16: 79 us,
+// 32: 85 us).
 constexpr int64_t kApplyUnitsPerWG = 8;
+constexpr int64_t kApplyUnitsPerWGLarge = 16;
+constexpr int64_t kApplyLargeUnits = 2048;
 
 template <int R>
 void apply_plan(ApplyBatch& b, int n, const int64_t* ds, const int64_t* ks) {
   using Tr = ApplyTraits<R>;
-  const int64_t per = kApplyUnitsPerWG;
   b.wbase[0] = 0;
   for (int m = 0; m < n; ++m) {
     b.it[m].ctiles = (ks[m] + kApplyCols - 1) / kApplyCols;
     b.it[m].units = (ds[m] + Tr::ROWS - 1) / Tr::ROWS * b.it[m].ctiles;
+    const int64_t per = b.it[m].units >= kApplyLargeUnits ? kApplyUnitsPerWGLarge : kApplyUnitsPerWG;
     b.wbase[m + 1] = b.wbase[m] + (int)((b.it[m].units + per - 1) / per);
   }
   b.n = n;
@@ -1247,7 +1263,7 @@ rgc_status_t apply_launch(int n, uint16_t* const* Ws, const int64_t* ldws, const
   }
   const int G = b.wbase[n];
   if (alphas) {  // fixed scale: the update sweep alone, no workspace
-    hipLaunchKernelGGL((apply_kernel<R, kModeUpdate>), dim3((unsigned)G), dim3(256), 0, st, b);
+    hipLaunchKernelGGL((apply_kernel<R, kModeUpdate>), dim3((unsigned)G), dim3(ApplyTraits<R>::THREADS), 0, st, b);
     return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
   }
   const ApplyWorkspace l = apply_ws_layout<R>(b);
@@ -1261,10 +1277,11 @@ rgc_status_t apply_launch(int n, uint16_t* const* Ws, const int64_t* ldws, const
   const int nw = carry == kCarryIn ? 0 : b.sbase[n];
   hipLaunchKernelGGL(gram_norms_kernel<R>, dim3((unsigned)(b.gbase[n] + nw)), dim3(256), 0, st, b);
   hipLaunchKernelGGL(gram_reduce_kernel<R>, dim3((unsigned)(n * GramShape<R>::NP)), dim3(256), 0, st, b);
+  constexpr unsigned T = ApplyTraits<R>::THREADS;
   if (carry == kCarryNone) {
-    hipLaunchKernelGGL((apply_kernel<R, kModeUpdate>), dim3((unsigned)G), dim3(256), 0, st, b);
+    hipLaunchKernelGGL((apply_kernel<R, kModeUpdate>), dim3((unsigned)G), dim3(T), 0, st, b);
   } else {
-    hipLaunchKernelGGL((apply_kernel<R, kModeUpdateCarry>), dim3((unsigned)G), dim3(256), 0, st, b);
+    hipLaunchKernelGGL((apply_kernel<R, kModeUpdateCarry>), dim3((unsigned)G), dim3(T), 0, st, b);
     hipLaunchKernelGGL(carry_norm_kernel, dim3((unsigned)n), dim3(256), 0, st, b);
   }
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
@@ -1376,7 +1393,8 @@ rgc_status_t reconstruct_launch(const float* C, const uint16_t* P, float* H, int
   b.it[0].d = d;
   b.it[0].k = k;
   b.H = H;
-  hipLaunchKernelGGL((apply_kernel<R, kModeReconstruct>), dim3((unsigned)b.wbase[1]), dim3(256), 0, st, b);
+  hipLaunchKernelGGL((apply_kernel<R, kModeReconstruct>), dim3((unsigned)b.wbase[1]), dim3(ApplyTraits<R>::THREADS), 0,
+                     st, b);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
@@ -1566,6 +1584,16 @@ extern "C" rgc_status_t rgc_test_stochastic_round(const float* v, uint16_t* out,
   const int64_t nel = rows * cols;
   hipLaunchKernelGGL(stochastic_round_kernel, dim3((unsigned)((nel + 255) / 256)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), v, out, rows, cols, ld, row0, col0, seed);
+  return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+}
+
+extern "C" rgc_status_t rgc_test_round_nearest(const float* v, uint16_t* out, int64_t n, void* stream) {
+  if (n < 0 || n > (int64_t(1) << 31)) return RGC_ERR_SHAPE;
+  if (n == 0) return RGC_OK;
+  if (!v || !out) return RGC_ERR_NULL;
+  if (!aligned_to(v, 4) || !aligned_to(out, 2)) return RGC_ERR_ALIGN;
+  hipLaunchKernelGGL(round_nearest_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), v, out, n);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 

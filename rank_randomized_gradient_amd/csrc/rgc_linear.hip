@@ -283,8 +283,8 @@ __device__ __forceinline__ void lin_tile(const uint16_t* __restrict__ A, int64_t
       if (row >= m_rem) continue;
       const f32x4_t v = accx[q][u];
       *reinterpret_cast<uint2*>(XP + row * R + 16 * (q == 0 ? sl0 : sl1) + 4 * g) =
-          make_uint2(pack_bf16x2(f32_to_bf16_rne(v[0]), f32_to_bf16_rne(v[1])),
-                     pack_bf16x2(f32_to_bf16_rne(v[2]), f32_to_bf16_rne(v[3])));
+          make_uint2(f32x2_to_bf16x2_rne(v[0], v[1]),
+                     f32x2_to_bf16x2_rne(v[2], v[3]));
     }
   }
 
@@ -299,8 +299,8 @@ __device__ __forceinline__ void lin_tile(const uint16_t* __restrict__ A, int64_t
       if (col >= n_rem) continue;  // n_rem is a multiple of 8: four columns are all in or all out
       const f32x4_t v = acc[mt][nt];
       *reinterpret_cast<uint2*>(O + row * ldo + col) =
-          make_uint2(pack_bf16x2(f32_to_bf16_rne(v[0]), f32_to_bf16_rne(v[1])),
-                     pack_bf16x2(f32_to_bf16_rne(v[2]), f32_to_bf16_rne(v[3])));
+          make_uint2(f32x2_to_bf16x2_rne(v[0], v[1]),
+                     f32x2_to_bf16x2_rne(v[2], v[3]));
     }
   }
 }

@@ -513,8 +513,8 @@ struct ProjectPolicy {
           const int mi = GM == 1 ? 0 : B / NRB_ITEM;
           if (t < pb.s.next[m])
             *reinterpret_cast<uint2*>(pb.XP[m][mi] + t * RM + rcol - mi * RM) =
-                make_uint2(pack_bf16x2(f32_to_bf16_rne(v[0]), f32_to_bf16_rne(v[1])),
-                           pack_bf16x2(f32_to_bf16_rne(v[2]), f32_to_bf16_rne(v[3])));
+                make_uint2(f32x2_to_bf16x2_rne(v[0], v[1]),
+                           f32x2_to_bf16x2_rne(v[2], v[3]));
         } else {
           reinterpret_cast<float4*>(pb.part + slot * Sh::TILE * R)[slot_pos4<Sh::MT>(rw * Sh::WN + wn, nt, mt,
                                                                                      16 * g + li)] =
@@ -716,8 +716,8 @@ __global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
       }
     }
     if constexpr (TO_BF16) {
-      const uint2 o = make_uint2(pack_bf16x2(f32_to_bf16_rne(sum[0]), f32_to_bf16_rne(sum[1])),
-                                 pack_bf16x2(f32_to_bf16_rne(sum[2]), f32_to_bf16_rne(sum[3])));
+      const uint2 o = make_uint2(f32x2_to_bf16x2_rne(sum[0], sum[1]),
+                                 f32x2_to_bf16x2_rne(sum[2], sum[3]));
       *reinterpret_cast<uint2*>(fb.XP[m][mi] + out) = o;
     } else {
       old.x += sum[0];
@@ -778,7 +778,7 @@ __global__ __launch_bounds__(256) void small_project_kernel(SmallProjectBatch b)
   if (lane == 0) {
     uint32_t o[R / 2];
 #pragma unroll
-    for (int i = 0; i < R / 2; ++i) o[i] = pack_bf16x2(f32_to_bf16_rne(acc[2 * i]), f32_to_bf16_rne(acc[2 * i + 1]));
+    for (int i = 0; i < R / 2; ++i) o[i] = f32x2_to_bf16x2_rne(acc[2 * i], acc[2 * i + 1]);
     uint16_t* dst = b.XP[m] + t * R;
     if constexpr (R == 4)
       *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);

@@ -97,6 +97,7 @@ SIGNATURES = {
                                            _vp]),
     "rgc_test_philox": (ctypes.c_int, [_u64, _i64, _vp, _vp, _vp]),
     "rgc_test_stochastic_round": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _u64, _vp]),
+    "rgc_test_round_nearest": (ctypes.c_int, [_vp, _vp, _i64, _vp]),
     "rgc_test_reconstruct": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "rgc_test_sketch_workspace_size": (_sz, [ctypes.c_int, _i64, _i64, ctypes.POINTER(_i64), _i64, _i64]),
     "rgc_project_shared_workspace_size": (_sz, [_i64, _i64, _i64, _i64]),
@@ -651,6 +652,15 @@ def rgc_test_stochastic_round(v: torch.Tensor, seed: int, row0: int = 0, col0: i
     out = torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)
     _check(lib.rgc_test_stochastic_round(v.data_ptr(), out.data_ptr(), rows, cols, cols, row0, col0,
                                          seed & 0xFFFFFFFFFFFFFFFF, _stream(dev)))
+    return out
+
+
+def rgc_test_round_nearest(v: torch.Tensor) -> torch.Tensor:
+    lib = load_library()
+    dev = _need_gpu(v)
+    _dense(v, torch.float32, "v")
+    out = torch.empty(v.shape, dtype=torch.bfloat16, device=dev)
+    _check(lib.rgc_test_round_nearest(v.data_ptr(), out.data_ptr(), v.numel(), _stream(dev)))
     return out
 
 

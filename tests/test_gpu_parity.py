@@ -84,6 +84,23 @@ def test_stochastic_round_bitexact(dev, rows, cols, row0, col0, seed):
     assert np.array_equal(bits(got), ref)
 
 
+def test_round_nearest_bitexact(dev):
+    """The kernels' nearest-even bf16 conversion (the conversion instruction)
+    against the oracle's integer definition: every sign, exponent and upper
+    mantissa (all 2^16 high halves) with the low halves that decide the
+    rounding (zero, just above zero, just below, at and just above the tie, all
+    ones), then 2^20 arbitrary bit patterns: NaNs with payloads, infinities,
+    subnormals, the overflow to infinity at the top of the range."""
+    high = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    grid = (high[:, None] | lows[None, :]).ravel()
+    rnd = np.random.default_rng(77).integers(0, 2**32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    v = orc.bits_f32(np.concatenate([grid, rnd]))
+    got = rgc.rgc_test_round_nearest(torch.from_numpy(v).to(dev))
+    _sync()
+    assert np.array_equal(bits(got), orc.f32_to_bf16_rne(v))
+
+
 # ---------------------------------------------------------------------------
 # Projection
 # ---------------------------------------------------------------------------

@@ -249,6 +249,11 @@ def test_test_hooks_validation(lib):
     assert lib.rgc_test_philox(0, -1, FAKE, FAKE, s) == SHAPE
     assert lib.rgc_test_philox(0, 0, None, None, s) == OK
     assert lib.rgc_test_stochastic_round(FAKE, FAKE, 4, 8, 7, 0, 0, 0, s) == SHAPE
+    assert lib.rgc_test_round_nearest(FAKE, FAKE, -1, s) == SHAPE
+    assert lib.rgc_test_round_nearest(FAKE, FAKE, (1 << 31) + 1, s) == SHAPE
+    assert lib.rgc_test_round_nearest(None, None, 0, s) == OK
+    assert lib.rgc_test_round_nearest(None, FAKE, 4, s) == NULL
+    assert lib.rgc_test_round_nearest(FAKE + 2, FAKE, 4, s) == ALIGN
     assert lib.rgc_test_reconstruct(FAKE, FAKE, FAKE, 64, 256, 24, s) == UNSUP
 
 
