@@ -10,13 +10,16 @@
 // here a workgroup rebuilds 128 rows (64 at r = 128) x 64 columns per step
 // (the result does not depend on the tile shape).
 //
-// One batch (e.g. all projections of a block) takes three launches:
-//   norms:  sum w^2 over W, and ||H||^2 = tr((C^T C)(P^T P)) (the Frobenius
-//           norm of a product through the two r x r Gram matrices), so W is
-//           only streamed and squared while a few workgroups per matrix form
+// One batch (e.g. all projections of a block) takes three or four launches:
+//   norms:  sum w^2 over W (fp64 partials per 128 KB of W), and ||H||^2 =
+//           tr((C^T C)(P^T P)) (the Frobenius norm of a product through the
+//           two r x r Gram matrices): a few workgroups per matrix form
 //           partial Gram matrices of C and of P (above r = 128 in four
-//           groups of block pairs). The W partials are fp64, the Gram
-//           partials fp32, with fixed-order reductions across lanes and waves;
+//           groups of block pairs) on MFMA, fp32 partials; every reduction
+//           has a fixed order across lanes and waves. Up to r = 64 the W
+//           stream and the Gram workgroups share one launch; above, the Gram
+//           workgroups' registers would leave the W stream one workgroup per
+//           compute unit, so it runs first in a launch of its own;
 //   reduce: one workgroup per (matrix, block pair) sums that pair's partials
 //           in a fixed order into one term of ||H||^2 (and ||W||^2);
 //   update: every wave forms s = fp32(tau ||W|| / ||H||) from its matrix's
@@ -89,9 +92,11 @@ struct ApplyBatch {
   int carry;  // CarryMode
   float tau;
   int wbase[kApplyMaxItems + 1];  // update workgroups [wbase[m], wbase[m+1]) serve item m
-  // Norms launch: Gram workgroups [gbase[m], gbase[m+1]) (per pair group,
-  // the first ncg[m] over rows of C, the rest over rows of P), then W-stream
-  // workgroups gbase[n] + [sbase[m], sbase[m+1]).
+  // Norms: Gram workgroups [gbase[m], gbase[m+1]) (per pair group, the
+  // first ncg[m] over rows of C, the rest over rows of P) and W-stream
+  // workgroups [sbase[m], sbase[m+1]) (a launch of their own at the tiled
+  // ranks; in the small ranks' norms launch they follow the Gram workgroups,
+  // from gbase[n]).
   int gbase[kApplyMaxItems + 1];
   int sbase[kApplyMaxItems + 1];
   int ncg[kApplyMaxItems];
@@ -563,12 +568,16 @@ __global__ __launch_bounds__(ApplyTraits<R>::THREADS, R > 128 ? 1 : 2) void appl
 constexpr int64_t kWStreamChunks = 8192;
 
 // The values one lane reads in one 32-row step: rows 8g .. 8g+7 of the step,
-// for the NL blocks of its pair group (raw bits: fp32 for C, bf16 for P; 0
-// past row1). Slot s < N0 holds block LO0 + s, slot N0 + s block LO1 + s; the
-// value of block b in lane x is column NB x + b of the row.
+// for the NL blocks of its pair group (raw bits: fp32 for C, bf16 for P).
+// Slot s < N0 holds block LO0 + s, slot N0 + s block LO1 + s; the value of
+// block b in lane x is column NB x + b of the row. Rows past row1 are read
+// from row row1 - 1 and masked to 0 where they are used (keep), so that the
+// loads carry no branch: a load under a per-row branch was followed by a
+// wait for it, which serialised every step's sixteen loads.
 template <int NL>
 struct GramRows {
   uint32_t v[8][NL];
+  uint32_t keep[8];  // ~0 for a row below row1, else 0
 };
 
 // Blocks LO .. LO+N-1 of one row (p = the row's column NB x) into slots
@@ -633,14 +642,10 @@ __device__ __forceinline__ void load_gram_rows(const T* __restrict__ src, int64_
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int64_t row = base + 8 * g + e;
-    if (row < row1) {
-      const T* p = src + row * (16 * NB) + NB * x;
-      load_range<NB, LO0, N0, 0>(p, o.v[e]);
-      load_range<NB, LO1, N1, N0>(p, o.v[e]);
-    } else {
-#pragma unroll
-      for (int c = 0; c < N0 + N1; ++c) o.v[e][c] = 0u;
-    }
+    o.keep[e] = row < row1 ? ~0u : 0u;
+    const T* p = src + (row < row1 ? row : row1 - 1) * (16 * NB) + NB * x;
+    load_range<NB, LO0, N0, 0>(p, o.v[e]);
+    load_range<NB, LO1, N1, N0>(p, o.v[e]);
   }
 }
 
@@ -658,12 +663,13 @@ __device__ __forceinline__ void gram_step(const GramRows<N0 + N1>& rw,
 #pragma unroll
     for (int a = 0; a < NL; ++a) {
       if constexpr (TWO_TERM) {
-        const float v0 = __uint_as_float(rw.v[2 * p][a]), v1 = __uint_as_float(rw.v[2 * p + 1][a]);
+        const float v0 = __uint_as_float(rw.v[2 * p][a] & rw.keep[2 * p]);
+        const float v1 = __uint_as_float(rw.v[2 * p + 1][a] & rw.keep[2 * p + 1]);
         const uint32_t hv = f32x2_to_bf16x2_rne(v0, v1);
         hi[a][p] = hv;
         lo[a][p] = f32x2_to_bf16x2_rne(v0 - __uint_as_float(hv << 16), v1 - __uint_as_float(hv & 0xFFFF0000u));
       } else {
-        hi[a][p] = pack_bf16x2(rw.v[2 * p][a], rw.v[2 * p + 1][a]);
+        hi[a][p] = pack_bf16x2(rw.v[2 * p][a] & rw.keep[2 * p], rw.v[2 * p + 1][a] & rw.keep[2 * p + 1]);
         lo[a][p] = 0u;
       }
     }
@@ -729,7 +735,8 @@ __device__ void gram_partial(const T* __restrict__ src, int64_t row0, int64_t ro
 // Sum of squares of the 16-byte chunks [c0, c1) of W (row-major d x k, row
 // stride ldw; chunk c is columns 8 (c % (k/8)) .. +7 of row c / (k/8)):
 // fp32 per chunk (the squares of bf16 values are exact in fp32), fp64 across
-// chunks, lanes and waves; returned in thread 0.
+// chunks, lanes and waves; returned in thread 0. NT: non-temporal loads.
+template <bool NT>
 __device__ double wstream_sumsq(const uint16_t* __restrict__ W, int64_t ldw, int64_t k, int64_t c0, int64_t c1,
                                 double* red) {
   constexpr int U = 8;
@@ -743,8 +750,9 @@ __device__ double wstream_sumsq(const uint16_t* __restrict__ W, int64_t ldw, int
     uint4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      v[u] = c + 256 * u < c1 ? *reinterpret_cast<const uint4*>(W + (int64_t)row * ldw + 8 * col)
-                              : make_uint4(0u, 0u, 0u, 0u);
+      const u32x4v_t* src = reinterpret_cast<const u32x4v_t*>(W + (int64_t)row * ldw + 8 * col);
+      const u32x4v_t t = c + 256 * u < c1 ? (NT ? __builtin_nontemporal_load(src) : *src) : u32x4v_t{0u, 0u, 0u, 0u};
+      v[u] = make_uint4(t.x, t.y, t.z, t.w);
       col += dc;
       row += dr;
       const bool wrap = col >= cpr;
@@ -776,15 +784,47 @@ __device__ __forceinline__ int item_of(const int* base, int n, int w) {
   return m;
 }
 
-// The norms launch: Gram workgroups first (per item and pair group, the
-// C-row chunks, then the P-row chunks), then the W-stream workgroups.
+// W-stream workgroup sw: the squares of its kWStreamChunks chunks of one
+// matrix into b.partials[sw].
+template <bool NT>
+__device__ __forceinline__ void wstream_workgroup(const ApplyBatch& b, int sw, double* red) {
+  const int m = item_of(b.sbase, b.n, sw);
+  const ApplyItem& it = b.it[m];
+  const int64_t total = it.d * (it.k >> 3);
+  const int64_t c0 = (sw - b.sbase[m]) * kWStreamChunks;
+  const int64_t c1 = c0 + kWStreamChunks < total ? c0 + kWStreamChunks : total;
+  const double sq = wstream_sumsq<NT>(it.W, it.ldw, it.k, c0, c1, red);
+  if (threadIdx.x == 0) b.partials[sw] = sq;
+}
+
+// The W stream in a launch of its own (r > 64): in one launch with the Gram
+// workgroups it took their register allocation (one workgroup per compute
+// unit) and streamed W at 4.2 TB/s; alone, with non-temporal loads, at
+// 6.6 TB/s (the Qwen3-8B-shaped layer at r = 128: 386 MB in 58 us, the apply
+// 295 -> 273 us). Up to r = 64 the shared launch measured faster (the
+// Qwen3-1.7B-shaped block: 71 against 78 us).
+__global__ __launch_bounds__(256) void wstream_kernel(ApplyBatch b) {
+  __shared__ double red[kApplyWaves];
+  wstream_workgroup<true>(b, blockIdx.x, red);
+}
+
+// Where the W stream runs at rank R (see wstream_kernel).
+template <int R>
+constexpr bool wstream_own_launch() { return R > 64; }
+
+// The norms launch: per item and pair group, the C-row chunks, then the
+// P-row chunks; up to r = 64 the W-stream workgroups follow.
 template <int R>
 __global__ __launch_bounds__(256) void gram_norms_kernel(ApplyBatch b) {
   using Gs = GramShape<R>;
   __shared__ __attribute__((aligned(16))) float red[Gs::NE];
   const int w = blockIdx.x;
   const int ng = b.gbase[b.n];
-  if (w < ng) {
+  if (!wstream_own_launch<R>() && w >= ng) {
+    wstream_workgroup<false>(b, w - ng, reinterpret_cast<double*>(red));
+    return;
+  }
+  {
     const int m = item_of(b.gbase, b.n, w);
     const ApplyItem& it = b.it[m];
     const int per_group = (b.gbase[m + 1] - b.gbase[m]) / Gs::NG;  // C and P chunks of one group
@@ -802,16 +842,7 @@ __global__ __launch_bounds__(256) void gram_norms_kernel(ApplyBatch b) {
         gram_partial<R, false, GR>(it.P, r0, r1, out, red);
       }
     });
-    return;
   }
-  const int sw = w - ng;
-  const int m = item_of(b.sbase, b.n, sw);
-  const ApplyItem& it = b.it[m];
-  const int64_t total = it.d * (it.k >> 3);
-  const int64_t c0 = (sw - b.sbase[m]) * kWStreamChunks;
-  const int64_t c1 = c0 + kWStreamChunks < total ? c0 + kWStreamChunks : total;
-  const double sq = wstream_sumsq(it.W, it.ldw, it.k, c0, c1, reinterpret_cast<double*>(red));
-  if (threadIdx.x == 0) b.partials[sw] = sq;
 }
 
 // Per item: the scale launches sum its norms partials in a fixed order (each
@@ -1012,7 +1043,7 @@ __global__ __launch_bounds__(256) void small_norms_kernel(ApplyBatch b) {
   const int64_t total = it.d * (it.k >> 3);
   const int64_t c0 = (sw - b.sbase[m]) * kWStreamChunks;
   const int64_t c1 = c0 + kWStreamChunks < total ? c0 + kWStreamChunks : total;
-  const double sq = wstream_sumsq(it.W, it.ldw, it.k, c0, c1, red);
+  const double sq = wstream_sumsq<false>(it.W, it.ldw, it.k, c0, c1, red);
   if (threadIdx.x == 0) b.partials[sw] = sq;
 }
 
@@ -1273,9 +1304,14 @@ rgc_status_t apply_launch(int n, uint16_t* const* Ws, const int64_t* ldws, const
   b.wnorm2 = carry != kCarryNone ? wnorm2 : reinterpret_cast<double*>(static_cast<char*>(ws) + l.wnorm2_off);
   b.scale = reinterpret_cast<float*>(static_cast<char*>(ws) + l.scale_off);
   b.wpart = reinterpret_cast<double*>(static_cast<char*>(ws) + l.wpart_off);
-  // with a carried ||W|| the launch holds the Gram workgroups alone
+  // with a carried ||W|| there is no W stream
   const int nw = carry == kCarryIn ? 0 : b.sbase[n];
-  hipLaunchKernelGGL(gram_norms_kernel<R>, dim3((unsigned)(b.gbase[n] + nw)), dim3(256), 0, st, b);
+  if (wstream_own_launch<R>()) {
+    if (nw > 0) hipLaunchKernelGGL(wstream_kernel, dim3((unsigned)nw), dim3(256), 0, st, b);
+    hipLaunchKernelGGL(gram_norms_kernel<R>, dim3((unsigned)b.gbase[n]), dim3(256), 0, st, b);
+  } else {
+    hipLaunchKernelGGL(gram_norms_kernel<R>, dim3((unsigned)(b.gbase[n] + nw)), dim3(256), 0, st, b);
+  }
   hipLaunchKernelGGL(gram_reduce_kernel<R>, dim3((unsigned)(n * GramShape<R>::NP)), dim3(256), 0, st, b);
   constexpr unsigned T = ApplyTraits<R>::THREADS;
   if (carry == kCarryNone) {
