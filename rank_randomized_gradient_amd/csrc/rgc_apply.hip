@@ -799,9 +799,9 @@ __device__ __forceinline__ void wstream_workgroup(const ApplyBatch& b, int sw, d
 
 // The W stream in a launch of its own (r > 64): in one launch with the Gram
 // workgroups it took their register allocation (one workgroup per compute
-// unit) and streamed W at 4.2 TB/s; alone, with non-temporal loads, at
-// 6.6 TB/s (the Qwen3-8B-shaped layer at r = 128: 386 MB in 58 us, the apply
-// 295 -> 273 us). Up to r = 64 the shared launch measured faster (the
+// unit) and streamed W at about 4.2 TB/s; alone, with non-temporal loads, at
+// 5.5 TB/s (the Qwen3-8B-shaped layer at r = 128: 386 MB in 70 us; the apply
+// 295 -> 271 us). Up to r = 64 the shared launch measured faster (the
 // Qwen3-1.7B-shaped block: 71 against 78 us).
 __global__ __launch_bounds__(256) void wstream_kernel(ApplyBatch b) {
   __shared__ double red[kApplyWaves];
@@ -888,21 +888,24 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(ApplyBatch b) {
   const int nc = b.ncg[m], np = (b.gbase[m + 1] - b.gbase[m]) / Gs::NG - nc;
   const float* gc = b.gram + (int64_t)(b.gbase[m] + grp * (nc + np)) * Gs::NE + 256 * ql + threadIdx.x;
   const float* gp = gc + (int64_t)nc * Gs::NE;
-  constexpr int U = 8;  // loads in flight per thread
+  // the C and P partials are loaded together, U of each in flight per thread
+  // (row clamped, value masked past the count, so that no load sits under a
+  // branch), and summed in partial order
+  constexpr int U = 16;
   double G = 0.0, M = 0.0;
-  for (int u = 0; u < nc; u += U) {
-    float v[U];
+  const int nmax = nc > np ? nc : np;
+  for (int u = 0; u < nmax; u += U) {
+    float vc[U], vp[U];
 #pragma unroll
-    for (int i = 0; i < U; ++i) v[i] = u + i < nc ? gc[(int64_t)(u + i) * Gs::NE] : 0.f;
+    for (int i = 0; i < U; ++i) {
+      vc[i] = gc[(int64_t)(u + i < nc ? u + i : nc - 1) * Gs::NE];
+      vp[i] = gp[(int64_t)(u + i < np ? u + i : np - 1) * Gs::NE];
+    }
 #pragma unroll
-    for (int i = 0; i < U; ++i) G += (double)v[i];
-  }
-  for (int u = 0; u < np; u += U) {
-    float v[U];
-#pragma unroll
-    for (int i = 0; i < U; ++i) v[i] = u + i < np ? gp[(int64_t)(u + i) * Gs::NE] : 0.f;
-#pragma unroll
-    for (int i = 0; i < U; ++i) M += (double)v[i];
+    for (int i = 0; i < U; ++i) {
+      if (u + i < nc) G += (double)vc[i];
+      if (u + i < np) M += (double)vp[i];
+    }
   }
   // a within-half group lists its pairs (a, c) for a = 0.., c = a .. n0-1
   // (diagonal when c = a); a cross group has no diagonal pair
@@ -918,8 +921,18 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(ApplyBatch b) {
   double th = (diag ? 1.0 : 2.0) * G * M;
   double tw = 0.0;
   const bool streamed = q == 0 && b.carry != kCarryIn;  // else ||W||^2 is the caller's carried value
-  if (streamed)
-    for (int w = b.sbase[m] + (int)threadIdx.x; w < b.sbase[m + 1]; w += 256) tw += b.partials[w];
+  if (streamed) {
+    // thread t sums partials t, t + 256, ... in order, four loads in flight
+    const int w1 = b.sbase[m + 1];
+    for (int w = b.sbase[m] + (int)threadIdx.x; w < w1; w += 4 * 256) {
+      double v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = b.partials[w + 256 * i < w1 ? w + 256 * i : w1 - 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (w + 256 * i < w1) tw += v[i];
+    }
+  }
   th = wave_sum(th);
   tw = wave_sum(tw);
   if (lane == 0) {
