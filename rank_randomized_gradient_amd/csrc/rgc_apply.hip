@@ -60,14 +60,15 @@ constexpr int64_t kMaxApplyElems = int64_t(1) << 38;  // d * k (workgroup counts
 template <int R>
 struct ApplyTraits {
   static constexpr int KQ = (R + 31) / 32;              // K-steps of 32 over r
-  // Update sweeps: tiles of 128 rows. Up to r = 128 eight waves of one
-  // 16-row N-tile each, so that two workgroups (four waves per SIMD) overlap
-  // the per-tile arithmetic with the copies; above, four waves of two N-tiles
-  // (the P stage leaves one workgroup per compute unit anyway). The 128-row
-  // tile halves the P rows re-read per W byte against 64 rows (measured on
-  // the Qwen3-1.7B-shaped block at r = 256: 253 -> 205 us).
-  static constexpr int WAVES = R <= 128 ? 8 : kApplyWaves;  // waves of an update workgroup
-  static constexpr int NTW = R <= 128 ? 1 : 2;
+  // Update sweeps: tiles of 128 rows, eight waves of one 16-row N-tile each,
+  // so that more waves overlap the per-tile arithmetic with the copies: two
+  // workgroups (four waves per SIMD) up to r = 128, one above, where the P
+  // stage leaves one workgroup per compute unit (there eight waves against
+  // four of two N-tiles: the Qwen3-1.7B-shaped block's apply at r = 256
+  // 161 -> 148 us, at r = 192 139 -> 128 us). The 128-row tile halves the P
+  // rows re-read per W byte against 64 rows (r = 256: 253 -> 205 us).
+  static constexpr int WAVES = 8;  // waves of an update workgroup
+  static constexpr int NTW = 1;
   static constexpr int RW = 16 * NTW;                   // rows per wave
   static constexpr int ROWS = WAVES * RW;               // rows per workgroup tile
   static constexpr int THREADS = 64 * WAVES;
@@ -232,7 +233,8 @@ __device__ __forceinline__ void load_row_operand(const float* __restrict__ C, in
 // rebuild on MFMA, Philox, rounding) is heavy enough that other waves
 // overlapping it pay more than deeper staging (measured on the Qwen3-1.7B-
 // shaped block and the Qwen3-8B-shaped layer). At r > 128 the P rows make a
-// stage too large for two, so one workgroup takes up to six.
+// stage too large for two, so one workgroup takes up to six (three at
+// r = 256).
 
 template <int R, int MODE>
 struct ApplyShape {
