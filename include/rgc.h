@@ -222,8 +222,9 @@ rgc_status_t rgc_apply(uint16_t* W, int64_t ldw, const float* C, const uint16_t*
                        size_t ws_bytes, void* stream);
 
 /* rgc_apply for n <= 16 matrices of one rank r (e.g. the projections of a
- * block) in three launches: a norms sweep over all of them, one step scalar
- * per matrix, an update sweep. Item m: W Ws[m] (ds[m] x ks[m], row stride
+ * block) in three or four launches: the norms (W streamed for ||W||, the
+ * Gram partials of C and P for ||H||; one launch up to r = 64, two above),
+ * one step scalar per matrix, an update sweep. Item m: W Ws[m] (ds[m] x ks[m], row stride
  * ldws[m]), C Cs[m] (ds[m] x r), P Ps[m] (ks[m] x r), rounding seed seeds[m],
  * stats NULL or stats[m] NULL or device float[4]. All arrays are HOST arrays
  * of n entries; tau is shared. Each matrix gets exactly the bits that

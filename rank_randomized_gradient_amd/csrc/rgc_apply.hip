@@ -216,7 +216,7 @@ __device__ __forceinline__ void load_row_operand(const float* __restrict__ C, in
 // The sweeps are software pipelines over the workgroup's tiles: each tile's
 // W rows (ROWS x 64 bf16) and P rows (64 x R bf16) are copied from memory
 // straight into an LDS stage (1 KB copies that bypass the VGPRs, spread over
-// the four waves), S - 1 tiles ahead of the tile being processed.
+// the workgroup's waves), S - 1 tiles ahead of the tile being processed.
 //
 // W stage layout: copy c holds tile rows 8c .. 8c+7 (128 bytes each); lane l
 // reads row 8c + l / 8, 8-column chunk q such that its 16 bytes land at
