@@ -13,9 +13,9 @@
 // fetching the rank operand as rarely as possible:
 //
 // * A workgroup tile is TILE = 64*WN columns of N by all R columns of r; its
-//   four waves split it WN ways along N and WR ways along r (WN * WR = 4),
-//   so every wave multiplies a 64 (N) x RW (r) block with 16x16x32 MFMAs, r
-//   on the M side.
+//   waves (four, or eight for the accumulate above 128 ranks) split it WN
+//   ways along N and WR ways along r, so every wave multiplies a 64 (N) x RW
+//   (r) block with 16x16x32 MFMAs, r on the M side.
 // * A K-step is 32 rows of K. The step's stream slab (32 x TILE) and rank
 //   slab (32 x R) are copied from memory straight into an LDS stage by all
 //   four waves, in 1 KB copies that do not pass through VGPRs, S - 1 steps
@@ -153,15 +153,19 @@ constexpr int kStages = 6;
 __host__ __device__ constexpr int sketch_width(int RM) { return RM > 128 && (RM / 16) % 2 == 1 ? RM + 16 : RM; }
 
 // Waves along r: up to 128 ranks one (the N tile is 256 wide, each wave holds
-// all ranks, up to 8 M-tiles); above 128 two, each with half the ranks, so
-// that the N tile is 128 wide and the rank operand is re-read half as often
-// as with four waves of a quarter. (Measured on the 1.7B block at r = 256
-// and the 8B layer at r = 128 against a split that gave every wave at most
-// 64 ranks.)
+// all ranks, up to 8 M-tiles); above 128 two, each with half the ranks (a
+// split that gave every wave at most 64 ranks re-read the rank operand twice
+// as often: measured on the 1.7B block at r = 256 and the 8B layer at
+// r = 128). Above 128 the accumulate keeps the 256-wide N tile with eight
+// waves (two per SIMD), so that its XP slab (32 tokens x r) is shared by 256
+// columns of D, not 128: the 1.7B block's accumulate at r = 256 71.0 -> 63.2
+// us per call. The project's X and P slabs (64 k per step) leave room for a
+// 128-wide tile only, with four waves.
 template <int R, int KH>
 struct StageShape {
   static constexpr int WR = R <= 128 ? 1 : 2;
-  static constexpr int WN = 4 / WR;                              // waves along N
+  static constexpr int WN = R <= 128 || KH == 1 ? 4 : 2;         // waves along N
+  static constexpr int WAVES = WR * WN;
   static constexpr int RW = R / WR;                              // r per wave
   static constexpr int MT = RW / 16;                             // MFMA M-tiles per wave
   static constexpr int TILE = 64 * WN;                           // N per workgroup tile
@@ -173,7 +177,7 @@ struct StageShape {
   static constexpr int STREAM = 1024 * NSC;                      // stream slab bytes
   static constexpr int STAGE = 1024 * NI;
   static constexpr int S = kStages * STAGE <= 160 * 1024 ? kStages : 160 * 1024 / STAGE;
-  static constexpr int NV_LO = NI / 4, NV_HI = (NI + 3) / 4;  // copies per wave (waves below NI % 4 take one more)
+  static constexpr int NV_LO = NI / WAVES, NV_HI = (NI + WAVES - 1) / WAVES;  // copies per wave
   static_assert(RW % 16 == 0 && RW <= 128, "rank split");
   static_assert(S >= 3 && S * STAGE <= 160 * 1024, "LDS");
   static_assert((S - 1) * NV_HI <= 63, "vector memory counter");
@@ -216,7 +220,8 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
   const int64_t w = logical_workgroup(blockIdx.x, s.G);
   const int64_t u0 = uniform_i64(range_begin(s, w)), u1 = uniform_i64(range_begin(s, w + 1));
   const uint32_t lds0 = (uint32_t)(uintptr_t)(RGC_LDS char*)smem;
-  const bool more = wave < Sh::NI % 4;  // this wave issues NV_HI copies per stage (else NV_LO)
+  constexpr int NW = Sh::WAVES;
+  const bool more = wave < Sh::NI % NW;  // this wave issues NV_HI copies per stage (else NV_LO)
 
   // ---- the copy side: a cursor over this workgroup's units, S - 1 ahead
   const int m0 = item_of_unit(s, u0);
@@ -245,7 +250,7 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
     const int64_t rows = window_rows(l_kext, KS);
 #pragma unroll
     for (int v = 0; v < Sh::NV_HI; ++v) {
-      const int c = wave + 4 * v;
+      const int c = wave + NW * v;
       if (c < Sh::NSC) {
         voff[v] = pol.stream_offset(m, tile, c, lane, rows);
       } else {
@@ -269,9 +274,9 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
     const uint32_t st = lds0 + lslot * Sh::STAGE;
     static_for<0, Sh::NV_HI>([&](auto vc) {
       constexpr int v = decltype(vc)::value;
-      const int c = wave + 4 * v;  // a stream copy if c < NSC, a rank copy if NSC <= c < NI
+      const int c = wave + NW * v;  // a stream copy if c < NSC, a rank copy if NSC <= c < NI
       const uint16_t* Rb = nullptr;
-      if constexpr (4 * v + 3 >= Sh::NSC) {
+      if constexpr (NW * v + NW - 1 >= Sh::NSC) {
         if constexpr (GM == 1) {
           Rb = uniform_ptr(l_rank[0] + wb * RM);
         } else {
@@ -283,9 +288,9 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
           Rb = uniform_ptr(base + wb * RM);
         }
       }
-      if constexpr (4 * v + 3 < Sh::NSC) {
+      if constexpr (NW * v + NW - 1 < Sh::NSC) {
         dma_16b_stream(Sb, voff[v], st + 1024 * c);
-      } else if constexpr (4 * v >= Sh::NSC && 4 * v + 3 < Sh::NI) {
+      } else if constexpr (NW * v >= Sh::NSC && NW * v + NW - 1 < Sh::NI) {
         dma_16b_cached(Rb, voff[v], st + 1024 * c);
       } else {
         if (c < Sh::NSC)
@@ -643,7 +648,9 @@ struct AccumulatePolicy {
 };
 
 template <int RM>
-__global__ __launch_bounds__(256, 1) void accumulate_kernel(AccumulateBatch ab) {
+constexpr int acc_threads() { return 64 * StageShape<sketch_width(RM), 1>::WAVES; }
+template <int RM>
+__global__ __launch_bounds__(acc_threads<RM>(), 1) void accumulate_kernel(AccumulateBatch ab) {
   using Sh = StageShape<sketch_width(RM), 1>;
   __shared__ __attribute__((aligned(1024))) char smem[Sh::S * Sh::STAGE];
   AccumulatePolicy<RM> pol{ab};
@@ -677,7 +684,9 @@ __global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
   const int64_t tn = s.tile_n;
   const int64_t left = s.next[m] - tile * tn;
   const int64_t rows = left < tn ? left : tn;
-  using Sh = StageShape<R, 1>;  // the slot layout depends on R only (slot_pos4)
+  // the slots' layout (slot_pos4) is the producing kernel's: the project's
+  // tile shape (K-steps of 64) or the accumulate's (32)
+  using Sh = StageShape<R, TO_BF16 ? kProjectKH : 1>;
   constexpr int MAXP = 8;        // partial loads in flight at once
   {
     // one float4 of the slots per thread, at the same store-order position in each
@@ -1144,7 +1153,7 @@ rgc_status_t accumulate_launch(int n, const uint16_t* const* Ds, const int64_t* 
   ab.part = static_cast<float*>(ws);
   ab.add_part = (phase & 1) ? 0 : 1;
   fb.part = ab.part;
-  hipLaunchKernelGGL(accumulate_kernel<R>, dim3((unsigned)ab.s.G), dim3(256), 0, st, ab);
+  hipLaunchKernelGGL(accumulate_kernel<R>, dim3((unsigned)ab.s.G), dim3(acc_threads<R>()), 0, st, ab);
   if ((phase & 2) && has_split_tiles(ab.s))
     hipLaunchKernelGGL((finish_tiles_kernel<R, 1, false>), finish_grid<R>(ab.s), dim3(256), 0, st, fb);
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
