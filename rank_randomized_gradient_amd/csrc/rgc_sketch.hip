@@ -160,10 +160,15 @@ __host__ __device__ constexpr int sketch_width(int RM) { return RM > 128 && (RM 
 // waves (two per SIMD), so that its XP slab (32 tokens x r) is shared by 256
 // columns of D, not 128: the 1.7B block's accumulate at r = 256 71.0 -> 63.2
 // us per call. The project's X and P slabs (64 k per step) leave room for a
-// 128-wide tile only, with four waves.
+// 128-wide tile only, with four waves. At r = 64, 96 and 128 both kernels
+// run eight waves too, two along r: two waves per SIMD hide more of each
+// step's latency, and the first segment's sums fit in registers (the 8B
+// layer at r = 128: accumulate 81.5 -> 74 us, project 78 -> 76 us; the 1.7B
+// block at r = 64: 33.6 -> 32.9 and 39.6 -> 38.6 us). Ranks with an odd
+// number of 16-column blocks up to 128 (48, 80, 112) keep four waves.
 template <int R, int KH>
 struct StageShape {
-  static constexpr int WR = R <= 128 ? 1 : 2;
+  static constexpr int WR = R > 128 || (R > 32 && (R / 16) % 2 == 0) ? 2 : 1;
   static constexpr int WN = R <= 128 || KH == 1 ? 4 : 2;         // waves along N
   static constexpr int WAVES = WR * WN;
   static constexpr int RW = R / WR;                              // r per wave
@@ -531,7 +536,9 @@ struct ProjectPolicy {
 };
 
 template <int RM, int GM>
-__global__ __launch_bounds__(256, 1) void project_kernel(ProjectBatch pb) {
+constexpr int prj_threads() { return 64 * StageShape<sketch_width(GM * RM), kProjectKH>::WAVES; }
+template <int RM, int GM>
+__global__ __launch_bounds__((prj_threads<RM, GM>()), 1) void project_kernel(ProjectBatch pb) {
   using Sh = StageShape<sketch_width(GM * RM), kProjectKH>;
   __shared__ __attribute__((aligned(1024))) char smem[Sh::S * Sh::STAGE];
   ProjectPolicy<RM, GM> pol{pb};
@@ -1080,7 +1087,7 @@ rgc_status_t project_launch_groups(const ProjectGroups& gr, const uint16_t* cons
   fb.s = pb.s;
   pb.part = static_cast<float*>(ws);
   fb.part = pb.part;
-  hipLaunchKernelGGL((project_kernel<RM, GM>), dim3((unsigned)pb.s.G), dim3(256), 0, st, pb);
+  hipLaunchKernelGGL((project_kernel<RM, GM>), dim3((unsigned)pb.s.G), dim3((prj_threads<RM, GM>())), 0, st, pb);
   if (has_split_tiles(pb.s)) {
     const dim3 grid = finish_grid<RM, GM>(pb.s);
     hipLaunchKernelGGL((finish_tiles_kernel<RM, GM, true>), grid, dim3(256), 0, st, fb);
