@@ -799,12 +799,15 @@ __device__ __forceinline__ void wstream_workgroup(const ApplyBatch& b, int sw, d
   if (threadIdx.x == 0) b.partials[sw] = sq;
 }
 
-// The W stream in a launch of its own (r > 64): in one launch with the Gram
-// workgroups it took their register allocation (one workgroup per compute
-// unit) and streamed W at about 4.2 TB/s; alone, with non-temporal loads, at
-// 5.5 TB/s (the Qwen3-8B-shaped layer at r = 128: 386 MB in 70 us; the apply
-// 295 -> 271 us). Up to r = 64 the shared launch measured faster (the
-// Qwen3-1.7B-shaped block: 71 against 78 us).
+// The W stream in a launch of its own (64 < r <= 128): in one launch with the
+// Gram workgroups it took their register allocation (one workgroup per
+// compute unit) and streamed W at about 4.2 TB/s; alone, with non-temporal
+// loads, at 5.5 TB/s (the Qwen3-8B-shaped layer at r = 128: 386 MB in 70 us;
+// the apply 295 -> 271 us). Up to r = 64 the shared launch measured faster
+// (the Qwen3-1.7B-shaped block: 71 against 78 us), and above r = 128 too,
+// where the Gram workgroups take longer than the stream and the shared launch
+// hides it behind them (the same block at r = 256: 142 against 135 us per
+// update).
 __global__ __launch_bounds__(256) void wstream_kernel(ApplyBatch b) {
   __shared__ double red[kApplyWaves];
   wstream_workgroup<true>(b, blockIdx.x, red);
@@ -812,10 +815,10 @@ __global__ __launch_bounds__(256) void wstream_kernel(ApplyBatch b) {
 
 // Where the W stream runs at rank R (see wstream_kernel).
 template <int R>
-constexpr bool wstream_own_launch() { return R > 64; }
+constexpr bool wstream_own_launch() { return R > 64 && R <= 128; }
 
 // The norms launch: per item and pair group, the C-row chunks, then the
-// P-row chunks; up to r = 64 the W-stream workgroups follow.
+// P-row chunks; outside 64 < r <= 128 the W-stream workgroups follow.
 template <int R>
 __global__ __launch_bounds__(256) void gram_norms_kernel(ApplyBatch b) {
   using Gs = GramShape<R>;
