@@ -166,10 +166,12 @@ __host__ __device__ constexpr int sketch_width(int RM) { return RM > 128 && (RM 
 // layer at r = 128: accumulate 81.5 -> 74 us, project 78 -> 76 us; the 1.7B
 // block at r = 64: 33.6 -> 32.9 and 39.6 -> 38.6 us). Ranks with an odd
 // number of 16-column blocks up to 128 (48, 80, 112) keep four waves.
-template <int R, int KH>
+//
+// WNF > 0 forces WNF waves along N (the narrow accumulate tile below).
+template <int R, int KH, int WNF = 0>
 struct StageShape {
   static constexpr int WR = R > 128 || (R > 32 && (R / 16) % 2 == 0) ? 2 : 1;
-  static constexpr int WN = R <= 128 || KH == 1 ? 4 : 2;         // waves along N
+  static constexpr int WN = WNF > 0 ? WNF : R <= 128 || KH == 1 ? 4 : 2;  // waves along N
   static constexpr int WAVES = WR * WN;
   static constexpr int RW = R / WR;                              // r per wave
   static constexpr int MT = RW / 16;                             // MFMA M-tiles per wave
@@ -217,7 +219,8 @@ __device__ __forceinline__ void staged_pipeline(const Schedule& s, Policy& pol, 
   constexpr int NRB_ITEM = RM / 16;         // rank blocks of one member
   constexpr int NRB_MEM = GM * NRB_ITEM;    // rank blocks that exist in memory
   constexpr int CPM = KH * NRB_ITEM;        // rank copies per member and stage
-  using Sh = StageShape<R, KH>;
+  using Sh = typename Policy::Sh;
+  static_assert(Sh::KS == 32 * KH, "policy shape");
   constexpr int S = Sh::S, MT = Sh::MT, KS = Sh::KS;
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int wn = wave % Sh::WN, rw = wave / Sh::WN;
@@ -458,11 +461,11 @@ struct ProjectBatch {
   float* part;                    // 2 G slots of TILE x R fp32
 };
 
-template <int RM, int GM>
+template <int RM, int GM, int WNF = 0>
 struct ProjectPolicy {
   static constexpr int R = sketch_width(GM * RM);
   static constexpr int NRB_ITEM = RM / 16;
-  using Sh = StageShape<R, kProjectKH>;
+  using Sh = StageShape<R, kProjectKH, WNF>;
   // a group's sums leave no room for a second set (measured: spills)
   static constexpr bool kKeepLargeFirst = GM == 1;
   const ProjectBatch& pb;
@@ -535,14 +538,22 @@ struct ProjectPolicy {
   }
 };
 
-template <int RM, int GM>
-constexpr int prj_threads() { return 64 * StageShape<sketch_width(GM * RM), kProjectKH>::WAVES; }
+template <int RM, int GM, int WNF = 0>
+constexpr int prj_threads() { return 64 * StageShape<sketch_width(GM * RM), kProjectKH, WNF>::WAVES; }
 template <int RM, int GM>
 __global__ __launch_bounds__((prj_threads<RM, GM>()), 1) void project_kernel(ProjectBatch pb) {
   using Sh = StageShape<sketch_width(GM * RM), kProjectKH>;
   __shared__ __attribute__((aligned(1024))) char smem[Sh::S * Sh::STAGE];
   ProjectPolicy<RM, GM> pol{pb};
   staged_pipeline<RM, kProjectKH, ProjectPolicy<RM, GM>, GM>(pb.s, pol, smem);
+}
+// The narrow tiles (128 tokens, two waves along N) of small one-matrix launches.
+template <int RM>
+__global__ __launch_bounds__((prj_threads<RM, 1, 2>()), 1) void project_narrow_kernel(ProjectBatch pb) {
+  using Sh = StageShape<sketch_width(RM), kProjectKH, 2>;
+  __shared__ __attribute__((aligned(1024))) char smem[Sh::S * Sh::STAGE];
+  ProjectPolicy<RM, 1, 2> pol{pb};
+  staged_pipeline<RM, kProjectKH, ProjectPolicy<RM, 1, 2>, 1>(pb.s, pol, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -564,10 +575,10 @@ struct AccumulateBatch {
   int add_part;                   // 1: add the split tiles' partials to the slots (a later call of a deferred accumulation)
 };
 
-template <int RM>
+template <int RM, int WNF = 0>
 struct AccumulatePolicy {
   static constexpr int R = sketch_width(RM);
-  using Sh = StageShape<R, 1>;
+  using Sh = StageShape<R, 1, WNF>;
   static constexpr bool kKeepLargeFirst = false;
   const AccumulateBatch& ab;
   int64_t ldd = 0, d = 0;  // of the copy cursor's item
@@ -654,13 +665,21 @@ struct AccumulatePolicy {
   }
 };
 
-template <int RM>
-constexpr int acc_threads() { return 64 * StageShape<sketch_width(RM), 1>::WAVES; }
+template <int RM, int WNF = 0>
+constexpr int acc_threads() { return 64 * StageShape<sketch_width(RM), 1, WNF>::WAVES; }
 template <int RM>
 __global__ __launch_bounds__(acc_threads<RM>(), 1) void accumulate_kernel(AccumulateBatch ab) {
   using Sh = StageShape<sketch_width(RM), 1>;
   __shared__ __attribute__((aligned(1024))) char smem[Sh::S * Sh::STAGE];
   AccumulatePolicy<RM> pol{ab};
+  staged_pipeline<RM, 1>(ab.s, pol, smem);
+}
+// The narrow tiles (128 columns of d, two waves along N) of small launches.
+template <int RM>
+__global__ __launch_bounds__((acc_threads<RM, 2>()), 1) void accumulate_narrow_kernel(AccumulateBatch ab) {
+  using Sh = StageShape<sketch_width(RM), 1, 2>;
+  __shared__ __attribute__((aligned(1024))) char smem[Sh::S * Sh::STAGE];
+  AccumulatePolicy<RM, 2> pol{ab};
   staged_pipeline<RM, 1>(ab.s, pol, smem);
 }
 
@@ -678,8 +697,8 @@ struct FinishBatch {
   uint16_t* XP[kMaxItems][kMaxGroup];     // project targets (per group member)
 };
 
-template <int RM, int GM, bool TO_BF16>
-__global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
+template <int RM, int GM, bool TO_BF16, int WNF>
+__device__ __forceinline__ void finish_tiles(const FinishBatch& fb) {
   constexpr int R = sketch_width(GM * RM);  // partials are tile_n x R; outputs have row stride RM
   const Schedule& s = fb.s;
   const int64_t t = blockIdx.y;
@@ -693,7 +712,7 @@ __global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
   const int64_t rows = left < tn ? left : tn;
   // the slots' layout (slot_pos4) is the producing kernel's: the project's
   // tile shape (K-steps of 64) or the accumulate's (32)
-  using Sh = StageShape<R, TO_BF16 ? kProjectKH : 1>;
+  using Sh = StageShape<R, TO_BF16 ? kProjectKH : 1, WNF>;
   constexpr int MAXP = 8;        // partial loads in flight at once
   {
     // one float4 of the slots per thread, at the same store-order position in each
@@ -743,6 +762,17 @@ __global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
       *reinterpret_cast<float4*>(fb.C[m] + out) = old;
     }
   }
+}
+
+template <int RM, int GM, bool TO_BF16>
+__global__ __launch_bounds__(256) void finish_tiles_kernel(FinishBatch fb) {
+  finish_tiles<RM, GM, TO_BF16, 0>(fb);
+}
+
+// The same over the narrow tiles' partials (their slot layout).
+template <int RM, bool TO_BF16>
+__global__ __launch_bounds__(256) void finish_narrow_tiles_kernel(FinishBatch fb) {
+  finish_tiles<RM, 1, TO_BF16, 2>(fb);
 }
 
 // ---------------------------------------------------------------------------
@@ -994,10 +1024,39 @@ dim3 finish_grid(const Schedule& s) {
   return dim3((unsigned)((s.tile_n * sketch_width(GM * RM) + 1023) / 1024), (unsigned)s.tbase[s.n]);
 }
 
-template <int RM, int GM = 1>
+// Waves along N of the narrow tiles (128 columns of N) of small launches:
+// only at ranks where the wide tile has WN = 4 and two waves along r, so that
+// the narrow one keeps four waves.
+constexpr int kNarrowWN = 2;
+static_assert(kNarrowWN == 2, "the narrow kernels above take two waves along N");
+template <int R, int KH>
+constexpr bool narrow_tile_ok() {
+  return StageShape<R, KH>::WR == 2 && StageShape<R, KH>::WN != kNarrowWN;
+}
+
+template <int RM, int GM = 1, int WNF = 0>
 Schedule project_schedule(int n, const int64_t* ns, const int64_t* ks, int64_t forced) {
-  using Sh = StageShape<sketch_width(GM * RM), kProjectKH>;
-  return make_schedule(n, ns, ks, Sh::TILE, Sh::KS, forced);
+  using Sh = StageShape<sketch_width(GM * RM), kProjectKH, WNF>;
+  Schedule s = make_schedule(n, ns, ks, Sh::TILE, Sh::KS, forced);
+  if (WNF > 0 && forced <= 0) {
+    // narrow tiles: one workgroup per compute unit (see project_narrow)
+    const int64_t cus = device_compute_units();
+    s.G = (int)(s.U < cus ? s.U : cus);
+  }
+  return s;
+}
+
+// Narrow project tiles (128 tokens, WN = 2), as for the accumulate: when a
+// one-matrix-per-group launch has too few K-steps for one workgroup per
+// compute unit with 256-token tiles, the wide schedule takes half the compute
+// units with ranges of a few K-steps; 128-token tiles give every compute unit
+// such a range, at the same split-tile partial bytes. Only where the narrow
+// tile keeps four waves. Never with a forced count.
+template <int RM, int GM>
+bool project_narrow(int n, const int64_t* ns, const int64_t* ks, int64_t forced) {
+  if (GM != 1 || forced > 0 || !narrow_tile_ok<sketch_width(RM), kProjectKH>()) return false;
+  const Schedule wide = project_schedule<RM, GM>(n, ns, ks, forced);
+  return wide.U < kMinUnitsPerWorkgroup * device_compute_units();
 }
 
 // When every tile has the same K-steps (one token count for all items, as in
@@ -1017,12 +1076,25 @@ void align_ranges_to_tiles(Schedule& s, int64_t forced) {
   if (p >= 2 && p <= s.nkb[0] && 10 * p * tiles >= 9 * (int64_t)s.G) s.G = (int)(p * tiles);
 }
 
-template <int RM>
+template <int RM, int WNF = 0>
 Schedule accumulate_schedule(int n, const int64_t* ns, const int64_t* ks, int64_t forced) {
-  using Sh = StageShape<sketch_width(RM), 1>;
+  using Sh = StageShape<sketch_width(RM), 1, WNF>;
   Schedule s = make_schedule(n, ns, ks, Sh::TILE, Sh::KS, forced);
   align_ranges_to_tiles(s, forced);
   return s;
+}
+
+// Narrow accumulate tiles (128 columns of d, WN = 2): when a launch has too
+// few K-steps for one workgroup per compute unit with 256-column tiles (a
+// single 4096-wide matrix per microbatch: 16 tiles), the wide schedule takes
+// half the compute units; 128-column tiles give twice the tiles, so every
+// compute unit streams D, each tile cut no finer than before. Only where the
+// narrow tile keeps four waves (two along r). Never with a forced count.
+template <int RM>
+bool accumulate_narrow(int n, const int64_t* ns, const int64_t* ks, int64_t forced) {
+  if (forced > 0 || !narrow_tile_ok<sketch_width(RM), 1>()) return false;
+  const Schedule wide = accumulate_schedule<RM>(n, ns, ks, forced);
+  return wide.U < kMinUnitsPerWorkgroup * device_compute_units();
 }
 
 // Groups of a launch: with `shared`, the matrices that read the same X (same
@@ -1083,14 +1155,25 @@ rgc_status_t project_launch_groups(const ProjectGroups& gr, const uint16_t* cons
     ++n;
   }
   if (n == 0) return RGC_OK;
-  pb.s = project_schedule<RM, GM>(n, ns, kk, forced);
-  fb.s = pb.s;
   pb.part = static_cast<float*>(ws);
   fb.part = pb.part;
-  hipLaunchKernelGGL((project_kernel<RM, GM>), dim3((unsigned)pb.s.G), dim3((prj_threads<RM, GM>())), 0, st, pb);
-  if (has_split_tiles(pb.s)) {
-    const dim3 grid = finish_grid<RM, GM>(pb.s);
-    hipLaunchKernelGGL((finish_tiles_kernel<RM, GM, true>), grid, dim3(256), 0, st, fb);
+  if constexpr (GM == 1 && narrow_tile_ok<sketch_width(RM), kProjectKH>()) {
+    if (project_narrow<RM, GM>(n, ns, kk, forced)) {
+      pb.s = project_schedule<RM, GM, kNarrowWN>(n, ns, kk, forced);
+      fb.s = pb.s;
+      hipLaunchKernelGGL(project_narrow_kernel<RM>, dim3((unsigned)pb.s.G), dim3((prj_threads<RM, 1, kNarrowWN>())),
+                         0, st, pb);
+      if (has_split_tiles(pb.s))
+        hipLaunchKernelGGL((finish_narrow_tiles_kernel<RM, true>), (finish_grid<RM, GM>(pb.s)), dim3(256), 0, st, fb);
+      return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+    }
+  }
+  pb.s = project_schedule<RM, GM>(n, ns, kk, forced);
+  fb.s = pb.s;
+  const dim3 grid = finish_grid<RM, GM>(pb.s);
+  {
+    hipLaunchKernelGGL((project_kernel<RM, GM>), dim3((unsigned)pb.s.G), dim3((prj_threads<RM, GM>())), 0, st, pb);
+    if (has_split_tiles(pb.s)) hipLaunchKernelGGL((finish_tiles_kernel<RM, GM, true>), grid, dim3(256), 0, st, fb);
   }
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
@@ -1131,7 +1214,10 @@ size_t project_workspace(int n, const int64_t* ks, int64_t T, int64_t forced, bo
     for (int m = 0; m < n; ++m) ns[m] = T;
     // the same items as one group each: at least as many units, so at least
     // as many workgroups as any launch of the call with GM-member groups
-    const size_t b = partial_bytes<R, GM>(project_schedule<R, GM>(n, ns, ks, forced));
+    size_t b = partial_bytes<R, GM>(project_schedule<R, GM>(n, ns, ks, forced));
+    if constexpr (GM == 1 && narrow_tile_ok<sketch_width(R), kProjectKH>())
+      if (project_narrow<R, GM>(n, ns, ks, forced))
+        b = partial_bytes<R, GM>(project_schedule<R, GM, kNarrowWN>(n, ns, ks, forced));
     out = b > out ? b : out;
   });
   return out;
@@ -1146,8 +1232,11 @@ rgc_status_t accumulate_launch(int n, const uint16_t* const* Ds, const int64_t* 
                                int64_t forced, int phase) {
   int64_t ks[kMaxItems];
   for (int m = 0; m < n; ++m) ks[m] = T;
+  constexpr bool kNarrowOk = narrow_tile_ok<sketch_width(R), 1>();
+  const bool narrow = kNarrowOk && accumulate_narrow<R>(n, ds, ks, forced);
   AccumulateBatch ab = {};
-  ab.s = accumulate_schedule<R>(n, ds, ks, forced);
+  ab.s = narrow ? accumulate_schedule<R, kNarrowOk ? kNarrowWN : 0>(n, ds, ks, forced)
+                : accumulate_schedule<R>(n, ds, ks, forced);
   FinishBatch fb = {};
   fb.s = ab.s;
   for (int m = 0; m < n; ++m) {
@@ -1160,9 +1249,20 @@ rgc_status_t accumulate_launch(int n, const uint16_t* const* Ds, const int64_t* 
   ab.part = static_cast<float*>(ws);
   ab.add_part = (phase & 1) ? 0 : 1;
   fb.part = ab.part;
-  hipLaunchKernelGGL(accumulate_kernel<R>, dim3((unsigned)ab.s.G), dim3(acc_threads<R>()), 0, st, ab);
-  if ((phase & 2) && has_split_tiles(ab.s))
-    hipLaunchKernelGGL((finish_tiles_kernel<R, 1, false>), finish_grid<R>(ab.s), dim3(256), 0, st, fb);
+  if constexpr (kNarrowOk) {
+    if (narrow) {
+      hipLaunchKernelGGL(accumulate_narrow_kernel<R>, dim3((unsigned)ab.s.G), dim3((acc_threads<R, kNarrowWN>())), 0,
+                         st, ab);
+      if ((phase & 2) && has_split_tiles(ab.s))
+        hipLaunchKernelGGL((finish_narrow_tiles_kernel<R, false>), finish_grid<R>(ab.s), dim3(256), 0, st, fb);
+      return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
+    }
+  }
+  {
+    hipLaunchKernelGGL(accumulate_kernel<R>, dim3((unsigned)ab.s.G), dim3(acc_threads<R>()), 0, st, ab);
+    if ((phase & 2) && has_split_tiles(ab.s))
+      hipLaunchKernelGGL((finish_tiles_kernel<R, 1, false>), finish_grid<R>(ab.s), dim3(256), 0, st, fb);
+  }
   return hipGetLastError() == hipSuccess ? RGC_OK : RGC_ERR_HIP;
 }
 
@@ -1170,6 +1270,9 @@ template <int R>
 size_t accumulate_workspace(int n, const int64_t* ds, int64_t T, int64_t forced) {
   int64_t ks[kMaxItems];
   for (int m = 0; m < n; ++m) ks[m] = T;
+  if constexpr (narrow_tile_ok<sketch_width(R), 1>())
+    if (accumulate_narrow<R>(n, ds, ks, forced))
+      return partial_bytes<R>(accumulate_schedule<R, kNarrowWN>(n, ds, ks, forced));
   return partial_bytes<R>(accumulate_schedule<R>(n, ds, ks, forced));
 }
 

@@ -165,10 +165,12 @@ def test_projection_repeatable(dev):
 # Sketch contractions
 # ---------------------------------------------------------------------------
 # includes k < 32 (a single, short K window), k = 2056 (a short last k chunk)
-# and T < 64 (one partial token tile)
+# and T < 64 (one partial token tile); one matrix per launch takes the narrow
+# 128-token tiles at r = 64, 96 and 128 where its K-steps are few (e.g.
+# 4096 x 2048 at r = 64), the wide 256-token tiles otherwise
 PROJECT_CASES = [(256, 512, 16), (1000, 520, 48), (37, 2048, 64), (4096, 2048, 64), (300, 1024, 128),
                  (129, 512, 192), (200, 2048, 256), (64, 512, 32), (4096, 6144, 64), (20, 24, 16),
-                 (100, 2056, 64), (7, 16, 16)]
+                 (100, 2056, 64), (7, 16, 16), (4096, 4096, 96)]
 
 
 @pytest.mark.parametrize("T,k,r", PROJECT_CASES)
@@ -187,7 +189,7 @@ def test_project_parity(dev, T, k, r):
 # split of 4 tokens)
 ACC_CASES = [(256, 256, 16), (1000, 1000, 48), (4096, 2048, 64), (77, 520, 128), (300, 264, 192),
              (513, 1024, 256), (33, 64, 32), (4096, 6144, 64), (4096, 1024, 256), (20, 72, 16), (5, 8, 64),
-             (4100, 256, 64)]
+             (4100, 256, 64), (4096, 4096, 96)]
 
 
 @pytest.mark.parametrize("T,d,r", ACC_CASES)
