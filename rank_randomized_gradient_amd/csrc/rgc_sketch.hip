@@ -13,14 +13,14 @@
 // fetching the rank operand as rarely as possible:
 //
 // * A workgroup tile is TILE = 64*WN columns of N by all R columns of r; its
-//   waves (four, or eight for the accumulate above 128 ranks) split it WN
-//   ways along N and WR ways along r, so every wave multiplies a 64 (N) x RW
-//   (r) block with 16x16x32 MFMAs, r on the M side.
-// * A K-step is 32 rows of K. The step's stream slab (32 x TILE) and rank
-//   slab (32 x R) are copied from memory straight into an LDS stage by all
-//   four waves, in 1 KB copies that do not pass through VGPRs, S - 1 steps
-//   ahead of the step being multiplied. The rank slab is fetched once per
-//   workgroup and shared by its waves.
+//   waves (four or eight, by rank: StageShape below) split it WN ways along
+//   N and WR ways along r, so every wave multiplies a 64 (N) x RW (r) block
+//   with 16x16x32 MFMAs, r on the M side.
+// * A K-step is 32 rows of K (64 for the project). The step's stream slab
+//   (32 x TILE) and rank slab (32 x R) are copied from memory straight into
+//   an LDS stage by all the waves, in 1 KB copies that do not pass through
+//   VGPRs, S - 1 steps ahead of the step being multiplied. The rank slab is
+//   fetched once per workgroup and shared by its waves.
 // * Each wave reads its A operand from the stage with transposing LDS reads
 //   (the rank operand is K-major), and its B operand with plain reads
 //   (project: X is already k-contiguous per token) or transposing reads
@@ -153,14 +153,18 @@ constexpr int kStages = 6;
 __host__ __device__ constexpr int sketch_width(int RM) { return RM > 128 && (RM / 16) % 2 == 1 ? RM + 16 : RM; }
 
 // Waves along r: up to 128 ranks one (the N tile is 256 wide, each wave holds
-// all ranks, up to 8 M-tiles); above 128 two, each with half the ranks (a
-// split that gave every wave at most 64 ranks re-read the rank operand twice
-// as often: measured on the 1.7B block at r = 256 and the 8B layer at
-// r = 128). Above 128 the accumulate keeps the 256-wide N tile with eight
-// waves (two per SIMD), so that its XP slab (32 tokens x r) is shared by 256
-// columns of D, not 128: the 1.7B block's accumulate at r = 256 71.0 -> 63.2
-// us per call. The project's X and P slabs (64 k per step) leave room for a
-// 128-wide tile only, with four waves. At r = 64, 96 and 128 both kernels
+// all ranks, up to 8 M-tiles); above 128 two, each with half the ranks (with
+// four waves, a split that gave every wave at most 64 ranks re-read the rank
+// operand twice as often: measured on the 1.7B block at r = 256 and the 8B
+// layer at r = 128). Above 128 the accumulate keeps the 256-wide N tile with
+// eight waves (two per SIMD), so that its XP slab (32 tokens x r) is shared
+// by 256 columns of D, not 128: the 1.7B block's accumulate at r = 256 71.0
+// -> 63.2 us per call. The project's X and P slabs (64 k per step) leave
+// room for a 128-wide tile only: four waves, or at r = 192 and 256, where r
+// splits into four whole 16-column blocks, eight (four along r, two per
+// SIMD), whose second wave per SIMD outweighs the X operand read by four
+// waves instead of two (the 1.7B block at r = 256: 78.3 -> 65.1 us per
+// call). At r = 64, 96 and 128 both kernels
 // run eight waves too, two along r: two waves per SIMD hide more of each
 // step's latency, and the first segment's sums fit in registers (the 8B
 // layer at r = 128: accumulate 81.5 -> 74 us, project 78 -> 76 us; the 1.7B
@@ -170,7 +174,7 @@ __host__ __device__ constexpr int sketch_width(int RM) { return RM > 128 && (RM 
 // WNF > 0 forces WNF waves along N (the narrow accumulate tile below).
 template <int R, int KH, int WNF = 0>
 struct StageShape {
-  static constexpr int WR = R > 128 || (R > 32 && (R / 16) % 2 == 0) ? 2 : 1;
+  static constexpr int WR = KH == 2 && R > 128 && (R / 16) % 4 == 0 ? 4 : R > 128 || (R > 32 && (R / 16) % 2 == 0) ? 2 : 1;
   static constexpr int WN = WNF > 0 ? WNF : R <= 128 || KH == 1 ? 4 : 2;  // waves along N
   static constexpr int WAVES = WR * WN;
   static constexpr int RW = R / WR;                              // r per wave
@@ -510,7 +514,7 @@ struct ProjectPolicy {
 #pragma unroll
       for (int p = 0; p < 4; ++p) b[nt][p] &= keep;
   }
-  __device__ void store(const AccTile<R>& res, int m, int64_t tile, bool full, int64_t slot, int wn, int rw, int g,
+  __device__ void store(const f32x4_t (&res)[Sh::MT][4], int m, int64_t tile, bool full, int64_t slot, int wn, int rw, int g,
                         int li) const {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
