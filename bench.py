@@ -296,7 +296,7 @@ class Calls:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (got --gpus {args.gpus})",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (got --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
     import torch
